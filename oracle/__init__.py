@@ -1,0 +1,150 @@
+"""fp64 CPU oracle for the Kimi Delta Attention forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU
+product path (``gated_delta_rule_05_amd``) never imports it, and this package
+imports nothing from there.
+
+The arithmetic lives in ``kda_oracle.c`` (a plain per-token recurrence in
+double precision, following the step list of "Kimi Delta Attention: la
+atencion lineal detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta
+Attention paso a paso").  This module only builds that file with gcc and
+marshals numpy arrays into it.
+
+Pins (the tests that tie this oracle to something other than itself) live in
+``tests/test_oracle_pins.py``: a brute-force product of explicit transition
+matrices, the DeltaNet and Gated DeltaNet special cases, the beta = 0 closed
+form, the beta = 1 read-back, the basis-key closed form, linearity, the
+stability bound and a hand-derived worked example.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kda_oracle.c")
+_LIB = os.path.join(_HERE, "libkda_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile kda_oracle.c into libkda_oracle.so with gcc (host only)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
+               _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64p = ctypes.POINTER(ctypes.c_int64)
+        i64 = ctypes.c_int64
+        lib.kdaref_prefill.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p, i64p,
+                                       i64, i64, i64, i64, ctypes.c_double,
+                                       f64p, f64p, ctypes.c_int]
+        lib.kdaref_prefill.restype = ctypes.c_int
+        lib.kdaref_decode_step.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p,
+                                           i64, i64, i64, i64, ctypes.c_double,
+                                           f64p]
+        lib.kdaref_decode_step.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(x, shape):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    if a.shape != tuple(shape):
+        raise ValueError("expected shape %s, got %s" % (tuple(shape), a.shape))
+    return a
+
+
+def _ptr(a, ctype):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
+            threads: int = 0):
+    """Run the token-by-token recurrence over a packed batch.
+
+    q, k: [T, H, d_k]; v: [T, H, d_v]; log_alpha: [T, H, d_k]; beta: [T, H];
+    h0: [N, H, d_k, d_v] or None (zeros); cu_seqlens: [N+1] or None (one
+    sequence of length T).  Inputs are taken as float32 values (bf16 and fp32
+    stored values convert exactly).  Returns (o [T, H, d_v], hT [N, H, d_k,
+    d_v]) as float64.  ``scale`` defaults to 1/sqrt(d_k).
+    """
+    q = np.asarray(q)
+    T, H, dk = q.shape
+    dv = np.asarray(v).shape[2]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens[-1] must equal the token count")
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    qa = _f32(q, (T, H, dk))
+    ka = _f32(k, (T, H, dk))
+    va = _f32(v, (T, H, dv))
+    la = _f32(log_alpha, (T, H, dk))
+    ba = _f32(beta, (T, H))
+    h0a = None
+    if h0 is not None:
+        h0a = np.ascontiguousarray(np.asarray(h0, dtype=np.float64))
+        if h0a.shape != (N, H, dk, dv):
+            raise ValueError("h0 must be [N, H, d_k, d_v]")
+    o = np.zeros((T, H, dv), dtype=np.float64)
+    hT = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = _load().kdaref_prefill(
+        _ptr(qa, ctypes.c_float), _ptr(ka, ctypes.c_float),
+        _ptr(va, ctypes.c_float), _ptr(la, ctypes.c_float),
+        _ptr(ba, ctypes.c_float), _ptr(h0a, ctypes.c_double),
+        _ptr(cu, ctypes.c_int64), N, H, dk, dv, float(scale),
+        _ptr(o, ctypes.c_double), _ptr(hT, ctypes.c_double), int(threads))
+    if rc != 0:
+        raise RuntimeError("kdaref_prefill failed with code %d" % rc)
+    return o, hT
+
+
+def decode_step(q, k, v, log_alpha, beta, S, scale=None):
+    """One token per sequence.  q, k: [N, H, d_k]; v: [N, H, d_v];
+    log_alpha: [N, H, d_k]; beta: [N, H]; S: [N, H, d_k, d_v] (not modified).
+    Returns (o [N, H, d_v], S_new [N, H, d_k, d_v]) as float64."""
+    q = np.asarray(q)
+    N, H, dk = q.shape
+    dv = np.asarray(v).shape[2]
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    qa = _f32(q, (N, H, dk))
+    ka = _f32(k, (N, H, dk))
+    va = _f32(v, (N, H, dv))
+    la = _f32(log_alpha, (N, H, dk))
+    ba = _f32(beta, (N, H))
+    Sa = np.array(S, dtype=np.float64, copy=True, order="C")
+    if Sa.shape != (N, H, dk, dv):
+        raise ValueError("S must be [N, H, d_k, d_v]")
+    o = np.zeros((N, H, dv), dtype=np.float64)
+    rc = _load().kdaref_decode_step(
+        _ptr(qa, ctypes.c_float), _ptr(ka, ctypes.c_float),
+        _ptr(va, ctypes.c_float), _ptr(la, ctypes.c_float),
+        _ptr(ba, ctypes.c_float), _ptr(Sa, ctypes.c_double),
+        N, H, dk, dv, float(scale), _ptr(o, ctypes.c_double))
+    if rc != 0:
+        raise RuntimeError("kdaref_decode_step failed with code %d" % rc)
+    return o, Sa
