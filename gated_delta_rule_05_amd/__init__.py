@@ -1,0 +1,227 @@
+"""MI355X (gfx950) Kimi Delta Attention forward pass: Python binding.
+
+Thin ctypes layer over ``libkda.so`` (the C ABI in ``include/kda.h``).  It
+checks tensor dtypes, shapes, devices and contiguity, allocates outputs and
+the workspace with torch, and passes raw pointers plus torch's current HIP
+stream.  Every step of the computation runs in the library's HIP kernels;
+there is no fallback: if the library is missing or the tensors are not on a
+GPU, the calls raise.
+
+    o, hT = prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None)
+    o = decode_step(q, k, v, log_alpha, beta, S, scale=None)   # S updated in place
+
+Operation: the per-key-channel gated delta rule of "Kimi Delta Attention: la
+atencion lineal detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi
+Delta Attention paso a paso"; the scale defaults to 1/sqrt(d_k) as there.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "library_path", "load_library",
+    "abi_version", "status_string", "prefill_workspace_bytes", "prefill",
+    "decode_step", "EXPORTED_SYMBOLS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+STATUS = {
+    0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "MISALIGNED",
+    4: "WORKSPACE_TOO_SMALL", 5: "HIP_ERROR",
+}
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+# Every function include/kda.h declares.
+EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
+                    "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill",
+                    "kda_decode_step")
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d: %s)" % (
+            where, STATUS.get(status, "?"), status, status_string(status)))
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            "libkda.so is not built at %s; build it with "
+            "`python -m gated_delta_rule_05_amd.build` (hipcc, gfx950)" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = ctypes.c_int
+    lib.kda_status_string.argtypes = [ctypes.c_int]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_fwd_prefill_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
+    lib.kda_fwd_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                    i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.kda_fwd_prefill.restype = ctypes.c_int
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                    vp, vp]
+    lib.kda_decode_step.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load_library().kda_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def prefill_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
+                            dtype: int = DTYPE_BF16) -> int:
+    return int(load_library().kda_fwd_prefill_workspace_bytes(total_T, N, H, d_k, d_v, dtype))
+
+
+# --------------------------------------------------------------------------
+# torch-facing wrappers
+# --------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError("q, k, v must be bfloat16 or float32, got %s" % t.dtype)
+
+
+def _check(t, name, shape, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s must be on %s, got %s" % (name, device, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
+
+
+def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
+            out=None, final_state=True, workspace=None):
+    """Chunked prefill over a packed batch.
+
+    q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
+    log_alpha: [T, H, d_k] fp32; beta: [T, H] fp32; h0: [N, H, d_k, d_v] fp32
+    or None (zeros); cu_seqlens: int32 [N+1] on the device, or None for one
+    sequence of length T.  Returns (o [T, H, d_v] in the input dtype,
+    hT [N, H, d_k, d_v] fp32 or None when final_state is False).
+    ``final_state`` may also be a preallocated tensor (it may be h0 itself).
+    """
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d_k]")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU (HIP) device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (T, H, dk), dt, dev)
+    _check(k, "k", (T, H, dk), dt, dev)
+    _check(v, "v", (T, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    if cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be 1-D")
+    N = cu_seqlens.shape[0] - 1
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if h0 is not None:
+        _check(h0, "h0", (N, H, dk, dv), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (T, H, dv), dt, dev)
+    if final_state is True:
+        hT = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    elif final_state is False or final_state is None:
+        hT = None
+    else:
+        hT = final_state
+        _check(hT, "final_state", (N, H, dk, dv), torch.float32, dev)
+    need = lib.kda_fwd_prefill_workspace_bytes(T, N, H, dk, dv, code)
+    if workspace is None:
+        workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)
+    st = lib.kda_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(h0), _ptr(cu_seqlens), T, N, H, dk, dv, code,
+                             float(scale), _ptr(out), _ptr(hT), _ptr(workspace),
+                             workspace.numel(), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_fwd_prefill")
+    return out, hT
+
+
+def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None):
+    """One decode step.  q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32);
+    log_alpha: [N, H, d_k] fp32; beta: [N, H] fp32; S: [N, H, d_k, d_v] fp32,
+    updated in place.  Returns o [N, H, d_v] in the input dtype."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU (HIP) device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (N, H, dk), dt, dev)
+    _check(k, "k", (N, H, dk), dt, dev)
+    _check(v, "v", (N, H, dv), dt, dev)
+    _check(log_alpha, "log_alpha", (N, H, dk), torch.float32, dev)
+    _check(beta, "beta", (N, H), torch.float32, dev)
+    _check(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, H, dv), dt, dev)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                             _ptr(S), N, H, dk, dv, code, float(scale), _ptr(out),
+                             _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_step")
+    return out

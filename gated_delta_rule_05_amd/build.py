@@ -1,0 +1,70 @@
+"""Build libkda.so (the gfx950 HIP kernels plus the C ABI) in-tree with hipcc.
+
+Usage: ``python -m gated_delta_rule_05_amd.build`` (or ``build()`` from
+Python).  Objects go to ``_build/`` at the repository root; the shared
+library lands next to this file so the binding finds it.  Every source is
+compiled for gfx950 only.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+OBJDIR = os.path.join(ROOT, "_build", "kda")
+LIB = os.path.join(PKG, "libkda.so")
+
+SOURCES = ["kda_api.cpp", "decode.hip", "plan.hip", "prefill_valu.hip",
+           "prefill_mfma.hip"]
+
+HIPCC_FLAGS = [
+    "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Wall", "-Wno-unused-function",
+    # no packed fp32 instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the KDA library needs ROCm's hipcc")
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc()] + HIPCC_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), res.stderr))
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libkda.so; returns its path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    sources = [s for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    jobs = max(1, min(len(sources), int(os.environ.get("MAX_JOBS", "8"))))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, sources))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=gfx950"] + objs + ["-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), res.stderr))
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

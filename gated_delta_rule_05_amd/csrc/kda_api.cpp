@@ -1,0 +1,204 @@
+// kda_api.cpp -- the C entry points declared in include/kda.h.
+//
+// Each entry point validates every argument on the host (null pointers,
+// sizes and their byte-count overflow, supported head dimensions and dtype,
+// 16-byte alignment, aliasing of outputs with inputs, workspace size) and
+// only then enqueues kernels on the caller's stream.  Nothing here
+// allocates, synchronises or keeps state between calls.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/kda.h"
+#include "kda_internal.h"
+
+namespace kda {
+hipError_t launch_prefill_valu(const PrefillArgs& a, hipStream_t stream);
+int valu_value_tiles(int d_v);
+}  // namespace kda
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr size_t kWorkspaceAlign = 256;
+
+bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// a * b without signed overflow, for non-negative operands.
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return false;
+    if (a != 0 && b > INT64_MAX / a) return false;
+    *out = a * b;
+    return true;
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Common size validation; fills byte counts.  Returns a kda_status.
+struct Sizes {
+    int64_t qk_bytes, v_bytes, la_bytes, beta_bytes, state_bytes;
+};
+
+int check_sizes(int64_t tokens, int64_t N, int64_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+                Sizes* sz) {
+    if (N < 1 || H < 1 || tokens < 0) return KDA_STATUS_INVALID_ARGUMENT;
+    if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_STATUS_UNSUPPORTED;
+    if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_STATUS_UNSUPPORTED;
+    const int64_t esz = dtype == KDA_DTYPE_F32 ? 4 : 2;
+    int64_t th, x;
+    if (!mul_ok(tokens, H, &th)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!mul_ok(th, d_k, &x) || !mul_ok(x, 4, &sz->la_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!mul_ok(th, d_k, &x) || !mul_ok(x, esz, &sz->qk_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!mul_ok(th, d_v, &x) || !mul_ok(x, esz, &sz->v_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!mul_ok(th, 4, &sz->beta_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
+    int64_t nh;
+    if (!mul_ok(N, H, &nh) || !mul_ok(nh, d_k, &x) || !mul_ok(x, d_v, &x) ||
+        !mul_ok(x, 4, &sz->state_bytes))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    // keep every byte count (and the largest launch grid) far from int64 and
+    // 32-bit grid limits: 2^31 work-groups at most, 2^62 bytes at most
+    if (nh > (int64_t{1} << 27)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (sz->la_bytes > (int64_t{1} << 62) || sz->state_bytes > (int64_t{1} << 62))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    return KDA_STATUS_OK;
+}
+
+size_t plan_bytes(int32_t N) { return round_up(static_cast<size_t>(N) * sizeof(int32_t), kWorkspaceAlign); }
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return kAbiVersion; }
+
+const char* kda_status_string(int status) {
+    switch (status) {
+        case KDA_STATUS_OK: return "ok";
+        case KDA_STATUS_INVALID_ARGUMENT: return "invalid argument";
+        case KDA_STATUS_UNSUPPORTED: return "unsupported head dimension or dtype";
+        case KDA_STATUS_MISALIGNED: return "pointer misaligned (16 bytes; beta and cu_seqlens 4)";
+        case KDA_STATUS_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KDA_STATUS_HIP_ERROR: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t kda_fwd_prefill_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k,
+                                       int32_t d_v, int32_t dtype) {
+    Sizes sz;
+    if (check_sizes(total_T, N, H, d_k, d_v, dtype, &sz) != KDA_STATUS_OK) return 0;
+    return plan_bytes(N);
+}
+
+int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, const float* h0, const int32_t* cu_seqlens,
+                    int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                    int32_t dtype, float scale, void* o, float* hT, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    Sizes sz;
+    const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, &sz);
+    if (st != KDA_STATUS_OK) return st;
+    if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!cu_seqlens) return KDA_STATUS_INVALID_ARGUMENT;
+    if (total_T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    // vector-loaded tensors need 16 bytes; beta and cu_seqlens are read as scalars
+    const void* ptrs[] = {q, k, v, log_alpha, h0, o, hT, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_STATUS_MISALIGNED;
+    if (!aligned4(beta) || !aligned4(cu_seqlens)) return KDA_STATUS_MISALIGNED;
+    const size_t need = plan_bytes(N);
+    if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_STATUS_WORKSPACE_TOO_SMALL;
+
+    // outputs may not overlap inputs (hT == h0 exactly is allowed)
+    const Range r_o = range_of(o, sz.v_bytes);
+    const Range r_hT = range_of(hT, hT ? sz.state_bytes : 0);
+    const Range r_ws = range_of(workspace, static_cast<int64_t>(need));
+    const Range inputs[] = {range_of(q, sz.qk_bytes),       range_of(k, sz.qk_bytes),
+                            range_of(v, sz.v_bytes),        range_of(log_alpha, sz.la_bytes),
+                            range_of(beta, sz.beta_bytes),  range_of(cu_seqlens, (N + 1) * 4),
+                            range_of(h0, h0 ? sz.state_bytes : 0)};
+    for (const Range& in : inputs) {
+        if (overlaps(r_o, in) || overlaps(r_ws, in)) return KDA_STATUS_INVALID_ARGUMENT;
+    }
+    for (int i = 0; i < 6; ++i)
+        if (overlaps(r_hT, inputs[i])) return KDA_STATUS_INVALID_ARGUMENT;
+    if (h0 && hT && h0 != hT && overlaps(r_hT, inputs[6])) return KDA_STATUS_INVALID_ARGUMENT;
+    if (overlaps(r_o, r_hT) || overlaps(r_o, r_ws) || overlaps(r_hT, r_ws))
+        return KDA_STATUS_INVALID_ARGUMENT;
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
+    a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
+    a.order = static_cast<int32_t*>(workspace);
+    a.total_T = total_T; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.dtype_f32 = dtype == KDA_DTYPE_F32;
+    a.scale = scale;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::launch_plan(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
+    if (kda::launch_prefill(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
+    return KDA_STATUS_OK;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                    int32_t d_v, int32_t dtype, float scale, void* o, void* stream) {
+    Sizes sz;
+    const int st = check_sizes(N, N, H, d_k, d_v, dtype, &sz);
+    if (st != KDA_STATUS_OK) return st;
+    if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_STATUS_INVALID_ARGUMENT;
+    const void* ptrs[] = {q, k, v, log_alpha, S, o};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return KDA_STATUS_MISALIGNED;
+    if (!aligned4(beta)) return KDA_STATUS_MISALIGNED;
+    const Range r_o = range_of(o, sz.v_bytes);
+    const Range others[] = {range_of(q, sz.qk_bytes),      range_of(k, sz.qk_bytes),
+                            range_of(v, sz.v_bytes),       range_of(log_alpha, sz.la_bytes),
+                            range_of(beta, sz.beta_bytes), range_of(S, sz.state_bytes)};
+    for (const Range& in : others)
+        if (overlaps(r_o, in)) return KDA_STATUS_INVALID_ARGUMENT;
+    for (int i = 0; i < 5; ++i)
+        if (overlaps(others[5], others[i])) return KDA_STATUS_INVALID_ARGUMENT;
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S; a.o = o;
+    a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.dtype_f32 = dtype == KDA_DTYPE_F32;
+    a.scale = scale;
+    if (kda::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_STATUS_HIP_ERROR;
+    return KDA_STATUS_OK;
+}
+
+}  // extern "C"
+
+namespace kda {
+
+int prefill_value_tiles(const PrefillArgs& a) { return valu_value_tiles(a.d_v); }
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+    if (a.total_T == 0 && a.hT == nullptr) return hipSuccess;
+    return launch_prefill_valu(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,51 @@
+// kda_internal.h -- argument bundles and launcher declarations shared by the
+// host entry points (kda_api.cpp) and the kernel translation units.  Every
+// launcher only enqueues work on the given stream; argument validation has
+// already happened on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    float* S;
+    void* o;
+    int32_t N, H, d_k, d_v;
+    bool dtype_f32;
+    float scale;
+};
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;
+    const float* beta;
+    const float* h0;            // may be null (zero initial state)
+    const int32_t* cu_seqlens;  // device, [N+1]
+    void* o;
+    float* hT;                  // may be null (not written)
+    int32_t* order;             // device scratch [N]: sequences by length, longest first
+    int64_t total_T;
+    int32_t N, H, d_k, d_v;
+    bool dtype_f32;
+    float scale;
+};
+
+// Work-groups per (sequence, head) that the prefill splits the d_v columns
+// of the state into (host-side choice, no device data needed).
+int prefill_value_tiles(const PrefillArgs& a);
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_plan(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,225 @@
+// prefill_valu.hip -- chunked KDA prefill with fp32 vector arithmetic.
+//
+// This is the exact-precision path: fp32 inputs (and any shape the matrix
+// core path does not cover) run here, with every product, the triangular
+// solve and the state in fp32.  It computes the same chunked (UT / WY) form
+// as the matrix-core kernel, so it also checks that algebra at a tight
+// tolerance.
+//
+// Chunked form (the pages only say the recurrence is evaluated blockwise
+// with a diagonal-plus-low-rank transition -- "Kimi Linear acaba de superar
+// a la atención completa en sus propios términos", section "Cómo Kimi
+// Linear utiliza una memoria recurrente más inteligente"; the algebra below
+// is derived from the per-token recurrence).  For a chunk of C tokens with
+// start state S0 (d_k x d_v), per key channel c:
+//   g_r   = sum_{s<=r} log_alpha_s            (cumulative gate inside the chunk)
+//   Kg    = K * e^{g},  Qg = Q * e^{g},  Kn = K * e^{-g},  Kd = K * e^{g_C - g}
+//   A     = strictly-lower(Diag(beta) Kg Kn^T)     the chunk's delta-rule system
+//   P     = lower(Qg Kn^T)                         (diagonal included)
+//   E     = (I + A)^{-1} Diag(beta) (V - Kg S0)    the delta errors of the chunk
+//   O     = scale (Qg S0 + P E)
+//   S_C   = Diag(e^{g_C}) S0 + Kd^T E
+// The rows of S never mix in any of these maps, so each work-group owns a
+// tile of TV state columns (value channels) and the tiles run in parallel.
+//
+// One work-group of 256 threads per (sequence, head, value tile) walks the
+// sequence's chunks in order; the last chunk is masked (rows past the end
+// carry k = q = v = 0, log_alpha = 0, beta = 0, so they change nothing).
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_sched.h"
+
+namespace kda {
+
+template <typename T, int DK, int TV, int C>
+__global__ __launch_bounds__(256)
+void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                         const T* __restrict__ v, const float* __restrict__ log_alpha,
+                         const float* __restrict__ beta, const float* __restrict__ h0,
+                         const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
+                         int64_t groups, int R, int H, int DV, float scale,
+                         T* __restrict__ o, float* __restrict__ hT)
+{
+    constexpr int NT = 256;
+    constexpr int KP = DK + 1;   // padded row stride: column walks hit distinct banks
+    __shared__ float sKg[C * KP], sQg[C * KP], sKn[C * KP], sKd[C * KP];
+    __shared__ float sA[C * C], sP[C * C], sTi[C * C];
+    __shared__ float sS[DK * TV], sV[C * TV], sX[C * TV], sE[C * TV];
+    __shared__ float sBeta[C], sGl[DK], sGe[DK];
+
+    int64_t pair;
+    int tile;
+    if (!prefill_map_block(blockIdx.x, groups, R, pair, tile)) return;
+    const int tid = threadIdx.x;
+    const int h = static_cast<int>(pair % H);
+    const int n = order[pair / H];
+    const int64_t t_begin = cu[n];
+    const int64_t t_end = cu[n + 1];
+    const int j0 = tile * TV;
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV + j0;
+
+    for (int i = tid; i < DK * TV; i += NT) {
+        const int c = i / TV, j = i % TV;
+        sS[i] = h0 ? h0[sbase + static_cast<int64_t>(c) * DV + j] : 0.f;
+    }
+
+    for (int64_t c0 = t_begin; c0 < t_end; c0 += C) {
+        const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
+        __syncthreads();
+        // stage k, q and log_alpha (masked past the end of the sequence)
+        for (int i = tid; i < C * DK; i += NT) {
+            const int r = i / DK, c = i % DK;
+            float kk = 0.f, qq = 0.f, la = 0.f;
+            if (r < len) {
+                const int64_t off = ((c0 + r) * H + h) * DK + c;
+                kk = elem<T>::load(k + off);
+                qq = elem<T>::load(q + off);
+                la = log_alpha[off];
+            }
+            sKg[r * KP + c] = kk;
+            sQg[r * KP + c] = qq;
+            sKn[r * KP + c] = la;
+        }
+        for (int i = tid; i < C * TV; i += NT) {
+            const int r = i / TV, j = i % TV;
+            sV[i] = (r < len) ? elem<T>::load(v + ((c0 + r) * H + h) * DV + j0 + j) : 0.f;
+        }
+        for (int r = tid; r < C; r += NT)
+            sBeta[r] = (r < len) ? beta[(c0 + r) * H + h] : 0.f;
+        __syncthreads();
+        // cumulative gate per key channel
+        for (int c = tid; c < DK; c += NT) {
+            float g = 0.f;
+            for (int r = 0; r < C; ++r) {
+                g += sKn[r * KP + c];
+                sKn[r * KP + c] = g;
+            }
+            sGl[c] = g;
+            sGe[c] = gate_exp(g);
+        }
+        __syncthreads();
+        // decay-weighted copies of k and q
+        for (int i = tid; i < C * DK; i += NT) {
+            const int r = i / DK, c = i % DK;
+            const float g = sKn[r * KP + c];
+            const float kk = sKg[r * KP + c];
+            const float eg = gate_exp(g);
+            const float emg = gate_exp(-g);
+            sKg[r * KP + c] = kk * eg;
+            sQg[r * KP + c] = sQg[r * KP + c] * eg;
+            sKn[r * KP + c] = kk * emg;
+            sKd[r * KP + c] = kk * gate_exp(sGl[c] - g);
+        }
+        __syncthreads();
+        // A (strictly lower, rows scaled by beta) and P (lower, with diagonal)
+        for (int i = tid; i < C * C; i += NT) {
+            const int r = i / C, s = i % C;
+            float a = 0.f, p = 0.f;
+            if (s <= r) {
+                const float* kg = sKg + r * KP;
+                const float* qg = sQg + r * KP;
+                const float* kn = sKn + s * KP;
+                for (int c = 0; c < DK; ++c) {
+                    a += kg[c] * kn[c];
+                    p += qg[c] * kn[c];
+                }
+                a = (s < r) ? sBeta[r] * a : 0.f;
+            }
+            sA[i] = a;
+            sP[i] = p;
+        }
+        __syncthreads();
+        // Ti = (I + A)^{-1} by forward substitution, one column per thread
+        for (int col = tid; col < C; col += NT) {
+            for (int r = 0; r < C; ++r) {
+                float x = (r == col) ? 1.f : 0.f;
+                if (r > col) {
+                    for (int s = col; s < r; ++s) x -= sA[r * C + s] * sTi[s * C + col];
+                }
+                sTi[r * C + col] = x;
+            }
+        }
+        __syncthreads();
+        // X = Diag(beta) (V - Kg S0)
+        for (int i = tid; i < C * TV; i += NT) {
+            const int r = i / TV, j = i % TV;
+            float acc = 0.f;
+            for (int c = 0; c < DK; ++c) acc += sKg[r * KP + c] * sS[c * TV + j];
+            sX[i] = sBeta[r] * (sV[i] - acc);
+        }
+        __syncthreads();
+        // E = (I + A)^{-1} X
+        for (int i = tid; i < C * TV; i += NT) {
+            const int r = i / TV, j = i % TV;
+            float acc = 0.f;
+            for (int s = 0; s <= r; ++s) acc += sTi[r * C + s] * sX[s * TV + j];
+            sE[i] = acc;
+        }
+        __syncthreads();
+        // O = scale (Qg S0 + P E)
+        for (int i = tid; i < C * TV; i += NT) {
+            const int r = i / TV, j = i % TV;
+            if (r < len) {
+                float acc = 0.f;
+                for (int c = 0; c < DK; ++c) acc += sQg[r * KP + c] * sS[c * TV + j];
+                for (int s = 0; s <= r; ++s) acc += sP[r * C + s] * sE[s * TV + j];
+                elem<T>::store(o + ((c0 + r) * H + h) * DV + j0 + j, scale * acc);
+            }
+        }
+        __syncthreads();
+        // S_C = Diag(e^{g_C}) S0 + Kd^T E
+        for (int i = tid; i < DK * TV; i += NT) {
+            const int c = i / TV, j = i % TV;
+            float acc = sGe[c] * sS[i];
+            for (int r = 0; r < C; ++r) acc += sKd[r * KP + c] * sE[r * TV + j];
+            sS[i] = acc;
+        }
+    }
+    if (hT) {
+        __syncthreads();
+        for (int i = tid; i < DK * TV; i += NT) {
+            const int c = i / TV, j = i % TV;
+            hT[sbase + static_cast<int64_t>(c) * DV + j] = sS[i];
+        }
+    }
+}
+
+template <typename T, int DK, int TV>
+static hipError_t launch_valu_t(const PrefillArgs& a, int R, hipStream_t stream) {
+    constexpr int C = 32;
+    const int64_t groups = static_cast<int64_t>(a.N) * a.H;
+    const int64_t blocks = prefill_grid_blocks(groups, R);
+    hipLaunchKernelGGL((prefill_valu_kernel<T, DK, TV, C>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(256), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.log_alpha, a.beta, a.h0,
+                       a.cu_seqlens, a.order, groups, R, a.H, a.d_v, a.scale,
+                       static_cast<T*>(a.o), a.hT);
+    return hipGetLastError();
+}
+
+template <typename T, int DK>
+static hipError_t launch_valu_dk(const PrefillArgs& a, hipStream_t stream) {
+    if (a.d_v == 16) return launch_valu_t<T, DK, 16>(a, 1, stream);
+    return launch_valu_t<T, DK, 32>(a, a.d_v / 32, stream);
+}
+
+template <typename T>
+static hipError_t launch_valu(const PrefillArgs& a, hipStream_t stream) {
+    switch (a.d_k) {
+        case 16: return launch_valu_dk<T, 16>(a, stream);
+        case 32: return launch_valu_dk<T, 32>(a, stream);
+        case 64: return launch_valu_dk<T, 64>(a, stream);
+        case 128: return launch_valu_dk<T, 128>(a, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+int valu_value_tiles(int d_v) { return d_v == 16 ? 1 : d_v / 32; }
+
+hipError_t launch_prefill_valu(const PrefillArgs& a, hipStream_t stream) {
+    if (a.dtype_f32) return launch_valu<float>(a, stream);
+    return launch_valu<bf16_t>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,152 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention forward pass.
+ *
+ * The operation.  Kimi Delta Attention (KDA) keeps one fixed-size state per
+ * head and updates it once per token with a per-key-channel gated delta
+ * rule:
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t ,        alpha_t = exp(log_alpha_t)
+ * i.e. decay every key channel of the state, predict the value stored for
+ * k_t, scale the prediction error by beta_t, write it back along k_t, and
+ * read the corrected state with the query.  Defined in "Kimi Delta
+ * Attention: la atencion lineal detras de Kimi K2 y Qwen3", section "Cómo
+ * funciona Kimi Delta Attention paso a paso" (the kda_step listing and the
+ * flowchart); the per-channel gate is what "Cos'è Kimi Delta Attention
+ * (KDA)?" (section "Gating per canale: cosa rende KDA diverso") sets apart
+ * from Gated DeltaNet.  That listing scales the query by 1/sqrt(d_k); here
+ * the scale is an argument and callers pass 1/sqrt(d_k) for that reading.
+ * Keys are expected to be L2-normalised by the caller (the first page's
+ * notes on key normalisation explain why the delta rule needs it).
+ *
+ * Layouts.  Every tensor is dense, contiguous, row-major:
+ *     q, k        [total_T][H][d_k]     dtype (bf16 or fp32)
+ *     v, o        [total_T][H][d_v]     dtype
+ *     log_alpha   [total_T][H][d_k]     fp32, expected <= 0
+ *     beta        [total_T][H]          fp32
+ *     h0, hT, S   [N][H][d_k][d_v]      fp32 (d_v contiguous)
+ *     cu_seqlens  [N+1]                 int32, DEVICE memory
+ * A batch of N sequences is packed along the token axis: sequence n owns
+ * tokens cu_seqlens[n] .. cu_seqlens[n+1]-1.  The state is always fp32.
+ *
+ * Ownership and execution.  The caller allocates every buffer (device
+ * memory), including the prefill workspace.  The library keeps no global
+ * mutable state, allocates nothing and never synchronises: each call only
+ * enqueues kernels on `stream` (a hipStream_t; NULL = the default stream)
+ * and returns.  Faults inside those kernels surface at the caller's next
+ * synchronisation.  Calls on different streams may run concurrently if
+ * their output buffers do not overlap.
+ *
+ * Errors.  Each entry point returns a kda_status value.  Every argument
+ * check listed below happens on the host before any HIP call, so a
+ * rejected call has no effect on the device.  Values inside device buffers
+ * are NOT checked (that would need a synchronisation): cu_seqlens must be
+ * 0 = c_0 <= c_1 <= ... <= c_N = total_T, and inputs must be finite.
+ * A violated device-side precondition gives undefined values confined to
+ * the sequences it touches; it never writes outside the caller's buffers
+ * for sequences whose cu_seqlens entries lie inside [0, total_T].
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum kda_status {
+    KDA_STATUS_OK = 0,
+    KDA_STATUS_INVALID_ARGUMENT = 1,   /* null required pointer, bad size,
+                                          size overflow, bad aliasing,
+                                          non-finite scale */
+    KDA_STATUS_UNSUPPORTED = 2,        /* d_k or d_v not in {16,32,64,128},
+                                          unknown dtype */
+    KDA_STATUS_MISALIGNED = 3,         /* a tensor pointer is not 16-byte
+                                          aligned (beta, cu_seqlens: 4) */
+    KDA_STATUS_WORKSPACE_TOO_SMALL = 4,
+    KDA_STATUS_HIP_ERROR = 5           /* a kernel launch was refused */
+};
+
+/* Element type of q, k, v and o.  The state, log_alpha and beta are fp32. */
+enum kda_dtype {
+    KDA_DTYPE_BF16 = 0,
+    KDA_DTYPE_F32 = 1
+};
+
+/* Version of this ABI; bumped whenever a signature or a layout changes. */
+int kda_abi_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+const char *kda_status_string(int status);
+
+/*
+ * Bytes of device workspace kda_fwd_prefill needs for these sizes (the
+ * sequence scheduling table).  Pure host arithmetic; returns 0 for
+ * arguments kda_fwd_prefill would reject.
+ */
+size_t kda_fwd_prefill_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
+                                       int32_t d_k, int32_t d_v, int32_t dtype);
+
+/*
+ * Chunked prefill over a packed batch of N sequences.
+ *
+ * Computes o for every token and, if hT != NULL, the state after each
+ * sequence's last token (hT[n] = h0[n], or zeros, for an empty sequence).
+ * h0 == NULL means a zero initial state.  hT may be the same buffer as h0
+ * (each state is read before it is written by the same work-group); any
+ * other overlap between an output (o, hT) and any input is rejected.
+ *
+ * Precision: bf16 inputs use bf16 matrix-core products with fp32
+ * accumulation and an fp32 state; fp32 inputs use fp32 arithmetic
+ * throughout.  o is written in the input dtype (round to nearest even).
+ * Within one chunk of tokens the decay factors exp(+-cumulative log_alpha)
+ * are formed separately, so the summed log_alpha of one channel over a
+ * chunk (64 tokens) must stay above -80 (e.g. per-token gates >= -1.25).
+ *
+ * Requirements (else the status in brackets):
+ *   N >= 1, H >= 1, total_T >= 0, sizes whose byte counts fit in int64
+ *     [INVALID_ARGUMENT];
+ *   q, k, v, log_alpha, beta, o non-NULL when total_T > 0; cu_seqlens
+ *     non-NULL; scale finite [INVALID_ARGUMENT];
+ *   d_k, d_v in {16, 32, 64, 128}; dtype a kda_dtype [UNSUPPORTED];
+ *   q, k, v, log_alpha, h0, o, hT and workspace 16-byte aligned, beta and
+ *     cu_seqlens 4-byte aligned [MISALIGNED];
+ *   workspace_bytes >= kda_fwd_prefill_workspace_bytes(...) and workspace
+ *     non-NULL if that is > 0 [WORKSPACE_TOO_SMALL].
+ */
+int kda_fwd_prefill(const void *q, const void *k, const void *v,
+                    const float *log_alpha, const float *beta,
+                    const float *h0, const int32_t *cu_seqlens,
+                    int64_t total_T, int32_t N, int32_t H,
+                    int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+                    void *o, float *hT,
+                    void *workspace, size_t workspace_bytes,
+                    void *stream);
+
+/*
+ * One decode step: one new token for each of N sequences.
+ *
+ * Inputs q, k [N][H][d_k], v [N][H][d_v] (dtype), log_alpha [N][H][d_k],
+ * beta [N][H] (fp32).  The state S [N][H][d_k][d_v] (fp32) is read and
+ * overwritten in place with the state after the token; o [N][H][d_v]
+ * (dtype) receives the token's output.  This is exactly one token of the
+ * recurrence above; chaining T calls equals a prefill over those T tokens.
+ * o must not overlap any input or S.
+ *
+ * Requirements: N >= 1, H >= 1, all pointers non-NULL, scale finite
+ * [INVALID_ARGUMENT]; d_k, d_v in {16, 32, 64, 128}, dtype a kda_dtype
+ * [UNSUPPORTED]; q, k, v, log_alpha, S and o 16-byte aligned, beta 4-byte
+ * aligned [MISALIGNED].
+ */
+int kda_decode_step(const void *q, const void *k, const void *v,
+                    const float *log_alpha, const float *beta, float *S,
+                    int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                    int32_t dtype, float scale, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,43 @@
+"""Helpers shared by the GPU parity tests: error metric, tolerances, host
+copies and calls into the oracle."""
+import numpy as np
+import torch
+
+import oracle
+
+# Parity bars: max-relative error of each output tensor against the fp64
+# oracle on identical stored inputs.
+TOL_F32 = 1e-5
+TOL_BF16 = 2e-2
+
+
+def tol_for(dtype):
+    return TOL_F32 if dtype in ("f32", torch.float32) else TOL_BF16
+
+
+def rel_err(x, ref):
+    """max |x - ref| / max |ref| over the whole tensor."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    denom = max(float(np.max(np.abs(ref))), 1e-30)
+    return float(np.max(np.abs(x - ref))) / denom
+
+
+def host(t):
+    """Device tensor -> float64 numpy (bf16 and fp32 widen exactly)."""
+    if t is None:
+        return None
+    return t.detach().to(torch.float64).cpu().numpy()
+
+
+def oracle_prefill(inp, scale=None, threads=0):
+    cu = inp["cu_seqlens"].cpu().numpy().astype(np.int64)
+    return oracle.prefill(host(inp["q"]), host(inp["k"]), host(inp["v"]),
+                          host(inp["log_alpha"]), host(inp["beta"]), h0=host(inp["h0"]),
+                          cu_seqlens=cu, scale=scale, threads=threads)
+
+
+def report(name, **errs):
+    print("[parity] %s " % name + " ".join("%s=%.3e" % kv for kv in errs.items()), flush=True)

@@ -1,0 +1,133 @@
+"""Host-only checks of the C ABI (no GPU needed, no kernel is ever launched).
+
+* libkda.so loads and exports every function include/kda.h declares;
+* status strings and the workspace query;
+* every argument check of kda_fwd_prefill / kda_decode_step returns its
+  documented status.  All of these calls fail validation, which happens on
+  the host before any HIP call, so they are safe on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_05_amd as kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, MISALIGNED, WS_SMALL, HIP_ERR = range(6)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "kda.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load_library()
+    declared = header_functions()
+    assert declared, "no declarations found in include/kda.h"
+    assert sorted(kda.EXPORTED_SYMBOLS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    out = os.popen("nm -D --defined-only %s" % kda.library_path()).read()
+    for name in declared:
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_status_strings_and_version():
+    assert kda.abi_version() == 1
+    for s in range(6):
+        assert kda.status_string(s)
+    assert kda.status_string(99) == "unknown status"
+
+
+def test_workspace_query():
+    assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128) == 256
+    assert kda.prefill_workspace_bytes(1000, 100, 16, 128, 128) == 512
+    assert kda.prefill_workspace_bytes(1000, 0, 16, 128, 128) == 0      # rejected
+    assert kda.prefill_workspace_bytes(1000, 4, 16, 96, 128) == 0       # unsupported
+
+
+# fake, well-aligned, non-overlapping "device" addresses; never dereferenced
+BASE = 1 << 40
+GAP = 1 << 36
+
+
+def addr(i, off=0):
+    return ctypes.c_void_p(BASE + i * GAP + off)
+
+
+def prefill_call(**over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
+                cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
+                o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
+    args.update(over)
+    lib = kda.load_library()
+    return lib.kda_fwd_prefill(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                               args["h0"], args["cu"], args["T"], args["N"], args["H"],
+                               args["dk"], args["dv"], args["dtype"], args["scale"],
+                               args["o"], args["hT"], args["ws"], args["wsb"],
+                               args["stream"])
+
+
+def decode_call(**over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), S=addr(5),
+                N=8, H=4, dk=128, dv=128, dtype=0, scale=0.1, o=addr(6), stream=None)
+    args.update(over)
+    lib = kda.load_library()
+    return lib.kda_decode_step(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                               args["S"], args["N"], args["H"], args["dk"], args["dv"],
+                               args["dtype"], args["scale"], args["o"], args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(N=0), INVALID), (dict(N=-1), INVALID), (dict(H=0), INVALID), (dict(T=-1), INVALID),
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(la=None), INVALID), (dict(beta=None), INVALID), (dict(o=None), INVALID),
+    (dict(cu=None), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(T=1 << 60), INVALID), (dict(H=1 << 30, N=1 << 30), INVALID),
+    (dict(dk=96), UNSUPPORTED), (dict(dv=8), UNSUPPORTED), (dict(dk=256), UNSUPPORTED),
+    (dict(dtype=7), UNSUPPORTED),
+    (dict(q=addr(0, 8)), MISALIGNED), (dict(o=addr(6, 4)), MISALIGNED),
+    (dict(h0=addr(9, 2)), MISALIGNED), (dict(cu=addr(5, 2)), MISALIGNED),
+    (dict(beta=addr(4, 2)), MISALIGNED), (dict(la=addr(3, 4)), MISALIGNED),
+    (dict(ws=addr(8, 8)), MISALIGNED),
+    (dict(wsb=255), WS_SMALL), (dict(ws=None), WS_SMALL),
+    # aliasing: output overlapping an input, hT partially overlapping h0
+    (dict(o=addr(2)), INVALID), (dict(o=addr(0, 256)), INVALID),
+    (dict(hT=addr(3)), INVALID), (dict(h0=addr(9), hT=addr(9, 256)), INVALID),
+    (dict(ws=addr(6)), INVALID), (dict(hT=addr(6)), INVALID),
+])
+def test_prefill_argument_checks(over, status):
+    assert prefill_call(**over) == status
+
+
+def test_prefill_empty_batch_allows_null_token_buffers():
+    # total_T = 0 with null token buffers passes the null checks; it still
+    # fails here on the (deliberately) tiny workspace, before any HIP call
+    assert prefill_call(T=0, q=None, k=None, v=None, la=None, beta=None, o=None,
+                        wsb=0) == WS_SMALL
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(N=0), INVALID), (dict(H=-2), INVALID), (dict(S=None), INVALID),
+    (dict(o=None), INVALID), (dict(q=None), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(dk=48), UNSUPPORTED), (dict(dv=512), UNSUPPORTED), (dict(dtype=2), UNSUPPORTED),
+    (dict(S=addr(5, 4)), MISALIGNED), (dict(v=addr(2, 8)), MISALIGNED),
+    (dict(beta=addr(4, 1)), MISALIGNED),
+    (dict(o=addr(5)), INVALID), (dict(S=addr(0)), INVALID),
+])
+def test_decode_argument_checks(over, status):
+    assert decode_call(**over) == status
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    q = torch.zeros(4, 2, 16)
+    with pytest.raises(ValueError):
+        kda.prefill(q, q, q, q, torch.zeros(4, 2))
+    with pytest.raises(ValueError):
+        kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))

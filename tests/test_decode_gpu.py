@@ -1,0 +1,113 @@
+"""GPU parity of kda_decode_step against the fp64 oracle (through the C ABI).
+
+Cases: every supported (d_k, d_v) pair in bf16 and fp32 over a few chained
+steps; the 256-sequence x 32-head workload over its 64 steps (sampled
+(sequence, head) pairs checked against the oracle, all pairs checked for
+finiteness); decode steps chained over a sequence equal a prefill of it;
+in-place update leaves other sequences' states untouched."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_05_amd as kda
+import kda_inputs as gen
+import oracle
+from kda_testutil import host, rel_err, report, tol_for, TOL_F32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_steps(N, H, dk, dv, dtype, steps, seed, scale=None):
+    S = gen.decode_state(N, H, dk, dv, std=0.5, seed=seed, device=DEV)
+    S_ref = host(S)
+    errs_o, errs_s = [], []
+    for step in range(steps):
+        tok = gen.decode_token_inputs(N, H, dk, dv, dtype, "uniform", seed=seed, step=step,
+                                      device=DEV)
+        o = kda.decode_step(tok["q"], tok["k"], tok["v"], tok["log_alpha"], tok["beta"], S,
+                            scale=scale)
+        o_ref, S_ref = oracle.decode_step(host(tok["q"]), host(tok["k"]), host(tok["v"]),
+                                          host(tok["log_alpha"]), host(tok["beta"]), S_ref,
+                                          scale=scale)
+        errs_o.append(rel_err(host(o), o_ref))
+        errs_s.append(rel_err(host(S), S_ref))
+    return max(errs_o), max(errs_s)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_decode_shapes(dtype, dk, dv):
+    eo, es = run_steps(5, 3, dk, dv, dtype, steps=3, seed=dk * 1000 + dv)
+    report("decode %s dk=%d dv=%d" % (dtype, dk, dv), o=eo, S=es)
+    assert eo <= tol_for(dtype)
+    assert es <= TOL_F32           # the state update is fp32 arithmetic on both dtypes
+
+
+def test_decode_custom_scale():
+    eo, es = run_steps(3, 2, 128, 64, "f32", steps=2, seed=7, scale=0.3)
+    assert eo <= TOL_F32 and es <= TOL_F32
+
+
+def test_decode_n256_workload():
+    """256 sequences x 32 heads, d = 128, fp32 state ~ N(0, 0.02), 64 steps of
+    one bf16 token each, state updated in place."""
+    w = gen.WORKLOADS["decode_n256"]
+    N, H, d = w.N, w.H, w.dk
+    seed = 3
+    S = gen.decode_state(N, H, d, d, std=w.state_std, seed=seed, device=DEV)
+    rng = np.random.default_rng(0)
+    pairs = [(0, 0), (N - 1, H - 1)] + [tuple(x) for x in zip(rng.integers(0, N, 62),
+                                                               rng.integers(0, H, 62))]
+    ns = np.array([p[0] for p in pairs])
+    hs = np.array([p[1] for p in pairs])
+    S_ref = host(S)[ns, hs][:, None]            # [P, 1, d, d]
+    worst_o = worst_s = 0.0
+    for step in range(w.steps):
+        tok = gen.decode_token_inputs(N, H, d, d, w.dtype, w.gate, seed=seed, step=step,
+                                      device=DEV)
+        o = kda.decode_step(tok["q"], tok["k"], tok["v"], tok["log_alpha"], tok["beta"], S)
+        sub = {kk: host(tok[kk])[ns, hs][:, None] for kk in tok}
+        o_ref, S_ref = oracle.decode_step(sub["q"], sub["k"], sub["v"], sub["log_alpha"],
+                                          sub["beta"], S_ref)
+        worst_o = max(worst_o, rel_err(host(o)[ns, hs], o_ref[:, 0]))
+    Sh = host(S)
+    worst_s = rel_err(Sh[ns, hs], S_ref[:, 0])
+    report("decode_n256 (64 sampled pairs, 64 steps)", o=worst_o, S=worst_s)
+    assert np.isfinite(Sh).all()
+    assert worst_o <= tol_for(w.dtype)
+    assert worst_s <= tol_for(w.dtype)
+
+
+def test_decode_chain_equals_prefill():
+    """T decode steps from h0 give the same outputs and state as one prefill
+    of those T tokens (the prefill's chunked path vs the per-token path)."""
+    T, H, dk, dv = 37, 2, 64, 32
+    inp = gen.prefill_inputs([T], H, dk, dv, "f32", "uniform", state_std=0.1, seed=11,
+                             device=DEV)
+    o_p, hT = kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                          h0=inp["h0"], cu_seqlens=inp["cu_seqlens"])
+    S = inp["h0"].clone()
+    outs = []
+    for t in range(T):
+        sl = slice(t, t + 1)
+        outs.append(kda.decode_step(inp["q"][sl], inp["k"][sl], inp["v"][sl],
+                                    inp["log_alpha"][sl], inp["beta"][sl], S))
+    o_d = torch.cat(outs, 0)
+    e_o = rel_err(host(o_d), host(o_p))
+    e_s = rel_err(host(S), host(hT))
+    report("decode chain vs prefill", o=e_o, S=e_s)
+    assert e_o <= TOL_F32 and e_s <= TOL_F32
+
+
+def test_decode_only_touches_own_state():
+    N, H, d = 6, 2, 32
+    S = gen.decode_state(N, H, d, d, std=1.0, seed=5, device=DEV)
+    tok = gen.decode_token_inputs(N - 2, H, d, d, "bf16", seed=5, device=DEV)
+    before = S.clone()
+    Sv = S[1:N - 1]                       # contiguous middle slice
+    kda.decode_step(tok["q"], tok["k"], tok["v"], tok["log_alpha"], tok["beta"], Sv)
+    torch.cuda.synchronize()
+    assert torch.equal(S[0], before[0]) and torch.equal(S[N - 1], before[N - 1])
+    assert not torch.equal(S[1], before[1])

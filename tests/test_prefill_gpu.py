@@ -1,0 +1,194 @@
+"""GPU parity of kda_fwd_prefill against the fp64 oracle (through the C ABI),
+plus properties that hold at any size.
+
+Parity: max-relative error of o and of the final states hT against the
+oracle on the same seeded inputs, at 1e-5 for fp32 inputs and 2e-2 for bf16
+inputs (fp32 state).  Cases span several chunks, ragged tails, empty
+sequences, non-zero initial states and every supported head dimension.
+
+Properties (the regression list that serving a chunked recurrent state
+calls for -- long-context recall, batching, state across block boundaries):
+varlen == separate calls (bitwise), run-to-run determinism (bitwise),
+causality (bitwise), split prefill == whole prefill, hT aliasing h0,
+empty sequences keep h0, NaN confined to its own sequence.
+"""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_05_amd as kda
+import kda_inputs as gen
+from kda_testutil import host, oracle_prefill, rel_err, report, tol_for, TOL_F32
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def call(inp, **kw):
+    return kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                       h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], **kw)
+
+
+def parity(inp, name, tol, scale=None):
+    o, hT = call(inp, scale=scale)
+    o_ref, hT_ref = oracle_prefill(inp, scale=scale)
+    eo = rel_err(host(o), o_ref)
+    es = rel_err(host(hT), hT_ref)
+    report(name, o=eo, hT=es)
+    assert eo <= tol, "o max-rel error %.3e > %.1e" % (eo, tol)
+    assert es <= tol, "hT max-rel error %.3e > %.1e" % (es, tol)
+    return eo, es
+
+
+def test_tiny_f32_workload():
+    """1 x 64 tokens, H=2, d=16, fp32, zero initial state."""
+    w = gen.WORKLOADS["tiny_f32"]
+    inp = gen.workload_prefill_inputs(w, seed=0, device=DEV)
+    parity(inp, "tiny_f32", TOL_F32)
+
+
+@pytest.mark.parametrize("dk,dv", [(16, 16), (16, 128), (128, 16), (32, 64), (64, 32),
+                                   (128, 128), (64, 128)])
+def test_f32_shapes_ragged(dk, dv):
+    inp = gen.prefill_inputs([1, 33, 70, 0, 100, 64], 2, dk, dv, "f32", "uniform",
+                             state_std=0.1, seed=dk + dv, device=DEV)
+    parity(inp, "f32 dk=%d dv=%d ragged" % (dk, dv), TOL_F32)
+
+
+@pytest.mark.parametrize("dk,dv", [(128, 128), (128, 64), (128, 32), (128, 16), (64, 64),
+                                   (32, 128), (16, 16)])
+def test_bf16_shapes_ragged(dk, dv):
+    inp = gen.prefill_inputs([1, 31, 64, 65, 200, 0, 129, 300], 3, dk, dv, "bf16",
+                             "softplus", state_std=0.02, seed=7 * dk + dv, device=DEV)
+    parity(inp, "bf16 dk=%d dv=%d ragged" % (dk, dv), tol_for("bf16"))
+
+
+def test_custom_scale():
+    inp = gen.prefill_inputs([50, 77], 2, 128, 128, "bf16", "uniform", state_std=0.02,
+                             seed=9, device=DEV)
+    parity(inp, "bf16 scale=0.05", tol_for("bf16"), scale=0.05)
+
+
+def test_batch4_t4096_workload():
+    """4 x 4096 tokens, H=16, d=128, bf16, zero initial state (every pair checked)."""
+    w = gen.WORKLOADS["batch4_t4096"]
+    inp = gen.workload_prefill_inputs(w, seed=1, device=DEV)
+    parity(inp, "batch4_t4096", tol_for("bf16"))
+
+
+# --------------------------------------------------------------------------
+# properties
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_varlen_equals_separate_calls_bitwise(dtype):
+    lens = [70, 0, 5, 130, 64]
+    inp = gen.prefill_inputs(lens, 2, 128, 64, dtype, "softplus", state_std=0.02, seed=21,
+                             device=DEV)
+    o, hT = call(inp)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    for n, L in enumerate(lens):
+        a, b = int(cu[n]), int(cu[n + 1])
+        sub = {kk: inp[kk][a:b] for kk in ("q", "k", "v", "log_alpha", "beta")}
+        o_n, h_n = kda.prefill(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub["beta"],
+                               h0=inp["h0"][n:n + 1].contiguous())
+        assert torch.equal(o[a:b], o_n)
+        assert torch.equal(hT[n:n + 1], h_n)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_repeat_runs_bitwise(dtype):
+    inp = gen.prefill_inputs([300, 45, 129], 4, 128, 128, dtype, "softplus",
+                             state_std=0.02, seed=22, device=DEV)
+    o1, h1 = call(inp)
+    o2, h2 = call(inp)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_causal_prefix_bitwise(dtype):
+    """Changing tokens after position t leaves every output up to t unchanged."""
+    T, t_cut = 200, 90            # cut inside a chunk
+    inp = gen.prefill_inputs([T], 2, 128, 128, dtype, "uniform", state_std=0.02, seed=23,
+                             device=DEV)
+    o1, _ = call(inp)
+    pert = dict(inp)
+    for kk in ("q", "k", "v"):
+        x = inp[kk].clone()
+        x[t_cut + 1:] = x[t_cut + 1:].flip(0)
+        pert[kk] = x
+    la = inp["log_alpha"].clone()
+    la[t_cut + 1:] *= 0.5
+    pert["log_alpha"] = la
+    o2, _ = call(pert)
+    assert torch.equal(o1[:t_cut + 1], o2[:t_cut + 1])
+    assert not torch.equal(o1[t_cut + 1:], o2[t_cut + 1:])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_split_prefill_equals_whole(dtype):
+    """Prefill of the first part, then of the rest from the carried state,
+    equals one prefill of the whole sequence (state across a call boundary
+    that falls inside a chunk)."""
+    T, cut = 333, 150
+    inp = gen.prefill_inputs([T], 3, 128, 128, dtype, "softplus", state_std=0.02, seed=24,
+                             device=DEV)
+    o_all, h_all = call(inp)
+    first = {kk: inp[kk][:cut] for kk in ("q", "k", "v", "log_alpha", "beta")}
+    rest = {kk: inp[kk][cut:] for kk in ("q", "k", "v", "log_alpha", "beta")}
+    o1, h1 = kda.prefill(first["q"], first["k"], first["v"], first["log_alpha"],
+                         first["beta"], h0=inp["h0"])
+    o2, h2 = kda.prefill(rest["q"], rest["k"], rest["v"], rest["log_alpha"], rest["beta"],
+                         h0=h1)
+    tol = tol_for(dtype)
+    e_o = rel_err(host(torch.cat([o1, o2])), host(o_all))
+    e_h = rel_err(host(h2), host(h_all))
+    report("split prefill %s" % dtype, o=e_o, hT=e_h)
+    assert e_o <= tol and e_h <= tol
+
+
+def test_final_state_may_alias_initial_state():
+    inp = gen.prefill_inputs([100, 7], 2, 128, 128, "bf16", "uniform", state_std=0.02,
+                             seed=25, device=DEV)
+    o1, h1 = call(inp)
+    h = inp["h0"].clone()
+    o2, h2 = kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=h,
+                         cu_seqlens=inp["cu_seqlens"], final_state=h)
+    assert h2.data_ptr() == h.data_ptr()
+    assert torch.equal(o1, o2) and torch.equal(h1, h)
+
+
+def test_empty_sequences_keep_initial_state():
+    inp = gen.prefill_inputs([0, 10, 0], 2, 64, 64, "bf16", "uniform", state_std=0.5,
+                             seed=26, device=DEV)
+    _, hT = call(inp)
+    assert torch.equal(hT[0], inp["h0"][0]) and torch.equal(hT[2], inp["h0"][2])
+    empty = gen.prefill_inputs([0, 0], 2, 64, 64, "bf16", "uniform", state_std=0.5, seed=27,
+                               device=DEV)
+    o, hT = call(empty)
+    assert o.shape[0] == 0 and torch.equal(hT, empty["h0"])
+    no_h0 = dict(empty, h0=None)
+    _, hT = call(no_h0)
+    assert torch.count_nonzero(hT) == 0
+
+
+def test_no_final_state_requested():
+    inp = gen.prefill_inputs([90], 2, 128, 128, "bf16", "uniform", seed=28, device=DEV)
+    o1, _ = call(inp)
+    o2, h = call(inp, final_state=False)
+    assert h is None and torch.equal(o1, o2)
+
+
+def test_nan_stays_in_its_sequence():
+    lens = [100, 100, 100]
+    inp = gen.prefill_inputs(lens, 2, 128, 128, "bf16", "uniform", state_std=0.02, seed=29,
+                             device=DEV)
+    o_ref, h_ref = call(inp)
+    bad = dict(inp)
+    v = inp["v"].clone()
+    v[150, 1, 3] = float("nan")         # sequence 1, head 1
+    bad["v"] = v
+    o, hT = call(bad)
+    assert torch.equal(o[:100], o_ref[:100]) and torch.equal(o[200:], o_ref[200:])
+    assert torch.equal(hT[0], h_ref[0]) and torch.equal(hT[2], h_ref[2])
+    assert torch.equal(o[100:200, 0], o_ref[100:200, 0])     # other head untouched
+    assert torch.isnan(hT[1, 1]).any()
