@@ -21,7 +21,7 @@ import math
 import os
 
 __all__ = [
-    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "library_path", "load_library",
+    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "PrefillOptions", "library_path", "load_library",
     "abi_version", "status_string", "prefill_workspace_bytes", "prefill",
     "decode_step", "EXPORTED_SYMBOLS",
 ]
@@ -35,11 +35,17 @@ STATUS = {
 }
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
+PATHS = {"auto": 0, "vector": 1, "matrix": 2}
+
+
+class PrefillOptions(ctypes.Structure):
+    """Mirror of kda_prefill_options."""
+    _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32)]
 
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
                     "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill",
-                    "kda_decode_step")
+                    "kda_fwd_prefill_ex", "kda_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -76,6 +82,10 @@ def load_library():
     lib.kda_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                     i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_fwd_prefill.restype = ctypes.c_int
+    lib.kda_fwd_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                       i32, f32, vp, vp, vp, ctypes.c_size_t,
+                                       ctypes.POINTER(PrefillOptions), vp]
+    lib.kda_fwd_prefill_ex.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -133,7 +143,7 @@ def _stream(device):
 
 
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
-            out=None, final_state=True, workspace=None):
+            out=None, final_state=True, workspace=None, path="auto", value_tiles=0):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -142,6 +152,8 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     sequence of length T.  Returns (o [T, H, d_v] in the input dtype,
     hT [N, H, d_k, d_v] fp32 or None when final_state is False).
     ``final_state`` may also be a preallocated tensor (it may be h0 itself).
+    ``path`` ("auto", "vector" or "matrix") and ``value_tiles`` (0 = automatic)
+    are the kda_prefill_options tuning knobs.
     """
     torch = _torch()
     lib = load_library()
@@ -183,12 +195,13 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     need = lib.kda_fwd_prefill_workspace_bytes(T, N, H, dk, dv, code)
     if workspace is None:
         workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)
-    st = lib.kda_fwd_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(h0), _ptr(cu_seqlens), T, N, H, dk, dv, code,
-                             float(scale), _ptr(out), _ptr(hT), _ptr(workspace),
-                             workspace.numel(), _stream(dev))
+    opts = PrefillOptions(PATHS[path], int(value_tiles))
+    st = lib.kda_fwd_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(h0), _ptr(cu_seqlens), T, N, H, dk, dv, code,
+                                float(scale), _ptr(out), _ptr(hT), _ptr(workspace),
+                                workspace.numel(), ctypes.byref(opts), _stream(dev))
     if st != 0:
-        raise KDAError(st, "kda_fwd_prefill")
+        raise KDAError(st, "kda_fwd_prefill_ex")
     return out, hT
 
 

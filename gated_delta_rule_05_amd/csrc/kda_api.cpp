@@ -14,14 +14,9 @@
 #include "../../include/kda.h"
 #include "kda_internal.h"
 
-namespace kda {
-hipError_t launch_prefill_valu(const PrefillArgs& a, hipStream_t stream);
-int valu_value_tiles(int d_v);
-}  // namespace kda
-
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr size_t kWorkspaceAlign = 256;
 
 bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -109,11 +104,12 @@ size_t kda_fwd_prefill_workspace_bytes(int64_t total_T, int32_t N, int32_t H, in
     return plan_bytes(N);
 }
 
-int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
-                    const float* beta, const float* h0, const int32_t* cu_seqlens,
-                    int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
-                    int32_t dtype, float scale, void* o, float* hT, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, const float* h0, const int32_t* cu_seqlens,
+                       int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                       int32_t dtype, float scale, void* o, float* hT, void* workspace,
+                       size_t workspace_bytes, const kda_prefill_options* options,
+                       void* stream) {
     Sizes sz;
     const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, &sz);
     if (st != KDA_STATUS_OK) return st;
@@ -146,6 +142,11 @@ int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* lo
     if (overlaps(r_o, r_hT) || overlaps(r_o, r_ws) || overlaps(r_hT, r_ws))
         return KDA_STATUS_INVALID_ARGUMENT;
 
+    const int32_t path = options ? options->path : KDA_PATH_AUTO;
+    const int32_t tiles = options ? options->value_tiles : 0;
+    if (path != KDA_PATH_AUTO && path != KDA_PATH_VECTOR && path != KDA_PATH_MATRIX)
+        return KDA_STATUS_INVALID_ARGUMENT;
+
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
@@ -153,10 +154,33 @@ int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* lo
     a.total_T = total_T; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
     a.dtype_f32 = dtype == KDA_DTYPE_F32;
     a.scale = scale;
+    const bool matrix_ok = kda::mfma_supported(a);
+    if (path == KDA_PATH_MATRIX && !matrix_ok) return KDA_STATUS_UNSUPPORTED;
+    const bool use_matrix = path == KDA_PATH_MATRIX || (path == KDA_PATH_AUTO && matrix_ok);
+    int R = 0;
+    if (use_matrix) {
+        if (tiles < 0 || (tiles & (tiles - 1)) != 0 || (tiles > 0 && d_v / tiles < 16))
+            return KDA_STATUS_INVALID_ARGUMENT;
+        R = tiles > 0 ? tiles : kda::mfma_value_tiles(a);
+    } else if (tiles < 0) {
+        return KDA_STATUS_INVALID_ARGUMENT;
+    }
+
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (kda::launch_plan(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
-    if (kda::launch_prefill(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
-    return KDA_STATUS_OK;
+    const hipError_t e = use_matrix ? kda::launch_prefill_mfma(a, R, s)
+                                    : kda::launch_prefill_valu(a, s);
+    return e == hipSuccess ? KDA_STATUS_OK : KDA_STATUS_HIP_ERROR;
+}
+
+int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, const float* h0, const int32_t* cu_seqlens,
+                    int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                    int32_t dtype, float scale, void* o, float* hT, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    return kda_fwd_prefill_ex(q, k, v, log_alpha, beta, h0, cu_seqlens, total_T, N, H, d_k,
+                              d_v, dtype, scale, o, hT, workspace, workspace_bytes, nullptr,
+                              stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -192,13 +216,3 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
 
 }  // extern "C"
 
-namespace kda {
-
-int prefill_value_tiles(const PrefillArgs& a) { return valu_value_tiles(a.d_v); }
-
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-    if (a.total_T == 0 && a.hT == nullptr) return hipSuccess;
-    return launch_prefill_valu(a, stream);
-}
-
-}  // namespace kda

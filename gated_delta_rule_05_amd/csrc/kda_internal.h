@@ -40,12 +40,14 @@ struct PrefillArgs {
     float scale;
 };
 
-// Work-groups per (sequence, head) that the prefill splits the d_v columns
-// of the state into (host-side choice, no device data needed).
-int prefill_value_tiles(const PrefillArgs& a);
-
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// fp32 vector path (any dtype and supported head dimensions)
+hipError_t launch_prefill_valu(const PrefillArgs& a, hipStream_t stream);
+// bf16 matrix-core path (d_k = 128); R value tiles per (sequence, head)
+bool mfma_supported(const PrefillArgs& a);
+int mfma_value_tiles(const PrefillArgs& a);
+hipError_t launch_prefill_mfma(const PrefillArgs& a, int R, hipStream_t stream);
 
 }  // namespace kda

@@ -215,8 +215,6 @@ static hipError_t launch_valu(const PrefillArgs& a, hipStream_t stream) {
     return hipErrorInvalidValue;
 }
 
-int valu_value_tiles(int d_v) { return d_v == 16 ? 1 : d_v / 32; }
-
 hipError_t launch_prefill_valu(const PrefillArgs& a, hipStream_t stream) {
     if (a.dtype_f32) return launch_valu<float>(a, stream);
     return launch_valu<bf16_t>(a, stream);

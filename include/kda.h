@@ -75,6 +75,26 @@ enum kda_dtype {
     KDA_DTYPE_F32 = 1
 };
 
+/* Which kernel family computes a prefill. */
+enum kda_path {
+    KDA_PATH_AUTO = 0,     /* matrix path when supported, else vector path */
+    KDA_PATH_VECTOR = 1,   /* fp32 vector arithmetic, chunks of 32 tokens;
+                              any supported dtype and head dimensions */
+    KDA_PATH_MATRIX = 2    /* bf16 matrix cores, fp32 accumulation and
+                              state, chunks of 64 tokens; bf16 and d_k = 128 */
+};
+
+/* Tuning options of kda_fwd_prefill_ex (zero-initialise for defaults). */
+typedef struct kda_prefill_options {
+    int32_t path;          /* a kda_path */
+    int32_t value_tiles;   /* work-groups per (sequence, head), each owning
+                              d_v / value_tiles state columns; 0 = automatic.
+                              Matrix path: a power of two with
+                              d_v / value_tiles >= 16.  Ignored by the vector
+                              path, which always uses 32-column tiles
+                              (16 when d_v = 16). */
+} kda_prefill_options;
+
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
 int kda_abi_version(void);
 
@@ -124,6 +144,24 @@ int kda_fwd_prefill(const void *q, const void *k, const void *v,
                     void *o, float *hT,
                     void *workspace, size_t workspace_bytes,
                     void *stream);
+
+/*
+ * kda_fwd_prefill with explicit tuning options (NULL = defaults).  Same
+ * arguments, results and requirements as kda_fwd_prefill, plus:
+ *   options->path not a kda_path, or value_tiles invalid for the chosen path
+ *     [INVALID_ARGUMENT];
+ *   KDA_PATH_MATRIX requested for fp32 inputs or d_k != 128 [UNSUPPORTED].
+ * Both paths compute the same chunked form of the recurrence with different
+ * chunk lengths and precisions; results agree to the precision bound above.
+ */
+int kda_fwd_prefill_ex(const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *beta,
+                       const float *h0, const int32_t *cu_seqlens,
+                       int64_t total_T, int32_t N, int32_t H,
+                       int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+                       void *o, float *hT,
+                       void *workspace, size_t workspace_bytes,
+                       const kda_prefill_options *options, void *stream);
 
 /*
  * One decode step: one new token for each of N sequences.

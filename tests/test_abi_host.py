@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 1
+    assert kda.abi_version() == 2
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -131,3 +131,31 @@ def test_binding_rejects_cpu_tensors():
         kda.prefill(q, q, q, q, torch.zeros(4, 2))
     with pytest.raises(ValueError):
         kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
+
+
+def prefill_ex_call(path, tiles, **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
+                cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
+                o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
+    args.update(over)
+    opts = kda.PrefillOptions(path, tiles)
+    lib = kda.load_library()
+    return lib.kda_fwd_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                  args["h0"], args["cu"], args["T"], args["N"], args["H"],
+                                  args["dk"], args["dv"], args["dtype"], args["scale"],
+                                  args["o"], args["hT"], args["ws"], args["wsb"],
+                                  ctypes.byref(opts), args["stream"])
+
+
+@pytest.mark.parametrize("path,tiles,over,status", [
+    (3, 0, {}, INVALID), (-1, 0, {}, INVALID),
+    (2, 3, {}, INVALID), (2, 16, {}, INVALID), (2, -2, {}, INVALID),
+    (2, 4, dict(dv=32), INVALID),                 # 8 columns per tile
+    (2, 0, dict(dtype=1), UNSUPPORTED),           # matrix path needs bf16
+    (2, 0, dict(dk=64), UNSUPPORTED),             # matrix path needs d_k = 128
+    (1, -1, {}, INVALID),
+    (2, 8, dict(N=0), INVALID),                   # ordinary checks still apply
+    (1, 0, dict(q=addr(0, 4)), MISALIGNED),
+])
+def test_prefill_ex_option_checks(path, tiles, over, status):
+    assert prefill_ex_call(path, tiles, **over) == status

@@ -63,6 +63,35 @@ def test_bf16_shapes_ragged(dk, dv):
     parity(inp, "bf16 dk=%d dv=%d ragged" % (dk, dv), tol_for("bf16"))
 
 
+@pytest.mark.parametrize("tiles", [1, 2, 4, 8])
+def test_matrix_path_every_tile_width(tiles):
+    """Each value-tile width of the matrix path (128, 64, 32, 16 columns)."""
+    inp = gen.prefill_inputs([200, 64, 1, 129], 3, 128, 128, "bf16", "softplus",
+                             state_std=0.02, seed=40 + tiles, device=DEV)
+    o, hT = call(inp, path="matrix", value_tiles=tiles)
+    o_ref, hT_ref = oracle_prefill(inp)
+    eo, es = rel_err(host(o), o_ref), rel_err(host(hT), hT_ref)
+    report("matrix path, %d value tiles" % tiles, o=eo, hT=es)
+    assert eo <= tol_for("bf16") and es <= tol_for("bf16")
+
+
+def test_chunk_length_invariance():
+    """The vector path (chunks of 32, fp32 products) and the matrix path
+    (chunks of 64, bf16 products) on the same bf16 inputs agree with each
+    other to the bf16 bar: the chunk length is not part of the result."""
+    inp = gen.prefill_inputs([300, 77, 1], 2, 128, 128, "bf16", "uniform", state_std=0.02,
+                             seed=44, device=DEV)
+    o_v, h_v = call(inp, path="vector")
+    o_m, h_m = call(inp, path="matrix")
+    o_ref, h_ref = oracle_prefill(inp)
+    e_vm = rel_err(host(o_m), host(o_v))
+    report("vector (C=32) vs matrix (C=64)", o=e_vm, hT=rel_err(host(h_m), host(h_v)),
+           o_vec_vs_oracle=rel_err(host(o_v), o_ref))
+    assert rel_err(host(o_v), o_ref) <= 5e-3     # vector path: only the bf16 output rounding
+    assert e_vm <= tol_for("bf16")
+    assert rel_err(host(h_m), host(h_v)) <= tol_for("bf16")
+
+
 def test_custom_scale():
     inp = gen.prefill_inputs([50, 77], 2, 128, 128, "bf16", "uniform", state_std=0.02,
                              seed=9, device=DEV)
