@@ -1,0 +1,210 @@
+"""Benchmark of the KDA forward pass on one MI355X.
+
+One step = one pass of the whole hot path on resident synthetic inputs:
+  * a chunked prefill of 1 x 1,048,576 tokens, H = 32, d_k = d_v = 128, bf16
+    (log_alpha = -0.05 softplus(N(0,1)), beta = sigmoid(N(0,1)), zero state);
+  * 64 decode steps of 256 sequences x 32 heads, d = 128, on a resident fp32
+    state (512 MiB) updated in place.
+``value`` is the prefill throughput in tokens/s (B*T per second, each token
+counted once across its 32 heads), from HIP events around the prefill
+launches.  The decode figures (sequence-steps/s and state GB/s) are reported
+beside it.  ``roofline`` is the prefill kernel against MI355X HBM (8 TB/s):
+algorithmic bytes per launch = 1540 B per head-token (bf16 q, k, v, o; fp32
+log_alpha; fp32 beta) plus the final states, over the measured launch time.
+
+cpu_baseline: the fp64 oracle on a bounded sample of the same workload (a
+few heads over the first tokens), on the host's cores, scaled to tokens/s of
+the full 32-head layer.  It doubles as a parity spot check of those outputs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+PREFILL_BYTES_PER_HT = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (512) + beta (4)
+DECODE_BYTES_PER_HS = 2 * 128 * 128 * 4 + 1540   # state read + write, token inputs, output
+PREFILL_KERNEL = "prefill_mfma_kernel"
+DECODE_KERNEL = "decode_step_kernel"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=16)
+    ap.add_argument("--cpu-tokens", type=int, default=524288)
+    return ap.parse_args()
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gated_delta_rule_05_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_file, digest):
+    """HBM traffic per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_file)
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU; this build has no multi-GPU path "
+              "(heads and sequences shard across GPUs without communication).",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import gated_delta_rule_05_amd as kda
+    import kda_inputs as gen
+
+    dev = "cuda"
+    kda.load_library()
+    stream = torch.cuda.current_stream()
+
+    # ---------------- inputs (resident before timing) ----------------------
+    wp = gen.WORKLOADS["long_t1m"]
+    inp = gen.workload_prefill_inputs(wp, seed=2, device=dev)
+    T, H = sum(inp["lengths"]), wp.H
+    o = torch.empty((T, H, wp.dv), dtype=torch.bfloat16, device=dev)
+    hT = torch.empty((1, H, wp.dk, wp.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.prefill_workspace_bytes(T, 1, H, wp.dk, wp.dv), dtype=torch.uint8,
+                     device=dev)
+    wd = gen.WORKLOADS["decode_n256"]
+    S = gen.decode_state(wd.N, wd.H, wd.dk, wd.dv, std=wd.state_std, seed=3, device=dev)
+    S0 = S.clone()
+    toks = [gen.decode_token_inputs(wd.N, wd.H, wd.dk, wd.dv, wd.dtype, wd.gate, seed=3,
+                                    step=s, device=dev) for s in range(wd.steps)]
+    o_dec = torch.empty((wd.N, wd.H, wd.dv), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill():
+        kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                    cu_seqlens=inp["cu_seqlens"], out=o, final_state=hT, workspace=ws)
+
+    def decode_all():
+        for t in toks:
+            kda.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], S, out=o_dec)
+
+    for _ in range(args.warmup):
+        prefill()
+        decode_all()
+    S.copy_(S0)
+    torch.cuda.synchronize()
+
+    # ---------------- timed steps -------------------------------------------
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        prefill()
+        e1.record(stream)
+        decode_all()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [a.elapsed_time(b) for a, b, _ in ev]
+    dec_ms = [b.elapsed_time(c) for _, b, c in ev]
+    pre_avg = sum(pre_ms) / len(pre_ms)
+    dec_avg = sum(dec_ms) / len(dec_ms)
+    ms_per_step = wall * 1e3 / args.steps
+
+    tokens_per_s = T / (pre_avg * 1e-3)
+    alg_bytes = PREFILL_BYTES_PER_HT * T * H + hT.numel() * 4
+    achieved = alg_bytes / (pre_avg * 1e-3) / 1e9
+    flops_c64 = (10 * 64 * 128 + 6 * 128 * 128) * T * H
+    dec_step_us = dec_avg * 1e3 / wd.steps
+    dec_bytes = DECODE_BYTES_PER_HS * wd.N * wd.H
+    dec_gbps = dec_bytes / (dec_step_us * 1e-6) / 1e9
+
+    digest = source_digest(["prefill_mfma.hip", "kda_device.h", "kda_sched.h"])
+    traffic = load_traffic("prefill_mfma.hip", digest)
+
+    result = {
+        "metric": "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, % of MI355X roofline",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long_t1m: prefill B=1 T=1048576 H=32 d_k=d_v=128 bf16, "
+                               "fp32 state; plus decode_n256: 64 steps x 256 seqs x 32 heads",
+                   "global_batch": 1, "seq_len": T, "heads": H, "d_k": 128, "d_v": 128,
+                   "parallelism": "none (1 GPU)"},
+        "prefill_ms": pre_avg,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "kernel": PREFILL_KERNEL,
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "mfma_useful_frac_c64": flops_c64 / (pre_avg * 1e-3) / 1e12
+                     / MFMA_BF16_PEAK_TFLOPS},
+        "decode": {"workload": "decode_n256", "us_per_step": dec_step_us,
+                   "seq_steps_per_s": wd.N / (dec_step_us * 1e-6),
+                   "state_GBps": dec_gbps, "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS,
+                   "algorithmic_bytes_per_step": dec_bytes, "kernel": DECODE_KERNEL},
+        "cpu_baseline": None,
+    }
+
+    # ---------------- CPU baseline: the oracle on a bounded sample ---------
+    if not args.no_cpu_baseline:
+        import oracle
+        nh, nt = min(args.cpu_heads, H), min(args.cpu_tokens, T)
+        heads = list(range(0, H, max(1, H // nh)))[:nh]
+
+        def hostsel(t):
+            return t[:nt, heads].to(torch.float32).cpu().numpy()
+
+        sub = {kk: hostsel(inp[kk]) for kk in ("q", "k", "v", "log_alpha")}
+        sub_beta = inp["beta"][:nt, heads].cpu().numpy()
+        threads = min(len(heads), os.cpu_count() or 1)
+        t_c = time.perf_counter()
+        o_ref, _ = oracle.prefill(sub["q"], sub["k"], sub["v"], sub["log_alpha"], sub_beta,
+                                  scale=1.0 / math.sqrt(wp.dk), threads=threads)
+        cpu_s = time.perf_counter() - t_c
+        got = o[:nt, heads].to(torch.float64).cpu().numpy()
+        err = float(np.max(np.abs(got - o_ref)) / max(np.max(np.abs(o_ref)), 1e-30))
+        head_tokens_per_s = nt * len(heads) / cpu_s
+        result["cpu_baseline"] = {
+            "value": head_tokens_per_s / H, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d heads x first %d tokens of the prefill workload (fp64 "
+                      "token loop, one thread per head), %.1f s; tokens/s scaled to all "
+                      "%d heads" % (len(heads), H, nt, cpu_s, H),
+            "parity_max_rel_err_o": err}
+
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -84,9 +84,13 @@ __device__ __forceinline__ u32x4 perm_row(const uint16_t* row, int kk, int g) {
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// the ten lower-triangular 16x16 tiles of a 64x64 matrix
-__constant__ int8_t kTileI[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kTileJ[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// the ten lower-triangular 16x16 tiles (I, J), J <= I, of a 64x64 matrix,
+// numbered row by row: job = I (I + 1) / 2 + J
+__device__ __forceinline__ int tile_row(int job) { return (job >= 1) + (job >= 3) + (job >= 6); }
+__device__ __forceinline__ int tile_col(int job) {
+    const int I = tile_row(job);
+    return job - I * (I + 1) / 2;
+}
 
 template <int TV>
 struct alignas(16) Smem {
@@ -168,13 +172,16 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int row = 16 * qr + r;
-                uint32_t kv = 0u, qv = 0u;
-                float2 la = make_float2(0.f, 0.f);
-                if (row < len) {
-                    const int64_t off = ((c0 + row) * H + h) * DK + 2 * cp;
-                    kv = *reinterpret_cast<const uint32_t*>(k + off);
-                    qv = *reinterpret_cast<const uint32_t*>(q + off);
-                    la = *reinterpret_cast<const float2*>(log_alpha + off);
+                // rows past the end read row 0 of the chunk and are zeroed
+                const bool valid = row < len;
+                const int64_t off = ((c0 + (valid ? row : 0)) * H + h) * DK + 2 * cp;
+                uint32_t kv = *reinterpret_cast<const uint32_t*>(k + off);
+                uint32_t qv = *reinterpret_cast<const uint32_t*>(q + off);
+                float2 la = *reinterpret_cast<const float2*>(log_alpha + off);
+                if (!valid) {
+                    kv = 0u;
+                    qv = 0u;
+                    la = make_float2(0.f, 0.f);
                 }
                 kx[r] = __uint_as_float(kv << 16);
                 ky[r] = __uint_as_float(kv & 0xffff0000u);
@@ -239,7 +246,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 
         // ---- 2. A = strictly-lower(Diag(beta) Kg Kn^T) -----------------
         for (int job = wave; job < 10; job += 4) {
-            const int I = kTileI[job], J = kTileJ[job];
+            const int I = tile_row(job), J = tile_col(job);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
@@ -250,7 +257,8 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * I + 4 * g + i, s = 16 * J + ln;
-                const float val = (r > s) ? sm.beta[r] * acc[i] : 0.f;
+                const float br = sm.beta[r];
+                const float val = (r > s) ? br * acc[i] : 0.f;
                 sm.an[r * RS + s] = bf(-val);
                 if (I == J) sm.adiag[(I * 16 + 4 * g + i) * AS + ln] = val;
             }
@@ -273,7 +281,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             for (int r = 0; r < 16; ++r) sm.dinv[(g * 16 + r) * DS + ln] = bf(d[r]);
         } else {
             for (int job = wave - 1; job < 10; job += 3) {
-                const int I = kTileI[job], J = kTileJ[job];
+                const int I = tile_row(job), J = tile_col(job);
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {

@@ -1,0 +1,131 @@
+"""Full-size workloads on the GPU, in the launch configuration bench.py times.
+
+* long_t1m (1 x 1,048,576 tokens, H = 32, d = 128, bf16): the oracle checks
+  two whole heads, every token and the final state;
+* varlen_n64 (64 packed sequences, lengths log-uniform in [128, 32768],
+  non-zero initial states): the oracle checks every head of the longest
+  sequence plus random (sequence, head) pairs;
+* needle at 1,048,576 tokens on every head: reserved key channels are
+  written once (beta = 1, a basis key, no decay on that channel) at
+  different depths and never touched again, so reading them back with a
+  basis query at the end must return scale * the stored value exactly, up
+  to the output's bf16 rounding.  This checks the state carried across all
+  16,384 chunk boundaries -- the failure the pages report for a serving
+  stack's chunked prefill (short prompts fine, long-range retrieval broken;
+  "Kimi Linear acaba de superar a la atención completa en sus propios
+  términos", section on open source and the software-stack risk).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_05_amd as kda
+import kda_inputs as gen
+import oracle
+from kda_testutil import host, rel_err, report, TOL_BF16
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run(inp):
+    return kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                       h0=inp["h0"], cu_seqlens=inp["cu_seqlens"])
+
+
+def oracle_pairs(inp, pairs, threads=16):
+    """Oracle on selected (sequence, head) pairs; returns {pair: (o, hT)}."""
+    cu = inp["cu_seqlens"].cpu().numpy()
+    out = {}
+    # group the pairs by sequence so one oracle call covers several heads
+    by_seq = {}
+    for n, h in pairs:
+        by_seq.setdefault(n, []).append(h)
+    for n, heads in by_seq.items():
+        a, b = int(cu[n]), int(cu[n + 1])
+        sel = lambda t: t[a:b][:, heads].to(torch.float32).cpu().numpy()
+        h0 = None if inp["h0"] is None else inp["h0"][n:n + 1][:, heads].cpu().numpy()
+        o_ref, hT_ref = oracle.prefill(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]),
+                                       sel(inp["log_alpha"]),
+                                       inp["beta"][a:b][:, heads].cpu().numpy(), h0=h0,
+                                       threads=threads)
+        for i, h in enumerate(heads):
+            out[(n, h)] = (o_ref[:, i], hT_ref[0, i])
+    return out
+
+
+def test_long_t1m_two_heads_full_length():
+    w = gen.WORKLOADS["long_t1m"]
+    inp = gen.workload_prefill_inputs(w, seed=5, device=DEV)
+    o, hT = run(inp)
+    heads = [0, 29]
+    ref = oracle_pairs(inp, [(0, h) for h in heads])
+    worst_o = worst_h = 0.0
+    for h in heads:
+        o_ref, h_ref = ref[(0, h)]
+        worst_o = max(worst_o, rel_err(host(o[:, h]), o_ref))
+        worst_h = max(worst_h, rel_err(host(hT[0, h]), h_ref))
+    report("long_t1m heads %s, all 1048576 tokens" % heads, o=worst_o, hT=worst_h)
+    assert worst_o <= TOL_BF16 and worst_h <= TOL_BF16
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+
+
+def test_varlen_n64_sampled_pairs():
+    w = gen.WORKLOADS["varlen_n64"]
+    inp = gen.workload_prefill_inputs(w, seed=6, device=DEV)
+    o, hT = run(inp)
+    lens = np.array(inp["lengths"])
+    longest = int(np.argmax(lens))
+    rng = np.random.default_rng(1)
+    pairs = [(longest, h) for h in range(w.H)]
+    pairs += [(int(n), int(h)) for n, h in zip(rng.integers(0, w.N, 24), rng.integers(0, w.H, 24))]
+    pairs = sorted(set(pairs))
+    ref = oracle_pairs(inp, pairs)
+    cu = inp["cu_seqlens"].cpu().numpy()
+    worst_o = worst_h = 0.0
+    for (n, h), (o_ref, h_ref) in ref.items():
+        a, b = int(cu[n]), int(cu[n + 1])
+        worst_o = max(worst_o, rel_err(host(o[a:b, h]), o_ref))
+        worst_h = max(worst_h, rel_err(host(hT[n, h]), h_ref))
+    report("varlen_n64 (%d pairs, longest L=%d, total T=%d)" % (len(ref), lens.max(),
+                                                                 lens.sum()),
+           o=worst_o, hT=worst_h)
+    assert worst_o <= TOL_BF16 and worst_h <= TOL_BF16
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+
+
+def test_needles_survive_one_million_tokens():
+    T, H, d = 1 << 20, 32, 128
+    inp = gen.prefill_inputs([T], H, d, d, "bf16", "softplus", state_std=0.0, seed=7,
+                             device=DEV)
+    chans = [0, 17, 64, 100, 127]                  # reserved key channels
+    depths = [0, 1, 4095, 65537, 700001]           # where each needle is written
+    probes = [T - 1 - i for i in range(len(chans))]
+    k = inp["k"].float()
+    k[:, :, chans] = 0.0                           # no other token touches them
+    k = k / k.norm(dim=-1, keepdim=True)
+    la = inp["log_alpha"]
+    la[:, :, chans] = 0.0                          # and they never decay
+    q = inp["q"].float()
+    beta = inp["beta"]
+    for c, t in zip(chans, depths):
+        k[t] = 0.0
+        k[t, :, c] = 1.0
+        beta[t] = 1.0
+    for c, t in zip(chans, probes):
+        q[t] = 0.0
+        q[t, :, c] = 1.0
+    inp["k"] = k.to(torch.bfloat16)
+    inp["q"] = q.to(torch.bfloat16)
+    o, _ = run(inp)
+    scale = 1.0 / math.sqrt(d)
+    worst = 0.0
+    for c, t, p in zip(chans, depths, probes):
+        want = scale * inp["v"][t].double()        # [H, d]
+        got = o[p].double()
+        worst = max(worst, float(((got - want).abs() / want.abs().clamp_min(1e-3)).max()))
+    report("needles at depths %s read at the end of 1048576 tokens, all heads" % depths,
+           max_rel=worst)
+    assert worst <= 2.0 ** -8                      # one bf16 rounding of the output
