@@ -159,7 +159,7 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     const bool use_matrix = path == KDA_PATH_MATRIX || (path == KDA_PATH_AUTO && matrix_ok);
     int R = 0;
     if (use_matrix) {
-        if (tiles < 0 || (tiles & (tiles - 1)) != 0 || (tiles > 0 && d_v / tiles < 16))
+        if (tiles < 0 || (tiles > 0 && !kda::mfma_tiles_ok(d_v, tiles)))
             return KDA_STATUS_INVALID_ARGUMENT;
         R = tiles > 0 ? tiles : kda::mfma_value_tiles(a);
     } else if (tiles < 0) {

@@ -48,6 +48,7 @@ hipError_t launch_prefill_valu(const PrefillArgs& a, hipStream_t stream);
 // bf16 matrix-core path (d_k = 128); R value tiles per (sequence, head)
 bool mfma_supported(const PrefillArgs& a);
 int mfma_value_tiles(const PrefillArgs& a);
+bool mfma_tiles_ok(int d_v, int R);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int R, hipStream_t stream);
 
 }  // namespace kda

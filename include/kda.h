@@ -90,7 +90,7 @@ typedef struct kda_prefill_options {
     int32_t value_tiles;   /* work-groups per (sequence, head), each owning
                               d_v / value_tiles state columns; 0 = automatic.
                               Matrix path: a power of two with
-                              d_v / value_tiles >= 16.  Ignored by the vector
+                              16 <= d_v / value_tiles <= 64.  Ignored by the vector
                               path, which always uses 32-column tiles
                               (16 when d_v = 16). */
 } kda_prefill_options;

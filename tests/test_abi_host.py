@@ -151,6 +151,7 @@ def prefill_ex_call(path, tiles, **over):
     (3, 0, {}, INVALID), (-1, 0, {}, INVALID),
     (2, 3, {}, INVALID), (2, 16, {}, INVALID), (2, -2, {}, INVALID),
     (2, 4, dict(dv=32), INVALID),                 # 8 columns per tile
+    (2, 1, {}, INVALID),                          # 128 columns per tile
     (2, 0, dict(dtype=1), UNSUPPORTED),           # matrix path needs bf16
     (2, 0, dict(dk=64), UNSUPPORTED),             # matrix path needs d_k = 128
     (1, -1, {}, INVALID),

@@ -63,9 +63,9 @@ def test_bf16_shapes_ragged(dk, dv):
     parity(inp, "bf16 dk=%d dv=%d ragged" % (dk, dv), tol_for("bf16"))
 
 
-@pytest.mark.parametrize("tiles", [1, 2, 4, 8])
+@pytest.mark.parametrize("tiles", [2, 4, 8])
 def test_matrix_path_every_tile_width(tiles):
-    """Each value-tile width of the matrix path (128, 64, 32, 16 columns)."""
+    """Each value-tile width of the matrix path (64, 32, 16 columns)."""
     inp = gen.prefill_inputs([200, 64, 1, 129], 3, 128, 128, "bf16", "softplus",
                              state_std=0.02, seed=40 + tiles, device=DEV)
     o, hT = call(inp, path="matrix", value_tiles=tiles)
