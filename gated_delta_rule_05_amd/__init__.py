@@ -22,7 +22,7 @@ import os
 
 __all__ = [
     "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "PrefillOptions", "library_path", "load_library",
-    "abi_version", "status_string", "prefill_workspace_bytes", "prefill",
+    "abi_version", "status_string", "prefill_options", "prefill_workspace_bytes", "prefill",
     "decode_step", "EXPORTED_SYMBOLS",
 ]
 
@@ -35,17 +35,18 @@ STATUS = {
 }
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
-PATHS = {"auto": 0, "vector": 1, "matrix": 2}
+PATHS = {"auto": 0, "vector": 1, "matrix": 2, "two_pass": 3}
 
 
 class PrefillOptions(ctypes.Structure):
     """Mirror of kda_prefill_options."""
-    _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32)]
+    _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32),
+                ("block_chunks", ctypes.c_int32)]
 
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
-                    "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill",
-                    "kda_fwd_prefill_ex", "kda_decode_step")
+                    "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill_workspace_bytes_ex",
+                    "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step")
 
 
 class KDAError(RuntimeError):
@@ -79,6 +80,9 @@ def load_library():
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_fwd_prefill_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32]
     lib.kda_fwd_prefill_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_fwd_prefill_workspace_bytes_ex.argtypes = [i64, i32, i32, i32, i32, i32,
+                                                       ctypes.POINTER(PrefillOptions)]
+    lib.kda_fwd_prefill_workspace_bytes_ex.restype = ctypes.c_size_t
     lib.kda_fwd_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
                                     i32, f32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.kda_fwd_prefill.restype = ctypes.c_int
@@ -101,9 +105,18 @@ def status_string(status: int) -> str:
     return load_library().kda_status_string(int(status)).decode()
 
 
+def prefill_options(path="auto", value_tiles=0, block_chunks=0) -> PrefillOptions:
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % sorted(PATHS))
+    return PrefillOptions(PATHS[path], int(value_tiles), int(block_chunks))
+
+
 def prefill_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
-                            dtype: int = DTYPE_BF16) -> int:
-    return int(load_library().kda_fwd_prefill_workspace_bytes(total_T, N, H, d_k, d_v, dtype))
+                            dtype: int = DTYPE_BF16, path="auto", value_tiles=0,
+                            block_chunks=0) -> int:
+    opts = prefill_options(path, value_tiles, block_chunks)
+    return int(load_library().kda_fwd_prefill_workspace_bytes_ex(
+        total_T, N, H, d_k, d_v, dtype, ctypes.byref(opts)))
 
 
 # --------------------------------------------------------------------------
@@ -143,7 +156,8 @@ def _stream(device):
 
 
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
-            out=None, final_state=True, workspace=None, path="auto", value_tiles=0):
+            out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
+            block_chunks=0):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -152,8 +166,8 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     sequence of length T.  Returns (o [T, H, d_v] in the input dtype,
     hT [N, H, d_k, d_v] fp32 or None when final_state is False).
     ``final_state`` may also be a preallocated tensor (it may be h0 itself).
-    ``path`` ("auto", "vector" or "matrix") and ``value_tiles`` (0 = automatic)
-    are the kda_prefill_options tuning knobs.
+    ``path`` ("auto", "vector", "matrix" or "two_pass"), ``value_tiles`` and
+    ``block_chunks`` (0 = automatic) are the kda_prefill_options tuning knobs.
     """
     torch = _torch()
     lib = load_library()
@@ -192,10 +206,10 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     else:
         hT = final_state
         _check(hT, "final_state", (N, H, dk, dv), torch.float32, dev)
-    need = lib.kda_fwd_prefill_workspace_bytes(T, N, H, dk, dv, code)
+    opts = prefill_options(path, value_tiles, block_chunks)
+    need = lib.kda_fwd_prefill_workspace_bytes_ex(T, N, H, dk, dv, code, ctypes.byref(opts))
     if workspace is None:
         workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)
-    opts = PrefillOptions(PATHS[path], int(value_tiles))
     st = lib.kda_fwd_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                 _ptr(h0), _ptr(cu_seqlens), T, N, H, dk, dv, code,
                                 float(scale), _ptr(out), _ptr(hT), _ptr(workspace),

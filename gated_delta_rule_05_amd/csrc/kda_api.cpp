@@ -16,7 +16,11 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
+// the automatic choice takes the two-pass matrix path below this many
+// (sequence, head) pairs: there the fused kernel would split each pair into
+// 4 or more value tiles that all redo the pair's state-independent work
+constexpr int64_t kTwoPassMaxPairs = 128;
 constexpr size_t kWorkspaceAlign = 256;
 
 bool supported_dim(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -79,6 +83,55 @@ int check_sizes(int64_t tokens, int64_t N, int64_t H, int32_t d_k, int32_t d_v, 
 
 size_t plan_bytes(int32_t N) { return round_up(static_cast<size_t>(N) * sizeof(int32_t), kWorkspaceAlign); }
 
+// Sizes-only view of a prefill for the path checks.
+kda::PrefillArgs shape_args(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                            int32_t dtype) {
+    kda::PrefillArgs a{};
+    a.total_T = total_T; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.dtype_f32 = dtype == KDA_DTYPE_F32;
+    return a;
+}
+
+// The kernel path, its tiling and the workspace it needs.
+struct Plan {
+    int32_t path;      // VECTOR, MATRIX or MATRIX_TWO_PASS
+    int R;             // value tiles (matrix paths)
+    int L_b;           // chunks per block (two-pass)
+    size_t ws_bytes;   // scheduling table [+ two-pass slots and state copy]
+};
+
+// Sizes must already have passed check_sizes.
+int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
+            const kda_prefill_options* options, Plan* pl) {
+    const int32_t path = options ? options->path : KDA_PATH_AUTO;
+    const int32_t tiles = options ? options->value_tiles : 0;
+    const int32_t blk = options ? options->block_chunks : 0;
+    if (path < KDA_PATH_AUTO || path > KDA_PATH_MATRIX_TWO_PASS) return KDA_STATUS_INVALID_ARGUMENT;
+    if (tiles < 0 || blk < 0) return KDA_STATUS_INVALID_ARGUMENT;
+    const kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
+    const bool matrix_ok = kda::mfma_supported(a) && kda::wy_supported(a);
+    if ((path == KDA_PATH_MATRIX || path == KDA_PATH_MATRIX_TWO_PASS) && !matrix_ok)
+        return KDA_STATUS_UNSUPPORTED;
+    pl->path = path;
+    if (path == KDA_PATH_AUTO) {
+        pl->path = !matrix_ok ? KDA_PATH_VECTOR
+                   : static_cast<int64_t>(N) * H < kTwoPassMaxPairs ? KDA_PATH_MATRIX_TWO_PASS
+                                                                     : KDA_PATH_MATRIX;
+    }
+    pl->R = 0;
+    pl->L_b = 0;
+    pl->ws_bytes = plan_bytes(N);
+    if (pl->path == KDA_PATH_VECTOR) return KDA_STATUS_OK;
+    if (tiles > 0 && !kda::mfma_tiles_ok(d_v, tiles)) return KDA_STATUS_INVALID_ARGUMENT;
+    pl->R = tiles > 0 ? tiles : kda::mfma_value_tiles(a);
+    if (pl->path == KDA_PATH_MATRIX_TWO_PASS) {
+        pl->L_b = blk > 0 ? blk : kda::wy_default_block_chunks(total_T, N, H, d_v);
+        if (!kda::wy_block_chunks_ok(N, H, pl->L_b)) return KDA_STATUS_INVALID_ARGUMENT;
+        pl->ws_bytes += kda::wy_workspace_bytes(N, H, d_k, d_v, pl->L_b);
+    }
+    return KDA_STATUS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,11 +150,19 @@ const char* kda_status_string(int status) {
     return "unknown status";
 }
 
-size_t kda_fwd_prefill_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k,
-                                       int32_t d_v, int32_t dtype) {
+size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H, int32_t d_k,
+                                          int32_t d_v, int32_t dtype,
+                                          const kda_prefill_options* options) {
     Sizes sz;
     if (check_sizes(total_T, N, H, d_k, d_v, dtype, &sz) != KDA_STATUS_OK) return 0;
-    return plan_bytes(N);
+    Plan pl;
+    if (resolve(total_T, N, H, d_k, d_v, dtype, options, &pl) != KDA_STATUS_OK) return 0;
+    return pl.ws_bytes;
+}
+
+size_t kda_fwd_prefill_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k,
+                                       int32_t d_v, int32_t dtype) {
+    return kda_fwd_prefill_workspace_bytes_ex(total_T, N, H, d_k, d_v, dtype, nullptr);
 }
 
 int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -122,7 +183,10 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_STATUS_MISALIGNED;
     if (!aligned4(beta) || !aligned4(cu_seqlens)) return KDA_STATUS_MISALIGNED;
-    const size_t need = plan_bytes(N);
+    Plan pl;
+    const int rs = resolve(total_T, N, H, d_k, d_v, dtype, options, &pl);
+    if (rs != KDA_STATUS_OK) return rs;
+    const size_t need = pl.ws_bytes;
     if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_STATUS_WORKSPACE_TOO_SMALL;
 
     // outputs may not overlap inputs (hT == h0 exactly is allowed)
@@ -142,34 +206,28 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     if (overlaps(r_o, r_hT) || overlaps(r_o, r_ws) || overlaps(r_hT, r_ws))
         return KDA_STATUS_INVALID_ARGUMENT;
 
-    const int32_t path = options ? options->path : KDA_PATH_AUTO;
-    const int32_t tiles = options ? options->value_tiles : 0;
-    if (path != KDA_PATH_AUTO && path != KDA_PATH_VECTOR && path != KDA_PATH_MATRIX)
-        return KDA_STATUS_INVALID_ARGUMENT;
-
-    kda::PrefillArgs a;
+    kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
     a.order = static_cast<int32_t*>(workspace);
-    a.total_T = total_T; a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
-    a.dtype_f32 = dtype == KDA_DTYPE_F32;
     a.scale = scale;
-    const bool matrix_ok = kda::mfma_supported(a);
-    if (path == KDA_PATH_MATRIX && !matrix_ok) return KDA_STATUS_UNSUPPORTED;
-    const bool use_matrix = path == KDA_PATH_MATRIX || (path == KDA_PATH_AUTO && matrix_ok);
-    int R = 0;
-    if (use_matrix) {
-        if (tiles < 0 || (tiles > 0 && !kda::mfma_tiles_ok(d_v, tiles)))
-            return KDA_STATUS_INVALID_ARGUMENT;
-        R = tiles > 0 ? tiles : kda::mfma_value_tiles(a);
-    } else if (tiles < 0) {
-        return KDA_STATUS_INVALID_ARGUMENT;
-    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (kda::launch_plan(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
-    const hipError_t e = use_matrix ? kda::launch_prefill_mfma(a, R, s)
-                                    : kda::launch_prefill_valu(a, s);
+    hipError_t e = hipSuccess;
+    switch (pl.path) {
+        case KDA_PATH_VECTOR:
+            if (kda::launch_plan(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
+            e = kda::launch_prefill_valu(a, s);
+            break;
+        case KDA_PATH_MATRIX:
+            if (kda::launch_plan(a, s) != hipSuccess) return KDA_STATUS_HIP_ERROR;
+            e = kda::launch_prefill_mfma(a, pl.R, s);
+            break;
+        default:
+            e = kda::launch_prefill_wy(a, pl.R, pl.L_b,
+                                       static_cast<uint8_t*>(workspace) + plan_bytes(N), s);
+            break;
+    }
     return e == hipSuccess ? KDA_STATUS_OK : KDA_STATUS_HIP_ERROR;
 }
 

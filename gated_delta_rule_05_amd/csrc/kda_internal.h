@@ -50,5 +50,13 @@ bool mfma_supported(const PrefillArgs& a);
 int mfma_value_tiles(const PrefillArgs& a);
 bool mfma_tiles_ok(int d_v, int R);
 hipError_t launch_prefill_mfma(const PrefillArgs& a, int R, hipStream_t stream);
+// bf16 two-pass matrix-core path (d_k = 128): a chunk-parallel prep kernel
+// and a serial carry kernel, alternated over blocks of L_b chunks; the
+// workspace holds one block of per-(chunk, head) slots plus a state copy
+bool wy_supported(const PrefillArgs& a);
+int wy_default_block_chunks(int64_t total_T, int32_t N, int32_t H, int32_t d_v);
+bool wy_block_chunks_ok(int32_t N, int32_t H, int L_b);
+size_t wy_workspace_bytes(int32_t N, int32_t H, int32_t d_k, int32_t d_v, int L_b);
+hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hipStream_t stream);
 
 }  // namespace kda

@@ -51,16 +51,11 @@
 // accumulator layout already is the B-operand layout.
 #include "kda_device.h"
 #include "kda_internal.h"
+#include "kda_mfma.h"
 #include "kda_sched.h"
 
 namespace kda {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;        // tokens per chunk
 constexpr int DK = 128;      // key channels
@@ -72,52 +67,6 @@ constexpr int DS = 20;       // bf16 row stride of 16x16 blocks (-A off-diagonal
 constexpr int NSTAGE = 4;    // stager waves, 16 rows of each chunk apiece
 constexpr int kMaxTileColumns = 64;  // one 16-column slab per consumer wave
 constexpr int kMaxHeads = 16384;     // keeps every chunk-relative byte offset in 31 bits
-constexpr int kBufferWord3 = 0x00020000;  // raw buffer resource, gfx9 family
-constexpr float kLog2e = 1.4426950408889634f;
-
-// ---- buffer resources: chunk-relative loads with a hardware range check
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes),
-                                             kBufferWord3);
-}
-__device__ __forceinline__ uint32_t ld32(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-__device__ __forceinline__ u32x2 ld64(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-}
-__device__ __forceinline__ uint16_t ld16(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
-__device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, int off, uint16_t x) {
-    __builtin_amdgcn_raw_buffer_store_b16(x, r, off, 0, 0);
-}
-
-// round-to-nearest-even pack of two fp32 into a bf16 pair (low half = a)
-__device__ __forceinline__ uint32_t pk(float a, float b) {
-    bf16x2_t r;
-    r[0] = static_cast<__bf16>(a);
-    r[1] = static_cast<__bf16>(b);
-    return __builtin_bit_cast(uint32_t, r);
-}
-__device__ __forceinline__ uint16_t bf(float a) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(a));
-}
-__device__ __forceinline__ float lo_bf(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float hi_bf(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ f32x4 mma32(u32x4 a, u32x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma16(u32x2 a, u32x2 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
-                                                     __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
-}
-__device__ __forceinline__ u32x4 pack4(f32x4 lo, f32x4 hi) {
-    return u32x4{pk(lo[0], lo[1]), pk(lo[2], lo[3]), pk(hi[0], hi[1]), pk(hi[2], hi[3])};
-}
-__device__ __forceinline__ u32x2 pack2(f32x4 x) { return u32x2{pk(x[0], x[1]), pk(x[2], x[3])}; }
-__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
 
 // A-operand fragment of a bf16 row with the permuted K order of K-step kk
 __device__ __forceinline__ u32x4 perm_row(const uint16_t* row, int kk, int g) {

@@ -1,0 +1,709 @@
+// prefill_wy.hip -- two-pass chunked KDA prefill on gfx950 matrix cores
+// (bf16 operands, fp32 accumulation, fp32 state), d_k = 128, chunks of 64
+// tokens.  Meant for batches with few (sequence, head) pairs, where the
+// serial walk over chunks, not the total work, sets the time.
+//
+// Per chunk of C = 64 tokens with start state S0 (d_k x d_v, fp32), per key
+// channel c (the chunked form of the per-token recurrence; the pages only
+// say it is evaluated blockwise, with a diagonal-plus-low-rank transition):
+//   g_r  = sum_{s<=r} log_alpha_s,  G = g_last
+//   Kg   = K * e^{g},  Qg = Q * e^{g},  Kn = K * e^{-g},  Kd = K * e^{G-g}
+//   A    = strictly-lower(Diag(beta) Kg Kn^T)
+//   T    = (I + A)^{-1} Diag(beta)          (UT transform of the delta rule)
+//   W    = T Kg,  U = T V,  P = lower(Qg Kn^T)
+//   E    = U - W S0                          the chunk's delta errors
+//   O    = scale (Qg S0 + P E)
+//   S    = Diag(e^{G}) S0 + Kd^T E
+// The factors of the chunked form split at the chunk start, so a row's
+// factors depend only on the gates up to that row: an output never depends,
+// even in rounding, on tokens after it.
+//
+// Pass 1, the prep kernel: one work-group per (chunk, head), all chunks at
+// once.  It computes everything that does not depend on the state -- W, U,
+// Qg, Kd^T, P and e^{G} -- and writes them to a workspace slot already in
+// the MFMA operand layouts (kda_mfma.h) that pass 2 feeds to the matrix
+// cores, so pass 2 copies them without any rearranging.  T comes from the
+// inverses of the 16x16 diagonal blocks of I + A (on MFMA, from (I + N)^{-1}
+// = (I - N)(I + N^2)(I + N^4)(I + N^8) for the nilpotent N = A_II) and a
+// block forward substitution for the blocks below them.
+// Pass 2, the carry kernel: one work-group per (sequence, head, value tile)
+// walks the chunks in order with its fp32 state slabs in registers.  Per
+// chunk it needs three products on the serial path (W S0, then Kd^T E) and
+// one off it (O).  Loader waves copy the next chunk's slot into the other
+// half of a double buffer in LDS, their global loads two chunks ahead.
+// The host alternates the passes over blocks of chunks, so the workspace
+// holds a bounded block of slots (and stays mostly cache-resident) while
+// the state is carried between blocks through hT (or a workspace copy).
+#include <algorithm>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_mfma.h"
+#include "kda_sched.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64;          // tokens per chunk
+constexpr int DK = 128;        // key channels
+constexpr int kMaxHeads = 16384;   // keeps every chunk-relative byte offset in 31 bits
+
+// ---- workspace slot of one (chunk, head), bytes
+constexpr int kFrag = 1024;                 // one MFMA operand: 64 lanes x 16 B
+constexpr int kFragW = 0;                   // W:     [I 4][kk 4] A operands
+constexpr int kFragQ = 16;                  // Qg:    [I 4][kk 4] A operands
+constexpr int kFragK = 32;                  // Kd^T:  [m 8][kk 2] A operands
+constexpr int kFragP = 48;                  // P:     (I,kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+constexpr int kNumFrag = 54;
+constexpr int kOffGam = kNumFrag * kFrag;   // e^{G}: 128 fp32
+constexpr int kOffU = kOffGam + 512;        // U: [slab d_v/16][I 4][64 lanes][4 bf16]
+constexpr int kSlabBytes = 4 * 64 * 8;      // U of one 16-column slab
+__host__ __device__ constexpr int slot_bytes(int dv) { return kOffU + 128 * dv; }
+static_assert(kOffU % 256 == 0, "slots stay 256-byte aligned");
+
+__device__ __forceinline__ int p_frag(int I, int kk) { return I < 2 ? I : 2 * I - 2 + kk; }
+
+// position of index x of a row stored in fragment order: in each 32-wide
+// block, K-step group g reads 8 consecutive entries, x = 4g + j and
+// 16 + 4g + j (j < 4)
+__device__ __forceinline__ int fpos(int x) {
+    const int y = x & 31;
+    return (x & ~31) + 8 * ((y & 15) >> 2) + 4 * (y >> 4) + (y & 3);
+}
+
+// ===================================================================
+// pass 1: prep
+// ===================================================================
+constexpr int PT = 256;        // threads (4 waves)
+constexpr int TS = DK + 8;     // bf16 stride of token rows (272 B: conflict-free 16-byte reads)
+constexpr int CS = C + 8;      // bf16 stride of channel rows (144 B)
+constexpr int BS = 20;         // bf16 stride of 16x16 blocks
+
+struct PrepSmem {
+    uint16_t tok[3][C * TS];   // Kg, Kn, Qg: token rows, channels in fragment order
+    uint16_t kgt[DK * CS];     // Kg: channel rows, tokens in fragment order
+    float scan[16][DK];        // per 4-row group gate sums, then their exclusive prefix
+    float beta[C];
+    float glog[DK];            // G / ln 2
+};
+// after the products the token rows are dead and their space is reused:
+//   tok[0]:        -A strictly-lower blocks | (I + A_II)^{-1} | T (= T Diag(beta) above)
+//   tok[1..2]:     V, channel rows, tokens in fragment order
+constexpr int kAnOff = 0;                  // 6 blocks
+constexpr int kDinvOff = 6 * 16 * BS;      // 4 blocks
+constexpr int kTbOff = 10 * 16 * BS;       // 64 rows x CS
+static_assert(kTbOff + C * CS <= C * TS, "aliases fit in one token array");
+static_assert((kTbOff * 2) % 16 == 0, "16-byte aligned");
+static_assert(DK * CS <= 2 * C * TS, "V fits in two token arrays");
+
+// 16x16 product of two 16-row blocks stored in fragment order:
+// D[m][n] = sum_c X[m][c] Y[n][c]
+__device__ __forceinline__ f32x4 row_product(const uint16_t* x, const uint16_t* y, int g, int ln) {
+    const uint16_t* xr = x + ln * TS + 8 * g;
+    const uint16_t* yr = y + ln * TS + 8 * g;
+    u32x4 xf[4], yf[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        xf[kk] = *reinterpret_cast<const u32x4*>(xr + 32 * kk);
+        yf[kk] = *reinterpret_cast<const u32x4*>(yr + 32 * kk);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mma32(xf[kk], yf[kk], acc);
+    return acc;
+}
+
+// (I + N)^{-1} for N = strictly-lower(Diag(beta) Kg_I Kn_I^T), on MFMA.
+// With Y in the accumulator layout (lane (g, ln) holds Y[4g+i][ln]) passed
+// as the A operand of a 16x16x16 product, the product sees Y^T; keeping
+// both N and N^T lets every factor enter in the layout it is needed in.
+// The result is formed transposed, X^T = (I + N^2^T)(I + N^4^T)(I + N^8^T)
+// (I - N^T), whose accumulator layout is the A-operand layout of X: lane
+// (g, ln) gets X[ln][4g .. 4g+3].
+__device__ __forceinline__ u32x2 diag_inverse(const PrepSmem& sm, int I, int g, int ln) {
+    const uint16_t* kgI = sm.tok[0] + 16 * I * TS;
+    const uint16_t* knI = sm.tok[1] + 16 * I * TS;
+    const f32x4 a = row_product(kgI, knI, g, ln);    // (Kg_I Kn_I^T)[4g+i][ln]
+    const f32x4 at = row_product(knI, kgI, g, ln);   // (Kg_I Kn_I^T)[ln][4g+i]
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta + 16 * I + 4 * g);
+    const float bl = sm.beta[16 * I + ln];
+    f32x4 N, NT, eye;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        N[i] = (r > ln) ? bt[i] * a[i] : 0.f;       // N[r][ln]
+        NT[i] = (ln > r) ? bl * at[i] : 0.f;        // N^T[r][ln] = N[ln][r]
+        eye[i] = (r == ln) ? 1.f : 0.f;
+    }
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    const u32x2 n_b = pack2(N), nt_b = pack2(NT);
+    const f32x4 M2 = mma16(nt_b, n_b, zero);         // N N
+    const f32x4 M2T = mma16(n_b, nt_b, zero);        // N^T N^T
+    const u32x2 m2_b = pack2(M2), m2t_b = pack2(M2T);
+    const f32x4 M4 = mma16(m2t_b, m2_b, zero);
+    const f32x4 M4T = mma16(m2_b, m2t_b, zero);
+    const f32x4 M8 = mma16(pack2(M4T), pack2(M4), zero);
+    const f32x4 Z1 = mma16(pack2(eye + M8), pack2(eye - NT), zero);
+    const f32x4 Z2 = mma16(pack2(eye + M4), pack2(Z1), zero);
+    const f32x4 Z3 = mma16(pack2(eye + M2), pack2(Z2), zero);
+    return pack2(Z3);
+}
+
+// the six strictly-lower 16x16 blocks (I > J), numbered I (I - 1) / 2 + J
+__device__ __forceinline__ int an_index(int I, int J) { return I * (I - 1) / 2 + J; }
+
+// Column J of T = (I + A)^{-1} below the diagonal by block forward
+// substitution, T_IJ = (I + A_II)^{-1} sum_{J<=K<I} (-A_IK) T_KJ, then
+// T Diag(beta) into the fragment-ordered rows of tb.
+template <int J>
+__device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
+    const uint16_t* an = sm.tok[0] + kAnOff;
+    const uint16_t* dinv = sm.tok[0] + kDinvOff;
+    uint16_t* tb = sm.tok[0] + kTbOff;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 col[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)          // T_JJ = (I + A_JJ)^{-1}, accumulator layout
+        col[J][i] = lo_bf(dinv[(16 * J + 4 * g + i) * BS + ln]);
+#pragma unroll
+    for (int I = J + 1; I < 4; ++I) {
+        f32x4 z = zero;
+#pragma unroll
+        for (int K = J; K < I; ++K)
+            z = mma16(*reinterpret_cast<const u32x2*>(an + (an_index(I, K) * 16 + ln) * BS + 4 * g),
+                      pack2(col[K]), z);
+        col[I] = mma16(*reinterpret_cast<const u32x2*>(dinv + (16 * I + ln) * BS + 4 * g),
+                       pack2(z), zero);
+    }
+    const float bj = sm.beta[16 * J + ln];
+    const int cpos = fpos(16 * J + ln);
+#pragma unroll
+    for (int I = J; I < 4; ++I)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tb[(16 * I + 4 * g + i) * CS + cpos] = bf(col[I][i] * bj);
+    // the upper blocks the products of pass 1 read: (0,1) and (2,3)
+    if (J == 1 || J == 3) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tb[(16 * (J - 1) + 4 * g + i) * CS + cpos] = 0;
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(PT, 2)
+void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                            const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
+                            const float* __restrict__ beta, const int32_t* __restrict__ cu,
+                            int H, int DV, int c_lo, int L_b, uint8_t* __restrict__ ws)
+{
+    __shared__ PrepSmem sm;
+    const int slot = blockIdx.x;
+    const int h = slot % H;
+    const int q_ = slot / H;
+    const int n = q_ / L_b;
+    const int m = c_lo + q_ % L_b;
+    const int64_t t_begin = cu[n];
+    const int64_t t_end = cu[n + 1];
+    const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
+    if (c0 >= t_end) return;
+    const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
+    uint8_t* out = ws + static_cast<size_t>(slot) * slot_bytes(DV);
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int ln = lane & 15;
+    const int cg = lane & 15;                  // staging: channels 8cg .. 8cg+7
+    const int rg = 4 * wave + (lane >> 4);     //          rows 4rg .. 4rg+3
+
+    // ---------------- staging loads (rows past the end read zero) ----------
+    const int64_t e0 = (c0 * H + h) * DK;
+    const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
+    const __amdgpu_buffer_rsrc_t rk = rsrc(k + e0, 2u * span);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q + e0, 2u * span);
+    const __amdgpu_buffer_rsrc_t rla = rsrc(log_alpha + e0, 4u * span);
+    const __amdgpu_buffer_rsrc_t rv =
+        rsrc(v + (c0 * H + h) * DV, 2u * static_cast<uint32_t>((len - 1) * H * DV + DV));
+    u32x4 kr[4], qr[4], vr[4];
+    f32x4 la[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        const int off = r * H * DK + 8 * cg;
+        kr[i] = ld128(rk, 2 * off);
+        qr[i] = ld128(rq, 2 * off);
+        la[i][0] = __builtin_bit_cast(f32x4, ld128(rla, 4 * off));
+        la[i][1] = __builtin_bit_cast(f32x4, ld128(rla, 4 * off + 16));
+        vr[i] = (8 * cg < DV) ? ld128(rv, 2 * (r * H * DV + 8 * cg)) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (tid < C) {
+        const __amdgpu_buffer_rsrc_t rb =
+            rsrc(beta + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
+        sm.beta[tid] = __uint_as_float(ld32(rb, 4 * tid * H));
+    }
+
+    // ---------------- cumulative gate (log2 units) ----------------------------
+    float p[4][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run = __builtin_fmaf(la[i][j >> 2][j & 3], kLog2e, run);
+            p[i][j] = run;
+        }
+    }
+    *reinterpret_cast<f32x4*>(&sm.scan[rg][8 * cg]) = f32x4{p[3][0], p[3][1], p[3][2], p[3][3]};
+    *reinterpret_cast<f32x4*>(&sm.scan[rg][8 * cg + 4]) = f32x4{p[3][4], p[3][5], p[3][6], p[3][7]};
+    __syncthreads();
+    if (tid < DK) {
+        float run = 0.f;
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const float t = sm.scan[x][tid];
+            sm.scan[x][tid] = run;
+            run += t;
+        }
+        sm.glog[tid] = run;
+        reinterpret_cast<float*>(out + kOffGam)[tid] = __builtin_amdgcn_exp2f(run);
+    }
+    __syncthreads();
+
+    // ---------------- decay-weighted operands ---------------------------------
+    float off[8], G[8];
+    {
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(&sm.scan[rg][8 * cg]);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&sm.scan[rg][8 * cg + 4]);
+        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.glog[8 * cg]);
+        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.glog[8 * cg + 4]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            off[j] = o0[j]; off[j + 4] = o1[j];
+            G[j] = g0[j]; G[j + 4] = g1[j];
+        }
+    }
+    float kg[4][8], kd[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        float qg[8], kn[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float gl = off[j] + p[i][j];
+            const float u = __builtin_amdgcn_exp2f(gl);
+            const float w = __builtin_amdgcn_exp2f(-gl);
+            const float d = __builtin_amdgcn_exp2f(G[j] - gl);
+            const uint32_t kw = kr[i][j >> 1], qw = qr[i][j >> 1];
+            const float kx = (j & 1) ? hi_bf(kw) : lo_bf(kw);
+            const float qx = (j & 1) ? hi_bf(qw) : lo_bf(qw);
+            kg[i][j] = kx * u;
+            qg[j] = qx * u;
+            kn[j] = kx * w;
+            kd[i][j] = kx * d;
+        }
+#pragma unroll
+        for (int pc = 0; pc < 2; ++pc) {
+            const int x = 8 * cg + 4 * pc;      // first of 4 consecutive channels
+            const int pos = fpos(x);
+            const int b = 4 * pc;
+            *reinterpret_cast<u32x2*>(sm.tok[0] + r * TS + pos) =
+                u32x2{pk(kg[i][b], kg[i][b + 1]), pk(kg[i][b + 2], kg[i][b + 3])};
+            *reinterpret_cast<u32x2*>(sm.tok[1] + r * TS + pos) =
+                u32x2{pk(kn[b], kn[b + 1]), pk(kn[b + 2], kn[b + 3])};
+            const u32x2 qv = u32x2{pk(qg[b], qg[b + 1]), pk(qg[b + 2], qg[b + 3])};
+            *reinterpret_cast<u32x2*>(sm.tok[2] + r * TS + pos) = qv;
+            // Qg as the A operand of pass 2: fragment (I = r/16, kk = x/32),
+            // lane (g = (x%16)/4, r%16), half (x%32)/16
+            const int fl = 16 * ((x & 15) >> 2) + (r & 15);
+            *reinterpret_cast<u32x2*>(out + (kFragQ + 4 * (r >> 4) + (x >> 5)) * kFrag + fl * 16 +
+                                      8 * ((x & 31) >> 4)) = qv;
+        }
+    }
+    {
+        const int x = 4 * rg;                   // first of this thread's 4 tokens
+        const int pos = fpos(x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int c = 8 * cg + j;
+            *reinterpret_cast<u32x2*>(sm.kgt + c * CS + pos) =
+                u32x2{pk(kg[0][j], kg[1][j]), pk(kg[2][j], kg[3][j])};
+            // Kd^T as the A operand of pass 2: fragment (m = c/16, kk = x/32),
+            // lane (g = (x%16)/4, c%16), half (x%32)/16
+            const int fl = 16 * ((x & 15) >> 2) + (c & 15);
+            *reinterpret_cast<u32x2*>(out + (kFragK + 2 * (c >> 4) + (x >> 5)) * kFrag + fl * 16 +
+                                      8 * ((x & 31) >> 4)) =
+                u32x2{pk(kd[0][j], kd[1][j]), pk(kd[2][j], kd[3][j])};
+        }
+    }
+    __syncthreads();
+
+    // ---------------- A and P tiles, diagonal inverses ---------------------------
+    // jobs 0..5: strictly-lower A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
+    // jobs 6..15: lower P blocks (0,0) (1,0) (1,1) (2,0) .. (3,3); wave w takes
+    // jobs w, w+4, w+8, w+12 and the diagonal block I = w
+    const u32x2 dres = diag_inverse(sm, wave, g, ln);
+    f32x4 aval[2];
+    int aidx[2] = {-1, -1};
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+        const int j = wave + 4 * x;
+        if (x < 2 && j < 6) {
+            const int I = j < 1 ? 1 : j < 3 ? 2 : 3;
+            const int J = j - an_index(I, 0);
+            const f32x4 acc = row_product(sm.tok[0] + 16 * I * TS, sm.tok[1] + 16 * J * TS, g, ln);
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta + 16 * I + 4 * g);
+            aval[x] = -bt * acc;
+            aidx[x] = j;
+        } else if (j >= 6) {
+            const int t = j - 6;
+            const int I = (t >= 1) + (t >= 3) + (t >= 6);
+            const int J = t - I * (I + 1) / 2;
+            // P^T block: acc[i] = P[16I + ln][16J + 4g + i]; diagonal blocks keep s <= r
+            const f32x4 acc = row_product(sm.tok[1] + 16 * J * TS, sm.tok[2] + 16 * I * TS, g, ln);
+            u32x2 pv = pack2(acc);
+            if (I == J) {
+                f32x4 mk;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) mk[i] = (4 * g + i <= ln) ? acc[i] : 0.f;
+                pv = pack2(mk);
+            }
+            *reinterpret_cast<u32x2*>(out + (kFragP + p_frag(I, J >> 1)) * kFrag + lane * 16 +
+                                      8 * (J & 1)) = pv;
+        }
+    }
+    if (wave == 0 || wave == 2)   // zero upper halves of the P operands (0,0) and (2,1)
+        *reinterpret_cast<u32x2*>(out + (kFragP + p_frag(wave, wave >> 1)) * kFrag + lane * 16 + 8) =
+            u32x2{0u, 0u};
+    __syncthreads();
+
+    // ---------------- -A blocks, inverses and V into the freed token rows -------
+    {
+        uint16_t* an = sm.tok[0] + kAnOff;
+        uint16_t* dinv = sm.tok[0] + kDinvOff;
+        *reinterpret_cast<u32x2*>(dinv + (16 * wave + ln) * BS + 4 * g) = dres;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            if (aidx[x] < 0) continue;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) an[(aidx[x] * 16 + 4 * g + i) * BS + ln] = bf(aval[x][i]);
+        }
+        if (8 * cg < DV) {
+            uint16_t* vt = sm.tok[1];
+            const int pos = fpos(4 * rg);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int sh = 16 * (j & 1);
+                const uint32_t v0 = (vr[0][j >> 1] >> sh) & 0xffffu, v1 = (vr[1][j >> 1] >> sh) & 0xffffu;
+                const uint32_t v2 = (vr[2][j >> 1] >> sh) & 0xffffu, v3 = (vr[3][j >> 1] >> sh) & 0xffffu;
+                *reinterpret_cast<u32x2*>(vt + (8 * cg + j) * CS + pos) =
+                    u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---------------- T = (I + A)^{-1} Diag(beta), one block column per wave ----
+    if (wave == 0) t_column<0>(sm, g, ln);
+    else if (wave == 1) t_column<1>(sm, g, ln);
+    else if (wave == 2) t_column<2>(sm, g, ln);
+    else t_column<3>(sm, g, ln);
+    __syncthreads();
+
+    // ---------------- W = T Kg (as W^T tiles) and U = T V -----------------------
+    const uint16_t* tb = sm.tok[0] + kTbOff;
+    u32x4 tf[6];                                 // rows 16I + ln of T, K-steps kk <= I/2
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int kk = 0; kk <= (I >> 1); ++kk)
+            tf[p_frag(I, kk)] = *reinterpret_cast<const u32x4*>(tb + (16 * I + ln) * CS + 32 * kk + 8 * g);
+    {
+        // W^T tile (cb, I): lane gets W[16I + ln][16cb + 4g + i]; the two
+        // channel blocks 2w, 2w+1 together form W's A operand (I, kk = w)
+        u32x4 kf[2][2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+                kf[c][kk] = *reinterpret_cast<const u32x4*>(sm.kgt + (16 * (2 * wave + c) + ln) * CS +
+                                                            32 * kk + 8 * g);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 acc[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk <= (I >> 1); ++kk) acc[c] = mma32(kf[c][kk], tf[p_frag(I, kk)], acc[c]);
+            }
+            *reinterpret_cast<u32x4*>(out + (kFragW + 4 * I + wave) * kFrag + lane * 16) =
+                cat(pack2(acc[0]), pack2(acc[1]));
+        }
+    }
+    const uint16_t* vt = sm.tok[1];
+    for (int s = wave; s < DV / 16; s += 4) {
+        u32x4 vf[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            vf[kk] = *reinterpret_cast<const u32x4*>(vt + (16 * s + ln) * CS + 32 * kk + 8 * g);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk <= (I >> 1); ++kk) acc = mma32(tf[p_frag(I, kk)], vf[kk], acc);
+            // accumulator layout: lane gets U[16I + 4g + i][16s + ln]
+            *reinterpret_cast<u32x2*>(out + kOffU + s * kSlabBytes + (I * 64 + lane) * 8) = pack2(acc);
+        }
+    }
+}
+
+// ===================================================================
+// pass 2: carry
+// ===================================================================
+namespace {
+constexpr int CW = 8;              // waves
+constexpr int CT = CW * 64;
+}  // namespace
+
+template <int TV>
+__global__ __launch_bounds__(CT)
+void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __restrict__ h0,
+                             float* __restrict__ hstate, const int32_t* __restrict__ cu,
+                             int64_t groups, int R, int H, int DV, int c_lo, int L_b, float scale,
+                             bf16_t* __restrict__ o)
+{
+    constexpr int NSLAB = TV / 16;           // one 16-column slab per consumer wave
+    constexpr int NC = NSLAB;
+    constexpr int NL = CW - NC;              // loader waves
+    constexpr int NU = (kOffU + kSlabBytes * NSLAB) / 16;   // 16-byte units per chunk
+    constexpr int NPL = (NU + NL * 64 - 1) / (NL * 64);     // units per loader lane
+    static_assert(NC >= 1 && NC <= 4, "tile of 16 to 64 columns");
+    __shared__ u32x4 buf[2][NU];
+
+    int64_t pair;
+    int tile;
+    if (!prefill_map_block(blockIdx.x, groups, R, pair, tile)) return;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int g = lane >> 4;
+    const int ln = lane & 15;
+    const int h = static_cast<int>(pair % H);
+    const int n = static_cast<int>(pair / H);
+    const int64_t t_begin = cu[n];
+    const int64_t t_end = cu[n + 1];
+    const int nch = static_cast<int>((t_end - t_begin + C - 1) / C);
+    const int count = min(nch, c_lo + L_b) - c_lo;   // chunks of this block
+    const int j0 = tile * TV;
+    const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV + j0;
+    const float* s_in = c_lo == 0 ? h0 : hstate;
+
+    if (count <= 0) {
+        // an empty sequence still gets its final state (h0, or zeros)
+        if (c_lo == 0 && nch == 0 && wave < NC) {
+            const int jc = wave * 16 + ln;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int64_t e = sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc;
+                    hstate[e] = h0 ? h0[e] : 0.f;
+                }
+        }
+        return;
+    }
+    auto slot_of = [&](int m) {
+        return ws + static_cast<size_t>((static_cast<int64_t>(n) * L_b + (m - c_lo)) * H + h) *
+                        slot_bytes(DV);
+    };
+
+    if (wave >= NC) {
+        // ======================= loader waves =======================
+        const int ll = (wave - NC) * 64 + lane;
+        const int ubase = tile * NSLAB * kSlabBytes;   // this tile's U slabs within the slot's U
+        auto fetch = [&](u32x4* r, int m) {
+            const uint8_t* s = slot_of(m);
+#pragma unroll
+            for (int x = 0; x < NPL; ++x) {
+                const int u = ll + x * NL * 64;
+                if (u < NU) {
+                    const int byte = 16 * u + (16 * u >= kOffU ? ubase : 0);
+                    r[x] = *reinterpret_cast<const u32x4*>(s + byte);
+                }
+            }
+        };
+        auto put = [&](const u32x4* r, int b) {
+#pragma unroll
+            for (int x = 0; x < NPL; ++x) {
+                const int u = ll + x * NL * 64;
+                if (u < NU) buf[b][u] = r[x];
+            }
+        };
+        u32x4 ra[NPL], rb[NPL];
+        const int m0 = c_lo;
+        fetch(ra, m0);
+        if (count > 1) fetch(rb, m0 + 1);
+        put(ra, 0);
+        if (count > 2) fetch(ra, m0 + 2);
+        __syncthreads();
+        // iteration x: write chunk x+1 (fetched two iterations ago), fetch chunk x+3
+        for (int x = 0; x < count; x += 2) {
+            if (x + 1 < count) {
+                put(rb, 1);
+                if (x + 3 < count) fetch(rb, m0 + x + 3);
+            }
+            __syncthreads();
+            if (x + 1 >= count) break;
+            if (x + 2 < count) {
+                put(ra, 0);
+                if (x + 4 < count) fetch(ra, m0 + x + 4);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
+    // ======================= consumer waves =======================
+    // fp32 state slab in the accumulator layout:
+    // S[m][i] = state[c = 16m + 4g + i][j = wave * 16 + ln]
+    const int jc = wave * 16 + ln;
+    f32x4 S[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            S[m][i] = s_in ? s_in[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] : 0.f;
+    const int vrow = H * DV;
+    __syncthreads();
+    for (int x = 0; x < count; ++x) {
+        const int m = c_lo + x;
+        const u32x4* F = buf[x & 1];
+        const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
+        const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
+
+        u32x4 sb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
+        // E = U - W S0
+        const u32x2* U = reinterpret_cast<const u32x2*>(F + kOffU / 16) + wave * 4 * 64;
+        u32x2 eb[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mma32(F[(kFragW + 4 * I + kk) * 64 + lane], sb[kk], acc);
+            const u32x2 uw = U[I * 64 + lane];
+            const f32x4 e = {lo_bf(uw[0]) - acc[0], hi_bf(uw[0]) - acc[1],
+                             lo_bf(uw[1]) - acc[2], hi_bf(uw[1]) - acc[3]};
+            eb[I] = pack2(e);
+        }
+        const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
+        // S = Diag(e^{G}) S0 + Kd^T E
+        const float* gam = reinterpret_cast<const float*>(F + kOffGam / 16);
+        f32x4 Snew[8];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) {
+            const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
+            Snew[mm] = mma32(F[(kFragK + 2 * mm + 1) * 64 + lane], e23,
+                             mma32(F[(kFragK + 2 * mm) * 64 + lane], e01, gm * S[mm]));
+        }
+        // O = scale (Qg S0 + P E); rows past the end are dropped by the range check
+        const __amdgpu_buffer_rsrc_t ro = rsrc(o + (c0 * H + h) * DV + j0,
+                                               2u * static_cast<uint32_t>((len - 1) * vrow + TV));
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mma32(F[(kFragQ + 4 * I + kk) * 64 + lane], sb[kk], acc);
+            acc = mma32(F[(kFragP + p_frag(I, 0)) * 64 + lane], e01, acc);
+            if (I >= 2) acc = mma32(F[(kFragP + p_frag(I, 1)) * 64 + lane], e23, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * acc[i]));
+        }
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) S[mm] = Snew[mm];
+        __syncthreads();
+    }
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            hstate[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] = S[m][i];
+}
+
+// ===================================================================
+// host side
+// ===================================================================
+namespace {
+constexpr size_t kSlotBudget = size_t{256} << 20;   // default bytes of slots per block
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+int64_t chunk_bound(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) / C : 1; }
+
+template <int TV>
+hipError_t launch_carry_t(const PrefillArgs& a, int R, int c_lo, int L_b, const uint8_t* slots,
+                          float* hstate, hipStream_t stream) {
+    const int64_t groups = static_cast<int64_t>(a.N) * a.H;
+    const int64_t blocks = prefill_grid_blocks(groups, R);
+    hipLaunchKernelGGL((prefill_wy_carry_kernel<TV>), dim3(static_cast<unsigned>(blocks)), dim3(CT),
+                       0, stream, slots, a.h0, hstate, a.cu_seqlens, groups, R, a.H, a.d_v, c_lo,
+                       L_b, a.scale, static_cast<bf16_t*>(a.o));
+    return hipGetLastError();
+}
+}  // namespace
+
+bool wy_supported(const PrefillArgs& a) {
+    return !a.dtype_f32 && a.d_k == DK && a.H <= kMaxHeads;
+}
+
+int wy_default_block_chunks(int64_t total_T, int32_t N, int32_t H, int32_t d_v) {
+    const size_t per_chunk = static_cast<size_t>(N) * H * slot_bytes(d_v);
+    int64_t L = static_cast<int64_t>(kSlotBudget / per_chunk);
+    if (L >= 16) L -= L % 16;
+    L = std::max<int64_t>(1, std::min<int64_t>(L, chunk_bound(total_T)));
+    return static_cast<int>(L);
+}
+
+bool wy_block_chunks_ok(int32_t N, int32_t H, int L_b) {
+    if (L_b < 1) return false;
+    const int64_t slots = static_cast<int64_t>(N) * H * L_b;
+    return slots < (int64_t{1} << 31) && slots <= (int64_t{1} << 40) / slot_bytes(128);
+}
+
+size_t wy_workspace_bytes(int32_t N, int32_t H, int32_t d_k, int32_t d_v, int L_b) {
+    const size_t slots = static_cast<size_t>(N) * H * L_b * slot_bytes(d_v);
+    const size_t state = static_cast<size_t>(N) * H * d_k * d_v * sizeof(float);
+    return align_up(slots) + align_up(state);
+}
+
+hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hipStream_t stream) {
+    uint8_t* slots = static_cast<uint8_t*>(ws);
+    const size_t slot_total = align_up(static_cast<size_t>(a.N) * a.H * L_b * slot_bytes(a.d_v));
+    float* hstate = a.hT ? a.hT : reinterpret_cast<float*>(slots + slot_total);
+    const int64_t bound = chunk_bound(a.total_T);
+    const int TV = a.d_v / R;
+    for (int64_t c_lo = 0; c_lo < bound; c_lo += L_b) {
+        if (a.total_T > 0) {
+            const int64_t nslots = static_cast<int64_t>(a.N) * L_b * a.H;
+            hipLaunchKernelGGL(prefill_wy_prep_kernel, dim3(static_cast<unsigned>(nslots)), dim3(PT),
+                               0, stream, static_cast<const bf16_t*>(a.q),
+                               static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v),
+                               a.log_alpha, a.beta, a.cu_seqlens, a.H, a.d_v,
+                               static_cast<int>(c_lo), L_b, slots);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipError_t e = hipErrorInvalidValue;
+        switch (TV) {
+            case 16: e = launch_carry_t<16>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
+            case 32: e = launch_carry_t<32>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
+            case 64: e = launch_carry_t<64>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
+        }
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kda

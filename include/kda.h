@@ -77,11 +77,21 @@ enum kda_dtype {
 
 /* Which kernel family computes a prefill. */
 enum kda_path {
-    KDA_PATH_AUTO = 0,     /* matrix path when supported, else vector path */
+    KDA_PATH_AUTO = 0,     /* a matrix path when supported (two-pass for
+                              fewer than 128 (sequence, head) pairs, fused
+                              otherwise), else the vector path */
     KDA_PATH_VECTOR = 1,   /* fp32 vector arithmetic, chunks of 32 tokens;
                               any supported dtype and head dimensions */
-    KDA_PATH_MATRIX = 2    /* bf16 matrix cores, fp32 accumulation and
-                              state, chunks of 64 tokens; bf16 and d_k = 128 */
+    KDA_PATH_MATRIX = 2,   /* bf16 matrix cores, fp32 accumulation and
+                              state, chunks of 64 tokens, one fused kernel
+                              per (sequence, head, value tile); bf16 and
+                              d_k = 128 */
+    KDA_PATH_MATRIX_TWO_PASS = 3
+                           /* the same arithmetic in two kernels: a
+                              chunk-parallel pass builds each chunk's
+                              state-independent operands into the
+                              workspace, a serial pass carries the state;
+                              for few long sequences.  bf16, d_k = 128 */
 };
 
 /* Tuning options of kda_fwd_prefill_ex (zero-initialise for defaults). */
@@ -89,10 +99,16 @@ typedef struct kda_prefill_options {
     int32_t path;          /* a kda_path */
     int32_t value_tiles;   /* work-groups per (sequence, head), each owning
                               d_v / value_tiles state columns; 0 = automatic.
-                              Matrix path: a power of two with
+                              Matrix paths: a power of two with
                               16 <= d_v / value_tiles <= 64.  Ignored by the vector
                               path, which always uses 32-column tiles
                               (16 when d_v = 16). */
+    int32_t block_chunks;  /* two-pass path: chunks of every sequence per
+                              pass pair (the workspace holds
+                              N * H * block_chunks chunk slots of
+                              55808 + 128 d_v bytes); 0 = automatic
+                              (about 256 MiB of slots).  Ignored by the
+                              other paths. */
 } kda_prefill_options;
 
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
@@ -102,12 +118,18 @@ int kda_abi_version(void);
 const char *kda_status_string(int status);
 
 /*
- * Bytes of device workspace kda_fwd_prefill needs for these sizes (the
- * sequence scheduling table).  Pure host arithmetic; returns 0 for
- * arguments kda_fwd_prefill would reject.
+ * Bytes of device workspace kda_fwd_prefill needs for these sizes: the
+ * sequence scheduling table, plus, when the two-pass path is chosen, one
+ * block of per-(chunk, head) operand slots and a copy of the states.  Pure
+ * host arithmetic; returns 0 for arguments kda_fwd_prefill would reject.
  */
 size_t kda_fwd_prefill_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
                                        int32_t d_k, int32_t d_v, int32_t dtype);
+
+/* The same for kda_fwd_prefill_ex with these options (NULL = defaults). */
+size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H,
+                                          int32_t d_k, int32_t d_v, int32_t dtype,
+                                          const kda_prefill_options *options);
 
 /*
  * Chunked prefill over a packed batch of N sequences.
@@ -148,11 +170,16 @@ int kda_fwd_prefill(const void *q, const void *k, const void *v,
 /*
  * kda_fwd_prefill with explicit tuning options (NULL = defaults).  Same
  * arguments, results and requirements as kda_fwd_prefill, plus:
- *   options->path not a kda_path, or value_tiles invalid for the chosen path
- *     [INVALID_ARGUMENT];
- *   KDA_PATH_MATRIX requested for fp32 inputs or d_k != 128 [UNSUPPORTED].
- * Both paths compute the same chunked form of the recurrence with different
- * chunk lengths and precisions; results agree to the precision bound above.
+ *   options->path not a kda_path, value_tiles invalid for the chosen path,
+ *     or block_chunks negative or too large [INVALID_ARGUMENT];
+ *   a matrix path requested for fp32 inputs or d_k != 128 [UNSUPPORTED];
+ *   workspace_bytes below kda_fwd_prefill_workspace_bytes_ex(..., options)
+ *     [WORKSPACE_TOO_SMALL].
+ * Every path computes the same chunked form of the recurrence with its own
+ * chunk length and precision; results agree to the precision bound above.
+ * The two matrix paths round their operands the same way but sum in
+ * different orders, so they agree to that bound, not bitwise; two-pass
+ * results do not depend on block_chunks (the state crosses blocks in fp32).
  */
 int kda_fwd_prefill_ex(const void *q, const void *k, const void *v,
                        const float *log_alpha, const float *beta,

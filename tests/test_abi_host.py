@@ -37,17 +37,37 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 2
+    assert kda.abi_version() == 3
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
 
 
+def two_pass_bytes(N, H, dk, dv, block):
+    """Two-pass workspace as include/kda.h states it: the scheduling table,
+    N*H*block chunk slots of 55808 + 128 d_v bytes and one fp32 state copy
+    (each 256-byte aligned)."""
+    up = lambda x: (x + 255) // 256 * 256
+    return up(4 * N) + up(N * H * block * (55808 + 128 * dv)) + up(N * H * dk * dv * 4)
+
+
 def test_workspace_query():
-    assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128) == 256
+    # 1600 pairs: fused matrix path, just the scheduling table
     assert kda.prefill_workspace_bytes(1000, 100, 16, 128, 128) == 512
+    # fp32: vector path
+    assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128, kda.DTYPE_F32) == 256
+    # 64 pairs: two-pass path; the automatic block covers the 16 chunks of 1000 tokens
+    assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128) == two_pass_bytes(4, 16, 128, 128, 16)
+    assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128, path="matrix") == 256
+    assert (kda.prefill_workspace_bytes(1000, 4, 16, 128, 64, path="two_pass", block_chunks=3)
+            == two_pass_bytes(4, 16, 128, 64, 3))
+    # a long sequence: blocks capped near 256 MiB of slots, in multiples of 16 chunks
+    big = kda.prefill_workspace_bytes(1 << 20, 1, 32, 128, 128)
+    assert big == two_pass_bytes(1, 32, 128, 128, 112)
     assert kda.prefill_workspace_bytes(1000, 0, 16, 128, 128) == 0      # rejected
     assert kda.prefill_workspace_bytes(1000, 4, 16, 96, 128) == 0       # unsupported
+    assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128, path="two_pass",
+                                       block_chunks=-1) == 0
 
 
 # fake, well-aligned, non-overlapping "device" addresses; never dereferenced
@@ -62,7 +82,7 @@ def addr(i, off=0):
 def prefill_call(**over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
-                o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
+                o=addr(6), hT=addr(7), ws=addr(8), wsb=1 << 34, stream=None)
     args.update(over)
     lib = kda.load_library()
     return lib.kda_fwd_prefill(args["q"], args["k"], args["v"], args["la"], args["beta"],
@@ -133,12 +153,12 @@ def test_binding_rejects_cpu_tensors():
         kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
 
 
-def prefill_ex_call(path, tiles, **over):
+def prefill_ex_call(path, tiles, blk=0, **over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
                 o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
     args.update(over)
-    opts = kda.PrefillOptions(path, tiles)
+    opts = kda.PrefillOptions(path, tiles, blk)
     lib = kda.load_library()
     return lib.kda_fwd_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
                                   args["h0"], args["cu"], args["T"], args["N"], args["H"],
@@ -147,16 +167,22 @@ def prefill_ex_call(path, tiles, **over):
                                   ctypes.byref(opts), args["stream"])
 
 
-@pytest.mark.parametrize("path,tiles,over,status", [
-    (3, 0, {}, INVALID), (-1, 0, {}, INVALID),
-    (2, 3, {}, INVALID), (2, 16, {}, INVALID), (2, -2, {}, INVALID),
-    (2, 4, dict(dv=32), INVALID),                 # 8 columns per tile
-    (2, 1, {}, INVALID),                          # 128 columns per tile
-    (2, 0, dict(dtype=1), UNSUPPORTED),           # matrix path needs bf16
-    (2, 0, dict(dk=64), UNSUPPORTED),             # matrix path needs d_k = 128
-    (1, -1, {}, INVALID),
-    (2, 8, dict(N=0), INVALID),                   # ordinary checks still apply
-    (1, 0, dict(q=addr(0, 4)), MISALIGNED),
+@pytest.mark.parametrize("path,tiles,blk,over,status", [
+    (4, 0, 0, {}, INVALID), (-1, 0, 0, {}, INVALID),
+    (3, 3, 0, {}, INVALID), (3, 1, 0, {}, INVALID),       # two-pass tiles as for the matrix path
+    (3, 0, -1, {}, INVALID), (3, 0, 1 << 30, {}, INVALID),  # block_chunks
+    (3, 0, 0, dict(dtype=1), UNSUPPORTED), (3, 0, 0, dict(dk=32), UNSUPPORTED),
+    (3, 0, 0, {}, WS_SMALL), (0, 0, 0, {}, WS_SMALL),   # 8 pairs: auto is two-pass
+    (3, 0, 5, dict(wsb=two_pass_bytes(2, 4, 128, 128, 5) - 1), WS_SMALL),
+    (2, 3, 0, {}, INVALID), (2, 16, 0, {}, INVALID), (2, -2, 0, {}, INVALID),
+    (2, 4, 0, dict(dv=32), INVALID),              # 8 columns per tile
+    (2, 1, 0, {}, INVALID),                       # 128 columns per tile
+    (2, 0, 0, dict(dtype=1), UNSUPPORTED),        # matrix path needs bf16
+    (2, 0, 0, dict(dk=64), UNSUPPORTED),          # matrix path needs d_k = 128
+    (1, -1, 0, {}, INVALID),
+    (2, 8, 0, dict(N=0), INVALID),                # ordinary checks still apply
+    (1, 0, 0, dict(q=addr(0, 4)), MISALIGNED),
+    (3, 0, 2, dict(o=addr(2), wsb=1 << 34), INVALID),   # aliasing is checked after the workspace
 ])
-def test_prefill_ex_option_checks(path, tiles, over, status):
-    assert prefill_ex_call(path, tiles, **over) == status
+def test_prefill_ex_option_checks(path, tiles, blk, over, status):
+    assert prefill_ex_call(path, tiles, blk, **over) == status
