@@ -122,9 +122,11 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     pl->L_b = 0;
     pl->ws_bytes = plan_bytes(N);
     if (pl->path == KDA_PATH_VECTOR) return KDA_STATUS_OK;
-    if (tiles > 0 && !kda::mfma_tiles_ok(d_v, tiles)) return KDA_STATUS_INVALID_ARGUMENT;
-    pl->R = tiles > 0 ? tiles : kda::mfma_value_tiles(a);
-    if (pl->path == KDA_PATH_MATRIX_TWO_PASS) {
+    const bool two = pl->path == KDA_PATH_MATRIX_TWO_PASS;
+    if (tiles > 0 && !(two ? kda::wy_tiles_ok(d_v, tiles) : kda::mfma_tiles_ok(d_v, tiles)))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    pl->R = tiles > 0 ? tiles : two ? kda::wy_value_tiles(a) : kda::mfma_value_tiles(a);
+    if (two) {
         pl->L_b = blk > 0 ? blk : kda::wy_default_block_chunks(total_T, N, H, d_v);
         if (!kda::wy_block_chunks_ok(N, H, pl->L_b)) return KDA_STATUS_INVALID_ARGUMENT;
         pl->ws_bytes += kda::wy_workspace_bytes(N, H, d_k, d_v, pl->L_b);

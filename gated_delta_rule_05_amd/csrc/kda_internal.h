@@ -54,6 +54,8 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int R, hipStream_t stream);
 // and a serial carry kernel, alternated over blocks of L_b chunks; the
 // workspace holds one block of per-(chunk, head) slots plus a state copy
 bool wy_supported(const PrefillArgs& a);
+int wy_value_tiles(const PrefillArgs& a);
+bool wy_tiles_ok(int d_v, int R);
 int wy_default_block_chunks(int64_t total_T, int32_t N, int32_t H, int32_t d_v);
 bool wy_block_chunks_ok(int32_t N, int32_t H, int L_b);
 size_t wy_workspace_bytes(int32_t N, int32_t H, int32_t d_k, int32_t d_v, int L_b);

@@ -30,7 +30,7 @@
 // walks the chunks in order with its fp32 state slabs in registers.  Per
 // chunk it needs three products on the serial path (W S0, then Kd^T E) and
 // one off it (O).  Loader waves copy the next chunk's slot into the other
-// half of a double buffer in LDS, their global loads two chunks ahead.
+// half of a double buffer in LDS, their global loads four chunks ahead.
 // The host alternates the passes over blocks of chunks, so the workspace
 // holds a bounded block of slots (and stays mostly cache-resident) while
 // the state is carried between blocks through hT (or a workspace copy).
@@ -464,6 +464,8 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
 namespace {
 constexpr int CW = 8;              // waves
 constexpr int CT = CW * 64;
+constexpr int kRotDiv = 8;         // copy-order offsets of the value tiles
+constexpr int kMaxTwoPassTile = 32;   // columns per tile (register budget of the loaders)
 }  // namespace
 
 template <int TV>
@@ -478,7 +480,7 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
     constexpr int NL = CW - NC;              // loader waves
     constexpr int NU = (kOffU + kSlabBytes * NSLAB) / 16;   // 16-byte units per chunk
     constexpr int NPL = (NU + NL * 64 - 1) / (NL * 64);     // units per loader lane
-    static_assert(NC >= 1 && NC <= 4, "tile of 16 to 64 columns");
+    static_assert(TV >= 16 && TV <= kMaxTwoPassTile, "tile of 16 or 32 columns");
     __shared__ u32x4 buf[2][NU];
 
     int64_t pair;
@@ -522,43 +524,58 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
         // ======================= loader waves =======================
         const int ll = (wave - NC) * 64 + lane;
         const int ubase = tile * NSLAB * kSlabBytes;   // this tile's U slabs within the slot's U
+        // Every load is unconditional (indices clamped to valid data), so the
+        // wait before a store to LDS only covers the loads it needs while the
+        // later chunks' loads stay in flight.
+        // The R tiles of a pair copy the same slot at the same time; each
+        // starts at a different offset so they spread over the L2 channels.
+        const int rot = (tile * (NU / kRotDiv)) % NU;
+        auto unit = [&](int u) { return u + rot < NU ? u + rot : u + rot - NU; };
         auto fetch = [&](u32x4* r, int m) {
-            const uint8_t* s = slot_of(m);
+            const uint8_t* s = slot_of(min(m, c_lo + count - 1));
 #pragma unroll
             for (int x = 0; x < NPL; ++x) {
-                const int u = ll + x * NL * 64;
-                if (u < NU) {
-                    const int byte = 16 * u + (16 * u >= kOffU ? ubase : 0);
-                    r[x] = *reinterpret_cast<const u32x4*>(s + byte);
-                }
+                const int u = unit(min(ll + x * NL * 64, NU - 1));
+                const int byte = 16 * u + (16 * u >= kOffU ? ubase : 0);
+                r[x] = *reinterpret_cast<const u32x4*>(s + byte);
             }
         };
         auto put = [&](const u32x4* r, int b) {
 #pragma unroll
             for (int x = 0; x < NPL; ++x) {
                 const int u = ll + x * NL * 64;
-                if (u < NU) buf[b][u] = r[x];
+                if (u < NU) buf[b][unit(u)] = r[x];
             }
         };
-        u32x4 ra[NPL], rb[NPL];
+        // four register sets: chunk j lives in set j % 4 from its fetch until
+        // its store, four iterations later
+        u32x4 r0[NPL], r1[NPL], r2[NPL], r3[NPL];
         const int m0 = c_lo;
-        fetch(ra, m0);
-        if (count > 1) fetch(rb, m0 + 1);
-        put(ra, 0);
-        if (count > 2) fetch(ra, m0 + 2);
+        fetch(r0, m0);
+        fetch(r1, m0 + 1);
+        fetch(r2, m0 + 2);
+        fetch(r3, m0 + 3);
+        put(r0, 0);
+        fetch(r0, m0 + 4);
         __syncthreads();
-        // iteration x: write chunk x+1 (fetched two iterations ago), fetch chunk x+3
-        for (int x = 0; x < count; x += 2) {
-            if (x + 1 < count) {
-                put(rb, 1);
-                if (x + 3 < count) fetch(rb, m0 + x + 3);
-            }
+        // iteration x: store chunk x+1 into the buffer the consumers do not
+        // read and fetch chunk x+5 into the same set; past the last chunk
+        // the stores go to the idle buffer and are never read
+        for (int x = 0; x < count; x += 4) {
+            put(r1, 1);
+            fetch(r1, m0 + x + 5);
             __syncthreads();
             if (x + 1 >= count) break;
-            if (x + 2 < count) {
-                put(ra, 0);
-                if (x + 4 < count) fetch(ra, m0 + x + 4);
-            }
+            put(r2, 0);
+            fetch(r2, m0 + x + 6);
+            __syncthreads();
+            if (x + 2 >= count) break;
+            put(r3, 1);
+            fetch(r3, m0 + x + 7);
+            __syncthreads();
+            if (x + 3 >= count) break;
+            put(r0, 0);
+            fetch(r0, m0 + x + 8);
             __syncthreads();
         }
         return;
@@ -582,48 +599,77 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
         const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
         const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
 
+        // Each stage's LDS fragments are read one stage ahead (scheduling
+        // barriers keep the order), so their latency hides behind the
+        // previous stage's products; independent accumulators interleave.
+        const u32x2* U = reinterpret_cast<const u32x2*>(F + kOffU / 16) + wave * 4 * 64;
+        const float* gam = reinterpret_cast<const float*>(F + kOffGam / 16);
+        u32x4 wf[16];
+        u32x2 uw[4];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) wf[f] = F[(kFragW + f) * 64 + lane];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) uw[I] = U[I * 64 + lane];
         u32x4 sb[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
-        // E = U - W S0
-        const u32x2* U = reinterpret_cast<const u32x2*>(F + kOffU / 16) + wave * 4 * 64;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- E = U - W S0 (reads of Kd^T and e^{G} in flight)
+        u32x4 kf[16];
+        f32x4 gm[8];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK + f) * 64 + lane];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
+        f32x4 y[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) y[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) y[I] = mma32(wf[4 * I + kk], sb[kk], y[I]);
         u32x2 eb[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mma32(F[(kFragW + 4 * I + kk) * 64 + lane], sb[kk], acc);
-            const u32x2 uw = U[I * 64 + lane];
-            const f32x4 e = {lo_bf(uw[0]) - acc[0], hi_bf(uw[0]) - acc[1],
-                             lo_bf(uw[1]) - acc[2], hi_bf(uw[1]) - acc[3]};
+            const f32x4 e = {lo_bf(uw[I][0]) - y[I][0], hi_bf(uw[I][0]) - y[I][1],
+                             lo_bf(uw[I][1]) - y[I][2], hi_bf(uw[I][1]) - y[I][3]};
             eb[I] = pack2(e);
         }
         const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
-        // S = Diag(e^{G}) S0 + Kd^T E
-        const float* gam = reinterpret_cast<const float*>(F + kOffGam / 16);
-        f32x4 Snew[8];
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- S = Diag(e^{G}) S0 + Kd^T E (reads of Qg and P in flight)
+        u32x4 qf[16], pf[6];
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-            const f32x4 gm = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
-            Snew[mm] = mma32(F[(kFragK + 2 * mm + 1) * 64 + lane], e23,
-                             mma32(F[(kFragK + 2 * mm) * 64 + lane], e01, gm * S[mm]));
-        }
-        // O = scale (Qg S0 + P E); rows past the end are dropped by the range check
+        for (int f = 0; f < 16; ++f) qf[f] = F[(kFragQ + f) * 64 + lane];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) pf[f] = F[(kFragP + f) * 64 + lane];
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm], e01, gm[mm] * S[mm]);
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm + 1], e23, S[mm]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- O = scale (Qg S0 + P E); rows past the end are dropped by the range check
         const __amdgpu_buffer_rsrc_t ro = rsrc(o + (c0 * H + h) * DV + j0,
                                                2u * static_cast<uint32_t>((len - 1) * vrow + TV));
+        f32x4 oc[4];
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int I = 0; I < 4; ++I) oc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mma32(F[(kFragQ + 4 * I + kk) * 64 + lane], sb[kk], acc);
-            acc = mma32(F[(kFragP + p_frag(I, 0)) * 64 + lane], e01, acc);
-            if (I >= 2) acc = mma32(F[(kFragP + p_frag(I, 1)) * 64 + lane], e23, acc);
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int I = 0; I < 4; ++I) oc[I] = mma32(qf[4 * I + kk], sb[kk], oc[I]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) oc[I] = mma32(pf[p_frag(I, 0)], e01, oc[I]);
+        oc[2] = mma32(pf[p_frag(2, 1)], e23, oc[2]);
+        oc[3] = mma32(pf[p_frag(3, 1)], e23, oc[3]);
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * acc[i]));
-        }
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) S[mm] = Snew[mm];
+                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * oc[I][i]));
         __syncthreads();
     }
 #pragma unroll
@@ -637,7 +683,9 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
 // host side
 // ===================================================================
 namespace {
-constexpr size_t kSlotBudget = size_t{256} << 20;   // default bytes of slots per block
+// default bytes of slots per block: small enough that a block's slots stay
+// resident in the 256 MiB last-level cache between the two passes
+constexpr size_t kSlotBudget = size_t{150} << 20;
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t chunk_bound(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) / C : 1; }
@@ -656,6 +704,20 @@ hipError_t launch_carry_t(const PrefillArgs& a, int R, int c_lo, int L_b, const 
 
 bool wy_supported(const PrefillArgs& a) {
     return !a.dtype_f32 && a.d_k == DK && a.H <= kMaxHeads;
+}
+
+// Value tiles per (sequence, head): 16 or 32 columns, and enough
+// work-groups to cover the 256 compute units where the batch allows.
+int wy_value_tiles(const PrefillArgs& a) {
+    const int64_t groups = static_cast<int64_t>(a.N) * a.H;
+    int R = a.d_v > kMaxTwoPassTile ? a.d_v / kMaxTwoPassTile : 1;
+    while (R < a.d_v / 16 && groups * R < 256) R *= 2;
+    return R;
+}
+
+bool wy_tiles_ok(int d_v, int R) {
+    return R > 0 && (R & (R - 1)) == 0 && d_v % R == 0 && d_v / R >= 16 &&
+           d_v / R <= kMaxTwoPassTile;
 }
 
 int wy_default_block_chunks(int64_t total_T, int32_t N, int32_t H, int32_t d_v) {
@@ -699,7 +761,6 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hip
         switch (TV) {
             case 16: e = launch_carry_t<16>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
             case 32: e = launch_carry_t<32>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
-            case 64: e = launch_carry_t<64>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
         }
         if (e != hipSuccess) return e;
     }

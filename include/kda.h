@@ -99,15 +99,16 @@ typedef struct kda_prefill_options {
     int32_t path;          /* a kda_path */
     int32_t value_tiles;   /* work-groups per (sequence, head), each owning
                               d_v / value_tiles state columns; 0 = automatic.
-                              Matrix paths: a power of two with
-                              16 <= d_v / value_tiles <= 64.  Ignored by the vector
+                              A power of two with 16 <= d_v / value_tiles
+                              <= 64 (fused matrix path) or <= 32 (two-pass
+                              path).  Ignored by the vector
                               path, which always uses 32-column tiles
                               (16 when d_v = 16). */
     int32_t block_chunks;  /* two-pass path: chunks of every sequence per
                               pass pair (the workspace holds
                               N * H * block_chunks chunk slots of
                               55808 + 128 d_v bytes); 0 = automatic
-                              (about 256 MiB of slots).  Ignored by the
+                              (about 150 MiB of slots).  Ignored by the
                               other paths. */
 } kda_prefill_options;
 

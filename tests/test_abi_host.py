@@ -61,9 +61,9 @@ def test_workspace_query():
     assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128, path="matrix") == 256
     assert (kda.prefill_workspace_bytes(1000, 4, 16, 128, 64, path="two_pass", block_chunks=3)
             == two_pass_bytes(4, 16, 128, 64, 3))
-    # a long sequence: blocks capped near 256 MiB of slots, in multiples of 16 chunks
+    # a long sequence: blocks capped near 150 MiB of slots, in multiples of 16 chunks
     big = kda.prefill_workspace_bytes(1 << 20, 1, 32, 128, 128)
-    assert big == two_pass_bytes(1, 32, 128, 128, 112)
+    assert big == two_pass_bytes(1, 32, 128, 128, 64)
     assert kda.prefill_workspace_bytes(1000, 0, 16, 128, 128) == 0      # rejected
     assert kda.prefill_workspace_bytes(1000, 4, 16, 96, 128) == 0       # unsupported
     assert kda.prefill_workspace_bytes(1000, 4, 16, 128, 128, path="two_pass",
@@ -169,7 +169,8 @@ def prefill_ex_call(path, tiles, blk=0, **over):
 
 @pytest.mark.parametrize("path,tiles,blk,over,status", [
     (4, 0, 0, {}, INVALID), (-1, 0, 0, {}, INVALID),
-    (3, 3, 0, {}, INVALID), (3, 1, 0, {}, INVALID),       # two-pass tiles as for the matrix path
+    (3, 3, 0, {}, INVALID), (3, 1, 0, {}, INVALID),       # two-pass tiles: 16 or 32 columns
+    (3, 2, 0, {}, INVALID), (3, 2, 0, dict(dv=64), WS_SMALL),
     (3, 0, -1, {}, INVALID), (3, 0, 1 << 30, {}, INVALID),  # block_chunks
     (3, 0, 0, dict(dtype=1), UNSUPPORTED), (3, 0, 0, dict(dk=32), UNSUPPORTED),
     (3, 0, 0, {}, WS_SMALL), (0, 0, 0, {}, WS_SMALL),   # 8 pairs: auto is two-pass
