@@ -13,95 +13,137 @@
 // state, is what lets the kernel touch S once: one 128-bit load and one
 // 128-bit store per 4 state elements.
 //
-// Mapping: one work-group per head state.  Each wave owns CW = min(d_v, 32)
-// whole columns of the state; a lane holds 4 adjacent columns of every
-// (64 / (CW/4))-th row, so a wave instruction covers full 128-byte rows
-// segments, and both reductions over d_k finish inside the wave with
-// cross-lane shuffles (no LDS, no barrier).
+// Mapping: a persistent grid of work-groups, each walking head states
+// g, g + G, g + 2G, ...; NWV waves per work-group, each owning whole rows
+// (key channels) of the state: a lane holds 4 adjacent columns of every
+// (256 / d_v)-th row of its wave's rows, so each wave instruction reads or
+// writes whole 512-byte rows (contiguous 1 KB at d_v = 128) with
+// non-temporal 128-bit accesses.  While a work-group reduces and writes
+// back one head, the loads of its next head are already in flight, so the
+// state streams without a gap between reading and writing.  The column
+// reductions over d_k finish with cross-lane shuffles inside each wave and
+// one exchange of the per-wave partial sums through LDS (double-buffered,
+// so one barrier per head).
+#include <algorithm>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
 namespace kda {
 
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int LPR = DV / 4;                       // lanes sharing one row
+    static constexpr int RPI = 64 / LPR;                     // rows per wave instruction
+    static constexpr int PER = 16;                           // rows per lane (at most)
+    static constexpr int NWV = DK / RPI > PER ? DK / RPI / PER : 1;   // waves
+    static constexpr int ITERS = DK / (NWV * RPI);           // rows per lane
+    static_assert(ITERS >= 1 && ITERS * NWV * RPI == DK, "rows split evenly");
+};
+
+constexpr int kDecodeGrid = 256;   // persistent work-groups (one per compute unit)
+
 template <typename T, int DK, int DV>
-__global__ __launch_bounds__((DV < 32 ? 1 : DV / 32) * 64)
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NWV * 64))
 void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                         const T* __restrict__ v, const float* __restrict__ log_alpha,
                         const float* __restrict__ beta, float* __restrict__ S,
-                        T* __restrict__ o, float scale)
+                        T* __restrict__ o, float scale, int64_t nheads)
 {
-    constexpr int CW = DV < 32 ? DV : 32;   // state columns per wave
-    constexpr int LPR = CW / 4;             // lanes sharing one row
-    constexpr int RPI = 64 / LPR;           // rows covered per wave instruction
-    constexpr int ITERS = DK / RPI;         // rows per lane
-    static_assert(DK % RPI == 0, "d_k must be a multiple of the rows per instruction");
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NWV = Sh::NWV, ITERS = Sh::ITERS;
+    __shared__ f32x4 red[2][NWV][2][LPR];   // per-wave column partials of S~^T k and S~^T q
+    __shared__ float red_kq[2][NWV];
 
-    const int64_t nh = blockIdx.x;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int col = wave * CW + (lane % LPR) * 4;
-    const int row0 = lane / LPR;
+    const int cl = lane % LPR;                // 4 columns: 4cl .. 4cl+3
+    const int row0 = wave * (ITERS * RPI) + lane / LPR;
+    auto state = [&](int64_t nh, int it) { return S + nh * (DK * DV) + (row0 + it * RPI) * DV + 4 * cl; };
 
-    float* Sp = S + nh * (DK * DV);
-    const T* qp = q + nh * DK;
-    const T* kp = k + nh * DK;
-    const float* lap = log_alpha + nh * DK;
+    int64_t nh = blockIdx.x;
+    if (nh >= nheads) return;
+    f32x4 s[ITERS], sn[ITERS];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) s[it] = load_stream4(state(nh, it));
+    for (int par = 0; nh < nheads; nh += gridDim.x, par ^= 1) {
+        // next head's state (this head again past the end: same data, never stored)
+        const int64_t nn = nh + gridDim.x < nheads ? nh + gridDim.x : nh;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) sn[it] = load_stream4(state(nn, it));
 
-    f32x4 s[ITERS];
+        const T* qp = q + nh * DK;
+        const T* kp = k + nh * DK;
+        const float* lap = log_alpha + nh * DK;
+        f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
+        float kq = 0.f;
+        float kr[ITERS];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) s[it] = load_stream4(Sp + (row0 + it * RPI) * DV + col);
-
-    float rk0 = 0.f, rk1 = 0.f, rk2 = 0.f, rk3 = 0.f;
-    float rq0 = 0.f, rq1 = 0.f, rq2 = 0.f, rq3 = 0.f;
-    float kq = 0.f;
-    float kr[ITERS];
+        for (int it = 0; it < ITERS; ++it) {
+            const int r = row0 + it * RPI;
+            const float a = gate_exp(lap[r]);
+            const float kv = elem<T>::load(kp + r);
+            const float qv = elem<T>::load(qp + r);
+            kr[it] = kv;
+            kq += kv * qv;
+            s[it] *= a;
+            rk += kv * s[it];
+            rq += qv * s[it];
+        }
+        // sum over the lanes of this wave that hold other rows of the same columns
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        const int r = row0 + it * RPI;
-        const float a = gate_exp(lap[r]);
-        const float kv = elem<T>::load(kp + r);
-        const float qv = elem<T>::load(qp + r);
-        kr[it] = kv;
-        kq += kv * qv;
-        s[it].x *= a; s[it].y *= a; s[it].z *= a; s[it].w *= a;
-        rk0 += kv * s[it].x; rk1 += kv * s[it].y; rk2 += kv * s[it].z; rk3 += kv * s[it].w;
-        rq0 += qv * s[it].x; rq1 += qv * s[it].y; rq2 += qv * s[it].z; rq3 += qv * s[it].w;
-    }
-    // sum over the lanes that hold the other rows of the same columns
+        for (int m = LPR; m < 64; m <<= 1) {
 #pragma unroll
-    for (int m = LPR; m < 64; m <<= 1) {
-        rk0 += __shfl_xor(rk0, m); rk1 += __shfl_xor(rk1, m);
-        rk2 += __shfl_xor(rk2, m); rk3 += __shfl_xor(rk3, m);
-        rq0 += __shfl_xor(rq0, m); rq1 += __shfl_xor(rq1, m);
-        rq2 += __shfl_xor(rq2, m); rq3 += __shfl_xor(rq3, m);
-        kq += __shfl_xor(kq, m);
-    }
-    const float b = beta[nh];
-    const float4 vv = elem<T>::load4(v + nh * DV + col);
-    const float e0 = b * (vv.x - rk0), e1 = b * (vv.y - rk1);
-    const float e2 = b * (vv.z - rk2), e3 = b * (vv.w - rk3);
-    if (row0 == 0) {
-        elem<T>::store4(o + nh * DV + col,
-                        make_float4(scale * (rq0 + e0 * kq), scale * (rq1 + e1 * kq),
-                                    scale * (rq2 + e2 * kq), scale * (rq3 + e3 * kq)));
-    }
+            for (int c = 0; c < 4; ++c) {
+                rk[c] += __shfl_xor(rk[c], m);
+                rq[c] += __shfl_xor(rq[c], m);
+            }
+            kq += __shfl_xor(kq, m);
+        }
+        if (NWV > 1) {
+            // ... and over the waves
+            if (lane < LPR) {
+                red[par][wave][0][cl] = rk;
+                red[par][wave][1][cl] = rq;
+                if (lane == 0) red_kq[par][wave] = kq;
+            }
+            __syncthreads();
+            rk = red[par][0][0][cl];
+            rq = red[par][0][1][cl];
+            kq = red_kq[par][0];
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-        f32x4 x = s[it];
-        x.x += kr[it] * e0; x.y += kr[it] * e1; x.z += kr[it] * e2; x.w += kr[it] * e3;
-        store_stream4(Sp + (row0 + it * RPI) * DV + col, x);
+            for (int w = 1; w < NWV; ++w) {
+                rk += red[par][w][0][cl];
+                rq += red[par][w][1][cl];
+                kq += red_kq[par][w];
+            }
+        }
+        const float b = beta[nh];
+        const float4 vv = elem<T>::load4(v + nh * DV + 4 * cl);
+        const f32x4 e = {b * (vv.x - rk[0]), b * (vv.y - rk[1]), b * (vv.z - rk[2]),
+                         b * (vv.w - rk[3])};
+        if (wave == 0 && lane < LPR) {
+            const f32x4 oo = scale * (rq + kq * e);
+            elem<T>::store4(o + nh * DV + 4 * cl, make_float4(oo[0], oo[1], oo[2], oo[3]));
+        }
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) store_stream4(state(nh, it), s[it] + kr[it] * e);
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) s[it] = sn[it];
     }
 }
 
 template <typename T, int DK, int DV>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-    constexpr int threads = (DV < 32 ? 1 : DV / 32) * 64;
-    const int64_t blocks = static_cast<int64_t>(a.N) * a.H;
-    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(static_cast<unsigned>(blocks)),
+    constexpr int threads = DecodeShape<DK, DV>::NWV * 64;
+    const int64_t nheads = static_cast<int64_t>(a.N) * a.H;
+    // persistent grid; small states (one wave each) get more work-groups
+    const int64_t grid = std::min<int64_t>(nheads, kDecodeGrid * (threads == 64 ? 4 : 1));
+    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(static_cast<unsigned>(grid)),
                        dim3(threads), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.log_alpha, a.beta, a.S,
-                       static_cast<T*>(a.o), a.scale);
+                       static_cast<T*>(a.o), a.scale, nheads);
     return hipGetLastError();
 }
 
