@@ -61,8 +61,10 @@ def source_digest(names):
 
 
 def load_traffic(kernel_file, digest):
-    """HBM traffic per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+    """HBM traffic per launch (bytes read + written beyond L2, from rocprofv3
+    FETCH_SIZE and WRITE_SIZE scaled by a device copy's readings) from the
+    committed counter summary, if it was taken on the current kernel
+    source; else None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -148,6 +150,7 @@ def main():
 
     digest = source_digest(["prefill_wy.hip", "kda_mfma.h", "kda_device.h", "kda_sched.h"])
     traffic = load_traffic("prefill_wy.hip", digest)
+    dec_traffic = load_traffic("decode.hip", source_digest(["decode.hip", "kda_device.h"]))
 
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, % of MI355X roofline",
@@ -176,7 +179,8 @@ def main():
         "decode": {"workload": "decode_n256", "us_per_step": dec_step_us,
                    "seq_steps_per_s": wd.N / (dec_step_us * 1e-6),
                    "state_GBps": dec_gbps, "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS,
-                   "algorithmic_bytes_per_step": dec_bytes, "kernel": DECODE_KERNEL},
+                   "algorithmic_bytes_per_step": dec_bytes, "traffic_per_step": dec_traffic,
+                   "kernel": DECODE_KERNEL},
         "cpu_baseline": None,
     }
 
