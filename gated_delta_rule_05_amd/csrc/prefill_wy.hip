@@ -28,9 +28,11 @@
 // block forward substitution for the blocks below them.
 // Pass 2, the carry kernel: one work-group per (sequence, head, value tile)
 // walks the chunks in order with its fp32 state slabs in registers.  Per
-// chunk it needs three products on the serial path (W S0, then Kd^T E) and
-// one off it (O).  Loader waves copy the next chunk's slot into the other
-// half of a double buffer in LDS, their global loads four chunks ahead.
+// chunk it needs two products on the serial path (W S0, then Kd^T E), done
+// by a state wave per 16-column slab, and one off it (O), done one chunk
+// later by an output wave from the state wave's handover of S0 and E.
+// Loader waves copy the next chunk's slot into the other half of a double
+// buffer in LDS, their global loads four chunks ahead.
 // The host alternates the passes over blocks of chunks, so the workspace
 // holds a bounded block of slots (and stays mostly cache-resident) while
 // the state is carried between blocks through hT (or a workspace copy).
@@ -475,13 +477,17 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
                              int64_t groups, int R, int H, int DV, int c_lo, int L_b, float scale,
                              bf16_t* __restrict__ o)
 {
-    constexpr int NSLAB = TV / 16;           // one 16-column slab per consumer wave
-    constexpr int NC = NSLAB;
-    constexpr int NL = CW - NC;              // loader waves
+    constexpr int NSLAB = TV / 16;           // 16-column state slabs in the tile
+    constexpr int NC = NSLAB;                // state waves; as many output waves
+    constexpr int NL = CW - 2 * NC;          // loader waves
     constexpr int NU = (kOffU + kSlabBytes * NSLAB) / 16;   // 16-byte units per chunk
     constexpr int NPL = (NU + NL * 64 - 1) / (NL * 64);     // units per loader lane
     static_assert(TV >= 16 && TV <= kMaxTwoPassTile, "tile of 16 or 32 columns");
     __shared__ u32x4 buf[2][NU];
+    // handover from a state wave to its output wave: S0 and E of a chunk as
+    // B operands, double-buffered by chunk parity
+    __shared__ u32x4 xsb[2][NC][4][64];
+    __shared__ u32x2 xeb[2][NC][4][64];
 
     int64_t pair;
     int tile;
@@ -520,9 +526,9 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
                         slot_bytes(DV);
     };
 
-    if (wave >= NC) {
+    if (wave >= 2 * NC) {
         // ======================= loader waves =======================
-        const int ll = (wave - NC) * 64 + lane;
+        const int ll = (wave - 2 * NC) * 64 + lane;
         const int ubase = tile * NSLAB * kSlabBytes;   // this tile's U slabs within the slot's U
         // Every load is unconditional (indices clamped to valid data), so the
         // wait before a store to LDS only covers the loads it needs while the
@@ -547,113 +553,150 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
                 if (u < NU) buf[b][unit(u)] = r[x];
             }
         };
-        // four register sets: chunk j lives in set j % 4 from its fetch until
-        // its store, four iterations later
-        u32x4 r0[NPL], r1[NPL], r2[NPL], r3[NPL];
         const int m0 = c_lo;
-        fetch(r0, m0);
-        fetch(r1, m0 + 1);
-        fetch(r2, m0 + 2);
-        fetch(r3, m0 + 3);
-        put(r0, 0);
-        fetch(r0, m0 + 4);
-        __syncthreads();
-        // iteration x: store chunk x+1 into the buffer the consumers do not
-        // read and fetch chunk x+5 into the same set; past the last chunk
-        // the stores go to the idle buffer and are never read
-        for (int x = 0; x < count; x += 4) {
-            put(r1, 1);
-            fetch(r1, m0 + x + 5);
-            __syncthreads();
-            if (x + 1 >= count) break;
-            put(r2, 0);
-            fetch(r2, m0 + x + 6);
-            __syncthreads();
-            if (x + 2 >= count) break;
-            put(r3, 1);
-            fetch(r3, m0 + x + 7);
-            __syncthreads();
-            if (x + 3 >= count) break;
+        if constexpr (NPL <= 10) {
+            // four register sets: chunk j lives in set j % 4 from its fetch
+            // until its store, four iterations later
+            u32x4 r0[NPL], r1[NPL], r2[NPL], r3[NPL];
+            fetch(r0, m0);
+            fetch(r1, m0 + 1);
+            fetch(r2, m0 + 2);
+            fetch(r3, m0 + 3);
             put(r0, 0);
-            fetch(r0, m0 + x + 8);
+            fetch(r0, m0 + 4);
             __syncthreads();
+            // iteration x: store chunk x+1 into the buffer the consumers do
+            // not read and fetch chunk x+5 into the same set; past the last
+            // chunk the stores go to the idle buffer and are never read
+            for (int x = 0; x < count; x += 4) {
+                put(r1, 1);
+                fetch(r1, m0 + x + 5);
+                __syncthreads();
+                if (x + 1 >= count) break;
+                put(r2, 0);
+                fetch(r2, m0 + x + 6);
+                __syncthreads();
+                if (x + 2 >= count) break;
+                put(r3, 1);
+                fetch(r3, m0 + x + 7);
+                __syncthreads();
+                if (x + 3 >= count) break;
+                put(r0, 0);
+                fetch(r0, m0 + x + 8);
+                __syncthreads();
+            }
+        } else {
+            // two register sets (wider tiles: fewer loader waves, more units
+            // each), chunk j in set j % 2 for two iterations
+            u32x4 r0[NPL], r1[NPL];
+            fetch(r0, m0);
+            fetch(r1, m0 + 1);
+            put(r0, 0);
+            fetch(r0, m0 + 2);
+            __syncthreads();
+            for (int x = 0; x < count; x += 2) {
+                put(r1, 1);
+                fetch(r1, m0 + x + 3);
+                __syncthreads();
+                if (x + 1 >= count) break;
+                put(r0, 0);
+                fetch(r0, m0 + x + 4);
+                __syncthreads();
+            }
         }
         return;
     }
 
-    // ======================= consumer waves =======================
-    // fp32 state slab in the accumulator layout:
-    // S[m][i] = state[c = 16m + 4g + i][j = wave * 16 + ln]
-    const int jc = wave * 16 + ln;
-    f32x4 S[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[m][i] = s_in ? s_in[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] : 0.f;
     const int vrow = H * DV;
-    __syncthreads();
-    for (int x = 0; x < count; ++x) {
-        const int m = c_lo + x;
-        const u32x4* F = buf[x & 1];
+    if (wave < NC) {
+        // ======================= state waves =======================
+        // fp32 state slab in the accumulator layout:
+        // S[m][i] = state[c = 16m + 4g + i][j = j0 + wave * 16 + ln]
+        const int jc = wave * 16 + ln;
+        f32x4 S[8];
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[m][i] = s_in ? s_in[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] : 0.f;
+        __syncthreads();
+        for (int x = 0; x < count; ++x) {
+            const u32x4* F = buf[x & 1];
+            // fragments read one stage ahead (scheduling barriers keep the
+            // order); independent accumulators interleave
+            const u32x2* U = reinterpret_cast<const u32x2*>(F + kOffU / 16) + wave * 4 * 64;
+            const float* gam = reinterpret_cast<const float*>(F + kOffGam / 16);
+            u32x4 wf[16];
+            u32x2 uw[4];
+#pragma unroll
+            for (int f = 0; f < 16; ++f) wf[f] = F[(kFragW + f) * 64 + lane];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) uw[I] = U[I * 64 + lane];
+            u32x4 sb[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- E = U - W S0 (reads of Kd^T and e^{G} in flight)
+            u32x4 kf[16];
+            f32x4 gm[8];
+#pragma unroll
+            for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK + f) * 64 + lane];
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
+            f32x4 y[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) y[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int I = 0; I < 4; ++I) y[I] = mma32(wf[4 * I + kk], sb[kk], y[I]);
+            u32x2 eb[4];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const f32x4 e = {lo_bf(uw[I][0]) - y[I][0], hi_bf(uw[I][0]) - y[I][1],
+                                 lo_bf(uw[I][1]) - y[I][2], hi_bf(uw[I][1]) - y[I][3]};
+                eb[I] = pack2(e);
+            }
+            const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
+            // hand S0 and E of this chunk to the output wave
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) xsb[x & 1][wave][kk][lane] = sb[kk];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) xeb[x & 1][wave][I][lane] = eb[I];
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- S = Diag(e^{G}) S0 + Kd^T E
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm], e01, gm[mm] * S[mm]);
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm + 1], e23, S[mm]);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                hstate[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] = S[m][i];
+        return;
+    }
+
+    // ======================= output waves =======================
+    // O of chunk x-1 = scale (Qg S0 + P E), during iteration x: from the Qg
+    // and P fragments copied in iteration x-1 and the state wave's handover;
+    // rows past the end of the sequence are dropped by the range check
+    const int sl = wave - NC;                   // slab
+    const int jc = sl * 16 + ln;
+    auto out_chunk = [&](int m, const u32x4* qf, const u32x4* pf, int b) {
         const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
         const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
-
-        // Each stage's LDS fragments are read one stage ahead (scheduling
-        // barriers keep the order), so their latency hides behind the
-        // previous stage's products; independent accumulators interleave.
-        const u32x2* U = reinterpret_cast<const u32x2*>(F + kOffU / 16) + wave * 4 * 64;
-        const float* gam = reinterpret_cast<const float*>(F + kOffGam / 16);
-        u32x4 wf[16];
-        u32x2 uw[4];
-#pragma unroll
-        for (int f = 0; f < 16; ++f) wf[f] = F[(kFragW + f) * 64 + lane];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) uw[I] = U[I * 64 + lane];
-        u32x4 sb[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- E = U - W S0 (reads of Kd^T and e^{G} in flight)
-        u32x4 kf[16];
-        f32x4 gm[8];
-#pragma unroll
-        for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK + f) * 64 + lane];
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
-        f32x4 y[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) y[I] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int I = 0; I < 4; ++I) y[I] = mma32(wf[4 * I + kk], sb[kk], y[I]);
-        u32x2 eb[4];
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            const f32x4 e = {lo_bf(uw[I][0]) - y[I][0], hi_bf(uw[I][0]) - y[I][1],
-                             lo_bf(uw[I][1]) - y[I][2], hi_bf(uw[I][1]) - y[I][3]};
-            eb[I] = pack2(e);
-        }
-        const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- S = Diag(e^{G}) S0 + Kd^T E (reads of Qg and P in flight)
-        u32x4 qf[16], pf[6];
-#pragma unroll
-        for (int f = 0; f < 16; ++f) qf[f] = F[(kFragQ + f) * 64 + lane];
-#pragma unroll
-        for (int f = 0; f < 6; ++f) pf[f] = F[(kFragP + f) * 64 + lane];
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm], e01, gm[mm] * S[mm]);
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm + 1], e23, S[mm]);
-        __builtin_amdgcn_sched_barrier(0);
-
-        // ---- O = scale (Qg S0 + P E); rows past the end are dropped by the range check
         const __amdgpu_buffer_rsrc_t ro = rsrc(o + (c0 * H + h) * DV + j0,
                                                2u * static_cast<uint32_t>((len - 1) * vrow + TV));
+        u32x4 sb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) sb[kk] = xsb[b][sl][kk][lane];
+        const u32x4 e01 = cat(xeb[b][sl][0][lane], xeb[b][sl][1][lane]);
+        const u32x4 e23 = cat(xeb[b][sl][2][lane], xeb[b][sl][3][lane]);
         f32x4 oc[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) oc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -670,13 +713,27 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * oc[I][i]));
+    };
+    auto copy_qp = [&](u32x4* qf, u32x4* pf, int b) {
+#pragma unroll
+        for (int f = 0; f < 16; ++f) qf[f] = buf[b][(kFragQ + f) * 64 + lane];
+#pragma unroll
+        for (int f = 0; f < 6; ++f) pf[f] = buf[b][(kFragP + f) * 64 + lane];
+    };
+    u32x4 qa[16], pa[6], qb[16], pb[6];
+    __syncthreads();
+    for (int x = 0; x < count; x += 2) {
+        copy_qp(qa, pa, 0);                             // chunk x
+        if (x >= 1) out_chunk(c_lo + x - 1, qb, pb, 1);
+        __syncthreads();
+        if (x + 1 >= count) break;
+        copy_qp(qb, pb, 1);                             // chunk x+1
+        out_chunk(c_lo + x, qa, pa, 0);
         __syncthreads();
     }
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            hstate[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] = S[m][i];
+    // the last chunk: its handover was written before the final barrier
+    if (count & 1) out_chunk(c_lo + count - 1, qa, pa, 0);
+    else out_chunk(c_lo + count - 1, qb, pb, 1);
 }
 
 // ===================================================================
