@@ -76,7 +76,7 @@ __device__ __forceinline__ int fpos(int x) {
 // ===================================================================
 // pass 1: prep
 // ===================================================================
-constexpr int PT = 256;        // threads (4 waves)
+constexpr int PT = 512;        // threads (8 waves)
 constexpr int TS = DK + 8;     // bf16 stride of token rows (272 B: conflict-free 16-byte reads)
 constexpr int CS = C + 8;      // bf16 stride of channel rows (144 B)
 constexpr int BS = 20;         // bf16 stride of 16x16 blocks
@@ -216,8 +216,8 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int ln = lane & 15;
-    const int cg = lane & 15;                  // staging: channels 8cg .. 8cg+7
-    const int rg = 4 * wave + (lane >> 4);     //          rows 4rg .. 4rg+3
+    const int cg = lane & 31;                  // staging: channels 4cg .. 4cg+3
+    const int rg = 2 * wave + (lane >> 5);     //          rows 4rg .. 4rg+3
 
     // ---------------- staging loads (rows past the end read zero) ----------
     const int64_t e0 = (c0 * H + h) * DK;
@@ -227,17 +227,16 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     const __amdgpu_buffer_rsrc_t rla = rsrc(log_alpha + e0, 4u * span);
     const __amdgpu_buffer_rsrc_t rv =
         rsrc(v + (c0 * H + h) * DV, 2u * static_cast<uint32_t>((len - 1) * H * DV + DV));
-    u32x4 kr[4], qr[4], vr[4];
-    f32x4 la[4][2];
+    u32x2 kr[4], qr[4], vr[4];
+    f32x4 la[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
-        const int off = r * H * DK + 8 * cg;
-        kr[i] = ld128(rk, 2 * off);
-        qr[i] = ld128(rq, 2 * off);
-        la[i][0] = __builtin_bit_cast(f32x4, ld128(rla, 4 * off));
-        la[i][1] = __builtin_bit_cast(f32x4, ld128(rla, 4 * off + 16));
-        vr[i] = (8 * cg < DV) ? ld128(rv, 2 * (r * H * DV + 8 * cg)) : u32x4{0u, 0u, 0u, 0u};
+        const int off = r * H * DK + 4 * cg;
+        kr[i] = ld64(rk, 2 * off);
+        qr[i] = ld64(rq, 2 * off);
+        la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * off));
+        vr[i] = (4 * cg < DV) ? ld64(rv, 2 * (r * H * DV + 4 * cg)) : u32x2{0u, 0u};
     }
     if (tid < C) {
         const __amdgpu_buffer_rsrc_t rb =
@@ -246,18 +245,17 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     }
 
     // ---------------- cumulative gate (log2 units) ----------------------------
-    float p[4][8];
+    float p[4][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 4; ++j) {
         float run = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            run = __builtin_fmaf(la[i][j >> 2][j & 3], kLog2e, run);
+            run = __builtin_fmaf(la[i][j], kLog2e, run);
             p[i][j] = run;
         }
     }
-    *reinterpret_cast<f32x4*>(&sm.scan[rg][8 * cg]) = f32x4{p[3][0], p[3][1], p[3][2], p[3][3]};
-    *reinterpret_cast<f32x4*>(&sm.scan[rg][8 * cg + 4]) = f32x4{p[3][4], p[3][5], p[3][6], p[3][7]};
+    *reinterpret_cast<f32x4*>(&sm.scan[rg][4 * cg]) = f32x4{p[3][0], p[3][1], p[3][2], p[3][3]};
     __syncthreads();
     if (tid < DK) {
         float run = 0.f;
@@ -273,25 +271,16 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     __syncthreads();
 
     // ---------------- decay-weighted operands ---------------------------------
-    float off[8], G[8];
-    {
-        const f32x4 o0 = *reinterpret_cast<const f32x4*>(&sm.scan[rg][8 * cg]);
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(&sm.scan[rg][8 * cg + 4]);
-        const f32x4 g0 = *reinterpret_cast<const f32x4*>(&sm.glog[8 * cg]);
-        const f32x4 g1 = *reinterpret_cast<const f32x4*>(&sm.glog[8 * cg + 4]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            off[j] = o0[j]; off[j + 4] = o1[j];
-            G[j] = g0[j]; G[j + 4] = g1[j];
-        }
-    }
-    float kg[4][8], kd[4][8];
+    const f32x4 off = *reinterpret_cast<const f32x4*>(&sm.scan[rg][4 * cg]);
+    const f32x4 G = *reinterpret_cast<const f32x4*>(&sm.glog[4 * cg]);
+    const int cpos = fpos(4 * cg);              // the 4 channels' position in a token row
+    float kg[4][4], kd[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
-        float qg[8], kn[8];
+        float qg[4], kn[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const float gl = off[j] + p[i][j];
             const float u = __builtin_amdgcn_exp2f(gl);
             const float w = __builtin_amdgcn_exp2f(-gl);
@@ -304,30 +293,19 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             kn[j] = kx * w;
             kd[i][j] = kx * d;
         }
-#pragma unroll
-        for (int pc = 0; pc < 2; ++pc) {
-            const int x = 8 * cg + 4 * pc;      // first of 4 consecutive channels
-            const int pos = fpos(x);
-            const int b = 4 * pc;
-            *reinterpret_cast<u32x2*>(sm.tok[0] + r * TS + pos) =
-                u32x2{pk(kg[i][b], kg[i][b + 1]), pk(kg[i][b + 2], kg[i][b + 3])};
-            *reinterpret_cast<u32x2*>(sm.tok[1] + r * TS + pos) =
-                u32x2{pk(kn[b], kn[b + 1]), pk(kn[b + 2], kn[b + 3])};
-            const u32x2 qv = u32x2{pk(qg[b], qg[b + 1]), pk(qg[b + 2], qg[b + 3])};
-            *reinterpret_cast<u32x2*>(sm.tok[2] + r * TS + pos) = qv;
-            // Qg as the A operand of pass 2: fragment (I = r/16, kk = x/32),
-            // lane (g = (x%16)/4, r%16), half (x%32)/16
-            const int fl = 16 * ((x & 15) >> 2) + (r & 15);
-            *reinterpret_cast<u32x2*>(out + (kFragQ + 4 * (r >> 4) + (x >> 5)) * kFrag + fl * 16 +
-                                      8 * ((x & 31) >> 4)) = qv;
-        }
+        *reinterpret_cast<u32x2*>(sm.tok[0] + r * TS + cpos) =
+            u32x2{pk(kg[i][0], kg[i][1]), pk(kg[i][2], kg[i][3])};
+        *reinterpret_cast<u32x2*>(sm.tok[1] + r * TS + cpos) =
+            u32x2{pk(kn[0], kn[1]), pk(kn[2], kn[3])};
+        *reinterpret_cast<u32x2*>(sm.tok[2] + r * TS + cpos) =
+            u32x2{pk(qg[0], qg[1]), pk(qg[2], qg[3])};
     }
     {
         const int x = 4 * rg;                   // first of this thread's 4 tokens
         const int pos = fpos(x);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int c = 8 * cg + j;
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * cg + j;
             *reinterpret_cast<u32x2*>(sm.kgt + c * CS + pos) =
                 u32x2{pk(kg[0][j], kg[1][j]), pk(kg[2][j], kg[3][j])};
             // Kd^T as the A operand of pass 2: fragment (m = c/16, kk = x/32),
@@ -340,24 +318,40 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     }
     __syncthreads();
 
+    // Qg as the A operands of pass 2: its token rows are already in fragment
+    // order, so fragment (I, kk), lane (g, ln) is 16 contiguous bytes of row
+    // 16I + ln; 1024 units, two per thread
+#pragma unroll
+    for (int x = 0; x < 1024 / PT; ++x) {
+        const int u = tid + PT * x;                 // unit = (I, kk, lane)
+        const int f = u >> 6, ul = u & 63;
+        const int I = f >> 2, kk = f & 3;
+        *reinterpret_cast<u32x4*>(out + (kFragQ + f) * kFrag + ul * 16) =
+            *reinterpret_cast<const u32x4*>(sm.tok[2] + (16 * I + (ul & 15)) * TS + 32 * kk + 8 * (ul >> 4));
+    }
+
     // ---------------- A and P tiles, diagonal inverses ---------------------------
     // jobs 0..5: strictly-lower A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
-    // jobs 6..15: lower P blocks (0,0) (1,0) (1,1) (2,0) .. (3,3); wave w takes
-    // jobs w, w+4, w+8, w+12 and the diagonal block I = w
-    const u32x2 dres = diag_inverse(sm, wave, g, ln);
+    // jobs 6..15: lower P blocks (0,0) (1,0) (1,1) (2,0) .. (3,3).  Waves 0..3
+    // invert diagonal block I = wave and take job 12 + wave; waves 4..7 take
+    // jobs wave-4, wave and wave+4.
+    u32x2 dres = {0u, 0u};
+    if (wave < 4) dres = diag_inverse(sm, wave, g, ln);
     f32x4 aval[2];
     int aidx[2] = {-1, -1};
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int j = wave + 4 * x;
-        if (x < 2 && j < 6) {
+    for (int x = 0; x < 3; ++x) {
+        const int j = wave < 4 ? (x == 0 ? 12 + wave : -1) : wave - 4 + 4 * x;
+        if (j < 0) continue;
+        if (j < 6) {
             const int I = j < 1 ? 1 : j < 3 ? 2 : 3;
             const int J = j - an_index(I, 0);
             const f32x4 acc = row_product(sm.tok[0] + 16 * I * TS, sm.tok[1] + 16 * J * TS, g, ln);
             const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta + 16 * I + 4 * g);
-            aval[x] = -bt * acc;
-            aidx[x] = j;
-        } else if (j >= 6) {
+            const int slotx = x == 0 ? 0 : 1;      // jobs j < 6 come at x = 0 and x = 1
+            aval[slotx] = -bt * acc;
+            aidx[slotx] = j;
+        } else {
             const int t = j - 6;
             const int I = (t >= 1) + (t >= 3) + (t >= 6);
             const int J = t - I * (I + 1) / 2;
@@ -383,22 +377,22 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     {
         uint16_t* an = sm.tok[0] + kAnOff;
         uint16_t* dinv = sm.tok[0] + kDinvOff;
-        *reinterpret_cast<u32x2*>(dinv + (16 * wave + ln) * BS + 4 * g) = dres;
+        if (wave < 4) *reinterpret_cast<u32x2*>(dinv + (16 * wave + ln) * BS + 4 * g) = dres;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             if (aidx[x] < 0) continue;
 #pragma unroll
             for (int i = 0; i < 4; ++i) an[(aidx[x] * 16 + 4 * g + i) * BS + ln] = bf(aval[x][i]);
         }
-        if (8 * cg < DV) {
+        if (4 * cg < DV) {
             uint16_t* vt = sm.tok[1];
             const int pos = fpos(4 * rg);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 const int sh = 16 * (j & 1);
                 const uint32_t v0 = (vr[0][j >> 1] >> sh) & 0xffffu, v1 = (vr[1][j >> 1] >> sh) & 0xffffu;
                 const uint32_t v2 = (vr[2][j >> 1] >> sh) & 0xffffu, v3 = (vr[3][j >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<u32x2*>(vt + (8 * cg + j) * CS + pos) =
+                *reinterpret_cast<u32x2*>(vt + (4 * cg + j) * CS + pos) =
                     u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
             }
         }
@@ -409,53 +403,58 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     if (wave == 0) t_column<0>(sm, g, ln);
     else if (wave == 1) t_column<1>(sm, g, ln);
     else if (wave == 2) t_column<2>(sm, g, ln);
-    else t_column<3>(sm, g, ln);
+    else if (wave == 3) t_column<3>(sm, g, ln);
     __syncthreads();
 
     // ---------------- W = T Kg (as W^T tiles) and U = T V -----------------------
     const uint16_t* tb = sm.tok[0] + kTbOff;
-    u32x4 tf[6];                                 // rows 16I + ln of T, K-steps kk <= I/2
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int kk = 0; kk <= (I >> 1); ++kk)
-            tf[p_frag(I, kk)] = *reinterpret_cast<const u32x4*>(tb + (16 * I + ln) * CS + 32 * kk + 8 * g);
     {
-        // W^T tile (cb, I): lane gets W[16I + ln][16cb + 4g + i]; the two
-        // channel blocks 2w, 2w+1 together form W's A operand (I, kk = w)
+        // W^T tile (cb, I): lane gets W[16I + ln][16cb + 4g + i]; channel
+        // blocks cb = 2kk, 2kk+1 together form W's A operand (I, kk).  Wave
+        // w takes kk = w % 4 and the row blocks I = 2 (w / 4), 2 (w / 4) + 1.
+        const int kk2 = wave & 3;
+        const int Ib = 2 * (wave >> 2);
         u32x4 kf[2][2];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk)
-                kf[c][kk] = *reinterpret_cast<const u32x4*>(sm.kgt + (16 * (2 * wave + c) + ln) * CS +
+                kf[c][kk] = *reinterpret_cast<const u32x4*>(sm.kgt + (16 * (2 * kk2 + c) + ln) * CS +
                                                             32 * kk + 8 * g);
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
+        for (int ii = 0; ii < 2; ++ii) {
+            const int I = Ib + ii;
             f32x4 acc[2];
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk <= (I >> 1); ++kk) acc[c] = mma32(kf[c][kk], tf[p_frag(I, kk)], acc[c]);
+                for (int kk = 0; kk < 2; ++kk) {
+                    if (kk > (I >> 1)) continue;
+                    const u32x4 tf = *reinterpret_cast<const u32x4*>(tb + (16 * I + ln) * CS + 32 * kk + 8 * g);
+                    acc[c] = mma32(kf[c][kk], tf, acc[c]);
+                }
             }
-            *reinterpret_cast<u32x4*>(out + (kFragW + 4 * I + wave) * kFrag + lane * 16) =
+            *reinterpret_cast<u32x4*>(out + (kFragW + 4 * I + kk2) * kFrag + lane * 16) =
                 cat(pack2(acc[0]), pack2(acc[1]));
         }
     }
     const uint16_t* vt = sm.tok[1];
-    for (int s = wave; s < DV / 16; s += 4) {
+    for (int sl = wave; sl < DV / 16; sl += PT / 64) {
         u32x4 vf[2];
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            vf[kk] = *reinterpret_cast<const u32x4*>(vt + (16 * s + ln) * CS + 32 * kk + 8 * g);
+            vf[kk] = *reinterpret_cast<const u32x4*>(vt + (16 * sl + ln) * CS + 32 * kk + 8 * g);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk <= (I >> 1); ++kk) acc = mma32(tf[p_frag(I, kk)], vf[kk], acc);
-            // accumulator layout: lane gets U[16I + 4g + i][16s + ln]
-            *reinterpret_cast<u32x2*>(out + kOffU + s * kSlabBytes + (I * 64 + lane) * 8) = pack2(acc);
+            for (int kk = 0; kk <= (I >> 1); ++kk) {
+                const u32x4 tf = *reinterpret_cast<const u32x4*>(tb + (16 * I + ln) * CS + 32 * kk + 8 * g);
+                acc = mma32(tf, vf[kk], acc);
+            }
+            // accumulator layout: lane gets U[16I + 4g + i][16sl + ln]
+            *reinterpret_cast<u32x2*>(out + kOffU + sl * kSlabBytes + (I * 64 + lane) * 8) = pack2(acc);
         }
     }
 }
