@@ -229,13 +229,16 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
         rsrc(v + (c0 * H + h) * DV, 2u * static_cast<uint32_t>((len - 1) * H * DV + DV));
     u32x2 kr[4], qr[4], vr[4];
     f32x4 la[4];
+    // the gates first: the cumulative sum waits on them
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
         const int off = r * H * DK + 4 * cg;
         kr[i] = ld64(rk, 2 * off);
         qr[i] = ld64(rq, 2 * off);
-        la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * off));
         vr[i] = (4 * cg < DV) ? ld64(rv, 2 * (r * H * DV + 4 * cg)) : u32x2{0u, 0u};
     }
     if (tid < C) {
@@ -273,6 +276,9 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     // ---------------- decay-weighted operands ---------------------------------
     const f32x4 off = *reinterpret_cast<const f32x4*>(&sm.scan[rg][4 * cg]);
     const f32x4 G = *reinterpret_cast<const f32x4*>(&sm.glog[4 * cg]);
+    f32x4 gamma;                                // e^{G} of the 4 channels
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gamma[j] = __builtin_amdgcn_exp2f(G[j]);
     const int cpos = fpos(4 * cg);              // the 4 channels' position in a token row
     float kg[4][4], kd[4][4];
 #pragma unroll
@@ -284,7 +290,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             const float gl = off[j] + p[i][j];
             const float u = __builtin_amdgcn_exp2f(gl);
             const float w = __builtin_amdgcn_exp2f(-gl);
-            const float d = __builtin_amdgcn_exp2f(G[j] - gl);
+            const float d = gamma[j] * w;       // e^{G - g}: both factors stay in range
             const uint32_t kw = kr[i][j >> 1], qw = qr[i][j >> 1];
             const float kx = (j & 1) ? hi_bf(kw) : lo_bf(kw);
             const float qx = (j & 1) ? hi_bf(qw) : lo_bf(qw);
