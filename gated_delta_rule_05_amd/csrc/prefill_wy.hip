@@ -52,16 +52,19 @@ constexpr int kMaxHeads = 16384;   // keeps every chunk-relative byte offset in 
 
 // ---- workspace slot of one (chunk, head), bytes
 constexpr int kFrag = 1024;                 // one MFMA operand: 64 lanes x 16 B
-constexpr int kFragW = 0;                   // W:     [I 4][kk 4] A operands
-constexpr int kFragQ = 16;                  // Qg:    [I 4][kk 4] A operands
-constexpr int kFragK = 32;                  // Kd^T:  [m 8][kk 2] A operands
-constexpr int kFragP = 48;                  // P:     (I,kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+constexpr int kFragQ = 0;                   // Qg:    [I 4][kk 4] A operands
+constexpr int kFragP = 16;                  // P:     (I,kk) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
+constexpr int kFragW = 22;                  // -W:    [I 4][kk 4] A operands (negated: E = U + (-W) S0)
+constexpr int kFragK = 38;                  // Kd^T:  [m 8][kk 2] A operands
 constexpr int kNumFrag = 54;
+// the carry's output waves read Qg and P straight into registers; the rest
+// (W, Kd^T, e^{G}, U) is staged through LDS, from this byte on
+constexpr int kStageOff = kFragW * kFrag;
 constexpr int kOffGam = kNumFrag * kFrag;   // e^{G}: 128 fp32
 constexpr int kOffU = kOffGam + 512;        // U: [slab d_v/16][I 4][64 lanes][4 bf16]
 constexpr int kSlabBytes = 4 * 64 * 8;      // U of one 16-column slab
 __host__ __device__ constexpr int slot_bytes(int dv) { return kOffU + 128 * dv; }
-static_assert(kOffU % 256 == 0, "slots stay 256-byte aligned");
+static_assert(kOffU % 256 == 0 && kStageOff % 256 == 0, "slots stay 256-byte aligned");
 
 __device__ __forceinline__ int p_frag(int I, int kk) { return I < 2 ? I : 2 * I - 2 + kk; }
 
@@ -81,22 +84,30 @@ constexpr int TS = DK + 8;     // bf16 stride of token rows (272 B: conflict-fre
 constexpr int CS = C + 8;      // bf16 stride of channel rows (144 B)
 constexpr int BS = 20;         // bf16 stride of 16x16 blocks
 
-struct PrepSmem {
+struct alignas(16) PrepSmem {
     uint16_t tok[3][C * TS];   // Kg, Kn, Qg: token rows, channels in fragment order
-    uint16_t kgt[DK * CS];     // Kg: channel rows, tokens in fragment order
-    float scan[16][DK];        // per 4-row group gate sums, then their exclusive prefix
     float beta[C];
     float glog[DK];            // G / ln 2
 };
-// after the products the token rows are dead and their space is reused:
-//   tok[0]:        -A strictly-lower blocks | (I + A_II)^{-1} | T (= T Diag(beta) above)
-//   tok[1..2]:     V, channel rows, tokens in fragment order
-constexpr int kAnOff = 0;                  // 6 blocks
-constexpr int kDinvOff = 6 * 16 * BS;      // 4 blocks
-constexpr int kTbOff = 10 * 16 * BS;       // 64 rows x CS
-static_assert(kTbOff + C * CS <= C * TS, "aliases fit in one token array");
-static_assert((kTbOff * 2) % 16 == 0, "16-byte aligned");
-static_assert(DK * CS <= 2 * C * TS, "V fits in two token arrays");
+// 53 KB: three work-groups fit in one CU's LDS.  Reuse of the token rows:
+// - tok[0] first holds the per 4-row group gate sums and then their
+//   exclusive prefix (float [16][DK]), until the Kg rows are written;
+// - once A and P are formed, Kn and Qg (tok[1..2]) are dead and hold V
+//   (channel rows, tokens in fragment order), the -A strictly-lower
+//   blocks, the inverses (I + A_II)^{-1} and T Diag(beta) (upper blocks
+//   zero); Kg stays for W = T Kg.
+constexpr int kVtOff = 0;                          // d_k rows x CS
+constexpr int kAnOff = kVtOff + DK * CS;           // 6 blocks
+constexpr int kDinvOff = kAnOff + 6 * 16 * BS;     // 4 blocks
+constexpr int kTbOff = kDinvOff + 4 * 16 * BS;     // 64 rows x CS
+static_assert(kTbOff + C * CS <= 2 * C * TS, "V and T fit in two token arrays");
+static_assert(kAnOff % 8 == 0 && kDinvOff % 8 == 0 && kTbOff % 8 == 0, "16-byte aligned");
+static_assert(16 * DK * sizeof(float) <= C * TS * sizeof(uint16_t), "gate sums fit in one token array");
+static_assert(sizeof(PrepSmem) * 3 <= 160 * 1024, "three work-groups per CU");
+
+__device__ __forceinline__ float* gate_sums(PrepSmem& sm) { return reinterpret_cast<float*>(sm.tok[0]); }
+__device__ __forceinline__ uint16_t* spare_rows(PrepSmem& sm) { return &sm.tok[0][0] + C * TS; }
+__device__ __forceinline__ const uint16_t* spare_rows(const PrepSmem& sm) { return &sm.tok[0][0] + C * TS; }
 
 // 16x16 product of two 16-row blocks stored in fragment order:
 // D[m][n] = sum_c X[m][c] Y[n][c]
@@ -159,9 +170,9 @@ __device__ __forceinline__ int an_index(int I, int J) { return I * (I - 1) / 2 +
 // T Diag(beta) into the fragment-ordered rows of tb.
 template <int J>
 __device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
-    const uint16_t* an = sm.tok[0] + kAnOff;
-    const uint16_t* dinv = sm.tok[0] + kDinvOff;
-    uint16_t* tb = sm.tok[0] + kTbOff;
+    const uint16_t* an = spare_rows(sm) + kAnOff;
+    const uint16_t* dinv = spare_rows(sm) + kDinvOff;
+    uint16_t* tb = spare_rows(sm) + kTbOff;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
     f32x4 col[4];
 #pragma unroll
@@ -192,7 +203,7 @@ __device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
 
 }  // namespace
 
-__global__ __launch_bounds__(PT, 2)
+__global__ __launch_bounds__(PT, 3)
 void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                             const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
                             const float* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -258,14 +269,15 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             p[i][j] = run;
         }
     }
-    *reinterpret_cast<f32x4*>(&sm.scan[rg][4 * cg]) = f32x4{p[3][0], p[3][1], p[3][2], p[3][3]};
+    float* scan = gate_sums(sm);
+    *reinterpret_cast<f32x4*>(scan + rg * DK + 4 * cg) = f32x4{p[3][0], p[3][1], p[3][2], p[3][3]};
     __syncthreads();
     if (tid < DK) {
         float run = 0.f;
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-            const float t = sm.scan[x][tid];
-            sm.scan[x][tid] = run;
+            const float t = scan[x * DK + tid];
+            scan[x * DK + tid] = run;
             run += t;
         }
         sm.glog[tid] = run;
@@ -274,7 +286,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     __syncthreads();
 
     // ---------------- decay-weighted operands ---------------------------------
-    const f32x4 off = *reinterpret_cast<const f32x4*>(&sm.scan[rg][4 * cg]);
+    const f32x4 off = *reinterpret_cast<const f32x4*>(scan + rg * DK + 4 * cg);
     const f32x4 G = *reinterpret_cast<const f32x4*>(&sm.glog[4 * cg]);
     f32x4 gamma;                                // e^{G} of the 4 channels
 #pragma unroll
@@ -299,8 +311,6 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             kn[j] = kx * w;
             kd[i][j] = kx * d;
         }
-        *reinterpret_cast<u32x2*>(sm.tok[0] + r * TS + cpos) =
-            u32x2{pk(kg[i][0], kg[i][1]), pk(kg[i][2], kg[i][3])};
         *reinterpret_cast<u32x2*>(sm.tok[1] + r * TS + cpos) =
             u32x2{pk(kn[0], kn[1]), pk(kn[2], kn[3])};
         *reinterpret_cast<u32x2*>(sm.tok[2] + r * TS + cpos) =
@@ -308,12 +318,9 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     }
     {
         const int x = 4 * rg;                   // first of this thread's 4 tokens
-        const int pos = fpos(x);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 4 * cg + j;
-            *reinterpret_cast<u32x2*>(sm.kgt + c * CS + pos) =
-                u32x2{pk(kg[0][j], kg[1][j]), pk(kg[2][j], kg[3][j])};
             // Kd^T as the A operand of pass 2: fragment (m = c/16, kk = x/32),
             // lane (g = (x%16)/4, c%16), half (x%32)/16
             const int fl = 16 * ((x & 15) >> 2) + (c & 15);
@@ -322,6 +329,11 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
                 u32x2{pk(kd[0][j], kd[1][j]), pk(kd[2][j], kd[3][j])};
         }
     }
+    __syncthreads();   // every gate offset has been read: tok[0] takes the Kg rows
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x2*>(sm.tok[0] + (4 * rg + i) * TS + cpos) =
+            u32x2{pk(kg[i][0], kg[i][1]), pk(kg[i][2], kg[i][3])};
     __syncthreads();
 
     // Qg as the A operands of pass 2: its token rows are already in fragment
@@ -381,8 +393,8 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
 
     // ---------------- -A blocks, inverses and V into the freed token rows -------
     {
-        uint16_t* an = sm.tok[0] + kAnOff;
-        uint16_t* dinv = sm.tok[0] + kDinvOff;
+        uint16_t* an = spare_rows(sm) + kAnOff;
+        uint16_t* dinv = spare_rows(sm) + kDinvOff;
         if (wave < 4) *reinterpret_cast<u32x2*>(dinv + (16 * wave + ln) * BS + 4 * g) = dres;
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -391,7 +403,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             for (int i = 0; i < 4; ++i) an[(aidx[x] * 16 + 4 * g + i) * BS + ln] = bf(aval[x][i]);
         }
         if (4 * cg < DV) {
-            uint16_t* vt = sm.tok[1];
+            uint16_t* vt = spare_rows(sm) + kVtOff;
             const int pos = fpos(4 * rg);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -412,21 +424,28 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     else if (wave == 3) t_column<3>(sm, g, ln);
     __syncthreads();
 
-    // ---------------- W = T Kg (as W^T tiles) and U = T V -----------------------
-    const uint16_t* tb = sm.tok[0] + kTbOff;
+    // ---------------- -W = -T Kg (as W^T tiles) and U = T V ---------------------
+    const uint16_t* tb = spare_rows(sm) + kTbOff;
     {
         // W^T tile (cb, I): lane gets W[16I + ln][16cb + 4g + i]; channel
         // blocks cb = 2kk, 2kk+1 together form W's A operand (I, kk).  Wave
         // w takes kk = w % 4 and the row blocks I = 2 (w / 4), 2 (w / 4) + 1.
         const int kk2 = wave & 3;
         const int Ib = 2 * (wave >> 2);
+        // A operand Kg^T (channel 16 cb + ln, tokens in fragment order),
+        // gathered from the token rows of Kg: K-step kk, group g takes the
+        // tokens 32 kk + 4g + {0..3} and 32 kk + 16 + 4g + {0..3}
         u32x4 kf[2][2];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-                kf[c][kk] = *reinterpret_cast<const u32x4*>(sm.kgt + (16 * (2 * kk2 + c) + ln) * CS +
-                                                            32 * kk + 8 * g);
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint16_t* col = sm.tok[0] + (32 * kk + 4 * g) * TS + fpos(16 * (2 * kk2 + c) + ln);
+                auto two = [&](int x) {
+                    return static_cast<uint32_t>(col[x * TS]) | (static_cast<uint32_t>(col[(x + 1) * TS]) << 16);
+                };
+                kf[c][kk] = u32x4{two(0), two(2), two(16), two(18)};
+            }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
             const int I = Ib + ii;
@@ -442,10 +461,10 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
                 }
             }
             *reinterpret_cast<u32x4*>(out + (kFragW + 4 * I + kk2) * kFrag + lane * 16) =
-                cat(pack2(acc[0]), pack2(acc[1]));
+                cat(pack2(-acc[0]), pack2(-acc[1]));
         }
     }
-    const uint16_t* vt = sm.tok[1];
+    const uint16_t* vt = spare_rows(sm) + kVtOff;
     for (int sl = wave; sl < DV / 16; sl += PT / 64) {
         u32x4 vf[2];
 #pragma unroll
@@ -485,14 +504,25 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
     constexpr int NSLAB = TV / 16;           // 16-column state slabs in the tile
     constexpr int NC = NSLAB;                // state waves; as many output waves
     constexpr int NL = CW - 2 * NC;          // loader waves
-    constexpr int NU = (kOffU + kSlabBytes * NSLAB) / 16;   // 16-byte units per chunk
+    constexpr int NU = (kOffU - kStageOff + kSlabBytes * NSLAB) / 16;   // staged 16-byte units per chunk
     constexpr int NPL = (NU + NL * 64 - 1) / (NL * 64);     // units per loader lane
+    constexpr int NSET = NPL <= 6 ? 6 : 3;   // loader register sets
+    static_assert(NSET % 3 == 0, "chunk j is staged in LDS buffer j % 3");
     static_assert(TV >= 16 && TV <= kMaxTwoPassTile, "tile of 16 or 32 columns");
-    __shared__ u32x4 buf[2][NU];
+    // three staging buffers: during iteration x the state waves read chunk
+    // x and the W of chunk x+1, the loaders fill chunk x+2
+    constexpr int NUP = NPL * NL * 64;      // staged units, padded to whole loader rounds
+    __shared__ u32x4 buf[3][NUP];
     // handover from a state wave to its output wave: S0 and E of a chunk as
     // B operands, double-buffered by chunk parity
     __shared__ u32x4 xsb[2][NC][4][64];
     __shared__ u32x2 xeb[2][NC][4][64];
+    // O of a chunk (bf16, lane (g, ln) of row block I: row 16I + ln, columns
+    // 16 slab + 4g .. +3) from the output wave to the state wave, which
+    // stores it: a wave whose global loads are in flight then never has a
+    // store in flight as well (the compiler can wait on an in-order count of
+    // loads alone, not of loads mixed with stores)
+    __shared__ u32x2 xob[2][NC][4][64];
 
     int64_t pair;
     int tile;
@@ -547,65 +577,47 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
 #pragma unroll
             for (int x = 0; x < NPL; ++x) {
                 const int u = unit(min(ll + x * NL * 64, NU - 1));
-                const int byte = 16 * u + (16 * u >= kOffU ? ubase : 0);
+                const int byte = kStageOff + 16 * u + (kStageOff + 16 * u >= kOffU ? ubase : 0);
                 r[x] = *reinterpret_cast<const u32x4*>(s + byte);
             }
         };
         auto put = [&](const u32x4* r, int b) {
 #pragma unroll
             for (int x = 0; x < NPL; ++x) {
-                const int u = ll + x * NL * 64;
-                if (u < NU) buf[b][unit(u)] = r[x];
+                const int u = ll + x * NL * 64;   // padding units land past NU
+                buf[b][u < NU ? unit(u) : u] = r[x];
             }
         };
+        // NSET register sets: chunk j lives in set j % NSET from its fetch
+        // until its store into LDS
+        u32x4 r[NSET][NPL];
         const int m0 = c_lo;
-        if constexpr (NPL <= 10) {
-            // four register sets: chunk j lives in set j % 4 from its fetch
-            // until its store, four iterations later
-            u32x4 r0[NPL], r1[NPL], r2[NPL], r3[NPL];
-            fetch(r0, m0);
-            fetch(r1, m0 + 1);
-            fetch(r2, m0 + 2);
-            fetch(r3, m0 + 3);
-            put(r0, 0);
-            fetch(r0, m0 + 4);
-            __syncthreads();
-            // iteration x: store chunk x+1 into the buffer the consumers do
-            // not read and fetch chunk x+5 into the same set; past the last
-            // chunk the stores go to the idle buffer and are never read
-            for (int x = 0; x < count; x += 4) {
-                put(r1, 1);
-                fetch(r1, m0 + x + 5);
-                __syncthreads();
-                if (x + 1 >= count) break;
-                put(r2, 0);
-                fetch(r2, m0 + x + 6);
-                __syncthreads();
-                if (x + 2 >= count) break;
-                put(r3, 1);
-                fetch(r3, m0 + x + 7);
-                __syncthreads();
-                if (x + 3 >= count) break;
-                put(r0, 0);
-                fetch(r0, m0 + x + 8);
+#pragma unroll
+        for (int k = 0; k < NSET; ++k) fetch(r[k], m0 + k);
+        put(r[0], 0);
+        fetch(r[0], m0 + NSET);
+        put(r[1], 1);
+        fetch(r[1], m0 + NSET + 1);
+        __syncthreads();
+        // iteration x: store chunk x+2 into the buffer freed by chunk x-1 and
+        // fetch chunk x+2+NSET into the same set; past the last chunk the
+        // stores go to buffers that are never read again.  Whole rounds of
+        // NSET iterations run without an early exit, so every path into the
+        // loop header has the same loads in flight and the compiler's waits
+        // cover only the set being stored.
+        int x = 0;
+        for (; x + NSET <= count; x += NSET) {
+#pragma unroll
+            for (int k = 0; k < NSET; ++k) {
+                put(r[(k + 2) % NSET], (k + 2) % 3);
+                fetch(r[(k + 2) % NSET], m0 + x + k + 2 + NSET);
                 __syncthreads();
             }
-        } else {
-            // two register sets (wider tiles: fewer loader waves, more units
-            // each), chunk j in set j % 2 for two iterations
-            u32x4 r0[NPL], r1[NPL];
-            fetch(r0, m0);
-            fetch(r1, m0 + 1);
-            put(r0, 0);
-            fetch(r0, m0 + 2);
-            __syncthreads();
-            for (int x = 0; x < count; x += 2) {
-                put(r1, 1);
-                fetch(r1, m0 + x + 3);
-                __syncthreads();
-                if (x + 1 >= count) break;
-                put(r0, 0);
-                fetch(r0, m0 + x + 4);
+        }
+#pragma unroll
+        for (int k = 0; k < NSET - 1; ++k) {    // the remaining count - x < NSET iterations
+            if (x + k < count) {
+                put(r[(k + 2) % NSET], (k + 2) % 3);
                 __syncthreads();
             }
         }
@@ -613,7 +625,21 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
     }
 
     const int vrow = H * DV;
+    // buffer resource over the outputs of chunk m of this tile; rows past
+    // the end of the sequence fall outside it and are dropped
+    auto out_rsrc = [&](int m) {
+        const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
+        const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
+        return rsrc(o + (c0 * H + h) * DV + j0, 2u * static_cast<uint32_t>((len - 1) * vrow + TV));
+    };
     if (wave < NC) {
+        // O of chunk m, written by this slab's output wave into xob[b]
+        auto store_o = [&](int m, int b) {
+            const __amdgpu_buffer_rsrc_t ro = out_rsrc(m);
+#pragma unroll
+            for (int I = 0; I < 4; ++I)
+                st64(ro, 2 * ((16 * I + ln) * vrow + 16 * wave + 4 * g), xob[b][wave][I][lane]);
+        };
         // ======================= state waves =======================
         // fp32 state slab in the accumulator layout:
         // S[m][i] = state[c = 16m + 4g + i][j = j0 + wave * 16 + ln]
@@ -625,44 +651,51 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             for (int i = 0; i < 4; ++i)
                 S[m][i] = s_in ? s_in[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] : 0.f;
         __syncthreads();
-        for (int x = 0; x < count; ++x) {
-            const u32x4* F = buf[x & 1];
-            // fragments read one stage ahead (scheduling barriers keep the
-            // order); independent accumulators interleave
-            const u32x2* U = reinterpret_cast<const u32x2*>(F + kOffU / 16) + wave * 4 * 64;
-            const float* gam = reinterpret_cast<const float*>(F + kOffGam / 16);
-            u32x4 wf[16];
-            u32x2 uw[4];
+        // W of chunk x is read during iteration x-1 (chunk x is staged by
+        // then); the other fragments one stage ahead within the iteration
+        // (scheduling barriers keep the order); independent accumulators
+        // interleave
+        u32x4 wf[16];
 #pragma unroll
-            for (int f = 0; f < 16; ++f) wf[f] = F[(kFragW + f) * 64 + lane];
+        for (int f = 0; f < 16; ++f) wf[f] = buf[0][f * 64 + lane];
+        int bx = 0;                              // x % 3
+        for (int x = 0; x < count; ++x) {
+            const u32x4* F = buf[bx];
+            const int bn = bx == 2 ? 0 : bx + 1;
+            const u32x2* U = reinterpret_cast<const u32x2*>(F + (kOffU - kStageOff) / 16) + wave * 4 * 64;
+            const float* gam = reinterpret_cast<const float*>(F + (kOffGam - kStageOff) / 16);
+            u32x2 uw[4];
+            f32x4 gm[8];
 #pragma unroll
             for (int I = 0; I < 4; ++I) uw[I] = U[I * 64 + lane];
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
             u32x4 sb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
-            __builtin_amdgcn_sched_barrier(0);
-
-            // ---- E = U - W S0 (reads of Kd^T and e^{G} in flight)
-            u32x4 kf[16];
-            f32x4 gm[8];
-#pragma unroll
-            for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK + f) * 64 + lane];
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
+            // E = U + (-W) S0, accumulated from U: the MFMAs leave E itself
             f32x4 y[4];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) y[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int I = 0; I < 4; ++I)
+                y[I] = f32x4{lo_bf(uw[I][0]), hi_bf(uw[I][0]), lo_bf(uw[I][1]), hi_bf(uw[I][1])};
+            __builtin_amdgcn_sched_barrier(0);
+
+            // ---- E (4 independent chains), with Diag(e^{G}) S0 formed meanwhile
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int I = 0; I < 4; ++I) y[I] = mma32(wf[4 * I + kk], sb[kk], y[I]);
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) S[mm] = gm[mm] * S[mm];
+            u32x4 kf[16];
+#pragma unroll
+            for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int f = 0; f < 16; ++f) wf[f] = buf[bn][f * 64 + lane];   // -W of chunk x+1
             u32x2 eb[4];
 #pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const f32x4 e = {lo_bf(uw[I][0]) - y[I][0], hi_bf(uw[I][0]) - y[I][1],
-                                 lo_bf(uw[I][1]) - y[I][2], hi_bf(uw[I][1]) - y[I][3]};
-                eb[I] = pack2(e);
-            }
+            for (int I = 0; I < 4; ++I) eb[I] = pack2(y[I]);
             const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
             // hand S0 and E of this chunk to the output wave
 #pragma unroll
@@ -673,11 +706,14 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
 
             // ---- S = Diag(e^{G}) S0 + Kd^T E
 #pragma unroll
-            for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm], e01, gm[mm] * S[mm]);
+            for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm], e01, S[mm]);
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm + 1], e23, S[mm]);
+            if (x >= 2) store_o(c_lo + x - 2, x & 1);
             __syncthreads();
+            bx = bn;
         }
+        if (count >= 2) store_o(c_lo + count - 2, count & 1);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -691,54 +727,74 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
     // and P fragments copied in iteration x-1 and the state wave's handover;
     // rows past the end of the sequence are dropped by the range check
     const int sl = wave - NC;                   // slab
-    const int jc = sl * 16 + ln;
-    auto out_chunk = [&](int m, const u32x4* qf, const u32x4* pf, int b) {
-        const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
-        const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
-        const __amdgpu_buffer_rsrc_t ro = rsrc(o + (c0 * H + h) * DV + j0,
-                                               2u * static_cast<uint32_t>((len - 1) * vrow + TV));
+    auto out_chunk = [&](int m, const u32x4* qf, const u32x4* pf, int b, bool direct) {
         u32x4 sb[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) sb[kk] = xsb[b][sl][kk][lane];
         const u32x4 e01 = cat(xeb[b][sl][0][lane], xeb[b][sl][1][lane]);
         const u32x4 e23 = cat(xeb[b][sl][2][lane], xeb[b][sl][3][lane]);
+        // O^T = S0^T Qg^T + E^T P^T: the same fragments with the operands
+        // swapped (an A-operand lane layout is the transpose of a B-operand
+        // one), so lane (g, ln) gets O[16I + ln][16 sl + 4g + i] and stores
+        // four adjacent columns of one token row at once
         f32x4 oc[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) oc[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int I = 0; I < 4; ++I) oc[I] = mma32(qf[4 * I + kk], sb[kk], oc[I]);
+            for (int I = 0; I < 4; ++I) oc[I] = mma32(sb[kk], qf[4 * I + kk], oc[I]);
 #pragma unroll
-        for (int I = 0; I < 4; ++I) oc[I] = mma32(pf[p_frag(I, 0)], e01, oc[I]);
-        oc[2] = mma32(pf[p_frag(2, 1)], e23, oc[2]);
-        oc[3] = mma32(pf[p_frag(3, 1)], e23, oc[3]);
+        for (int I = 0; I < 4; ++I) oc[I] = mma32(e01, pf[p_frag(I, 0)], oc[I]);
+        oc[2] = mma32(e23, pf[p_frag(2, 1)], oc[2]);
+        oc[3] = mma32(e23, pf[p_frag(3, 1)], oc[3]);
+        if (direct) {
+            const __amdgpu_buffer_rsrc_t ro = out_rsrc(m);
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+            for (int I = 0; I < 4; ++I)
+                st64(ro, 2 * ((16 * I + ln) * vrow + 16 * sl + 4 * g), pack2(scale * oc[I]));
+        } else {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * oc[I][i]));
+            for (int I = 0; I < 4; ++I) xob[b][sl][I][lane] = pack2(scale * oc[I]);
+        }
     };
-    auto copy_qp = [&](u32x4* qf, u32x4* pf, int b) {
+    // Qg and P come from the slot straight into registers, two iterations
+    // before they are used: set a holds the block's even chunks, set b the
+    // odd ones (loads past the last chunk re-read it and are never used)
+    auto load_qp = [&](u32x4* qf, u32x4* pf, int m) {
+        const uint8_t* s = slot_of(min(m, c_lo + count - 1)) + lane * 16;
 #pragma unroll
-        for (int f = 0; f < 16; ++f) qf[f] = buf[b][(kFragQ + f) * 64 + lane];
+        for (int f = 0; f < 16; ++f) qf[f] = *reinterpret_cast<const u32x4*>(s + (kFragQ + f) * kFrag);
 #pragma unroll
-        for (int f = 0; f < 6; ++f) pf[f] = buf[b][(kFragP + f) * 64 + lane];
+        for (int f = 0; f < 6; ++f) pf[f] = *reinterpret_cast<const u32x4*>(s + (kFragP + f) * kFrag);
     };
     u32x4 qa[16], pa[6], qb[16], pb[6];
+    load_qp(qa, pa, c_lo);
+    load_qp(qb, pb, c_lo + 1);
     __syncthreads();
-    for (int x = 0; x < count; x += 2) {
-        copy_qp(qa, pa, 0);                             // chunk x
-        if (x >= 1) out_chunk(c_lo + x - 1, qb, pb, 1);
+    __syncthreads();                            // iteration 0 has no output
+    // iteration x >= 1: O of chunk x-1, whose handover the state wave wrote
+    // in iteration x-1, then the loads of chunk x+1 into the set just used.
+    // Two iterations per trip and no early exit: every path into the loop
+    // header has the same loads in flight, so the compiler's waits cover
+    // only the set being consumed.
+    int x = 1;
+    for (; x + 1 < count; x += 2) {
+        out_chunk(c_lo + x - 1, qa, pa, 0, false);
+        load_qp(qa, pa, c_lo + x + 1);
         __syncthreads();
-        if (x + 1 >= count) break;
-        copy_qp(qb, pb, 1);                             // chunk x+1
-        out_chunk(c_lo + x, qa, pa, 0);
+        out_chunk(c_lo + x, qb, pb, 1, false);
+        load_qp(qb, pb, c_lo + x + 2);
         __syncthreads();
     }
-    // the last chunk: its handover was written before the final barrier
-    if (count & 1) out_chunk(c_lo + count - 1, qa, pa, 0);
-    else out_chunk(c_lo + count - 1, qb, pb, 1);
+    if (x < count) {                            // iteration count-1 (even chunk count-2)
+        out_chunk(c_lo + x - 1, qa, pa, 0, false);
+        __syncthreads();
+    }
+    // the last chunk: its handover was written before the final barrier;
+    // its O is stored here (the state wave stores the one before it)
+    if ((count - 1) & 1) out_chunk(c_lo + count - 1, qb, pb, 1, true);
+    else out_chunk(c_lo + count - 1, qa, pa, 0, true);
 }
 
 // ===================================================================
