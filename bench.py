@@ -11,7 +11,11 @@ on the library's stream.  The decode figures (sequence-steps/s and state
 GB/s) are reported beside it.  ``roofline`` is the prefill against MI355X
 HBM (8 TB/s): algorithmic bytes per call = 1540 B per head-token (bf16 q, k,
 v, o; fp32 log_alpha; fp32 beta) plus the final states, over the measured
-call time.  For this workload (32 (sequence, head) pairs) the library takes
+call time; d2d_copy_GBps is a 2 GiB device-to-device copy (the runtime's
+copy kernel) measured in the same process, a reference point rather than an
+upper bound (the decode kernel streams faster), and mfma_busy_pct the
+rocprofv3 MfmaUtil of each kernel from the committed counter summary.  For this workload (32 (sequence,
+head) pairs) the library takes
 its two-pass path: one call enqueues, per block of chunks, a prep kernel
 (chunk-parallel) and a carry kernel (the serial state walk); the roofline
 covers the whole call, and the rocprofv3 summary splits it per kernel.
@@ -60,11 +64,12 @@ def source_digest(names):
     return h.hexdigest()[:16]
 
 
-def load_traffic(kernel_file, digest):
-    """HBM traffic per launch (bytes read + written beyond L2, from rocprofv3
-    FETCH_SIZE and WRITE_SIZE scaled by a device copy's readings) from the
-    committed counter summary, if it was taken on the current kernel
-    source; else None."""
+def load_counters(kernel_file, digest, key="bytes_per_launch"):
+    """A figure from the committed rocprofv3 counter summary
+    (profiles/traffic.json), if it was taken on the current kernel source;
+    else None.  bytes_per_launch: HBM traffic (bytes read + written beyond
+    L2, FETCH_SIZE and WRITE_SIZE scaled by a device copy's readings);
+    mfma: MfmaUtil (busy %) and MfmaFlopsBF16 per kernel."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -72,7 +77,26 @@ def load_traffic(kernel_file, digest):
         rec = json.load(f).get(kernel_file)
     if not rec or rec.get("source_digest") != digest:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(key)
+
+
+def copy_rate_gbps(torch, nbytes=2 << 30, reps=5):
+    """GB/s of a device-to-device copy of nbytes (read + write counted; the
+    runtime's copy kernel), best of reps, timed with HIP events."""
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1))
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (best * 1e-3) / 1e9
 
 
 def main():
@@ -149,8 +173,10 @@ def main():
     dec_gbps = dec_bytes / (dec_step_us * 1e-6) / 1e9
 
     digest = source_digest(["prefill_wy.hip", "kda_mfma.h", "kda_device.h", "kda_sched.h"])
-    traffic = load_traffic("prefill_wy.hip", digest)
-    dec_traffic = load_traffic("decode.hip", source_digest(["decode.hip", "kda_device.h"]))
+    traffic = load_counters("prefill_wy.hip", digest)
+    mfma = load_counters("prefill_wy.hip", digest, "mfma")
+    dec_traffic = load_counters("decode.hip", source_digest(["decode.hip", "kda_device.h"]))
+    copy_gbps = copy_rate_gbps(torch)
 
     result = {
         "metric": "KDA prefill tokens/s (H=32,d=128) + decode state GB/s, % of MI355X roofline",
@@ -174,11 +200,15 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": PREFILL_KERNELS, "unit_of_launch": "one kda_fwd_prefill call",
                      "algorithmic_bytes_per_launch": alg_bytes,
+                     "d2d_copy_GBps": copy_gbps,
+                     "frac_of_d2d_copy": achieved / copy_gbps,
                      "mfma_useful_frac_c64": flops_c64 / (pre_avg * 1e-3) / 1e12
-                     / MFMA_BF16_PEAK_TFLOPS},
+                     / MFMA_BF16_PEAK_TFLOPS,
+                     "mfma_busy_pct": mfma},
         "decode": {"workload": "decode_n256", "us_per_step": dec_step_us,
                    "seq_steps_per_s": wd.N / (dec_step_us * 1e-6),
                    "state_GBps": dec_gbps, "frac_of_hbm_peak": dec_gbps / HBM_PEAK_GBPS,
+                   "frac_of_d2d_copy": dec_gbps / copy_gbps,
                    "algorithmic_bytes_per_step": dec_bytes, "traffic_per_step": dec_traffic,
                    "kernel": DECODE_KERNEL},
         "cpu_baseline": None,
