@@ -20,6 +20,10 @@ its two-pass path: one call enqueues, per block of chunks, a prep kernel
 (chunk-parallel) and a carry kernel (the serial state walk); the roofline
 covers the whole call, and the rocprofv3 summary splits it per kernel.
 
+gate_variants: the same prefill as Gated DeltaNet (one gate per (token,
+head), 1032 B per head-token) and DeltaNet (no gate, 1028 B), timed the
+same way, each against the HBM peak.
+
 cpu_baseline: the fp64 oracle on a bounded sample of the same workload (a
 few heads over the first tokens), on the host's cores, scaled to tokens/s of
 the full 32-head layer.  It doubles as a parity spot check of those outputs.
@@ -172,6 +176,33 @@ def main():
     dec_bytes = DECODE_BYTES_PER_HS * wd.N * wd.H
     dec_gbps = dec_bytes / (dec_step_us * 1e-6) / 1e9
 
+    # ---------------- gate variants on the same workload ------------------
+    # Gated DeltaNet (one gate per (token, head)) and DeltaNet (no gate):
+    # the prefill without the fp32 per-channel gate, timed the same way
+    variants = {}
+    head_gate = gen.gates((T, H), 7, dev, wp.gate).contiguous()
+    for name, la, gate, bpht in (("gated_deltanet", head_gate, "head", PREFILL_BYTES_PER_HT - 512 + 4),
+                                 ("deltanet", None, "none", PREFILL_BYTES_PER_HT - 512)):
+        def run_v():
+            kda.prefill(inp["q"], inp["k"], inp["v"], la, inp["beta"], cu_seqlens=inp["cu_seqlens"],
+                        out=o, final_state=hT, workspace=ws, gate=gate)
+        for _ in range(args.warmup):
+            run_v()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a0, a1 in evs:
+            a0.record(stream)
+            run_v()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        v_ms = sum(a0.elapsed_time(a1) for a0, a1 in evs) / len(evs)
+        v_bytes = bpht * T * H + hT.numel() * 4
+        variants[name] = {"gate": gate, "prefill_ms": v_ms, "tokens_per_s": T / (v_ms * 1e-3),
+                          "algorithmic_bytes_per_head_token": bpht,
+                          "achieved_GBps": v_bytes / (v_ms * 1e-3) / 1e9,
+                          "frac_of_hbm_peak": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del head_gate
+
     digest = source_digest(["prefill_wy.hip", "kda_mfma.h", "kda_device.h", "kda_sched.h"])
     traffic = load_counters("prefill_wy.hip", digest)
     mfma = load_counters("prefill_wy.hip", digest, "mfma")
@@ -211,6 +242,7 @@ def main():
                    "frac_of_d2d_copy": dec_gbps / copy_gbps,
                    "algorithmic_bytes_per_step": dec_bytes, "traffic_per_step": dec_traffic,
                    "kernel": DECODE_KERNEL},
+        "gate_variants": variants,
         "cpu_baseline": None,
     }
 

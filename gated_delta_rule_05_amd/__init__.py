@@ -13,6 +13,10 @@ GPU, the calls raise.
 Operation: the per-key-channel gated delta rule of "Kimi Delta Attention: la
 atencion lineal detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi
 Delta Attention paso a paso"; the scale defaults to 1/sqrt(d_k) as there.
+gate="head" takes log_alpha [.., H] (Gated DeltaNet: one scalar gate per
+head, "Cos'è Kimi Delta Attention (KDA)?", section "Gating per canale: cosa
+rende KDA diverso"); gate="none" takes no gate (DeltaNet, alpha = 1).
+decode_step(state_index=...) updates states held in slots of a larger pool.
 """
 from __future__ import annotations
 
@@ -21,7 +25,8 @@ import math
 import os
 
 __all__ = [
-    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "PrefillOptions", "library_path", "load_library",
+    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "GATES", "PrefillOptions",
+    "DecodeOptions", "library_path", "load_library",
     "abi_version", "status_string", "prefill_options", "prefill_workspace_bytes", "prefill",
     "decode_step", "EXPORTED_SYMBOLS",
 ]
@@ -36,17 +41,25 @@ STATUS = {
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
 PATHS = {"auto": 0, "vector": 1, "matrix": 2, "two_pass": 3}
+GATES = {"channel": 0, "head": 1, "none": 2}
 
 
 class PrefillOptions(ctypes.Structure):
     """Mirror of kda_prefill_options."""
     _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32),
-                ("block_chunks", ctypes.c_int32)]
+                ("block_chunks", ctypes.c_int32), ("gate", ctypes.c_int32)]
+
+
+class DecodeOptions(ctypes.Structure):
+    """Mirror of kda_decode_options."""
+    _fields_ = [("gate", ctypes.c_int32), ("num_states", ctypes.c_int32),
+                ("state_index", ctypes.c_void_p)]
 
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
                     "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill_workspace_bytes_ex",
-                    "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step")
+                    "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step",
+                    "kda_decode_step_ex")
 
 
 class KDAError(RuntimeError):
@@ -93,6 +106,9 @@ def load_library():
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
+    lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
+                                       vp, ctypes.POINTER(DecodeOptions), vp]
+    lib.kda_decode_step_ex.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -105,16 +121,22 @@ def status_string(status: int) -> str:
     return load_library().kda_status_string(int(status)).decode()
 
 
-def prefill_options(path="auto", value_tiles=0, block_chunks=0) -> PrefillOptions:
+def _gate_code(gate):
+    if gate not in GATES:
+        raise ValueError("gate must be one of %s" % sorted(GATES))
+    return GATES[gate]
+
+
+def prefill_options(path="auto", value_tiles=0, block_chunks=0, gate="channel") -> PrefillOptions:
     if path not in PATHS:
         raise ValueError("path must be one of %s" % sorted(PATHS))
-    return PrefillOptions(PATHS[path], int(value_tiles), int(block_chunks))
+    return PrefillOptions(PATHS[path], int(value_tiles), int(block_chunks), _gate_code(gate))
 
 
 def prefill_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
                             dtype: int = DTYPE_BF16, path="auto", value_tiles=0,
-                            block_chunks=0) -> int:
-    opts = prefill_options(path, value_tiles, block_chunks)
+                            block_chunks=0, gate="channel") -> int:
+    opts = prefill_options(path, value_tiles, block_chunks, gate)
     return int(load_library().kda_fwd_prefill_workspace_bytes_ex(
         total_T, N, H, d_k, d_v, dtype, ctypes.byref(opts)))
 
@@ -155,13 +177,26 @@ def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
+def _check_gate(log_alpha, gate, lead, dk, dev):
+    """log_alpha for a gate layout: [*lead, d_k] (channel), [*lead] (head),
+    ignored (none; may be None)."""
+    torch = _torch()
+    code = _gate_code(gate)
+    if code == GATES["none"]:
+        return None, code
+    shape = tuple(lead) + ((dk,) if code == GATES["channel"] else ())
+    _check(log_alpha, "log_alpha", shape, torch.float32, dev)
+    return log_alpha, code
+
+
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
-            block_chunks=0):
+            block_chunks=0, gate="channel"):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
-    log_alpha: [T, H, d_k] fp32; beta: [T, H] fp32; h0: [N, H, d_k, d_v] fp32
+    log_alpha: [T, H, d_k] fp32 (gate="channel"), [T, H] fp32 (gate="head")
+    or None (gate="none"); beta: [T, H] fp32; h0: [N, H, d_k, d_v] fp32
     or None (zeros); cu_seqlens: int32 [N+1] on the device, or None for one
     sequence of length T.  Returns (o [T, H, d_v] in the input dtype,
     hT [N, H, d_k, d_v] fp32 or None when final_state is False).
@@ -183,7 +218,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     _check(q, "q", (T, H, dk), dt, dev)
     _check(k, "k", (T, H, dk), dt, dev)
     _check(v, "v", (T, H, dv), dt, dev)
-    _check(log_alpha, "log_alpha", (T, H, dk), torch.float32, dev)
+    log_alpha, _ = _check_gate(log_alpha, gate, (T, H), dk, dev)
     _check(beta, "beta", (T, H), torch.float32, dev)
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
@@ -206,7 +241,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     else:
         hT = final_state
         _check(hT, "final_state", (N, H, dk, dv), torch.float32, dev)
-    opts = prefill_options(path, value_tiles, block_chunks)
+    opts = prefill_options(path, value_tiles, block_chunks, gate)
     need = lib.kda_fwd_prefill_workspace_bytes_ex(T, N, H, dk, dv, code, ctypes.byref(opts))
     if workspace is None:
         workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)
@@ -219,10 +254,15 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     return out, hT
 
 
-def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None):
+def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel",
+                state_index=None):
     """One decode step.  q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32);
-    log_alpha: [N, H, d_k] fp32; beta: [N, H] fp32; S: [N, H, d_k, d_v] fp32,
-    updated in place.  Returns o [N, H, d_v] in the input dtype."""
+    log_alpha: [N, H, d_k] fp32 (gate="channel"), [N, H] (gate="head") or
+    None (gate="none"); beta: [N, H] fp32; S: [N, H, d_k, d_v] fp32, updated
+    in place.  With state_index (int32 [N] on the device) S is a pool
+    [num_states, H, d_k, d_v] and sequence n updates S[state_index[n]];
+    an index outside the pool skips that sequence (its o is not written).
+    Returns o [N, H, d_v] in the input dtype."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3:
@@ -237,18 +277,27 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None):
     _check(q, "q", (N, H, dk), dt, dev)
     _check(k, "k", (N, H, dk), dt, dev)
     _check(v, "v", (N, H, dv), dt, dev)
-    _check(log_alpha, "log_alpha", (N, H, dk), torch.float32, dev)
+    log_alpha, gcode = _check_gate(log_alpha, gate, (N, H), dk, dev)
     _check(beta, "beta", (N, H), torch.float32, dev)
-    _check(S, "S", (N, H, dk, dv), torch.float32, dev)
+    if state_index is None:
+        _check(S, "S", (N, H, dk, dv), torch.float32, dev)
+        nstates = N
+    else:
+        _check(state_index, "state_index", (N,), torch.int32, dev)
+        if S.dim() != 4:
+            raise ValueError("S must be [num_states, H, d_k, d_v]")
+        nstates = S.shape[0]
+        _check(S, "S", (nstates, H, dk, dv), torch.float32, dev)
     if scale is None:
         scale = 1.0 / math.sqrt(dk)
     if out is None:
         out = torch.empty((N, H, dv), dtype=dt, device=dev)
     else:
         _check(out, "out", (N, H, dv), dt, dev)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
-                             _ptr(S), N, H, dk, dv, code, float(scale), _ptr(out),
-                             _stream(dev))
+    opts = DecodeOptions(gcode, nstates, None if state_index is None else state_index.data_ptr())
+    st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                _ptr(S), N, H, dk, dv, code, float(scale), _ptr(out),
+                                ctypes.byref(opts), _stream(dev))
     if st != 0:
-        raise KDAError(st, "kda_decode_step")
+        raise KDAError(st, "kda_decode_step_ex")
     return out

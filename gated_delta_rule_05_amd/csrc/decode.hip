@@ -43,12 +43,13 @@ struct DecodeShape {
 
 constexpr int kDecodeGrid = 256;   // persistent work-groups (one per compute unit)
 
-template <typename T, int DK, int DV>
+template <typename T, int DK, int DV, int GATE, bool INDEXED>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NWV * 64))
 void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                         const T* __restrict__ v, const float* __restrict__ log_alpha,
                         const float* __restrict__ beta, float* __restrict__ S,
-                        T* __restrict__ o, float scale, int64_t nheads)
+                        T* __restrict__ o, float scale, int64_t nheads, int H,
+                        const int32_t* __restrict__ state_index, int num_states)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NWV = Sh::NWV, ITERS = Sh::ITERS;
@@ -59,29 +60,48 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
     const int lane = threadIdx.x & 63;
     const int cl = lane % LPR;                // 4 columns: 4cl .. 4cl+3
     const int row0 = wave * (ITERS * RPI) + lane / LPR;
-    auto state = [&](int64_t nh, int it) { return S + nh * (DK * DV) + (row0 + it * RPI) * DV + 4 * cl; };
+    // head nh = (sequence n, head h) keeps its state in slot state_index[n]
+    // (or n); a slot outside [0, num_states) marks a skipped sequence, whose
+    // loads read slot 0 and whose results are dropped
+    auto slot = [&](int64_t nh) -> int64_t {
+        if constexpr (!INDEXED) return nh;
+        const int64_t n = nh / H;
+        const int32_t x = state_index[n];
+        return x >= 0 && x < num_states ? static_cast<int64_t>(x) * H + (nh - n * H) : -1;
+    };
+    auto state = [&](int64_t sh, int it) {
+        return S + (sh < 0 ? 0 : sh) * (DK * DV) + (row0 + it * RPI) * DV + 4 * cl;
+    };
 
     int64_t nh = blockIdx.x;
     if (nh >= nheads) return;
     f32x4 s[ITERS], sn[ITERS];
+    int64_t sh = slot(nh);
 #pragma unroll
-    for (int it = 0; it < ITERS; ++it) s[it] = load_stream4(state(nh, it));
+    for (int it = 0; it < ITERS; ++it) s[it] = load_stream4(state(sh, it));
     for (int par = 0; nh < nheads; nh += gridDim.x, par ^= 1) {
         // next head's state (this head again past the end: same data, never stored)
         const int64_t nn = nh + gridDim.x < nheads ? nh + gridDim.x : nh;
+        const int64_t shn = slot(nn);
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it) sn[it] = load_stream4(state(nn, it));
+        for (int it = 0; it < ITERS; ++it) sn[it] = load_stream4(state(shn, it));
 
         const T* qp = q + nh * DK;
         const T* kp = k + nh * DK;
-        const float* lap = log_alpha + nh * DK;
+        // the gate of key channel r: its own (KDA), the head's (Gated
+        // DeltaNet) or none (DeltaNet: alpha = 1)
+        const float la_head = GATE == kGateHead && log_alpha ? log_alpha[nh] : 0.f;
+        auto la_of = [&](int r) {
+            if constexpr (GATE == kGateChannel) return log_alpha[nh * DK + r];
+            else return la_head;
+        };
         f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
         float kq = 0.f;
         float kr[ITERS];
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
             const int r = row0 + it * RPI;
-            const float a = gate_exp(lap[r]);
+            const float a = gate_exp(la_of(r));
             const float kv = elem<T>::load(kp + r);
             const float qv = elem<T>::load(qp + r);
             kr[it] = kv;
@@ -122,29 +142,45 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
         const float4 vv = elem<T>::load4(v + nh * DV + 4 * cl);
         const f32x4 e = {b * (vv.x - rk[0]), b * (vv.y - rk[1]), b * (vv.z - rk[2]),
                          b * (vv.w - rk[3])};
-        if (wave == 0 && lane < LPR) {
-            const f32x4 oo = scale * (rq + kq * e);
-            elem<T>::store4(o + nh * DV + 4 * cl, make_float4(oo[0], oo[1], oo[2], oo[3]));
+        if (!INDEXED || sh >= 0) {
+            if (wave == 0 && lane < LPR) {
+                const f32x4 oo = scale * (rq + kq * e);
+                elem<T>::store4(o + nh * DV + 4 * cl, make_float4(oo[0], oo[1], oo[2], oo[3]));
+            }
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) store_stream4(state(sh, it), s[it] + kr[it] * e);
         }
 #pragma unroll
-        for (int it = 0; it < ITERS; ++it) store_stream4(state(nh, it), s[it] + kr[it] * e);
-#pragma unroll
         for (int it = 0; it < ITERS; ++it) s[it] = sn[it];
+        sh = shn;
     }
 }
 
-template <typename T, int DK, int DV>
-static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+template <typename T, int DK, int DV, int GATE, bool INDEXED>
+static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
     constexpr int threads = DecodeShape<DK, DV>::NWV * 64;
     const int64_t nheads = static_cast<int64_t>(a.N) * a.H;
     // persistent grid; small states (one wave each) get more work-groups
     const int64_t grid = std::min<int64_t>(nheads, kDecodeGrid * (threads == 64 ? 4 : 1));
-    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV>), dim3(static_cast<unsigned>(grid)),
+    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV, GATE, INDEXED>), dim3(static_cast<unsigned>(grid)),
                        dim3(threads), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.log_alpha, a.beta, a.S,
-                       static_cast<T*>(a.o), a.scale, nheads);
+                       static_cast<T*>(a.o), a.scale, nheads, a.H, a.state_index,
+                       a.num_states);
     return hipGetLastError();
+}
+
+template <typename T, int DK, int DV>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+    // a per-head gate and no gate share one instantiation (no gate: a null
+    // log_alpha, read as zero)
+    const bool ch = a.gate == kGateChannel;
+    if (a.state_index)
+        return ch ? launch_decode_g<T, DK, DV, kGateChannel, true>(a, stream)
+                  : launch_decode_g<T, DK, DV, kGateHead, true>(a, stream);
+    return ch ? launch_decode_g<T, DK, DV, kGateChannel, false>(a, stream)
+              : launch_decode_g<T, DK, DV, kGateHead, false>(a, stream);
 }
 
 template <typename T, int DK>

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -58,14 +58,18 @@ struct Sizes {
 };
 
 int check_sizes(int64_t tokens, int64_t N, int64_t H, int32_t d_k, int32_t d_v, int32_t dtype,
-                Sizes* sz) {
+                int32_t gate, Sizes* sz) {
     if (N < 1 || H < 1 || tokens < 0) return KDA_STATUS_INVALID_ARGUMENT;
+    if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_HEAD && gate != KDA_GATE_NONE)
+        return KDA_STATUS_INVALID_ARGUMENT;
     if (dtype != KDA_DTYPE_BF16 && dtype != KDA_DTYPE_F32) return KDA_STATUS_UNSUPPORTED;
     if (!supported_dim(d_k) || !supported_dim(d_v)) return KDA_STATUS_UNSUPPORTED;
     const int64_t esz = dtype == KDA_DTYPE_F32 ? 4 : 2;
     int64_t th, x;
     if (!mul_ok(tokens, H, &th)) return KDA_STATUS_INVALID_ARGUMENT;
     if (!mul_ok(th, d_k, &x) || !mul_ok(x, 4, &sz->la_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (gate == KDA_GATE_HEAD) sz->la_bytes = th * 4;
+    if (gate == KDA_GATE_NONE) sz->la_bytes = 0;
     if (!mul_ok(th, d_k, &x) || !mul_ok(x, esz, &sz->qk_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
     if (!mul_ok(th, d_v, &x) || !mul_ok(x, esz, &sz->v_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
     if (!mul_ok(th, 4, &sz->beta_bytes)) return KDA_STATUS_INVALID_ARGUMENT;
@@ -76,8 +80,20 @@ int check_sizes(int64_t tokens, int64_t N, int64_t H, int32_t d_k, int32_t d_v, 
     // keep every byte count (and the largest launch grid) far from int64 and
     // 32-bit grid limits: 2^31 work-groups at most, 2^62 bytes at most
     if (nh > (int64_t{1} << 27)) return KDA_STATUS_INVALID_ARGUMENT;
-    if (sz->la_bytes > (int64_t{1} << 62) || sz->state_bytes > (int64_t{1} << 62))
+    if (!mul_ok(th, d_k, &x) || !mul_ok(x, 4, &x) || x > (int64_t{1} << 62))
         return KDA_STATUS_INVALID_ARGUMENT;
+    if (sz->state_bytes > (int64_t{1} << 62))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    return KDA_STATUS_OK;
+}
+
+// log_alpha is required unless the call has no gate; a per-channel gate is
+// vector-loaded (16 bytes), a per-head gate read as scalars (4 bytes)
+int check_gate_ptr(int32_t gate, const float* log_alpha, bool needed) {
+    if (gate == KDA_GATE_NONE || !needed) return KDA_STATUS_OK;
+    if (!log_alpha) return KDA_STATUS_INVALID_ARGUMENT;
+    if (gate == KDA_GATE_CHANNEL ? !aligned16(log_alpha) : !aligned4(log_alpha))
+        return KDA_STATUS_MISALIGNED;
     return KDA_STATUS_OK;
 }
 
@@ -156,7 +172,9 @@ size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H,
                                           int32_t d_v, int32_t dtype,
                                           const kda_prefill_options* options) {
     Sizes sz;
-    if (check_sizes(total_T, N, H, d_k, d_v, dtype, &sz) != KDA_STATUS_OK) return 0;
+    if (check_sizes(total_T, N, H, d_k, d_v, dtype, options ? options->gate : 0, &sz) !=
+        KDA_STATUS_OK)
+        return 0;
     Plan pl;
     if (resolve(total_T, N, H, d_k, d_v, dtype, options, &pl) != KDA_STATUS_OK) return 0;
     return pl.ws_bytes;
@@ -173,15 +191,18 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
                        int32_t dtype, float scale, void* o, float* hT, void* workspace,
                        size_t workspace_bytes, const kda_prefill_options* options,
                        void* stream) {
+    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
     Sizes sz;
-    const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, &sz);
+    const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, gate, &sz);
     if (st != KDA_STATUS_OK) return st;
     if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
     if (!cu_seqlens) return KDA_STATUS_INVALID_ARGUMENT;
-    if (total_T > 0 && (!q || !k || !v || !log_alpha || !beta || !o))
-        return KDA_STATUS_INVALID_ARGUMENT;
+    if (total_T > 0 && (!q || !k || !v || !beta || !o)) return KDA_STATUS_INVALID_ARGUMENT;
+    const int gs = check_gate_ptr(gate, log_alpha, total_T > 0);
+    if (gs != KDA_STATUS_OK) return gs;
+    if (gate == KDA_GATE_NONE) log_alpha = nullptr;   // never read
     // vector-loaded tensors need 16 bytes; beta and cu_seqlens are read as scalars
-    const void* ptrs[] = {q, k, v, log_alpha, h0, o, hT, workspace};
+    const void* ptrs[] = {q, k, v, h0, o, hT, workspace};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return KDA_STATUS_MISALIGNED;
     if (!aligned4(beta) || !aligned4(cu_seqlens)) return KDA_STATUS_MISALIGNED;
@@ -209,6 +230,7 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
         return KDA_STATUS_INVALID_ARGUMENT;
 
     kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
+    a.gate = gate;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
     a.order = static_cast<int32_t*>(workspace);
@@ -243,35 +265,55 @@ int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* lo
                               stream);
 }
 
-int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
-                    const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
-                    int32_t d_v, int32_t dtype, float scale, void* o, void* stream) {
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                       int32_t d_v, int32_t dtype, float scale, void* o,
+                       const kda_decode_options* options, void* stream) {
+    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
+    const int32_t* index = options ? options->state_index : nullptr;
+    const int32_t nstates = index ? options->num_states : N;
+    if (nstates < 1) return KDA_STATUS_INVALID_ARGUMENT;
     Sizes sz;
-    const int st = check_sizes(N, N, H, d_k, d_v, dtype, &sz);
+    const int st = check_sizes(N, N, H, d_k, d_v, dtype, gate, &sz);
     if (st != KDA_STATUS_OK) return st;
+    Sizes pool;   // the state pool: nstates states
+    if (check_sizes(0, nstates, H, d_k, d_v, dtype, gate, &pool) != KDA_STATUS_OK)
+        return KDA_STATUS_INVALID_ARGUMENT;
     if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
-    if (!q || !k || !v || !log_alpha || !beta || !S || !o) return KDA_STATUS_INVALID_ARGUMENT;
-    const void* ptrs[] = {q, k, v, log_alpha, S, o};
+    if (!q || !k || !v || !beta || !S || !o) return KDA_STATUS_INVALID_ARGUMENT;
+    const int gs = check_gate_ptr(gate, log_alpha, true);
+    if (gs != KDA_STATUS_OK) return gs;
+    if (gate == KDA_GATE_NONE) log_alpha = nullptr;   // never read
+    const void* ptrs[] = {q, k, v, S, o};
     for (const void* p : ptrs)
         if (!aligned16(p)) return KDA_STATUS_MISALIGNED;
-    if (!aligned4(beta)) return KDA_STATUS_MISALIGNED;
+    if (!aligned4(beta) || !aligned4(index)) return KDA_STATUS_MISALIGNED;
     const Range r_o = range_of(o, sz.v_bytes);
+    const Range r_S = range_of(S, pool.state_bytes);
     const Range others[] = {range_of(q, sz.qk_bytes),      range_of(k, sz.qk_bytes),
                             range_of(v, sz.v_bytes),       range_of(log_alpha, sz.la_bytes),
-                            range_of(beta, sz.beta_bytes), range_of(S, sz.state_bytes)};
+                            range_of(beta, sz.beta_bytes), range_of(index, index ? N * 4 : 0)};
     for (const Range& in : others)
-        if (overlaps(r_o, in)) return KDA_STATUS_INVALID_ARGUMENT;
-    for (int i = 0; i < 5; ++i)
-        if (overlaps(others[5], others[i])) return KDA_STATUS_INVALID_ARGUMENT;
+        if (overlaps(r_o, in) || overlaps(r_S, in)) return KDA_STATUS_INVALID_ARGUMENT;
+    if (overlaps(r_o, r_S)) return KDA_STATUS_INVALID_ARGUMENT;
 
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.S = S; a.o = o;
+    a.state_index = index; a.num_states = nstates;
     a.N = N; a.H = H; a.d_k = d_k; a.d_v = d_v;
+    a.gate = gate;
     a.dtype_f32 = dtype == KDA_DTYPE_F32;
     a.scale = scale;
     if (kda::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_STATUS_HIP_ERROR;
     return KDA_STATUS_OK;
+}
+
+int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,
+                    const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                    int32_t d_v, int32_t dtype, float scale, void* o, void* stream) {
+    return kda_decode_step_ex(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, scale, o,
+                              nullptr, stream);
 }
 
 }  // extern "C"

@@ -10,6 +10,10 @@
 
 namespace kda {
 
+// layout of log_alpha: one gate per key channel, one per (token, head)
+// shared by every channel, or none (alpha = 1; log_alpha not read)
+enum GateMode : int { kGateChannel = 0, kGateHead = 1, kGateNone = 2 };
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -18,7 +22,10 @@ struct DecodeArgs {
     const float* beta;
     float* S;
     void* o;
+    const int32_t* state_index;   // device [N] or null: sequence n uses S[state_index[n]]
+    int32_t num_states;           // states in S when state_index is set
     int32_t N, H, d_k, d_v;
+    int gate;                     // a GateMode
     bool dtype_f32;
     float scale;
 };
@@ -36,6 +43,7 @@ struct PrefillArgs {
     int32_t* order;             // device scratch [N]: sequences by length, longest first
     int64_t total_T;
     int32_t N, H, d_k, d_v;
+    int gate;                   // a GateMode
     bool dtype_f32;
     float scale;
 };

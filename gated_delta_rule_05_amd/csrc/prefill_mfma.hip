@@ -106,13 +106,20 @@ struct ChunkView {
 
 __device__ __forceinline__ ChunkView chunk_view(const bf16_t* k, const bf16_t* q,
                                                 const float* log_alpha, const float* beta,
-                                                int64_t c0, int len, int H, int h) {
+                                                int64_t c0, int len, int H, int h, int gate) {
     const int64_t e0 = (c0 * H + h) * DK;               // first element of row 0
     const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
     ChunkView cv;
     cv.k = rsrc(k + e0, 2u * span);
     cv.q = rsrc(q + e0, 2u * span);
-    cv.la = rsrc(log_alpha + e0, 4u * span);
+    // gates: per key channel, or one per (token, head); none at all (a null
+    // log_alpha) gives an empty range, where every load reads zero
+    if (gate == kGateChannel)
+        cv.la = rsrc(log_alpha + e0, 4u * span);
+    else if (log_alpha)
+        cv.la = rsrc(log_alpha + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
+    else
+        cv.la = rsrc(log_alpha, 0u);
     cv.beta = rsrc(beta + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
     return cv;
 }
@@ -124,6 +131,7 @@ struct StageRegs {
     u32x2 la[16];
 };
 
+template <int GATE>
 __device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, int H, int w,
                                           int lane) {
 #pragma unroll
@@ -131,7 +139,12 @@ __device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, in
         const int off = (16 * w + r) * H * DK + 2 * lane;   // elements
         rg.k2[r] = ld32(cv.k, 2 * off);
         rg.q2[r] = ld32(cv.q, 2 * off);
-        rg.la[r] = ld64(cv.la, 4 * off);
+        if constexpr (GATE == kGateChannel) {
+            rg.la[r] = ld64(cv.la, 4 * off);
+        } else {                                           // the row's scalar gate, both channels
+            const uint32_t x = ld32(cv.la, 4 * (16 * w + r) * H);
+            rg.la[r] = u32x2{x, x};
+        }
     }
 }
 
@@ -264,7 +277,7 @@ __device__ __forceinline__ void diag_job(Smem& sm, int b, int I, int g, int ln) 
 
 }  // namespace
 
-template <int TV>
+template <int TV, int GATE>
 __global__ __launch_bounds__(NT)
 void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                          const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
@@ -309,8 +322,8 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         uint32_t beta_next = 0u;
         auto prefetch = [&](int m) {
             if (!stager) return;
-            const ChunkView cv = chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h);
-            load_rows(rg, cv, H, pw, lane);
+            const ChunkView cv = chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h, GATE);
+            load_rows<GATE>(rg, cv, H, pw, lane);
             if (pw == 0) beta_next = ld32(cv.beta, 4 * lane * H);
         };
         auto totals = [&](int m) {
@@ -493,15 +506,23 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     }
 }
 
-template <int TV>
-static hipError_t launch_mfma_t(const PrefillArgs& a, int R, hipStream_t stream) {
+template <int TV, int GATE>
+static hipError_t launch_mfma_g(const PrefillArgs& a, int R, hipStream_t stream) {
     const int64_t groups = static_cast<int64_t>(a.N) * a.H;
     const int64_t blocks = prefill_grid_blocks(groups, R);
-    hipLaunchKernelGGL((prefill_mfma_kernel<TV>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
+    hipLaunchKernelGGL((prefill_mfma_kernel<TV, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
                        0, stream, static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), a.log_alpha, a.beta, a.h0, a.cu_seqlens,
                        a.order, groups, R, a.H, a.d_v, a.scale, static_cast<bf16_t*>(a.o), a.hT);
     return hipGetLastError();
+}
+
+// a per-head gate and no gate share one instantiation (no gate reads an
+// empty range: zeros)
+template <int TV>
+static hipError_t launch_mfma_t(const PrefillArgs& a, int R, hipStream_t stream) {
+    return a.gate == kGateChannel ? launch_mfma_g<TV, kGateChannel>(a, R, stream)
+                                  : launch_mfma_g<TV, kGateHead>(a, R, stream);
 }
 
 bool mfma_supported(const PrefillArgs& a) {

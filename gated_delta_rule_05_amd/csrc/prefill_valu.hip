@@ -38,7 +38,7 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
                          const float* __restrict__ beta, const float* __restrict__ h0,
                          const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
                          int64_t groups, int R, int H, int DV, float scale,
-                         T* __restrict__ o, float* __restrict__ hT)
+                         T* __restrict__ o, float* __restrict__ hT, int gate)
 {
     constexpr int NT = 256;
     constexpr int KP = DK + 1;   // padded row stride: column walks hit distinct banks
@@ -74,7 +74,10 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
                 const int64_t off = ((c0 + r) * H + h) * DK + c;
                 kk = elem<T>::load(k + off);
                 qq = elem<T>::load(q + off);
-                la = log_alpha[off];
+                // the key channel's own gate, the head's (broadcast) or none
+                la = gate == kGateChannel ? log_alpha[off]
+                     : gate == kGateHead  ? log_alpha[(c0 + r) * H + h]
+                                          : 0.f;
             }
             sKg[r * KP + c] = kk;
             sQg[r * KP + c] = qq;
@@ -194,7 +197,7 @@ static hipError_t launch_valu_t(const PrefillArgs& a, int R, hipStream_t stream)
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.log_alpha, a.beta, a.h0,
                        a.cu_seqlens, a.order, groups, R, a.H, a.d_v, a.scale,
-                       static_cast<T*>(a.o), a.hT);
+                       static_cast<T*>(a.o), a.hT, a.gate);
     return hipGetLastError();
 }
 

@@ -203,6 +203,7 @@ __device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
 
 }  // namespace
 
+template <int GATE>
 __global__ __launch_bounds__(PT, 3)
 void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                             const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
@@ -235,15 +236,26 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
     const __amdgpu_buffer_rsrc_t rk = rsrc(k + e0, 2u * span);
     const __amdgpu_buffer_rsrc_t rq = rsrc(q + e0, 2u * span);
-    const __amdgpu_buffer_rsrc_t rla = rsrc(log_alpha + e0, 4u * span);
+    // gates per key channel, or one per (token, head); none (a null
+    // log_alpha) gives an empty range, where every load reads zero
+    const __amdgpu_buffer_rsrc_t rla =
+        GATE == kGateChannel ? rsrc(log_alpha + e0, 4u * span)
+        : log_alpha          ? rsrc(log_alpha + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1))
+                             : rsrc(log_alpha, 0u);
     const __amdgpu_buffer_rsrc_t rv =
         rsrc(v + (c0 * H + h) * DV, 2u * static_cast<uint32_t>((len - 1) * H * DV + DV));
     u32x2 kr[4], qr[4], vr[4];
     f32x4 la[4];
     // the gates first: the cumulative sum waits on them
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
+    for (int i = 0; i < 4; ++i) {
+        if constexpr (GATE == kGateChannel) {
+            la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
+        } else {                                  // the row's scalar gate on every channel
+            const float x = __uint_as_float(ld32(rla, 4 * (4 * rg + i) * H));
+            la[i] = f32x4{x, x, x, x};
+        }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
@@ -867,7 +879,9 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hip
     for (int64_t c_lo = 0; c_lo < bound; c_lo += L_b) {
         if (a.total_T > 0) {
             const int64_t nslots = static_cast<int64_t>(a.N) * L_b * a.H;
-            hipLaunchKernelGGL(prefill_wy_prep_kernel, dim3(static_cast<unsigned>(nslots)), dim3(PT),
+            auto prep = a.gate == kGateChannel ? prefill_wy_prep_kernel<kGateChannel>
+                                               : prefill_wy_prep_kernel<kGateHead>;
+            hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(nslots)), dim3(PT),
                                0, stream, static_cast<const bf16_t*>(a.q),
                                static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v),
                                a.log_alpha, a.beta, a.cu_seqlens, a.H, a.d_v,

@@ -18,10 +18,22 @@
  * Keys are expected to be L2-normalised by the caller (the first page's
  * notes on key normalisation explain why the delta rule needs it).
  *
+ * Gate variants.  The same recurrence with a coarser gate gives the two
+ * models the pages compare KDA with: Gated DeltaNet, whose gate is one
+ * scalar per (token, head) shared by every key channel ("Cos'è Kimi Delta
+ * Attention (KDA)?", section "Gating per canale: cosa rende KDA diverso"
+ * and its table), and DeltaNet, the delta rule with no decay at all
+ * (alpha = 1) ("Kimi Delta Attention: la atencion lineal detras de Kimi K2
+ * y Qwen3", section "DeltaNet, Gated DeltaNet y KDA: tabla comparativa").  The gate option of the _ex entry points selects the
+ * layout of log_alpha (enum kda_gate); the kernels broadcast a scalar gate
+ * over the key channels when they load it, so a Gated DeltaNet call gives
+ * bitwise the result of a KDA call whose gate repeats that scalar.
+ *
  * Layouts.  Every tensor is dense, contiguous, row-major:
  *     q, k        [total_T][H][d_k]     dtype (bf16 or fp32)
  *     v, o        [total_T][H][d_v]     dtype
- *     log_alpha   [total_T][H][d_k]     fp32, expected <= 0
+ *     log_alpha   [total_T][H][d_k]     fp32, expected <= 0 (KDA_GATE_CHANNEL;
+ *                 [total_T][H] for KDA_GATE_HEAD, not read for KDA_GATE_NONE)
  *     beta        [total_T][H]          fp32
  *     h0, hT, S   [N][H][d_k][d_v]      fp32 (d_v contiguous)
  *     cu_seqlens  [N+1]                 int32, DEVICE memory
@@ -75,6 +87,15 @@ enum kda_dtype {
     KDA_DTYPE_F32 = 1
 };
 
+/* Layout of the gate log_alpha (see "Gate variants" above). */
+enum kda_gate {
+    KDA_GATE_CHANNEL = 0,  /* KDA: one gate per key channel, [..][H][d_k] */
+    KDA_GATE_HEAD = 1,     /* Gated DeltaNet: one gate per (token, head),
+                              [..][H], applied to every key channel */
+    KDA_GATE_NONE = 2      /* DeltaNet: alpha = 1; log_alpha is not read and
+                              may be NULL */
+};
+
 /* Which kernel family computes a prefill. */
 enum kda_path {
     KDA_PATH_AUTO = 0,     /* a matrix path when supported (two-pass for
@@ -110,7 +131,24 @@ typedef struct kda_prefill_options {
                               55808 + 128 d_v bytes); 0 = automatic
                               (about 150 MiB of slots).  Ignored by the
                               other paths. */
+    int32_t gate;          /* a kda_gate (0 = KDA_GATE_CHANNEL) */
 } kda_prefill_options;
+
+/* Options of kda_decode_step_ex (zero-initialise for defaults). */
+typedef struct kda_decode_options {
+    int32_t gate;                  /* a kda_gate (0 = KDA_GATE_CHANNEL) */
+    int32_t num_states;            /* states in S when state_index is set */
+    const int32_t *state_index;    /* DEVICE [N], or NULL: sequence n reads
+                                      and updates state S[state_index[n]]
+                                      (S is [num_states][H][d_k][d_v]); NULL
+                                      means S[n] (S is [N][H][d_k][d_v]).
+                                      A sequence whose index lies outside
+                                      [0, num_states) is skipped: its state
+                                      is not touched and its o not written.
+                                      Indices of one call must be distinct
+                                      (two sequences updating one state
+                                      race). */
+} kda_decode_options;
 
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
 int kda_abi_version(void);
@@ -169,10 +207,14 @@ int kda_fwd_prefill(const void *q, const void *k, const void *v,
                     void *stream);
 
 /*
- * kda_fwd_prefill with explicit tuning options (NULL = defaults).  Same
- * arguments, results and requirements as kda_fwd_prefill, plus:
+ * kda_fwd_prefill with explicit options (NULL = defaults).  Same arguments,
+ * results and requirements as kda_fwd_prefill, plus:
  *   options->path not a kda_path, value_tiles invalid for the chosen path,
- *     or block_chunks negative or too large [INVALID_ARGUMENT];
+ *     block_chunks negative or too large, or gate not a kda_gate
+ *     [INVALID_ARGUMENT];
+ *   log_alpha: [total_T][H][d_k], 16-byte aligned (KDA_GATE_CHANNEL);
+ *     [total_T][H], 4-byte aligned (KDA_GATE_HEAD); may be NULL
+ *     (KDA_GATE_NONE) [INVALID_ARGUMENT, MISALIGNED];
  *   a matrix path requested for fp32 inputs or d_k != 128 [UNSUPPORTED];
  *   workspace_bytes below kda_fwd_prefill_workspace_bytes_ex(..., options)
  *     [WORKSPACE_TOO_SMALL].
@@ -210,6 +252,25 @@ int kda_decode_step(const void *q, const void *k, const void *v,
                     const float *log_alpha, const float *beta, float *S,
                     int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                     int32_t dtype, float scale, void *o, void *stream);
+
+/*
+ * kda_decode_step with options (NULL = defaults): the gate layout, and a
+ * state map for serving, where the states of the running sequences sit in
+ * slots of a larger pool (continuous batching).  Same arguments, results
+ * and requirements as kda_decode_step, plus:
+ *   options->gate not a kda_gate, or state_index set with num_states < 1
+ *     [INVALID_ARGUMENT];
+ *   log_alpha as for kda_fwd_prefill_ex with that gate [INVALID_ARGUMENT,
+ *     MISALIGNED];
+ *   state_index 4-byte aligned [MISALIGNED]; S holds num_states states when
+ *     state_index is set, and no output may overlap state_index
+ *     [INVALID_ARGUMENT].
+ */
+int kda_decode_step_ex(const void *q, const void *k, const void *v,
+                       const float *log_alpha, const float *beta, float *S,
+                       int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                       int32_t dtype, float scale, void *o,
+                       const kda_decode_options *options, void *stream);
 
 #ifdef __cplusplus
 }

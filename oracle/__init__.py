@@ -71,6 +71,25 @@ def _f32(x, shape):
     return a
 
 
+def _gate(log_alpha, lead, dk):
+    """Per-key-channel log gates [*lead, d_k] from any of the three layouts.
+
+    KDA gives one gate per key channel.  Gated DeltaNet gives one scalar per
+    (token, head) that every key channel of the head shares ("Cos'è Kimi
+    Delta Attention (KDA)?", section "Gating per canale: cosa rende KDA
+    diverso"): that scalar repeated over d_k.  DeltaNet has no decay (the
+    delta rule alone, "Kimi Delta Attention: la atencion lineal detras de
+    Kimi K2 y Qwen3", section "DeltaNet, Gated DeltaNet y KDA: tabla
+    comparativa"): log_alpha None means zeros, alpha = 1."""
+    lead = tuple(lead)
+    if log_alpha is None:
+        return np.zeros(lead + (dk,), dtype=np.float32)
+    a = np.asarray(log_alpha, dtype=np.float32)
+    if a.shape == lead:
+        a = np.repeat(a[..., None], dk, axis=-1)
+    return _f32(a, lead + (dk,))
+
+
 def _ptr(a, ctype):
     if a is None:
         return None
@@ -81,7 +100,8 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             threads: int = 0):
     """Run the token-by-token recurrence over a packed batch.
 
-    q, k: [T, H, d_k]; v: [T, H, d_v]; log_alpha: [T, H, d_k]; beta: [T, H];
+    q, k: [T, H, d_k]; v: [T, H, d_v]; log_alpha: [T, H, d_k] (KDA),
+    [T, H] (Gated DeltaNet) or None (DeltaNet); beta: [T, H];
     h0: [N, H, d_k, d_v] or None (zeros); cu_seqlens: [N+1] or None (one
     sequence of length T).  Inputs are taken as float32 values (bf16 and fp32
     stored values convert exactly).  Returns (o [T, H, d_v], hT [N, H, d_k,
@@ -102,7 +122,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     qa = _f32(q, (T, H, dk))
     ka = _f32(k, (T, H, dk))
     va = _f32(v, (T, H, dv))
-    la = _f32(log_alpha, (T, H, dk))
+    la = _gate(log_alpha, (T, H), dk)
     ba = _f32(beta, (T, H))
     h0a = None
     if h0 is not None:
@@ -124,7 +144,8 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
 
 def decode_step(q, k, v, log_alpha, beta, S, scale=None):
     """One token per sequence.  q, k: [N, H, d_k]; v: [N, H, d_v];
-    log_alpha: [N, H, d_k]; beta: [N, H]; S: [N, H, d_k, d_v] (not modified).
+    log_alpha: [N, H, d_k], [N, H] or None (as in prefill); beta: [N, H];
+    S: [N, H, d_k, d_v] (not modified).
     Returns (o [N, H, d_v], S_new [N, H, d_k, d_v]) as float64."""
     q = np.asarray(q)
     N, H, dk = q.shape
@@ -134,7 +155,7 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None):
     qa = _f32(q, (N, H, dk))
     ka = _f32(k, (N, H, dk))
     va = _f32(v, (N, H, dv))
-    la = _f32(log_alpha, (N, H, dk))
+    la = _gate(log_alpha, (N, H), dk)
     ba = _f32(beta, (N, H))
     Sa = np.array(S, dtype=np.float64, copy=True, order="C")
     if Sa.shape != (N, H, dk, dv):

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 3
+    assert kda.abi_version() == 4
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -153,12 +153,12 @@ def test_binding_rejects_cpu_tensors():
         kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
 
 
-def prefill_ex_call(path, tiles, blk=0, **over):
+def prefill_ex_call(path, tiles, blk=0, gate=0, **over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
                 o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
     args.update(over)
-    opts = kda.PrefillOptions(path, tiles, blk)
+    opts = kda.PrefillOptions(path, tiles, blk, gate)
     lib = kda.load_library()
     return lib.kda_fwd_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
                                   args["h0"], args["cu"], args["T"], args["N"], args["H"],
@@ -187,3 +187,66 @@ def prefill_ex_call(path, tiles, blk=0, **over):
 ])
 def test_prefill_ex_option_checks(path, tiles, blk, over, status):
     assert prefill_ex_call(path, tiles, blk, **over) == status
+
+
+# gate layouts: 0 per key channel (KDA), 1 per head (Gated DeltaNet), 2 none
+# (DeltaNet).  Each case fails validation before any HIP call; a status past
+# the checked one (WS_SMALL with a 255-byte workspace on the vector path)
+# shows the earlier checks passed.
+@pytest.mark.parametrize("gate,over,status", [
+    (3, {}, INVALID), (-1, {}, INVALID),
+    (0, dict(la=None), INVALID), (1, dict(la=None), INVALID),
+    (2, dict(la=None, wsb=255), WS_SMALL),            # no gate: log_alpha may be NULL
+    (2, dict(la=addr(3, 2), wsb=255), WS_SMALL),      # ... and is never checked
+    (0, dict(la=addr(3, 4)), MISALIGNED),             # per channel: 16 bytes
+    (1, dict(la=addr(3, 4), wsb=255), WS_SMALL),      # per head: 4 bytes suffice
+    (1, dict(la=addr(3, 2)), MISALIGNED),
+    # a per-head gate spans T*H*4 bytes: an output 256 bytes into it overlaps
+    (1, dict(o=addr(3, 256), wsb=1 << 34), INVALID),
+    (0, dict(o=addr(3, 4096), wsb=1 << 34), INVALID),
+])
+def test_prefill_gate_checks(gate, over, status):
+    assert prefill_ex_call(1, 0, 0, gate, **over) == status
+
+
+def test_workspace_query_gate():
+    # the gate layout never changes the workspace; an unknown gate is rejected
+    for g in ("channel", "head", "none"):
+        assert (kda.prefill_workspace_bytes(1000, 4, 16, 128, 128, gate=g)
+                == two_pass_bytes(4, 16, 128, 128, 16))
+    lib = kda.load_library()
+    opts = kda.PrefillOptions(0, 0, 0, 5)
+    assert lib.kda_fwd_prefill_workspace_bytes_ex(1000, 4, 16, 128, 128, 0,
+                                                  ctypes.byref(opts)) == 0
+
+
+def decode_ex_call(gate=0, index=None, nstates=0, **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), S=addr(5),
+                N=8, H=4, dk=128, dv=128, dtype=0, scale=0.1, o=addr(6), stream=None)
+    args.update(over)
+    opts = kda.DecodeOptions(gate, nstates, index)
+    lib = kda.load_library()
+    return lib.kda_decode_step_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                  args["S"], args["N"], args["H"], args["dk"], args["dv"],
+                                  args["dtype"], args["scale"], args["o"], ctypes.byref(opts),
+                                  args["stream"])
+
+
+STATE = 128 * 128 * 4 * 4          # one state of the 4 heads, bytes
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(gate=3), INVALID), (dict(gate=0, la=None), INVALID),
+    # no gate: NULL log_alpha passes; the misaligned S is what fails
+    (dict(gate=2, la=None, S=addr(5, 4)), MISALIGNED),
+    (dict(gate=1, la=addr(3, 4), S=addr(5, 4)), MISALIGNED),
+    (dict(gate=1, la=addr(3, 2)), MISALIGNED),
+    # state pool
+    (dict(index=BASE + 9 * GAP, nstates=0), INVALID),
+    (dict(index=BASE + 9 * GAP + 2, nstates=4), MISALIGNED),
+    (dict(index=BASE + 6 * GAP + 8, nstates=4), INVALID),            # index inside o
+    (dict(index=BASE + 9 * GAP, nstates=4, o=addr(5, 3 * STATE)), INVALID),   # o in the pool
+    (dict(index=BASE + 9 * GAP, nstates=1 << 31 - 1, o=None), INVALID),
+])
+def test_decode_ex_checks(kw, status):
+    assert decode_ex_call(**kw) == status

@@ -125,6 +125,9 @@ def test_alpha_one_is_deltanet():
     q, k, v, la, beta = rand_case(rng, T, H, dk, dv)
     la[:] = 0.0
     o, hT = oracle.prefill(q, k, v, la, beta, scale=1.0)
+    # the DeltaNet layout (no gate at all) is the same computation
+    o2, hT2 = oracle.prefill(q, k, v, None, beta, scale=1.0)
+    assert np.array_equal(o, o2) and np.array_equal(hT, hT2)
     for h in range(H):
         S = np.zeros((dk, dv))
         for t in range(T):
@@ -143,6 +146,9 @@ def test_scalar_gate_is_gated_deltanet():
     la = np.repeat(scalar[:, :, None], dk, axis=2)
     h0 = rng.standard_normal((1, H, dk, dv))
     o, hT = oracle.prefill(q, k, v, la, beta, h0=h0, scale=0.5)
+    # the Gated DeltaNet layout ([T, H], one gate per head) is the same computation
+    o2, hT2 = oracle.prefill(q, k, v, scalar, beta, h0=h0, scale=0.5)
+    assert np.array_equal(o, o2) and np.array_equal(hT, hT2)
     for h in range(H):
         S = h0[0, h].copy()
         for t in range(T):
@@ -316,6 +322,14 @@ def test_decode_step_equals_one_token_prefill():
     o2, S2 = oracle.prefill(q, k, v, la, beta, h0=S, cu_seqlens=cu, scale=0.7)
     assert np.array_equal(o, o2)
     assert np.array_equal(S1, S2)
+    # gate layouts: a per-head gate and no gate, against their expanded forms
+    g = f32(rng.uniform(-0.3, 0.0, (N, H)))
+    oh, Sh = oracle.decode_step(q, k, v, g, beta, S, scale=0.7)
+    oe, Se = oracle.decode_step(q, k, v, np.repeat(g[:, :, None], dk, axis=2), beta, S, scale=0.7)
+    assert np.array_equal(oh, oe) and np.array_equal(Sh, Se)
+    on, Sn = oracle.decode_step(q, k, v, None, beta, S, scale=0.7)
+    oz, Sz = oracle.decode_step(q, k, v, np.zeros_like(la), beta, S, scale=0.7)
+    assert np.array_equal(on, oz) and np.array_equal(Sn, Sz)
 
 
 # --------------------------------------------------------------------------
