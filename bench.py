@@ -20,6 +20,10 @@ its two-pass path: one call enqueues, per block of chunks, a prep kernel
 (chunk-parallel) and a carry kernel (the serial state walk); the roofline
 covers the whole call, and the rocprofv3 summary splits it per kernel.
 
+serving: the prefill recording a state snapshot every 4096 tokens (prefix
+caching), and the 64 decode steps on states held in scattered slots of a
+512-state pool (continuous batching).
+
 gate_variants: the same prefill as Gated DeltaNet (one gate per (token,
 head), 1032 B per head-token) and DeltaNet (no gate, 1028 B), timed the
 same way, each against the HBM peak.
@@ -45,7 +49,7 @@ HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 PREFILL_BYTES_PER_HT = 1540          # q,k,v,o bf16 (4 x 256) + log_alpha fp32 (512) + beta (4)
 DECODE_BYTES_PER_HS = 2 * 128 * 128 * 4 + 1540   # state read + write, token inputs, output
-PREFILL_KERNELS = "prefill_wy_prep_kernel + prefill_wy_carry_kernel<16>"
+PREFILL_KERNELS = "prefill_wy_prep_kernel<0> + prefill_wy_carry_kernel<16, false>"
 DECODE_KERNEL = "decode_step_kernel"
 
 
@@ -203,6 +207,51 @@ def main():
                           "frac_of_hbm_peak": v_bytes / (v_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     del head_gate
 
+    # ---------------- serving features ----------------------------------
+    # prefill that also records the state every 4096 tokens (prefix
+    # caching), and the decode steps on states held in a pool of 512 slots
+    # (continuous batching: the 256 sequences own scattered slots)
+    def timed(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for a0, a1 in evs:
+            a0.record(stream)
+            fn()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        return sum(a0.elapsed_time(a1) for a0, a1 in evs) / len(evs)
+
+    snap_tokens = 4096
+    snaps = torch.empty((1, T // snap_tokens, H, wp.dk, wp.dv), dtype=torch.float32, device=dev)
+    snap_ms = timed(lambda: kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                        cu_seqlens=inp["cu_seqlens"], out=o, final_state=hT,
+                                        workspace=ws, snapshot_tokens=snap_tokens,
+                                        snapshots=snaps), args.steps)
+    snap_bytes = snaps.numel() * 4
+    del snaps
+    pool_n = 2 * wd.N
+    pool = gen.decode_state(pool_n, wd.H, wd.dk, wd.dv, std=wd.state_std, seed=4, device=dev)
+    slots = torch.randperm(pool_n, generator=torch.Generator().manual_seed(5))[:wd.N]
+    slots = slots.to(torch.int32).to(dev)
+
+    def decode_pool():
+        for t in toks:
+            kda.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], pool, out=o_dec,
+                            state_index=slots)
+    pool_us = timed(decode_pool, args.steps) * 1e3 / wd.steps
+    serving = {
+        "prefill_snapshots": {"snapshot_tokens": snap_tokens, "snapshot_bytes": snap_bytes,
+                              "prefill_ms": snap_ms,
+                              "overhead_vs_plain_pct": 100.0 * (snap_ms / pre_avg - 1.0)},
+        "decode_state_pool": {"pool_states": pool_n, "sequences": wd.N, "us_per_step": pool_us,
+                              "state_GBps": dec_bytes / (pool_us * 1e-6) / 1e9,
+                              "frac_of_hbm_peak": dec_bytes / (pool_us * 1e-6) / 1e9 / HBM_PEAK_GBPS},
+    }
+    del pool
+    torch.cuda.empty_cache()
+
     digest = source_digest(["prefill_wy.hip", "kda_mfma.h", "kda_device.h", "kda_sched.h"])
     traffic = load_counters("prefill_wy.hip", digest)
     mfma = load_counters("prefill_wy.hip", digest, "mfma")
@@ -243,6 +292,7 @@ def main():
                    "algorithmic_bytes_per_step": dec_bytes, "traffic_per_step": dec_traffic,
                    "kernel": DECODE_KERNEL},
         "gate_variants": variants,
+        "serving": serving,
         "cpu_baseline": None,
     }
 

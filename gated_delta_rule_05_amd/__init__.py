@@ -47,7 +47,9 @@ GATES = {"channel": 0, "head": 1, "none": 2}
 class PrefillOptions(ctypes.Structure):
     """Mirror of kda_prefill_options."""
     _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32),
-                ("block_chunks", ctypes.c_int32), ("gate", ctypes.c_int32)]
+                ("block_chunks", ctypes.c_int32), ("gate", ctypes.c_int32),
+                ("snapshot_tokens", ctypes.c_int32), ("snapshot_capacity", ctypes.c_int32),
+                ("snapshots", ctypes.c_void_p)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -191,7 +193,7 @@ def _check_gate(log_alpha, gate, lead, dk, dev):
 
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
-            block_chunks=0, gate="channel"):
+            block_chunks=0, gate="channel", snapshot_tokens=0, snapshots=None):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -203,6 +205,10 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     ``final_state`` may also be a preallocated tensor (it may be h0 itself).
     ``path`` ("auto", "vector", "matrix" or "two_pass"), ``value_tiles`` and
     ``block_chunks`` (0 = automatic) are the kda_prefill_options tuning knobs.
+    ``snapshot_tokens`` > 0 (a multiple of 64) also records the state after
+    every snapshot_tokens tokens of each sequence into ``snapshots``
+    [N, capacity, H, d_k, d_v] fp32 (allocated zeroed with capacity
+    T // snapshot_tokens when None) and returns (o, hT, snapshots).
     """
     torch = _torch()
     lib = load_library()
@@ -242,6 +248,16 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
         hT = final_state
         _check(hT, "final_state", (N, H, dk, dv), torch.float32, dev)
     opts = prefill_options(path, value_tiles, block_chunks, gate)
+    if snapshot_tokens:
+        if snapshots is None:
+            cap = max(1, T // int(snapshot_tokens))
+            snapshots = torch.zeros((N, cap, H, dk, dv), dtype=torch.float32, device=dev)
+        if snapshots.dim() != 5:
+            raise ValueError("snapshots must be [N, capacity, H, d_k, d_v]")
+        _check(snapshots, "snapshots", (N, snapshots.shape[1], H, dk, dv), torch.float32, dev)
+        opts.snapshot_tokens = int(snapshot_tokens)
+        opts.snapshot_capacity = int(snapshots.shape[1])
+        opts.snapshots = snapshots.data_ptr()
     need = lib.kda_fwd_prefill_workspace_bytes_ex(T, N, H, dk, dv, code, ctypes.byref(opts))
     if workspace is None:
         workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)
@@ -251,6 +267,8 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
                                 workspace.numel(), ctypes.byref(opts), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_fwd_prefill_ex")
+    if snapshot_tokens:
+        return out, hT, snapshots
     return out, hT
 
 

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 4;
+constexpr int kAbiVersion = 5;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -229,12 +229,35 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     if (overlaps(r_o, r_hT) || overlaps(r_o, r_ws) || overlaps(r_hT, r_ws))
         return KDA_STATUS_INVALID_ARGUMENT;
 
+    // state snapshots: [N][capacity][H][d_k][d_v] fp32, overlapping nothing
+    const int32_t snap = options ? options->snapshot_tokens : 0;
+    float* snaps = nullptr;
+    int32_t cap = 0;
+    if (snap != 0) {
+        cap = options->snapshot_capacity;
+        snaps = options->snapshots;
+        if (snap < 0 || snap % 64 != 0 || cap < 1 || !snaps) return KDA_STATUS_INVALID_ARGUMENT;
+        if (!aligned16(snaps)) return KDA_STATUS_MISALIGNED;
+        int64_t bytes;
+        if (!mul_ok(sz.state_bytes / N, static_cast<int64_t>(N) * cap, &bytes) ||
+            bytes > (int64_t{1} << 62))
+            return KDA_STATUS_INVALID_ARGUMENT;
+        const Range r_s = range_of(snaps, bytes);
+        for (const Range& in : inputs)
+            if (overlaps(r_s, in)) return KDA_STATUS_INVALID_ARGUMENT;
+        if (overlaps(r_s, r_o) || overlaps(r_s, r_hT) || overlaps(r_s, r_ws))
+            return KDA_STATUS_INVALID_ARGUMENT;
+    }
+
     kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
     a.gate = gate;
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta;
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
     a.order = static_cast<int32_t*>(workspace);
     a.scale = scale;
+    a.snapshots = snaps;
+    a.snap_tokens = snaps ? snap : 0;
+    a.snap_cap = cap;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;

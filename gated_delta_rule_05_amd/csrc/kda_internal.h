@@ -46,7 +46,17 @@ struct PrefillArgs {
     int gate;                   // a GateMode
     bool dtype_f32;
     float scale;
+    // state snapshots: after every snap_tokens tokens of a sequence (a
+    // multiple of 64), into snapshots[n][j][h] for j < snap_cap; null = none
+    float* snapshots;
+    int32_t snap_tokens, snap_cap;
 };
+
+// first element of snapshot j of (sequence n, head h): [N][snap_cap][H][d_k][d_v]
+__host__ __device__ __forceinline__ float* snapshot_at(float* snapshots, int snap_cap, int H,
+                                                       int64_t state_elems, int n, int j, int h) {
+    return snapshots + ((static_cast<int64_t>(n) * snap_cap + j) * H + h) * state_elems;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_plan(const PrefillArgs& a, hipStream_t stream);

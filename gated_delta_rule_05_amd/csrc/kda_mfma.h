@@ -54,6 +54,9 @@ __device__ __forceinline__ void st16(__amdgpu_buffer_rsrc_t r, int off, uint16_t
 __device__ __forceinline__ void st64(__amdgpu_buffer_rsrc_t r, int off, u32x2 x) {
     __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, 0);
 }
+__device__ __forceinline__ void st32(__amdgpu_buffer_rsrc_t r, int off, uint32_t x) {
+    __builtin_amdgcn_raw_buffer_store_b32(x, r, off, 0, 0);
+}
 
 // round-to-nearest-even pack of two fp32 into a bf16 pair (low half = a)
 __device__ __forceinline__ uint32_t pk(float a, float b) {

@@ -284,7 +284,8 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                          const float* __restrict__ beta, const float* __restrict__ h0,
                          const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
                          int64_t groups, int R, int H, int DV, float scale,
-                         bf16_t* __restrict__ o, float* __restrict__ hT)
+                         bf16_t* __restrict__ o, float* __restrict__ hT,
+                         float* __restrict__ snapshots, int snap_tokens, int snap_cap)
 {
     constexpr int NSLAB = TV / 16;                   // 16-column state slabs in the tile
     constexpr int NC = NSLAB < 4 ? NSLAB : 4;        // consumer waves, one slab each
@@ -420,6 +421,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         __syncthreads();
         __syncthreads();
     }
+    int snap_left = snapshots ? snap_tokens / C : 0;
     for (int ci = 0; ci < nch; ++ci) {
         const int b = ci & 1;
         const int len = chunk_len(ci);
@@ -494,6 +496,17 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             const f32x4 gm = *reinterpret_cast<const f32x4*>(sm.gam[b] + 16 * m + 4 * g);
             S[m] = mma32(f1, e23, mma32(f0, e01, gm * S[m]));
         }
+        // a snapshot after every snap_tokens / C chunks (a countdown: one
+        // decrement per chunk on the serial path)
+        const int js = snapshots && --snap_left == 0
+                           ? (snap_left = snap_tokens / C, (ci + 1) / (snap_tokens / C) - 1) : -1;
+        if (js >= 0 && js < snap_cap && len == C) {      // only a full chunk ends on a boundary
+            float* dst = snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0 + jc;
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dst[static_cast<int64_t>(16 * m + 4 * g + i) * DV] = S[m][i];
+        }
         __syncthreads();
     }
 
@@ -513,7 +526,8 @@ static hipError_t launch_mfma_g(const PrefillArgs& a, int R, hipStream_t stream)
     hipLaunchKernelGGL((prefill_mfma_kernel<TV, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
                        0, stream, static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), a.log_alpha, a.beta, a.h0, a.cu_seqlens,
-                       a.order, groups, R, a.H, a.d_v, a.scale, static_cast<bf16_t*>(a.o), a.hT);
+                       a.order, groups, R, a.H, a.d_v, a.scale, static_cast<bf16_t*>(a.o), a.hT,
+                       a.snapshots, a.snap_tokens, a.snap_cap);
     return hipGetLastError();
 }
 

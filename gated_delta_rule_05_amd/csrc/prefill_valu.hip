@@ -38,7 +38,8 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
                          const float* __restrict__ beta, const float* __restrict__ h0,
                          const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
                          int64_t groups, int R, int H, int DV, float scale,
-                         T* __restrict__ o, float* __restrict__ hT, int gate)
+                         T* __restrict__ o, float* __restrict__ hT, int gate,
+                         float* __restrict__ snapshots, int snap_tokens, int snap_cap)
 {
     constexpr int NT = 256;
     constexpr int KP = DK + 1;   // padded row stride: column walks hit distinct banks
@@ -63,6 +64,7 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
         sS[i] = h0 ? h0[sbase + static_cast<int64_t>(c) * DV + j] : 0.f;
     }
 
+    int snap_left = snapshots ? snap_tokens / C : 0;
     for (int64_t c0 = t_begin; c0 < t_end; c0 += C) {
         const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
         __syncthreads();
@@ -177,6 +179,15 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
             for (int r = 0; r < C; ++r) acc += sKd[r * KP + c] * sE[r * TV + j];
             sS[i] = acc;
         }
+        // a snapshot after every snap_tokens / C chunks (each thread copies
+        // the state entries it has just written)
+        const int js = snapshots && --snap_left == 0
+                           ? (snap_left = snap_tokens / C, static_cast<int>((c0 + len - t_begin) / snap_tokens) - 1)
+                           : -1;
+        if (js >= 0 && js < snap_cap && len == C) {      // only a full chunk ends on a boundary
+            float* dst = snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0;
+            for (int i = tid; i < DK * TV; i += NT) dst[(i / TV) * DV + i % TV] = sS[i];
+        }
     }
     if (hT) {
         __syncthreads();
@@ -197,7 +208,7 @@ static hipError_t launch_valu_t(const PrefillArgs& a, int R, hipStream_t stream)
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.log_alpha, a.beta, a.h0,
                        a.cu_seqlens, a.order, groups, R, a.H, a.d_v, a.scale,
-                       static_cast<T*>(a.o), a.hT, a.gate);
+                       static_cast<T*>(a.o), a.hT, a.gate, a.snapshots, a.snap_tokens, a.snap_cap);
     return hipGetLastError();
 }
 

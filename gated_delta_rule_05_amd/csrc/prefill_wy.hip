@@ -506,12 +506,15 @@ constexpr int kRotDiv = 8;         // copy-order offsets of the value tiles
 constexpr int kMaxTwoPassTile = 32;   // columns per tile (register budget of the loaders)
 }  // namespace
 
-template <int TV>
+// SNAP: the call records state snapshots (a separate instantiation, so the
+// plain carry's serial loop carries no trace of them)
+template <int TV, bool SNAP>
 __global__ __launch_bounds__(CT)
 void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __restrict__ h0,
                              float* __restrict__ hstate, const int32_t* __restrict__ cu,
                              int64_t groups, int R, int H, int DV, int c_lo, int L_b, float scale,
-                             bf16_t* __restrict__ o)
+                             bf16_t* __restrict__ o, float* __restrict__ snapshots, int snap_tokens,
+                             int snap_cap)
 {
     constexpr int NSLAB = TV / 16;           // 16-column state slabs in the tile
     constexpr int NC = NSLAB;                // state waves; as many output waves
@@ -548,7 +551,8 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
     const int n = static_cast<int>(pair / H);
     const int64_t t_begin = cu[n];
     const int64_t t_end = cu[n + 1];
-    const int nch = static_cast<int>((t_end - t_begin + C - 1) / C);
+    const int seq_len = static_cast<int>(t_end - t_begin);   // cu_seqlens are int32
+    const int nch = (seq_len + C - 1) / C;
     const int count = min(nch, c_lo + L_b) - c_lo;   // chunks of this block
     const int j0 = tile * TV;
     const int64_t sbase = (static_cast<int64_t>(n) * H + h) * DK * DV + j0;
@@ -671,6 +675,9 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
 #pragma unroll
         for (int f = 0; f < 16; ++f) wf[f] = buf[0][f * 64 + lane];
         int bx = 0;                              // x % 3
+        // chunks until the next snapshot boundary (snap_tokens is a multiple of C)
+        const int snap_stride = SNAP ? snap_tokens / C : 0;
+        int snap_left = SNAP ? snap_stride - c_lo % snap_stride : 0;
         for (int x = 0; x < count; ++x) {
             const u32x4* F = buf[bx];
             const int bn = bx == 2 ? 0 : bx + 1;
@@ -722,6 +729,22 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) S[mm] = mma32(kf[2 * mm + 1], e23, S[mm]);
             if (x >= 2) store_o(c_lo + x - 2, x & 1);
+            // a snapshot after every snap_stride chunks: a countdown, so the
+            // serial loop pays one decrement per chunk (buffer stores keep
+            // the addressing in scalar registers and one lane offset)
+            const int js = SNAP && --snap_left == 0
+                               ? (snap_left = snap_stride, (c_lo + x + 1) / snap_stride - 1) : -1;
+            // (only a full chunk ends on a boundary)
+            if (js >= 0 && js < snap_cap && (c_lo + x + 1) * C <= seq_len) {
+                const __amdgpu_buffer_rsrc_t rs = rsrc(
+                    snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0,
+                    4u * DK * DV);
+                const int lo = 4 * (4 * g * DV + jc);
+#pragma unroll
+                for (int m = 0; m < 8; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) st32(rs, lo + 4 * (16 * m + i) * DV, __float_as_uint(S[m][i]));
+            }
             __syncthreads();
             bx = bn;
         }
@@ -825,9 +848,10 @@ hipError_t launch_carry_t(const PrefillArgs& a, int R, int c_lo, int L_b, const 
                           float* hstate, hipStream_t stream) {
     const int64_t groups = static_cast<int64_t>(a.N) * a.H;
     const int64_t blocks = prefill_grid_blocks(groups, R);
-    hipLaunchKernelGGL((prefill_wy_carry_kernel<TV>), dim3(static_cast<unsigned>(blocks)), dim3(CT),
+    auto carry = a.snapshots ? prefill_wy_carry_kernel<TV, true> : prefill_wy_carry_kernel<TV, false>;
+    hipLaunchKernelGGL(carry, dim3(static_cast<unsigned>(blocks)), dim3(CT),
                        0, stream, slots, a.h0, hstate, a.cu_seqlens, groups, R, a.H, a.d_v, c_lo,
-                       L_b, a.scale, static_cast<bf16_t*>(a.o));
+                       L_b, a.scale, static_cast<bf16_t*>(a.o), a.snapshots, a.snap_tokens, a.snap_cap);
     return hipGetLastError();
 }
 }  // namespace

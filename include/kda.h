@@ -132,6 +132,21 @@ typedef struct kda_prefill_options {
                               (about 150 MiB of slots).  Ignored by the
                               other paths. */
     int32_t gate;          /* a kda_gate (0 = KDA_GATE_CHANNEL) */
+    int32_t snapshot_tokens;   /* 0 = no snapshots; else a positive multiple
+                                  of 64: the state after every
+                                  snapshot_tokens tokens of each sequence is
+                                  written to snapshots (for prefix caching:
+                                  a snapshot can seed a later call as its
+                                  h0) */
+    int32_t snapshot_capacity; /* snapshots kept per sequence (>= 1 when
+                                  snapshot_tokens > 0) */
+    float *snapshots;          /* DEVICE [N][snapshot_capacity][H][d_k][d_v]
+                                  fp32, 16-byte aligned: snapshot j of
+                                  sequence n is the state after its first
+                                  (j+1) * snapshot_tokens tokens, for those
+                                  j < snapshot_capacity that fit in the
+                                  sequence; other entries are not written.
+                                  May not overlap any other buffer. */
 } kda_prefill_options;
 
 /* Options of kda_decode_step_ex (zero-initialise for defaults). */
@@ -215,6 +230,10 @@ int kda_fwd_prefill(const void *q, const void *k, const void *v,
  *   log_alpha: [total_T][H][d_k], 16-byte aligned (KDA_GATE_CHANNEL);
  *     [total_T][H], 4-byte aligned (KDA_GATE_HEAD); may be NULL
  *     (KDA_GATE_NONE) [INVALID_ARGUMENT, MISALIGNED];
+ *   snapshot_tokens not 0 and not a positive multiple of 64, or set with
+ *     snapshot_capacity < 1, snapshots NULL, a byte count that overflows,
+ *     or snapshots overlapping another buffer [INVALID_ARGUMENT];
+ *     snapshots not 16-byte aligned [MISALIGNED];
  *   a matrix path requested for fp32 inputs or d_k != 128 [UNSUPPORTED];
  *   workspace_bytes below kda_fwd_prefill_workspace_bytes_ex(..., options)
  *     [WORKSPACE_TOO_SMALL].

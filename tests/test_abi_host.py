@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 4
+    assert kda.abi_version() == 5
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -153,12 +153,12 @@ def test_binding_rejects_cpu_tensors():
         kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
 
 
-def prefill_ex_call(path, tiles, blk=0, gate=0, **over):
+def prefill_ex_call(path, tiles, blk=0, gate=0, snap=(0, 0, None), **over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
                 o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
     args.update(over)
-    opts = kda.PrefillOptions(path, tiles, blk, gate)
+    opts = kda.PrefillOptions(path, tiles, blk, gate, snap[0], snap[1], snap[2])
     lib = kda.load_library()
     return lib.kda_fwd_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
                                   args["h0"], args["cu"], args["T"], args["N"], args["H"],
@@ -250,3 +250,24 @@ STATE = 128 * 128 * 4 * 4          # one state of the 4 heads, bytes
 ])
 def test_decode_ex_checks(kw, status):
     assert decode_ex_call(**kw) == status
+
+
+# snapshots: [N][capacity][H][d_k][d_v] fp32 (N = 2, H = 4, d = 128: 512 KiB
+# per snapshot index).  Each case fails before any HIP call; WS_SMALL with a
+# 255-byte workspace means the snapshot checks passed.
+SNAP = 2 * 4 * 128 * 128 * 4
+
+
+@pytest.mark.parametrize("snap,over,status", [
+    ((64, 2, BASE + 10 * GAP), dict(wsb=255), WS_SMALL),
+    ((0, 0, BASE + 10 * GAP + 4), dict(wsb=255), WS_SMALL),     # ignored when off
+    ((63, 2, BASE + 10 * GAP), {}, INVALID), ((-64, 2, BASE + 10 * GAP), {}, INVALID),
+    ((64, 0, BASE + 10 * GAP), {}, INVALID), ((64, 2, None), {}, INVALID),
+    ((64, 2, BASE + 10 * GAP + 8), {}, MISALIGNED),
+    ((64, 1 << 30, BASE + 10 * GAP), dict(H=1 << 20, N=1 << 6, hT=None), INVALID),   # bytes overflow
+    ((64, 2, BASE + 6 * GAP + 64), dict(wsb=1 << 34), INVALID),   # overlaps o
+    ((64, 3, BASE + 7 * GAP - SNAP), dict(wsb=1 << 34), INVALID),  # runs into hT
+    ((64, 2, BASE + 2 * GAP), dict(wsb=1 << 34), INVALID),        # overlaps v
+])
+def test_prefill_snapshot_checks(snap, over, status):
+    assert prefill_ex_call(1, 0, 0, 0, snap, **over) == status
