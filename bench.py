@@ -21,8 +21,11 @@ its two-pass path: one call enqueues, per block of chunks, a prep kernel
 covers the whole call, and the rocprofv3 summary splits it per kernel.
 
 serving: the prefill recording a state snapshot every 4096 tokens (prefix
-caching), and the 64 decode steps on states held in scattered slots of a
-512-state pool (continuous batching).
+caching), the 64 decode steps on states held in scattered slots of a
+512-state pool (continuous batching), and speculative decoding of 4 draft
+tokens per sequence: one call verifies them (outputs, states only read),
+one commits an accepted prefix of 0..4 tokens (states advanced), each
+reading a state once, beside the time of 4 single decode steps.
 
 gate_variants: the same prefill as Gated DeltaNet (one gate per (token,
 head), 1032 B per head-token) and DeltaNet (no gate, 1028 B), timed the
@@ -241,6 +244,24 @@ def main():
             kda.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], pool, out=o_dec,
                             state_index=slots)
     pool_us = timed(decode_pool, args.steps) * 1e3 / wd.steps
+    # speculative decoding: verify 4 draft tokens per sequence (outputs of
+    # all 4, states only read), then commit an accepted prefix of 0..4
+    # tokens (states advanced, no outputs); each call reads a state once
+    m_spec = 4
+    spec = {key: torch.stack([t[key] for t in toks[:m_spec]], dim=1).contiguous()
+            for key in ("q", "k", "v", "log_alpha", "beta")}
+    o_spec = torch.empty((wd.N, m_spec, wd.H, wd.dv), dtype=torch.bfloat16, device=dev)
+    accepted = torch.randint(0, m_spec + 1, (wd.N,), generator=torch.Generator().manual_seed(6))
+    accepted = accepted.to(torch.int32).to(dev)
+    verify_us = timed(lambda: kda.decode_multi(spec["q"], spec["k"], spec["v"], spec["log_alpha"],
+                                               spec["beta"], S, out=o_spec, write_state=False),
+                      args.steps) * 1e3
+    commit_us = timed(lambda: kda.decode_multi(spec["q"], spec["k"], spec["v"], spec["log_alpha"],
+                                               spec["beta"], S, outputs=False, lengths=accepted),
+                      args.steps) * 1e3
+    state_bytes = wd.N * wd.H * wd.dk * wd.dv * 4
+    live = int((accepted > 0).sum().item())
+    del spec, o_spec
     serving = {
         "prefill_snapshots": {"snapshot_tokens": snap_tokens, "snapshot_bytes": snap_bytes,
                               "prefill_ms": snap_ms,
@@ -248,6 +269,14 @@ def main():
         "decode_state_pool": {"pool_states": pool_n, "sequences": wd.N, "us_per_step": pool_us,
                               "state_GBps": dec_bytes / (pool_us * 1e-6) / 1e9,
                               "frac_of_hbm_peak": dec_bytes / (pool_us * 1e-6) / 1e9 / HBM_PEAK_GBPS},
+        "speculative_decode": {
+            "draft_tokens": m_spec, "sequences": wd.N,
+            "verify_us": verify_us,
+            "verify_state_read_GBps": state_bytes / (verify_us * 1e-6) / 1e9,
+            "commit_us": commit_us, "committing_sequences": live,
+            "commit_state_GBps": (state_bytes + live * wd.H * wd.dk * wd.dv * 4) /
+                                 (commit_us * 1e-6) / 1e9,
+            "single_steps_us": m_spec * dec_step_us},
     }
     del pool
     torch.cuda.empty_cache()

@@ -28,7 +28,7 @@ __all__ = [
     "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "GATES", "PrefillOptions",
     "DecodeOptions", "library_path", "load_library",
     "abi_version", "status_string", "prefill_options", "prefill_workspace_bytes", "prefill",
-    "decode_step", "EXPORTED_SYMBOLS",
+    "decode_step", "DecodeMultiOptions", "decode_multi", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -57,11 +57,18 @@ class DecodeOptions(ctypes.Structure):
     _fields_ = [("gate", ctypes.c_int32), ("num_states", ctypes.c_int32),
                 ("state_index", ctypes.c_void_p)]
 
+
+class DecodeMultiOptions(ctypes.Structure):
+    """Mirror of kda_decode_multi_options."""
+    _fields_ = [("gate", ctypes.c_int32), ("num_states", ctypes.c_int32),
+                ("state_index", ctypes.c_void_p), ("lengths", ctypes.c_void_p),
+                ("write_state", ctypes.c_int32)]
+
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
                     "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill_workspace_bytes_ex",
                     "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step",
-                    "kda_decode_step_ex")
+                    "kda_decode_step_ex", "kda_decode_multi")
 
 
 class KDAError(RuntimeError):
@@ -111,6 +118,9 @@ def load_library():
     lib.kda_decode_step_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                        vp, ctypes.POINTER(DecodeOptions), vp]
     lib.kda_decode_step_ex.restype = ctypes.c_int
+    lib.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                                     vp, ctypes.POINTER(DecodeMultiOptions), vp]
+    lib.kda_decode_multi.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -318,4 +328,65 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel
                                 ctypes.byref(opts), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_decode_step_ex")
+    return out
+
+
+def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True,
+                 write_state=True, lengths=None, gate="channel", state_index=None):
+    """m decode tokens per sequence in one pass over the states.
+
+    q, k: [N, m, H, d_k]; v: [N, m, H, d_v] (bf16 or fp32); log_alpha:
+    [N, m, H, d_k] fp32 (gate="channel"), [N, m, H] (gate="head") or None
+    (gate="none"); beta: [N, m, H] fp32; S: [N, H, d_k, d_v] fp32, or a pool
+    [num_states, H, d_k, d_v] with state_index (int32 [N] on the device).
+    Sequence n applies its first lengths[n] tokens (int32 [N] on the device,
+    clamped to [0, m]; None = all m).  With ``outputs`` the outputs of the
+    applied tokens are written into ``out`` (allocated when None) and
+    returned; with ``write_state`` S is advanced in place past the applied
+    tokens.  Verify draft tokens with write_state=False, commit an accepted
+    prefix with outputs=False and lengths."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [N, m, H, d_k]")
+    N, m, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU (HIP) device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (N, m, H, dk), dt, dev)
+    _check(k, "k", (N, m, H, dk), dt, dev)
+    _check(v, "v", (N, m, H, dv), dt, dev)
+    log_alpha, gcode = _check_gate(log_alpha, gate, (N, m, H), dk, dev)
+    _check(beta, "beta", (N, m, H), torch.float32, dev)
+    if state_index is None:
+        _check(S, "S", (N, H, dk, dv), torch.float32, dev)
+        nstates = N
+    else:
+        _check(state_index, "state_index", (N,), torch.int32, dev)
+        if S.dim() != 4:
+            raise ValueError("S must be [num_states, H, d_k, d_v]")
+        nstates = S.shape[0]
+        _check(S, "S", (nstates, H, dk, dv), torch.float32, dev)
+    if lengths is not None:
+        _check(lengths, "lengths", (N,), torch.int32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    if not outputs:
+        out = None
+    elif out is None:
+        out = torch.empty((N, m, H, dv), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, m, H, dv), dt, dev)
+    opts = DecodeMultiOptions(gcode, nstates,
+                              None if state_index is None else state_index.data_ptr(),
+                              None if lengths is None else lengths.data_ptr(),
+                              1 if write_state else 0)
+    st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
+                              N, m, H, dk, dv, code, float(scale), _ptr(out),
+                              ctypes.byref(opts), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_decode_multi")
     return out

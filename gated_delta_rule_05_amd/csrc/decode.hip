@@ -166,12 +166,150 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
 }
 
+// Several tokens per sequence (m, stored [N][m][H][.]), applied in order to
+// the state held in registers: one read of each state for all of them.
+// Sequence n applies its first len_n = clamp(lengths[n], 0, m) tokens (all
+// m without lengths), writes the outputs of those tokens when o is given,
+// and stores the state after them when write_state is set.  Speculative
+// decoding uses it twice: to verify m draft tokens (outputs only, the state
+// left as it was) and to commit the accepted prefix (state only).  Each
+// token is the same arithmetic as decode_step_kernel's single token, in the
+// same order, so a commit of m tokens equals m decode steps bit for bit.
+template <typename T, int DK, int DV, int GATE, bool INDEXED>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NWV * 64))
+void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
+                         const T* __restrict__ v, const float* __restrict__ log_alpha,
+                         const float* __restrict__ beta, float* __restrict__ S,
+                         T* __restrict__ o, float scale, int64_t nheads, int H, int m,
+                         const int32_t* __restrict__ lengths, int write_state,
+                         const int32_t* __restrict__ state_index, int num_states)
+{
+    using Sh = DecodeShape<DK, DV>;
+    constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NWV = Sh::NWV, ITERS = Sh::ITERS;
+    __shared__ f32x4 red[2][NWV][2][LPR];
+    __shared__ float red_kq[2][NWV];
+
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int cl = lane % LPR;
+    const int row0 = wave * (ITERS * RPI) + lane / LPR;
+    auto slot = [&](int64_t nh) -> int64_t {
+        if constexpr (!INDEXED) return nh;
+        const int64_t n = nh / H;
+        const int32_t x = state_index[n];
+        return x >= 0 && x < num_states ? static_cast<int64_t>(x) * H + (nh - n * H) : -1;
+    };
+    auto state = [&](int64_t sh, int it) {
+        return S + (sh < 0 ? 0 : sh) * (DK * DV) + (row0 + it * RPI) * DV + 4 * cl;
+    };
+
+    int64_t nh = blockIdx.x;
+    if (nh >= nheads) return;
+    f32x4 s[ITERS], sn[ITERS];
+    int64_t sh = slot(nh);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) s[it] = load_stream4(state(sh, it));
+    int par = 0;
+    for (; nh < nheads; nh += gridDim.x) {
+        const int64_t nn = nh + gridDim.x < nheads ? nh + gridDim.x : nh;
+        const int64_t shn = slot(nn);
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) sn[it] = load_stream4(state(shn, it));
+
+        const int64_t n = nh / H;
+        const int64_t h = nh - n * H;
+        const int len = lengths ? min(max(lengths[n], 0), m) : m;
+        const bool live = !INDEXED || sh >= 0;
+        for (int i = 0; i < len; ++i) {
+            const int64_t tk = (n * m + i) * H + h;      // token row
+            const T* qp = q + tk * DK;
+            const T* kp = k + tk * DK;
+            const float la_head = GATE == kGateHead && log_alpha ? log_alpha[tk] : 0.f;
+            auto la_of = [&](int r) {
+                if constexpr (GATE == kGateChannel) return log_alpha[tk * DK + r];
+                else return la_head;
+            };
+            f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
+            float kq = 0.f;
+            float kr[ITERS];
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) {
+                const int r = row0 + it * RPI;
+                const float a = gate_exp(la_of(r));
+                const float kv = elem<T>::load(kp + r);
+                const float qv = elem<T>::load(qp + r);
+                kr[it] = kv;
+                kq += kv * qv;
+                s[it] *= a;
+                rk += kv * s[it];
+                rq += qv * s[it];
+            }
+#pragma unroll
+            for (int mk = LPR; mk < 64; mk <<= 1) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    rk[c] += __shfl_xor(rk[c], mk);
+                    rq[c] += __shfl_xor(rq[c], mk);
+                }
+                kq += __shfl_xor(kq, mk);
+            }
+            if (NWV > 1) {
+                // double-buffered by a parity that flips per reduction: the
+                // barrier of the next one keeps a fast wave from overwriting
+                // partials a slow wave is still reading
+                if (lane < LPR) {
+                    red[par][wave][0][cl] = rk;
+                    red[par][wave][1][cl] = rq;
+                    if (lane == 0) red_kq[par][wave] = kq;
+                }
+                __syncthreads();
+                rk = red[par][0][0][cl];
+                rq = red[par][0][1][cl];
+                kq = red_kq[par][0];
+#pragma unroll
+                for (int w = 1; w < NWV; ++w) {
+                    rk += red[par][w][0][cl];
+                    rq += red[par][w][1][cl];
+                    kq += red_kq[par][w];
+                }
+                par ^= 1;
+            }
+            const float b = beta[tk];
+            const float4 vv = elem<T>::load4(v + tk * DV + 4 * cl);
+            const f32x4 e = {b * (vv.x - rk[0]), b * (vv.y - rk[1]), b * (vv.z - rk[2]),
+                             b * (vv.w - rk[3])};
+            if (o && live && wave == 0 && lane < LPR) {
+                const f32x4 oo = scale * (rq + kq * e);
+                elem<T>::store4(o + tk * DV + 4 * cl, make_float4(oo[0], oo[1], oo[2], oo[3]));
+            }
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) s[it] = s[it] + kr[it] * e;
+        }
+        if (write_state && live && len > 0) {
+#pragma unroll
+            for (int it = 0; it < ITERS; ++it) store_stream4(state(sh, it), s[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) s[it] = sn[it];
+        sh = shn;
+    }
+}
+
 template <typename T, int DK, int DV, int GATE, bool INDEXED>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
     constexpr int threads = DecodeShape<DK, DV>::NWV * 64;
     const int64_t nheads = static_cast<int64_t>(a.N) * a.H;
     // persistent grid; small states (one wave each) get more work-groups
     const int64_t grid = std::min<int64_t>(nheads, kDecodeGrid * (threads == 64 ? 4 : 1));
+    if (a.m > 0) {
+        hipLaunchKernelGGL((decode_multi_kernel<T, DK, DV, GATE, INDEXED>),
+                           dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream,
+                           static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                           static_cast<const T*>(a.v), a.log_alpha, a.beta, a.S,
+                           static_cast<T*>(a.o), a.scale, nheads, a.H, a.m, a.lengths,
+                           a.write_state ? 1 : 0, a.state_index, a.num_states);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((decode_step_kernel<T, DK, DV, GATE, INDEXED>), dim3(static_cast<unsigned>(grid)),
                        dim3(threads), 0, stream,
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -288,34 +288,43 @@ int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* lo
                               stream);
 }
 
-int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* log_alpha,
-                       const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
-                       int32_t d_v, int32_t dtype, float scale, void* o,
-                       const kda_decode_options* options, void* stream) {
-    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
-    const int32_t* index = options ? options->state_index : nullptr;
-    const int32_t nstates = index ? options->num_states : N;
-    if (nstates < 1) return KDA_STATUS_INVALID_ARGUMENT;
+}  // extern "C"
+
+namespace {
+// Shared validation and launch of the decode entry points.  m = 0 is the
+// single-step call (tokens [N][H][.], o required); m >= 1 is the
+// several-token call (tokens [N][m][H][.]).
+int decode_call(const void* q, const void* k, const void* v, const float* log_alpha,
+                const float* beta, float* S, int32_t N, int32_t m, int32_t H, int32_t d_k,
+                int32_t d_v, int32_t dtype, float scale, void* o, int32_t gate,
+                const int32_t* index, int32_t num_states, const int32_t* lengths,
+                bool write_state, void* stream) {
+    const int32_t nstates = index ? num_states : N;
+    if (nstates < 1 || m < 0 || N < 1) return KDA_STATUS_INVALID_ARGUMENT;
+    int64_t tokens = N;
+    if (m > 0 && !mul_ok(N, m, &tokens)) return KDA_STATUS_INVALID_ARGUMENT;
     Sizes sz;
-    const int st = check_sizes(N, N, H, d_k, d_v, dtype, gate, &sz);
+    const int st = check_sizes(tokens, N, H, d_k, d_v, dtype, gate, &sz);
     if (st != KDA_STATUS_OK) return st;
     Sizes pool;   // the state pool: nstates states
     if (check_sizes(0, nstates, H, d_k, d_v, dtype, gate, &pool) != KDA_STATUS_OK)
         return KDA_STATUS_INVALID_ARGUMENT;
     if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
-    if (!q || !k || !v || !beta || !S || !o) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!q || !k || !v || !beta || !S) return KDA_STATUS_INVALID_ARGUMENT;
+    if (!o && (m == 0 || !write_state)) return KDA_STATUS_INVALID_ARGUMENT;   // nothing to do
     const int gs = check_gate_ptr(gate, log_alpha, true);
     if (gs != KDA_STATUS_OK) return gs;
     if (gate == KDA_GATE_NONE) log_alpha = nullptr;   // never read
     const void* ptrs[] = {q, k, v, S, o};
     for (const void* p : ptrs)
         if (!aligned16(p)) return KDA_STATUS_MISALIGNED;
-    if (!aligned4(beta) || !aligned4(index)) return KDA_STATUS_MISALIGNED;
-    const Range r_o = range_of(o, sz.v_bytes);
+    if (!aligned4(beta) || !aligned4(index) || !aligned4(lengths)) return KDA_STATUS_MISALIGNED;
+    const Range r_o = range_of(o, o ? sz.v_bytes : 0);
     const Range r_S = range_of(S, pool.state_bytes);
     const Range others[] = {range_of(q, sz.qk_bytes),      range_of(k, sz.qk_bytes),
                             range_of(v, sz.v_bytes),       range_of(log_alpha, sz.la_bytes),
-                            range_of(beta, sz.beta_bytes), range_of(index, index ? N * 4 : 0)};
+                            range_of(beta, sz.beta_bytes), range_of(index, index ? N * 4 : 0),
+                            range_of(lengths, lengths ? N * 4 : 0)};
     for (const Range& in : others)
         if (overlaps(r_o, in) || overlaps(r_S, in)) return KDA_STATUS_INVALID_ARGUMENT;
     if (overlaps(r_o, r_S)) return KDA_STATUS_INVALID_ARGUMENT;
@@ -327,9 +336,38 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
     a.gate = gate;
     a.dtype_f32 = dtype == KDA_DTYPE_F32;
     a.scale = scale;
+    a.m = m;
+    a.lengths = lengths;
+    a.write_state = write_state;
     if (kda::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_STATUS_HIP_ERROR;
     return KDA_STATUS_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int kda_decode_step_ex(const void* q, const void* k, const void* v, const float* log_alpha,
+                       const float* beta, float* S, int32_t N, int32_t H, int32_t d_k,
+                       int32_t d_v, int32_t dtype, float scale, void* o,
+                       const kda_decode_options* options, void* stream) {
+    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
+    const int32_t* index = options ? options->state_index : nullptr;
+    return decode_call(q, k, v, log_alpha, beta, S, N, 0, H, d_k, d_v, dtype, scale, o, gate,
+                       index, options ? options->num_states : 0, nullptr, true, stream);
+}
+
+int kda_decode_multi(const void* q, const void* k, const void* v, const float* log_alpha,
+                     const float* beta, float* S, int32_t N, int32_t m, int32_t H, int32_t d_k,
+                     int32_t d_v, int32_t dtype, float scale, void* o,
+                     const kda_decode_multi_options* options, void* stream) {
+    if (m < 1) return KDA_STATUS_INVALID_ARGUMENT;
+    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
+    const int32_t* index = options ? options->state_index : nullptr;
+    return decode_call(q, k, v, log_alpha, beta, S, N, m, H, d_k, d_v, dtype, scale, o, gate,
+                       index, options ? options->num_states : 0,
+                       options ? options->lengths : nullptr,
+                       options ? options->write_state != 0 : true, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

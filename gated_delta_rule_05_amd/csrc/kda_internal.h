@@ -28,6 +28,11 @@ struct DecodeArgs {
     int gate;                     // a GateMode
     bool dtype_f32;
     float scale;
+    // several tokens per sequence (m > 0; 0 = the single-step kernel):
+    // tokens [N][m][H][.], lengths device [N] or null, o may be null
+    int32_t m = 0;
+    const int32_t* lengths = nullptr;
+    bool write_state = true;
 };
 
 struct PrefillArgs {

@@ -165,6 +165,22 @@ typedef struct kda_decode_options {
                                       race). */
 } kda_decode_options;
 
+/* Options of kda_decode_multi (zero-initialise, then set write_state, for
+ * the common call). */
+typedef struct kda_decode_multi_options {
+    int32_t gate;                  /* a kda_gate (0 = KDA_GATE_CHANNEL) */
+    int32_t num_states;            /* states in S when state_index is set */
+    const int32_t *state_index;    /* DEVICE [N] or NULL: the state map of
+                                      kda_decode_options, same rules */
+    const int32_t *lengths;        /* DEVICE [N] or NULL: sequence n applies
+                                      its first clamp(lengths[n], 0, m)
+                                      tokens; NULL means all m */
+    int32_t write_state;           /* nonzero: each sequence's state is
+                                      overwritten with the state after its
+                                      applied tokens (left as it was when it
+                                      applies none); zero: S is only read */
+} kda_decode_multi_options;
+
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
 int kda_abi_version(void);
 
@@ -290,6 +306,36 @@ int kda_decode_step_ex(const void *q, const void *k, const void *v,
                        int32_t N, int32_t H, int32_t d_k, int32_t d_v,
                        int32_t dtype, float scale, void *o,
                        const kda_decode_options *options, void *stream);
+
+/*
+ * Several decode tokens per sequence in one pass over the states: m tokens
+ * for each of N sequences, applied in order, each one token of the
+ * recurrence above exactly as kda_decode_step applies it.  This serves the
+ * speculative decoding that "Kimi Linear acaba de superar a la atención
+ * completa en sus propios términos" (section "Qué observar tras el
+ * lanzamiento de Kimi Linear") lists among the serving features KDA has to
+ * keep correct: one call verifies m draft tokens (o given, write_state = 0:
+ * the outputs of all m, the states untouched) and a second commits the
+ * accepted prefix (o = NULL, write_state = 1, lengths = tokens accepted per
+ * sequence).  Each state is read once per call and written at most once,
+ * whatever m is.
+ *
+ * Inputs q, k [N][m][H][d_k], v [N][m][H][d_v] (dtype), log_alpha laid out
+ * per options->gate over the same N*m tokens, beta [N][m][H] (fp32).  S as
+ * for kda_decode_step_ex.  o [N][m][H][d_v] (dtype) or NULL receives the
+ * outputs of the applied tokens; rows of tokens a sequence does not apply,
+ * and every row of a skipped sequence, are left unwritten.
+ *
+ * Requirements: m >= 1, and o != NULL or write_state != 0
+ * [INVALID_ARGUMENT]; lengths 4-byte aligned [MISALIGNED] and no overlap of
+ * an output with it [INVALID_ARGUMENT]; otherwise those of
+ * kda_decode_step_ex over N*m tokens.
+ */
+int kda_decode_multi(const void *q, const void *k, const void *v,
+                     const float *log_alpha, const float *beta, float *S,
+                     int32_t N, int32_t m, int32_t H, int32_t d_k, int32_t d_v,
+                     int32_t dtype, float scale, void *o,
+                     const kda_decode_multi_options *options, void *stream);
 
 #ifdef __cplusplus
 }

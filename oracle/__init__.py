@@ -169,3 +169,31 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None):
     if rc != 0:
         raise RuntimeError("kdaref_decode_step failed with code %d" % rc)
     return o, Sa
+
+
+def decode_multi(q, k, v, log_alpha, beta, S, lengths=None, scale=None):
+    """m tokens per sequence, applied in order to the sequence's state.
+
+    q, k: [N, m, H, d_k]; v: [N, m, H, d_v]; log_alpha: [N, m, H, d_k],
+    [N, m, H] or None; beta: [N, m, H]; S: [N, H, d_k, d_v] (not modified);
+    lengths: [N] tokens applied per sequence (clamped to [0, m]; None = m).
+    Returns (o [N, m, H, d_v] with NaN in the rows of tokens not applied,
+    S_new [N, H, d_k, d_v]) as float64.  Tokens applied in order are the
+    recurrence itself, so this is prefill() over each sequence's applied
+    tokens starting from its state: no arithmetic of its own."""
+    q = np.asarray(q)
+    N, m, H, dk = q.shape
+    dv = np.asarray(v).shape[3]
+    lens = np.full(N, m, dtype=np.int64) if lengths is None else \
+        np.clip(np.asarray(lengths, dtype=np.int64), 0, m)
+    take = np.concatenate([n * m + np.arange(lens[n]) for n in range(N)]).astype(np.int64)
+    flat = lambda x, tail: np.asarray(x).reshape((N * m, H) + tail)[take]
+    la = None if log_alpha is None else np.asarray(log_alpha).reshape((N * m, H, -1))[take]
+    if la is not None and la.shape[-1] == 1 and np.asarray(log_alpha).ndim == 3:
+        la = la[..., 0]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    o_t, S_new = prefill(flat(q, (dk,)), flat(k, (dk,)), flat(v, (dv,)), la,
+                         flat(beta, ()), h0=S, cu_seqlens=cu, scale=scale)
+    o = np.full((N * m, H, dv), np.nan)
+    o[take] = o_t
+    return o.reshape(N, m, H, dv), S_new

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 5
+    assert kda.abi_version() == 6
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -250,6 +250,36 @@ STATE = 128 * 128 * 4 * 4          # one state of the 4 heads, bytes
 ])
 def test_decode_ex_checks(kw, status):
     assert decode_ex_call(**kw) == status
+
+
+def decode_multi_call(m=4, gate=0, index=None, nstates=0, lengths=None, write_state=1,
+                      **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), S=addr(5),
+                N=8, H=4, dk=128, dv=128, dtype=0, scale=0.1, o=addr(6), stream=None)
+    args.update(over)
+    opts = kda.DecodeMultiOptions(gate, nstates, index, lengths, write_state)
+    lib = kda.load_library()
+    return lib.kda_decode_multi(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                args["S"], args["N"], m, args["H"], args["dk"], args["dv"],
+                                args["dtype"], args["scale"], args["o"], ctypes.byref(opts),
+                                args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(m=0), INVALID), (dict(m=-1), INVALID),
+    (dict(o=None, write_state=0), INVALID),              # nothing to compute
+    (dict(lengths=BASE + 10 * GAP + 2), MISALIGNED),
+    (dict(lengths=BASE + 6 * GAP + 64), INVALID),         # lengths inside o
+    (dict(lengths=BASE + 5 * GAP + 64), INVALID),         # lengths inside S
+    (dict(o=addr(0, 8 * 4 * 128 * 2 * 3)), INVALID),      # o inside q's m tokens
+    (dict(N=1 << 30, m=1 << 30), INVALID),                # token count overflows
+    (dict(dk=48), UNSUPPORTED),
+    (dict(gate=1, la=addr(3, 2)), MISALIGNED),
+    (dict(index=BASE + 9 * GAP, nstates=0), INVALID),
+    (dict(S=addr(5, 4), o=None), MISALIGNED),
+])
+def test_decode_multi_checks(kw, status):
+    assert decode_multi_call(**kw) == status
 
 
 # snapshots: [N][capacity][H][d_k][d_v] fp32 (N = 2, H = 4, d = 128: 512 KiB
