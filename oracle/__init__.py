@@ -11,8 +11,12 @@ atencion lineal detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta
 Attention paso a paso").  This module only builds that file with gcc and
 marshals numpy arrays into it.
 
+The gradients live in ``kda_oracle_bwd.c``: the reverse-mode derivative of
+the same token loop, step by step in reverse order (``backward`` below).
+
 Pins (the tests that tie this oracle to something other than itself) live in
-``tests/test_oracle_pins.py``: a brute-force product of explicit transition
+``tests/test_oracle_pins.py`` and, for the gradients,
+``tests/test_oracle_bwd_pins.py``: a brute-force product of explicit transition
 matrices, the DeltaNet and Gated DeltaNet special cases, the beta = 0 closed
 form, the beta = 1 read-back, the basis-key closed form, linearity, the
 stability bound and a hand-derived worked example.
@@ -28,17 +32,26 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kda_oracle.c")
 _LIB = os.path.join(_HERE, "libkda_oracle.so")
+_BWD_SRC = os.path.join(_HERE, "kda_oracle_bwd.c")
+_BWD_LIB = os.path.join(_HERE, "libkda_oracle_bwd.so")
 _lib = None
+_bwd_lib = None
+
+
+def _gcc(src, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread", src, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, lib)
 
 
 def build(force: bool = True) -> str:
-    """Compile kda_oracle.c into libkda_oracle.so with gcc (host only)."""
+    """Compile kda_oracle.c (forward) and kda_oracle_bwd.c (gradients) into
+    their shared libraries with gcc (host only)."""
     if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-pthread",
-               _SRC, "-o", tmp, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
+        _gcc(_SRC, _LIB)
+    if os.path.exists(_BWD_SRC) and (force or not os.path.exists(_BWD_LIB)):
+        _gcc(_BWD_SRC, _BWD_LIB)
     return _LIB
 
 
@@ -197,3 +210,69 @@ def decode_multi(q, k, v, log_alpha, beta, S, lengths=None, scale=None):
     o = np.full((N * m, H, dv), np.nan)
     o[take] = o_t
     return o.reshape(N, m, H, dv), S_new
+
+
+def _load_bwd():
+    global _bwd_lib
+    if _bwd_lib is None:
+        if not os.path.exists(_BWD_LIB):
+            _gcc(_BWD_SRC, _BWD_LIB)
+        lib = ctypes.CDLL(_BWD_LIB)
+        f32p = ctypes.POINTER(ctypes.c_float)
+        f64p = ctypes.POINTER(ctypes.c_double)
+        i64 = ctypes.c_int64
+        lib.kdaref_backward.argtypes = [f32p, f32p, f32p, f32p, f32p, f64p,
+                                        ctypes.POINTER(ctypes.c_int64), i64, i64, i64, i64,
+                                        ctypes.c_double, f64p, f64p, f64p, f64p, f64p, f64p,
+                                        f64p, f64p, ctypes.c_int]
+        lib.kdaref_backward.restype = ctypes.c_int
+        _bwd_lib = lib
+    return _bwd_lib
+
+
+def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, scale=None,
+             threads: int = 0):
+    """Gradients of <o, do> + <hT, dhT> for the prefill over a packed batch.
+
+    Arguments as in prefill(), plus do [T, H, d_v] (the adjoint of o) and
+    dhT [N, H, d_k, d_v] or None (zeros: the adjoint of the final states).
+    Returns a dict of float64 arrays: dq, dk [T, H, d_k], dv [T, H, d_v],
+    dlog_alpha (the layout of log_alpha: [T, H, d_k], [T, H] for one gate
+    per head, None without a gate), dbeta [T, H], dh0 [N, H, d_k, d_v].
+    A per-head gate reaches every key channel, so its gradient is the sum of
+    the per-channel gradients over the channels."""
+    q = np.asarray(q)
+    T, H, dk = q.shape
+    dv = np.asarray(v).shape[2]
+    if cu_seqlens is None:
+        cu = np.array([0, T], dtype=np.int64)
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    N = cu.shape[0] - 1
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens[-1] must equal the token count")
+    if scale is None:
+        scale = 1.0 / np.sqrt(dk)
+    la = _gate(log_alpha, (T, H), dk)
+    d = lambda x, shape: None if x is None else np.ascontiguousarray(
+        np.asarray(x, dtype=np.float64).reshape(shape))
+    h0a, dOa, dhTa = d(h0, (N, H, dk, dv)), d(do, (T, H, dv)), d(dhT, (N, H, dk, dv))
+    out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+               dlog_alpha=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)),
+               dh0=np.zeros((N, H, dk, dv)))
+    rc = _load_bwd().kdaref_backward(
+        _ptr(_f32(q, (T, H, dk)), ctypes.c_float), _ptr(_f32(k, (T, H, dk)), ctypes.c_float),
+        _ptr(_f32(v, (T, H, dv)), ctypes.c_float), _ptr(la, ctypes.c_float),
+        _ptr(_f32(beta, (T, H)), ctypes.c_float), _ptr(h0a, ctypes.c_double),
+        _ptr(cu, ctypes.c_int64), N, H, dk, dv, float(scale),
+        _ptr(dOa, ctypes.c_double), _ptr(dhTa, ctypes.c_double),
+        _ptr(out["dq"], ctypes.c_double), _ptr(out["dk"], ctypes.c_double),
+        _ptr(out["dv"], ctypes.c_double), _ptr(out["dlog_alpha"], ctypes.c_double),
+        _ptr(out["dbeta"], ctypes.c_double), _ptr(out["dh0"], ctypes.c_double), int(threads))
+    if rc != 0:
+        raise RuntimeError("kdaref_backward failed with code %d" % rc)
+    if log_alpha is None:
+        out["dlog_alpha"] = None
+    elif np.asarray(log_alpha).shape == (T, H):
+        out["dlog_alpha"] = out["dlog_alpha"].sum(axis=-1)
+    return out
