@@ -28,7 +28,8 @@ __all__ = [
     "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "GATES", "PrefillOptions",
     "DecodeOptions", "library_path", "load_library",
     "abi_version", "status_string", "prefill_options", "prefill_workspace_bytes", "prefill",
-    "decode_step", "DecodeMultiOptions", "decode_multi", "EXPORTED_SYMBOLS",
+    "decode_step", "DecodeMultiOptions", "decode_multi", "BwdOptions",
+    "backward_workspace_bytes", "backward", "EXPORTED_SYMBOLS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,11 +65,16 @@ class DecodeMultiOptions(ctypes.Structure):
                 ("state_index", ctypes.c_void_p), ("lengths", ctypes.c_void_p),
                 ("write_state", ctypes.c_int32)]
 
+class BwdOptions(ctypes.Structure):
+    """Mirror of kda_bwd_options."""
+    _fields_ = [("gate", ctypes.c_int32), ("block_chunks", ctypes.c_int32)]
+
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
                     "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill_workspace_bytes_ex",
                     "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step",
-                    "kda_decode_step_ex", "kda_decode_multi")
+                    "kda_decode_step_ex", "kda_decode_multi", "kda_bwd_workspace_bytes",
+                    "kda_bwd")
 
 
 class KDAError(RuntimeError):
@@ -121,6 +127,13 @@ def load_library():
     lib.kda_decode_multi.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                                      vp, ctypes.POINTER(DecodeMultiOptions), vp]
     lib.kda_decode_multi.restype = ctypes.c_int
+    lib.kda_bwd_workspace_bytes.argtypes = [i64, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(BwdOptions)]
+    lib.kda_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, i32, f32,
+                            vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
+                            ctypes.POINTER(BwdOptions), vp]
+    lib.kda_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -389,4 +402,65 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
                               ctypes.byref(opts), _stream(dev))
     if st != 0:
         raise KDAError(st, "kda_decode_multi")
+    return out
+
+
+def backward_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
+                             dtype: int = DTYPE_BF16, gate="channel", block_chunks=0) -> int:
+    opts = BwdOptions(_gate_code(gate), block_chunks)
+    return int(load_library().kda_bwd_workspace_bytes(total_T, N, H, d_k, d_v, dtype,
+                                                      ctypes.byref(opts)))
+
+
+def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, scale=None,
+             gate="channel", want_dh0=True, block_chunks=0, workspace=None):
+    """Gradients of <o, do> + <hT, dhT> for the prefill on these inputs.
+
+    Inputs as for prefill() (bf16 q, k, v with d_k = d_v = 128); do: [T, H,
+    d_v] bf16, the adjoint of o; dhT: [N, H, d_k, d_v] fp32 or None (zeros).
+    Returns a dict: dq, dk, dv (bf16, the shapes of q, k, v), dlog_alpha
+    (fp32, the layout of log_alpha; None without a gate), dbeta [T, H]
+    fp32, dh0 [N, H, d_k, d_v] fp32 (None when want_dh0 is False)."""
+    torch = _torch()
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [T, H, d_k]")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a GPU (HIP) device")
+    dt = q.dtype
+    code = _dtype_code(q)
+    _check(q, "q", (T, H, dk), dt, dev)
+    _check(k, "k", (T, H, dk), dt, dev)
+    _check(v, "v", (T, H, dv), dt, dev)
+    _check(do, "do", (T, H, dv), dt, dev)
+    log_alpha, gcode = _check_gate(log_alpha, gate, (T, H), dk, dev)
+    _check(beta, "beta", (T, H), torch.float32, dev)
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+    N = cu_seqlens.shape[0] - 1
+    if h0 is not None:
+        _check(h0, "h0", (N, H, dk, dv), torch.float32, dev)
+    if dhT is not None:
+        _check(dhT, "dhT", (N, H, dk, dv), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(dk)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dlog_alpha=None if log_alpha is None else torch.empty_like(log_alpha),
+               dbeta=torch.empty_like(beta),
+               dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
+    opts = BwdOptions(gcode, block_chunks)
+    need = int(lib.kda_bwd_workspace_bytes(T, N, H, dk, dv, code, ctypes.byref(opts)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(h0),
+                     _ptr(cu_seqlens), T, N, H, dk, dv, code, float(scale), _ptr(do), _ptr(dhT),
+                     _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dlog_alpha"]),
+                     _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace), workspace.numel(),
+                     ctypes.byref(opts), _stream(dev))
+    if st != 0:
+        raise KDAError(st, "kda_bwd")
     return out

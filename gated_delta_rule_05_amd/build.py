@@ -20,7 +20,7 @@ OBJDIR = os.path.join(ROOT, "_build", "kda")
 LIB = os.path.join(PKG, "libkda.so")
 
 SOURCES = ["kda_api.cpp", "decode.hip", "plan.hip", "prefill_valu.hip",
-           "prefill_mfma.hip", "prefill_wy.hip"]
+           "prefill_mfma.hip", "prefill_wy.hip", "backward.hip"]
 
 HIPCC_FLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -1,0 +1,892 @@
+// backward.hip -- gradients of the chunked KDA prefill on gfx950.
+//
+// L = <o, dO> + <hT, dhT>; the gradients of L with respect to q, k, v,
+// log_alpha, beta and h0, for the recurrence of "Kimi Delta Attention: la
+// atencion lineal detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi
+// Delta Attention paso a paso", in its chunked (UT/WY) form.  That page
+// names chunkwise computation as the production form of the forward pass;
+// "Kimi Linear acaba de superar a la atención completa en sus propios
+// términos" (section "Cómo Kimi Linear utiliza una memoria recurrente más
+// inteligente") presents the chunkwise algorithm as what makes training
+// efficient.  The derivation below is ours.
+//
+// One chunk (C = 64 rows r, s), S its start state, g the within-chunk
+// cumulative log gate, G = g of its last row, Kg = K e^g, Kn = K e^-g,
+// Qg = Q e^g, Kd = K e^{G-g}, gamma = e^G:
+//     B = Kg Kn^T, A = strict_lower(Diag(beta) B), Minv = (I + A)^-1,
+//     T = Minv Diag(beta), R = V - Kg S, E = T R  (= U - W S, U = T V, W = T Kg),
+//     P = lower(Qg Kn^T) (diagonal included),
+//     O = scale (Qg S + P E),   S' = Diag(gamma) S + Kd^T E.
+// Given dO and dS' (the adjoint of the chunk's end state), by reverse-mode
+// differentiation of those lines:
+//     dE  = Kd dS' + scale P^T dO                            (carry)
+//     dS  = Diag(gamma) dS' + scale Qg^T dO - W^T dE         (carry, serial)
+//     dV  = T^T dE,  dT = dE R^T,  dKg_W = -dV S^T,  dQg_S = scale dO S^T,
+//     dKd = E dS'^T,  dP = lower(scale dO E^T),  dgamma = rowsum(dS' . S),
+//     dbeta_T = diag(Minv^T dT),  dA = -strict_lower(Minv^T dT Diag(beta) Minv^T),
+//     dB = Diag(beta) dA,  dbeta_A = rowsum(dA . B),
+//     dKg = dKg_W + dB Kn,  dKn = dP^T Qg + dB^T Kg,  dQg = dQg_S + dP Kn,
+//     dK = dKg e^g + dKn e^-g + dKd e^{G-g},  dQ = dQg e^g,
+//     dg = dKg.Kg - dKn.Kn + dQg.Qg - dKd.Kd,  dG = colsum(dKd.Kd) + dgamma.gamma,
+//     dlog_alpha[s] = sum_{r >= s} dg[r] + dG,   dbeta = dbeta_T + dbeta_A.
+//
+// Passes (one call): the forward two-pass prefill records the start state of
+// every chunk (no outputs); then, over blocks of chunks from the last:
+//   prep   (chunk-parallel) recomputes a chunk's operands: Kd, Kg, scale P^T,
+//          scale Qg^T, -W^T, Minv, B, gamma;
+//   carry  (serial per (sequence, head, 64 value columns)) walks the chunks
+//          backwards with dS in registers, storing dS' and dE of each chunk;
+//   grad_a (chunk-parallel) the products with the states: dV, dT, dKg_W,
+//          dQg_S, dKd, dP, dgamma;
+//   grad_b (chunk-parallel) the triangular-system and gate terms, and the
+//          gradients of q, k, log_alpha and beta.
+// Every product is a bf16 MFMA (16x16x32) with fp32 accumulation on
+// operands staged in LDS; states, adjoints and gates stay fp32.
+#include <algorithm>
+
+#include "kda_device.h"
+#include "kda_internal.h"
+#include "kda_mfma.h"
+
+namespace kda {
+namespace {
+
+constexpr int C = 64;          // chunk rows
+constexpr int D = 128;         // d_k = d_v
+constexpr int NT = 256;        // threads of the chunk kernels (4 waves)
+constexpr int LDD = D + 8;     // padded LDS row of a [.][D] bf16 matrix
+constexpr int LDC = C + 8;     // padded LDS row of a [.][C] bf16 matrix
+constexpr int kCarryTile = 64; // value columns per carry work-group
+
+// per-(chunk, head) operands written by the prep pass (bytes)
+constexpr int kOffKd = 0;                    // [C][D] bf16   K e^{G-g}
+constexpr int kOffKg = kOffKd + C * D * 2;   // [C][D] bf16   K e^{g}
+constexpr int kOffPt = kOffKg + C * D * 2;   // [C][C] bf16   scale P^T
+constexpr int kOffQt = kOffPt + C * C * 2;   // [D][C] bf16   scale Qg^T
+constexpr int kOffWt = kOffQt + D * C * 2;   // [D][C] bf16   -W^T
+constexpr int kOffMinv = kOffWt + D * C * 2; // [C][C] fp32   (I + A)^-1
+constexpr int kOffB = kOffMinv + C * C * 4;  // [C][C] fp32   Kg Kn^T
+constexpr int kOffGam = kOffB + C * C * 4;   // [D]    fp32   e^{G}
+constexpr int kSlot = kOffGam + D * 4;
+// per-(chunk, head) terms from grad_a to grad_b (fp32)
+constexpr int gOffKgW = 0;                   // [C][D] dKg_W
+constexpr int gOffQgS = gOffKgW + C * D * 4; // [C][D] dQg_S
+constexpr int gOffKd = gOffQgS + C * D * 4;  // [C][D] dKd
+constexpr int gOffT = gOffKd + C * D * 4;    // [C][C] dT
+constexpr int gOffP = gOffT + C * C * 4;     // [C][C] dP
+constexpr int gOffGam = gOffP + C * C * 4;   // [D]    dgamma
+constexpr int kGrad = gOffGam + D * 4;
+constexpr int64_t kState = static_cast<int64_t>(D) * D;   // floats per state
+
+static_assert(kSlot % 256 == 0 && kGrad % 256 == 0, "256-byte aligned records");
+
+// ---- the chunk a work-group of a chunk-parallel pass owns
+struct ChunkRef {
+    int n, h, j, len;     // sequence, head, chunk index in the sequence, rows
+    int64_t t0;           // first token
+    int64_t slot;         // (sequence, chunk in block, head) record index
+};
+__device__ __forceinline__ bool chunk_of(int64_t b, int H, int c_lo, int L_b,
+                                         const int32_t* cu, ChunkRef& c) {
+    c.h = static_cast<int>(b % H);
+    const int64_t q = b / H;
+    const int jj = static_cast<int>(q % L_b);
+    c.n = static_cast<int>(q / L_b);
+    c.j = c_lo + jj;
+    c.slot = b;
+    c.t0 = static_cast<int64_t>(cu[c.n]) + static_cast<int64_t>(c.j) * C;
+    const int64_t end = cu[c.n + 1];
+    c.len = static_cast<int>(min<int64_t>(C, end - c.t0));
+    return c.len > 0;
+}
+
+// acc(16x16 tile) of A (M x K, row m at a + m * lda, K contiguous) times B,
+// B given as Bt (N x K, row n at bt + n * ldb): lane (g, ln) reads
+// A[m0 + ln][8g..8g+7] and Bt[n0 + ln][8g..8g+7] per 32-deep step.
+template <int K>
+__device__ __forceinline__ f32x4 tile_mm(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
+                                         int lane, f32x4 acc) {
+    const int g = lane >> 4, ln = lane & 15;
+    const bf16_t* ap = a + ln * lda + 8 * g;
+    const bf16_t* bp = bt + ln * ldb + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < K; kk += 32)
+        acc = mma32(*reinterpret_cast<const u32x4*>(ap + kk),
+                    *reinterpret_cast<const u32x4*>(bp + kk), acc);
+    return acc;
+}
+
+// all 16x16 tiles (mi < MT, ni < NT_) of A B, spread over the 4 waves;
+// fn(mi, ni, acc) consumes each (acc[i] = row 16 mi + 4g + i, column 16 ni + ln)
+template <int MT, int NTL, int K, typename Fn>
+__device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
+                                   Fn&& fn) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int t = wave; t < MT * NTL; t += NT / 64) {
+        const int mi = t / NTL, ni = t - mi * NTL;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = tile_mm<K>(a + 16 * mi * lda, lda, bt + 16 * ni * ldb, ldb, lane, acc);
+        fn(mi, ni, acc);
+    }
+}
+
+// store 4 values of one column, rows r0..r0+3, into a transposed bf16
+// matrix (row = column index): one 8-byte LDS or global store
+__device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
+    *reinterpret_cast<u32x2*>(p) = u32x2{pk(x[0], x[1]), pk(x[2], x[3])};
+}
+
+template <int GATE>
+__device__ __forceinline__ float gate_at(const float* la, int64_t row, int H, int h, int c) {
+    if constexpr (GATE == kGateChannel) return la[row * D + c];
+    else if constexpr (GATE == kGateHead) return la[row];
+    else return 0.f;
+}
+
+// cumulative gates of the chunk's rows, per channel, into g[C][D] (rows past
+// the chunk repeat the last row); beta of its rows into bs[C] (0 past it)
+template <int GATE>
+__device__ __forceinline__ void load_gates(const float* la, const float* beta, const ChunkRef& c,
+                                           int H, float* g, float* bs) {
+    const int tid = threadIdx.x;
+    if (tid < D) {
+        float run = 0.f;
+        for (int r = 0; r < C; ++r) {
+            if (r < c.len) run += gate_at<GATE>(la, (c.t0 + r) * H + c.h, H, c.h, tid);
+            g[r * D + tid] = run;
+        }
+    } else if (tid < D + C) {
+        const int r = tid - D;
+        bs[r] = r < c.len ? beta[(c.t0 + r) * H + c.h] : 0.f;
+    }
+}
+
+// ===================================================================
+// prep: a chunk's operands for the backward passes
+// ===================================================================
+struct alignas(16) PrepLds {
+    float g[C * D];
+    bf16_t kg[C * LDD], kn[C * LDD], qg[C * LDD];
+    bf16_t kgt[D * LDC];
+    float bm[C * (C + 1)], mi[C * (C + 1)];
+    bf16_t tt[C * LDC];
+    float bs[C];
+};
+
+template <int GATE>
+__global__ __launch_bounds__(NT)
+void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                     const float* __restrict__ la, const float* __restrict__ beta,
+                     const int32_t* __restrict__ cu, int H, int c_lo, int L_b, float scale,
+                     uint8_t* __restrict__ slots)
+{
+    __shared__ PrepLds sm;
+    ChunkRef c;
+    if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    uint8_t* out = slots + c.slot * static_cast<int64_t>(kSlot);
+    bf16_t* oKd = reinterpret_cast<bf16_t*>(out + kOffKd);
+    bf16_t* oKg = reinterpret_cast<bf16_t*>(out + kOffKg);
+    bf16_t* oPt = reinterpret_cast<bf16_t*>(out + kOffPt);
+    bf16_t* oQt = reinterpret_cast<bf16_t*>(out + kOffQt);
+    bf16_t* oWt = reinterpret_cast<bf16_t*>(out + kOffWt);
+    float* oMinv = reinterpret_cast<float*>(out + kOffMinv);
+    float* oB = reinterpret_cast<float*>(out + kOffB);
+    float* oGam = reinterpret_cast<float*>(out + kOffGam);
+
+    load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
+    __syncthreads();
+    // gated keys and queries; rows past the chunk are zero
+    for (int idx = tid; idx < C * (D / 4); idx += NT) {
+        const int r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+        if (r < c.len) {
+            const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
+            kv = elem<bf16_t>::load4(k + row);
+            qv = elem<bf16_t>::load4(q + row);
+        }
+        const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+        float kg[4], kn[4], qg[4], kd[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float gv = sm.g[r * D + c0 + e], G = sm.g[(c.len - 1) * D + c0 + e];
+            const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
+            kg[e] = kk[e] * eg;
+            kn[e] = kk[e] * en;
+            qg[e] = qq[e] * eg;
+            kd[e] = kk[e] * ed;
+            sm.kgt[(c0 + e) * LDC + r] = bf(kg[e]);
+            oQt[(c0 + e) * C + r] = bf(scale * qg[e]);
+        }
+        const f32x4 vkg = {kg[0], kg[1], kg[2], kg[3]}, vkn = {kn[0], kn[1], kn[2], kn[3]};
+        const f32x4 vqg = {qg[0], qg[1], qg[2], qg[3]}, vkd = {kd[0], kd[1], kd[2], kd[3]};
+        put4t(sm.kg + r * LDD + c0, vkg);
+        put4t(sm.kn + r * LDD + c0, vkn);
+        put4t(sm.qg + r * LDD + c0, vqg);
+        put4t(oKd + r * D + c0, vkd);
+        put4t(oKg + r * D + c0, vkg);
+    }
+    if (tid < D) oGam[tid] = gate_exp(sm.g[(c.len - 1) * D + tid]);
+    __syncthreads();
+    // B = Kg Kn^T (fp32) and scale P^T, P = lower(Qg Kn^T)
+    mm<4, 4, D>(sm.kg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
+            sm.bm[r * (C + 1) + s] = acc[i];
+            oB[r * C + s] = acc[i];
+        }
+    });
+    mm<4, 4, D>(sm.qg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+        const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
+        f32x4 x;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = s <= r0 + i ? scale * acc[i] : 0.f;
+        put4t(oPt + s * C + r0, x);
+    });
+    __syncthreads();
+    // Minv = (I + A)^-1, A = strict_lower(Diag(beta) B): each column by
+    // forward substitution, one thread per column
+    if (tid < C) {
+        const int col = tid;
+        for (int r = 0; r < C; ++r) {
+            float x = r == col ? 1.f : 0.f;
+            if (r > col) {
+                const float br = sm.bs[r];
+                float acc = 0.f;
+                for (int s = col; s < r; ++s) acc += sm.bm[r * (C + 1) + s] * sm.mi[s * (C + 1) + col];
+                x = -br * acc;
+            }
+            sm.mi[r * (C + 1) + col] = x;
+        }
+    }
+    __syncthreads();
+    for (int idx = tid; idx < C * C; idx += NT) {
+        const int r = idx / C, s = idx % C;
+        const float m = sm.mi[r * (C + 1) + s];
+        oMinv[idx] = m;
+        sm.tt[r * LDC + s] = bf(m * sm.bs[s]);     // T = Minv Diag(beta)
+    }
+    __syncthreads();
+    // -W^T, W = T Kg
+    mm<4, 8, C>(sm.tt, LDC, sm.kgt, LDC, [&](int mi, int ni, f32x4 acc) {
+        put4t(oWt + (16 * ni + ln) * C + 16 * mi + 4 * g4, -acc);
+    });
+}
+
+// ===================================================================
+// carry: dS backwards through the chunks of one block
+// ===================================================================
+struct alignas(16) CarryLds {
+    bf16_t kd[C * LDD];
+    bf16_t pt[C * LDC];
+    bf16_t qt[D * LDC];
+    bf16_t wt[D * LDC];
+    float gam[D];
+    bf16_t dot[kCarryTile * LDC];      // dO^T of the tile's columns
+    bf16_t dst[4][16 * LDD];           // each wave's dS slab, transposed
+    bf16_t det[4][16 * LDC];           // each wave's dE slab, transposed
+};
+
+// copy a [rows][cols] bf16 matrix (global, contiguous) into LDS rows of ld
+__device__ __forceinline__ void copy_rows(bf16_t* dst, int ld, const bf16_t* src, int rows,
+                                          int cols) {
+    const int per = cols / 8;
+    for (int u = threadIdx.x; u < rows * per; u += NT) {
+        const int r = u / per, x = (u % per) * 8;
+        *reinterpret_cast<u32x4*>(dst + r * ld + x) = *reinterpret_cast<const u32x4*>(src + r * cols + x);
+    }
+}
+
+__global__ __launch_bounds__(NT)
+void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dO,
+                      const int32_t* __restrict__ cu, int N, int H, int c_lo, int L_b,
+                      float* __restrict__ dstate, float* __restrict__ dsblk,
+                      float* __restrict__ deblk, float* __restrict__ dh0)
+{
+    __shared__ CarryLds sm;
+    constexpr int R = D / kCarryTile;
+    const int pair = blockIdx.x / R, tile = blockIdx.x % R;
+    const int n = pair / H, h = pair % H;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    const int64_t t_begin = cu[n], t_end = cu[n + 1];
+    const int nch = static_cast<int>((t_end - t_begin + C - 1) / C);
+    const int hi = min(nch, c_lo + L_b) - 1;          // last chunk of this block
+    const int jc = tile * kCarryTile + 16 * wave + ln; // this lane's value column
+    float* st = dstate + (static_cast<int64_t>(n) * H + h) * kState;
+    if (hi < c_lo) {
+        // no chunk here; an empty sequence still gets dh0 = dhT (or zeros)
+        if (c_lo == 0 && dh0) {
+            float* d0 = dh0 + (static_cast<int64_t>(n) * H + h) * kState;
+            for (int e = tid; e < D * kCarryTile; e += NT) {
+                const int row = e / kCarryTile, col = tile * kCarryTile + e % kCarryTile;
+                d0[row * D + col] = st[row * D + col];
+            }
+        }
+        return;
+    }
+    // dS slab: S[m][i] = dS[16m + 4g + i][jc]
+    f32x4 S[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) S[m][i] = st[(16 * m + 4 * g4 + i) * D + jc];
+
+    for (int j = hi; j >= c_lo; --j) {
+        const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
+        const uint8_t* sp = slots + slot * static_cast<int64_t>(kSlot);
+        const int64_t t0 = t_begin + static_cast<int64_t>(j) * C;
+        const int len = static_cast<int>(min<int64_t>(C, t_end - t0));
+        copy_rows(sm.kd, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKd), C, D);
+        copy_rows(sm.pt, LDC, reinterpret_cast<const bf16_t*>(sp + kOffPt), C, C);
+        copy_rows(sm.qt, LDC, reinterpret_cast<const bf16_t*>(sp + kOffQt), D, C);
+        copy_rows(sm.wt, LDC, reinterpret_cast<const bf16_t*>(sp + kOffWt), D, C);
+        if (tid < D) sm.gam[tid] = reinterpret_cast<const float*>(sp + kOffGam)[tid];
+        {   // dO^T of the tile: thread (row r, 16 columns)
+            const int r = tid >> 2, part = tid & 3;
+            u32x4 a = {0u, 0u, 0u, 0u}, b = a;
+            if (r < len) {
+                const bf16_t* src = dO + ((t0 + r) * H + h) * D + tile * kCarryTile + 16 * part;
+                a = *reinterpret_cast<const u32x4*>(src);
+                b = *reinterpret_cast<const u32x4*>(src + 8);
+            }
+            const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+#pragma unroll
+            for (int x = 0; x < 8; ++x) {
+                sm.dot[(16 * part + 2 * x) * LDC + r] = static_cast<bf16_t>(w[x] & 0xffffu);
+                sm.dot[(16 * part + 2 * x + 1) * LDC + r] = static_cast<bf16_t>(w[x] >> 16);
+            }
+        }
+        // dS' of this chunk (fp32, for grad_a) and as a bf16 B operand
+        float* dsp = dsblk + slot * kState;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dsp[(16 * m + 4 * g4 + i) * D + jc] = S[m][i];
+            put4t(&sm.dst[wave][ln * LDD + 16 * m + 4 * g4], S[m]);
+        }
+        __syncthreads();
+        // dE = Kd dS' + scale P^T dO  (this wave's 16 columns, 4 row tiles)
+        float* dep = deblk + slot * (static_cast<int64_t>(C) * D);
+        const bf16_t* dsw = sm.dst[wave];
+        const bf16_t* dow = sm.dot + 16 * wave * LDC;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = tile_mm<D>(sm.kd + 16 * m * LDD, LDD, dsw, LDD, lane, acc);
+            acc = tile_mm<C>(sm.pt + 16 * m * LDC, LDC, dow, LDC, lane, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dep[(16 * m + 4 * g4 + i) * D + jc] = acc[i];
+            put4t(&sm.det[wave][ln * LDC + 16 * m + 4 * g4], acc);
+        }
+        __syncthreads();
+        // dS = Diag(gamma) dS' + scale Qg^T dO - W^T dE
+        const bf16_t* dew = sm.det[wave];
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            f32x4 acc;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * m + 4 * g4 + i] * S[m][i];
+            acc = tile_mm<C>(sm.qt + 16 * m * LDC, LDC, dow, LDC, lane, acc);
+            acc = tile_mm<C>(sm.wt + 16 * m * LDC, LDC, dew, LDC, lane, acc);
+            S[m] = acc;
+        }
+        __syncthreads();
+    }
+    float* dst_out = c_lo == 0 ? dh0 : st;
+    if (dst_out) {
+        dst_out += c_lo == 0 ? (static_cast<int64_t>(n) * H + h) * kState : 0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst_out[(16 * m + 4 * g4 + i) * D + jc] = S[m][i];
+    }
+}
+
+// ===================================================================
+// grad_a: the products with the chunk's start state and its adjoints
+// ===================================================================
+struct alignas(16) GradALds {
+    bf16_t s0[D * LDD];        // S (row c, columns j)
+    bf16_t s0t[D * LDD];       // S^T; later dS'
+    bf16_t kg[C * LDD];        // Kg; later E
+    bf16_t r[C * LDD];         // V, then R; later dV
+    bf16_t brt[D * LDC];       // (Diag(beta) R)^T; later dE^T; later dO
+    bf16_t mv[C * LDC];        // Minv
+    bf16_t mvt[C * LDC];       // Minv^T
+    bf16_t de[C * LDD];        // dE
+    float bs[C];
+};
+
+// fp32 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
+__device__ __forceinline__ void stage_f32(const float* src, int rows, bf16_t* rm, int ld,
+                                          bf16_t* tr, int ldt) {
+    for (int u = threadIdx.x; u < rows * (D / 4); u += NT) {
+        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (src) x = *reinterpret_cast<const f32x4*>(src + r * D + c0);
+        if (rm) put4t(rm + r * ld + c0, x);
+        if (tr) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tr[(c0 + e) * ldt + r] = bf(x[e]);
+        }
+    }
+}
+
+// the start state of chunk j of sequence n: h0 (or null = zeros) for the
+// first chunk, else the state the forward pass recorded after chunk j-1
+__device__ __forceinline__ const float* start_state(const ChunkRef& c, const float* h0,
+                                                    const float* sall, const int32_t* cu, int H) {
+    if (c.j == 0) return h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState : nullptr;
+    const int64_t idx = c.n + cu[c.n] / C + (c.j - 1);
+    return sall + (idx * H + c.h) * kState;
+}
+
+template <typename T>
+__global__ __launch_bounds__(NT)
+void bwd_grad_a_kernel(const uint8_t* __restrict__ slots, uint8_t* __restrict__ grads,
+                       const float* __restrict__ dsblk, const float* __restrict__ deblk,
+                       const float* __restrict__ sall, const float* __restrict__ h0,
+                       const T* __restrict__ v, const T* __restrict__ dO,
+                       const float* __restrict__ beta, const int32_t* __restrict__ cu, int H,
+                       int c_lo, int L_b, float scale, T* __restrict__ dv)
+{
+    __shared__ GradALds sm;
+    ChunkRef c;
+    if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
+    uint8_t* gp = grads + c.slot * static_cast<int64_t>(kGrad);
+    float* gKgW = reinterpret_cast<float*>(gp + gOffKgW);
+    float* gQgS = reinterpret_cast<float*>(gp + gOffQgS);
+    float* gKd = reinterpret_cast<float*>(gp + gOffKd);
+    float* gT = reinterpret_cast<float*>(gp + gOffT);
+    float* gP = reinterpret_cast<float*>(gp + gOffP);
+    float* gGam = reinterpret_cast<float*>(gp + gOffGam);
+    const float* S = start_state(c, h0, sall, cu, H);
+    const float* dSp = dsblk + c.slot * kState;
+    const float* dE = deblk + c.slot * (static_cast<int64_t>(C) * D);
+
+    // ---- R = V - Kg S, and (Diag(beta) R)^T
+    stage_f32(S, D, sm.s0, LDD, sm.s0t, LDD);
+    copy_rows(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
+    for (int u = tid; u < C * (D / 4); u += NT) {
+        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < c.len) x = elem<T>::load4(v + ((c.t0 + r) * H + c.h) * D + c0);
+        put4t(sm.r + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
+    }
+    if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
+    __syncthreads();
+    mm<4, 8, D>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
+        const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
+        f32x4 br;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16_t* p = sm.r + (r0 + i) * LDD + col;
+            const float rv = bf16_to_f32(*p) - acc[i];
+            *p = bf(rv);
+            br[i] = sm.bs[r0 + i] * rv;
+        }
+        put4t(sm.brt + col * LDC + r0, br);
+    });
+    // ---- E = Minv (Diag(beta) R)
+    {
+        const float* mv = reinterpret_cast<const float*>(sp + kOffMinv);
+        for (int u = tid; u < C * C; u += NT) {
+            const int r = u / C, s = u % C;
+            const bf16_t x = bf(mv[u]);
+            sm.mv[r * LDC + s] = x;
+            sm.mvt[s * LDC + r] = x;
+        }
+    }
+    __syncthreads();
+    bf16_t* E = sm.kg;   // Kg is no longer needed
+    mm<4, 8, C>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
+    });
+    __syncthreads();
+    // ---- dT = dE R^T; dV = T^T dE = Diag(beta) Minv^T dE
+    bf16_t* det = sm.brt;
+    stage_f32(dE, C, sm.de, LDD, det, LDC);
+    __syncthreads();
+    mm<4, 4, D>(sm.de, LDD, sm.r, LDD, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gT[(16 * mi + 4 * g4 + i) * C + 16 * ni + ln] = acc[i];
+    });
+    __syncthreads();
+    bf16_t* dV = sm.r;   // R is no longer needed
+    mm<4, 8, C>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
+            const float x = sm.bs[s] * acc[i];
+            dV[s * LDD + col] = bf(x);
+            if (s < c.len) elem<T>::store(dv + ((c.t0 + s) * H + c.h) * D + col, x);
+        }
+    });
+    __syncthreads();
+    // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T
+    bf16_t* dOl = sm.brt;   // dE^T is no longer needed
+    for (int u = tid; u < C * (D / 4); u += NT) {
+        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < c.len) x = elem<T>::load4(dO + ((c.t0 + r) * H + c.h) * D + c0);
+        put4t(dOl + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
+    }
+    __syncthreads();
+    mm<4, 8, D>(dV, LDD, sm.s0, LDD, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gKgW[(16 * mi + 4 * g4 + i) * D + 16 * ni + ln] = -acc[i];
+    });
+    mm<4, 8, D>(dOl, LDD, sm.s0, LDD, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gQgS[(16 * mi + 4 * g4 + i) * D + 16 * ni + ln] = scale * acc[i];
+    });
+    // ---- dS' staged over S^T; dgamma = rowsum(dS' . S) in fp32
+    bf16_t* dsl = sm.s0t;
+    __syncthreads();
+    {
+        const int row = tid >> 1, half = tid & 1;
+        float part = 0.f;
+        for (int x = 0; x < D / 2; x += 4) {
+            const int col = 64 * half + x;
+            const f32x4 d = *reinterpret_cast<const f32x4*>(dSp + row * D + col);
+            f32x4 s = {0.f, 0.f, 0.f, 0.f};
+            if (S) s = *reinterpret_cast<const f32x4*>(S + row * D + col);
+            part += d[0] * s[0] + d[1] * s[1] + d[2] * s[2] + d[3] * s[3];
+            put4t(dsl + row * LDD + col, d);
+        }
+        part += __shfl_xor(part, 1);
+        if (half == 0) gGam[row] = part;
+    }
+    __syncthreads();
+    // ---- dKd = E dS'^T, dP = lower(scale dO E^T)
+    mm<4, 8, D>(E, LDD, dsl, LDD, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) gKd[(16 * mi + 4 * g4 + i) * D + 16 * ni + ln] = acc[i];
+    });
+    mm<4, 4, D>(dOl, LDD, E, LDD, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
+            gP[r * C + s] = s <= r ? scale * acc[i] : 0.f;
+        }
+    });
+}
+
+// ===================================================================
+// grad_b: the triangular system, the gates, and dq, dk, dlog_alpha, dbeta
+// ===================================================================
+struct alignas(16) GradBLds {
+    float g[C * D];            // cumulative gates; later dlog_alpha rows (head gate)
+    float dg[C * D];
+    bf16_t knt[D * LDC], kgt[D * LDC], qgt[D * LDC];
+    bf16_t ra[2][C * LDC];     // Minv, Minv^T; later dP, dP^T
+    bf16_t rb[2][C * LDC];     // (dT Diag(beta))^T, Z; later dB, dB^T
+    float bs[C];
+    float db[C];               // dbeta
+    float dbp[4][C];           // dbeta_A per 16-column block, summed in order
+    float dG[D];
+};
+
+template <typename T, int GATE>
+__global__ __launch_bounds__(NT)
+void bwd_grad_b_kernel(const uint8_t* __restrict__ slots, const uint8_t* __restrict__ grads,
+                       const T* __restrict__ q, const T* __restrict__ k,
+                       const float* __restrict__ la, const float* __restrict__ beta,
+                       const int32_t* __restrict__ cu, int H, int c_lo, int L_b,
+                       T* __restrict__ dq, T* __restrict__ dk, float* __restrict__ dla,
+                       float* __restrict__ dbeta)
+{
+    __shared__ GradBLds sm;
+    ChunkRef c;
+    if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
+    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
+    const uint8_t* gp = grads + c.slot * static_cast<int64_t>(kGrad);
+    const float* mv = reinterpret_cast<const float*>(sp + kOffMinv);
+    const float* Bm = reinterpret_cast<const float*>(sp + kOffB);
+    const float* gKgW = reinterpret_cast<const float*>(gp + gOffKgW);
+    const float* gQgS = reinterpret_cast<const float*>(gp + gOffQgS);
+    const float* gKd = reinterpret_cast<const float*>(gp + gOffKd);
+    const float* gT = reinterpret_cast<const float*>(gp + gOffT);
+    const float* gP = reinterpret_cast<const float*>(gp + gOffP);
+    const float* gGam = reinterpret_cast<const float*>(gp + gOffGam);
+
+    load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
+    __syncthreads();
+    // gated keys and queries, transposed (B operands); Minv, Minv^T;
+    // (dT Diag(beta))^T; dbeta_T = diag(Minv^T dT); dG starts at dgamma gamma
+    for (int u = tid; u < C * (D / 4); u += NT) {
+        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+        if (r < c.len) {
+            const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
+            kv = elem<T>::load4(k + row);
+            qv = elem<T>::load4(q + row);
+        }
+        const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float gv = sm.g[r * D + c0 + e];
+            const float eg = gate_exp(gv), en = gate_exp(-gv);
+            sm.kgt[(c0 + e) * LDC + r] = bf(kk[e] * eg);
+            sm.knt[(c0 + e) * LDC + r] = bf(kk[e] * en);
+            sm.qgt[(c0 + e) * LDC + r] = bf(qq[e] * eg);
+        }
+    }
+    for (int u = tid; u < C * C; u += NT) {
+        const int r = u / C, s = u % C;
+        const bf16_t x = bf(mv[u]);
+        sm.ra[0][r * LDC + s] = x;
+        sm.ra[1][s * LDC + r] = x;
+        sm.rb[0][s * LDC + r] = bf(gT[u] * sm.bs[s]);
+    }
+    if (tid < C) {
+        float acc = 0.f;
+        for (int i = 0; i < C; ++i) acc += mv[i * C + tid] * gT[i * C + tid];
+        sm.db[tid] = acc;
+    } else if (tid >= NT - D) {
+        const int ch = tid - (NT - D);
+        sm.dG[ch] = gGam[ch] * gate_exp(sm.g[(c.len - 1) * D + ch]);
+    }
+    __syncthreads();
+    // Z = Minv^T (dT Diag(beta))
+    mm<4, 4, C>(sm.ra[1], LDC, sm.rb[0], LDC, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.rb[1][(16 * mi + 4 * g4 + i) * LDC + 16 * ni + ln] = bf(acc[i]);
+    });
+    __syncthreads();
+    // dA = -strict_lower(Z Minv^T): held in registers (4 tiles per wave)
+    // until every wave is done reading Z
+    f32x4 dA[4];
+    {
+        const int wave = tid >> 6;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int t = wave + 4 * x, mi = t / 4, ni = t % 4;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            dA[x] = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.ra[0] + 16 * ni * LDC, LDC, lane, acc);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int t = wave + 4 * x, mi = t / 4, ni = t % 4;
+            const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
+            f32x4 db;
+            float rowpart[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = r0 + i;
+                const float a = s < r ? -dA[x][i] : 0.f;
+                rowpart[i] = a * Bm[r * C + s];              // dbeta_A
+                db[i] = sm.bs[r] * a;                        // dB = Diag(beta) dA
+                sm.rb[0][r * LDC + s] = bf(db[i]);
+            }
+            put4t(sm.rb[1] + s * LDC + r0, db);             // dB^T
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float p = rowpart[i];
+#pragma unroll
+                for (int m = 1; m < 16; m <<= 1) p += __shfl_xor(p, m);
+                if (ln == 0) sm.dbp[ni][r0 + i] = p;
+            }
+        }
+    }
+    // dP and dP^T over Minv (no longer needed)
+    for (int u = tid; u < C * C; u += NT) {
+        const int r = u / C, s = u % C;
+        const bf16_t x = bf(gP[u]);
+        sm.ra[0][r * LDC + s] = x;
+        sm.ra[1][s * LDC + r] = x;
+    }
+    __syncthreads();
+    // per 16x16 tile of (row r, key channel c): dKg = dKg_W + dB Kn,
+    // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain
+    {
+        const int wave = tid >> 6;
+        for (int t = wave; t < 4 * 8; t += 4) {
+            const int mi = t / 8, ni = t % 8;
+            f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 aKg = tile_mm<C>(sm.rb[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
+            f32x4 aKn = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.kgt + 16 * ni * LDC, LDC, lane, z);
+            aKn = tile_mm<C>(sm.ra[1] + 16 * mi * LDC, LDC, sm.qgt + 16 * ni * LDC, LDC, lane, aKn);
+            const f32x4 aQg = tile_mm<C>(sm.ra[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
+            const int ch = 16 * ni + ln;
+            const float G = sm.g[(c.len - 1) * D + ch];
+            float dGp = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i;
+                float dgv = 0.f;
+                if (r < c.len) {
+                    const int64_t row = ((c.t0 + r) * H + c.h) * D + ch;
+                    const float kv = elem<T>::load(k + row), qv = elem<T>::load(q + row);
+                    const float gv = sm.g[r * D + ch];
+                    const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
+                    const float dKg = aKg[i] + gKgW[r * D + ch];
+                    const float dQg = aQg[i] + gQgS[r * D + ch];
+                    const float dKn = aKn[i];
+                    const float dKd = gKd[r * D + ch];
+                    const float Kg = kv * eg, Kn = kv * en, Qg = qv * eg, Kd = kv * ed;
+                    elem<T>::store(dk + row, dKg * eg + dKn * en + dKd * ed);
+                    elem<T>::store(dq + row, dQg * eg);
+                    dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
+                    dGp += dKd * Kd;
+                }
+                sm.dg[r * D + ch] = dgv;
+            }
+            dGp += __shfl_xor(dGp, 16);
+            dGp += __shfl_xor(dGp, 32);
+            // the tiles of one channel block all belong to this wave (t = 8 mi
+            // + ni, wave = ni mod 4), so these adds happen in a fixed order
+            if (g4 == 0) atomicAdd(&sm.dG[ch], dGp);
+        }
+    }
+    __syncthreads();
+    // dlog_alpha[s] = sum_{r >= s} dg[r] + dG, per key channel
+    if (tid < D) {
+        float run = sm.dG[tid];
+        for (int r = c.len - 1; r >= 0; --r) {
+            run += sm.dg[r * D + tid];
+            if constexpr (GATE == kGateChannel) dla[((c.t0 + r) * H + c.h) * D + tid] = run;
+            else sm.g[r * D + tid] = run;
+        }
+    }
+    if (tid >= NT - C) {
+        const int r = tid - (NT - C);
+        if (r < c.len)
+            dbeta[(c.t0 + r) * H + c.h] = sm.db[r] + ((sm.dbp[0][r] + sm.dbp[1][r]) +
+                                                      (sm.dbp[2][r] + sm.dbp[3][r]));
+    }
+    if constexpr (GATE == kGateHead) {
+        __syncthreads();
+        // one gate per (token, head) reaches every key channel: the sum
+        if (tid < C && tid < c.len) {
+            float acc = 0.f;
+            for (int ch = 0; ch < D; ++ch) acc += sm.g[tid * D + ch];
+            dla[(c.t0 + tid) * H + c.h] = acc;
+        }
+    }
+}
+
+__global__ void bwd_init_kernel(const float* __restrict__ dhT, float* __restrict__ dstate,
+                                int64_t n4) {
+    for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (dhT) x = reinterpret_cast<const f32x4*>(dhT)[i];
+        reinterpret_cast<f32x4*>(dstate)[i] = x;
+    }
+}
+
+int64_t bound_chunks(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) / C : 0; }
+
+struct BwdLayout {
+    size_t fwd, sall, slots, grads, dsblk, deblk, dstate, total;
+};
+
+BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
+    BwdLayout l;
+    const size_t nh = static_cast<size_t>(N) * H;
+    const size_t blk = nh * L_b;
+    l.fwd = wy_workspace_bytes(N, H, D, D, wy_default_block_chunks(total_T, N, H, D));
+    l.sall = (static_cast<size_t>(N) + static_cast<size_t>(bound_chunks(total_T)) + 1) * H *
+             kState * 4;
+    l.slots = blk * kSlot;
+    l.grads = blk * kGrad;
+    l.dsblk = blk * kState * 4;
+    l.deblk = blk * C * D * 4;
+    l.dstate = nh * kState * 4;
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    l.total = up(l.fwd) + up(l.sall) + up(l.slots) + up(l.grads) + up(l.dsblk) + up(l.deblk) +
+              up(l.dstate);
+    return l;
+}
+
+}  // namespace
+
+int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
+    // about 1 GiB of per-block buffers (prep operands, carry outputs and
+    // grad_a terms: ~331 KB per (chunk, head)), at most the chunk count
+    const size_t per_chunk = static_cast<size_t>(N) * H *
+                             (kSlot + kGrad + kState * 4 + static_cast<size_t>(C) * D * 4);
+    int64_t L = static_cast<int64_t>((size_t{1} << 30) / per_chunk);
+    L = std::max<int64_t>(1, std::min<int64_t>(L, std::max<int64_t>(1, bound_chunks(total_T))));
+    return static_cast<int>(std::min<int64_t>(L, 64));
+}
+
+size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b) {
+    return bwd_layout(total_T, N, H, L_b).total;
+}
+
+hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream) {
+    const BwdLayout l = bwd_layout(a.total_T, a.N, a.H, L_b);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    uint8_t* fwd_ws = p;          p += up(l.fwd);
+    float* sall = reinterpret_cast<float*>(p);    p += up(l.sall);
+    uint8_t* slots = p;           p += up(l.slots);
+    uint8_t* grads = p;           p += up(l.grads);
+    float* dsblk = reinterpret_cast<float*>(p);   p += up(l.dsblk);
+    float* deblk = reinterpret_cast<float*>(p);   p += up(l.deblk);
+    float* dstate = reinterpret_cast<float*>(p);
+
+    // 1. forward: the state after every full chunk, no outputs
+    PrefillArgs f{};
+    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.beta = a.beta; f.h0 = a.h0;
+    f.cu_seqlens = a.cu_seqlens; f.o = nullptr; f.hT = nullptr; f.order = nullptr;
+    f.total_T = a.total_T; f.N = a.N; f.H = a.H; f.d_k = D; f.d_v = D; f.gate = a.gate;
+    f.dtype_f32 = false; f.scale = a.scale;
+    f.snapshots = sall; f.snap_tokens = C; f.snap_cap = -1;
+    hipError_t e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D),
+                                     fwd_ws, stream);
+    if (e != hipSuccess) return e;
+
+    // 2. backward over blocks of chunks, from the last
+    const int64_t n4 = static_cast<int64_t>(a.N) * a.H * kState / 4;
+    hipLaunchKernelGGL(bwd_init_kernel, dim3(static_cast<unsigned>(std::min<int64_t>(4096, (n4 + 255) / 256))),
+                       dim3(256), 0, stream, a.dhT, dstate, n4);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t bound = std::max<int64_t>(1, bound_chunks(a.total_T));
+    const int64_t nblk = (bound + L_b - 1) / L_b;
+    const unsigned chunks = static_cast<unsigned>(static_cast<int64_t>(a.N) * L_b * a.H);
+    const bf16_t* q = static_cast<const bf16_t*>(a.q);
+    const bf16_t* k = static_cast<const bf16_t*>(a.k);
+    const bf16_t* v = static_cast<const bf16_t*>(a.v);
+    const bf16_t* dO = static_cast<const bf16_t*>(a.dO);
+    for (int64_t b = nblk - 1; b >= 0; --b) {
+        const int c_lo = static_cast<int>(b * L_b);
+        if (a.total_T > 0) {
+            auto prep = a.gate == kGateChannel ? bwd_prep_kernel<kGateChannel>
+                      : a.gate == kGateHead    ? bwd_prep_kernel<kGateHead>
+                                               : bwd_prep_kernel<kGateNone>;
+            hipLaunchKernelGGL(prep, dim3(chunks), dim3(NT), 0, stream, q, k, a.log_alpha, a.beta,
+                               a.cu_seqlens, a.H, c_lo, L_b, a.scale, slots);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>(a.N * a.H * (D / kCarryTile))),
+                           dim3(NT), 0, stream, slots, dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
+                           dstate, dsblk, deblk, a.dh0);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        if (a.total_T == 0) continue;
+        hipLaunchKernelGGL(bwd_grad_a_kernel<bf16_t>, dim3(chunks), dim3(NT), 0, stream, slots,
+                           grads, dsblk, deblk, sall, a.h0, v, dO, a.beta, a.cu_seqlens, a.H,
+                           c_lo, L_b, a.scale, static_cast<bf16_t*>(a.dv));
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        auto gb = a.gate == kGateChannel ? bwd_grad_b_kernel<bf16_t, kGateChannel>
+                : a.gate == kGateHead    ? bwd_grad_b_kernel<bf16_t, kGateHead>
+                                         : bwd_grad_b_kernel<bf16_t, kGateNone>;
+        hipLaunchKernelGGL(gb, dim3(chunks), dim3(NT), 0, stream, slots, grads, q, k,
+                           a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo, L_b,
+                           static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk), a.dlog_alpha,
+                           a.dbeta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace kda

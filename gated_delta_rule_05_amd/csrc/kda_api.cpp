@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -375,6 +375,92 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
                     int32_t d_v, int32_t dtype, float scale, void* o, void* stream) {
     return kda_decode_step_ex(q, k, v, log_alpha, beta, S, N, H, d_k, d_v, dtype, scale, o,
                               nullptr, stream);
+}
+
+
+// ---- gradients of the prefill
+static int bwd_block_chunks(int64_t total_T, int32_t N, int32_t H,
+                            const kda_bwd_options* options, int* L_b) {
+    const int32_t blk = options ? options->block_chunks : 0;
+    if (blk < 0) return KDA_STATUS_INVALID_ARGUMENT;
+    *L_b = blk > 0 ? blk : kda::bwd_default_block_chunks(total_T, N, H);
+    int64_t chunks;
+    if (!mul_ok(static_cast<int64_t>(N) * H, *L_b, &chunks) || chunks >= (int64_t{1} << 31))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    return KDA_STATUS_OK;
+}
+
+size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                               int32_t dtype, const kda_bwd_options* options) {
+    Sizes sz;
+    if (check_sizes(total_T, N, H, d_k, d_v, dtype, options ? options->gate : 0, &sz) !=
+        KDA_STATUS_OK)
+        return 0;
+    if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16) return 0;
+    int L_b;
+    if (bwd_block_chunks(total_T, N, H, options, &L_b) != KDA_STATUS_OK) return 0;
+    return kda::bwd_workspace_bytes(total_T, N, H, L_b);
+}
+
+int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
+            const float* beta, const float* h0, const int32_t* cu_seqlens, int64_t total_T,
+            int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+            const void* dO, const float* dhT, void* dq, void* dk, void* dv, float* dlog_alpha,
+            float* dbeta, float* dh0, void* workspace, size_t workspace_bytes,
+            const kda_bwd_options* options, void* stream) {
+    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
+    Sizes sz;
+    const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, gate, &sz);
+    if (st != KDA_STATUS_OK) return st;
+    if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16) return KDA_STATUS_UNSUPPORTED;
+    if (!std::isfinite(scale) || !cu_seqlens) return KDA_STATUS_INVALID_ARGUMENT;
+    const bool any = total_T > 0;
+    if (any && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    int gs = check_gate_ptr(gate, log_alpha, any);
+    if (gs == KDA_STATUS_OK) gs = check_gate_ptr(gate, dlog_alpha, any);
+    if (gs != KDA_STATUS_OK) return gs;
+    if (gate == KDA_GATE_NONE) { log_alpha = nullptr; dlog_alpha = nullptr; }
+    const void* ptrs[] = {q, k, v, h0, dO, dhT, dq, dk, dv, dh0, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return KDA_STATUS_MISALIGNED;
+    if (!aligned4(beta) || !aligned4(dbeta) || !aligned4(cu_seqlens)) return KDA_STATUS_MISALIGNED;
+    int L_b;
+    const int bs = bwd_block_chunks(total_T, N, H, options, &L_b);
+    if (bs != KDA_STATUS_OK) return bs;
+    const size_t need = kda::bwd_workspace_bytes(total_T, N, H, L_b);
+
+    // no output may overlap an input, another output or the workspace
+    const Range inputs[] = {range_of(q, sz.qk_bytes),      range_of(k, sz.qk_bytes),
+                            range_of(v, sz.v_bytes),       range_of(log_alpha, sz.la_bytes),
+                            range_of(beta, sz.beta_bytes), range_of(cu_seqlens, (N + 1) * 4),
+                            range_of(h0, h0 ? sz.state_bytes : 0),
+                            range_of(dO, sz.v_bytes),      range_of(dhT, dhT ? sz.state_bytes : 0)};
+    const Range outputs[] = {range_of(dq, sz.qk_bytes),     range_of(dk, sz.qk_bytes),
+                             range_of(dv, sz.v_bytes),      range_of(dlog_alpha, sz.la_bytes),
+                             range_of(dbeta, sz.beta_bytes), range_of(dh0, dh0 ? sz.state_bytes : 0),
+                             range_of(workspace, static_cast<int64_t>(need))};
+    const int nout = sizeof(outputs) / sizeof(outputs[0]);   // the workspace last
+    for (int i = 0; i < nout - 1; ++i) {
+        for (const Range& in : inputs)
+            if (overlaps(outputs[i], in)) return KDA_STATUS_INVALID_ARGUMENT;
+        for (int j = i + 1; j < nout - 1; ++j)
+            if (overlaps(outputs[i], outputs[j])) return KDA_STATUS_INVALID_ARGUMENT;
+    }
+    if (workspace_bytes < need || !workspace) return KDA_STATUS_WORKSPACE_TOO_SMALL;
+    for (int i = 0; i < nout - 1; ++i)
+        if (overlaps(outputs[i], outputs[nout - 1])) return KDA_STATUS_INVALID_ARGUMENT;
+    for (const Range& in : inputs)
+        if (overlaps(outputs[nout - 1], in)) return KDA_STATUS_INVALID_ARGUMENT;
+
+    kda::BackwardArgs a{};
+    a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0;
+    a.cu_seqlens = cu_seqlens; a.dO = dO; a.dhT = dhT;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
+    a.total_T = total_T; a.N = N; a.H = H; a.gate = gate; a.scale = scale;
+    if (kda::launch_backward(a, L_b, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
+        return KDA_STATUS_HIP_ERROR;
+    return KDA_STATUS_OK;
 }
 
 }  // extern "C"

@@ -57,6 +57,32 @@ struct PrefillArgs {
     int32_t snap_tokens, snap_cap;
 };
 
+// gradients of the prefill (bf16, d_k = d_v = 128): see backward.hip
+struct BackwardArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* log_alpha;     // per the gate layout; null without a gate
+    const float* beta;
+    const float* h0;            // may be null (zero initial state)
+    const int32_t* cu_seqlens;  // device, [N+1]
+    const void* dO;             // [total_T][H][d_v], the adjoint of o
+    const float* dhT;           // may be null (zero adjoint of the final states)
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dlog_alpha;          // per the gate layout; null without a gate
+    float* dbeta;
+    float* dh0;                 // may be null (not written)
+    int64_t total_T;
+    int32_t N, H;
+    int gate;
+    float scale;
+};
+int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H);
+size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b);
+hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream);
+
 // first element of snapshot j of (sequence n, head h): [N][snap_cap][H][d_k][d_v]
 __host__ __device__ __forceinline__ float* snapshot_at(float* snapshots, int snap_cap, int H,
                                                        int64_t state_elems, int n, int j, int h) {

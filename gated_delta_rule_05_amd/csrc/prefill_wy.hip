@@ -646,7 +646,9 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
     auto out_rsrc = [&](int m) {
         const int64_t c0 = t_begin + static_cast<int64_t>(m) * C;
         const int len = static_cast<int>(min<int64_t>(C, t_end - c0));
-        return rsrc(o + (c0 * H + h) * DV + j0, 2u * static_cast<uint32_t>((len - 1) * vrow + TV));
+        // (a snapshot-recording call may pass no o: every output store is dropped)
+        const uint32_t bytes = 2u * static_cast<uint32_t>((len - 1) * vrow + TV);
+        return rsrc(o + (c0 * H + h) * DV + j0, SNAP && !o ? 0u : bytes);
     };
     if (wave < NC) {
         // O of chunk m, written by this slab's output wave into xob[b]
@@ -734,11 +736,16 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             // the addressing in scalar registers and one lane offset)
             const int js = SNAP && --snap_left == 0
                                ? (snap_left = snap_stride, (c_lo + x + 1) / snap_stride - 1) : -1;
-            // (only a full chunk ends on a boundary)
-            if (js >= 0 && js < snap_cap && (c_lo + x + 1) * C <= seq_len) {
-                const __amdgpu_buffer_rsrc_t rs = rsrc(
-                    snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0,
-                    4u * DK * DV);
+            // (only a full chunk ends on a boundary).  snap_cap < 0 selects the
+            // compact per-chunk layout: the state after chunk js of sequence
+            // n at index n + cu[n] / C + js, which never collides with the
+            // next sequence's (it starts at least ceil(len / C) indices on)
+            if (js >= 0 && (snap_cap < 0 || js < snap_cap) && (c_lo + x + 1) * C <= seq_len) {
+                const int64_t SE = static_cast<int64_t>(DK) * DV;
+                float* sp = snap_cap >= 0
+                                ? snapshot_at(snapshots, snap_cap, H, SE, n, js, h)
+                                : snapshots + ((n + t_begin / C + js) * H + h) * SE;
+                const __amdgpu_buffer_rsrc_t rs = rsrc(sp + j0, 4u * DK * DV);
                 const int lo = 4 * (4 * g * DV + jc);
 #pragma unroll
                 for (int m = 0; m < 8; ++m)

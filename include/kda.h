@@ -181,6 +181,13 @@ typedef struct kda_decode_multi_options {
                                       applies none); zero: S is only read */
 } kda_decode_multi_options;
 
+/* Options of kda_bwd (zero-initialise for defaults). */
+typedef struct kda_bwd_options {
+    int32_t gate;                  /* a kda_gate (0 = KDA_GATE_CHANNEL) */
+    int32_t block_chunks;          /* chunks of 64 tokens per backward block
+                                      (0 = automatic) */
+} kda_bwd_options;
+
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
 int kda_abi_version(void);
 
@@ -336,6 +343,51 @@ int kda_decode_multi(const void *q, const void *k, const void *v,
                      int32_t N, int32_t m, int32_t H, int32_t d_k, int32_t d_v,
                      int32_t dtype, float scale, void *o,
                      const kda_decode_multi_options *options, void *stream);
+
+/*
+ * Bytes of device workspace kda_bwd needs for these sizes and options:
+ * the start state of every chunk (one fp32 state per (chunk, head), so
+ * about 1 GiB per 16,384 head-chunks), the forward pass's operand block,
+ * and one block of per-(chunk, head) backward operands.  0 for arguments
+ * kda_bwd would reject.
+ */
+size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
+                               int32_t d_k, int32_t d_v, int32_t dtype,
+                               const kda_bwd_options *options);
+
+/*
+ * Gradients of the prefill: with L = <o, dO> + <hT, dhT> for the prefill
+ * kda_fwd_prefill computes on these inputs, writes dL/dq, dL/dk, dL/dv
+ * (dtype, the layouts of q, k, v), dL/dlog_alpha (fp32, the layout of
+ * log_alpha for the gate in options), dL/dbeta [total_T][H] (fp32) and,
+ * when dh0 != NULL, dL/dh0 [N][H][d_k][d_v] (fp32).  dhT == NULL means a
+ * zero adjoint of the final states.  This is the backward pass of the
+ * chunkwise training algorithm that "Kimi Linear acaba de superar a la
+ * atención completa en sus propios términos" (section "Cómo Kimi Linear
+ * utiliza una memoria recurrente más inteligente") credits for KDA's
+ * training efficiency; the forward is recomputed inside the call, so only
+ * the forward's inputs are needed.
+ *
+ * Requirements: those of kda_fwd_prefill for the shared inputs; dO
+ * [total_T][H][d_v] (dtype) non-NULL when total_T > 0, as are dq, dk, dv,
+ * dbeta, and dlog_alpha unless the gate is KDA_GATE_NONE
+ * [INVALID_ARGUMENT]; d_k = d_v = 128 and dtype KDA_DTYPE_BF16
+ * [UNSUPPORTED]; dO, dhT, dq, dk, dv, dh0, the workspace and a per-channel
+ * dlog_alpha 16-byte aligned, dbeta and a per-head dlog_alpha 4-byte
+ * aligned [MISALIGNED]; no output overlapping an input, another output or
+ * the workspace [INVALID_ARGUMENT]; workspace_bytes at least
+ * kda_bwd_workspace_bytes [WORKSPACE_TOO_SMALL].
+ * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
+ * adjoints, as in the forward pass.
+ */
+int kda_bwd(const void *q, const void *k, const void *v,
+            const float *log_alpha, const float *beta, const float *h0,
+            const int32_t *cu_seqlens, int64_t total_T, int32_t N, int32_t H,
+            int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+            const void *dO, const float *dhT, void *dq, void *dk, void *dv,
+            float *dlog_alpha, float *dbeta, float *dh0,
+            void *workspace, size_t workspace_bytes,
+            const kda_bwd_options *options, void *stream);
 
 #ifdef __cplusplus
 }

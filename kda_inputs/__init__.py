@@ -31,7 +31,7 @@ import numpy as np
 import torch
 
 # tensor ids of the seeded streams
-Q, K, V, LOG_ALPHA, BETA, STATE, LENGTHS = range(7)
+Q, K, V, LOG_ALPHA, BETA, STATE, LENGTHS, DO, DHT = range(9)   # DO, DHT: adjoints of o and hT
 SLAB = 1 << 16   # tokens per generation slab
 
 

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 6
+    assert kda.abi_version() == 7
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -280,6 +280,50 @@ def decode_multi_call(m=4, gate=0, index=None, nstates=0, lengths=None, write_st
 ])
 def test_decode_multi_checks(kw, status):
     assert decode_multi_call(**kw) == status
+
+
+def bwd_call(gate=0, blk=0, **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
+                cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
+                do=addr(6), dhT=None, dq=addr(7), dk_=addr(8), dv_=addr(9), dla=addr(10),
+                dbeta=addr(11), dh0=addr(12), ws=addr(13), wsb=256, stream=None)
+    args.update(over)
+    opts = kda.BwdOptions(gate, blk)
+    lib = kda.load_library()
+    return lib.kda_bwd(args["q"], args["k"], args["v"], args["la"], args["beta"], args["h0"],
+                       args["cu"], args["T"], args["N"], args["H"], args["dk"], args["dv"],
+                       args["dtype"], args["scale"], args["do"], args["dhT"], args["dq"],
+                       args["dk_"], args["dv_"], args["dla"], args["dbeta"], args["dh0"],
+                       args["ws"], args["wsb"], ctypes.byref(opts), args["stream"])
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(do=None), INVALID), (dict(dq=None), INVALID), (dict(dbeta=None), INVALID),
+    (dict(la=None), INVALID), (dict(dla=None), INVALID), (dict(cu=None), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(gate=5), INVALID), (dict(blk=-1), INVALID),
+    (dict(dk=64, dv=64), UNSUPPORTED), (dict(dtype=1), UNSUPPORTED),
+    (dict(do=addr(6, 8)), MISALIGNED), (dict(dh0=addr(12, 4)), MISALIGNED),
+    (dict(dbeta=addr(11, 2)), MISALIGNED), (dict(gate=1, dla=addr(10, 2)), MISALIGNED),
+    (dict(dq=addr(0, 256)), INVALID),            # dq inside q
+    (dict(dv_=addr(7, 512)), INVALID),           # dv inside dq
+    (dict(dh0=addr(6)), INVALID),                # dh0 on dO
+    (dict(), WS_SMALL),                          # every check passed: the workspace is tiny
+    (dict(gate=2, la=None, dla=None), WS_SMALL),
+])
+def test_backward_argument_checks(over, status):
+    assert bwd_call(**over) == status
+
+
+def test_backward_workspace_query():
+    lib = kda.load_library()
+    opts = kda.BwdOptions(0, 0)
+    assert lib.kda_bwd_workspace_bytes(4096, 4, 16, 64, 64, 0, ctypes.byref(opts)) == 0
+    assert lib.kda_bwd_workspace_bytes(4096, 4, 16, 128, 128, 1, ctypes.byref(opts)) == 0
+    a = lib.kda_bwd_workspace_bytes(4096, 4, 16, 128, 128, 0, ctypes.byref(opts))
+    b = lib.kda_bwd_workspace_bytes(8192, 4, 16, 128, 128, 0, ctypes.byref(opts))
+    # one fp32 state per (chunk, head) grows with the tokens
+    assert a > 0 and b - a >= 4096 // 64 * 16 * 128 * 128 * 4
+    assert kda.backward_workspace_bytes(4096, 4, 16, 128, 128) == a
 
 
 # snapshots: [N][capacity][H][d_k][d_v] fp32 (N = 2, H = 4, d = 128: 512 KiB
