@@ -136,28 +136,38 @@ __device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
     *reinterpret_cast<u32x2*>(p) = u32x2{pk(x[0], x[1]), pk(x[2], x[3])};
 }
 
-template <int GATE>
-__device__ __forceinline__ float gate_at(const float* la, int64_t row, int H, int h, int c) {
-    if constexpr (GATE == kGateChannel) return la[row * D + c];
-    else if constexpr (GATE == kGateHead) return la[row];
-    else return 0.f;
-}
 
 // cumulative gates of the chunk's rows, per channel, into g[C][D] (rows past
-// the chunk repeat the last row); beta of its rows into bs[C] (0 past it)
+// the chunk repeat the last row); beta of its rows into bs[C] (0 past it).
+// The raw gates land in g with parallel vector loads first; the scan then
+// runs over LDS.
 template <int GATE>
 __device__ __forceinline__ void load_gates(const float* la, const float* beta, const ChunkRef& c,
                                            int H, float* g, float* bs) {
     const int tid = threadIdx.x;
+    for (int u = tid; u < C * (D / 4); u += NT) {
+        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (r < c.len) {
+            const int64_t row = (c.t0 + r) * H + c.h;
+            if constexpr (GATE == kGateChannel) {
+                x = *reinterpret_cast<const f32x4*>(la + row * D + c0);
+            } else if constexpr (GATE == kGateHead) {
+                const float a = la[row];
+                x = f32x4{a, a, a, a};
+            }
+        }
+        *reinterpret_cast<f32x4*>(g + r * D + c0) = x;
+    }
+    if (tid < C) bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
+    __syncthreads();
     if (tid < D) {
         float run = 0.f;
+#pragma unroll 16
         for (int r = 0; r < C; ++r) {
-            if (r < c.len) run += gate_at<GATE>(la, (c.t0 + r) * H + c.h, H, c.h, tid);
+            run += g[r * D + tid];
             g[r * D + tid] = run;
         }
-    } else if (tid < D + C) {
-        const int r = tid - D;
-        bs[r] = r < c.len ? beta[(c.t0 + r) * H + c.h] : 0.f;
     }
 }
 
@@ -171,6 +181,7 @@ struct alignas(16) PrepLds {
     float bm[C * (C + 1)], mi[C * (C + 1)];
     bf16_t tt[C * LDC];
     float bs[C];
+    float xs[3][16 * 17];      // one wave's product block of the inverse
 };
 
 template <int GATE>
@@ -246,22 +257,57 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         put4t(oPt + s * C + r0, x);
     });
     __syncthreads();
-    // Minv = (I + A)^-1, A = strict_lower(Diag(beta) B): each column by
-    // forward substitution, one thread per column
+    // Minv = (I + A)^-1, A = strict_lower(Diag(beta) B), blockwise in 16x16
+    // blocks.  The diagonal blocks (unit lower triangular) by forward
+    // substitution, one thread per column with the column in registers;
+    // then block row I = 1..3 from the rows above it:
+    //     Minv_IJ = -Minv_II sum_{K=J}^{I-1} A_IK Minv_KJ     (J < I)
+    // on fp32 matrix cores (16x16x4), wave J computing block (I, J).
     if (tid < C) {
-        const int col = tid;
-        for (int r = 0; r < C; ++r) {
-            float x = r == col ? 1.f : 0.f;
-            if (r > col) {
-                const float br = sm.bs[r];
-                float acc = 0.f;
-                for (int s = col; s < r; ++s) acc += sm.bm[r * (C + 1) + s] * sm.mi[s * (C + 1) + col];
-                x = -br * acc;
-            }
-            sm.mi[r * (C + 1) + col] = x;
+        const int col = tid, base = col & ~15;
+        float x[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            const int r = base + rr;
+            float acc = 0.f;
+#pragma unroll
+            for (int ss = 0; ss < rr; ++ss) acc += sm.bm[r * (C + 1) + base + ss] * x[ss];
+            x[rr] = (r == col ? 1.f : 0.f) - sm.bs[r] * acc;
         }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) sm.mi[(base + rr) * (C + 1) + col] = x[rr];
+        for (int r = 0; r < base; ++r) sm.mi[r * (C + 1) + col] = 0.f;
     }
     __syncthreads();
+    for (int I = 1; I < 4; ++I) {
+        const int J = tid >> 6;
+        if (J < I) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * I + ln;
+            for (int K = J; K < I; ++K) {
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    const int kc = 16 * K + 4 * kk + g4;
+                    const float a = sm.bs[row] * sm.bm[row * (C + 1) + kc];
+                    const float b = sm.mi[kc * (C + 1) + 16 * J + ln];
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+                }
+            }
+            float* xs = sm.xs[J];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) xs[(4 * g4 + i) * 17 + ln] = acc[i];
+            f32x4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const float a = sm.mi[row * (C + 1) + 16 * I + 4 * kk + g4];
+                const float b = xs[(4 * kk + g4) * 17 + ln];
+                m = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, m, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.mi[(16 * I + 4 * g4 + i) * (C + 1) + 16 * J + ln] = -m[i];
+        }
+        __syncthreads();
+    }
     for (int idx = tid; idx < C * C; idx += NT) {
         const int r = idx / C, s = idx % C;
         const float m = sm.mi[r * (C + 1) + s];
@@ -333,31 +379,58 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[m][i] = st[(16 * m + 4 * g4 + i) * D + jc];
 
-    for (int j = hi; j >= c_lo; --j) {
+    // The next chunk's operands load into registers while this chunk
+    // computes.  Kd, P^T, Qg^T and W^T are 3584 16-byte units: 14 per
+    // thread, and with 256 threads unit x * 256 + tid falls in one matrix
+    // for every thread (Kd: x < 4; P^T: x < 6; Qg^T: x < 10; W^T: x < 14).
+    constexpr int PER = (C * D + C * C + 2 * D * C) / 8 / NT;
+    static_assert(PER * NT * 8 == C * D + C * C + 2 * D * C, "whole rounds");
+    u32x4 pre[PER], pdo[2];
+    float pgam = 0.f;
+    auto fetch = [&](int j) {
         const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
         const uint8_t* sp = slots + slot * static_cast<int64_t>(kSlot);
+#pragma unroll
+        for (int x = 0; x < PER; ++x) {
+            const int u = x * NT + tid;
+            const int byte = x < 4 ? 16 * u : kOffPt + 16 * (u - 4 * NT);
+            pre[x] = *reinterpret_cast<const u32x4*>(sp + byte);
+        }
+        if (tid < D) pgam = reinterpret_cast<const float*>(sp + kOffGam)[tid];
         const int64_t t0 = t_begin + static_cast<int64_t>(j) * C;
         const int len = static_cast<int>(min<int64_t>(C, t_end - t0));
-        copy_rows(sm.kd, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKd), C, D);
-        copy_rows(sm.pt, LDC, reinterpret_cast<const bf16_t*>(sp + kOffPt), C, C);
-        copy_rows(sm.qt, LDC, reinterpret_cast<const bf16_t*>(sp + kOffQt), D, C);
-        copy_rows(sm.wt, LDC, reinterpret_cast<const bf16_t*>(sp + kOffWt), D, C);
-        if (tid < D) sm.gam[tid] = reinterpret_cast<const float*>(sp + kOffGam)[tid];
-        {   // dO^T of the tile: thread (row r, 16 columns)
-            const int r = tid >> 2, part = tid & 3;
-            u32x4 a = {0u, 0u, 0u, 0u}, b = a;
-            if (r < len) {
-                const bf16_t* src = dO + ((t0 + r) * H + h) * D + tile * kCarryTile + 16 * part;
-                a = *reinterpret_cast<const u32x4*>(src);
-                b = *reinterpret_cast<const u32x4*>(src + 8);
-            }
-            const uint32_t w[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        const int r = tid >> 2, part = tid & 3;
+        const bf16_t* src = dO + ((t0 + min(r, len - 1)) * H + h) * D + tile * kCarryTile + 16 * part;
+        pdo[0] = *reinterpret_cast<const u32x4*>(src);
+        pdo[1] = *reinterpret_cast<const u32x4*>(src + 8);
+        if (r >= len) pdo[0] = pdo[1] = u32x4{0u, 0u, 0u, 0u};
+    };
+    auto put = [&]() {
 #pragma unroll
-            for (int x = 0; x < 8; ++x) {
-                sm.dot[(16 * part + 2 * x) * LDC + r] = static_cast<bf16_t>(w[x] & 0xffffu);
-                sm.dot[(16 * part + 2 * x + 1) * LDC + r] = static_cast<bf16_t>(w[x] >> 16);
-            }
+        for (int x = 0; x < PER; ++x) {
+            const int u = x * NT + tid;
+            bf16_t* dst;
+            if (x < 4) dst = sm.kd + (u / 16) * LDD + (u % 16) * 8;
+            else if (x < 6) { const int w = u - 4 * NT; dst = sm.pt + (w / 8) * LDC + (w % 8) * 8; }
+            else if (x < 10) { const int w = u - 6 * NT; dst = sm.qt + (w / 8) * LDC + (w % 8) * 8; }
+            else { const int w = u - 10 * NT; dst = sm.wt + (w / 8) * LDC + (w % 8) * 8; }
+            *reinterpret_cast<u32x4*>(dst) = pre[x];
         }
+        if (tid < D) sm.gam[tid] = pgam;
+        const int r = tid >> 2, part = tid & 3;
+        const uint32_t w[8] = {pdo[0][0], pdo[0][1], pdo[0][2], pdo[0][3],
+                               pdo[1][0], pdo[1][1], pdo[1][2], pdo[1][3]};
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            sm.dot[(16 * part + 2 * x) * LDC + r] = static_cast<bf16_t>(w[x] & 0xffffu);
+            sm.dot[(16 * part + 2 * x + 1) * LDC + r] = static_cast<bf16_t>(w[x] >> 16);
+        }
+    };
+
+    fetch(hi);
+    for (int j = hi; j >= c_lo; --j) {
+        const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
+        put();
         // dS' of this chunk (fp32, for grad_a) and as a bf16 B operand
         float* dsp = dsblk + slot * kState;
 #pragma unroll
@@ -367,6 +440,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
             put4t(&sm.dst[wave][ln * LDD + 16 * m + 4 * g4], S[m]);
         }
         __syncthreads();
+        if (j > c_lo) fetch(j - 1);
         // dE = Kd dS' + scale P^T dO  (this wave's 16 columns, 4 row tiles)
         float* dep = deblk + slot * (static_cast<int64_t>(C) * D);
         const bf16_t* dsw = sm.dst[wave];
@@ -710,12 +784,26 @@ void bwd_grad_b_kernel(const uint8_t* __restrict__ slots, const uint8_t* __restr
         const int wave = tid >> 6;
         for (int t = wave; t < 4 * 8; t += 4) {
             const int mi = t / 8, ni = t % 8;
+            const int ch = 16 * ni + ln;
+            // this lane's 4 elements' inputs, loaded before the products so
+            // their latency overlaps the matrix work
+            float kv[4], qv[4], wKg[4], wQg[4], wKd[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i;
+                const int rr = min(r, c.len - 1);        // rows past the chunk: any valid row
+                const int64_t row = ((c.t0 + rr) * H + c.h) * D + ch;
+                kv[i] = elem<T>::load(k + row);
+                qv[i] = elem<T>::load(q + row);
+                wKg[i] = gKgW[r * D + ch];
+                wQg[i] = gQgS[r * D + ch];
+                wKd[i] = gKd[r * D + ch];
+            }
             f32x4 z = {0.f, 0.f, 0.f, 0.f};
             const f32x4 aKg = tile_mm<C>(sm.rb[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
             f32x4 aKn = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.kgt + 16 * ni * LDC, LDC, lane, z);
             aKn = tile_mm<C>(sm.ra[1] + 16 * mi * LDC, LDC, sm.qgt + 16 * ni * LDC, LDC, lane, aKn);
             const f32x4 aQg = tile_mm<C>(sm.ra[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
-            const int ch = 16 * ni + ln;
             const float G = sm.g[(c.len - 1) * D + ch];
             float dGp = 0.f;
 #pragma unroll
@@ -724,14 +812,13 @@ void bwd_grad_b_kernel(const uint8_t* __restrict__ slots, const uint8_t* __restr
                 float dgv = 0.f;
                 if (r < c.len) {
                     const int64_t row = ((c.t0 + r) * H + c.h) * D + ch;
-                    const float kv = elem<T>::load(k + row), qv = elem<T>::load(q + row);
                     const float gv = sm.g[r * D + ch];
                     const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
-                    const float dKg = aKg[i] + gKgW[r * D + ch];
-                    const float dQg = aQg[i] + gQgS[r * D + ch];
+                    const float dKg = aKg[i] + wKg[i];
+                    const float dQg = aQg[i] + wQg[i];
                     const float dKn = aKn[i];
-                    const float dKd = gKd[r * D + ch];
-                    const float Kg = kv * eg, Kn = kv * en, Qg = qv * eg, Kd = kv * ed;
+                    const float dKd = wKd[i];
+                    const float Kg = kv[i] * eg, Kn = kv[i] * en, Qg = qv[i] * eg, Kd = kv[i] * ed;
                     elem<T>::store(dk + row, dKg * eg + dKn * en + dKd * ed);
                     elem<T>::store(dq + row, dQg * eg);
                     dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
