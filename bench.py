@@ -27,6 +27,11 @@ tokens per sequence: one call verifies them (outputs, states only read),
 one commits an accepted prefix of 0..4 tokens (states advanced), each
 reading a state once, beside the time of 4 single decode steps.
 
+backward: the gradients of that prefill (kda_bwd; a random dO, zero dhT),
+which recompute the forward, against 2824 algorithmic bytes per head-token
+(q, k, v, dO and gates read, dq, dk, dv and gate gradients written), with
+the time relative to the forward call.
+
 gate_variants: the same prefill as Gated DeltaNet (one gate per (token,
 head), 1032 B per head-token) and DeltaNet (no gate, 1028 B), timed the
 same way, each against the HBM peak.
@@ -36,6 +41,7 @@ few heads over the first tokens), on the host's cores, scaled to tokens/s of
 the full 32-head layer.  It doubles as a parity spot check of those outputs.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                       [--only-backward]
 """
 import argparse
 import hashlib
@@ -64,6 +70,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=16)
     ap.add_argument("--cpu-tokens", type=int, default=1048576)
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time only the prefill gradients (for profiling)")
     return ap.parse_args()
 
 
@@ -110,6 +118,53 @@ def copy_rate_gbps(torch, nbytes=2 << 30, reps=5):
     return 2 * nbytes / (best * 1e-3) / 1e9
 
 
+# algorithmic bytes of the prefill gradients per head-token: reads q, k, v,
+# dO (bf16) and log_alpha, beta (fp32); writes dq, dk, dv (bf16), dlog_alpha
+# and dbeta (fp32)
+BACKWARD_BYTES_PER_HT = 4 * 256 + 512 + 4 + 3 * 256 + 512 + 4
+BACKWARD_KERNELS = ("prefill_wy_prep_kernel<0> + prefill_wy_carry_kernel<16, true> (forward "
+                    "recompute) + bwd_prep_kernel<0> + bwd_carry_kernel + bwd_grad_a_kernel + "
+                    "bwd_grad_b_kernel<0>")
+
+
+def bench_backward(torch, kda, gen, inp, steps, warmup):
+    """Gradients of the 1M-token prefill (zero h0 and dhT adjoint, random
+    dO), timed with HIP events on the launch stream."""
+    T, H = inp["q"].shape[:2]
+    N = inp["cu_seqlens"].shape[0] - 1
+    do = gen.normal((T, H, inp["v"].shape[-1]), 9, gen.DO, "cuda", torch.bfloat16)
+    need = kda.backward_workspace_bytes(T, N, H, 128, 128)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    grads = {}
+
+    def run():
+        grads.update(kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do,
+                                  cu_seqlens=inp["cu_seqlens"], workspace=ws, want_dh0=False))
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        run()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a0, a1 in evs:
+        a0.record(stream)
+        run()
+        a1.record(stream)
+    torch.cuda.synchronize()
+    ms = sum(a0.elapsed_time(a1) for a0, a1 in evs) / len(evs)
+    nbytes = BACKWARD_BYTES_PER_HT * T * H
+    out = {"workload": "long_t1m", "ms": ms, "tokens_per_s": T / (ms * 1e-3),
+           "vs_forward": None, "workspace_bytes": need,
+           "algorithmic_bytes_per_head_token": BACKWARD_BYTES_PER_HT,
+           "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
+           "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+           "kernels": BACKWARD_KERNELS}
+    del ws, do
+    grads.clear()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -125,6 +180,11 @@ def main():
     dev = "cuda"
     kda.load_library()
     stream = torch.cuda.current_stream()
+    if args.only_backward:
+        wb = gen.WORKLOADS["long_t1m"]
+        inb = gen.workload_prefill_inputs(wb, seed=2, device=dev)
+        print(json.dumps(bench_backward(torch, kda, gen, inb, args.steps, args.warmup)), flush=True)
+        return
 
     # ---------------- inputs (resident before timing) ----------------------
     wp = gen.WORKLOADS["long_t1m"]
@@ -281,6 +341,10 @@ def main():
     del pool
     torch.cuda.empty_cache()
 
+    # ---------------- prefill gradients on the same workload ----------------
+    backward = bench_backward(torch, kda, gen, inp, args.steps, args.warmup)
+    backward["vs_forward"] = backward["ms"] / pre_avg
+
     digest = source_digest(["prefill_wy.hip", "kda_mfma.h", "kda_device.h", "kda_sched.h"])
     traffic = load_counters("prefill_wy.hip", digest)
     mfma = load_counters("prefill_wy.hip", digest, "mfma")
@@ -322,6 +386,7 @@ def main():
                    "kernel": DECODE_KERNEL},
         "gate_variants": variants,
         "serving": serving,
+        "backward": backward,
         "cpu_baseline": None,
     }
 

@@ -36,10 +36,10 @@
 //          scale Qg^T, -W^T, Minv, B, gamma;
 //   carry  (serial per (sequence, head, 64 value columns)) walks the chunks
 //          backwards with dS in registers, storing dS' and dE of each chunk;
-//   grad_a (chunk-parallel) the products with the states: dV, dT, dKg_W,
-//          dQg_S, dKd, dP, dgamma;
-//   grad_b (chunk-parallel) the triangular-system and gate terms, and the
-//          gradients of q, k, log_alpha and beta.
+//   grad   (chunk-parallel) first the products with the states (dV, dT,
+//          dKg_W, dQg_S, dKd, dP, dgamma), kept in registers, then the
+//          triangular-system and gate terms and the gradients of q, k,
+//          log_alpha and beta.
 // Every product is a bf16 MFMA (16x16x32) with fp32 accumulation on
 // operands staged in LDS; states, adjoints and gates stay fp32.
 #include <algorithm>
@@ -68,17 +68,9 @@ constexpr int kOffMinv = kOffWt + D * C * 2; // [C][C] fp32   (I + A)^-1
 constexpr int kOffB = kOffMinv + C * C * 4;  // [C][C] fp32   Kg Kn^T
 constexpr int kOffGam = kOffB + C * C * 4;   // [D]    fp32   e^{G}
 constexpr int kSlot = kOffGam + D * 4;
-// per-(chunk, head) terms from grad_a to grad_b (fp32)
-constexpr int gOffKgW = 0;                   // [C][D] dKg_W
-constexpr int gOffQgS = gOffKgW + C * D * 4; // [C][D] dQg_S
-constexpr int gOffKd = gOffQgS + C * D * 4;  // [C][D] dKd
-constexpr int gOffT = gOffKd + C * D * 4;    // [C][C] dT
-constexpr int gOffP = gOffT + C * C * 4;     // [C][C] dP
-constexpr int gOffGam = gOffP + C * C * 4;   // [D]    dgamma
-constexpr int kGrad = gOffGam + D * 4;
 constexpr int64_t kState = static_cast<int64_t>(D) * D;   // floats per state
 
-static_assert(kSlot % 256 == 0 && kGrad % 256 == 0, "256-byte aligned records");
+static_assert(kSlot % 256 == 0, "256-byte aligned records");
 
 // ---- the chunk a work-group of a chunk-parallel pass owns
 struct ChunkRef {
@@ -431,7 +423,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     for (int j = hi; j >= c_lo; --j) {
         const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
         put();
-        // dS' of this chunk (fp32, for grad_a) and as a bf16 B operand
+        // dS' of this chunk (fp32, for the grad pass) and as a bf16 B operand
         float* dsp = dsblk + slot * kState;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -479,7 +471,12 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
 }
 
 // ===================================================================
-// grad_a: the products with the chunk's start state and its adjoints
+// grad: one work-group per (chunk, head).  Phase A takes the products with
+// the chunk's start state and its adjoints; the terms phase B needs stay in
+// registers (dKg_W, dQg_S, dKd, dT, dP: each wave keeps the 16x16 tiles it
+// computed, and phase B hands the same tiles to the same waves); phase B
+// then solves the triangular-system and gate terms and writes dq, dk,
+// dlog_alpha and dbeta.  The two phases share the LDS.
 // ===================================================================
 struct alignas(16) GradALds {
     bf16_t s0[D * LDD];        // S (row c, columns j)
@@ -491,6 +488,21 @@ struct alignas(16) GradALds {
     bf16_t mvt[C * LDC];       // Minv^T
     bf16_t de[C * LDD];        // dE
     float bs[C];
+};
+struct alignas(16) GradBLds {
+    float g[C * D];            // cumulative gates; later dlog_alpha rows (head gate)
+    float dg[C * D];
+    bf16_t knt[D * LDC], kgt[D * LDC], qgt[D * LDC];
+    bf16_t ra[2][C * LDC];     // Minv, Minv^T; later dP, dP^T
+    bf16_t rb[2][C * LDC];     // (dT Diag(beta))^T, Z; later dB, dB^T
+    float bs[C];
+    float db[C];               // dbeta
+    float dbp[4][C];           // dbeta_A per 16-column block, summed in order
+    float dG[D];
+};
+union alignas(16) GradLds {
+    GradALds a;
+    GradBLds b;
 };
 
 // fp32 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
@@ -508,6 +520,20 @@ __device__ __forceinline__ void stage_f32(const float* src, int rows, bf16_t* rm
     }
 }
 
+// this wave's tiles of a (4 x NTL)-tile product, in a fixed order: tile x
+// is t = wave + 4 x (row block t / NTL, column block t % NTL)
+template <int NTL, int K, int NX>
+__device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
+                                        f32x4 (&out)[NX]) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int t = wave + 4 * x, mi = t / NTL, ni = t % NTL;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        out[x] = tile_mm<K>(a + 16 * mi * lda, lda, bt + 16 * ni * ldb, ldb, lane, acc);
+    }
+}
+
 // the start state of chunk j of sequence n: h0 (or null = zeros) for the
 // first chunk, else the state the forward pass recorded after chunk j-1
 __device__ __forceinline__ const float* start_state(const ChunkRef& c, const float* h0,
@@ -517,183 +543,151 @@ __device__ __forceinline__ const float* start_state(const ChunkRef& c, const flo
     return sall + (idx * H + c.h) * kState;
 }
 
-template <typename T>
+template <typename T, int GATE>
 __global__ __launch_bounds__(NT)
-void bwd_grad_a_kernel(const uint8_t* __restrict__ slots, uint8_t* __restrict__ grads,
-                       const float* __restrict__ dsblk, const float* __restrict__ deblk,
-                       const float* __restrict__ sall, const float* __restrict__ h0,
-                       const T* __restrict__ v, const T* __restrict__ dO,
-                       const float* __restrict__ beta, const int32_t* __restrict__ cu, int H,
-                       int c_lo, int L_b, float scale, T* __restrict__ dv)
+void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict__ dsblk,
+                     const float* __restrict__ deblk, const float* __restrict__ sall,
+                     const float* __restrict__ h0, const T* __restrict__ q,
+                     const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
+                     const float* __restrict__ la, const float* __restrict__ beta,
+                     const int32_t* __restrict__ cu, int H, int c_lo, int L_b, float scale,
+                     T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
+                     float* __restrict__ dla, float* __restrict__ dbeta)
 {
-    __shared__ GradALds sm;
+    __shared__ GradLds sm_u;
+    __shared__ float s_dgam[D], s_dbT[C];      // phase A -> phase B
     ChunkRef c;
     if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
-    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
     const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
-    uint8_t* gp = grads + c.slot * static_cast<int64_t>(kGrad);
-    float* gKgW = reinterpret_cast<float*>(gp + gOffKgW);
-    float* gQgS = reinterpret_cast<float*>(gp + gOffQgS);
-    float* gKd = reinterpret_cast<float*>(gp + gOffKd);
-    float* gT = reinterpret_cast<float*>(gp + gOffT);
-    float* gP = reinterpret_cast<float*>(gp + gOffP);
-    float* gGam = reinterpret_cast<float*>(gp + gOffGam);
+    const float* mvg = reinterpret_cast<const float*>(sp + kOffMinv);
+    const float* Bm = reinterpret_cast<const float*>(sp + kOffB);
     const float* S = start_state(c, h0, sall, cu, H);
     const float* dSp = dsblk + c.slot * kState;
     const float* dE = deblk + c.slot * (static_cast<int64_t>(C) * D);
 
-    // ---- R = V - Kg S, and (Diag(beta) R)^T
-    stage_f32(S, D, sm.s0, LDD, sm.s0t, LDD);
-    copy_rows(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
-    for (int u = tid; u < C * (D / 4); u += NT) {
-        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < c.len) x = elem<T>::load4(v + ((c.t0 + r) * H + c.h) * D + c0);
-        put4t(sm.r + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
-    }
-    if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
-    __syncthreads();
-    mm<4, 8, D>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
-        const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
-        f32x4 br;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            bf16_t* p = sm.r + (r0 + i) * LDD + col;
-            const float rv = bf16_to_f32(*p) - acc[i];
-            *p = bf(rv);
-            br[i] = sm.bs[r0 + i] * rv;
-        }
-        put4t(sm.brt + col * LDC + r0, br);
-    });
-    // ---- E = Minv (Diag(beta) R)
+    f32x4 rKgW[8], rQgS[8], rKd[8];   // [C][D] terms, tiles t = wave + 4x of 4 x 8
+    f32x4 rT[4], rP[4];               // [C][C] terms, tiles t = wave + 4x of 4 x 4
+    // =========================== phase A ===========================
     {
-        const float* mv = reinterpret_cast<const float*>(sp + kOffMinv);
+        GradALds& sm = sm_u.a;
+        // ---- R = V - Kg S, and (Diag(beta) R)^T
+        stage_f32(S, D, sm.s0, LDD, sm.s0t, LDD);
+        copy_rows(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
+        for (int u = tid; u < C * (D / 4); u += NT) {
+            const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < c.len) x = elem<T>::load4(v + ((c.t0 + r) * H + c.h) * D + c0);
+            put4t(sm.r + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
+        }
+        if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
+        __syncthreads();
+        mm<4, 8, D>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
+            const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
+            f32x4 br;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16_t* p = sm.r + (r0 + i) * LDD + col;
+                const float rv = bf16_to_f32(*p) - acc[i];
+                *p = bf(rv);
+                br[i] = sm.bs[r0 + i] * rv;
+            }
+            put4t(sm.brt + col * LDC + r0, br);
+        });
+        // ---- E = Minv (Diag(beta) R)
         for (int u = tid; u < C * C; u += NT) {
-            const int r = u / C, s = u % C;
-            const bf16_t x = bf(mv[u]);
-            sm.mv[r * LDC + s] = x;
-            sm.mvt[s * LDC + r] = x;
+            const int r = u / C, s2 = u % C;
+            const bf16_t x = bf(mvg[u]);
+            sm.mv[r * LDC + s2] = x;
+            sm.mvt[s2 * LDC + r] = x;
         }
+        __syncthreads();
+        bf16_t* E = sm.kg;   // Kg is no longer needed
+        mm<4, 8, C>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
+        });
+        __syncthreads();
+        // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT);
+        //      dV = T^T dE = Diag(beta) Minv^T dE
+        bf16_t* det = sm.brt;
+        stage_f32(dE, C, sm.de, LDD, det, LDC);
+        __syncthreads();
+        mm_regs<4, D>(sm.de, LDD, sm.r, LDD, rT);
+        {   // wave w holds column block w of dT, row blocks x = 0..3
+            const int s2 = 16 * wave + ln;
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) part += mvg[(16 * x + 4 * g4 + i) * C + s2] * rT[x][i];
+            part += __shfl_xor(part, 16);
+            part += __shfl_xor(part, 32);
+            if (g4 == 0) s_dbT[s2] = part;
+        }
+        __syncthreads();
+        bf16_t* dV = sm.r;   // R is no longer needed
+        mm<4, 8, C>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s2 = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
+                const float x = sm.bs[s2] * acc[i];
+                dV[s2 * LDD + col] = bf(x);
+                if (s2 < c.len) elem<T>::store(dv + ((c.t0 + s2) * H + c.h) * D + col, x);
+            }
+        });
+        __syncthreads();
+        // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T (kept)
+        bf16_t* dOl = sm.brt;   // dE^T is no longer needed
+        for (int u = tid; u < C * (D / 4); u += NT) {
+            const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (r < c.len) x = elem<T>::load4(dO + ((c.t0 + r) * H + c.h) * D + c0);
+            put4t(dOl + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
+        }
+        __syncthreads();
+        mm_regs<8, D>(dV, LDD, sm.s0, LDD, rKgW);
+        mm_regs<8, D>(dOl, LDD, sm.s0, LDD, rQgS);
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+            rKgW[x] = -rKgW[x];
+            rQgS[x] = scale * rQgS[x];
+        }
+        // ---- dS' over S^T; dgamma = rowsum(dS' . S) in fp32
+        bf16_t* dsl = sm.s0t;
+        {
+            const int row = tid >> 1, half = tid & 1;
+            float part = 0.f;
+            for (int x = 0; x < D / 2; x += 4) {
+                const int col = 64 * half + x;
+                const f32x4 d = *reinterpret_cast<const f32x4*>(dSp + row * D + col);
+                f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+                if (S) sv = *reinterpret_cast<const f32x4*>(S + row * D + col);
+                part += d[0] * sv[0] + d[1] * sv[1] + d[2] * sv[2] + d[3] * sv[3];
+                put4t(dsl + row * LDD + col, d);
+            }
+            part += __shfl_xor(part, 1);
+            if (half == 0) s_dgam[row] = part;
+        }
+        __syncthreads();
+        // ---- dKd = E dS'^T, dP = lower(scale dO E^T) (kept)
+        mm_regs<8, D>(E, LDD, dsl, LDD, rKd);
+        mm_regs<4, D>(dOl, LDD, E, LDD, rP);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * x + 4 * g4 + i, s2 = 16 * wave + ln;
+                rP[x][i] = s2 <= r ? scale * rP[x][i] : 0.f;
+            }
+        __syncthreads();   // phase B reuses the LDS
     }
-    __syncthreads();
-    bf16_t* E = sm.kg;   // Kg is no longer needed
-    mm<4, 8, C>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
-    });
-    __syncthreads();
-    // ---- dT = dE R^T; dV = T^T dE = Diag(beta) Minv^T dE
-    bf16_t* det = sm.brt;
-    stage_f32(dE, C, sm.de, LDD, det, LDC);
-    __syncthreads();
-    mm<4, 4, D>(sm.de, LDD, sm.r, LDD, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gT[(16 * mi + 4 * g4 + i) * C + 16 * ni + ln] = acc[i];
-    });
-    __syncthreads();
-    bf16_t* dV = sm.r;   // R is no longer needed
-    mm<4, 8, C>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
-            const float x = sm.bs[s] * acc[i];
-            dV[s * LDD + col] = bf(x);
-            if (s < c.len) elem<T>::store(dv + ((c.t0 + s) * H + c.h) * D + col, x);
-        }
-    });
-    __syncthreads();
-    // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T
-    bf16_t* dOl = sm.brt;   // dE^T is no longer needed
-    for (int u = tid; u < C * (D / 4); u += NT) {
-        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < c.len) x = elem<T>::load4(dO + ((c.t0 + r) * H + c.h) * D + c0);
-        put4t(dOl + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
-    }
-    __syncthreads();
-    mm<4, 8, D>(dV, LDD, sm.s0, LDD, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gKgW[(16 * mi + 4 * g4 + i) * D + 16 * ni + ln] = -acc[i];
-    });
-    mm<4, 8, D>(dOl, LDD, sm.s0, LDD, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gQgS[(16 * mi + 4 * g4 + i) * D + 16 * ni + ln] = scale * acc[i];
-    });
-    // ---- dS' staged over S^T; dgamma = rowsum(dS' . S) in fp32
-    bf16_t* dsl = sm.s0t;
-    __syncthreads();
-    {
-        const int row = tid >> 1, half = tid & 1;
-        float part = 0.f;
-        for (int x = 0; x < D / 2; x += 4) {
-            const int col = 64 * half + x;
-            const f32x4 d = *reinterpret_cast<const f32x4*>(dSp + row * D + col);
-            f32x4 s = {0.f, 0.f, 0.f, 0.f};
-            if (S) s = *reinterpret_cast<const f32x4*>(S + row * D + col);
-            part += d[0] * s[0] + d[1] * s[1] + d[2] * s[2] + d[3] * s[3];
-            put4t(dsl + row * LDD + col, d);
-        }
-        part += __shfl_xor(part, 1);
-        if (half == 0) gGam[row] = part;
-    }
-    __syncthreads();
-    // ---- dKd = E dS'^T, dP = lower(scale dO E^T)
-    mm<4, 8, D>(E, LDD, dsl, LDD, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gKd[(16 * mi + 4 * g4 + i) * D + 16 * ni + ln] = acc[i];
-    });
-    mm<4, 4, D>(dOl, LDD, E, LDD, [&](int mi, int ni, f32x4 acc) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
-            gP[r * C + s] = s <= r ? scale * acc[i] : 0.f;
-        }
-    });
-}
-
-// ===================================================================
-// grad_b: the triangular system, the gates, and dq, dk, dlog_alpha, dbeta
-// ===================================================================
-struct alignas(16) GradBLds {
-    float g[C * D];            // cumulative gates; later dlog_alpha rows (head gate)
-    float dg[C * D];
-    bf16_t knt[D * LDC], kgt[D * LDC], qgt[D * LDC];
-    bf16_t ra[2][C * LDC];     // Minv, Minv^T; later dP, dP^T
-    bf16_t rb[2][C * LDC];     // (dT Diag(beta))^T, Z; later dB, dB^T
-    float bs[C];
-    float db[C];               // dbeta
-    float dbp[4][C];           // dbeta_A per 16-column block, summed in order
-    float dG[D];
-};
-
-template <typename T, int GATE>
-__global__ __launch_bounds__(NT)
-void bwd_grad_b_kernel(const uint8_t* __restrict__ slots, const uint8_t* __restrict__ grads,
-                       const T* __restrict__ q, const T* __restrict__ k,
-                       const float* __restrict__ la, const float* __restrict__ beta,
-                       const int32_t* __restrict__ cu, int H, int c_lo, int L_b,
-                       T* __restrict__ dq, T* __restrict__ dk, float* __restrict__ dla,
-                       float* __restrict__ dbeta)
-{
-    __shared__ GradBLds sm;
-    ChunkRef c;
-    if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
-    const int tid = threadIdx.x, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
-    const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
-    const uint8_t* gp = grads + c.slot * static_cast<int64_t>(kGrad);
-    const float* mv = reinterpret_cast<const float*>(sp + kOffMinv);
-    const float* Bm = reinterpret_cast<const float*>(sp + kOffB);
-    const float* gKgW = reinterpret_cast<const float*>(gp + gOffKgW);
-    const float* gQgS = reinterpret_cast<const float*>(gp + gOffQgS);
-    const float* gKd = reinterpret_cast<const float*>(gp + gOffKd);
-    const float* gT = reinterpret_cast<const float*>(gp + gOffT);
-    const float* gP = reinterpret_cast<const float*>(gp + gOffP);
-    const float* gGam = reinterpret_cast<const float*>(gp + gOffGam);
-
+    // =========================== phase B ===========================
+    GradBLds& sm = sm_u.b;
     load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
     __syncthreads();
     // gated keys and queries, transposed (B operands); Minv, Minv^T;
-    // (dT Diag(beta))^T; dbeta_T = diag(Minv^T dT); dG starts at dgamma gamma
+    // (dT Diag(beta))^T; dbeta starts at dbeta_T, dG at dgamma gamma
     for (int u = tid; u < C * (D / 4); u += NT) {
         const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
@@ -713,19 +707,21 @@ void bwd_grad_b_kernel(const uint8_t* __restrict__ slots, const uint8_t* __restr
         }
     }
     for (int u = tid; u < C * C; u += NT) {
-        const int r = u / C, s = u % C;
-        const bf16_t x = bf(mv[u]);
-        sm.ra[0][r * LDC + s] = x;
-        sm.ra[1][s * LDC + r] = x;
-        sm.rb[0][s * LDC + r] = bf(gT[u] * sm.bs[s]);
+        const int r = u / C, s2 = u % C;
+        const bf16_t x = bf(mvg[u]);
+        sm.ra[0][r * LDC + s2] = x;
+        sm.ra[1][s2 * LDC + r] = x;
+    }
+    {   // Y^T[s][i] = dT[i][s] beta_s from this wave's dT tiles (column block = wave)
+        const int s2 = 16 * wave + ln;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) put4t(sm.rb[0] + s2 * LDC + 16 * x + 4 * g4, sm.bs[s2] * rT[x]);
     }
     if (tid < C) {
-        float acc = 0.f;
-        for (int i = 0; i < C; ++i) acc += mv[i * C + tid] * gT[i * C + tid];
-        sm.db[tid] = acc;
+        sm.db[tid] = s_dbT[tid];
     } else if (tid >= NT - D) {
         const int ch = tid - (NT - D);
-        sm.dG[ch] = gGam[ch] * gate_exp(sm.g[(c.len - 1) * D + ch]);
+        sm.dG[ch] = s_dgam[ch] * gate_exp(sm.g[(c.len - 1) * D + ch]);
     }
     __syncthreads();
     // Z = Minv^T (dT Diag(beta))
@@ -734,104 +730,92 @@ void bwd_grad_b_kernel(const uint8_t* __restrict__ slots, const uint8_t* __restr
         for (int i = 0; i < 4; ++i) sm.rb[1][(16 * mi + 4 * g4 + i) * LDC + 16 * ni + ln] = bf(acc[i]);
     });
     __syncthreads();
-    // dA = -strict_lower(Z Minv^T): held in registers (4 tiles per wave)
-    // until every wave is done reading Z
-    f32x4 dA[4];
+    // dA = -strict_lower(Z Minv^T): held in registers until every wave is
+    // done reading Z and Minv
     {
-        const int wave = tid >> 6;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int t = wave + 4 * x, mi = t / 4, ni = t % 4;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            dA[x] = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.ra[0] + 16 * ni * LDC, LDC, lane, acc);
-        }
+        f32x4 dA[4];
+        mm_regs<4, C>(sm.rb[1], LDC, sm.ra[0], LDC, dA);
         __syncthreads();
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             const int t = wave + 4 * x, mi = t / 4, ni = t % 4;
-            const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
+            const int r0 = 16 * mi + 4 * g4, s2 = 16 * ni + ln;
             f32x4 db;
             float rowpart[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = r0 + i;
-                const float a = s < r ? -dA[x][i] : 0.f;
-                rowpart[i] = a * Bm[r * C + s];              // dbeta_A
+                const float a = s2 < r ? -dA[x][i] : 0.f;
+                rowpart[i] = a * Bm[r * C + s2];             // dbeta_A
                 db[i] = sm.bs[r] * a;                        // dB = Diag(beta) dA
-                sm.rb[0][r * LDC + s] = bf(db[i]);
+                sm.rb[0][r * LDC + s2] = bf(db[i]);
             }
-            put4t(sm.rb[1] + s * LDC + r0, db);             // dB^T
+            put4t(sm.rb[1] + s2 * LDC + r0, db);            // dB^T
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float p = rowpart[i];
+                float pp = rowpart[i];
 #pragma unroll
-                for (int m = 1; m < 16; m <<= 1) p += __shfl_xor(p, m);
-                if (ln == 0) sm.dbp[ni][r0 + i] = p;
+                for (int m = 1; m < 16; m <<= 1) pp += __shfl_xor(pp, m);
+                if (ln == 0) sm.dbp[ni][r0 + i] = pp;
             }
         }
-    }
-    // dP and dP^T over Minv (no longer needed)
-    for (int u = tid; u < C * C; u += NT) {
-        const int r = u / C, s = u % C;
-        const bf16_t x = bf(gP[u]);
-        sm.ra[0][r * LDC + s] = x;
-        sm.ra[1][s * LDC + r] = x;
+        // dP and dP^T over Minv, from this wave's dP tiles (column block = wave)
+        const int s2 = 16 * wave + ln;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.ra[0][(16 * x + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
+            put4t(sm.ra[1] + s2 * LDC + 16 * x + 4 * g4, rP[x]);
+        }
     }
     __syncthreads();
     // per 16x16 tile of (row r, key channel c): dKg = dKg_W + dB Kn,
     // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain
-    {
-        const int wave = tid >> 6;
-        for (int t = wave; t < 4 * 8; t += 4) {
-            const int mi = t / 8, ni = t % 8;
-            const int ch = 16 * ni + ln;
-            // this lane's 4 elements' inputs, loaded before the products so
-            // their latency overlaps the matrix work
-            float kv[4], qv[4], wKg[4], wQg[4], wKd[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mi + 4 * g4 + i;
-                const int rr = min(r, c.len - 1);        // rows past the chunk: any valid row
-                const int64_t row = ((c.t0 + rr) * H + c.h) * D + ch;
-                kv[i] = elem<T>::load(k + row);
-                qv[i] = elem<T>::load(q + row);
-                wKg[i] = gKgW[r * D + ch];
-                wQg[i] = gQgS[r * D + ch];
-                wKd[i] = gKd[r * D + ch];
-            }
-            f32x4 z = {0.f, 0.f, 0.f, 0.f};
-            const f32x4 aKg = tile_mm<C>(sm.rb[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
-            f32x4 aKn = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.kgt + 16 * ni * LDC, LDC, lane, z);
-            aKn = tile_mm<C>(sm.ra[1] + 16 * mi * LDC, LDC, sm.qgt + 16 * ni * LDC, LDC, lane, aKn);
-            const f32x4 aQg = tile_mm<C>(sm.ra[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
-            const float G = sm.g[(c.len - 1) * D + ch];
-            float dGp = 0.f;
+    for (int x = 0; x < 8; ++x) {
+        const int t = wave + 4 * x, mi = t / 8, ni = t % 8;
+        const int ch = 16 * ni + ln;
+        float kv[4], qv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 16 * mi + 4 * g4 + i;
-                float dgv = 0.f;
-                if (r < c.len) {
-                    const int64_t row = ((c.t0 + r) * H + c.h) * D + ch;
-                    const float gv = sm.g[r * D + ch];
-                    const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
-                    const float dKg = aKg[i] + wKg[i];
-                    const float dQg = aQg[i] + wQg[i];
-                    const float dKn = aKn[i];
-                    const float dKd = wKd[i];
-                    const float Kg = kv[i] * eg, Kn = kv[i] * en, Qg = qv[i] * eg, Kd = kv[i] * ed;
-                    elem<T>::store(dk + row, dKg * eg + dKn * en + dKd * ed);
-                    elem<T>::store(dq + row, dQg * eg);
-                    dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
-                    dGp += dKd * Kd;
-                }
-                sm.dg[r * D + ch] = dgv;
-            }
-            dGp += __shfl_xor(dGp, 16);
-            dGp += __shfl_xor(dGp, 32);
-            // the tiles of one channel block all belong to this wave (t = 8 mi
-            // + ni, wave = ni mod 4), so these adds happen in a fixed order
-            if (g4 == 0) atomicAdd(&sm.dG[ch], dGp);
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mi + 4 * g4 + i;
+            const int rr = min(r, c.len - 1);        // rows past the chunk: any valid row
+            const int64_t row = ((c.t0 + rr) * H + c.h) * D + ch;
+            kv[i] = elem<T>::load(k + row);
+            qv[i] = elem<T>::load(q + row);
         }
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        const f32x4 aKg = tile_mm<C>(sm.rb[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
+        f32x4 aKn = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.kgt + 16 * ni * LDC, LDC, lane, z);
+        aKn = tile_mm<C>(sm.ra[1] + 16 * mi * LDC, LDC, sm.qgt + 16 * ni * LDC, LDC, lane, aKn);
+        const f32x4 aQg = tile_mm<C>(sm.ra[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
+        const float G = sm.g[(c.len - 1) * D + ch];
+        float dGp = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * mi + 4 * g4 + i;
+            float dgv = 0.f;
+            if (r < c.len) {
+                const int64_t row = ((c.t0 + r) * H + c.h) * D + ch;
+                const float gv = sm.g[r * D + ch];
+                const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
+                const float dKg = aKg[i] + rKgW[x][i];
+                const float dQg = aQg[i] + rQgS[x][i];
+                const float dKn = aKn[i];
+                const float dKd = rKd[x][i];
+                const float Kg = kv[i] * eg, Kn = kv[i] * en, Qg = qv[i] * eg, Kd = kv[i] * ed;
+                elem<T>::store(dk + row, dKg * eg + dKn * en + dKd * ed);
+                elem<T>::store(dq + row, dQg * eg);
+                dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
+                dGp += dKd * Kd;
+            }
+            sm.dg[r * D + ch] = dgv;
+        }
+        dGp += __shfl_xor(dGp, 16);
+        dGp += __shfl_xor(dGp, 32);
+        // the tiles of one channel block all belong to this wave (t = 8 mi
+        // + ni, wave = ni mod 4), so these adds happen in a fixed order
+        if (g4 == 0) atomicAdd(&sm.dG[ch], dGp);
     }
     __syncthreads();
     // dlog_alpha[s] = sum_{r >= s} dg[r] + dG, per key channel
@@ -873,7 +857,7 @@ __global__ void bwd_init_kernel(const float* __restrict__ dhT, float* __restrict
 int64_t bound_chunks(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) / C : 0; }
 
 struct BwdLayout {
-    size_t fwd, sall, slots, grads, dsblk, deblk, dstate, total;
+    size_t fwd, sall, slots, dsblk, deblk, dstate, total;
 };
 
 BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
@@ -884,12 +868,11 @@ BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
     l.sall = (static_cast<size_t>(N) + static_cast<size_t>(bound_chunks(total_T)) + 1) * H *
              kState * 4;
     l.slots = blk * kSlot;
-    l.grads = blk * kGrad;
     l.dsblk = blk * kState * 4;
     l.deblk = blk * C * D * 4;
     l.dstate = nh * kState * 4;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    l.total = up(l.fwd) + up(l.sall) + up(l.slots) + up(l.grads) + up(l.dsblk) + up(l.deblk) +
+    l.total = up(l.fwd) + up(l.sall) + up(l.slots) + up(l.dsblk) + up(l.deblk) +
               up(l.dstate);
     return l;
 }
@@ -897,10 +880,10 @@ BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
 }  // namespace
 
 int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
-    // about 1 GiB of per-block buffers (prep operands, carry outputs and
-    // grad_a terms: ~331 KB per (chunk, head)), at most the chunk count
+    // about 1 GiB of per-block buffers (prep operands and carry outputs:
+    // ~200 KB per (chunk, head)), at most 64 chunks
     const size_t per_chunk = static_cast<size_t>(N) * H *
-                             (kSlot + kGrad + kState * 4 + static_cast<size_t>(C) * D * 4);
+                             (kSlot + kState * 4 + static_cast<size_t>(C) * D * 4);
     int64_t L = static_cast<int64_t>((size_t{1} << 30) / per_chunk);
     L = std::max<int64_t>(1, std::min<int64_t>(L, std::max<int64_t>(1, bound_chunks(total_T))));
     return static_cast<int>(std::min<int64_t>(L, 64));
@@ -917,7 +900,6 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
     uint8_t* fwd_ws = p;          p += up(l.fwd);
     float* sall = reinterpret_cast<float*>(p);    p += up(l.sall);
     uint8_t* slots = p;           p += up(l.slots);
-    uint8_t* grads = p;           p += up(l.grads);
     float* dsblk = reinterpret_cast<float*>(p);   p += up(l.dsblk);
     float* deblk = reinterpret_cast<float*>(p);   p += up(l.deblk);
     float* dstate = reinterpret_cast<float*>(p);
@@ -960,17 +942,13 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
                            dstate, dsblk, deblk, a.dh0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (a.total_T == 0) continue;
-        hipLaunchKernelGGL(bwd_grad_a_kernel<bf16_t>, dim3(chunks), dim3(NT), 0, stream, slots,
-                           grads, dsblk, deblk, sall, a.h0, v, dO, a.beta, a.cu_seqlens, a.H,
-                           c_lo, L_b, a.scale, static_cast<bf16_t*>(a.dv));
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        auto gb = a.gate == kGateChannel ? bwd_grad_b_kernel<bf16_t, kGateChannel>
-                : a.gate == kGateHead    ? bwd_grad_b_kernel<bf16_t, kGateHead>
-                                         : bwd_grad_b_kernel<bf16_t, kGateNone>;
-        hipLaunchKernelGGL(gb, dim3(chunks), dim3(NT), 0, stream, slots, grads, q, k,
-                           a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo, L_b,
-                           static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk), a.dlog_alpha,
-                           a.dbeta);
+        auto gk = a.gate == kGateChannel ? bwd_grad_kernel<bf16_t, kGateChannel>
+                : a.gate == kGateHead    ? bwd_grad_kernel<bf16_t, kGateHead>
+                                         : bwd_grad_kernel<bf16_t, kGateNone>;
+        hipLaunchKernelGGL(gk, dim3(chunks), dim3(NT), 0, stream, slots, dsblk, deblk, sall, a.h0,
+                           q, k, v, dO, a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo, L_b, a.scale,
+                           static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
+                           static_cast<bf16_t*>(a.dv), a.dlog_alpha, a.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     return hipSuccess;
