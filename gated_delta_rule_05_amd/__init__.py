@@ -25,7 +25,8 @@ import math
 import os
 
 __all__ = [
-    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "GATES", "PrefillOptions",
+    "KDAError", "STATUS", "DTYPE_BF16", "DTYPE_F32", "PATHS", "GATES", "FrontEnd",
+    "PrefillOptions",
     "DecodeOptions", "library_path", "load_library",
     "abi_version", "status_string", "prefill_options", "prefill_workspace_bytes", "prefill",
     "decode_step", "DecodeMultiOptions", "decode_multi", "BwdOptions",
@@ -45,18 +46,24 @@ PATHS = {"auto": 0, "vector": 1, "matrix": 2, "two_pass": 3}
 GATES = {"channel": 0, "head": 1, "none": 2}
 
 
+class FrontEnd(ctypes.Structure):
+    """Mirror of kda_front_end."""
+    _fields_ = [("l2norm_qk", ctypes.c_int32), ("gate_scale", ctypes.c_float),
+                ("gate_pre", ctypes.c_void_p), ("beta_pre", ctypes.c_void_p)]
+
+
 class PrefillOptions(ctypes.Structure):
     """Mirror of kda_prefill_options."""
     _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32),
                 ("block_chunks", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("snapshot_tokens", ctypes.c_int32), ("snapshot_capacity", ctypes.c_int32),
-                ("snapshots", ctypes.c_void_p)]
+                ("snapshots", ctypes.c_void_p), ("front", FrontEnd)]
 
 
 class DecodeOptions(ctypes.Structure):
     """Mirror of kda_decode_options."""
     _fields_ = [("gate", ctypes.c_int32), ("num_states", ctypes.c_int32),
-                ("state_index", ctypes.c_void_p)]
+                ("state_index", ctypes.c_void_p), ("front", FrontEnd)]
 
 
 class DecodeMultiOptions(ctypes.Structure):
@@ -152,16 +159,42 @@ def _gate_code(gate):
     return GATES[gate]
 
 
-def prefill_options(path="auto", value_tiles=0, block_chunks=0, gate="channel") -> PrefillOptions:
+def prefill_options(path="auto", value_tiles=0, block_chunks=0, gate="channel",
+                    front=None) -> PrefillOptions:
     if path not in PATHS:
         raise ValueError("path must be one of %s" % sorted(PATHS))
-    return PrefillOptions(PATHS[path], int(value_tiles), int(block_chunks), _gate_code(gate))
+    opts = PrefillOptions(PATHS[path], int(value_tiles), int(block_chunks), _gate_code(gate))
+    if front is not None:
+        opts.front = front
+    return opts
+
+
+def front_end(l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, shape=None,
+              gate="channel", device=None):
+    """A kda_front_end from torch tensors (None when every part is off).
+    gate_pre: bf16 in log_alpha's layout; beta_pre: bf16 [tokens, H]."""
+    if not l2norm_qk and gate_pre is None and beta_pre is None:
+        return None
+    torch = _torch()
+    if gate_pre is not None:
+        if gate == "none":
+            raise ValueError("gate_pre needs a gate")
+        _check(gate_pre, "gate_pre", tuple(shape) + ((gate_pre.shape[-1],) if gate == "channel" else ()),
+               torch.bfloat16, device)
+    if beta_pre is not None:
+        _check(beta_pre, "beta_pre", tuple(shape), torch.bfloat16, device)
+    return FrontEnd(1 if l2norm_qk else 0, float(gate_scale),
+                    None if gate_pre is None else gate_pre.data_ptr(),
+                    None if beta_pre is None else beta_pre.data_ptr())
 
 
 def prefill_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
                             dtype: int = DTYPE_BF16, path="auto", value_tiles=0,
-                            block_chunks=0, gate="channel") -> int:
-    opts = prefill_options(path, value_tiles, block_chunks, gate)
+                            block_chunks=0, gate="channel", front=False) -> int:
+    """``front``: True when the call will use the fused input front-end
+    (it can change the automatic path, and with it the workspace)."""
+    fe = FrontEnd(1, 0.0, None, None) if front else None
+    opts = prefill_options(path, value_tiles, block_chunks, gate, fe)
     return int(load_library().kda_fwd_prefill_workspace_bytes_ex(
         total_T, N, H, d_k, d_v, dtype, ctypes.byref(opts)))
 
@@ -216,7 +249,8 @@ def _check_gate(log_alpha, gate, lead, dk, dev):
 
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
-            block_chunks=0, gate="channel", snapshot_tokens=0, snapshots=None):
+            block_chunks=0, gate="channel", snapshot_tokens=0, snapshots=None,
+            l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -232,6 +266,10 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     every snapshot_tokens tokens of each sequence into ``snapshots``
     [N, capacity, H, d_k, d_v] fp32 (allocated zeroed with capacity
     T // snapshot_tokens when None) and returns (o, hT, snapshots).
+    The fused input front-end: ``l2norm_qk`` normalises q and k in the
+    kernel; ``gate_pre`` (bf16, log_alpha's layout; log_alpha must be None)
+    gives log_alpha = -gate_scale * softplus(gate_pre); ``beta_pre`` (bf16
+    [T, H]; beta must be None) gives beta = sigmoid(beta_pre).
     """
     torch = _torch()
     lib = load_library()
@@ -247,8 +285,15 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     _check(q, "q", (T, H, dk), dt, dev)
     _check(k, "k", (T, H, dk), dt, dev)
     _check(v, "v", (T, H, dv), dt, dev)
-    log_alpha, _ = _check_gate(log_alpha, gate, (T, H), dk, dev)
-    _check(beta, "beta", (T, H), torch.float32, dev)
+    fe = front_end(l2norm_qk, gate_pre, gate_scale, beta_pre, (T, H), gate, dev)
+    if gate_pre is None:
+        log_alpha, _ = _check_gate(log_alpha, gate, (T, H), dk, dev)
+    elif log_alpha is not None:
+        raise ValueError("log_alpha must be None with gate_pre")
+    if beta_pre is None:
+        _check(beta, "beta", (T, H), torch.float32, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None with beta_pre")
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
     if cu_seqlens.dim() != 1:
@@ -270,7 +315,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     else:
         hT = final_state
         _check(hT, "final_state", (N, H, dk, dv), torch.float32, dev)
-    opts = prefill_options(path, value_tiles, block_chunks, gate)
+    opts = prefill_options(path, value_tiles, block_chunks, gate, fe)
     if snapshot_tokens:
         if snapshots is None:
             cap = max(1, T // int(snapshot_tokens))
@@ -296,13 +341,15 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
 
 
 def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel",
-                state_index=None):
+                state_index=None, l2norm_qk=False, gate_pre=None, gate_scale=1.0,
+                beta_pre=None):
     """One decode step.  q, k: [N, H, d_k]; v: [N, H, d_v] (bf16 or fp32);
     log_alpha: [N, H, d_k] fp32 (gate="channel"), [N, H] (gate="head") or
     None (gate="none"); beta: [N, H] fp32; S: [N, H, d_k, d_v] fp32, updated
     in place.  With state_index (int32 [N] on the device) S is a pool
     [num_states, H, d_k, d_v] and sequence n updates S[state_index[n]];
     an index outside the pool skips that sequence (its o is not written).
+    The front-end arguments are those of prefill(), over the N tokens.
     Returns o [N, H, d_v] in the input dtype."""
     torch = _torch()
     lib = load_library()
@@ -318,8 +365,16 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel
     _check(q, "q", (N, H, dk), dt, dev)
     _check(k, "k", (N, H, dk), dt, dev)
     _check(v, "v", (N, H, dv), dt, dev)
-    log_alpha, gcode = _check_gate(log_alpha, gate, (N, H), dk, dev)
-    _check(beta, "beta", (N, H), torch.float32, dev)
+    fe = front_end(l2norm_qk, gate_pre, gate_scale, beta_pre, (N, H), gate, dev)
+    gcode = _gate_code(gate)
+    if gate_pre is None:
+        log_alpha, gcode = _check_gate(log_alpha, gate, (N, H), dk, dev)
+    elif log_alpha is not None:
+        raise ValueError("log_alpha must be None with gate_pre")
+    if beta_pre is None:
+        _check(beta, "beta", (N, H), torch.float32, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None with beta_pre")
     if state_index is None:
         _check(S, "S", (N, H, dk, dv), torch.float32, dev)
         nstates = N
@@ -336,6 +391,8 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel
     else:
         _check(out, "out", (N, H, dv), dt, dev)
     opts = DecodeOptions(gcode, nstates, None if state_index is None else state_index.data_ptr())
+    if fe is not None:
+        opts.front = fe
     st = lib.kda_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
                                 _ptr(S), N, H, dk, dv, code, float(scale), _ptr(out),
                                 ctypes.byref(opts), _stream(dev))

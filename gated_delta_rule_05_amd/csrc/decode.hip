@@ -43,18 +43,24 @@ struct DecodeShape {
 
 constexpr int kDecodeGrid = 256;   // persistent work-groups (one per compute unit)
 
-template <typename T, int DK, int DV, int GATE, bool INDEXED>
+// FRONT: the fused input front-end (its own instantiation): gates from
+// bf16 pre-activations (log_alpha = -fe.gate_scale softplus(x)), beta =
+// sigmoid of a bf16 pre-activation, and q, k divided by their L2 norms,
+// which are reduced together with k . q and applied after the reductions
+// (the reductions are linear in q and k)
+template <typename T, int DK, int DV, int GATE, bool INDEXED, bool FRONT>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NWV * 64))
 void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                         const T* __restrict__ v, const float* __restrict__ log_alpha,
                         const float* __restrict__ beta, float* __restrict__ S,
                         T* __restrict__ o, float scale, int64_t nheads, int H,
-                        const int32_t* __restrict__ state_index, int num_states)
+                        const int32_t* __restrict__ state_index, int num_states, FrontEnd fe)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NWV = Sh::NWV, ITERS = Sh::ITERS;
     __shared__ f32x4 red[2][NWV][2][LPR];   // per-wave column partials of S~^T k and S~^T q
     __shared__ float red_kq[2][NWV];
+    __shared__ float red_nrm[FRONT ? 2 : 1][NWV][2];   // front-end: sum of k^2 and q^2
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -100,13 +106,20 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
         const T* kp = k + nx * DK;
         // the gate of key channel r: its own (KDA), the head's (Gated
         // DeltaNet) or none (DeltaNet: alpha = 1)
-        const float la_head = GATE == kGateHead && log_alpha ? log_alpha[nx] : 0.f;
+        const bool pre = FRONT && fe.gate_pre;
+        const float la_head = GATE != kGateHead ? 0.f
+                              : pre ? -fe.gate_scale * softplus_f32(bf16_to_f32(fe.gate_pre[nx]))
+                              : log_alpha ? log_alpha[nx] : 0.f;
         auto la_of = [&](int r) {
-            if constexpr (GATE == kGateChannel) return log_alpha[nx * DK + r];
-            else return la_head;
+            if constexpr (GATE == kGateChannel) {
+                if (pre) return -fe.gate_scale * softplus_f32(bf16_to_f32(fe.gate_pre[nx * DK + r]));
+                return log_alpha[nx * DK + r];
+            } else {
+                return la_head;
+            }
         };
         f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
-        float kq = 0.f;
+        float kq = 0.f, kk = 0.f, qq = 0.f;
         float kr[ITERS];
 #pragma unroll
         for (int it = 0; it < ITERS; ++it) {
@@ -116,6 +129,10 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
             const float qv = elem<T>::load(qp + r);
             kr[it] = kv;
             kq += kv * qv;
+            if constexpr (FRONT) {
+                kk += kv * kv;
+                qq += qv * qv;
+            }
             s[it] *= a;
             rk += kv * s[it];
             rq += qv * s[it];
@@ -129,6 +146,10 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                 rq[c] += __shfl_xor(rq[c], m);
             }
             kq += __shfl_xor(kq, m);
+            if constexpr (FRONT) {
+                kk += __shfl_xor(kk, m);
+                qq += __shfl_xor(qq, m);
+            }
         }
         if (NWV > 1) {
             // ... and over the waves
@@ -136,19 +157,43 @@ void decode_step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                 red[par][wave][0][cl] = rk;
                 red[par][wave][1][cl] = rq;
                 if (lane == 0) red_kq[par][wave] = kq;
+                if (FRONT && lane == 0) {
+                    red_nrm[FRONT ? par : 0][wave][0] = kk;
+                    red_nrm[FRONT ? par : 0][wave][1] = qq;
+                }
             }
             __syncthreads();
             rk = red[par][0][0][cl];
             rq = red[par][0][1][cl];
             kq = red_kq[par][0];
+            if constexpr (FRONT) {
+                kk = red_nrm[par][0][0];
+                qq = red_nrm[par][0][1];
+            }
 #pragma unroll
             for (int w = 1; w < NWV; ++w) {
                 rk += red[par][w][0][cl];
                 rq += red[par][w][1][cl];
                 kq += red_kq[par][w];
+                if constexpr (FRONT) {
+                    kk += red_nrm[par][w][0];
+                    qq += red_nrm[par][w][1];
+                }
             }
         }
-        const float b = beta[nx];
+        if constexpr (FRONT) {
+            // the reductions are linear in k and q: normalise them afterwards
+            if (fe.l2norm) {
+                const float ik = 1.f / fmaxf(sqrtf(kk), kFrontEps);
+                const float iq = 1.f / fmaxf(sqrtf(qq), kFrontEps);
+                rk *= ik;
+                rq *= iq;
+                kq *= ik * iq;
+#pragma unroll
+                for (int it = 0; it < ITERS; ++it) kr[it] *= ik;
+            }
+        }
+        const float b = FRONT && fe.beta_pre ? sigmoid_f32(bf16_to_f32(fe.beta_pre[nx])) : beta[nx];
         const float4 vv = elem<T>::load4(v + nx * DV + 4 * cl);
         const f32x4 e = {b * (vv.x - rk[0]), b * (vv.y - rk[1]), b * (vv.z - rk[2]),
                          b * (vv.w - rk[3])};
@@ -310,6 +355,18 @@ void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
     }
 }
 
+template <typename T, int DK, int DV, int GATE, bool INDEXED, bool FRONT>
+static hipError_t launch_step_f(const DecodeArgs& a, int64_t grid, int threads, hipStream_t stream) {
+    const int64_t nheads = static_cast<int64_t>(a.N) * a.H;
+    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV, GATE, INDEXED, FRONT>),
+                       dim3(static_cast<unsigned>(grid)), dim3(threads), 0, stream,
+                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
+                       static_cast<const T*>(a.v), a.log_alpha, a.beta, a.S,
+                       static_cast<T*>(a.o), a.scale, nheads, a.H, a.state_index,
+                       a.num_states, a.fe);
+    return hipGetLastError();
+}
+
 template <typename T, int DK, int DV, int GATE, bool INDEXED>
 static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
     constexpr int threads = DecodeShape<DK, DV>::NWV * 64;
@@ -329,13 +386,8 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
                            a.write_state ? 1 : 0, a.state_index, a.num_states);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((decode_step_kernel<T, DK, DV, GATE, INDEXED>), dim3(static_cast<unsigned>(grid)),
-                       dim3(threads), 0, stream,
-                       static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.log_alpha, a.beta, a.S,
-                       static_cast<T*>(a.o), a.scale, nheads, a.H, a.state_index,
-                       a.num_states);
-    return hipGetLastError();
+    return a.fe.active() ? launch_step_f<T, DK, DV, GATE, INDEXED, true>(a, grid, threads, stream)
+                         : launch_step_f<T, DK, DV, GATE, INDEXED, false>(a, grid, threads, stream);
 }
 
 template <typename T, int DK, int DV>

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -97,6 +97,41 @@ int check_gate_ptr(int32_t gate, const float* log_alpha, bool needed) {
     return KDA_STATUS_OK;
 }
 
+// The fused input front-end: checks and conversion.  With gate_pre the
+// caller's log_alpha must be NULL (and a gate layout other than none); with
+// beta_pre the caller's beta must be NULL.  *la_needed / *beta_needed tell
+// the caller whether log_alpha / beta are still required.
+int check_front(const kda_front_end* f, int32_t gate, const float* log_alpha, const float* beta,
+                int64_t tokens, int64_t H, int32_t d_k, kda::FrontEnd* fe, bool* la_needed,
+                bool* beta_needed, Range* r_gate, Range* r_beta) {
+    *fe = kda::FrontEnd{};
+    *la_needed = true;
+    *beta_needed = true;
+    *r_gate = Range{0, 0};
+    *r_beta = Range{0, 0};
+    if (!f) return KDA_STATUS_OK;
+    fe->l2norm = f->l2norm_qk != 0;
+    if (f->gate_pre) {
+        if (gate == KDA_GATE_NONE || log_alpha) return KDA_STATUS_INVALID_ARGUMENT;
+        if (!std::isfinite(f->gate_scale) || f->gate_scale < 0.f) return KDA_STATUS_INVALID_ARGUMENT;
+        if (gate == KDA_GATE_CHANNEL ? !aligned16(f->gate_pre)
+                                     : (reinterpret_cast<uintptr_t>(f->gate_pre) & 1u))
+            return KDA_STATUS_MISALIGNED;
+        fe->gate_pre = static_cast<const uint16_t*>(f->gate_pre);
+        fe->gate_scale = f->gate_scale;
+        *la_needed = false;
+        *r_gate = range_of(f->gate_pre, tokens * H * (gate == KDA_GATE_CHANNEL ? d_k : 1) * 2);
+    }
+    if (f->beta_pre) {
+        if (beta) return KDA_STATUS_INVALID_ARGUMENT;
+        if (reinterpret_cast<uintptr_t>(f->beta_pre) & 1u) return KDA_STATUS_MISALIGNED;
+        fe->beta_pre = static_cast<const uint16_t*>(f->beta_pre);
+        *beta_needed = false;
+        *r_beta = range_of(f->beta_pre, tokens * H * 2);
+    }
+    return KDA_STATUS_OK;
+}
+
 size_t plan_bytes(int32_t N) { return round_up(static_cast<size_t>(N) * sizeof(int32_t), kWorkspaceAlign); }
 
 // Sizes-only view of a prefill for the path checks.
@@ -128,11 +163,16 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     const bool matrix_ok = kda::mfma_supported(a) && kda::wy_supported(a);
     if ((path == KDA_PATH_MATRIX || path == KDA_PATH_MATRIX_TWO_PASS) && !matrix_ok)
         return KDA_STATUS_UNSUPPORTED;
+    // the fused input front-end runs on the vector and two-pass paths
+    const bool front = options && (options->front.l2norm_qk || options->front.gate_pre ||
+                                   options->front.beta_pre);
+    if (front && path == KDA_PATH_MATRIX) return KDA_STATUS_UNSUPPORTED;
     pl->path = path;
     if (path == KDA_PATH_AUTO) {
         pl->path = !matrix_ok ? KDA_PATH_VECTOR
-                   : static_cast<int64_t>(N) * H < kTwoPassMaxPairs ? KDA_PATH_MATRIX_TWO_PASS
-                                                                     : KDA_PATH_MATRIX;
+                   : front || static_cast<int64_t>(N) * H < kTwoPassMaxPairs
+                       ? KDA_PATH_MATRIX_TWO_PASS
+                       : KDA_PATH_MATRIX;
     }
     pl->R = 0;
     pl->L_b = 0;
@@ -197,8 +237,15 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     if (st != KDA_STATUS_OK) return st;
     if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
     if (!cu_seqlens) return KDA_STATUS_INVALID_ARGUMENT;
-    if (total_T > 0 && (!q || !k || !v || !beta || !o)) return KDA_STATUS_INVALID_ARGUMENT;
-    const int gs = check_gate_ptr(gate, log_alpha, total_T > 0);
+    kda::FrontEnd fe;
+    bool la_needed, beta_needed;
+    Range r_gp, r_bp;
+    const int fs = check_front(options ? &options->front : nullptr, gate, log_alpha, beta,
+                               total_T, H, d_k, &fe, &la_needed, &beta_needed, &r_gp, &r_bp);
+    if (fs != KDA_STATUS_OK) return fs;
+    if (total_T > 0 && (!q || !k || !v || (beta_needed && !beta) || !o))
+        return KDA_STATUS_INVALID_ARGUMENT;
+    const int gs = check_gate_ptr(gate, log_alpha, total_T > 0 && la_needed);
     if (gs != KDA_STATUS_OK) return gs;
     if (gate == KDA_GATE_NONE) log_alpha = nullptr;   // never read
     // vector-loaded tensors need 16 bytes; beta and cu_seqlens are read as scalars
@@ -223,6 +270,10 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     for (const Range& in : inputs) {
         if (overlaps(r_o, in) || overlaps(r_ws, in)) return KDA_STATUS_INVALID_ARGUMENT;
     }
+    for (const Range& in : {r_gp, r_bp}) {
+        if (overlaps(r_o, in) || overlaps(r_ws, in) || overlaps(r_hT, in))
+            return KDA_STATUS_INVALID_ARGUMENT;
+    }
     for (int i = 0; i < 6; ++i)
         if (overlaps(r_hT, inputs[i])) return KDA_STATUS_INVALID_ARGUMENT;
     if (h0 && hT && h0 != hT && overlaps(r_hT, inputs[6])) return KDA_STATUS_INVALID_ARGUMENT;
@@ -245,6 +296,7 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
         const Range r_s = range_of(snaps, bytes);
         for (const Range& in : inputs)
             if (overlaps(r_s, in)) return KDA_STATUS_INVALID_ARGUMENT;
+        if (overlaps(r_s, r_gp) || overlaps(r_s, r_bp)) return KDA_STATUS_INVALID_ARGUMENT;
         if (overlaps(r_s, r_o) || overlaps(r_s, r_hT) || overlaps(r_s, r_ws))
             return KDA_STATUS_INVALID_ARGUMENT;
     }
@@ -258,6 +310,7 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     a.snapshots = snaps;
     a.snap_tokens = snaps ? snap : 0;
     a.snap_cap = cap;
+    a.fe = fe;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
@@ -298,7 +351,7 @@ int decode_call(const void* q, const void* k, const void* v, const float* log_al
                 const float* beta, float* S, int32_t N, int32_t m, int32_t H, int32_t d_k,
                 int32_t d_v, int32_t dtype, float scale, void* o, int32_t gate,
                 const int32_t* index, int32_t num_states, const int32_t* lengths,
-                bool write_state, void* stream) {
+                bool write_state, const kda_front_end* front, void* stream) {
     const int32_t nstates = index ? num_states : N;
     if (nstates < 1 || m < 0 || N < 1) return KDA_STATUS_INVALID_ARGUMENT;
     int64_t tokens = N;
@@ -310,9 +363,15 @@ int decode_call(const void* q, const void* k, const void* v, const float* log_al
     if (check_sizes(0, nstates, H, d_k, d_v, dtype, gate, &pool) != KDA_STATUS_OK)
         return KDA_STATUS_INVALID_ARGUMENT;
     if (!std::isfinite(scale)) return KDA_STATUS_INVALID_ARGUMENT;
-    if (!q || !k || !v || !beta || !S) return KDA_STATUS_INVALID_ARGUMENT;
+    kda::FrontEnd fe;
+    bool la_needed, beta_needed;
+    Range r_gp, r_bp;
+    const int fs = check_front(front, gate, log_alpha, beta, tokens, H, d_k, &fe, &la_needed,
+                               &beta_needed, &r_gp, &r_bp);
+    if (fs != KDA_STATUS_OK) return fs;
+    if (!q || !k || !v || (beta_needed && !beta) || !S) return KDA_STATUS_INVALID_ARGUMENT;
     if (!o && (m == 0 || !write_state)) return KDA_STATUS_INVALID_ARGUMENT;   // nothing to do
-    const int gs = check_gate_ptr(gate, log_alpha, true);
+    const int gs = check_gate_ptr(gate, log_alpha, la_needed);
     if (gs != KDA_STATUS_OK) return gs;
     if (gate == KDA_GATE_NONE) log_alpha = nullptr;   // never read
     const void* ptrs[] = {q, k, v, S, o};
@@ -327,6 +386,8 @@ int decode_call(const void* q, const void* k, const void* v, const float* log_al
                             range_of(lengths, lengths ? N * 4 : 0)};
     for (const Range& in : others)
         if (overlaps(r_o, in) || overlaps(r_S, in)) return KDA_STATUS_INVALID_ARGUMENT;
+    for (const Range& in : {r_gp, r_bp})
+        if (overlaps(r_o, in) || overlaps(r_S, in)) return KDA_STATUS_INVALID_ARGUMENT;
     if (overlaps(r_o, r_S)) return KDA_STATUS_INVALID_ARGUMENT;
 
     kda::DecodeArgs a;
@@ -339,6 +400,7 @@ int decode_call(const void* q, const void* k, const void* v, const float* log_al
     a.m = m;
     a.lengths = lengths;
     a.write_state = write_state;
+    a.fe = fe;
     if (kda::launch_decode(a, static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_STATUS_HIP_ERROR;
     return KDA_STATUS_OK;
@@ -354,7 +416,8 @@ int kda_decode_step_ex(const void* q, const void* k, const void* v, const float*
     const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
     const int32_t* index = options ? options->state_index : nullptr;
     return decode_call(q, k, v, log_alpha, beta, S, N, 0, H, d_k, d_v, dtype, scale, o, gate,
-                       index, options ? options->num_states : 0, nullptr, true, stream);
+                       index, options ? options->num_states : 0, nullptr, true,
+                       options ? &options->front : nullptr, stream);
 }
 
 int kda_decode_multi(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -367,7 +430,7 @@ int kda_decode_multi(const void* q, const void* k, const void* v, const float* l
     return decode_call(q, k, v, log_alpha, beta, S, N, m, H, d_k, d_v, dtype, scale, o, gate,
                        index, options ? options->num_states : 0,
                        options ? options->lengths : nullptr,
-                       options ? options->write_state != 0 : true, stream);
+                       options ? options->write_state != 0 : true, nullptr, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -68,6 +68,18 @@ template <> struct elem<bf16_t> {
     }
 };
 
+// softplus(x) = log(1 + e^x) = max(x, 0) + log(1 + e^-|x|), through the
+// hardware base-2 exponential and logarithm (the second term is in (0, ln 2])
+__device__ __forceinline__ float softplus_f32(float x) {
+    const float t = __builtin_amdgcn_exp2f(-fabsf(x) * 1.4426950408889634f);
+    return fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + t) * 0.6931471805599453f;
+}
+
+// sigmoid(x) = 1 / (1 + e^-x)
+__device__ __forceinline__ float sigmoid_f32(float x) {
+    return __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-x * 1.4426950408889634f));
+}
+
 // exp(x) through the hardware base-2 exponential.  Relative error is a few
 // ulp plus |x| * 2^-24 from scaling x by log2(e); |x| stays below ~90 on
 // every path that calls it.

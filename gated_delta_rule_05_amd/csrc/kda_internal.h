@@ -14,6 +14,20 @@ namespace kda {
 // shared by every channel, or none (alpha = 1; log_alpha not read)
 enum GateMode : int { kGateChannel = 0, kGateHead = 1, kGateNone = 2 };
 
+// The fused input front-end: each part is optional.
+//   l2norm:   q and k are divided by max(||x||_2, kFrontEps) per (token, head)
+//   gate_pre: bf16 pre-activations x in log_alpha's layout, which is then
+//             unused: log_alpha = -gate_scale * softplus(x)
+//   beta_pre: bf16 [tokens][H] pre-activations y: beta = sigmoid(y)
+struct FrontEnd {
+    const uint16_t* gate_pre = nullptr;   // bf16 bits
+    const uint16_t* beta_pre = nullptr;   // bf16 bits
+    float gate_scale = 0.f;
+    bool l2norm = false;
+    bool active() const { return l2norm || gate_pre || beta_pre; }
+};
+constexpr float kFrontEps = 1e-6f;
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -28,6 +42,7 @@ struct DecodeArgs {
     int gate;                     // a GateMode
     bool dtype_f32;
     float scale;
+    FrontEnd fe;
     // several tokens per sequence (m > 0; 0 = the single-step kernel):
     // tokens [N][m][H][.], lengths device [N] or null, o may be null
     int32_t m = 0;
@@ -55,6 +70,7 @@ struct PrefillArgs {
     // multiple of 64), into snapshots[n][j][h] for j < snap_cap; null = none
     float* snapshots;
     int32_t snap_tokens, snap_cap;
+    FrontEnd fe;
 };
 
 // gradients of the prefill (bf16, d_k = d_v = 128): see backward.hip

@@ -39,7 +39,8 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
                          const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
                          int64_t groups, int R, int H, int DV, float scale,
                          T* __restrict__ o, float* __restrict__ hT, int gate,
-                         float* __restrict__ snapshots, int snap_tokens, int snap_cap)
+                         float* __restrict__ snapshots, int snap_tokens, int snap_cap,
+                         FrontEnd fe)
 {
     constexpr int NT = 256;
     constexpr int KP = DK + 1;   // padded row stride: column walks hit distinct banks
@@ -47,6 +48,7 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
     __shared__ float sA[C * C], sP[C * C], sTi[C * C];
     __shared__ float sS[DK * TV], sV[C * TV], sX[C * TV], sE[C * TV];
     __shared__ float sBeta[C], sGl[DK], sGe[DK];
+    __shared__ float sNk[C], sNq[C];   // front-end: 1 / ||k||, 1 / ||q|| per row
 
     int64_t pair;
     int tile;
@@ -76,10 +78,17 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
                 const int64_t off = ((c0 + r) * H + h) * DK + c;
                 kk = elem<T>::load(k + off);
                 qq = elem<T>::load(q + off);
-                // the key channel's own gate, the head's (broadcast) or none
-                la = gate == kGateChannel ? log_alpha[off]
-                     : gate == kGateHead  ? log_alpha[(c0 + r) * H + h]
-                                          : 0.f;
+                // the key channel's own gate, the head's (broadcast) or none;
+                // with the front-end, from its bf16 pre-activation
+                if (fe.gate_pre) {
+                    const int64_t go = gate == kGateChannel ? off : (c0 + r) * H + h;
+                    la = gate == kGateNone ? 0.f
+                                           : -fe.gate_scale * softplus_f32(bf16_to_f32(fe.gate_pre[go]));
+                } else {
+                    la = gate == kGateChannel ? log_alpha[off]
+                         : gate == kGateHead  ? log_alpha[(c0 + r) * H + h]
+                                              : 0.f;
+                }
             }
             sKg[r * KP + c] = kk;
             sQg[r * KP + c] = qq;
@@ -90,8 +99,29 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
             sV[i] = (r < len) ? elem<T>::load(v + ((c0 + r) * H + h) * DV + j0 + j) : 0.f;
         }
         for (int r = tid; r < C; r += NT)
-            sBeta[r] = (r < len) ? beta[(c0 + r) * H + h] : 0.f;
+            sBeta[r] = r >= len ? 0.f
+                       : fe.beta_pre ? sigmoid_f32(bf16_to_f32(fe.beta_pre[(c0 + r) * H + h]))
+                                     : beta[(c0 + r) * H + h];
         __syncthreads();
+        if (fe.l2norm) {
+            // front-end: each row of k and q divided by its L2 norm
+            for (int r = tid; r < C; r += NT) {
+                float sk = 0.f, sq = 0.f;
+                for (int c = 0; c < DK; ++c) {
+                    sk += sKg[r * KP + c] * sKg[r * KP + c];
+                    sq += sQg[r * KP + c] * sQg[r * KP + c];
+                }
+                sNk[r] = 1.f / fmaxf(sqrtf(sk), kFrontEps);
+                sNq[r] = 1.f / fmaxf(sqrtf(sq), kFrontEps);
+            }
+            __syncthreads();
+            for (int i = tid; i < C * DK; i += NT) {
+                const int r = i / DK, c = i % DK;
+                sKg[r * KP + c] *= sNk[r];
+                sQg[r * KP + c] *= sNq[r];
+            }
+            __syncthreads();
+        }
         // cumulative gate per key channel
         for (int c = tid; c < DK; c += NT) {
             float g = 0.f;
@@ -208,7 +238,8 @@ static hipError_t launch_valu_t(const PrefillArgs& a, int R, hipStream_t stream)
                        static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.log_alpha, a.beta, a.h0,
                        a.cu_seqlens, a.order, groups, R, a.H, a.d_v, a.scale,
-                       static_cast<T*>(a.o), a.hT, a.gate, a.snapshots, a.snap_tokens, a.snap_cap);
+                       static_cast<T*>(a.o), a.hT, a.gate, a.snapshots, a.snap_tokens, a.snap_cap,
+                       a.fe);
     return hipGetLastError();
 }
 

@@ -203,12 +203,17 @@ __device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
 
 }  // namespace
 
-template <int GATE>
+// FRONT: the fused input front-end (a separate instantiation, so the plain
+// prep is unchanged): q and k L2-normalised per row when fe.l2norm, gates
+// from bf16 pre-activations (log_alpha = -fe.gate_scale softplus(x)) when
+// fe.gate_pre, beta = sigmoid(y) from bf16 fe.beta_pre
+template <int GATE, bool FRONT>
 __global__ __launch_bounds__(PT, 3)
 void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                             const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
                             const float* __restrict__ beta, const int32_t* __restrict__ cu,
-                            int H, int DV, int c_lo, int L_b, uint8_t* __restrict__ ws)
+                            int H, int DV, int c_lo, int L_b, uint8_t* __restrict__ ws,
+                            FrontEnd fe)
 {
     __shared__ PrepSmem sm;
     const int slot = blockIdx.x;
@@ -247,13 +252,37 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     u32x2 kr[4], qr[4], vr[4];
     f32x4 la[4];
     // the gates first: the cumulative sum waits on them
+    if (FRONT && fe.gate_pre) {
+        // bf16 pre-activations in the same layout: log_alpha = -c softplus(x)
+        const bf16_t* gp = reinterpret_cast<const bf16_t*>(fe.gate_pre);
+        const __amdgpu_buffer_rsrc_t rgp =
+            GATE == kGateChannel ? rsrc(gp + e0, 2u * span)
+                                 : rsrc(gp + c0 * H + h, 2u * static_cast<uint32_t>((len - 1) * H + 1));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        if constexpr (GATE == kGateChannel) {
-            la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
-        } else {                                  // the row's scalar gate on every channel
-            const float x = __uint_as_float(ld32(rla, 4 * (4 * rg + i) * H));
-            la[i] = f32x4{x, x, x, x};
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (GATE == kGateChannel) {
+                const u32x2 w = ld64(rgp, 2 * ((4 * rg + i) * H * DK + 4 * cg));
+                la[i] = f32x4{-fe.gate_scale * softplus_f32(lo_bf(w[0])),
+                              -fe.gate_scale * softplus_f32(hi_bf(w[0])),
+                              -fe.gate_scale * softplus_f32(lo_bf(w[1])),
+                              -fe.gate_scale * softplus_f32(hi_bf(w[1]))};
+            } else {
+                const float x = -fe.gate_scale *
+                                softplus_f32(bf16_to_f32(ld16(rgp, 2 * (4 * rg + i) * H)));
+                la[i] = f32x4{x, x, x, x};
+            }
+            // rows past the end read a zero pre-activation: keep their gate 0
+            if (4 * rg + i >= len) la[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if constexpr (GATE == kGateChannel) {
+                la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
+            } else {                                  // the row's scalar gate on every channel
+                const float x = __uint_as_float(ld32(rla, 4 * (4 * rg + i) * H));
+                la[i] = f32x4{x, x, x, x};
+            }
         }
     }
 #pragma unroll
@@ -265,9 +294,39 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
         vr[i] = (4 * cg < DV) ? ld64(rv, 2 * (r * H * DV + 4 * cg)) : u32x2{0u, 0u};
     }
     if (tid < C) {
-        const __amdgpu_buffer_rsrc_t rb =
-            rsrc(beta + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
-        sm.beta[tid] = __uint_as_float(ld32(rb, 4 * tid * H));
+        if (FRONT && fe.beta_pre) {
+            const __amdgpu_buffer_rsrc_t rb = rsrc(fe.beta_pre + c0 * H + h,
+                                                   2u * static_cast<uint32_t>((len - 1) * H + 1));
+            const float y = bf16_to_f32(ld16(rb, 2 * tid * H));
+            sm.beta[tid] = tid < len ? sigmoid_f32(y) : 0.f;
+        } else {
+            const __amdgpu_buffer_rsrc_t rb =
+                rsrc(beta + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
+            sm.beta[tid] = __uint_as_float(ld32(rb, 4 * tid * H));
+        }
+    }
+    // L2 norms of the 4 rows' k and q: a row is spread over the 32 lanes of
+    // this half-wave, 4 channels each
+    float nk[4] = {1.f, 1.f, 1.f, 1.f}, nq[4] = {1.f, 1.f, 1.f, 1.f};
+    if (FRONT && fe.l2norm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float kx = (j & 1) ? hi_bf(kr[i][j >> 1]) : lo_bf(kr[i][j >> 1]);
+                const float qx = (j & 1) ? hi_bf(qr[i][j >> 1]) : lo_bf(qr[i][j >> 1]);
+                sk += kx * kx;
+                sq += qx * qx;
+            }
+#pragma unroll
+            for (int m = 1; m < 32; m <<= 1) {
+                sk += __shfl_xor(sk, m);
+                sq += __shfl_xor(sq, m);
+            }
+            nk[i] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sk), kFrontEps));
+            nq[i] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sq), kFrontEps));
+        }
     }
 
     // ---------------- cumulative gate (log2 units) ----------------------------
@@ -316,8 +375,12 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             const float w = __builtin_amdgcn_exp2f(-gl);
             const float d = gamma[j] * w;       // e^{G - g}: both factors stay in range
             const uint32_t kw = kr[i][j >> 1], qw = qr[i][j >> 1];
-            const float kx = (j & 1) ? hi_bf(kw) : lo_bf(kw);
-            const float qx = (j & 1) ? hi_bf(qw) : lo_bf(qw);
+            float kx = (j & 1) ? hi_bf(kw) : lo_bf(kw);
+            float qx = (j & 1) ? hi_bf(qw) : lo_bf(qw);
+            if constexpr (FRONT) {
+                kx *= nk[i];
+                qx *= nq[i];
+            }
             kg[i][j] = kx * u;
             qg[j] = qx * u;
             kn[j] = kx * w;
@@ -910,13 +973,16 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hip
     for (int64_t c_lo = 0; c_lo < bound; c_lo += L_b) {
         if (a.total_T > 0) {
             const int64_t nslots = static_cast<int64_t>(a.N) * L_b * a.H;
-            auto prep = a.gate == kGateChannel ? prefill_wy_prep_kernel<kGateChannel>
-                                               : prefill_wy_prep_kernel<kGateHead>;
+            const bool ch = a.gate == kGateChannel, fr = a.fe.active();
+            auto prep = ch ? (fr ? prefill_wy_prep_kernel<kGateChannel, true>
+                                 : prefill_wy_prep_kernel<kGateChannel, false>)
+                           : (fr ? prefill_wy_prep_kernel<kGateHead, true>
+                                 : prefill_wy_prep_kernel<kGateHead, false>);
             hipLaunchKernelGGL(prep, dim3(static_cast<unsigned>(nslots)), dim3(PT),
                                0, stream, static_cast<const bf16_t*>(a.q),
                                static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v),
                                a.log_alpha, a.beta, a.cu_seqlens, a.H, a.d_v,
-                               static_cast<int>(c_lo), L_b, slots);
+                               static_cast<int>(c_lo), L_b, slots, a.fe);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -115,6 +115,30 @@ enum kda_path {
                               for few long sequences.  bf16, d_k = 128 */
 };
 
+/*
+ * The fused input front-end: raw projections go in, the kernels apply the
+ * activations while they stage the inputs.  Every part is optional:
+ *   l2norm_qk  nonzero: q and k are divided, per (token, head), by
+ *              max(||x||_2, 1e-6) -- the unit keys the delta rule needs
+ *              ("Kimi Delta Attention: la atencion lineal detras de Kimi K2
+ *              y Qwen3", notes on key normalisation);
+ *   gate_pre   DEVICE bf16 pre-activations x in log_alpha's layout for the
+ *              call's gate (KDA: [tokens][H][d_k], 16-byte aligned; Gated
+ *              DeltaNet: [tokens][H], 2-byte aligned), replacing log_alpha,
+ *              which must then be NULL: log_alpha = -gate_scale *
+ *              softplus(x), so alpha is in (0, 1] for gate_scale >= 0;
+ *   beta_pre   DEVICE bf16 [tokens][H] pre-activations y (2-byte aligned),
+ *              replacing beta, which must then be NULL: beta = sigmoid(y).
+ * The pre-activations are bf16 whatever the dtype of q, k, v.  They cut a
+ * prefill's input from 1540 to 1282 bytes per head-token at d = 128.
+ */
+typedef struct kda_front_end {
+    int32_t l2norm_qk;
+    float gate_scale;              /* finite, >= 0; used with gate_pre */
+    const void *gate_pre;
+    const void *beta_pre;
+} kda_front_end;
+
 /* Tuning options of kda_fwd_prefill_ex (zero-initialise for defaults). */
 typedef struct kda_prefill_options {
     int32_t path;          /* a kda_path */
@@ -147,7 +171,10 @@ typedef struct kda_prefill_options {
                                   j < snapshot_capacity that fit in the
                                   sequence; other entries are not written.
                                   May not overlap any other buffer. */
+    kda_front_end front;       /* the fused input front-end (all off when
+                                  zeroed); vector and two-pass paths */
 } kda_prefill_options;
+
 
 /* Options of kda_decode_step_ex (zero-initialise for defaults). */
 typedef struct kda_decode_options {
@@ -163,6 +190,8 @@ typedef struct kda_decode_options {
                                       Indices of one call must be distinct
                                       (two sequences updating one state
                                       race). */
+    kda_front_end front;           /* the fused input front-end, as for the
+                                      prefill (tokens = N) */
 } kda_decode_options;
 
 /* Options of kda_decode_multi (zero-initialise, then set write_state, for

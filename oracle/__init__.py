@@ -276,3 +276,27 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
     elif np.asarray(log_alpha).shape == (T, H):
         out["dlog_alpha"] = out["dlog_alpha"].sum(axis=-1)
     return out
+
+
+def front_end(q, k, gate_pre=None, beta_pre=None, gate_scale=1.0, l2norm=True, eps=1e-6):
+    """The fused input front-end's activations, in float64.
+
+    q, k divided by max(||x||_2, eps) per (token, head) when l2norm (the
+    unit keys the delta rule needs: "Kimi Delta Attention: la atencion
+    lineal detras de Kimi K2 y Qwen3", notes on key normalisation);
+    log_alpha = -gate_scale * softplus(gate_pre), softplus(x) = log(1 + e^x)
+    written as max(x, 0) + log1p(e^-|x|); beta = 1 / (1 + e^-beta_pre).
+    Missing pre-activations give None.  Returns (q, k, log_alpha, beta)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    if l2norm:
+        q = q / np.maximum(np.linalg.norm(q, axis=-1, keepdims=True), eps)
+        k = k / np.maximum(np.linalg.norm(k, axis=-1, keepdims=True), eps)
+    la = None
+    if gate_pre is not None:
+        x = np.asarray(gate_pre, dtype=np.float64)
+        la = -gate_scale * (np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x))))
+    beta = None
+    if beta_pre is not None:
+        beta = 1.0 / (1.0 + np.exp(-np.asarray(beta_pre, dtype=np.float64)))
+    return q, k, la, beta

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 7
+    assert kda.abi_version() == 8
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -153,12 +153,14 @@ def test_binding_rejects_cpu_tensors():
         kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
 
 
-def prefill_ex_call(path, tiles, blk=0, gate=0, snap=(0, 0, None), **over):
+def prefill_ex_call(path, tiles, blk=0, gate=0, snap=(0, 0, None), front=None, **over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
                 o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
     args.update(over)
     opts = kda.PrefillOptions(path, tiles, blk, gate, snap[0], snap[1], snap[2])
+    if front is not None:
+        opts.front = kda.FrontEnd(*front)
     lib = kda.load_library()
     return lib.kda_fwd_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
                                   args["h0"], args["cu"], args["T"], args["N"], args["H"],
@@ -324,6 +326,51 @@ def test_backward_workspace_query():
     # one fp32 state per (chunk, head) grows with the tokens
     assert a > 0 and b - a >= 4096 // 64 * 16 * 128 * 128 * 4
     assert kda.backward_workspace_bytes(4096, 4, 16, 128, 128) == a
+
+
+# the fused input front-end: (l2norm_qk, gate_scale, gate_pre, beta_pre);
+# every case fails before any HIP call (WS_SMALL: all checks passed)
+GP, BP = BASE + 14 * GAP, BASE + 15 * GAP
+
+
+@pytest.mark.parametrize("path,front,over,status", [
+    (0, (1, 0.0, None, None), {}, WS_SMALL),                        # normalisation only
+    (0, (0, 0.05, GP, BP), dict(la=None, beta=None), WS_SMALL),      # both activations
+    (0, (0, 0.05, GP, None), {}, INVALID),                           # log_alpha must be NULL
+    (0, (0, 0.05, None, BP), {}, INVALID),                           # beta must be NULL
+    (0, (0, -1.0, GP, None), dict(la=None), INVALID),                # negative gate scale
+    (0, (0, float("nan"), GP, None), dict(la=None), INVALID),
+    (0, (0, 0.05, GP + 8, None), dict(la=None), MISALIGNED),         # per-channel: 16 bytes
+    (0, (0, 0.05, None, BP + 1), dict(beta=None), MISALIGNED),
+    (2, (1, 0.0, None, None), {}, UNSUPPORTED),                      # not on the fused path
+    (3, (0, 0.05, GP, BP), dict(la=None, beta=None, o=addr(14, 64), wsb=1 << 34), INVALID),
+])
+def test_prefill_front_end_checks(path, front, over, status):
+    assert prefill_ex_call(path, 0, front=front, **over) == status
+
+
+def test_prefill_front_end_gate_layouts():
+    # per-head gate pre-activations need 2-byte alignment only; none: no gate_pre
+    assert prefill_ex_call(0, 0, gate=1, front=(0, 0.1, GP + 2, None), la=None) == WS_SMALL
+    assert prefill_ex_call(0, 0, gate=2, front=(0, 0.1, GP, None), la=None) == INVALID
+
+
+def test_decode_front_end_checks():
+    def call(front, **over):
+        args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), S=addr(5),
+                    N=8, H=4, dk=128, dv=128, dtype=0, scale=0.1, o=addr(6), stream=None)
+        args.update(over)
+        opts = kda.DecodeOptions(0, 0, None)
+        opts.front = kda.FrontEnd(*front)
+        return kda.load_library().kda_decode_step_ex(
+            args["q"], args["k"], args["v"], args["la"], args["beta"], args["S"], args["N"],
+            args["H"], args["dk"], args["dv"], args["dtype"], args["scale"], args["o"],
+            ctypes.byref(opts), args["stream"])
+    assert call((0, 0.05, GP, None)) == INVALID                      # log_alpha not NULL
+    assert call((0, 0.05, GP, BP)) == INVALID
+    assert call((0, 0.05, GP, None), la=None, S=addr(5, 4)) == MISALIGNED   # passed the front-end checks
+    assert call((0, 0.05, None, BP + 1), beta=None) == MISALIGNED
+    assert call((0, 0.05, GP, None), la=None, o=addr(14, 32)) == INVALID    # o on gate_pre
 
 
 # snapshots: [N][capacity][H][d_k][d_v] fp32 (N = 2, H = 4, d = 128: 512 KiB

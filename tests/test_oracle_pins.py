@@ -392,3 +392,34 @@ def test_planted_mistakes_are_caught(tmp_path):
         mod = importlib.util.module_from_spec(spec)
         spec.loader.exec_module(mod)
         assert not _pins_pass(mod), "planted mistake not caught: " + name
+
+
+# --------------------------------------------------------------------------
+# the fused input front-end's activations
+# --------------------------------------------------------------------------
+def test_front_end_closed_forms():
+    """softplus(0) = ln 2 and sigmoid(0) = 1/2; softplus(x) - softplus(-x) = x
+    and sigmoid(y) + sigmoid(-y) = 1 (both follow from e^x / (1 + e^x) =
+    1 - 1 / (1 + e^x)); softplus equals log(1 + e^x) where that form is
+    exact enough; the normalised rows have unit norm and do not change when
+    q, k are scaled."""
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((50, 3, 4)) * 4
+    z = np.zeros((1, 1, 2))
+    _, _, la0, b0 = oracle.front_end(z, z, gate_pre=z, beta_pre=z[..., 0], gate_scale=1.0,
+                                     l2norm=False)
+    assert np.allclose(la0, -np.log(2.0), rtol=0, atol=1e-15)
+    assert np.allclose(b0, 0.5, rtol=0, atol=1e-15)
+    q = rng.standard_normal((50, 3, 8))
+    _, _, lp, bp = oracle.front_end(q, q, gate_pre=x, beta_pre=x[..., 0], gate_scale=0.3)
+    _, _, lm, bm = oracle.front_end(q, q, gate_pre=-x, beta_pre=-x[..., 0], gate_scale=0.3)
+    assert np.allclose(lp - lm, -0.3 * x, rtol=0, atol=1e-12)
+    assert np.allclose(bp + bm, 1.0, rtol=0, atol=1e-14)
+    small = np.abs(x) < 20
+    assert np.allclose(lp[small], -0.3 * np.log(1.0 + np.exp(x[small])), rtol=1e-12, atol=1e-14)
+    qn, kn, _, _ = oracle.front_end(q, 2.5 * q)
+    assert np.allclose(np.linalg.norm(qn, axis=-1), 1.0, atol=1e-14)
+    assert np.allclose(qn, kn, atol=1e-15)
+    qs, _, _, _ = oracle.front_end(7.0 * q, q)
+    assert np.allclose(qs, qn, atol=1e-15)
+
