@@ -571,7 +571,16 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
     // =========================== phase A ===========================
     {
         GradALds& sm = sm_u.a;
-        // ---- R = V - Kg S, and (Diag(beta) R)^T
+        // ---- one round of loads: S (both layouts), Kg, V, beta, Minv (both
+        //      layouts), dE; dO into registers until its LDS region frees
+        u32x4 pdo[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int u = x * NT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
+            pdo[x] = u32x4{0u, 0u, 0u, 0u};
+            if (r < c.len)
+                pdo[x] = *reinterpret_cast<const u32x4*>(dO + ((c.t0 + r) * H + c.h) * D + c8);
+        }
         stage_f32(S, D, sm.s0, LDD, sm.s0t, LDD);
         copy_rows(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
         for (int u = tid; u < C * (D / 4); u += NT) {
@@ -581,7 +590,15 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             put4t(sm.r + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
         }
         if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
+        for (int u = tid; u < C * C; u += NT) {
+            const int r = u / C, s2 = u % C;
+            const bf16_t x = bf(mvg[u]);
+            sm.mv[r * LDC + s2] = x;
+            sm.mvt[s2 * LDC + r] = x;
+        }
+        stage_f32(dE, C, sm.de, LDD, nullptr, 0);
         __syncthreads();
+        // ---- R = V - Kg S, and (Diag(beta) R)^T
         mm<4, 8, D>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
             const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
             f32x4 br;
@@ -594,25 +611,42 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             }
             put4t(sm.brt + col * LDC + r0, br);
         });
-        // ---- E = Minv (Diag(beta) R)
-        for (int u = tid; u < C * C; u += NT) {
-            const int r = u / C, s2 = u % C;
-            const bf16_t x = bf(mvg[u]);
-            sm.mv[r * LDC + s2] = x;
-            sm.mvt[s2 * LDC + r] = x;
-        }
         __syncthreads();
-        bf16_t* E = sm.kg;   // Kg is no longer needed
+        // ---- E = Minv (Diag(beta) R) over Kg; dS' over S^T, with dgamma =
+        //      rowsum(dS' . S) in fp32
+        bf16_t* E = sm.kg;
         mm<4, 8, C>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
         });
+        bf16_t* dsl = sm.s0t;
+        {
+            const int row = tid >> 1, half = tid & 1;
+            float part = 0.f;
+#pragma unroll 4
+            for (int x = 0; x < D / 2; x += 4) {
+                const int col = 64 * half + x;
+                const f32x4 d = *reinterpret_cast<const f32x4*>(dSp + row * D + col);
+                f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+                if (S) sv = *reinterpret_cast<const f32x4*>(S + row * D + col);
+                part += d[0] * sv[0] + d[1] * sv[1] + d[2] * sv[2] + d[3] * sv[3];
+                put4t(dsl + row * LDD + col, d);
+            }
+            part += __shfl_xor(part, 1);
+            if (half == 0) s_dgam[row] = part;
+        }
         __syncthreads();
-        // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT);
-        //      dV = T^T dE = Diag(beta) Minv^T dE
+        // ---- dE^T (over (Diag(beta) R)^T, now free) from dE in LDS
         bf16_t* det = sm.brt;
-        stage_f32(dE, C, sm.de, LDD, det, LDC);
-        __syncthreads();
+        for (int u = tid; u < C * (D / 4); u += NT) {
+            const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+            const u32x2 w = *reinterpret_cast<const u32x2*>(sm.de + r * LDD + c0);
+            det[(c0 + 0) * LDC + r] = static_cast<bf16_t>(w[0] & 0xffffu);
+            det[(c0 + 1) * LDC + r] = static_cast<bf16_t>(w[0] >> 16);
+            det[(c0 + 2) * LDC + r] = static_cast<bf16_t>(w[1] & 0xffffu);
+            det[(c0 + 3) * LDC + r] = static_cast<bf16_t>(w[1] >> 16);
+        }
+        // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT)
         mm_regs<4, D>(sm.de, LDD, sm.r, LDD, rT);
         {   // wave w holds column block w of dT, row blocks x = 0..3
             const int s2 = 16 * wave + ln;
@@ -626,7 +660,8 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             if (g4 == 0) s_dbT[s2] = part;
         }
         __syncthreads();
-        bf16_t* dV = sm.r;   // R is no longer needed
+        // ---- dV = T^T dE = Diag(beta) Minv^T dE (over R)
+        bf16_t* dV = sm.r;
         mm<4, 8, C>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -637,13 +672,12 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             }
         });
         __syncthreads();
-        // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T (kept)
-        bf16_t* dOl = sm.brt;   // dE^T is no longer needed
-        for (int u = tid; u < C * (D / 4); u += NT) {
-            const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-            float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (r < c.len) x = elem<T>::load4(dO + ((c.t0 + r) * H + c.h) * D + c0);
-            put4t(dOl + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
+        // ---- dO (over dE^T); dKg_W = -dV S^T, dQg_S = scale dO S^T (kept)
+        bf16_t* dOl = sm.brt;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int u = x * NT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
+            *reinterpret_cast<u32x4*>(dOl + r * LDD + c8) = pdo[x];
         }
         __syncthreads();
         mm_regs<8, D>(dV, LDD, sm.s0, LDD, rKgW);
@@ -653,23 +687,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             rKgW[x] = -rKgW[x];
             rQgS[x] = scale * rQgS[x];
         }
-        // ---- dS' over S^T; dgamma = rowsum(dS' . S) in fp32
-        bf16_t* dsl = sm.s0t;
-        {
-            const int row = tid >> 1, half = tid & 1;
-            float part = 0.f;
-            for (int x = 0; x < D / 2; x += 4) {
-                const int col = 64 * half + x;
-                const f32x4 d = *reinterpret_cast<const f32x4*>(dSp + row * D + col);
-                f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-                if (S) sv = *reinterpret_cast<const f32x4*>(S + row * D + col);
-                part += d[0] * sv[0] + d[1] * sv[1] + d[2] * sv[2] + d[3] * sv[3];
-                put4t(dsl + row * LDD + col, d);
-            }
-            part += __shfl_xor(part, 1);
-            if (half == 0) s_dgam[row] = part;
-        }
-        __syncthreads();
         // ---- dKd = E dS'^T, dP = lower(scale dO E^T) (kept)
         mm_regs<8, D>(E, LDD, dsl, LDD, rKd);
         mm_regs<4, D>(dOl, LDD, E, LDD, rP);
@@ -684,19 +701,33 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
     }
     // =========================== phase B ===========================
     GradBLds& sm = sm_u.b;
-    load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
-    __syncthreads();
-    // gated keys and queries, transposed (B operands); Minv, Minv^T;
-    // (dT Diag(beta))^T; dbeta starts at dbeta_T, dG at dgamma gamma
-    for (int u = tid; u < C * (D / 4); u += NT) {
-        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+    // k and q of the chunk into registers while the gates load and scan,
+    // and Minv into LDS: one round of loads
+    float4 kr4[8], qr4[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        const int u = x * NT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        kr4[x] = qr4[x] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (r < c.len) {
             const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
-            kv = elem<T>::load4(k + row);
-            qv = elem<T>::load4(q + row);
+            kr4[x] = elem<T>::load4(k + row);
+            qr4[x] = elem<T>::load4(q + row);
         }
-        const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+    }
+    for (int u = tid; u < C * C; u += NT) {
+        const int r = u / C, s2 = u % C;
+        const bf16_t x = bf(mvg[u]);
+        sm.ra[0][r * LDC + s2] = x;
+        sm.ra[1][s2 * LDC + r] = x;
+    }
+    load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
+    __syncthreads();
+    // gated keys and queries, transposed (B operands)
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+        const int u = x * NT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        const float kk[4] = {kr4[x].x, kr4[x].y, kr4[x].z, kr4[x].w};
+        const float qq[4] = {qr4[x].x, qr4[x].y, qr4[x].z, qr4[x].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const float gv = sm.g[r * D + c0 + e];
@@ -705,12 +736,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             sm.knt[(c0 + e) * LDC + r] = bf(kk[e] * en);
             sm.qgt[(c0 + e) * LDC + r] = bf(qq[e] * eg);
         }
-    }
-    for (int u = tid; u < C * C; u += NT) {
-        const int r = u / C, s2 = u % C;
-        const bf16_t x = bf(mvg[u]);
-        sm.ra[0][r * LDC + s2] = x;
-        sm.ra[1][s2 * LDC + r] = x;
     }
     {   // Y^T[s][i] = dT[i][s] beta_s from this wave's dT tiles (column block = wave)
         const int s2 = 16 * wave + ln;

@@ -107,3 +107,35 @@ def test_backward_batch4_t4096_sampled_heads():
     g = gpu(inp, "channel")
     heads = [0, 11]
     compare("backward batch4_t4096 heads %s" % heads, g, ref(inp, heads), heads)
+
+
+def test_backward_long_t1m_last_window():
+    """The 1M-token backward in the configuration bench.py times, checked on
+    the last 8192 tokens of two heads: the oracle's backward over that
+    window starts from the state the forward reaches at its first token (a
+    snapshot of the same two-pass forward the backward recomputes, so the
+    same bits) and takes the same dO and dhT; every gradient of a token in
+    the window depends on nothing else."""
+    w = gen.WORKLOADS["long_t1m"]
+    inp = gen.workload_prefill_inputs(w, seed=340, device=DEV)
+    T, H = inp["q"].shape[:2]
+    W, heads = 8192, [3, 30]
+    t0 = T - W
+    do = gen.normal((T, H, 128), 340, gen.DO, DEV, torch.bfloat16)
+    dhT = gen.normal((1, H, 128, 128), 340, gen.DHT, DEV, torch.float32, std=0.1)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    g = kda.backward(*args, do, dhT=dhT, cu_seqlens=inp["cu_seqlens"], want_dh0=False)
+    win = {key: host(x[t0:, heads]) for key, x in g.items() if x is not None}
+    del g
+    torch.cuda.empty_cache()
+    _, _, snaps = kda.prefill(*args, cu_seqlens=inp["cu_seqlens"], final_state=False,
+                              snapshot_tokens=t0)
+    S0 = host(snaps[:, 0][:, heads])
+    del snaps
+    sel = lambda x: host(x[t0:, heads])
+    ref = oracle.backward(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["log_alpha"]),
+                          sel(inp["beta"]), sel(do), h0=S0, dhT=host(dhT[:, heads]))
+    errs = {key: rel_err(win[key], ref[key]) for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta")}
+    report("backward long_t1m last %d tokens, heads %s" % (W, heads), **errs)
+    for key, e in errs.items():
+        assert e <= TOL, (key, e)
