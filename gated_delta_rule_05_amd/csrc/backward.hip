@@ -340,8 +340,8 @@ __device__ __forceinline__ void copy_rows(bf16_t* dst, int ld, const bf16_t* src
 __global__ __launch_bounds__(NT)
 void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dO,
                       const int32_t* __restrict__ cu, int N, int H, int c_lo, int L_b,
-                      float* __restrict__ dstate, float* __restrict__ dsblk,
-                      float* __restrict__ deblk, float* __restrict__ dh0)
+                      float* __restrict__ dstate, bf16_t* __restrict__ dsblk,
+                      bf16_t* __restrict__ deblk, float* __restrict__ dh0)
 {
     __shared__ CarryLds sm;
     constexpr int R = D / kCarryTile;
@@ -423,18 +423,18 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     for (int j = hi; j >= c_lo; --j) {
         const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
         put();
-        // dS' of this chunk (fp32, for the grad pass) and as a bf16 B operand
-        float* dsp = dsblk + slot * kState;
+        // dS' of this chunk (bf16, for the grad pass) and as a bf16 B operand
+        bf16_t* dsp = dsblk + slot * kState;
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dsp[(16 * m + 4 * g4 + i) * D + jc] = S[m][i];
+            for (int i = 0; i < 4; ++i) dsp[(16 * m + 4 * g4 + i) * D + jc] = bf(S[m][i]);
             put4t(&sm.dst[wave][ln * LDD + 16 * m + 4 * g4], S[m]);
         }
         __syncthreads();
         if (j > c_lo) fetch(j - 1);
         // dE = Kd dS' + scale P^T dO  (this wave's 16 columns, 4 row tiles)
-        float* dep = deblk + slot * (static_cast<int64_t>(C) * D);
+        bf16_t* dep = deblk + slot * (static_cast<int64_t>(C) * D);
         const bf16_t* dsw = sm.dst[wave];
         const bf16_t* dow = sm.dot + 16 * wave * LDC;
 #pragma unroll
@@ -443,7 +443,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
             acc = tile_mm<D>(sm.kd + 16 * m * LDD, LDD, dsw, LDD, lane, acc);
             acc = tile_mm<C>(sm.pt + 16 * m * LDC, LDC, dow, LDC, lane, acc);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dep[(16 * m + 4 * g4 + i) * D + jc] = acc[i];
+            for (int i = 0; i < 4; ++i) dep[(16 * m + 4 * g4 + i) * D + jc] = bf(acc[i]);
             put4t(&sm.det[wave][ln * LDC + 16 * m + 4 * g4], acc);
         }
         __syncthreads();
@@ -520,6 +520,22 @@ __device__ __forceinline__ void stage_f32(const float* src, int rows, bf16_t* rm
     }
 }
 
+// bf16 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
+__device__ __forceinline__ void stage_bf16(const bf16_t* src, int rows, bf16_t* rm, int ld,
+                                           bf16_t* tr, int ldt) {
+    for (int u = threadIdx.x; u < rows * (D / 4); u += NT) {
+        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+        const u32x2 w = *reinterpret_cast<const u32x2*>(src + r * D + c0);
+        if (rm) *reinterpret_cast<u32x2*>(rm + r * ld + c0) = w;
+        if (tr) {
+            tr[(c0 + 0) * ldt + r] = static_cast<bf16_t>(w[0] & 0xffffu);
+            tr[(c0 + 1) * ldt + r] = static_cast<bf16_t>(w[0] >> 16);
+            tr[(c0 + 2) * ldt + r] = static_cast<bf16_t>(w[1] & 0xffffu);
+            tr[(c0 + 3) * ldt + r] = static_cast<bf16_t>(w[1] >> 16);
+        }
+    }
+}
+
 // this wave's tiles of a (4 x NTL)-tile product, in a fixed order: tile x
 // is t = wave + 4 x (row block t / NTL, column block t % NTL)
 template <int NTL, int K, int NX>
@@ -534,19 +550,19 @@ __device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* 
     }
 }
 
-// the start state of chunk j of sequence n: h0 (or null = zeros) for the
-// first chunk, else the state the forward pass recorded after chunk j-1
-__device__ __forceinline__ const float* start_state(const ChunkRef& c, const float* h0,
-                                                    const float* sall, const int32_t* cu, int H) {
-    if (c.j == 0) return h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState : nullptr;
+// the start state of chunk j of sequence n: for the first chunk h0 (fp32;
+// null = zeros), else the state the forward pass recorded after chunk j-1
+// (bf16, transposed: [value column][key row])
+__device__ __forceinline__ const bf16_t* recorded_state(const ChunkRef& c, const bf16_t* sall,
+                                                        const int32_t* cu, int H) {
     const int64_t idx = c.n + cu[c.n] / C + (c.j - 1);
     return sall + (idx * H + c.h) * kState;
 }
 
 template <typename T, int GATE>
 __global__ __launch_bounds__(NT)
-void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict__ dsblk,
-                     const float* __restrict__ deblk, const float* __restrict__ sall,
+void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dsblk,
+                     const bf16_t* __restrict__ deblk, const bf16_t* __restrict__ sall,
                      const float* __restrict__ h0, const T* __restrict__ q,
                      const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
                      const float* __restrict__ la, const float* __restrict__ beta,
@@ -562,9 +578,10 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
     const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
     const float* mvg = reinterpret_cast<const float*>(sp + kOffMinv);
     const float* Bm = reinterpret_cast<const float*>(sp + kOffB);
-    const float* S = start_state(c, h0, sall, cu, H);
-    const float* dSp = dsblk + c.slot * kState;
-    const float* dE = deblk + c.slot * (static_cast<int64_t>(C) * D);
+    const float* S0f = c.j == 0 && h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState
+                                      : nullptr;
+    const bf16_t* dSp = dsblk + c.slot * kState;
+    const bf16_t* dE = deblk + c.slot * (static_cast<int64_t>(C) * D);
 
     f32x4 rKgW[8], rQgS[8], rKd[8];   // [C][D] terms, tiles t = wave + 4x of 4 x 8
     f32x4 rT[4], rP[4];               // [C][C] terms, tiles t = wave + 4x of 4 x 4
@@ -581,7 +598,8 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             if (r < c.len)
                 pdo[x] = *reinterpret_cast<const u32x4*>(dO + ((c.t0 + r) * H + c.h) * D + c8);
         }
-        stage_f32(S, D, sm.s0, LDD, sm.s0t, LDD);
+        if (c.j == 0) stage_f32(S0f, D, sm.s0, LDD, sm.s0t, LDD);
+        else stage_bf16(recorded_state(c, sall, cu, H), D, sm.s0t, LDD, sm.s0, LDD);   // S^T rows
         copy_rows(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
         for (int u = tid; u < C * (D / 4); u += NT) {
             const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
@@ -596,7 +614,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
             sm.mv[r * LDC + s2] = x;
             sm.mvt[s2 * LDC + r] = x;
         }
-        stage_f32(dE, C, sm.de, LDD, nullptr, 0);
+        stage_bf16(dE, C, sm.de, LDD, nullptr, 0);
         __syncthreads();
         // ---- R = V - Kg S, and (Diag(beta) R)^T
         mm<4, 8, D>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
@@ -613,7 +631,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
         });
         __syncthreads();
         // ---- E = Minv (Diag(beta) R) over Kg; dS' over S^T, with dgamma =
-        //      rowsum(dS' . S) in fp32
+        //      rowsum(dS' . S) from the bf16 records, summed in fp32
         bf16_t* E = sm.kg;
         mm<4, 8, C>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
@@ -626,11 +644,11 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const float* __restrict_
 #pragma unroll 4
             for (int x = 0; x < D / 2; x += 4) {
                 const int col = 64 * half + x;
-                const f32x4 d = *reinterpret_cast<const f32x4*>(dSp + row * D + col);
-                f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-                if (S) sv = *reinterpret_cast<const f32x4*>(S + row * D + col);
-                part += d[0] * sv[0] + d[1] * sv[1] + d[2] * sv[2] + d[3] * sv[3];
-                put4t(dsl + row * LDD + col, d);
+                const u32x2 dw = *reinterpret_cast<const u32x2*>(dSp + row * D + col);
+                const u32x2 sw = *reinterpret_cast<const u32x2*>(sm.s0 + row * LDD + col);
+                part += lo_bf(dw[0]) * lo_bf(sw[0]) + hi_bf(dw[0]) * hi_bf(sw[0]) +
+                        lo_bf(dw[1]) * lo_bf(sw[1]) + hi_bf(dw[1]) * hi_bf(sw[1]);
+                *reinterpret_cast<u32x2*>(dsl + row * LDD + col) = dw;
             }
             part += __shfl_xor(part, 1);
             if (half == 0) s_dgam[row] = part;
@@ -891,10 +909,10 @@ BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
     const size_t blk = nh * L_b;
     l.fwd = wy_workspace_bytes(N, H, D, D, wy_default_block_chunks(total_T, N, H, D));
     l.sall = (static_cast<size_t>(N) + static_cast<size_t>(bound_chunks(total_T)) + 1) * H *
-             kState * 4;
+             kState * 2;
     l.slots = blk * kSlot;
-    l.dsblk = blk * kState * 4;
-    l.deblk = blk * C * D * 4;
+    l.dsblk = blk * kState * 2;
+    l.deblk = blk * C * D * 2;
     l.dstate = nh * kState * 4;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     l.total = up(l.fwd) + up(l.sall) + up(l.slots) + up(l.dsblk) + up(l.deblk) +
@@ -906,9 +924,9 @@ BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
 
 int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
     // about 1 GiB of per-block buffers (prep operands and carry outputs:
-    // ~200 KB per (chunk, head)), at most 64 chunks
+    // ~155 KB per (chunk, head)), at most 64 chunks
     const size_t per_chunk = static_cast<size_t>(N) * H *
-                             (kSlot + kState * 4 + static_cast<size_t>(C) * D * 4);
+                             (kSlot + kState * 2 + static_cast<size_t>(C) * D * 2);
     int64_t L = static_cast<int64_t>((size_t{1} << 30) / per_chunk);
     L = std::max<int64_t>(1, std::min<int64_t>(L, std::max<int64_t>(1, bound_chunks(total_T))));
     return static_cast<int>(std::min<int64_t>(L, 64));
@@ -923,10 +941,10 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     uint8_t* p = static_cast<uint8_t*>(ws);
     uint8_t* fwd_ws = p;          p += up(l.fwd);
-    float* sall = reinterpret_cast<float*>(p);    p += up(l.sall);
+    bf16_t* sall = reinterpret_cast<bf16_t*>(p);  p += up(l.sall);
     uint8_t* slots = p;           p += up(l.slots);
-    float* dsblk = reinterpret_cast<float*>(p);   p += up(l.dsblk);
-    float* deblk = reinterpret_cast<float*>(p);   p += up(l.deblk);
+    bf16_t* dsblk = reinterpret_cast<bf16_t*>(p);  p += up(l.dsblk);
+    bf16_t* deblk = reinterpret_cast<bf16_t*>(p);  p += up(l.deblk);
     float* dstate = reinterpret_cast<float*>(p);
 
     // 1. forward: the state after every full chunk, no outputs
@@ -935,7 +953,8 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
     f.cu_seqlens = a.cu_seqlens; f.o = nullptr; f.hT = nullptr; f.order = nullptr;
     f.total_T = a.total_T; f.N = a.N; f.H = a.H; f.d_k = D; f.d_v = D; f.gate = a.gate;
     f.dtype_f32 = false; f.scale = a.scale;
-    f.snapshots = sall; f.snap_tokens = C; f.snap_cap = -1;
+    f.snapshots = reinterpret_cast<float*>(sall);   // bf16 record (snap_cap < 0)
+    f.snap_tokens = C; f.snap_cap = -1;
     hipError_t e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D),
                                      fwd_ws, stream);
     if (e != hipSuccess) return e;

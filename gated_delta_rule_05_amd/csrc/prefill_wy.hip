@@ -800,20 +800,29 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             const int js = SNAP && --snap_left == 0
                                ? (snap_left = snap_stride, (c_lo + x + 1) / snap_stride - 1) : -1;
             // (only a full chunk ends on a boundary).  snap_cap < 0 selects the
-            // compact per-chunk layout: the state after chunk js of sequence
-            // n at index n + cu[n] / C + js, which never collides with the
-            // next sequence's (it starts at least ceil(len / C) indices on)
+            // compact per-chunk record of the gradient pass: bf16 transposed states, the
+            // state after chunk js of sequence n at index n + cu[n] / C + js,
+            // which never collides with the next sequence's (it starts at
+            // least ceil(len / C) indices on)
             if (js >= 0 && (snap_cap < 0 || js < snap_cap) && (c_lo + x + 1) * C <= seq_len) {
                 const int64_t SE = static_cast<int64_t>(DK) * DV;
-                float* sp = snap_cap >= 0
-                                ? snapshot_at(snapshots, snap_cap, H, SE, n, js, h)
-                                : snapshots + ((n + t_begin / C + js) * H + h) * SE;
-                const __amdgpu_buffer_rsrc_t rs = rsrc(sp + j0, 4u * DK * DV);
-                const int lo = 4 * (4 * g * DV + jc);
+                const int lo = 4 * g * DV + jc;
+                if (snap_cap >= 0) {
+                    float* sp = snapshot_at(snapshots, snap_cap, H, SE, n, js, h);
+                    const __amdgpu_buffer_rsrc_t rs = rsrc(sp + j0, 4u * DK * DV);
 #pragma unroll
-                for (int m = 0; m < 8; ++m)
+                    for (int m = 0; m < 8; ++m)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) st32(rs, lo + 4 * (16 * m + i) * DV, __float_as_uint(S[m][i]));
+                        for (int i = 0; i < 4; ++i)
+                            st32(rs, 4 * (lo + (16 * m + i) * DV), __float_as_uint(S[m][i]));
+                } else {
+                    // bf16, transposed ([value column][key row]): a lane's 4
+                    // rows of one column are one 8-byte store
+                    bf16_t* sp = reinterpret_cast<bf16_t*>(snapshots) + ((n + t_begin / C + js) * H + h) * SE;
+                    const __amdgpu_buffer_rsrc_t rs = rsrc(sp + static_cast<int64_t>(j0) * DK, 2u * TV * DK);
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) st64(rs, 2 * (jc * DK + 16 * m + 4 * g), pack2(S[m]));
+                }
             }
             __syncthreads();
             bx = bn;

@@ -375,9 +375,9 @@ int kda_decode_multi(const void *q, const void *k, const void *v,
 
 /*
  * Bytes of device workspace kda_bwd needs for these sizes and options:
- * the start state of every chunk (one fp32 state per (chunk, head), so
- * about 1 GiB per 16,384 head-chunks), the forward pass's operand block,
- * and one block of per-(chunk, head) backward operands.  0 for arguments
+ * the start state of every chunk (one bf16 state per (chunk, head), so
+ * 512 MiB per 16,384 head-chunks), the forward pass's operand block, and
+ * one block of per-(chunk, head) backward operands.  0 for arguments
  * kda_bwd would reject.
  */
 size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
