@@ -27,6 +27,10 @@ tokens per sequence: one call verifies them (outputs, states only read),
 one commits an accepted prefix of 0..4 tokens (states advanced), each
 reading a state once, beside the time of 4 single decode steps.
 
+other_prefill_workloads: the tiny fp32 batch, the 4 x 4096-token batch and
+the 64-sequence varlen batch, each timed alone against its algorithmic
+bytes (the library picks the path).
+
 front_end: the same prefill from raw inputs (the fused input front-end:
 q, k normalised in the kernel, bf16 gate and beta pre-activations, 1282
 algorithmic bytes per head-token).
@@ -380,6 +384,33 @@ def main():
     del pool
     torch.cuda.empty_cache()
 
+    # ---------------- the other prefill workloads (the library's automatic path)
+    others = {}
+    for wname in ("tiny_f32", "batch4_t4096", "varlen_n64"):
+        wo = gen.WORKLOADS[wname]
+        io = gen.workload_prefill_inputs(wo, seed=11, device=dev)
+        To, No = io["q"].shape[0], io["cu_seqlens"].shape[0] - 1
+        esz = 4 if wo.dtype == "f32" else 2
+        oo = torch.empty((To, wo.H, wo.dv), dtype=io["q"].dtype, device=dev)
+        ho = torch.empty((No, wo.H, wo.dk, wo.dv), dtype=torch.float32, device=dev)
+        wso = torch.empty(max(1, kda.prefill_workspace_bytes(To, No, wo.H, wo.dk, wo.dv,
+                                                             kda.DTYPE_F32 if esz == 4 else kda.DTYPE_BF16)),
+                          dtype=torch.uint8, device=dev)
+
+        def run_o():
+            kda.prefill(io["q"], io["k"], io["v"], io["log_alpha"], io["beta"], h0=io["h0"],
+                        cu_seqlens=io["cu_seqlens"], out=oo, final_state=ho, workspace=wso)
+        o_ms = timed(run_o, max(args.steps, 20))
+        # q, k, v, o in the input dtype, fp32 gates and beta; states in and out
+        per_ht = (2 * wo.dk + 2 * wo.dv) * esz + 4 * wo.dk + 4
+        nb = per_ht * To * wo.H + ho.numel() * 4 * (2 if io["h0"] is not None else 1)
+        others[wname] = {"tokens": To, "sequences": No, "heads": wo.H, "dtype": wo.dtype,
+                         "ms": o_ms, "tokens_per_s": To / (o_ms * 1e-3),
+                         "algorithmic_bytes": nb, "achieved_GBps": nb / (o_ms * 1e-3) / 1e9,
+                         "frac_of_hbm_peak": nb / (o_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+        del io, oo, ho, wso
+    torch.cuda.empty_cache()
+
     # ---------------- prefill gradients on the same workload ----------------
     backward = bench_backward(torch, kda, gen, inp, args.steps, args.warmup)
     backward["vs_forward"] = backward["ms"] / pre_avg
@@ -426,6 +457,7 @@ def main():
         "gate_variants": variants,
         "front_end": front,
         "serving": serving,
+        "other_prefill_workloads": others,
         "backward": backward,
         "cpu_baseline": None,
     }
