@@ -110,11 +110,11 @@ __device__ __forceinline__ f32x4 tile_mm(const bf16_t* a, int lda, const bf16_t*
 
 // all 16x16 tiles (mi < MT, ni < NT_) of A B, spread over the 4 waves;
 // fn(mi, ni, acc) consumes each (acc[i] = row 16 mi + 4g + i, column 16 ni + ln)
-template <int MT, int NTL, int K, typename Fn>
+template <int MT, int NTL, int K, int NTH = NT, typename Fn>
 __device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
                                    Fn&& fn) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int t = wave; t < MT * NTL; t += NT / 64) {
+    for (int t = wave; t < MT * NTL; t += NTH / 64) {
         const int mi = t / NTL, ni = t - mi * NTL;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = tile_mm<K>(a + 16 * mi * lda, lda, bt + 16 * ni * ldb, ldb, lane, acc);
@@ -133,11 +133,11 @@ __device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
 // the chunk repeat the last row); beta of its rows into bs[C] (0 past it).
 // The raw gates land in g with parallel vector loads first; the scan then
 // runs over LDS.
-template <int GATE>
+template <int GATE, int NTH = NT>
 __device__ __forceinline__ void load_gates(const float* la, const float* beta, const ChunkRef& c,
                                            int H, float* g, float* bs) {
     const int tid = threadIdx.x;
-    for (int u = tid; u < C * (D / 4); u += NT) {
+    for (int u = tid; u < C * (D / 4); u += NTH) {
         const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (r < c.len) {
@@ -328,10 +328,11 @@ struct alignas(16) CarryLds {
 };
 
 // copy a [rows][cols] bf16 matrix (global, contiguous) into LDS rows of ld
+template <int NTH = NT>
 __device__ __forceinline__ void copy_rows(bf16_t* dst, int ld, const bf16_t* src, int rows,
                                           int cols) {
     const int per = cols / 8;
-    for (int u = threadIdx.x; u < rows * per; u += NT) {
+    for (int u = threadIdx.x; u < rows * per; u += NTH) {
         const int r = u / per, x = (u % per) * 8;
         *reinterpret_cast<u32x4*>(dst + r * ld + x) = *reinterpret_cast<const u32x4*>(src + r * cols + x);
     }
@@ -506,9 +507,10 @@ union alignas(16) GradLds {
 };
 
 // fp32 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
+template <int NTH = NT>
 __device__ __forceinline__ void stage_f32(const float* src, int rows, bf16_t* rm, int ld,
                                           bf16_t* tr, int ldt) {
-    for (int u = threadIdx.x; u < rows * (D / 4); u += NT) {
+    for (int u = threadIdx.x; u < rows * (D / 4); u += NTH) {
         const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (src) x = *reinterpret_cast<const f32x4*>(src + r * D + c0);
@@ -521,9 +523,10 @@ __device__ __forceinline__ void stage_f32(const float* src, int rows, bf16_t* rm
 }
 
 // bf16 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
+template <int NTH = NT>
 __device__ __forceinline__ void stage_bf16(const bf16_t* src, int rows, bf16_t* rm, int ld,
                                            bf16_t* tr, int ldt) {
-    for (int u = threadIdx.x; u < rows * (D / 4); u += NT) {
+    for (int u = threadIdx.x; u < rows * (D / 4); u += NTH) {
         const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         const u32x2 w = *reinterpret_cast<const u32x2*>(src + r * D + c0);
         if (rm) *reinterpret_cast<u32x2*>(rm + r * ld + c0) = w;
@@ -537,14 +540,14 @@ __device__ __forceinline__ void stage_bf16(const bf16_t* src, int rows, bf16_t* 
 }
 
 // this wave's tiles of a (4 x NTL)-tile product, in a fixed order: tile x
-// is t = wave + 4 x (row block t / NTL, column block t % NTL)
-template <int NTL, int K, int NX>
+// is t = wave + W x for W waves (row block t / NTL, column block t % NTL)
+template <int NTL, int K, int NX, int NTH = NT>
 __device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
                                         f32x4 (&out)[NX]) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
-        const int t = wave + 4 * x, mi = t / NTL, ni = t % NTL;
+        const int t = wave + (NTH / 64) * x, mi = t / NTL, ni = t % NTL;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         out[x] = tile_mm<K>(a + 16 * mi * lda, lda, bt + 16 * ni * ldb, ldb, lane, acc);
     }
@@ -559,8 +562,10 @@ __device__ __forceinline__ const bf16_t* recorded_state(const ChunkRef& c, const
     return sall + (idx * H + c.h) * kState;
 }
 
+constexpr int GT = 512;   // threads of the gradient kernel: 8 waves, 2 per SIMD
+
 template <typename T, int GATE>
-__global__ __launch_bounds__(NT)
+__global__ __launch_bounds__(GT)
 void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dsblk,
                      const bf16_t* __restrict__ deblk, const bf16_t* __restrict__ sall,
                      const float* __restrict__ h0, const T* __restrict__ q,
@@ -570,8 +575,9 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                      T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
                      float* __restrict__ dla, float* __restrict__ dbeta)
 {
+    constexpr int W = GT / 64;                 // waves
     __shared__ GradLds sm_u;
-    __shared__ float s_dgam[D], s_dbT[C];      // phase A -> phase B
+    __shared__ float s_dgam[D], s_dbT[2][C];   // phase A -> phase B
     ChunkRef c;
     if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
@@ -583,41 +589,42 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     const bf16_t* dSp = dsblk + c.slot * kState;
     const bf16_t* dE = deblk + c.slot * (static_cast<int64_t>(C) * D);
 
-    f32x4 rKgW[8], rQgS[8], rKd[8];   // [C][D] terms, tiles t = wave + 4x of 4 x 8
-    f32x4 rT[4], rP[4];               // [C][C] terms, tiles t = wave + 4x of 4 x 4
+    // tiles kept in registers: tile x of this wave is t = wave + 8x
+    f32x4 rKgW[4], rQgS[4], rKd[4];   // [C][D] terms, 4 x 8 tiles (row block x, column block wave)
+    f32x4 rT[2], rP[2];               // [C][C] terms, 4 x 4 tiles
     // =========================== phase A ===========================
     {
         GradALds& sm = sm_u.a;
         // ---- one round of loads: S (both layouts), Kg, V, beta, Minv (both
         //      layouts), dE; dO into registers until its LDS region frees
-        u32x4 pdo[4];
+        u32x4 pdo[2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int u = x * NT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
+        for (int x = 0; x < 2; ++x) {
+            const int u = x * GT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
             pdo[x] = u32x4{0u, 0u, 0u, 0u};
             if (r < c.len)
                 pdo[x] = *reinterpret_cast<const u32x4*>(dO + ((c.t0 + r) * H + c.h) * D + c8);
         }
-        if (c.j == 0) stage_f32(S0f, D, sm.s0, LDD, sm.s0t, LDD);
-        else stage_bf16(recorded_state(c, sall, cu, H), D, sm.s0t, LDD, sm.s0, LDD);   // S^T rows
-        copy_rows(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
-        for (int u = tid; u < C * (D / 4); u += NT) {
+        if (c.j == 0) stage_f32<GT>(S0f, D, sm.s0, LDD, sm.s0t, LDD);
+        else stage_bf16<GT>(recorded_state(c, sall, cu, H), D, sm.s0t, LDD, sm.s0, LDD);   // S^T rows
+        copy_rows<GT>(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
+        for (int u = tid; u < C * (D / 4); u += GT) {
             const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
             if (r < c.len) x = elem<T>::load4(v + ((c.t0 + r) * H + c.h) * D + c0);
             put4t(sm.r + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
         }
         if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
-        for (int u = tid; u < C * C; u += NT) {
+        for (int u = tid; u < C * C; u += GT) {
             const int r = u / C, s2 = u % C;
             const bf16_t x = bf(mvg[u]);
             sm.mv[r * LDC + s2] = x;
             sm.mvt[s2 * LDC + r] = x;
         }
-        stage_bf16(dE, C, sm.de, LDD, nullptr, 0);
+        stage_bf16<GT>(dE, C, sm.de, LDD, nullptr, 0);
         __syncthreads();
         // ---- R = V - Kg S, and (Diag(beta) R)^T
-        mm<4, 8, D>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, D, GT>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
             const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
             f32x4 br;
 #pragma unroll
@@ -633,17 +640,17 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         // ---- E = Minv (Diag(beta) R) over Kg; dS' over S^T, with dgamma =
         //      rowsum(dS' . S) from the bf16 records, summed in fp32
         bf16_t* E = sm.kg;
-        mm<4, 8, C>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, C, GT>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
         });
         bf16_t* dsl = sm.s0t;
         {
-            const int row = tid >> 1, half = tid & 1;
+            const int row = tid >> 2, quarter = tid & 3;
             float part = 0.f;
-#pragma unroll 4
-            for (int x = 0; x < D / 2; x += 4) {
-                const int col = 64 * half + x;
+#pragma unroll
+            for (int x = 0; x < D / 4; x += 4) {
+                const int col = 32 * quarter + x;
                 const u32x2 dw = *reinterpret_cast<const u32x2*>(dSp + row * D + col);
                 const u32x2 sw = *reinterpret_cast<const u32x2*>(sm.s0 + row * LDD + col);
                 part += lo_bf(dw[0]) * lo_bf(sw[0]) + hi_bf(dw[0]) * hi_bf(sw[0]) +
@@ -651,12 +658,13 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 *reinterpret_cast<u32x2*>(dsl + row * LDD + col) = dw;
             }
             part += __shfl_xor(part, 1);
-            if (half == 0) s_dgam[row] = part;
+            part += __shfl_xor(part, 2);
+            if (quarter == 0) s_dgam[row] = part;
         }
         __syncthreads();
         // ---- dE^T (over (Diag(beta) R)^T, now free) from dE in LDS
         bf16_t* det = sm.brt;
-        for (int u = tid; u < C * (D / 4); u += NT) {
+        for (int u = tid; u < C * (D / 4); u += GT) {
             const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
             const u32x2 w = *reinterpret_cast<const u32x2*>(sm.de + r * LDD + c0);
             det[(c0 + 0) * LDC + r] = static_cast<bf16_t>(w[0] & 0xffffu);
@@ -664,23 +672,26 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             det[(c0 + 2) * LDC + r] = static_cast<bf16_t>(w[1] & 0xffffu);
             det[(c0 + 3) * LDC + r] = static_cast<bf16_t>(w[1] >> 16);
         }
-        // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT)
-        mm_regs<4, D>(sm.de, LDD, sm.r, LDD, rT);
-        {   // wave w holds column block w of dT, row blocks x = 0..3
-            const int s2 = 16 * wave + ln;
+        // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT): wave w holds
+        //      column block w % 4 of dT, row blocks w / 4 and w / 4 + 2
+        mm_regs<4, D, 2, GT>(sm.de, LDD, sm.r, LDD, rT);
+        {
+            const int s2 = 16 * (wave % 4) + ln;
             float part = 0.f;
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 2; ++x) {
+                const int mi = (wave + W * x) / 4;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part += mvg[(16 * x + 4 * g4 + i) * C + s2] * rT[x][i];
+                for (int i = 0; i < 4; ++i) part += mvg[(16 * mi + 4 * g4 + i) * C + s2] * rT[x][i];
+            }
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
-            if (g4 == 0) s_dbT[s2] = part;
+            if (g4 == 0) s_dbT[wave / 4][s2] = part;
         }
         __syncthreads();
         // ---- dV = T^T dE = Diag(beta) Minv^T dE (over R)
         bf16_t* dV = sm.r;
-        mm<4, 8, C>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, C, GT>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s2 = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
@@ -693,38 +704,40 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         // ---- dO (over dE^T); dKg_W = -dV S^T, dQg_S = scale dO S^T (kept)
         bf16_t* dOl = sm.brt;
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int u = x * NT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
+        for (int x = 0; x < 2; ++x) {
+            const int u = x * GT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
             *reinterpret_cast<u32x4*>(dOl + r * LDD + c8) = pdo[x];
         }
         __syncthreads();
-        mm_regs<8, D>(dV, LDD, sm.s0, LDD, rKgW);
-        mm_regs<8, D>(dOl, LDD, sm.s0, LDD, rQgS);
+        mm_regs<8, D, 4, GT>(dV, LDD, sm.s0, LDD, rKgW);
+        mm_regs<8, D, 4, GT>(dOl, LDD, sm.s0, LDD, rQgS);
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
+        for (int x = 0; x < 4; ++x) {
             rKgW[x] = -rKgW[x];
             rQgS[x] = scale * rQgS[x];
         }
         // ---- dKd = E dS'^T, dP = lower(scale dO E^T) (kept)
-        mm_regs<8, D>(E, LDD, dsl, LDD, rKd);
-        mm_regs<4, D>(dOl, LDD, E, LDD, rP);
+        mm_regs<8, D, 4, GT>(E, LDD, dsl, LDD, rKd);
+        mm_regs<4, D, 2, GT>(dOl, LDD, E, LDD, rP);
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < 2; ++x) {
+            const int t = wave + W * x, mi = t / 4, ni = t % 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * x + 4 * g4 + i, s2 = 16 * wave + ln;
+                const int r = 16 * mi + 4 * g4 + i, s2 = 16 * ni + ln;
                 rP[x][i] = s2 <= r ? scale * rP[x][i] : 0.f;
             }
+        }
         __syncthreads();   // phase B reuses the LDS
     }
     // =========================== phase B ===========================
     GradBLds& sm = sm_u.b;
     // k and q of the chunk into registers while the gates load and scan,
     // and Minv into LDS: one round of loads
-    float4 kr4[8], qr4[8];
+    float4 kr4[4], qr4[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int u = x * NT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+    for (int x = 0; x < 4; ++x) {
+        const int u = x * GT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         kr4[x] = qr4[x] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (r < c.len) {
             const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
@@ -732,18 +745,18 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             qr4[x] = elem<T>::load4(q + row);
         }
     }
-    for (int u = tid; u < C * C; u += NT) {
+    for (int u = tid; u < C * C; u += GT) {
         const int r = u / C, s2 = u % C;
         const bf16_t x = bf(mvg[u]);
         sm.ra[0][r * LDC + s2] = x;
         sm.ra[1][s2 * LDC + r] = x;
     }
-    load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
+    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs);
     __syncthreads();
     // gated keys and queries, transposed (B operands)
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int u = x * NT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
+    for (int x = 0; x < 4; ++x) {
+        const int u = x * GT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         const float kk[4] = {kr4[x].x, kr4[x].y, kr4[x].z, kr4[x].w};
         const float qq[4] = {qr4[x].x, qr4[x].y, qr4[x].z, qr4[x].w};
 #pragma unroll
@@ -755,20 +768,21 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             sm.qgt[(c0 + e) * LDC + r] = bf(qq[e] * eg);
         }
     }
-    {   // Y^T[s][i] = dT[i][s] beta_s from this wave's dT tiles (column block = wave)
-        const int s2 = 16 * wave + ln;
+    // Y^T[s][i] = dT[i][s] beta_s from this wave's dT tiles
 #pragma unroll
-        for (int x = 0; x < 4; ++x) put4t(sm.rb[0] + s2 * LDC + 16 * x + 4 * g4, sm.bs[s2] * rT[x]);
+    for (int x = 0; x < 2; ++x) {
+        const int t = wave + W * x, mi = t / 4, ni = t % 4, s2 = 16 * ni + ln;
+        put4t(sm.rb[0] + s2 * LDC + 16 * mi + 4 * g4, sm.bs[s2] * rT[x]);
     }
     if (tid < C) {
-        sm.db[tid] = s_dbT[tid];
-    } else if (tid >= NT - D) {
-        const int ch = tid - (NT - D);
+        sm.db[tid] = s_dbT[0][tid] + s_dbT[1][tid];
+    } else if (tid >= GT - D) {
+        const int ch = tid - (GT - D);
         sm.dG[ch] = s_dgam[ch] * gate_exp(sm.g[(c.len - 1) * D + ch]);
     }
     __syncthreads();
     // Z = Minv^T (dT Diag(beta))
-    mm<4, 4, C>(sm.ra[1], LDC, sm.rb[0], LDC, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 4, C, GT>(sm.ra[1], LDC, sm.rb[0], LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.rb[1][(16 * mi + 4 * g4 + i) * LDC + 16 * ni + ln] = bf(acc[i]);
     });
@@ -776,12 +790,12 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // dA = -strict_lower(Z Minv^T): held in registers until every wave is
     // done reading Z and Minv
     {
-        f32x4 dA[4];
-        mm_regs<4, C>(sm.rb[1], LDC, sm.ra[0], LDC, dA);
+        f32x4 dA[2];
+        mm_regs<4, C, 2, GT>(sm.rb[1], LDC, sm.ra[0], LDC, dA);
         __syncthreads();
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            const int t = wave + 4 * x, mi = t / 4, ni = t % 4;
+        for (int x = 0; x < 2; ++x) {
+            const int t = wave + W * x, mi = t / 4, ni = t % 4;
             const int r0 = 16 * mi + 4 * g4, s2 = 16 * ni + ln;
             f32x4 db;
             float rowpart[4];
@@ -802,21 +816,22 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 if (ln == 0) sm.dbp[ni][r0 + i] = pp;
             }
         }
-        // dP and dP^T over Minv, from this wave's dP tiles (column block = wave)
-        const int s2 = 16 * wave + ln;
+        // dP and dP^T over Minv, from this wave's dP tiles
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int x = 0; x < 2; ++x) {
+            const int t = wave + W * x, mi = t / 4, ni = t % 4, s2 = 16 * ni + ln;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm.ra[0][(16 * x + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
-            put4t(sm.ra[1] + s2 * LDC + 16 * x + 4 * g4, rP[x]);
+            for (int i = 0; i < 4; ++i) sm.ra[0][(16 * mi + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
+            put4t(sm.ra[1] + s2 * LDC + 16 * mi + 4 * g4, rP[x]);
         }
     }
     __syncthreads();
     // per 16x16 tile of (row r, key channel c): dKg = dKg_W + dB Kn,
-    // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain
+    // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain;
+    // wave w owns channel block w (tiles t = w + 8x: row block x)
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-        const int t = wave + 4 * x, mi = t / 8, ni = t % 8;
+    for (int x = 0; x < 4; ++x) {
+        const int mi = x, ni = wave;
         const int ch = 16 * ni + ln;
         float kv[4], qv[4];
 #pragma unroll
@@ -856,8 +871,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         }
         dGp += __shfl_xor(dGp, 16);
         dGp += __shfl_xor(dGp, 32);
-        // the tiles of one channel block all belong to this wave (t = 8 mi
-        // + ni, wave = ni mod 4), so these adds happen in a fixed order
+        // channel block ni belongs to this wave alone: the adds come in a fixed order
         if (g4 == 0) atomicAdd(&sm.dG[ch], dGp);
     }
     __syncthreads();
@@ -870,8 +884,8 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             else sm.g[r * D + tid] = run;
         }
     }
-    if (tid >= NT - C) {
-        const int r = tid - (NT - C);
+    if (tid >= GT - C) {
+        const int r = tid - (GT - C);
         if (r < c.len)
             dbeta[(c.t0 + r) * H + c.h] = sm.db[r] + ((sm.dbp[0][r] + sm.dbp[1][r]) +
                                                       (sm.dbp[2][r] + sm.dbp[3][r]));
@@ -989,7 +1003,7 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
         auto gk = a.gate == kGateChannel ? bwd_grad_kernel<bf16_t, kGateChannel>
                 : a.gate == kGateHead    ? bwd_grad_kernel<bf16_t, kGateHead>
                                          : bwd_grad_kernel<bf16_t, kGateNone>;
-        hipLaunchKernelGGL(gk, dim3(chunks), dim3(NT), 0, stream, slots, dsblk, deblk, sall, a.h0,
+        hipLaunchKernelGGL(gk, dim3(chunks), dim3(GT), 0, stream, slots, dsblk, deblk, sall, a.h0,
                            q, k, v, dO, a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo, L_b, a.scale,
                            static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
                            static_cast<bf16_t*>(a.dv), a.dlog_alpha, a.dbeta);
