@@ -53,7 +53,8 @@ namespace {
 
 constexpr int C = 64;          // chunk rows
 constexpr int D = 128;         // d_k = d_v
-constexpr int NT = 256;        // threads of the chunk kernels (4 waves)
+constexpr int NT = 256;        // threads of the carry (4 waves)
+constexpr int GT = 512;        // threads of the chunk-parallel kernels: 8 waves, 2 per SIMD
 constexpr int LDD = D + 8;     // padded LDS row of a [.][D] bf16 matrix
 constexpr int LDC = C + 8;     // padded LDS row of a [.][C] bf16 matrix
 constexpr int kCarryTile = 64; // value columns per carry work-group
@@ -108,7 +109,7 @@ __device__ __forceinline__ f32x4 tile_mm(const bf16_t* a, int lda, const bf16_t*
     return acc;
 }
 
-// all 16x16 tiles (mi < MT, ni < NT_) of A B, spread over the 4 waves;
+// all 16x16 tiles (mi < MT, ni < NTL) of A B, spread over the NTH / 64 waves;
 // fn(mi, ni, acc) consumes each (acc[i] = row 16 mi + 4g + i, column 16 ni + ln)
 template <int MT, int NTL, int K, int NTH = NT, typename Fn>
 __device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
@@ -177,7 +178,7 @@ struct alignas(16) PrepLds {
 };
 
 template <int GATE>
-__global__ __launch_bounds__(NT)
+__global__ __launch_bounds__(GT)
 void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const float* __restrict__ la, const float* __restrict__ beta,
                      const int32_t* __restrict__ cu, int H, int c_lo, int L_b, float scale,
@@ -198,10 +199,10 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     float* oB = reinterpret_cast<float*>(out + kOffB);
     float* oGam = reinterpret_cast<float*>(out + kOffGam);
 
-    load_gates<GATE>(la, beta, c, H, sm.g, sm.bs);
+    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs);
     __syncthreads();
     // gated keys and queries; rows past the chunk are zero
-    for (int idx = tid; idx < C * (D / 4); idx += NT) {
+    for (int idx = tid; idx < C * (D / 4); idx += GT) {
         const int r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
         float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
         if (r < c.len) {
@@ -233,7 +234,7 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     if (tid < D) oGam[tid] = gate_exp(sm.g[(c.len - 1) * D + tid]);
     __syncthreads();
     // B = Kg Kn^T (fp32) and scale P^T, P = lower(Qg Kn^T)
-    mm<4, 4, D>(sm.kg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 4, D, GT>(sm.kg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
@@ -241,7 +242,7 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             oB[r * C + s] = acc[i];
         }
     });
-    mm<4, 4, D>(sm.qg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 4, D, GT>(sm.qg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
         const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
         f32x4 x;
 #pragma unroll
@@ -300,7 +301,7 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         }
         __syncthreads();
     }
-    for (int idx = tid; idx < C * C; idx += NT) {
+    for (int idx = tid; idx < C * C; idx += GT) {
         const int r = idx / C, s = idx % C;
         const float m = sm.mi[r * (C + 1) + s];
         oMinv[idx] = m;
@@ -308,7 +309,7 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     }
     __syncthreads();
     // -W^T, W = T Kg
-    mm<4, 8, C>(sm.tt, LDC, sm.kgt, LDC, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 8, C, GT>(sm.tt, LDC, sm.kgt, LDC, [&](int mi, int ni, f32x4 acc) {
         put4t(oWt + (16 * ni + ln) * C + 16 * mi + 4 * g4, -acc);
     });
 }
@@ -561,8 +562,6 @@ __device__ __forceinline__ const bf16_t* recorded_state(const ChunkRef& c, const
     const int64_t idx = c.n + cu[c.n] / C + (c.j - 1);
     return sall + (idx * H + c.h) * kState;
 }
-
-constexpr int GT = 512;   // threads of the gradient kernel: 8 waves, 2 per SIMD
 
 template <typename T, int GATE>
 __global__ __launch_bounds__(GT)
@@ -991,7 +990,7 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
             auto prep = a.gate == kGateChannel ? bwd_prep_kernel<kGateChannel>
                       : a.gate == kGateHead    ? bwd_prep_kernel<kGateHead>
                                                : bwd_prep_kernel<kGateNone>;
-            hipLaunchKernelGGL(prep, dim3(chunks), dim3(NT), 0, stream, q, k, a.log_alpha, a.beta,
+            hipLaunchKernelGGL(prep, dim3(chunks), dim3(GT), 0, stream, q, k, a.log_alpha, a.beta,
                                a.cu_seqlens, a.H, c_lo, L_b, a.scale, slots);
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
