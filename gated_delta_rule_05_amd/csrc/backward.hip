@@ -53,7 +53,7 @@ namespace {
 
 constexpr int C = 64;          // chunk rows
 constexpr int D = 128;         // d_k = d_v
-constexpr int NT = 256;        // threads of the carry (4 waves)
+constexpr int NT = 256;        // default work-group size of the LDS helpers
 constexpr int GT = 512;        // threads of the chunk-parallel kernels: 8 waves, 2 per SIMD
 constexpr int LDD = D + 8;     // padded LDS row of a [.][D] bf16 matrix
 constexpr int LDC = C + 8;     // padded LDS row of a [.][C] bf16 matrix
@@ -339,7 +339,7 @@ __device__ __forceinline__ void copy_rows(bf16_t* dst, int ld, const bf16_t* src
     }
 }
 
-__global__ __launch_bounds__(NT)
+__global__ __launch_bounds__(GT)
 void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dO,
                       const int32_t* __restrict__ cu, int N, int H, int c_lo, int L_b,
                       float* __restrict__ dstate, bf16_t* __restrict__ dsblk,
@@ -350,74 +350,76 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     const int pair = blockIdx.x / R, tile = blockIdx.x % R;
     const int n = pair / H, h = pair % H;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    // 8 waves: wave w owns value columns 16 (w % 4) .. +15 of the tile and
+    // key rows 64 (w / 4) .. +63 of the state
+    const int slab = wave % 4, half = wave / 4;
     const int64_t t_begin = cu[n], t_end = cu[n + 1];
     const int nch = static_cast<int>((t_end - t_begin + C - 1) / C);
     const int hi = min(nch, c_lo + L_b) - 1;          // last chunk of this block
-    const int jc = tile * kCarryTile + 16 * wave + ln; // this lane's value column
+    const int jc = tile * kCarryTile + 16 * slab + ln; // this lane's value column
+    const int rb = 64 * half;                          // this wave's first key row
     float* st = dstate + (static_cast<int64_t>(n) * H + h) * kState;
     if (hi < c_lo) {
         // no chunk here; an empty sequence still gets dh0 = dhT (or zeros)
         if (c_lo == 0 && dh0) {
             float* d0 = dh0 + (static_cast<int64_t>(n) * H + h) * kState;
-            for (int e = tid; e < D * kCarryTile; e += NT) {
+            for (int e = tid; e < D * kCarryTile; e += GT) {
                 const int row = e / kCarryTile, col = tile * kCarryTile + e % kCarryTile;
                 d0[row * D + col] = st[row * D + col];
             }
         }
         return;
     }
-    // dS slab: S[m][i] = dS[16m + 4g + i][jc]
-    f32x4 S[8];
+    // dS slab: S[m][i] = dS[rb + 16m + 4g + i][jc]
+    f32x4 S[4];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) S[m][i] = st[(16 * m + 4 * g4 + i) * D + jc];
+        for (int i = 0; i < 4; ++i) S[m][i] = st[(rb + 16 * m + 4 * g4 + i) * D + jc];
 
     // The next chunk's operands load into registers while this chunk
-    // computes.  Kd, P^T, Qg^T and W^T are 3584 16-byte units: 14 per
-    // thread, and with 256 threads unit x * 256 + tid falls in one matrix
-    // for every thread (Kd: x < 4; P^T: x < 6; Qg^T: x < 10; W^T: x < 14).
-    constexpr int PER = (C * D + C * C + 2 * D * C) / 8 / NT;
-    static_assert(PER * NT * 8 == C * D + C * C + 2 * D * C, "whole rounds");
-    u32x4 pre[PER], pdo[2];
+    // computes.  Kd, P^T, Qg^T and W^T are 3584 16-byte units: 7 per
+    // thread, and with 512 threads unit x * 512 + tid falls in one matrix
+    // for every thread (Kd: x < 2; P^T: x = 2; Qg^T: x < 5; W^T: x < 7).
+    constexpr int PER = (C * D + C * C + 2 * D * C) / 8 / GT;
+    static_assert(PER * GT * 8 == C * D + C * C + 2 * D * C, "whole rounds");
+    static_assert(GT == 512, "the unit-to-matrix map below assumes 512 threads");
+    u32x4 pre[PER], pdo;
     float pgam = 0.f;
     auto fetch = [&](int j) {
         const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
         const uint8_t* sp = slots + slot * static_cast<int64_t>(kSlot);
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int u = x * NT + tid;
-            const int byte = x < 4 ? 16 * u : kOffPt + 16 * (u - 4 * NT);
+            const int u = x * GT + tid;
+            const int byte = x < 2 ? 16 * u : kOffPt + 16 * (u - 2 * GT);
             pre[x] = *reinterpret_cast<const u32x4*>(sp + byte);
         }
         if (tid < D) pgam = reinterpret_cast<const float*>(sp + kOffGam)[tid];
         const int64_t t0 = t_begin + static_cast<int64_t>(j) * C;
         const int len = static_cast<int>(min<int64_t>(C, t_end - t0));
-        const int r = tid >> 2, part = tid & 3;
-        const bf16_t* src = dO + ((t0 + min(r, len - 1)) * H + h) * D + tile * kCarryTile + 16 * part;
-        pdo[0] = *reinterpret_cast<const u32x4*>(src);
-        pdo[1] = *reinterpret_cast<const u32x4*>(src + 8);
-        if (r >= len) pdo[0] = pdo[1] = u32x4{0u, 0u, 0u, 0u};
+        const int r = tid >> 3, part = tid & 7;
+        pdo = *reinterpret_cast<const u32x4*>(dO + ((t0 + min(r, len - 1)) * H + h) * D +
+                                              tile * kCarryTile + 8 * part);
+        if (r >= len) pdo = u32x4{0u, 0u, 0u, 0u};
     };
     auto put = [&]() {
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int u = x * NT + tid;
+            const int u = x * GT + tid;
             bf16_t* dst;
-            if (x < 4) dst = sm.kd + (u / 16) * LDD + (u % 16) * 8;
-            else if (x < 6) { const int w = u - 4 * NT; dst = sm.pt + (w / 8) * LDC + (w % 8) * 8; }
-            else if (x < 10) { const int w = u - 6 * NT; dst = sm.qt + (w / 8) * LDC + (w % 8) * 8; }
-            else { const int w = u - 10 * NT; dst = sm.wt + (w / 8) * LDC + (w % 8) * 8; }
+            if (x < 2) dst = sm.kd + (u / 16) * LDD + (u % 16) * 8;
+            else if (x < 3) { const int w = u - 2 * GT; dst = sm.pt + (w / 8) * LDC + (w % 8) * 8; }
+            else if (x < 5) { const int w = u - 3 * GT; dst = sm.qt + (w / 8) * LDC + (w % 8) * 8; }
+            else { const int w = u - 5 * GT; dst = sm.wt + (w / 8) * LDC + (w % 8) * 8; }
             *reinterpret_cast<u32x4*>(dst) = pre[x];
         }
         if (tid < D) sm.gam[tid] = pgam;
-        const int r = tid >> 2, part = tid & 3;
-        const uint32_t w[8] = {pdo[0][0], pdo[0][1], pdo[0][2], pdo[0][3],
-                               pdo[1][0], pdo[1][1], pdo[1][2], pdo[1][3]};
+        const int r = tid >> 3, part = tid & 7;
 #pragma unroll
-        for (int x = 0; x < 8; ++x) {
-            sm.dot[(16 * part + 2 * x) * LDC + r] = static_cast<bf16_t>(w[x] & 0xffffu);
-            sm.dot[(16 * part + 2 * x + 1) * LDC + r] = static_cast<bf16_t>(w[x] >> 16);
+        for (int x = 0; x < 4; ++x) {
+            sm.dot[(8 * part + 2 * x) * LDC + r] = static_cast<bf16_t>(pdo[x] & 0xffffu);
+            sm.dot[(8 * part + 2 * x + 1) * LDC + r] = static_cast<bf16_t>(pdo[x] >> 16);
         }
     };
 
@@ -428,36 +430,38 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         // dS' of this chunk (bf16, for the grad pass) and as a bf16 B operand
         bf16_t* dsp = dsblk + slot * kState;
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 4; ++m) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dsp[(16 * m + 4 * g4 + i) * D + jc] = bf(S[m][i]);
-            put4t(&sm.dst[wave][ln * LDD + 16 * m + 4 * g4], S[m]);
+            for (int i = 0; i < 4; ++i) dsp[(rb + 16 * m + 4 * g4 + i) * D + jc] = bf(S[m][i]);
+            put4t(&sm.dst[slab][ln * LDD + rb + 16 * m + 4 * g4], S[m]);
         }
         __syncthreads();
         if (j > c_lo) fetch(j - 1);
-        // dE = Kd dS' + scale P^T dO  (this wave's 16 columns, 4 row tiles)
+        // dE = Kd dS' + scale P^T dO  (this slab's 16 columns, row tiles 2 half, 2 half + 1)
         bf16_t* dep = deblk + slot * (static_cast<int64_t>(C) * D);
-        const bf16_t* dsw = sm.dst[wave];
-        const bf16_t* dow = sm.dot + 16 * wave * LDC;
+        const bf16_t* dsw = sm.dst[slab];
+        const bf16_t* dow = sm.dot + 16 * slab * LDC;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int mm2 = 0; mm2 < 2; ++mm2) {
+            const int m = 2 * half + mm2;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = tile_mm<D>(sm.kd + 16 * m * LDD, LDD, dsw, LDD, lane, acc);
             acc = tile_mm<C>(sm.pt + 16 * m * LDC, LDC, dow, LDC, lane, acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dep[(16 * m + 4 * g4 + i) * D + jc] = bf(acc[i]);
-            put4t(&sm.det[wave][ln * LDC + 16 * m + 4 * g4], acc);
+            put4t(&sm.det[slab][ln * LDC + 16 * m + 4 * g4], acc);
         }
         __syncthreads();
-        // dS = Diag(gamma) dS' + scale Qg^T dO - W^T dE
-        const bf16_t* dew = sm.det[wave];
+        // dS = Diag(gamma) dS' + scale Qg^T dO - W^T dE  (this wave's key rows)
+        const bf16_t* dew = sm.det[slab];
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
+        for (int m = 0; m < 4; ++m) {
+            const int mb = 4 * half + m;
             f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * m + 4 * g4 + i] * S[m][i];
-            acc = tile_mm<C>(sm.qt + 16 * m * LDC, LDC, dow, LDC, lane, acc);
-            acc = tile_mm<C>(sm.wt + 16 * m * LDC, LDC, dew, LDC, lane, acc);
+            for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * mb + 4 * g4 + i] * S[m][i];
+            acc = tile_mm<C>(sm.qt + 16 * mb * LDC, LDC, dow, LDC, lane, acc);
+            acc = tile_mm<C>(sm.wt + 16 * mb * LDC, LDC, dew, LDC, lane, acc);
             S[m] = acc;
         }
         __syncthreads();
@@ -466,9 +470,9 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     if (dst_out) {
         dst_out += c_lo == 0 ? (static_cast<int64_t>(n) * H + h) * kState : 0;
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst_out[(16 * m + 4 * g4 + i) * D + jc] = S[m][i];
+            for (int i = 0; i < 4; ++i) dst_out[(rb + 16 * m + 4 * g4 + i) * D + jc] = S[m][i];
     }
 }
 
@@ -995,7 +999,7 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
             if ((e = hipGetLastError()) != hipSuccess) return e;
         }
         hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>(a.N * a.H * (D / kCarryTile))),
-                           dim3(NT), 0, stream, slots, dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
+                           dim3(GT), 0, stream, slots, dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
                            dstate, dsblk, deblk, a.dh0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if (a.total_T == 0) continue;
