@@ -93,32 +93,48 @@ __device__ __forceinline__ bool chunk_of(int64_t b, int H, int c_lo, int L_b,
     return c.len > 0;
 }
 
-// acc(16x16 tile) of A (M x K, row m at a + m * lda, K contiguous) times B,
-// B given as Bt (N x K, row n at bt + n * ldb): lane (g, ln) reads
-// A[m0 + ln][8g..8g+7] and Bt[n0 + ln][8g..8g+7] per 32-deep step.
-template <int K>
-__device__ __forceinline__ f32x4 tile_mm(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
+// Operand storage in LDS.  kKc: one row per M (or N) index with K
+// contiguous -- lane (g, ln) reads row ln, K indices 8g .. 8g+7 (one 16-byte
+// read).  kMc: one row per K index with M (or N) contiguous -- the same
+// fragment by two transpose reads (frag_tr).
+constexpr int kKc = 0, kMc = 1;
+
+// tile i (16 rows or columns) of an operand stored with layout L
+template <int L>
+__device__ __forceinline__ const bf16_t* tile_at(const bf16_t* x, int ld, int i) {
+    return L == kKc ? x + 16 * i * ld : x + 16 * i;
+}
+template <int L>
+__device__ __forceinline__ u32x4 frag(const bf16_t* x, int ld, int kk, int lane) {
+    if constexpr (L == kKc)
+        return *reinterpret_cast<const u32x4*>(x + (lane & 15) * ld + 8 * (lane >> 4) + kk);
+    else
+        return frag_tr(x + kk * ld, ld, lane);
+}
+
+// acc(16x16 tile) of A (M x K) times B (K x N), a and b pointing at the
+// tile (tile_at), A stored with layout AL and B with layout BL; the kKc
+// form of B is B^T (N x K, row n at b + n * ldb).
+template <int K, int AL = kKc, int BL = kKc>
+__device__ __forceinline__ f32x4 tile_mm(const bf16_t* a, int lda, const bf16_t* b, int ldb,
                                          int lane, f32x4 acc) {
-    const int g = lane >> 4, ln = lane & 15;
-    const bf16_t* ap = a + ln * lda + 8 * g;
-    const bf16_t* bp = bt + ln * ldb + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < K; kk += 32)
-        acc = mma32(*reinterpret_cast<const u32x4*>(ap + kk),
-                    *reinterpret_cast<const u32x4*>(bp + kk), acc);
+        acc = mma32(frag<AL>(a, lda, kk, lane), frag<BL>(b, ldb, kk, lane), acc);
     return acc;
 }
 
 // all 16x16 tiles (mi < MT, ni < NTL) of A B, spread over the NTH / 64 waves;
 // fn(mi, ni, acc) consumes each (acc[i] = row 16 mi + 4g + i, column 16 ni + ln)
-template <int MT, int NTL, int K, int NTH = NT, typename Fn>
-__device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
+template <int MT, int NTL, int K, int NTH = NT, int AL = kKc, int BL = kKc, typename Fn>
+__device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* b, int ldb,
                                    Fn&& fn) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     for (int t = wave; t < MT * NTL; t += NTH / 64) {
         const int mi = t / NTL, ni = t - mi * NTL;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_mm<K>(a + 16 * mi * lda, lda, bt + 16 * ni * ldb, ldb, lane, acc);
+        acc = tile_mm<K, AL, BL>(tile_at<AL>(a, lda, mi), lda, tile_at<BL>(b, ldb, ni), ldb,
+                                 lane, acc);
         fn(mi, ni, acc);
     }
 }
@@ -482,25 +498,32 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
 // registers (dKg_W, dQg_S, dKd, dT, dP: each wave keeps the 16x16 tiles it
 // computed, and phase B hands the same tiles to the same waves); phase B
 // then solves the triangular-system and gate terms and writes dq, dk,
-// dlog_alpha and dbeta.  The two phases share the LDS.
+// dlog_alpha and dbeta.  The two phases share the LDS.  Every matrix is
+// staged once, in the layout it arrives in; a product that contracts over
+// the contiguous index of an operand reads it with 16-byte reads, one that
+// contracts over its rows with transpose reads (kMc).
 // ===================================================================
+constexpr int LDT = D + 16;    // rows read only by transpose reads: a row step of 8 banks
+
 struct alignas(16) GradALds {
-    bf16_t s0[D * LDD];        // S (row c, columns j)
-    bf16_t s0t[D * LDD];       // S^T; later dS'
+    bf16_t st[D * LDD];        // S^T [value j][key c] (the recorded layout)
+    bf16_t dsl[D * LDD];       // dS' [key c][value j]
     bf16_t kg[C * LDD];        // Kg; later E
     bf16_t r[C * LDD];         // V, then R; later dV
-    bf16_t brt[D * LDC];       // (Diag(beta) R)^T; later dE^T; later dO
-    bf16_t mv[C * LDC];        // Minv
-    bf16_t mvt[C * LDC];       // Minv^T
     bf16_t de[C * LDD];        // dE
+    bf16_t dol[C * LDD];       // dO
+    bf16_t mvb[C * LDC];       // Minv Diag(beta)
     float bs[C];
+    float dgp[4][D];           // dgamma over four quarters of the value columns
 };
 struct alignas(16) GradBLds {
     float g[C * D];            // cumulative gates; later dlog_alpha rows (head gate)
     float dg[C * D];
-    bf16_t knt[D * LDC], kgt[D * LDC], qgt[D * LDC];
-    bf16_t ra[2][C * LDC];     // Minv, Minv^T; later dP, dP^T
-    bf16_t rb[2][C * LDC];     // (dT Diag(beta))^T, Z; later dB, dB^T
+    bf16_t kg[C * LDT], kn[C * LDT], qg[C * LDT];   // gated keys and queries, row-major
+    bf16_t mv[C * LDC];        // Minv
+    bf16_t dp[C * LDC];        // dP
+    bf16_t yt[C * LDC];        // (dT Diag(beta))^T; later dB
+    bf16_t z[C * LDC];         // Z = Minv^T dT Diag(beta)
     float bs[C];
     float db[C];               // dbeta
     float dbp[4][C];           // dbeta_A per 16-column block, summed in order
@@ -511,50 +534,30 @@ union alignas(16) GradLds {
     GradBLds b;
 };
 
-// fp32 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
+// fp32 [rows][D] global (null = zeros) -> bf16 LDS, transposed (row = column index)
 template <int NTH = NT>
-__device__ __forceinline__ void stage_f32(const float* src, int rows, bf16_t* rm, int ld,
-                                          bf16_t* tr, int ldt) {
+__device__ __forceinline__ void stage_f32_t(const float* src, int rows, bf16_t* tr, int ldt) {
     for (int u = threadIdx.x; u < rows * (D / 4); u += NTH) {
         const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (src) x = *reinterpret_cast<const f32x4*>(src + r * D + c0);
-        if (rm) put4t(rm + r * ld + c0, x);
-        if (tr) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tr[(c0 + e) * ldt + r] = bf(x[e]);
-        }
-    }
-}
-
-// bf16 [rows][D] global -> bf16 LDS, row-major (ld) and/or transposed (ldt)
-template <int NTH = NT>
-__device__ __forceinline__ void stage_bf16(const bf16_t* src, int rows, bf16_t* rm, int ld,
-                                           bf16_t* tr, int ldt) {
-    for (int u = threadIdx.x; u < rows * (D / 4); u += NTH) {
-        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        const u32x2 w = *reinterpret_cast<const u32x2*>(src + r * D + c0);
-        if (rm) *reinterpret_cast<u32x2*>(rm + r * ld + c0) = w;
-        if (tr) {
-            tr[(c0 + 0) * ldt + r] = static_cast<bf16_t>(w[0] & 0xffffu);
-            tr[(c0 + 1) * ldt + r] = static_cast<bf16_t>(w[0] >> 16);
-            tr[(c0 + 2) * ldt + r] = static_cast<bf16_t>(w[1] & 0xffffu);
-            tr[(c0 + 3) * ldt + r] = static_cast<bf16_t>(w[1] >> 16);
-        }
+        for (int e = 0; e < 4; ++e) tr[(c0 + e) * ldt + r] = bf(x[e]);
     }
 }
 
 // this wave's tiles of a (4 x NTL)-tile product, in a fixed order: tile x
 // is t = wave + W x for W waves (row block t / NTL, column block t % NTL)
-template <int NTL, int K, int NX, int NTH = NT>
-__device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* bt, int ldb,
+template <int NTL, int K, int NX, int NTH = NT, int AL = kKc, int BL = kKc>
+__device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* b, int ldb,
                                         f32x4 (&out)[NX]) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
     for (int x = 0; x < NX; ++x) {
         const int t = wave + (NTH / 64) * x, mi = t / NTL, ni = t % NTL;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        out[x] = tile_mm<K>(a + 16 * mi * lda, lda, bt + 16 * ni * ldb, ldb, lane, acc);
+        out[x] = tile_mm<K, AL, BL>(tile_at<AL>(a, lda, mi), lda, tile_at<BL>(b, ldb, ni), ldb,
+                                    lane, acc);
     }
 }
 
@@ -589,8 +592,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     const float* Bm = reinterpret_cast<const float*>(sp + kOffB);
     const float* S0f = c.j == 0 && h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState
                                       : nullptr;
-    const bf16_t* dSp = dsblk + c.slot * kState;
-    const bf16_t* dE = deblk + c.slot * (static_cast<int64_t>(C) * D);
 
     // tiles kept in registers: tile x of this wave is t = wave + 8x
     f32x4 rKgW[4], rQgS[4], rKd[4];   // [C][D] terms, 4 x 8 tiles (row block x, column block wave)
@@ -598,19 +599,19 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // =========================== phase A ===========================
     {
         GradALds& sm = sm_u.a;
-        // ---- one round of loads: S (both layouts), Kg, V, beta, Minv (both
-        //      layouts), dE; dO into registers until its LDS region frees
-        u32x4 pdo[2];
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int u = x * GT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
-            pdo[x] = u32x4{0u, 0u, 0u, 0u};
-            if (r < c.len)
-                pdo[x] = *reinterpret_cast<const u32x4*>(dO + ((c.t0 + r) * H + c.h) * D + c8);
-        }
-        if (c.j == 0) stage_f32<GT>(S0f, D, sm.s0, LDD, sm.s0t, LDD);
-        else stage_bf16<GT>(recorded_state(c, sall, cu, H), D, sm.s0t, LDD, sm.s0, LDD);   // S^T rows
+        // ---- one round of loads, each matrix in its own layout: S^T, dS',
+        //      Kg, V, dE, dO, beta, Minv Diag(beta)
+        if (c.j == 0) stage_f32_t<GT>(S0f, D, sm.st, LDD);
+        else copy_rows<GT>(sm.st, LDD, recorded_state(c, sall, cu, H), D, D);
+        copy_rows<GT>(sm.dsl, LDD, dsblk + c.slot * kState, D, D);
         copy_rows<GT>(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
+        copy_rows<GT>(sm.de, LDD, deblk + c.slot * (static_cast<int64_t>(C) * D), C, D);
+        for (int u = tid; u < C * (D / 8); u += GT) {
+            const int r = u / (D / 8), c8 = (u % (D / 8)) * 8;
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (r < c.len) x = *reinterpret_cast<const u32x4*>(dO + ((c.t0 + r) * H + c.h) * D + c8);
+            *reinterpret_cast<u32x4*>(sm.dol + r * LDD + c8) = x;
+        }
         for (int u = tid; u < C * (D / 4); u += GT) {
             const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -618,63 +619,45 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             put4t(sm.r + r * LDD + c0, f32x4{x.x, x.y, x.z, x.w});
         }
         if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
-        for (int u = tid; u < C * C; u += GT) {
-            const int r = u / C, s2 = u % C;
-            const bf16_t x = bf(mvg[u]);
-            sm.mv[r * LDC + s2] = x;
-            sm.mvt[s2 * LDC + r] = x;
-        }
-        stage_bf16<GT>(dE, C, sm.de, LDD, nullptr, 0);
         __syncthreads();
-        // ---- R = V - Kg S, and (Diag(beta) R)^T
-        mm<4, 8, D, GT>(sm.kg, LDD, sm.s0t, LDD, [&](int mi, int ni, f32x4 acc) {
+        for (int u = tid; u < C * (C / 4); u += GT) {
+            const int r = u / (C / 4), s0 = (u % (C / 4)) * 4;
+            const f32x4 m = *reinterpret_cast<const f32x4*>(mvg + r * C + s0);
+            put4t(sm.mvb + r * LDC + s0, f32x4{m[0] * sm.bs[s0], m[1] * sm.bs[s0 + 1],
+                                               m[2] * sm.bs[s0 + 2], m[3] * sm.bs[s0 + 3]});
+        }
+        // ---- R = V - Kg S (B = S^T rows)
+        mm<4, 8, D, GT>(sm.kg, LDD, sm.st, LDD, [&](int mi, int ni, f32x4 acc) {
             const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
-            f32x4 br;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 bf16_t* p = sm.r + (r0 + i) * LDD + col;
-                const float rv = bf16_to_f32(*p) - acc[i];
-                *p = bf(rv);
-                br[i] = sm.bs[r0 + i] * rv;
+                *p = bf(bf16_to_f32(*p) - acc[i]);
             }
-            put4t(sm.brt + col * LDC + r0, br);
         });
+        // ---- dgamma = rowsum(dS' . S) from the bf16 records, summed in fp32:
+        //      thread (quarter, key c) takes value columns 32 quarter .. +31
+        {
+            const int ch = tid & (D - 1), quarter = tid >> 7;
+            float part = 0.f;
+#pragma unroll
+            for (int x = 0; x < 32; x += 8) {
+                const int j0 = 32 * quarter + x;
+                const u32x4 dw = *reinterpret_cast<const u32x4*>(sm.dsl + ch * LDD + j0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part += lo_bf(dw[e]) * bf16_to_f32(sm.st[(j0 + 2 * e) * LDD + ch]) +
+                            hi_bf(dw[e]) * bf16_to_f32(sm.st[(j0 + 2 * e + 1) * LDD + ch]);
+            }
+            sm.dgp[quarter][ch] = part;
+        }
         __syncthreads();
-        // ---- E = Minv (Diag(beta) R) over Kg; dS' over S^T, with dgamma =
-        //      rowsum(dS' . S) from the bf16 records, summed in fp32
+        // ---- E = (Minv Diag(beta)) R over Kg (R read by rows of K)
         bf16_t* E = sm.kg;
-        mm<4, 8, C, GT>(sm.mv, LDC, sm.brt, LDC, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, C, GT, kKc, kMc>(sm.mvb, LDC, sm.r, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
         });
-        bf16_t* dsl = sm.s0t;
-        {
-            const int row = tid >> 2, quarter = tid & 3;
-            float part = 0.f;
-#pragma unroll
-            for (int x = 0; x < D / 4; x += 4) {
-                const int col = 32 * quarter + x;
-                const u32x2 dw = *reinterpret_cast<const u32x2*>(dSp + row * D + col);
-                const u32x2 sw = *reinterpret_cast<const u32x2*>(sm.s0 + row * LDD + col);
-                part += lo_bf(dw[0]) * lo_bf(sw[0]) + hi_bf(dw[0]) * hi_bf(sw[0]) +
-                        lo_bf(dw[1]) * lo_bf(sw[1]) + hi_bf(dw[1]) * hi_bf(sw[1]);
-                *reinterpret_cast<u32x2*>(dsl + row * LDD + col) = dw;
-            }
-            part += __shfl_xor(part, 1);
-            part += __shfl_xor(part, 2);
-            if (quarter == 0) s_dgam[row] = part;
-        }
-        __syncthreads();
-        // ---- dE^T (over (Diag(beta) R)^T, now free) from dE in LDS
-        bf16_t* det = sm.brt;
-        for (int u = tid; u < C * (D / 4); u += GT) {
-            const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-            const u32x2 w = *reinterpret_cast<const u32x2*>(sm.de + r * LDD + c0);
-            det[(c0 + 0) * LDC + r] = static_cast<bf16_t>(w[0] & 0xffffu);
-            det[(c0 + 1) * LDC + r] = static_cast<bf16_t>(w[0] >> 16);
-            det[(c0 + 2) * LDC + r] = static_cast<bf16_t>(w[1] & 0xffffu);
-            det[(c0 + 3) * LDC + r] = static_cast<bf16_t>(w[1] >> 16);
-        }
         // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT): wave w holds
         //      column block w % 4 of dT, row blocks w / 4 and w / 4 + 2
         mm_regs<4, D, 2, GT>(sm.de, LDD, sm.r, LDD, rT);
@@ -691,37 +674,30 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             part += __shfl_xor(part, 32);
             if (g4 == 0) s_dbT[wave / 4][s2] = part;
         }
+        if (tid < D) s_dgam[tid] = (sm.dgp[0][tid] + sm.dgp[1][tid]) + (sm.dgp[2][tid] + sm.dgp[3][tid]);
         __syncthreads();
-        // ---- dV = T^T dE = Diag(beta) Minv^T dE (over R)
+        // ---- dV = T^T dE = (Minv Diag(beta))^T dE (over R; both operands by rows of K)
         bf16_t* dV = sm.r;
-        mm<4, 8, C, GT>(sm.mvt, LDC, det, LDC, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, C, GT, kMc, kMc>(sm.mvb, LDC, sm.de, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s2 = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
-                const float x = sm.bs[s2] * acc[i];
-                dV[s2 * LDD + col] = bf(x);
-                if (s2 < c.len) elem<T>::store(dv + ((c.t0 + s2) * H + c.h) * D + col, x);
+                dV[s2 * LDD + col] = bf(acc[i]);
+                if (s2 < c.len) elem<T>::store(dv + ((c.t0 + s2) * H + c.h) * D + col, acc[i]);
             }
         });
         __syncthreads();
-        // ---- dO (over dE^T); dKg_W = -dV S^T, dQg_S = scale dO S^T (kept)
-        bf16_t* dOl = sm.brt;
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int u = x * GT + tid, r = u / (D / 8), c8 = (u % (D / 8)) * 8;
-            *reinterpret_cast<u32x4*>(dOl + r * LDD + c8) = pdo[x];
-        }
-        __syncthreads();
-        mm_regs<8, D, 4, GT>(dV, LDD, sm.s0, LDD, rKgW);
-        mm_regs<8, D, 4, GT>(dOl, LDD, sm.s0, LDD, rQgS);
+        // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T (kept; S^T read by rows of K)
+        mm_regs<8, D, 4, GT, kKc, kMc>(dV, LDD, sm.st, LDD, rKgW);
+        mm_regs<8, D, 4, GT, kKc, kMc>(sm.dol, LDD, sm.st, LDD, rQgS);
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
             rKgW[x] = -rKgW[x];
             rQgS[x] = scale * rQgS[x];
         }
         // ---- dKd = E dS'^T, dP = lower(scale dO E^T) (kept)
-        mm_regs<8, D, 4, GT>(E, LDD, dsl, LDD, rKd);
-        mm_regs<4, D, 2, GT>(dOl, LDD, E, LDD, rP);
+        mm_regs<8, D, 4, GT>(E, LDD, sm.dsl, LDD, rKd);
+        mm_regs<4, D, 2, GT>(sm.dol, LDD, E, LDD, rP);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int t = wave + W * x, mi = t / 4, ni = t % 4;
@@ -748,34 +724,38 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             qr4[x] = elem<T>::load4(q + row);
         }
     }
-    for (int u = tid; u < C * C; u += GT) {
-        const int r = u / C, s2 = u % C;
-        const bf16_t x = bf(mvg[u]);
-        sm.ra[0][r * LDC + s2] = x;
-        sm.ra[1][s2 * LDC + r] = x;
+    for (int u = tid; u < C * (C / 4); u += GT) {
+        const int r = u / (C / 4), s0 = (u % (C / 4)) * 4;
+        put4t(sm.mv + r * LDC + s0, *reinterpret_cast<const f32x4*>(mvg + r * C + s0));
     }
     load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs);
     __syncthreads();
-    // gated keys and queries, transposed (B operands)
+    // gated keys and queries, row-major
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int u = x * GT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
         const float kk[4] = {kr4[x].x, kr4[x].y, kr4[x].z, kr4[x].w};
         const float qq[4] = {qr4[x].x, qr4[x].y, qr4[x].z, qr4[x].w};
+        const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.g + r * D + c0);
+        f32x4 kg, kn, qg;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float gv = sm.g[r * D + c0 + e];
-            const float eg = gate_exp(gv), en = gate_exp(-gv);
-            sm.kgt[(c0 + e) * LDC + r] = bf(kk[e] * eg);
-            sm.knt[(c0 + e) * LDC + r] = bf(kk[e] * en);
-            sm.qgt[(c0 + e) * LDC + r] = bf(qq[e] * eg);
+            const float eg = gate_exp(gv[e]), en = gate_exp(-gv[e]);
+            kg[e] = kk[e] * eg;
+            kn[e] = kk[e] * en;
+            qg[e] = qq[e] * eg;
         }
+        put4t(sm.kg + r * LDT + c0, kg);
+        put4t(sm.kn + r * LDT + c0, kn);
+        put4t(sm.qg + r * LDT + c0, qg);
     }
-    // Y^T[s][i] = dT[i][s] beta_s from this wave's dT tiles
+    // (dT Diag(beta))^T and dP from this wave's dT and dP tiles
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int t = wave + W * x, mi = t / 4, ni = t % 4, s2 = 16 * ni + ln;
-        put4t(sm.rb[0] + s2 * LDC + 16 * mi + 4 * g4, sm.bs[s2] * rT[x]);
+        put4t(sm.yt + s2 * LDC + 16 * mi + 4 * g4, sm.bs[s2] * rT[x]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.dp[(16 * mi + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
     }
     if (tid < C) {
         sm.db[tid] = s_dbT[0][tid] + s_dbT[1][tid];
@@ -784,33 +764,29 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         sm.dG[ch] = s_dgam[ch] * gate_exp(sm.g[(c.len - 1) * D + ch]);
     }
     __syncthreads();
-    // Z = Minv^T (dT Diag(beta))
-    mm<4, 4, C, GT>(sm.ra[1], LDC, sm.rb[0], LDC, [&](int mi, int ni, f32x4 acc) {
+    // Z = Minv^T (dT Diag(beta))  (Minv read by rows of K)
+    mm<4, 4, C, GT, kMc, kKc>(sm.mv, LDC, sm.yt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.rb[1][(16 * mi + 4 * g4 + i) * LDC + 16 * ni + ln] = bf(acc[i]);
+        for (int i = 0; i < 4; ++i) sm.z[(16 * mi + 4 * g4 + i) * LDC + 16 * ni + ln] = bf(acc[i]);
     });
     __syncthreads();
-    // dA = -strict_lower(Z Minv^T): held in registers until every wave is
-    // done reading Z and Minv
+    // dA = -strict_lower(Z Minv^T); dB = Diag(beta) dA over (dT Diag(beta))^T,
+    // which nothing reads any more
     {
         f32x4 dA[2];
-        mm_regs<4, C, 2, GT>(sm.rb[1], LDC, sm.ra[0], LDC, dA);
-        __syncthreads();
+        mm_regs<4, C, 2, GT>(sm.z, LDC, sm.mv, LDC, dA);
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
             const int t = wave + W * x, mi = t / 4, ni = t % 4;
             const int r0 = 16 * mi + 4 * g4, s2 = 16 * ni + ln;
-            f32x4 db;
             float rowpart[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = r0 + i;
                 const float a = s2 < r ? -dA[x][i] : 0.f;
                 rowpart[i] = a * Bm[r * C + s2];             // dbeta_A
-                db[i] = sm.bs[r] * a;                        // dB = Diag(beta) dA
-                sm.rb[0][r * LDC + s2] = bf(db[i]);
+                sm.yt[r * LDC + s2] = bf(sm.bs[r] * a);      // dB = Diag(beta) dA
             }
-            put4t(sm.rb[1] + s2 * LDC + r0, db);            // dB^T
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float pp = rowpart[i];
@@ -819,19 +795,13 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 if (ln == 0) sm.dbp[ni][r0 + i] = pp;
             }
         }
-        // dP and dP^T over Minv, from this wave's dP tiles
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int t = wave + W * x, mi = t / 4, ni = t % 4, s2 = 16 * ni + ln;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.ra[0][(16 * mi + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
-            put4t(sm.ra[1] + s2 * LDC + 16 * mi + 4 * g4, rP[x]);
-        }
     }
     __syncthreads();
+    const bf16_t* dB = sm.yt;
     // per 16x16 tile of (row r, key channel c): dKg = dKg_W + dB Kn,
     // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain;
-    // wave w owns channel block w (tiles t = w + 8x: row block x)
+    // wave w owns channel block w (tiles t = w + 8x: row block x).  Kn, Kg
+    // and Qg, and dB and dP where transposed, are read by rows of K.
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int mi = x, ni = wave;
@@ -846,10 +816,11 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             qv[i] = elem<T>::load(q + row);
         }
         f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const f32x4 aKg = tile_mm<C>(sm.rb[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
-        f32x4 aKn = tile_mm<C>(sm.rb[1] + 16 * mi * LDC, LDC, sm.kgt + 16 * ni * LDC, LDC, lane, z);
-        aKn = tile_mm<C>(sm.ra[1] + 16 * mi * LDC, LDC, sm.qgt + 16 * ni * LDC, LDC, lane, aKn);
-        const f32x4 aQg = tile_mm<C>(sm.ra[0] + 16 * mi * LDC, LDC, sm.knt + 16 * ni * LDC, LDC, lane, z);
+        const bf16_t* knt = sm.kn + 16 * ni;
+        const f32x4 aKg = tile_mm<C, kKc, kMc>(dB + 16 * mi * LDC, LDC, knt, LDT, lane, z);
+        f32x4 aKn = tile_mm<C, kMc, kMc>(dB + 16 * mi, LDC, sm.kg + 16 * ni, LDT, lane, z);
+        aKn = tile_mm<C, kMc, kMc>(sm.dp + 16 * mi, LDC, sm.qg + 16 * ni, LDT, lane, aKn);
+        const f32x4 aQg = tile_mm<C, kKc, kMc>(sm.dp + 16 * mi * LDC, LDC, knt, LDT, lane, z);
         const float G = sm.g[(c.len - 1) * D + ch];
         float dGp = 0.f;
 #pragma unroll

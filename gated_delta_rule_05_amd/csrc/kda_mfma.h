@@ -85,4 +85,24 @@ __device__ __forceinline__ u32x4 pack4(f32x4 lo, f32x4 hi) {
 __device__ __forceinline__ u32x2 pack2(f32x4 x) { return u32x2{pk(x[0], x[1]), pk(x[2], x[3])}; }
 __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a[0], a[1], b[0], b[1]}; }
 
+// ---- gfx950 LDS transpose read (ds_read_b64_tr_b16).  Each 16-lane group
+// exchanges the 8-byte chunks its lanes address: lane 4a + b receives, as
+// element e, element b of the chunk addressed by lane 4e + a (a, b, e in
+// 0..3; layout measured on the device).  If lane s of a group addresses row
+// k0 + s / 4, columns n0 + 4 (s % 4) .. +3 of a row-major bf16 array, lane
+// n of the group therefore gets rows k0 .. k0 + 3 of column n0 + n.
+__device__ __forceinline__ u32x2 ld_tr4(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) i16x4_t* lds_i16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (lds_i16x4)(const_cast<uint16_t*>(p))));
+}
+// the 16x16x32 operand fragment of lane (g, ln) -- K indices k0 + 8g .. +7
+// of column ln -- from a bf16 LDS array stored [k][column] with row stride
+// ld (a multiple of 4), x pointing at (k0, column 0): two transpose reads
+__device__ __forceinline__ u32x4 frag_tr(const uint16_t* x, int ld, int lane) {
+    const int g = lane >> 4, ln = lane & 15;
+    const uint16_t* p = x + (8 * g + (ln >> 2)) * ld + 4 * (ln & 3);
+    return cat(ld_tr4(p), ld_tr4(p + 4 * ld));
+}
+
 }  // namespace kda
