@@ -43,6 +43,7 @@
 // Every product is a bf16 MFMA (16x16x32) with fp32 accumulation on
 // operands staged in LDS; states, adjoints and gates stay fp32.
 #include <algorithm>
+#include <mutex>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -887,6 +888,10 @@ __global__ void bwd_init_kernel(const float* __restrict__ dhT, float* __restrict
 
 int64_t bound_chunks(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) / C : 0; }
 
+// Per-block buffers come in pairs: while the gradient pass of block b reads
+// its pair, the prep and the carry of block b - 1 fill the other.
+constexpr int kRing = 2;
+
 struct BwdLayout {
     size_t fwd, sall, slots, dsblk, deblk, dstate, total;
 };
@@ -903,17 +908,55 @@ BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
     l.deblk = blk * C * D * 2;
     l.dstate = nh * kState * 4;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    l.total = up(l.fwd) + up(l.sall) + up(l.slots) + up(l.dsblk) + up(l.deblk) +
+    l.total = up(l.fwd) + up(l.sall) + kRing * (up(l.slots) + up(l.dsblk) + up(l.deblk)) +
               up(l.dstate);
     return l;
 }
+
+// the serial carry runs on a second stream of the caller's device, created
+// once per device at the default priority and kept for the process
+hipError_t aux_stream(hipStream_t* out) {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev]) {
+        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
+        if (e != hipSuccess) { streams[dev] = nullptr; return e; }
+    }
+    *out = streams[dev];
+    return hipSuccess;
+}
+
+// events of one call, released when the call returns (a destroyed event
+// still completes the waits already queued on it)
+struct CallEvents {
+    hipEvent_t prep[kRing] = {}, carry[kRing] = {};
+    hipError_t create() {
+        for (int i = 0; i < kRing; ++i) {
+            hipError_t e = hipEventCreateWithFlags(&prep[i], hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventCreateWithFlags(&carry[i], hipEventDisableTiming);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    ~CallEvents() {
+        for (int i = 0; i < kRing; ++i) {
+            if (prep[i]) (void)hipEventDestroy(prep[i]);
+            if (carry[i]) (void)hipEventDestroy(carry[i]);
+        }
+    }
+};
 
 }  // namespace
 
 int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
     // about 1 GiB of per-block buffers (prep operands and carry outputs:
-    // ~155 KB per (chunk, head)), at most 64 chunks
-    const size_t per_chunk = static_cast<size_t>(N) * H *
+    // ~155 KB per (chunk, head), two blocks' worth), at most 64 chunks
+    const size_t per_chunk = static_cast<size_t>(N) * H * kRing *
                              (kSlot + kState * 2 + static_cast<size_t>(C) * D * 2);
     int64_t L = static_cast<int64_t>((size_t{1} << 30) / per_chunk);
     L = std::max<int64_t>(1, std::min<int64_t>(L, std::max<int64_t>(1, bound_chunks(total_T))));
@@ -930,10 +973,20 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
     uint8_t* p = static_cast<uint8_t*>(ws);
     uint8_t* fwd_ws = p;          p += up(l.fwd);
     bf16_t* sall = reinterpret_cast<bf16_t*>(p);  p += up(l.sall);
-    uint8_t* slots = p;           p += up(l.slots);
-    bf16_t* dsblk = reinterpret_cast<bf16_t*>(p);  p += up(l.dsblk);
-    bf16_t* deblk = reinterpret_cast<bf16_t*>(p);  p += up(l.deblk);
+    uint8_t* slots[kRing];
+    bf16_t* dsblk[kRing];
+    bf16_t* deblk[kRing];
+    for (int i = 0; i < kRing; ++i) {
+        slots[i] = p;                                  p += up(l.slots);
+        dsblk[i] = reinterpret_cast<bf16_t*>(p);       p += up(l.dsblk);
+        deblk[i] = reinterpret_cast<bf16_t*>(p);       p += up(l.deblk);
+    }
     float* dstate = reinterpret_cast<float*>(p);
+    hipStream_t serial = nullptr;
+    hipError_t e = aux_stream(&serial);
+    if (e != hipSuccess) return e;
+    CallEvents ev;
+    if ((e = ev.create()) != hipSuccess) return e;
 
     // 1. forward: the state after every full chunk, no outputs
     PrefillArgs f{};
@@ -943,11 +996,18 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
     f.dtype_f32 = false; f.scale = a.scale;
     f.snapshots = reinterpret_cast<float*>(sall);   // bf16 record (snap_cap < 0)
     f.snap_tokens = C; f.snap_cap = -1;
-    hipError_t e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D),
-                                     fwd_ws, stream);
+    e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D), fwd_ws,
+                          stream);
     if (e != hipSuccess) return e;
 
-    // 2. backward over blocks of chunks, from the last
+    // 2. backward over blocks of chunks, from the last.  Caller's stream:
+    //    prep(b - 1), then grad(b) once carry(b) is done; second stream:
+    //    carry(b) once prep(b) is done.  Ring slot b % 2 holds block b's
+    //    operands and carry outputs; prep(b - 1) and carry(b - 1) reuse the
+    //    slot of block b + 1, whose readers (carry(b + 1), grad(b + 1)) come
+    //    before them in stream order.  The caller's stream ends with
+    //    grad(0), which waits for the last carry: the call's work is whole
+    //    on the caller's stream.
     const int64_t n4 = static_cast<int64_t>(a.N) * a.H * kState / 4;
     hipLaunchKernelGGL(bwd_init_kernel, dim3(static_cast<unsigned>(std::min<int64_t>(4096, (n4 + 255) / 256))),
                        dim3(256), 0, stream, a.dhT, dstate, n4);
@@ -959,27 +1019,40 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
     const bf16_t* k = static_cast<const bf16_t*>(a.k);
     const bf16_t* v = static_cast<const bf16_t*>(a.v);
     const bf16_t* dO = static_cast<const bf16_t*>(a.dO);
-    for (int64_t b = nblk - 1; b >= 0; --b) {
-        const int c_lo = static_cast<int>(b * L_b);
+    auto prep = a.gate == kGateChannel ? bwd_prep_kernel<kGateChannel>
+              : a.gate == kGateHead    ? bwd_prep_kernel<kGateHead>
+                                       : bwd_prep_kernel<kGateNone>;
+    auto gk = a.gate == kGateChannel ? bwd_grad_kernel<bf16_t, kGateChannel>
+            : a.gate == kGateHead    ? bwd_grad_kernel<bf16_t, kGateHead>
+                                     : bwd_grad_kernel<bf16_t, kGateNone>;
+    // prep(b) (nothing to prepare for an empty batch) and the event the
+    // carry of block b waits for
+    auto launch_prep = [&](int64_t b) -> hipError_t {
+        const int r = static_cast<int>(b % kRing);
         if (a.total_T > 0) {
-            auto prep = a.gate == kGateChannel ? bwd_prep_kernel<kGateChannel>
-                      : a.gate == kGateHead    ? bwd_prep_kernel<kGateHead>
-                                               : bwd_prep_kernel<kGateNone>;
-            hipLaunchKernelGGL(prep, dim3(chunks), dim3(GT), 0, stream, q, k, a.log_alpha, a.beta,
-                               a.cu_seqlens, a.H, c_lo, L_b, a.scale, slots);
-            if ((e = hipGetLastError()) != hipSuccess) return e;
+            hipLaunchKernelGGL(prep, dim3(chunks), dim3(GT), 0, stream, q, k, a.log_alpha,
+                               a.beta, a.cu_seqlens, a.H, static_cast<int>(b * L_b), L_b,
+                               a.scale, slots[r]);
+            const hipError_t le = hipGetLastError();
+            if (le != hipSuccess) return le;
         }
+        return hipEventRecord(ev.prep[r], stream);
+    };
+    if ((e = launch_prep(nblk - 1)) != hipSuccess) return e;
+    for (int64_t b = nblk - 1; b >= 0; --b) {
+        const int c_lo = static_cast<int>(b * L_b), r = static_cast<int>(b % kRing);
+        if ((e = hipStreamWaitEvent(serial, ev.prep[r], 0)) != hipSuccess) return e;
         hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>(a.N * a.H * (D / kCarryTile))),
-                           dim3(GT), 0, stream, slots, dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
-                           dstate, dsblk, deblk, a.dh0);
+                           dim3(GT), 0, serial, slots[r], dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
+                           dstate, dsblk[r], deblk[r], a.dh0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipEventRecord(ev.carry[r], serial)) != hipSuccess) return e;
+        if (b > 0 && (e = launch_prep(b - 1)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(stream, ev.carry[r], 0)) != hipSuccess) return e;
         if (a.total_T == 0) continue;
-        auto gk = a.gate == kGateChannel ? bwd_grad_kernel<bf16_t, kGateChannel>
-                : a.gate == kGateHead    ? bwd_grad_kernel<bf16_t, kGateHead>
-                                         : bwd_grad_kernel<bf16_t, kGateNone>;
-        hipLaunchKernelGGL(gk, dim3(chunks), dim3(GT), 0, stream, slots, dsblk, deblk, sall, a.h0,
-                           q, k, v, dO, a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo, L_b, a.scale,
-                           static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
+        hipLaunchKernelGGL(gk, dim3(chunks), dim3(GT), 0, stream, slots[r], dsblk[r], deblk[r],
+                           sall, a.h0, q, k, v, dO, a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo,
+                           L_b, a.scale, static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
                            static_cast<bf16_t*>(a.dv), a.dlog_alpha, a.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

@@ -377,8 +377,8 @@ int kda_decode_multi(const void *q, const void *k, const void *v,
  * Bytes of device workspace kda_bwd needs for these sizes and options:
  * the start state of every chunk (one bf16 state per (chunk, head), so
  * 512 MiB per 16,384 head-chunks), the forward pass's operand block, and
- * one block of per-(chunk, head) backward operands.  0 for arguments
- * kda_bwd would reject.
+ * two blocks of per-(chunk, head) backward operands (one filled while the
+ * other is consumed).  0 for arguments kda_bwd would reject.
  */
 size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
                                int32_t d_k, int32_t d_v, int32_t dtype,
@@ -408,6 +408,11 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * kda_bwd_workspace_bytes [WORKSPACE_TOO_SMALL].
  * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
  * adjoints, as in the forward pass.
+ * Streams: the serial state-adjoint pass runs on a second stream of the
+ * device (created by the library on first use, default priority, kept for
+ * the process), ordered against the caller's stream by events; all of the
+ * call's work is complete once the caller's stream reaches the point after
+ * the call.
  */
 int kda_bwd(const void *q, const void *k, const void *v,
             const float *log_alpha, const float *beta, const float *h0,

@@ -323,8 +323,8 @@ def test_backward_workspace_query():
     assert lib.kda_bwd_workspace_bytes(4096, 4, 16, 128, 128, 1, ctypes.byref(opts)) == 0
     a = lib.kda_bwd_workspace_bytes(4096, 4, 16, 128, 128, 0, ctypes.byref(opts))
     b = lib.kda_bwd_workspace_bytes(8192, 4, 16, 128, 128, 0, ctypes.byref(opts))
-    # one fp32 state per (chunk, head) grows with the tokens
-    assert a > 0 and b - a >= 4096 // 64 * 16 * 128 * 128 * 4
+    # one bf16 state per (chunk, head) grows with the tokens
+    assert a > 0 and b - a >= 4096 // 64 * 16 * 128 * 128 * 2
     assert kda.backward_workspace_bytes(4096, 4, 16, 128, 128) == a
 
 
