@@ -33,7 +33,7 @@
 // Passes (one call): the forward two-pass prefill records the start state of
 // every chunk (no outputs); then, over blocks of chunks from the last:
 //   prep   (chunk-parallel) recomputes a chunk's operands: Kd, Kg, scale P^T,
-//          scale Qg^T, -W^T, Minv, B, gamma;
+//          scale Qg, -W^T, Minv, B, gamma;
 //   carry  (serial per (sequence, head, 64 value columns)) walks the chunks
 //          backwards with dS in registers, storing dS' and dE of each chunk;
 //   grad   (chunk-parallel) first the products with the states (dV, dT,
@@ -59,13 +59,14 @@ constexpr int GT = 512;        // threads of the chunk-parallel kernels: 8 waves
 constexpr int LDD = D + 8;     // padded LDS row of a [.][D] bf16 matrix
 constexpr int LDC = C + 8;     // padded LDS row of a [.][C] bf16 matrix
 constexpr int kCarryTile = 64; // value columns per carry work-group
+constexpr int LDO = kCarryTile + 16;   // the carry's dO tile: rows read by transpose reads
 
 // per-(chunk, head) operands written by the prep pass (bytes)
 constexpr int kOffKd = 0;                    // [C][D] bf16   K e^{G-g}
 constexpr int kOffKg = kOffKd + C * D * 2;   // [C][D] bf16   K e^{g}
 constexpr int kOffPt = kOffKg + C * D * 2;   // [C][C] bf16   scale P^T
-constexpr int kOffQt = kOffPt + C * C * 2;   // [D][C] bf16   scale Qg^T
-constexpr int kOffWt = kOffQt + D * C * 2;   // [D][C] bf16   -W^T
+constexpr int kOffQg = kOffPt + C * C * 2;   // [C][D] bf16   scale Qg
+constexpr int kOffWt = kOffQg + C * D * 2;   // [D][C] bf16   -W^T
 constexpr int kOffMinv = kOffWt + D * C * 2; // [C][C] fp32   (I + A)^-1
 constexpr int kOffB = kOffMinv + C * C * 4;  // [C][C] fp32   Kg Kn^T
 constexpr int kOffGam = kOffB + C * C * 4;   // [D]    fp32   e^{G}
@@ -187,7 +188,6 @@ __device__ __forceinline__ void load_gates(const float* la, const float* beta, c
 struct alignas(16) PrepLds {
     float g[C * D];
     bf16_t kg[C * LDD], kn[C * LDD], qg[C * LDD];
-    bf16_t kgt[D * LDC];
     float bm[C * (C + 1)], mi[C * (C + 1)];
     bf16_t tt[C * LDC];
     float bs[C];
@@ -210,7 +210,7 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     bf16_t* oKd = reinterpret_cast<bf16_t*>(out + kOffKd);
     bf16_t* oKg = reinterpret_cast<bf16_t*>(out + kOffKg);
     bf16_t* oPt = reinterpret_cast<bf16_t*>(out + kOffPt);
-    bf16_t* oQt = reinterpret_cast<bf16_t*>(out + kOffQt);
+    bf16_t* oQg = reinterpret_cast<bf16_t*>(out + kOffQg);
     bf16_t* oWt = reinterpret_cast<bf16_t*>(out + kOffWt);
     float* oMinv = reinterpret_cast<float*>(out + kOffMinv);
     float* oB = reinterpret_cast<float*>(out + kOffB);
@@ -237,8 +237,6 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             kn[e] = kk[e] * en;
             qg[e] = qq[e] * eg;
             kd[e] = kk[e] * ed;
-            sm.kgt[(c0 + e) * LDC + r] = bf(kg[e]);
-            oQt[(c0 + e) * C + r] = bf(scale * qg[e]);
         }
         const f32x4 vkg = {kg[0], kg[1], kg[2], kg[3]}, vkn = {kn[0], kn[1], kn[2], kn[3]};
         const f32x4 vqg = {qg[0], qg[1], qg[2], qg[3]}, vkd = {kd[0], kd[1], kd[2], kd[3]};
@@ -247,6 +245,7 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         put4t(sm.qg + r * LDD + c0, vqg);
         put4t(oKd + r * D + c0, vkd);
         put4t(oKg + r * D + c0, vkg);
+        put4t(oQg + r * D + c0, scale * vqg);
     }
     if (tid < D) oGam[tid] = gate_exp(sm.g[(c.len - 1) * D + tid]);
     __syncthreads();
@@ -325,8 +324,8 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         sm.tt[r * LDC + s] = bf(m * sm.bs[s]);     // T = Minv Diag(beta)
     }
     __syncthreads();
-    // -W^T, W = T Kg
-    mm<4, 8, C, GT>(sm.tt, LDC, sm.kgt, LDC, [&](int mi, int ni, f32x4 acc) {
+    // -W^T, W = T Kg (Kg read by rows of K)
+    mm<4, 8, C, GT, kKc, kMc>(sm.tt, LDC, sm.kg, LDD, [&](int mi, int ni, f32x4 acc) {
         put4t(oWt + (16 * ni + ln) * C + 16 * mi + 4 * g4, -acc);
     });
 }
@@ -337,10 +336,10 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 struct alignas(16) CarryLds {
     bf16_t kd[C * LDD];
     bf16_t pt[C * LDC];
-    bf16_t qt[D * LDC];
+    bf16_t qg[C * LDD];                // scale Qg
     bf16_t wt[D * LDC];
     float gam[D];
-    bf16_t dot[kCarryTile * LDC];      // dO^T of the tile's columns
+    bf16_t dol[C * LDO];               // dO of the tile's columns
     bf16_t dst[4][16 * LDD];           // each wave's dS slab, transposed
     bf16_t det[4][16 * LDC];           // each wave's dE slab, transposed
 };
@@ -395,9 +394,9 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         for (int i = 0; i < 4; ++i) S[m][i] = st[(rb + 16 * m + 4 * g4 + i) * D + jc];
 
     // The next chunk's operands load into registers while this chunk
-    // computes.  Kd, P^T, Qg^T and W^T are 3584 16-byte units: 7 per
+    // computes.  Kd, P^T, Qg and W^T are 3584 16-byte units: 7 per
     // thread, and with 512 threads unit x * 512 + tid falls in one matrix
-    // for every thread (Kd: x < 2; P^T: x = 2; Qg^T: x < 5; W^T: x < 7).
+    // for every thread (Kd: x < 2; P^T: x = 2; Qg: x < 5; W^T: x < 7).
     constexpr int PER = (C * D + C * C + 2 * D * C) / 8 / GT;
     static_assert(PER * GT * 8 == C * D + C * C + 2 * D * C, "whole rounds");
     static_assert(GT == 512, "the unit-to-matrix map below assumes 512 threads");
@@ -427,17 +426,13 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
             bf16_t* dst;
             if (x < 2) dst = sm.kd + (u / 16) * LDD + (u % 16) * 8;
             else if (x < 3) { const int w = u - 2 * GT; dst = sm.pt + (w / 8) * LDC + (w % 8) * 8; }
-            else if (x < 5) { const int w = u - 3 * GT; dst = sm.qt + (w / 8) * LDC + (w % 8) * 8; }
+            else if (x < 5) { const int w = u - 3 * GT; dst = sm.qg + (w / 16) * LDD + (w % 16) * 8; }
             else { const int w = u - 5 * GT; dst = sm.wt + (w / 8) * LDC + (w % 8) * 8; }
             *reinterpret_cast<u32x4*>(dst) = pre[x];
         }
         if (tid < D) sm.gam[tid] = pgam;
         const int r = tid >> 3, part = tid & 7;
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-            sm.dot[(8 * part + 2 * x) * LDC + r] = static_cast<bf16_t>(pdo[x] & 0xffffu);
-            sm.dot[(8 * part + 2 * x + 1) * LDC + r] = static_cast<bf16_t>(pdo[x] >> 16);
-        }
+        *reinterpret_cast<u32x4*>(sm.dol + r * LDO + 8 * part) = pdo;
     };
 
     fetch(hi);
@@ -457,13 +452,13 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         // dE = Kd dS' + scale P^T dO  (this slab's 16 columns, row tiles 2 half, 2 half + 1)
         bf16_t* dep = deblk + slot * (static_cast<int64_t>(C) * D);
         const bf16_t* dsw = sm.dst[slab];
-        const bf16_t* dow = sm.dot + 16 * slab * LDC;
+        const bf16_t* dow = sm.dol + 16 * slab;   // dO by rows of K
 #pragma unroll
         for (int mm2 = 0; mm2 < 2; ++mm2) {
             const int m = 2 * half + mm2;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = tile_mm<D>(sm.kd + 16 * m * LDD, LDD, dsw, LDD, lane, acc);
-            acc = tile_mm<C>(sm.pt + 16 * m * LDC, LDC, dow, LDC, lane, acc);
+            acc = tile_mm<C, kKc, kMc>(sm.pt + 16 * m * LDC, LDC, dow, LDO, lane, acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i) dep[(16 * m + 4 * g4 + i) * D + jc] = bf(acc[i]);
             put4t(&sm.det[slab][ln * LDC + 16 * m + 4 * g4], acc);
@@ -477,7 +472,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * mb + 4 * g4 + i] * S[m][i];
-            acc = tile_mm<C>(sm.qt + 16 * mb * LDC, LDC, dow, LDC, lane, acc);
+            acc = tile_mm<C, kMc, kMc>(sm.qg + 16 * mb, LDD, dow, LDO, lane, acc);
             acc = tile_mm<C>(sm.wt + 16 * mb * LDC, LDC, dew, LDC, lane, acc);
             S[m] = acc;
         }
