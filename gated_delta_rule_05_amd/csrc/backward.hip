@@ -126,18 +126,45 @@ __device__ __forceinline__ f32x4 tile_mm(const bf16_t* a, int lda, const bf16_t*
     return acc;
 }
 
-// all 16x16 tiles (mi < MT, ni < NTL) of A B, spread over the NTH / 64 waves;
-// fn(mi, ni, acc) consumes each (acc[i] = row 16 mi + 4g + i, column 16 ni + ln)
+// this wave's tiles of a (MT x NTL)-tile product, in a fixed order: tile x
+// is t = wave + W x for W waves (row block t / NTL, column block t % NTL).
+// W is a multiple of NTL, so all of a wave's tiles share one column block:
+// each B fragment is read from LDS once per K step and used for every tile.
+template <int NTL, int K, int NX, int NTH = NT, int AL = kKc, int BL = kKc>
+__device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* b, int ldb,
+                                        f32x4 (&out)[NX]) {
+    constexpr int W = NTH / 64;
+    static_assert(W % NTL == 0, "a wave's tiles in one column block");
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int m0 = wave / NTL;
+    const bf16_t* bt = tile_at<BL>(b, ldb, wave % NTL);
+#pragma unroll
+    for (int x = 0; x < NX; ++x) out[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < K; kk += 32) {
+        const u32x4 fb = frag<BL>(bt, ldb, kk, lane);
+#pragma unroll
+        for (int x = 0; x < NX; ++x)
+            out[x] = mma32(frag<AL>(tile_at<AL>(a, lda, m0 + (W / NTL) * x), lda, kk, lane), fb,
+                           out[x]);
+    }
+}
+
+// all 16x16 tiles (mi < MT, ni < NTL) of A B, spread over the NTH / 64 waves
+// as in mm_regs; fn(mi, ni, acc) consumes each (acc[i] = row 16 mi + 4g + i,
+// column 16 ni + ln)
 template <int MT, int NTL, int K, int NTH = NT, int AL = kKc, int BL = kKc, typename Fn>
 __device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* b, int ldb,
                                    Fn&& fn) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    for (int t = wave; t < MT * NTL; t += NTH / 64) {
-        const int mi = t / NTL, ni = t - mi * NTL;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        acc = tile_mm<K, AL, BL>(tile_at<AL>(a, lda, mi), lda, tile_at<BL>(b, ldb, ni), ldb,
-                                 lane, acc);
-        fn(mi, ni, acc);
+    constexpr int W = NTH / 64, NX = MT * NTL / W;
+    static_assert(MT * NTL % W == 0, "whole tiles per wave");
+    f32x4 acc[NX];
+    mm_regs<NTL, K, NX, NTH, AL, BL>(a, lda, b, ldb, acc);
+    const int wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int x = 0; x < NX; ++x) {
+        const int t = wave + W * x;
+        fn(t / NTL, t % NTL, acc[x]);
     }
 }
 
@@ -513,8 +540,7 @@ struct alignas(16) GradALds {
     float dgp[4][D];           // dgamma over four quarters of the value columns
 };
 struct alignas(16) GradBLds {
-    float g[C * D];            // cumulative gates; later dlog_alpha rows (head gate)
-    float dg[C * D];
+    float g[C * D];            // cumulative gates
     bf16_t kg[C * LDT], kn[C * LDT], qg[C * LDT];   // gated keys and queries, row-major
     bf16_t mv[C * LDC];        // Minv
     bf16_t dp[C * LDC];        // dP
@@ -523,7 +549,7 @@ struct alignas(16) GradBLds {
     float bs[C];
     float db[C];               // dbeta
     float dbp[4][C];           // dbeta_A per 16-column block, summed in order
-    float dG[D];
+    float hp[GT / 64][C];      // per-head gate: dlog_alpha per wave's channel block
 };
 union alignas(16) GradLds {
     GradALds a;
@@ -539,21 +565,6 @@ __device__ __forceinline__ void stage_f32_t(const float* src, int rows, bf16_t* 
         if (src) x = *reinterpret_cast<const f32x4*>(src + r * D + c0);
 #pragma unroll
         for (int e = 0; e < 4; ++e) tr[(c0 + e) * ldt + r] = bf(x[e]);
-    }
-}
-
-// this wave's tiles of a (4 x NTL)-tile product, in a fixed order: tile x
-// is t = wave + W x for W waves (row block t / NTL, column block t % NTL)
-template <int NTL, int K, int NX, int NTH = NT, int AL = kKc, int BL = kKc>
-__device__ __forceinline__ void mm_regs(const bf16_t* a, int lda, const bf16_t* b, int ldb,
-                                        f32x4 (&out)[NX]) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-#pragma unroll
-    for (int x = 0; x < NX; ++x) {
-        const int t = wave + (NTH / 64) * x, mi = t / NTL, ni = t % NTL;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        out[x] = tile_mm<K, AL, BL>(tile_at<AL>(a, lda, mi), lda, tile_at<BL>(b, ldb, ni), ldb,
-                                    lane, acc);
     }
 }
 
@@ -753,12 +764,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.dp[(16 * mi + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
     }
-    if (tid < C) {
-        sm.db[tid] = s_dbT[0][tid] + s_dbT[1][tid];
-    } else if (tid >= GT - D) {
-        const int ch = tid - (GT - D);
-        sm.dG[ch] = s_dgam[ch] * gate_exp(sm.g[(c.len - 1) * D + ch]);
-    }
+    if (tid < C) sm.db[tid] = s_dbT[0][tid] + s_dbT[1][tid];
     __syncthreads();
     // Z = Minv^T (dT Diag(beta))  (Minv read by rows of K)
     mm<4, 4, C, GT, kMc, kKc>(sm.mv, LDC, sm.yt, LDC, [&](int mi, int ni, f32x4 acc) {
@@ -794,14 +800,31 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
     __syncthreads();
     const bf16_t* dB = sm.yt;
+    if (tid >= GT - C) {
+        const int r = tid - (GT - C);
+        if (r < c.len)
+            dbeta[(c.t0 + r) * H + c.h] = sm.db[r] + ((sm.dbp[0][r] + sm.dbp[1][r]) +
+                                                      (sm.dbp[2][r] + sm.dbp[3][r]));
+    }
     // per 16x16 tile of (row r, key channel c): dKg = dKg_W + dB Kn,
     // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain;
-    // wave w owns channel block w (tiles t = w + 8x: row block x).  Kn, Kg
-    // and Qg, and dB and dP where transposed, are read by rows of K.
+    // wave w owns channel block w (tiles t = w + 8x: row block x), so the
+    // B fragments of Kn, Kg and Qg (read by rows of K) serve all four tiles,
+    // and every per-channel sum over the chunk's rows stays in the wave.
+    const int ch = 16 * wave + ln;
+    u32x4 fkn[2], fkg[2], fqg[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        fkn[s2] = frag<kMc>(sm.kn + 16 * wave, LDT, 32 * s2, lane);
+        fkg[s2] = frag<kMc>(sm.kg + 16 * wave, LDT, 32 * s2, lane);
+        fqg[s2] = frag<kMc>(sm.qg + 16 * wave, LDT, 32 * s2, lane);
+    }
+    const float G = sm.g[(c.len - 1) * D + ch];
+    float dgr[4][4];          // dg of rows 16x + 4 g4 + i, this lane's channel
+    float dGp = 0.f;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
-        const int mi = x, ni = wave;
-        const int ch = 16 * ni + ln;
+        const int mi = x;
         float kv[4], qv[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -811,14 +834,14 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             kv[i] = elem<T>::load(k + row);
             qv[i] = elem<T>::load(q + row);
         }
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        const bf16_t* knt = sm.kn + 16 * ni;
-        const f32x4 aKg = tile_mm<C, kKc, kMc>(dB + 16 * mi * LDC, LDC, knt, LDT, lane, z);
-        f32x4 aKn = tile_mm<C, kMc, kMc>(dB + 16 * mi, LDC, sm.kg + 16 * ni, LDT, lane, z);
-        aKn = tile_mm<C, kMc, kMc>(sm.dp + 16 * mi, LDC, sm.qg + 16 * ni, LDT, lane, aKn);
-        const f32x4 aQg = tile_mm<C, kKc, kMc>(sm.dp + 16 * mi * LDC, LDC, knt, LDT, lane, z);
-        const float G = sm.g[(c.len - 1) * D + ch];
-        float dGp = 0.f;
+        f32x4 aKg = {0.f, 0.f, 0.f, 0.f}, aKn = aKg, aQg = aKg;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            aKg = mma32(frag<kKc>(dB + 16 * mi * LDC, LDC, 32 * s2, lane), fkn[s2], aKg);
+            aKn = mma32(frag<kMc>(dB + 16 * mi, LDC, 32 * s2, lane), fkg[s2], aKn);
+            aKn = mma32(frag<kMc>(sm.dp + 16 * mi, LDC, 32 * s2, lane), fqg[s2], aKn);
+            aQg = mma32(frag<kKc>(sm.dp + 16 * mi * LDC, LDC, 32 * s2, lane), fkn[s2], aQg);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * mi + 4 * g4 + i;
@@ -837,36 +860,63 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
                 dGp += dKd * Kd;
             }
-            sm.dg[r * D + ch] = dgv;
+            dgr[x][i] = dgv;
         }
+    }
+    if constexpr (GATE != kGateNone) {
+        // dlog_alpha[r] = sum_{r' >= r} dg[r'] + dG per key channel, in
+        // registers: row r = 16x + 4 g4 + i is summed over the rows after it
+        // in its lane (i), in the lane groups after it (g4) and in the row
+        // blocks after it (x), in that fixed order
         dGp += __shfl_xor(dGp, 16);
         dGp += __shfl_xor(dGp, 32);
-        // channel block ni belongs to this wave alone: the adds come in a fixed order
-        if (g4 == 0) atomicAdd(&sm.dG[ch], dGp);
-    }
-    __syncthreads();
-    // dlog_alpha[s] = sum_{r >= s} dg[r] + dG, per key channel
-    if (tid < D) {
-        float run = sm.dG[tid];
-        for (int r = c.len - 1; r >= 0; --r) {
-            run += sm.dg[r * D + tid];
-            if constexpr (GATE == kGateChannel) dla[((c.t0 + r) * H + c.h) * D + tid] = run;
-            else sm.g[r * D + tid] = run;
+        const float dG = s_dgam[ch] * gate_exp(G) + dGp;
+        float after = dG;                     // rows of the row blocks after x
+        float out[4][4];
+#pragma unroll
+        for (int x = 3; x >= 0; --x) {
+            float lane_sum = (dgr[x][0] + dgr[x][1]) + (dgr[x][2] + dgr[x][3]);
+            const float s16 = __shfl_down(lane_sum, 16), s32 = __shfl_down(lane_sum, 32),
+                        s48 = __shfl_down(lane_sum, 48);
+            const float groups_after = (g4 < 3 ? s16 : 0.f) + (g4 < 2 ? s32 : 0.f) +
+                                       (g4 < 1 ? s48 : 0.f);
+            float run = after + groups_after;
+#pragma unroll
+            for (int i = 3; i >= 0; --i) {
+                run += dgr[x][i];
+                out[x][i] = run;
+            }
+            const float block = lane_sum + __shfl_xor(lane_sum, 16);
+            after += block + __shfl_xor(block, 32);
         }
-    }
-    if (tid >= GT - C) {
-        const int r = tid - (GT - C);
-        if (r < c.len)
-            dbeta[(c.t0 + r) * H + c.h] = sm.db[r] + ((sm.dbp[0][r] + sm.dbp[1][r]) +
-                                                      (sm.dbp[2][r] + sm.dbp[3][r]));
-    }
-    if constexpr (GATE == kGateHead) {
-        __syncthreads();
-        // one gate per (token, head) reaches every key channel: the sum
-        if (tid < C && tid < c.len) {
-            float acc = 0.f;
-            for (int ch = 0; ch < D; ++ch) acc += sm.g[tid * D + ch];
-            dla[(c.t0 + tid) * H + c.h] = acc;
+        if constexpr (GATE == kGateChannel) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * x + 4 * g4 + i;
+                    if (r < c.len) dla[((c.t0 + r) * H + c.h) * D + ch] = out[x][i];
+                }
+        } else {
+            // one gate per (token, head) reaches every key channel: the sum
+            // over the channels, per wave across its 16 lanes, then over the
+            // waves in order
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v2 = out[x][i];
+#pragma unroll
+                    for (int m = 1; m < 16; m <<= 1) v2 += __shfl_xor(v2, m);
+                    if (ln == 0) sm.hp[wave][16 * x + 4 * g4 + i] = v2;
+                }
+            __syncthreads();
+            if (tid < C && tid < c.len) {
+                float acc = 0.f;
+#pragma unroll
+                for (int w = 0; w < W; ++w) acc += sm.hp[w][tid];
+                dla[(c.t0 + tid) * H + c.h] = acc;
+            }
         }
     }
 }
