@@ -603,6 +603,26 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // tiles kept in registers: tile x of this wave is t = wave + 8x
     f32x4 rKgW[4], rQgS[4], rKd[4];   // [C][D] terms, 4 x 8 tiles (row block x, column block wave)
     f32x4 rT[2], rP[2];               // [C][C] terms, 4 x 4 tiles
+    // fp32 Minv and B, loaded with the first round and used later: the rows
+    // of Minv this thread stages (twice), and the entries of this wave's
+    // dT / dA tiles (row 16 mi + 4 g4 + i, mi = wave / 4 + 2x, column s2)
+    // for dbeta_T and dbeta_A
+    f32x4 mvr[2];
+    float mvd[2][4], bmd[2][4];
+    {
+        const int s2 = 16 * (wave % 4) + ln;
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int u = tid + GT * x;
+            mvr[x] = *reinterpret_cast<const f32x4*>(mvg + (u / (C / 4)) * C + 4 * (u % (C / 4)));
+            const int mi = wave / 4 + 2 * x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                mvd[x][i] = mvg[(16 * mi + 4 * g4 + i) * C + s2];
+                bmd[x][i] = Bm[(16 * mi + 4 * g4 + i) * C + s2];
+            }
+        }
+    }
     // =========================== phase A ===========================
     {
         GradALds& sm = sm_u.a;
@@ -627,9 +647,10 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         }
         if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
         __syncthreads();
-        for (int u = tid; u < C * (C / 4); u += GT) {
-            const int r = u / (C / 4), s0 = (u % (C / 4)) * 4;
-            const f32x4 m = *reinterpret_cast<const f32x4*>(mvg + r * C + s0);
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int u = tid + GT * x, r = u / (C / 4), s0 = (u % (C / 4)) * 4;
+            const f32x4 m = mvr[x];
             put4t(sm.mvb + r * LDC + s0, f32x4{m[0] * sm.bs[s0], m[1] * sm.bs[s0 + 1],
                                                m[2] * sm.bs[s0 + 2], m[3] * sm.bs[s0 + 3]});
         }
@@ -672,11 +693,9 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             const int s2 = 16 * (wave % 4) + ln;
             float part = 0.f;
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
-                const int mi = (wave + W * x) / 4;
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) part += mvg[(16 * mi + 4 * g4 + i) * C + s2] * rT[x][i];
-            }
+                for (int i = 0; i < 4; ++i) part += mvd[x][i] * rT[x][i];
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
             if (g4 == 0) s_dbT[wave / 4][s2] = part;
@@ -731,9 +750,10 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             qr4[x] = elem<T>::load4(q + row);
         }
     }
-    for (int u = tid; u < C * (C / 4); u += GT) {
-        const int r = u / (C / 4), s0 = (u % (C / 4)) * 4;
-        put4t(sm.mv + r * LDC + s0, *reinterpret_cast<const f32x4*>(mvg + r * C + s0));
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int u = tid + GT * x;
+        put4t(sm.mv + (u / (C / 4)) * LDC + 4 * (u % (C / 4)), mvr[x]);
     }
     load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs);
     __syncthreads();
@@ -756,6 +776,19 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         put4t(sm.kn + r * LDT + c0, kn);
         put4t(sm.qg + r * LDT + c0, qg);
     }
+    // k and q again, at this lane's positions of the final tiles: loaded
+    // here, used after the triangular-system products
+    const int ch = 16 * wave + ln;
+    float kv[4][4], qv[4][4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = min(16 * x + 4 * g4 + i, c.len - 1);   // rows past the chunk: any valid row
+            const int64_t row = ((c.t0 + rr) * H + c.h) * D + ch;
+            kv[x][i] = elem<T>::load(k + row);
+            qv[x][i] = elem<T>::load(q + row);
+        }
     // (dT Diag(beta))^T and dP from this wave's dT and dP tiles
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
@@ -786,7 +819,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             for (int i = 0; i < 4; ++i) {
                 const int r = r0 + i;
                 const float a = s2 < r ? -dA[x][i] : 0.f;
-                rowpart[i] = a * Bm[r * C + s2];             // dbeta_A
+                rowpart[i] = a * bmd[x][i];                  // dbeta_A
                 sm.yt[r * LDC + s2] = bf(sm.bs[r] * a);      // dB = Diag(beta) dA
             }
 #pragma unroll
@@ -811,7 +844,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // wave w owns channel block w (tiles t = w + 8x: row block x), so the
     // B fragments of Kn, Kg and Qg (read by rows of K) serve all four tiles,
     // and every per-channel sum over the chunk's rows stays in the wave.
-    const int ch = 16 * wave + ln;
     u32x4 fkn[2], fkg[2], fqg[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
@@ -825,15 +857,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
         const int mi = x;
-        float kv[4], qv[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mi + 4 * g4 + i;
-            const int rr = min(r, c.len - 1);        // rows past the chunk: any valid row
-            const int64_t row = ((c.t0 + rr) * H + c.h) * D + ch;
-            kv[i] = elem<T>::load(k + row);
-            qv[i] = elem<T>::load(q + row);
-        }
         f32x4 aKg = {0.f, 0.f, 0.f, 0.f}, aKn = aKg, aQg = aKg;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -854,7 +877,8 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 const float dQg = aQg[i] + rQgS[x][i];
                 const float dKn = aKn[i];
                 const float dKd = rKd[x][i];
-                const float Kg = kv[i] * eg, Kn = kv[i] * en, Qg = qv[i] * eg, Kd = kv[i] * ed;
+                const float Kg = kv[x][i] * eg, Kn = kv[x][i] * en, Qg = qv[x][i] * eg;
+                const float Kd = kv[x][i] * ed;
                 elem<T>::store(dk + row, dKg * eg + dKn * en + dKd * ed);
                 elem<T>::store(dq + row, dQg * eg);
                 dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
