@@ -33,7 +33,7 @@
 // Passes (one call): the forward two-pass prefill records the start state of
 // every chunk (no outputs); then, over blocks of chunks from the last:
 //   prep   (chunk-parallel) recomputes a chunk's operands: Kd, Kg, scale P^T,
-//          scale Qg, -W^T, Minv, B, gamma;
+//          scale Qg, -W^T, Minv, gamma;
 //   carry  (serial per (sequence, head, 64 value columns)) walks the chunks
 //          backwards with dS in registers, storing dS' and dE of each chunk;
 //   grad   (chunk-parallel) first the products with the states (dV, dT,
@@ -68,8 +68,7 @@ constexpr int kOffPt = kOffKg + C * D * 2;   // [C][C] bf16   scale P^T
 constexpr int kOffQg = kOffPt + C * C * 2;   // [C][D] bf16   scale Qg
 constexpr int kOffWt = kOffQg + C * D * 2;   // [D][C] bf16   -W^T
 constexpr int kOffMinv = kOffWt + D * C * 2; // [C][C] fp32   (I + A)^-1
-constexpr int kOffB = kOffMinv + C * C * 4;  // [C][C] fp32   Kg Kn^T
-constexpr int kOffGam = kOffB + C * C * 4;   // [D]    fp32   e^{G}
+constexpr int kOffGam = kOffMinv + C * C * 4; // [D]    fp32   e^{G}
 constexpr int kSlot = kOffGam + D * 4;
 constexpr int64_t kState = static_cast<int64_t>(D) * D;   // floats per state
 
@@ -178,10 +177,12 @@ __device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
 // cumulative gates of the chunk's rows, per channel, into g[C][D] (rows past
 // the chunk repeat the last row); beta of its rows into bs[C] (0 past it).
 // The raw gates land in g with parallel vector loads first; the scan then
-// runs over LDS.
+// runs over LDS: each of four row quarters per channel on its own thread,
+// then the totals of the quarters before it added (part: 4 x D floats).
 template <int GATE, int NTH = NT>
 __device__ __forceinline__ void load_gates(const float* la, const float* beta, const ChunkRef& c,
-                                           int H, float* g, float* bs) {
+                                           int H, float* g, float* bs, float* part) {
+    static_assert(NTH >= 4 * D, "one thread per (row quarter, channel)");
     const int tid = threadIdx.x;
     for (int u = tid; u < C * (D / 4); u += NTH) {
         const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
@@ -199,13 +200,22 @@ __device__ __forceinline__ void load_gates(const float* la, const float* beta, c
     }
     if (tid < C) bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
     __syncthreads();
-    if (tid < D) {
-        float run = 0.f;
-#pragma unroll 16
-        for (int r = 0; r < C; ++r) {
-            run += g[r * D + tid];
-            g[r * D + tid] = run;
+    const int ch = tid % D, qr = tid / D;
+    float run = 0.f;
+    if (qr < 4) {
+#pragma unroll
+        for (int r = 16 * qr; r < 16 * qr + 16; ++r) {
+            run += g[r * D + ch];
+            g[r * D + ch] = run;
         }
+        part[qr * D + ch] = run;
+    }
+    __syncthreads();
+    if (qr < 4 && qr > 0) {
+        float off = part[ch];
+        for (int x = 1; x < qr; ++x) off += part[x * D + ch];
+#pragma unroll
+        for (int r = 16 * qr; r < 16 * qr + 16; ++r) g[r * D + ch] += off;
     }
 }
 
@@ -219,6 +229,7 @@ struct alignas(16) PrepLds {
     bf16_t tt[C * LDC];
     float bs[C];
     float xs[3][16 * 17];      // one wave's product block of the inverse
+    float gpart[4 * D];        // row-quarter totals of the gate scan
 };
 
 template <int GATE>
@@ -240,20 +251,27 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     bf16_t* oQg = reinterpret_cast<bf16_t*>(out + kOffQg);
     bf16_t* oWt = reinterpret_cast<bf16_t*>(out + kOffWt);
     float* oMinv = reinterpret_cast<float*>(out + kOffMinv);
-    float* oB = reinterpret_cast<float*>(out + kOffB);
     float* oGam = reinterpret_cast<float*>(out + kOffGam);
 
-    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs);
-    __syncthreads();
-    // gated keys and queries; rows past the chunk are zero
-    for (int idx = tid; idx < C * (D / 4); idx += GT) {
-        const int r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
-        float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+    // k and q of the chunk (rows past it zero) load while the gates scan
+    float4 kr4[C * (D / 4) / GT], qr4[C * (D / 4) / GT];
+#pragma unroll
+    for (int x = 0; x < C * (D / 4) / GT; ++x) {
+        const int idx = tid + GT * x, r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
+        kr4[x] = qr4[x] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (r < c.len) {
             const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
-            kv = elem<bf16_t>::load4(k + row);
-            qv = elem<bf16_t>::load4(q + row);
+            kr4[x] = elem<bf16_t>::load4(k + row);
+            qr4[x] = elem<bf16_t>::load4(q + row);
         }
+    }
+    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs, sm.gpart);
+    __syncthreads();
+    // gated keys and queries
+#pragma unroll
+    for (int x = 0; x < C * (D / 4) / GT; ++x) {
+        const int idx = tid + GT * x, r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
+        const float4 kv = kr4[x], qv = qr4[x];
         const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
         float kg[4], kn[4], qg[4], kd[4];
 #pragma unroll
@@ -282,7 +300,6 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
             sm.bm[r * (C + 1) + s] = acc[i];
-            oB[r * C + s] = acc[i];
         }
     });
     mm<4, 4, D, GT>(sm.qg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
@@ -550,6 +567,7 @@ struct alignas(16) GradBLds {
     float db[C];               // dbeta
     float dbp[4][C];           // dbeta_A per 16-column block, summed in order
     float hp[GT / 64][C];      // per-head gate: dlog_alpha per wave's channel block
+    float gpart[4 * D];        // row-quarter totals of the gate scan
 };
 union alignas(16) GradLds {
     GradALds a;
@@ -596,19 +614,17 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
     const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
     const float* mvg = reinterpret_cast<const float*>(sp + kOffMinv);
-    const float* Bm = reinterpret_cast<const float*>(sp + kOffB);
     const float* S0f = c.j == 0 && h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState
                                       : nullptr;
 
     // tiles kept in registers: tile x of this wave is t = wave + 8x
     f32x4 rKgW[4], rQgS[4], rKd[4];   // [C][D] terms, 4 x 8 tiles (row block x, column block wave)
     f32x4 rT[2], rP[2];               // [C][C] terms, 4 x 4 tiles
-    // fp32 Minv and B, loaded with the first round and used later: the rows
-    // of Minv this thread stages (twice), and the entries of this wave's
-    // dT / dA tiles (row 16 mi + 4 g4 + i, mi = wave / 4 + 2x, column s2)
-    // for dbeta_T and dbeta_A
+    // fp32 Minv, loaded with the first round and used later: the rows this
+    // thread stages (twice), and the entries of this wave's dT tiles (row
+    // 16 mi + 4 g4 + i, mi = wave / 4 + 2x, column s2) for dbeta_T
     f32x4 mvr[2];
-    float mvd[2][4], bmd[2][4];
+    float mvd[2][4];
     {
         const int s2 = 16 * (wave % 4) + ln;
 #pragma unroll
@@ -619,7 +635,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 mvd[x][i] = mvg[(16 * mi + 4 * g4 + i) * C + s2];
-                bmd[x][i] = Bm[(16 * mi + 4 * g4 + i) * C + s2];
             }
         }
     }
@@ -755,7 +770,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         const int u = tid + GT * x;
         put4t(sm.mv + (u / (C / 4)) * LDC + 4 * (u % (C / 4)), mvr[x]);
     }
-    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs);
+    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs, sm.gpart);
     __syncthreads();
     // gated keys and queries, row-major
 #pragma unroll
@@ -799,6 +814,10 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
     if (tid < C) sm.db[tid] = s_dbT[0][tid] + s_dbT[1][tid];
     __syncthreads();
+    // B = Kg Kn^T at this wave's dA tiles (for dbeta_A; the prep's inverse
+    // used the same bf16 operands and product order)
+    f32x4 bmt[2];
+    mm_regs<4, D, 2, GT>(sm.kg, LDT, sm.kn, LDT, bmt);
     // Z = Minv^T (dT Diag(beta))  (Minv read by rows of K)
     mm<4, 4, C, GT, kMc, kKc>(sm.mv, LDC, sm.yt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
@@ -819,7 +838,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             for (int i = 0; i < 4; ++i) {
                 const int r = r0 + i;
                 const float a = s2 < r ? -dA[x][i] : 0.f;
-                rowpart[i] = a * bmd[x][i];                  // dbeta_A
+                rowpart[i] = a * bmt[x][i];                  // dbeta_A
                 sm.yt[r * LDC + s2] = bf(sm.bs[r] * a);      // dB = Diag(beta) dA
             }
 #pragma unroll
