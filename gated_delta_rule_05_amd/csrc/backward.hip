@@ -174,66 +174,102 @@ __device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
 }
 
 
-// cumulative gates of the chunk's rows, per channel, into g[C][D] (rows past
-// the chunk repeat the last row); beta of its rows into bs[C] (0 past it).
-// The raw gates land in g with parallel vector loads first; the scan then
-// runs over LDS: each of four row quarters per channel on its own thread,
-// then the totals of the quarters before it added (part: 4 x D floats).
-template <int GATE, int NTH = NT>
-__device__ __forceinline__ void load_gates(const float* la, const float* beta, const ChunkRef& c,
-                                           int H, float* g, float* bs, float* part) {
-    static_assert(NTH >= 4 * D, "one thread per (row quarter, channel)");
-    const int tid = threadIdx.x;
-    for (int u = tid; u < C * (D / 4); u += NTH) {
-        const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+// Cumulative gates of a chunk at the thread's 4 rows 4 rg + i and 4
+// channels 4 cg + j (rg = tid / 32, cg = tid % 32, all GT threads): each
+// thread sums down its own rows, then a scan over the 16 row groups adds the
+// groups before.  Rows past the chunk add zero, so they repeat the last row,
+// and G (the chunk's total per channel) equals the last row's value.  Beta
+// of the rows into bs (0 past the chunk).  scan: 16 x D floats, tot: D
+// floats, both LDS; two barriers inside.
+template <int GATE>
+__device__ __forceinline__ void chunk_gates(const float* la, const float* beta, const ChunkRef& c,
+                                            int H, float* scan, float* tot, float* bs,
+                                            float (&g)[4][4], f32x4& G) {
+    static_assert(GT == (C / 4) * (D / 4), "one thread per 4 x 4 block of the chunk");
+    const int tid = threadIdx.x, rg = tid >> 5, cg = tid & 31;
+    f32x4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        raw[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (r < c.len) {
             const int64_t row = (c.t0 + r) * H + c.h;
             if constexpr (GATE == kGateChannel) {
-                x = *reinterpret_cast<const f32x4*>(la + row * D + c0);
+                raw[i] = *reinterpret_cast<const f32x4*>(la + row * D + 4 * cg);
             } else if constexpr (GATE == kGateHead) {
                 const float a = la[row];
-                x = f32x4{a, a, a, a};
+                raw[i] = f32x4{a, a, a, a};
             }
         }
-        *reinterpret_cast<f32x4*>(g + r * D + c0) = x;
     }
     if (tid < C) bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
-    __syncthreads();
-    const int ch = tid % D, qr = tid / D;
-    float run = 0.f;
-    if (qr < 4) {
 #pragma unroll
-        for (int r = 16 * qr; r < 16 * qr + 16; ++r) {
-            run += g[r * D + ch];
-            g[r * D + ch] = run;
+    for (int j = 0; j < 4; ++j) {
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            run += raw[i][j];
+            g[i][j] = run;
         }
-        part[qr * D + ch] = run;
+    }
+    *reinterpret_cast<f32x4*>(scan + rg * D + 4 * cg) = f32x4{g[3][0], g[3][1], g[3][2], g[3][3]};
+    __syncthreads();
+    if (tid < D) {
+        float run = 0.f;
+#pragma unroll
+        for (int x = 0; x < C / 4; ++x) {
+            const float t = scan[x * D + tid];
+            scan[x * D + tid] = run;
+            run += t;
+        }
+        tot[tid] = run;
     }
     __syncthreads();
-    if (qr < 4 && qr > 0) {
-        float off = part[ch];
-        for (int x = 1; x < qr; ++x) off += part[x * D + ch];
+    const f32x4 off = *reinterpret_cast<const f32x4*>(scan + rg * D + 4 * cg);
+    G = *reinterpret_cast<const f32x4*>(tot + 4 * cg);
 #pragma unroll
-        for (int r = 16 * qr; r < 16 * qr + 16; ++r) g[r * D + ch] += off;
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[i][j] += off[j];
+}
+
+// k or q of the thread's 4 rows 4 rg + i, channels 4 cg .. +3 (zero past
+// the chunk), as fp32
+template <typename T>
+__device__ __forceinline__ void load_rows4(const T* x, const ChunkRef& c, int H, float4 (&out)[4]) {
+    const int tid = threadIdx.x, rg = tid >> 5, cg = tid & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        out[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (r < c.len) out[i] = elem<T>::load4(x + ((c.t0 + r) * H + c.h) * D + 4 * cg);
     }
 }
 
 // ===================================================================
 // prep: a chunk's operands for the backward passes
 // ===================================================================
+// 69 KB, so two work-groups share a CU: buffers whose lives do not overlap
+// share LDS (the gate scan, then B; K e^-g and Q e^g, then the inverse)
 struct alignas(16) PrepLds {
-    float g[C * D];
-    bf16_t kg[C * LDD], kn[C * LDD], qg[C * LDD];
-    float bm[C * (C + 1)], mi[C * (C + 1)];
-    bf16_t tt[C * LDC];
+    bf16_t kg[C * LDD];
+    union {
+        struct { bf16_t kn[C * LDD], qg[C * LDD]; } a;
+        struct {
+            float mi[C * (C + 1)];
+            bf16_t tt[C * LDC];
+            float xs[3][16 * 17];      // one wave's product block of the inverse
+        } b;
+    } u1;
+    union {
+        struct { float scan[(C / 4) * D], tot[D]; } a;
+        float bm[C * (C + 1)];
+    } u2;
     float bs[C];
-    float xs[3][16 * 17];      // one wave's product block of the inverse
-    float gpart[4 * D];        // row-quarter totals of the gate scan
 };
 
 template <int GATE>
-__global__ __launch_bounds__(GT)
+__global__ __launch_bounds__(GT, 2)
 void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const float* __restrict__ la, const float* __restrict__ beta,
                      const int32_t* __restrict__ cu, int H, int c_lo, int L_b, float scale,
@@ -253,56 +289,48 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     float* oMinv = reinterpret_cast<float*>(out + kOffMinv);
     float* oGam = reinterpret_cast<float*>(out + kOffGam);
 
-    // k and q of the chunk (rows past it zero) load while the gates scan
-    float4 kr4[C * (D / 4) / GT], qr4[C * (D / 4) / GT];
-#pragma unroll
-    for (int x = 0; x < C * (D / 4) / GT; ++x) {
-        const int idx = tid + GT * x, r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
-        kr4[x] = qr4[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < c.len) {
-            const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
-            kr4[x] = elem<bf16_t>::load4(k + row);
-            qr4[x] = elem<bf16_t>::load4(q + row);
-        }
-    }
-    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs, sm.gpart);
-    __syncthreads();
+    // k and q of the thread's rows load while the gates scan
+    const int rg = tid >> 5, cg = tid & 31;
+    float4 kr4[4], qr4[4];
+    load_rows4(k, c, H, kr4);
+    load_rows4(q, c, H, qr4);
+    float g[4][4];
+    f32x4 G;
+    chunk_gates<GATE>(la, beta, c, H, sm.u2.a.scan, sm.u2.a.tot, sm.bs, g, G);
+    if (tid < D) oGam[tid] = gate_exp(sm.u2.a.tot[tid]);
     // gated keys and queries
 #pragma unroll
-    for (int x = 0; x < C * (D / 4) / GT; ++x) {
-        const int idx = tid + GT * x, r = idx / (D / 4), c0 = (idx % (D / 4)) * 4;
-        const float4 kv = kr4[x], qv = qr4[x];
-        const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
-        float kg[4], kn[4], qg[4], kd[4];
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i, c0 = 4 * cg;
+        const float kk[4] = {kr4[i].x, kr4[i].y, kr4[i].z, kr4[i].w};
+        const float qq[4] = {qr4[i].x, qr4[i].y, qr4[i].z, qr4[i].w};
+        f32x4 vkg, vkn, vqg, vkd;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float gv = sm.g[r * D + c0 + e], G = sm.g[(c.len - 1) * D + c0 + e];
-            const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
-            kg[e] = kk[e] * eg;
-            kn[e] = kk[e] * en;
-            qg[e] = qq[e] * eg;
-            kd[e] = kk[e] * ed;
+            const float gv = g[i][e];
+            const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G[e] - gv);
+            vkg[e] = kk[e] * eg;
+            vkn[e] = kk[e] * en;
+            vqg[e] = qq[e] * eg;
+            vkd[e] = kk[e] * ed;
         }
-        const f32x4 vkg = {kg[0], kg[1], kg[2], kg[3]}, vkn = {kn[0], kn[1], kn[2], kn[3]};
-        const f32x4 vqg = {qg[0], qg[1], qg[2], qg[3]}, vkd = {kd[0], kd[1], kd[2], kd[3]};
         put4t(sm.kg + r * LDD + c0, vkg);
-        put4t(sm.kn + r * LDD + c0, vkn);
-        put4t(sm.qg + r * LDD + c0, vqg);
+        put4t(sm.u1.a.kn + r * LDD + c0, vkn);
+        put4t(sm.u1.a.qg + r * LDD + c0, vqg);
         put4t(oKd + r * D + c0, vkd);
         put4t(oKg + r * D + c0, vkg);
         put4t(oQg + r * D + c0, scale * vqg);
     }
-    if (tid < D) oGam[tid] = gate_exp(sm.g[(c.len - 1) * D + tid]);
     __syncthreads();
     // B = Kg Kn^T (fp32) and scale P^T, P = lower(Qg Kn^T)
-    mm<4, 4, D, GT>(sm.kg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 4, D, GT>(sm.kg, LDD, sm.u1.a.kn, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
-            sm.bm[r * (C + 1) + s] = acc[i];
+            sm.u2.bm[r * (C + 1) + s] = acc[i];
         }
     });
-    mm<4, 4, D, GT>(sm.qg, LDD, sm.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 4, D, GT>(sm.u1.a.qg, LDD, sm.u1.a.kn, LDD, [&](int mi, int ni, f32x4 acc) {
         const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
         f32x4 x;
 #pragma unroll
@@ -324,12 +352,12 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             const int r = base + rr;
             float acc = 0.f;
 #pragma unroll
-            for (int ss = 0; ss < rr; ++ss) acc += sm.bm[r * (C + 1) + base + ss] * x[ss];
+            for (int ss = 0; ss < rr; ++ss) acc += sm.u2.bm[r * (C + 1) + base + ss] * x[ss];
             x[rr] = (r == col ? 1.f : 0.f) - sm.bs[r] * acc;
         }
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) sm.mi[(base + rr) * (C + 1) + col] = x[rr];
-        for (int r = 0; r < base; ++r) sm.mi[r * (C + 1) + col] = 0.f;
+        for (int rr = 0; rr < 16; ++rr) sm.u1.b.mi[(base + rr) * (C + 1) + col] = x[rr];
+        for (int r = 0; r < base; ++r) sm.u1.b.mi[r * (C + 1) + col] = 0.f;
     }
     __syncthreads();
     for (int I = 1; I < 4; ++I) {
@@ -341,35 +369,35 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     const int kc = 16 * K + 4 * kk + g4;
-                    const float a = sm.bs[row] * sm.bm[row * (C + 1) + kc];
-                    const float b = sm.mi[kc * (C + 1) + 16 * J + ln];
+                    const float a = sm.bs[row] * sm.u2.bm[row * (C + 1) + kc];
+                    const float b = sm.u1.b.mi[kc * (C + 1) + 16 * J + ln];
                     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
                 }
             }
-            float* xs = sm.xs[J];
+            float* xs = sm.u1.b.xs[J];
 #pragma unroll
             for (int i = 0; i < 4; ++i) xs[(4 * g4 + i) * 17 + ln] = acc[i];
             f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                const float a = sm.mi[row * (C + 1) + 16 * I + 4 * kk + g4];
+                const float a = sm.u1.b.mi[row * (C + 1) + 16 * I + 4 * kk + g4];
                 const float b = xs[(4 * kk + g4) * 17 + ln];
                 m = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, m, 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sm.mi[(16 * I + 4 * g4 + i) * (C + 1) + 16 * J + ln] = -m[i];
+            for (int i = 0; i < 4; ++i) sm.u1.b.mi[(16 * I + 4 * g4 + i) * (C + 1) + 16 * J + ln] = -m[i];
         }
         __syncthreads();
     }
     for (int idx = tid; idx < C * C; idx += GT) {
         const int r = idx / C, s = idx % C;
-        const float m = sm.mi[r * (C + 1) + s];
+        const float m = sm.u1.b.mi[r * (C + 1) + s];
         oMinv[idx] = m;
-        sm.tt[r * LDC + s] = bf(m * sm.bs[s]);     // T = Minv Diag(beta)
+        sm.u1.b.tt[r * LDC + s] = bf(m * sm.bs[s]);     // T = Minv Diag(beta)
     }
     __syncthreads();
     // -W^T, W = T Kg (Kg read by rows of K)
-    mm<4, 8, C, GT, kKc, kMc>(sm.tt, LDC, sm.kg, LDD, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 8, C, GT, kKc, kMc>(sm.u1.b.tt, LDC, sm.kg, LDD, [&](int mi, int ni, f32x4 acc) {
         put4t(oWt + (16 * ni + ln) * C + 16 * mi + 4 * g4, -acc);
     });
 }
@@ -567,7 +595,8 @@ struct alignas(16) GradBLds {
     float db[C];               // dbeta
     float dbp[4][C];           // dbeta_A per 16-column block, summed in order
     float hp[GT / 64][C];      // per-head gate: dlog_alpha per wave's channel block
-    float gpart[4 * D];        // row-quarter totals of the gate scan
+    float gscan[(C / 4) * D];  // the gate scan over row groups
+    float gtot[D];
 };
 union alignas(16) GradLds {
     GradALds a;
@@ -752,44 +781,40 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
     // =========================== phase B ===========================
     GradBLds& sm = sm_u.b;
-    // k and q of the chunk into registers while the gates load and scan,
-    // and Minv into LDS: one round of loads
+    // k and q of the thread's rows into registers while the gates load and
+    // scan (the prep's scan, so the same gate bits), and Minv into LDS
     float4 kr4[4], qr4[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int u = x * GT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        kr4[x] = qr4[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (r < c.len) {
-            const int64_t row = ((c.t0 + r) * H + c.h) * D + c0;
-            kr4[x] = elem<T>::load4(k + row);
-            qr4[x] = elem<T>::load4(q + row);
-        }
-    }
+    load_rows4(k, c, H, kr4);
+    load_rows4(q, c, H, qr4);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int u = tid + GT * x;
         put4t(sm.mv + (u / (C / 4)) * LDC + 4 * (u % (C / 4)), mvr[x]);
     }
-    load_gates<GATE, GT>(la, beta, c, H, sm.g, sm.bs, sm.gpart);
-    __syncthreads();
-    // gated keys and queries, row-major
+    {
+        float gr[4][4];
+        f32x4 Gr;
+        chunk_gates<GATE>(la, beta, c, H, sm.gscan, sm.gtot, sm.bs, gr, Gr);
+        // the gates for the final tiles, and the gated keys and queries
+        const int rg = tid >> 5, c0 = 4 * (tid & 31);
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int u = x * GT + tid, r = u / (D / 4), c0 = (u % (D / 4)) * 4;
-        const float kk[4] = {kr4[x].x, kr4[x].y, kr4[x].z, kr4[x].w};
-        const float qq[4] = {qr4[x].x, qr4[x].y, qr4[x].z, qr4[x].w};
-        const f32x4 gv = *reinterpret_cast<const f32x4*>(sm.g + r * D + c0);
-        f32x4 kg, kn, qg;
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            *reinterpret_cast<f32x4*>(sm.g + r * D + c0) = f32x4{gr[i][0], gr[i][1], gr[i][2], gr[i][3]};
+            const float kk[4] = {kr4[i].x, kr4[i].y, kr4[i].z, kr4[i].w};
+            const float qq[4] = {qr4[i].x, qr4[i].y, qr4[i].z, qr4[i].w};
+            f32x4 kg, kn, qg;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const float eg = gate_exp(gv[e]), en = gate_exp(-gv[e]);
-            kg[e] = kk[e] * eg;
-            kn[e] = kk[e] * en;
-            qg[e] = qq[e] * eg;
+            for (int e = 0; e < 4; ++e) {
+                const float eg = gate_exp(gr[i][e]), en = gate_exp(-gr[i][e]);
+                kg[e] = kk[e] * eg;
+                kn[e] = kk[e] * en;
+                qg[e] = qq[e] * eg;
+            }
+            put4t(sm.kg + r * LDT + c0, kg);
+            put4t(sm.kn + r * LDT + c0, kn);
+            put4t(sm.qg + r * LDT + c0, qg);
         }
-        put4t(sm.kg + r * LDT + c0, kg);
-        put4t(sm.kn + r * LDT + c0, kn);
-        put4t(sm.qg + r * LDT + c0, qg);
     }
     // k and q again, at this lane's positions of the final tiles: loaded
     // here, used after the triangular-system products
