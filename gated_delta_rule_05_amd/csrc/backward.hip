@@ -1026,7 +1026,24 @@ BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
     return l;
 }
 
-// the serial carry runs on a second stream of the caller's device, created
+// the device of the caller's stream is current for the call (the second
+// stream and the events must live on it); the previous device is restored
+struct DeviceOfStream {
+    int prev = -1;
+    hipError_t set(hipStream_t stream) {
+        hipError_t e = hipGetDevice(&prev);
+        if (e != hipSuccess || !stream) return e;
+        int dev = prev;
+        if ((e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+        return dev == prev ? hipSuccess : hipSetDevice(dev);
+    }
+    ~DeviceOfStream() {
+        int cur = -1;
+        if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+    }
+};
+
+// the serial carry runs on a second stream of the current device, created
 // once per device at the default priority and kept for the process
 hipError_t aux_stream(hipStream_t* out) {
     static std::mutex mu;
@@ -1095,8 +1112,11 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
         deblk[i] = reinterpret_cast<bf16_t*>(p);       p += up(l.deblk);
     }
     float* dstate = reinterpret_cast<float*>(p);
+    DeviceOfStream on_device;
+    hipError_t e = on_device.set(stream);
+    if (e != hipSuccess) return e;
     hipStream_t serial = nullptr;
-    hipError_t e = aux_stream(&serial);
+    e = aux_stream(&serial);
     if (e != hipSuccess) return e;
     CallEvents ev;
     if ((e = ev.create()) != hipSuccess) return e;
