@@ -13,13 +13,17 @@ marshals numpy arrays into it.
 
 The gradients live in ``kda_oracle_bwd.c``: the reverse-mode derivative of
 the same token loop, step by step in reverse order (``backward`` below).
+The fused input front-end's activations (``front_end``) and the chain rule
+through them (``front_end_backward``) are numpy, in float64.
 
 Pins (the tests that tie this oracle to something other than itself) live in
 ``tests/test_oracle_pins.py`` and, for the gradients,
 ``tests/test_oracle_bwd_pins.py``: a brute-force product of explicit transition
 matrices, the DeltaNet and Gated DeltaNet special cases, the beta = 0 closed
 form, the beta = 1 read-back, the basis-key closed form, linearity, the
-stability bound and a hand-derived worked example.
+stability bound and a hand-derived worked example; the front-end's chain
+rule is pinned by finite differences in
+``tests/test_oracle_front_bwd_pins.py``.
 """
 from __future__ import annotations
 
@@ -300,3 +304,41 @@ def front_end(q, k, gate_pre=None, beta_pre=None, gate_scale=1.0, l2norm=True, e
     if beta_pre is not None:
         beta = 1.0 / (1.0 + np.exp(-np.asarray(beta_pre, dtype=np.float64)))
     return q, k, la, beta
+
+
+def front_end_backward(q, k, gate_pre, beta_pre, dq, dk, dlog_alpha, dbeta, gate_scale=1.0,
+                       l2norm=True, eps=1e-6):
+    """Gradients through front_end, in float64: given the gradients with
+    respect to its outputs (normalised q and k, log_alpha, beta), those with
+    respect to its inputs (raw q and k, gate_pre, beta_pre).  By the chain
+    rule through each of its three maps:
+      x_n = x / n with n = max(||x||_2, eps): where ||x|| > eps the Jacobian
+        of x / ||x|| is (I - x_n x_n^T) / ||x||, so dx = (dx_n - x_n (x_n .
+        dx_n)) / n; where ||x|| <= eps, n is the constant eps and dx = dx_n / eps;
+      log_alpha = -c softplus(g): softplus' = sigmoid, so dg = -c sigmoid(g) dlog_alpha;
+      beta = sigmoid(y): sigmoid' = beta (1 - beta), so dy = beta (1 - beta) dbeta.
+    Without l2norm dq and dk pass through; a missing gate_pre / beta_pre
+    gives None for its gradient.  Returns (dq, dk, dgate_pre, dbeta_pre)."""
+    def unit_back(x, dxn):
+        x = np.asarray(x, dtype=np.float64)
+        dxn = np.asarray(dxn, dtype=np.float64)
+        nrm = np.linalg.norm(x, axis=-1, keepdims=True)
+        n = np.maximum(nrm, eps)
+        xn = x / n
+        proj = np.sum(xn * dxn, axis=-1, keepdims=True)
+        return np.where(nrm > eps, (dxn - xn * proj) / n, dxn / eps)
+
+    if l2norm:
+        dq_raw, dk_raw = unit_back(q, dq), unit_back(k, dk)
+    else:
+        dq_raw = np.asarray(dq, dtype=np.float64)
+        dk_raw = np.asarray(dk, dtype=np.float64)
+    dg = None
+    if gate_pre is not None:
+        g = np.asarray(gate_pre, dtype=np.float64)
+        dg = -gate_scale / (1.0 + np.exp(-g)) * np.asarray(dlog_alpha, dtype=np.float64)
+    dy = None
+    if beta_pre is not None:
+        b = 1.0 / (1.0 + np.exp(-np.asarray(beta_pre, dtype=np.float64)))
+        dy = b * (1.0 - b) * np.asarray(dbeta, dtype=np.float64)
+    return dq_raw, dk_raw, dg, dy
