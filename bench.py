@@ -148,7 +148,10 @@ def bench_backward(torch, kda, gen, inp, steps, warmup):
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
     grads = {}
 
+    # each call frees the previous call's gradients first, so the caching
+    # allocator hands the same memory back (no device allocation is timed)
     def run():
+        grads.clear()
         grads.update(kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do,
                                   cu_seqlens=inp["cu_seqlens"], workspace=ws, want_dh0=False))
 
@@ -170,7 +173,38 @@ def bench_backward(torch, kda, gen, inp, steps, warmup):
            "achieved_GBps": nbytes / (ms * 1e-3) / 1e9,
            "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
            "kernels": BACKWARD_KERNELS}
-    del ws, do
+    del ws
+    grads.clear()
+    torch.cuda.empty_cache()
+
+    # the same gradients through the fused input front-end: q and k taken
+    # as raw (normalised in the call), bf16 gate and beta pre-activations;
+    # the gradients come out with respect to those
+    gp = gen.normal(tuple(inp["log_alpha"].shape), 9, gen.LOG_ALPHA, "cuda", torch.bfloat16)
+    bp = gen.normal((T, H), 9, gen.BETA, "cuda", torch.bfloat16)
+    need_f = kda.backward_workspace_bytes(T, N, H, 128, 128, l2norm_qk=True, gate_pre=True,
+                                          beta_pre=True)
+    ws = torch.empty(need_f, dtype=torch.uint8, device="cuda")
+
+    def run_front():
+        grads.clear()
+        grads.update(kda.backward(inp["q"], inp["k"], inp["v"], None, None, do,
+                                  cu_seqlens=inp["cu_seqlens"], workspace=ws, want_dh0=False,
+                                  l2norm_qk=True, gate_pre=gp, gate_scale=0.05, beta_pre=bp))
+
+    run_front()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(2)]
+    for a0, a1 in evs:
+        a0.record(stream)
+        run_front()
+        a1.record(stream)
+    torch.cuda.synchronize()
+    ms_f = sum(a0.elapsed_time(a1) for a0, a1 in evs) / len(evs)
+    out["front_end"] = {"ms": ms_f, "tokens_per_s": T / (ms_f * 1e-3), "workspace_bytes": need_f,
+                        "vs_plain_pct": 100.0 * (ms_f / ms - 1.0),
+                        "kernels": "front_act_kernel + the backward above + front_chain_kernel"}
+    del ws, do, gp, bp
     grads.clear()
     torch.cuda.empty_cache()
     return out

@@ -74,7 +74,8 @@ class DecodeMultiOptions(ctypes.Structure):
 
 class BwdOptions(ctypes.Structure):
     """Mirror of kda_bwd_options."""
-    _fields_ = [("gate", ctypes.c_int32), ("block_chunks", ctypes.c_int32)]
+    _fields_ = [("gate", ctypes.c_int32), ("block_chunks", ctypes.c_int32),
+                ("front", FrontEnd)]
 
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
@@ -463,21 +464,32 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
 
 
 def backward_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
-                             dtype: int = DTYPE_BF16, gate="channel", block_chunks=0) -> int:
-    opts = BwdOptions(_gate_code(gate), block_chunks)
+                             dtype: int = DTYPE_BF16, gate="channel", block_chunks=0,
+                             l2norm_qk=False, gate_pre=False, beta_pre=False) -> int:
+    """The front-end flags say which parts the call will use (their tensors
+    are not needed here)."""
+    dummy = ctypes.c_void_p(16)
+    fe = FrontEnd(1 if l2norm_qk else 0, 1.0, dummy if gate_pre else None,
+                  dummy if beta_pre else None)
+    opts = BwdOptions(_gate_code(gate), block_chunks, fe)
     return int(load_library().kda_bwd_workspace_bytes(total_T, N, H, d_k, d_v, dtype,
                                                       ctypes.byref(opts)))
 
 
 def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, scale=None,
-             gate="channel", want_dh0=True, block_chunks=0, workspace=None):
+             gate="channel", want_dh0=True, block_chunks=0, workspace=None,
+             l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None):
     """Gradients of <o, do> + <hT, dhT> for the prefill on these inputs.
 
     Inputs as for prefill() (bf16 q, k, v with d_k = d_v = 128); do: [T, H,
     d_v] bf16, the adjoint of o; dhT: [N, H, d_k, d_v] fp32 or None (zeros).
     Returns a dict: dq, dk, dv (bf16, the shapes of q, k, v), dlog_alpha
     (fp32, the layout of log_alpha; None without a gate), dbeta [T, H]
-    fp32, dh0 [N, H, d_k, d_v] fp32 (None when want_dh0 is False)."""
+    fp32, dh0 [N, H, d_k, d_v] fp32 (None when want_dh0 is False).
+
+    The fused input front-end as for prefill(): with it, dq and dk are the
+    gradients with respect to the raw q and k, dlog_alpha with respect to
+    gate_pre (fp32, its layout) and dbeta with respect to beta_pre."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3:
@@ -493,8 +505,19 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
     _check(k, "k", (T, H, dk), dt, dev)
     _check(v, "v", (T, H, dv), dt, dev)
     _check(do, "do", (T, H, dv), dt, dev)
-    log_alpha, gcode = _check_gate(log_alpha, gate, (T, H), dk, dev)
-    _check(beta, "beta", (T, H), torch.float32, dev)
+    fe = front_end(l2norm_qk, gate_pre, gate_scale, beta_pre, (T, H), gate, dev)
+    if gate_pre is None:
+        log_alpha, gcode = _check_gate(log_alpha, gate, (T, H), dk, dev)
+        la_like = log_alpha
+    elif log_alpha is not None:
+        raise ValueError("log_alpha must be None with gate_pre")
+    else:
+        gcode = _gate_code(gate)
+        la_like = torch.empty(gate_pre.shape, dtype=torch.float32, device=dev)
+    if beta_pre is None:
+        _check(beta, "beta", (T, H), torch.float32, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None with beta_pre")
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
     _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
@@ -506,10 +529,10 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
     if scale is None:
         scale = 1.0 / math.sqrt(dk)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
-               dlog_alpha=None if log_alpha is None else torch.empty_like(log_alpha),
-               dbeta=torch.empty_like(beta),
+               dlog_alpha=None if la_like is None else torch.empty_like(la_like),
+               dbeta=torch.empty((T, H), dtype=torch.float32, device=dev),
                dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
-    opts = BwdOptions(gcode, block_chunks)
+    opts = BwdOptions(gcode, block_chunks, fe if fe is not None else FrontEnd())
     need = int(lib.kda_bwd_workspace_bytes(T, N, H, dk, dv, code, ctypes.byref(opts)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

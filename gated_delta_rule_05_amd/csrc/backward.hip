@@ -989,6 +989,111 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
 }
 
+// ===================================================================
+// the fused input front-end around the backward: its activations ahead of
+// the call (one 32-lane group per (token, head) row, 4 channels per lane,
+// the forward front-end's arithmetic), and the chain rule through them
+// after it, in place on the gradients:
+//   x_n = x / n, n = max(||x||, eps):  dx = (dx_n - x_n (x_n . dx_n)) / n
+//                                      (dx_n / eps below the floor)
+//   log_alpha = -c softplus(g):        dg = -c sigmoid(g) dlog_alpha
+//   beta = sigmoid(y):                 dy = beta (1 - beta) dbeta
+// ===================================================================
+constexpr int FT = 256;    // threads per block: 8 rows
+
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) x += __shfl_xor(x, m);
+    return x;
+}
+
+template <int GATE>
+__global__ __launch_bounds__(FT)
+void front_act_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, FrontEnd fe,
+                      int64_t rows, bf16_t* __restrict__ qn, bf16_t* __restrict__ kn,
+                      float* __restrict__ la, float* __restrict__ beta) {
+    const int64_t row = (static_cast<int64_t>(blockIdx.x) * FT + threadIdx.x) >> 5;
+    const int j = threadIdx.x & 31;
+    if (row >= rows) return;     // whole 32-lane groups leave together
+    if (fe.l2norm) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const bf16_t* x = (t == 0 ? q : k) + row * D + 4 * j;
+            const u32x2 w = *reinterpret_cast<const u32x2*>(x);
+            const float v[4] = {lo_bf(w[0]), hi_bf(w[0]), lo_bf(w[1]), hi_bf(w[1])};
+            float s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s2 += v[e] * v[e];
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(group_sum(s2)), kFrontEps));
+            *reinterpret_cast<u32x2*>((t == 0 ? qn : kn) + row * D + 4 * j) =
+                u32x2{pk(v[0] * inv, v[1] * inv), pk(v[2] * inv, v[3] * inv)};
+        }
+    }
+    if (fe.gate_pre) {
+        if constexpr (GATE == kGateChannel) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(fe.gate_pre + row * D + 4 * j);
+            const float x[4] = {lo_bf(w[0]), hi_bf(w[0]), lo_bf(w[1]), hi_bf(w[1])};
+            f32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = -fe.gate_scale * softplus_f32(x[e]);
+            *reinterpret_cast<f32x4*>(la + row * D + 4 * j) = o;
+        } else if (j == 0) {
+            la[row] = -fe.gate_scale * softplus_f32(bf16_to_f32(fe.gate_pre[row]));
+        }
+    }
+    if (fe.beta_pre && j == 0) beta[row] = sigmoid_f32(bf16_to_f32(fe.beta_pre[row]));
+}
+
+template <int GATE>
+__global__ __launch_bounds__(FT)
+void front_chain_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, FrontEnd fe,
+                        int64_t rows, bf16_t* __restrict__ dq, bf16_t* __restrict__ dk,
+                        float* __restrict__ dla, float* __restrict__ dbeta) {
+    const int64_t row = (static_cast<int64_t>(blockIdx.x) * FT + threadIdx.x) >> 5;
+    const int j = threadIdx.x & 31;
+    if (row >= rows) return;     // whole 32-lane groups leave together
+    if (fe.l2norm) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>((t == 0 ? q : k) + row * D + 4 * j);
+            bf16_t* gp = (t == 0 ? dq : dk) + row * D + 4 * j;
+            const u32x2 gw = *reinterpret_cast<const u32x2*>(gp);
+            const float v[4] = {lo_bf(w[0]), hi_bf(w[0]), lo_bf(w[1]), hi_bf(w[1])};
+            const float d[4] = {lo_bf(gw[0]), hi_bf(gw[0]), lo_bf(gw[1]), hi_bf(gw[1])};
+            float s2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s2 += v[e] * v[e];
+            const float nrm = __builtin_sqrtf(group_sum(s2));
+            const float inv = __builtin_amdgcn_rcpf(fmaxf(nrm, kFrontEps));
+            float p = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) p += v[e] * inv * d[e];
+            p = group_sum(p);
+            if (!(nrm > kFrontEps)) p = 0.f;            // below the floor n is constant
+            float o[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = (d[e] - v[e] * inv * p) * inv;
+            *reinterpret_cast<u32x2*>(gp) = u32x2{pk(o[0], o[1]), pk(o[2], o[3])};
+        }
+    }
+    if (fe.gate_pre) {
+        if constexpr (GATE == kGateChannel) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(fe.gate_pre + row * D + 4 * j);
+            const float x[4] = {lo_bf(w[0]), hi_bf(w[0]), lo_bf(w[1]), hi_bf(w[1])};
+            f32x4 g = *reinterpret_cast<const f32x4*>(dla + row * D + 4 * j);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) g[e] *= -fe.gate_scale * sigmoid_f32(x[e]);
+            *reinterpret_cast<f32x4*>(dla + row * D + 4 * j) = g;
+        } else if (j == 0) {
+            dla[row] *= -fe.gate_scale * sigmoid_f32(bf16_to_f32(fe.gate_pre[row]));
+        }
+    }
+    if (fe.beta_pre && j == 0) {
+        const float b = sigmoid_f32(bf16_to_f32(fe.beta_pre[row]));
+        dbeta[row] *= b * (1.f - b);
+    }
+}
+
 __global__ void bwd_init_kernel(const float* __restrict__ dhT, float* __restrict__ dstate,
                                 int64_t n4) {
     for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < n4;
@@ -1093,11 +1198,68 @@ int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
     return static_cast<int>(std::min<int64_t>(L, 64));
 }
 
-size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b) {
-    return bwd_layout(total_T, N, H, L_b).total;
+// the front-end's activated inputs: normalised q and k (bf16), log_alpha
+// and beta (fp32), each present when its part of the front-end is on
+struct FrontLayout {
+    size_t qk, la, beta, total;
+};
+FrontLayout front_layout(int64_t total_T, int32_t H, int gate, const FrontEnd& fe) {
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    const size_t rows = static_cast<size_t>(total_T) * H;
+    FrontLayout f;
+    f.qk = fe.l2norm ? rows * D * 2 : 0;
+    f.la = fe.gate_pre ? rows * (gate == kGateChannel ? D : 1) * 4 : 0;
+    f.beta = fe.beta_pre ? rows * 4 : 0;
+    f.total = 2 * up(f.qk) + up(f.la) + up(f.beta);
+    return f;
 }
 
+size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b, int gate,
+                           const FrontEnd& fe) {
+    return (fe.active() ? front_layout(total_T, H, gate, fe).total : 0) +
+           bwd_layout(total_T, N, H, L_b).total;
+}
+
+hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream);
+
 hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream) {
+    if (!a.fe.active()) return launch_backward_core(a, L_b, ws, stream);
+    // activations ahead, the recurrence's backward on them, the chain rule after
+    const FrontLayout f = front_layout(a.total_T, a.H, a.gate, a.fe);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+    uint8_t* p = static_cast<uint8_t*>(ws);
+    bf16_t* qn = reinterpret_cast<bf16_t*>(p);         p += up(f.qk);
+    bf16_t* kn = reinterpret_cast<bf16_t*>(p);         p += up(f.qk);
+    float* la = reinterpret_cast<float*>(p);           p += up(f.la);
+    float* be = reinterpret_cast<float*>(p);           p += up(f.beta);
+    BackwardArgs b = a;
+    b.fe = FrontEnd{};
+    if (a.fe.l2norm) { b.q = qn; b.k = kn; }
+    if (a.fe.gate_pre) b.log_alpha = la;
+    if (a.fe.beta_pre) b.beta = be;
+    const int64_t rows = a.total_T * a.H;
+    const unsigned blocks = static_cast<unsigned>((rows * 32 + FT - 1) / FT);
+    const bf16_t* q = static_cast<const bf16_t*>(a.q);
+    const bf16_t* k = static_cast<const bf16_t*>(a.k);
+    hipError_t e;
+    if (rows > 0) {
+        auto act = a.gate == kGateChannel ? front_act_kernel<kGateChannel> : front_act_kernel<kGateHead>;
+        hipLaunchKernelGGL(act, dim3(blocks), dim3(FT), 0, stream, q, k, a.fe, rows, qn, kn, la, be);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if ((e = launch_backward_core(b, L_b, p, stream)) != hipSuccess) return e;
+    if (rows > 0) {
+        auto chain = a.gate == kGateChannel ? front_chain_kernel<kGateChannel>
+                                            : front_chain_kernel<kGateHead>;
+        hipLaunchKernelGGL(chain, dim3(blocks), dim3(FT), 0, stream, q, k, a.fe, rows,
+                           static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk), a.dlog_alpha,
+                           a.dbeta);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream) {
     const BwdLayout l = bwd_layout(a.total_T, a.N, a.H, L_b);
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     uint8_t* p = static_cast<uint8_t*>(ws);

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 8;
+constexpr int kAbiVersion = 9;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -462,7 +462,14 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_
     if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16) return 0;
     int L_b;
     if (bwd_block_chunks(total_T, N, H, options, &L_b) != KDA_STATUS_OK) return 0;
-    return kda::bwd_workspace_bytes(total_T, N, H, L_b);
+    kda::FrontEnd fe;
+    bool la_needed, beta_needed;
+    Range r_gp, r_bp;
+    const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
+    if (check_front(options ? &options->front : nullptr, gate, nullptr, nullptr, total_T, H, d_k,
+                    &fe, &la_needed, &beta_needed, &r_gp, &r_bp) != KDA_STATUS_OK)
+        return 0;
+    return kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe);
 }
 
 int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -478,9 +485,15 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16) return KDA_STATUS_UNSUPPORTED;
     if (!std::isfinite(scale) || !cu_seqlens) return KDA_STATUS_INVALID_ARGUMENT;
     const bool any = total_T > 0;
-    if (any && (!q || !k || !v || !beta || !dO || !dq || !dk || !dv || !dbeta))
+    kda::FrontEnd fe;
+    bool la_needed, beta_needed;
+    Range r_gp, r_bp;
+    const int fs = check_front(options ? &options->front : nullptr, gate, log_alpha, beta, total_T,
+                               H, d_k, &fe, &la_needed, &beta_needed, &r_gp, &r_bp);
+    if (fs != KDA_STATUS_OK) return fs;
+    if (any && (!q || !k || !v || (beta_needed && !beta) || !dO || !dq || !dk || !dv || !dbeta))
         return KDA_STATUS_INVALID_ARGUMENT;
-    int gs = check_gate_ptr(gate, log_alpha, any);
+    int gs = la_needed ? check_gate_ptr(gate, log_alpha, any) : KDA_STATUS_OK;
     if (gs == KDA_STATUS_OK) gs = check_gate_ptr(gate, dlog_alpha, any);
     if (gs != KDA_STATUS_OK) return gs;
     if (gate == KDA_GATE_NONE) { log_alpha = nullptr; dlog_alpha = nullptr; }
@@ -491,14 +504,15 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     int L_b;
     const int bs = bwd_block_chunks(total_T, N, H, options, &L_b);
     if (bs != KDA_STATUS_OK) return bs;
-    const size_t need = kda::bwd_workspace_bytes(total_T, N, H, L_b);
+    const size_t need = kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe);
 
     // no output may overlap an input, another output or the workspace
     const Range inputs[] = {range_of(q, sz.qk_bytes),      range_of(k, sz.qk_bytes),
                             range_of(v, sz.v_bytes),       range_of(log_alpha, sz.la_bytes),
                             range_of(beta, sz.beta_bytes), range_of(cu_seqlens, (N + 1) * 4),
                             range_of(h0, h0 ? sz.state_bytes : 0),
-                            range_of(dO, sz.v_bytes),      range_of(dhT, dhT ? sz.state_bytes : 0)};
+                            range_of(dO, sz.v_bytes),      range_of(dhT, dhT ? sz.state_bytes : 0),
+                            r_gp,                          r_bp};
     const Range outputs[] = {range_of(dq, sz.qk_bytes),     range_of(dk, sz.qk_bytes),
                              range_of(dv, sz.v_bytes),      range_of(dlog_alpha, sz.la_bytes),
                              range_of(dbeta, sz.beta_bytes), range_of(dh0, dh0 ? sz.state_bytes : 0),
@@ -520,7 +534,7 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     a.q = q; a.k = k; a.v = v; a.log_alpha = log_alpha; a.beta = beta; a.h0 = h0;
     a.cu_seqlens = cu_seqlens; a.dO = dO; a.dhT = dhT;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
-    a.total_T = total_T; a.N = N; a.H = H; a.gate = gate; a.scale = scale;
+    a.total_T = total_T; a.N = N; a.H = H; a.gate = gate; a.scale = scale; a.fe = fe;
     if (kda::launch_backward(a, L_b, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_STATUS_HIP_ERROR;
     return KDA_STATUS_OK;

@@ -215,6 +215,8 @@ typedef struct kda_bwd_options {
     int32_t gate;                  /* a kda_gate (0 = KDA_GATE_CHANNEL) */
     int32_t block_chunks;          /* chunks of 64 tokens per backward block
                                       (0 = automatic) */
+    kda_front_end front;           /* the fused input front-end the forward
+                                      used (zero = none); see kda_bwd */
 } kda_bwd_options;
 
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
@@ -378,7 +380,10 @@ int kda_decode_multi(const void *q, const void *k, const void *v,
  * the start state of every chunk (one bf16 state per (chunk, head), so
  * 512 MiB per 16,384 head-chunks), the forward pass's operand block, and
  * two blocks of per-(chunk, head) backward operands (one filled while the
- * other is consumed).  0 for arguments kda_bwd would reject.
+ * other is consumed); with the front-end, also the activated inputs it
+ * produces (normalised q and k in bf16, log_alpha and beta in fp32, each
+ * when its part is on; only whether options->front's pointers are set
+ * matters here).  0 for arguments kda_bwd would reject.
  */
 size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
                                int32_t d_k, int32_t d_v, int32_t dtype,
@@ -408,6 +413,15 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * kda_bwd_workspace_bytes [WORKSPACE_TOO_SMALL].
  * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
  * adjoints, as in the forward pass.
+ * Front-end (options->front, as for kda_fwd_prefill_ex): q and k are the raw
+ * inputs when l2norm_qk is set, and dq, dk the gradients with respect to
+ * them; with gate_pre, log_alpha must be NULL and dlog_alpha (fp32, the
+ * gate's layout) receives the gradient with respect to gate_pre; with
+ * beta_pre, beta must be NULL and dbeta receives the gradient with respect
+ * to beta_pre.  The activations are computed once ahead of the backward
+ * (normalised q and k are stored in bf16), and the chain rule through them
+ * is applied to the gradients afterwards.  Requirements and errors as for
+ * kda_fwd_prefill_ex's front-end.
  * Streams: the serial state-adjoint pass runs on a second stream of the
  * device (created by the library on first use, default priority, kept for
  * the process), ordered against the caller's stream by events; all of the

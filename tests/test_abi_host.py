@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 8
+    assert kda.abi_version() == 9
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -392,3 +392,53 @@ SNAP = 2 * 4 * 128 * 128 * 4
 ])
 def test_prefill_snapshot_checks(snap, over, status):
     assert prefill_ex_call(1, 0, 0, 0, snap, **over) == status
+
+
+# kda_bwd with the front-end: (l2norm_qk, gate_scale, gate_pre, beta_pre);
+# every case fails before any HIP call
+def bwd_front_call(front, gate=0, **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
+                cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
+                do=addr(6), dhT=None, dq=addr(7), dk_=addr(8), dv_=addr(9), dla=addr(10),
+                dbeta=addr(11), dh0=addr(12), ws=addr(13), wsb=256, stream=None)
+    args.update(over)
+    opts = kda.BwdOptions(gate, 0, kda.FrontEnd(*front))
+    lib = kda.load_library()
+    return lib.kda_bwd(args["q"], args["k"], args["v"], args["la"], args["beta"], args["h0"],
+                       args["cu"], args["T"], args["N"], args["H"], args["dk"], args["dv"],
+                       args["dtype"], args["scale"], args["do"], args["dhT"], args["dq"],
+                       args["dk_"], args["dv_"], args["dla"], args["dbeta"], args["dh0"],
+                       args["ws"], args["wsb"], ctypes.byref(opts), args["stream"])
+
+
+@pytest.mark.parametrize("front,over,status", [
+    ((1, 0.0, None, None), {}, WS_SMALL),                           # normalisation only
+    ((0, 0.05, GP, BP), dict(la=None, beta=None), WS_SMALL),         # both activations
+    ((0, 0.05, GP, None), {}, INVALID),                              # log_alpha must be NULL
+    ((0, 0.05, None, BP), {}, INVALID),                              # beta must be NULL
+    ((0, 0.05, GP, None), dict(la=None, dla=None), INVALID),         # the gradient still needs dlog_alpha
+    ((0, -1.0, GP, None), dict(la=None), INVALID),                   # negative gate scale
+    ((0, 0.05, GP + 8, None), dict(la=None), MISALIGNED),            # per-channel: 16 bytes
+    ((0, 0.05, None, BP + 1), dict(beta=None), MISALIGNED),
+    ((0, 0.05, GP, BP), dict(la=None, beta=None, dla=addr(14, 64)), INVALID),   # dlog_alpha on gate_pre
+    ((0, 0.05, GP, BP), dict(la=None, beta=None, dbeta=addr(15)), INVALID),     # dbeta on beta_pre
+])
+def test_backward_front_end_checks(front, over, status):
+    assert bwd_front_call(front, **over) == status
+
+
+def test_backward_front_end_gate_none_rejected():
+    assert bwd_front_call((0, 0.05, GP, None), gate=2, la=None, dla=None) == INVALID
+
+
+def test_backward_front_end_workspace():
+    # the activated copies: q and k bf16 (normalisation), log_alpha fp32
+    # (per channel), beta fp32, each 256-byte aligned
+    T, N, H = 4096, 4, 16
+    base = kda.backward_workspace_bytes(T, N, H, 128, 128)
+    up = lambda x: (x + 255) // 256 * 256
+    assert kda.backward_workspace_bytes(T, N, H, 128, 128, l2norm_qk=True) == base + 2 * up(T * H * 256)
+    assert kda.backward_workspace_bytes(T, N, H, 128, 128, gate_pre=True) == base + up(T * H * 512)
+    assert kda.backward_workspace_bytes(T, N, H, 128, 128, gate="head", gate_pre=True,
+                                        beta_pre=True) == base + 2 * up(T * H * 4)
+    assert kda.backward_workspace_bytes(T, N, H, 128, 128, gate="none", gate_pre=True) == 0
