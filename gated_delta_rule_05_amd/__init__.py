@@ -70,7 +70,7 @@ class DecodeMultiOptions(ctypes.Structure):
     """Mirror of kda_decode_multi_options."""
     _fields_ = [("gate", ctypes.c_int32), ("num_states", ctypes.c_int32),
                 ("state_index", ctypes.c_void_p), ("lengths", ctypes.c_void_p),
-                ("write_state", ctypes.c_int32)]
+                ("write_state", ctypes.c_int32), ("front", FrontEnd)]
 
 class BwdOptions(ctypes.Structure):
     """Mirror of kda_bwd_options."""
@@ -403,7 +403,8 @@ def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel
 
 
 def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True,
-                 write_state=True, lengths=None, gate="channel", state_index=None):
+                 write_state=True, lengths=None, gate="channel", state_index=None,
+                 l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None):
     """m decode tokens per sequence in one pass over the states.
 
     q, k: [N, m, H, d_k]; v: [N, m, H, d_v] (bf16 or fp32); log_alpha:
@@ -415,7 +416,9 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
     applied tokens are written into ``out`` (allocated when None) and
     returned; with ``write_state`` S is advanced in place past the applied
     tokens.  Verify draft tokens with write_state=False, commit an accepted
-    prefix with outputs=False and lengths."""
+    prefix with outputs=False and lengths.  The fused input front-end per
+    token as for decode_step() (gate_pre in log_alpha's layout, beta_pre
+    [N, m, H] bf16)."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 4:
@@ -430,8 +433,17 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
     _check(q, "q", (N, m, H, dk), dt, dev)
     _check(k, "k", (N, m, H, dk), dt, dev)
     _check(v, "v", (N, m, H, dv), dt, dev)
-    log_alpha, gcode = _check_gate(log_alpha, gate, (N, m, H), dk, dev)
-    _check(beta, "beta", (N, m, H), torch.float32, dev)
+    fe = front_end(l2norm_qk, gate_pre, gate_scale, beta_pre, (N, m, H), gate, dev)
+    if gate_pre is None:
+        log_alpha, gcode = _check_gate(log_alpha, gate, (N, m, H), dk, dev)
+    elif log_alpha is not None:
+        raise ValueError("log_alpha must be None with gate_pre")
+    else:
+        gcode = _gate_code(gate)
+    if beta_pre is None:
+        _check(beta, "beta", (N, m, H), torch.float32, dev)
+    elif beta is not None:
+        raise ValueError("beta must be None with beta_pre")
     if state_index is None:
         _check(S, "S", (N, H, dk, dv), torch.float32, dev)
         nstates = N
@@ -454,7 +466,7 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
     opts = DecodeMultiOptions(gcode, nstates,
                               None if state_index is None else state_index.data_ptr(),
                               None if lengths is None else lengths.data_ptr(),
-                              1 if write_state else 0)
+                              1 if write_state else 0, fe if fe is not None else FrontEnd())
     st = lib.kda_decode_multi(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(S),
                               N, m, H, dk, dv, code, float(scale), _ptr(out),
                               ctypes.byref(opts), _stream(dev))

@@ -229,20 +229,24 @@ struct DecodeTok {
     float4 vv;
 };
 
-template <typename T, int DK, int DV, int GATE, bool INDEXED>
+// FRONT: the fused input front-end, per token as in decode_step_kernel
+// (activations at load; norms reduced with k . q and applied after the
+// reductions), so m tokens still equal m single steps bit for bit
+template <typename T, int DK, int DV, int GATE, bool INDEXED, bool FRONT>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NWV * 64))
 void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
                          const T* __restrict__ v, const float* __restrict__ log_alpha,
                          const float* __restrict__ beta, float* __restrict__ S,
                          T* __restrict__ o, float scale, int64_t nheads, int H, int m,
                          const int32_t* __restrict__ lengths, int write_state,
-                         const int32_t* __restrict__ state_index, int num_states)
+                         const int32_t* __restrict__ state_index, int num_states, FrontEnd fe)
 {
     using Sh = DecodeShape<DK, DV>;
     constexpr int LPR = Sh::LPR, RPI = Sh::RPI, NWV = Sh::NWV, ITERS = Sh::ITERS;
     using Tok = DecodeTok<ITERS>;
     __shared__ f32x4 red[2][NWV][2][LPR];
     __shared__ float red_kq[2][NWV];
+    __shared__ float red_nrm[FRONT ? 2 : 1][NWV][2];   // front-end: sum of k^2 and q^2
 
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -279,16 +283,23 @@ void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
             const int64_t tk = (n * m + i) * H + h;      // token row
             const T* qp = q + tk * DK;
             const T* kp = k + tk * DK;
-            const float la_head = GATE == kGateHead && log_alpha ? log_alpha[tk] : 0.f;
+            const bool pre = FRONT && fe.gate_pre;
+            const float la_head = GATE != kGateHead ? 0.f
+                                  : pre ? -fe.gate_scale * softplus_f32(bf16_to_f32(fe.gate_pre[tk]))
+                                  : log_alpha ? log_alpha[tk] : 0.f;
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
                 const int r = row0 + it * RPI;
-                if constexpr (GATE == kGateChannel) t.la[it] = log_alpha[tk * DK + r];
-                else t.la[it] = la_head;
+                if constexpr (GATE == kGateChannel) {
+                    t.la[it] = pre ? -fe.gate_scale * softplus_f32(bf16_to_f32(fe.gate_pre[tk * DK + r]))
+                                   : log_alpha[tk * DK + r];
+                } else {
+                    t.la[it] = la_head;
+                }
                 t.kv[it] = elem<T>::load(kp + r);
                 t.qv[it] = elem<T>::load(qp + r);
             }
-            t.b = beta[tk];
+            t.b = FRONT && fe.beta_pre ? sigmoid_f32(bf16_to_f32(fe.beta_pre[tk])) : beta[tk];
             t.vv = elem<T>::load4(v + tk * DV + 4 * cl);
         };
         Tok cur, nxt;
@@ -297,11 +308,15 @@ void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
             if (i + 1 < len) load_tok(nxt, i + 1);
             const int64_t tk = (n * m + i) * H + h;
             f32x4 rk = {0.f, 0.f, 0.f, 0.f}, rq = {0.f, 0.f, 0.f, 0.f};
-            float kq = 0.f;
+            float kq = 0.f, kk = 0.f, qq = 0.f;
 #pragma unroll
             for (int it = 0; it < ITERS; ++it) {
                 const float a = gate_exp(cur.la[it]);
                 kq += cur.kv[it] * cur.qv[it];
+                if constexpr (FRONT) {
+                    kk += cur.kv[it] * cur.kv[it];
+                    qq += cur.qv[it] * cur.qv[it];
+                }
                 s[it] *= a;
                 rk += cur.kv[it] * s[it];
                 rq += cur.qv[it] * s[it];
@@ -314,6 +329,10 @@ void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
                     rq[c] += __shfl_xor(rq[c], mk);
                 }
                 kq += __shfl_xor(kq, mk);
+                if constexpr (FRONT) {
+                    kk += __shfl_xor(kk, mk);
+                    qq += __shfl_xor(qq, mk);
+                }
             }
             if (NWV > 1) {
                 // double-buffered by a parity that flips per reduction: the
@@ -323,18 +342,40 @@ void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
                     red[par][wave][0][cl] = rk;
                     red[par][wave][1][cl] = rq;
                     if (lane == 0) red_kq[par][wave] = kq;
+                    if (FRONT && lane == 0) {
+                        red_nrm[FRONT ? par : 0][wave][0] = kk;
+                        red_nrm[FRONT ? par : 0][wave][1] = qq;
+                    }
                 }
                 __syncthreads();
                 rk = red[par][0][0][cl];
                 rq = red[par][0][1][cl];
                 kq = red_kq[par][0];
+                if constexpr (FRONT) {
+                    kk = red_nrm[par][0][0];
+                    qq = red_nrm[par][0][1];
+                }
 #pragma unroll
                 for (int w = 1; w < NWV; ++w) {
                     rk += red[par][w][0][cl];
                     rq += red[par][w][1][cl];
                     kq += red_kq[par][w];
+                    if constexpr (FRONT) {
+                        kk += red_nrm[par][w][0];
+                        qq += red_nrm[par][w][1];
+                    }
                 }
                 par ^= 1;
+            }
+            float ik = 1.f;                              // the key's normalisation
+            if constexpr (FRONT) {
+                if (fe.l2norm) {
+                    ik = 1.f / fmaxf(sqrtf(kk), kFrontEps);
+                    const float iq = 1.f / fmaxf(sqrtf(qq), kFrontEps);
+                    rk *= ik;
+                    rq *= iq;
+                    kq *= ik * iq;
+                }
             }
             const float b = cur.b;
             const float4 vv = cur.vv;
@@ -345,7 +386,11 @@ void decode_multi_kernel(const T* __restrict__ q, const T* __restrict__ k,
                 elem<T>::store4(o + tk * DV + 4 * cl, make_float4(oo[0], oo[1], oo[2], oo[3]));
             }
 #pragma unroll
-            for (int it = 0; it < ITERS; ++it) s[it] = s[it] + cur.kv[it] * e;
+            for (int it = 0; it < ITERS; ++it) {
+                float kn = cur.kv[it];
+                if constexpr (FRONT) kn *= ik;
+                s[it] = s[it] + kn * e;
+            }
             cur = nxt;
         }
         if (write_state && live && len > 0) {
@@ -378,12 +423,13 @@ static hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
         // the other's latencies (measured: m = 4 verify 271 -> 184 us at
         // 256 sequences x 32 heads, d = 128)
         const int64_t mgrid = std::min<int64_t>(nheads, 2 * grid);
-        hipLaunchKernelGGL((decode_multi_kernel<T, DK, DV, GATE, INDEXED>),
-                           dim3(static_cast<unsigned>(mgrid)), dim3(threads), 0, stream,
+        auto kern = a.fe.active() ? decode_multi_kernel<T, DK, DV, GATE, INDEXED, true>
+                                  : decode_multi_kernel<T, DK, DV, GATE, INDEXED, false>;
+        hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(mgrid)), dim3(threads), 0, stream,
                            static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                            static_cast<const T*>(a.v), a.log_alpha, a.beta, a.S,
                            static_cast<T*>(a.o), a.scale, nheads, a.H, a.m, a.lengths,
-                           a.write_state ? 1 : 0, a.state_index, a.num_states);
+                           a.write_state ? 1 : 0, a.state_index, a.num_states, a.fe);
         return hipGetLastError();
     }
     return a.fe.active() ? launch_step_f<T, DK, DV, GATE, INDEXED, true>(a, grid, threads, stream)

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 9;
+constexpr int kAbiVersion = 10;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -430,7 +430,8 @@ int kda_decode_multi(const void* q, const void* k, const void* v, const float* l
     return decode_call(q, k, v, log_alpha, beta, S, N, m, H, d_k, d_v, dtype, scale, o, gate,
                        index, options ? options->num_states : 0,
                        options ? options->lengths : nullptr,
-                       options ? options->write_state != 0 : true, nullptr, stream);
+                       options ? options->write_state != 0 : true,
+                       options ? &options->front : nullptr, stream);
 }
 
 int kda_decode_step(const void* q, const void* k, const void* v, const float* log_alpha,

@@ -208,6 +208,8 @@ typedef struct kda_decode_multi_options {
                                       overwritten with the state after its
                                       applied tokens (left as it was when it
                                       applies none); zero: S is only read */
+    kda_front_end front;           /* the fused input front-end, per token
+                                      (zero = none); as for kda_decode_step_ex */
 } kda_decode_multi_options;
 
 /* Options of kda_bwd (zero-initialise for defaults). */

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 9
+    assert kda.abi_version() == 10
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"

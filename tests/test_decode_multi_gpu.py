@@ -136,3 +136,49 @@ def test_state_pool(dtype, d, gate):
     owned = set(int(slots[n]) for n in live)
     free = torch.tensor([x for x in range(M) if x not in owned], device=DEV)
     assert torch.equal(pool[free], pool0[free])
+
+
+# ---------------------------------------------------------------------------
+# the fused input front-end, per token
+# ---------------------------------------------------------------------------
+C_GATE = 0.05
+
+
+def raw_tokens(N, m, H, d, dtype, gate, seed):
+    """Raw q and k, bf16 gate and beta pre-activations, [N, m, H, .]."""
+    dt = gen.torch_dtype(dtype)
+    gshape = (N, m, H, d) if gate == "channel" else (N, m, H)
+    return dict(q=gen.normal((N, m, H, d), seed, gen.Q, DEV, dt, std=3.0),
+                k=gen.normal((N, m, H, d), seed, gen.K, DEV, dt, std=0.5),
+                v=gen.normal((N, m, H, d), seed, gen.V, DEV, dt),
+                gp=gen.normal(gshape, seed, gen.LOG_ALPHA, DEV, torch.bfloat16),
+                bp=gen.normal((N, m, H), seed, gen.BETA, DEV, torch.bfloat16))
+
+
+@pytest.mark.parametrize("dtype,d,gate,m", [("bf16", 128, "channel", 4), ("f32", 64, "head", 3),
+                                            ("bf16", 32, "channel", 5)])
+def test_front_end_matches_oracle_and_single_steps(dtype, d, gate, m):
+    """With every part of the front-end: the outputs and the committed states
+    against the oracle's activations fed to its recurrence, and bit for bit
+    against m single front-end decode steps."""
+    N, H = 29, 3
+    t = raw_tokens(N, m, H, d, dtype, gate, 230 + m)
+    S = gen.decode_state(N, H, d, d, std=0.05, seed=231, device=DEV)
+    S0 = S.clone()
+    fe = dict(l2norm_qk=True, gate_pre=t["gp"], gate_scale=C_GATE, beta_pre=t["bp"])
+    o = kda.decode_multi(t["q"], t["k"], t["v"], None, None, S, gate=gate, **fe)
+    qn, kn, la, b = oracle.front_end(host(t["q"]), host(t["k"]), host(t["gp"]), host(t["bp"]),
+                                     gate_scale=C_GATE)
+    o_ref, S_ref = oracle.decode_multi(qn, kn, host(t["v"]), la, b, host(S0))
+    eo, es = rel_err(host(o), o_ref), rel_err(host(S), S_ref)
+    report("decode multi front-end %s d=%d %s m=%d" % (dtype, d, gate, m), o=eo, S=es)
+    assert eo <= tol_for(dtype) and es <= tol_for(dtype)
+    # m single steps with the same front-end
+    S1 = S0.clone()
+    for i in range(m):
+        oi = kda.decode_step(t["q"][:, i].contiguous(), t["k"][:, i].contiguous(),
+                             t["v"][:, i].contiguous(), None, None, S1, gate=gate,
+                             l2norm_qk=True, gate_pre=t["gp"][:, i].contiguous(),
+                             gate_scale=C_GATE, beta_pre=t["bp"][:, i].contiguous())
+        assert torch.equal(oi, o[:, i]), i
+    assert torch.equal(S1, S)
