@@ -174,20 +174,13 @@ __device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
 }
 
 
-// Cumulative gates of a chunk at the thread's 4 rows 4 rg + i and 4
-// channels 4 cg + j (rg = tid / 32, cg = tid % 32, all GT threads): each
-// thread sums down its own rows, then a scan over the 16 row groups adds the
-// groups before.  Rows past the chunk add zero, so they repeat the last row,
-// and G (the chunk's total per channel) equals the last row's value.  Beta
-// of the rows into bs (0 past the chunk).  scan: 16 x D floats, tot: D
-// floats, both LDS; two barriers inside.
+// the raw gates of the thread's 4 x 4 block (zero past the chunk), and
+// beta of row tid (tid < C; 0 past the chunk)
 template <int GATE>
-__device__ __forceinline__ void chunk_gates(const float* la, const float* beta, const ChunkRef& c,
-                                            int H, float* scan, float* tot, float* bs,
-                                            float (&g)[4][4], f32x4& G) {
-    static_assert(GT == (C / 4) * (D / 4), "one thread per 4 x 4 block of the chunk");
+__device__ __forceinline__ void load_gate_block(const float* la, const float* beta,
+                                                const ChunkRef& c, int H, f32x4 (&raw)[4],
+                                                float& b) {
     const int tid = threadIdx.x, rg = tid >> 5, cg = tid & 31;
-    f32x4 raw[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int r = 4 * rg + i;
@@ -202,7 +195,16 @@ __device__ __forceinline__ void chunk_gates(const float* la, const float* beta, 
             }
         }
     }
-    if (tid < C) bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
+    b = tid < C && tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
+}
+
+// the scan of chunk_gates over a thread's raw 4 x 4 block (two barriers)
+__device__ __forceinline__ void scan_gate_block(const f32x4 (&raw)[4], float b, float* scan,
+                                                float* tot, float* bs, float (&g)[4][4],
+                                                f32x4& G) {
+    static_assert(GT == (C / 4) * (D / 4), "one thread per 4 x 4 block of the chunk");
+    const int tid = threadIdx.x, rg = tid >> 5, cg = tid & 31;
+    if (tid < C) bs[tid] = b;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         float run = 0.f;
@@ -231,6 +233,23 @@ __device__ __forceinline__ void chunk_gates(const float* la, const float* beta, 
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) g[i][j] += off[j];
+}
+
+// Cumulative gates of a chunk at the thread's 4 rows 4 rg + i and 4
+// channels 4 cg + j (rg = tid / 32, cg = tid % 32, all GT threads): each
+// thread sums down its own rows, then a scan over the 16 row groups adds the
+// groups before.  Rows past the chunk add zero, so they repeat the last row,
+// and G (the chunk's total per channel) equals the last row's value.  Beta
+// of the rows into bs (0 past the chunk).  scan: 16 x D floats, tot: D
+// floats, both LDS; two barriers inside.
+template <int GATE>
+__device__ __forceinline__ void chunk_gates(const float* la, const float* beta, const ChunkRef& c,
+                                            int H, float* scan, float* tot, float* bs,
+                                            float (&g)[4][4], f32x4& G) {
+    f32x4 raw[4];
+    float b;
+    load_gate_block<GATE>(la, beta, c, H, raw, b);
+    scan_gate_block(raw, b, scan, tot, bs, g, G);
 }
 
 // k or q of the thread's 4 rows 4 rg + i, channels 4 cg .. +3 (zero past
@@ -654,6 +673,14 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // 16 mi + 4 g4 + i, mi = wave / 4 + 2x, column s2) for dbeta_T
     f32x4 mvr[2];
     float mvd[2][4];
+    // phase B's inputs load with phase A's: k and q of this thread's block
+    // of rows and channels, its raw gates, and beta
+    float4 kr4[4], qr4[4];
+    f32x4 graw[4];
+    float bsv;
+    load_rows4(k, c, H, kr4);
+    load_rows4(q, c, H, qr4);
+    load_gate_block<GATE>(la, beta, c, H, graw, bsv);
     {
         const int s2 = 16 * (wave % 4) + ln;
 #pragma unroll
@@ -781,11 +808,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
     // =========================== phase B ===========================
     GradBLds& sm = sm_u.b;
-    // k and q of the thread's rows into registers while the gates load and
-    // scan (the prep's scan, so the same gate bits), and Minv into LDS
-    float4 kr4[4], qr4[4];
-    load_rows4(k, c, H, kr4);
-    load_rows4(q, c, H, qr4);
+    // Minv into LDS; the gates scanned as in the prep (the same gate bits)
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         const int u = tid + GT * x;
@@ -794,7 +817,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     {
         float gr[4][4];
         f32x4 Gr;
-        chunk_gates<GATE>(la, beta, c, H, sm.gscan, sm.gtot, sm.bs, gr, Gr);
+        scan_gate_block(graw, bsv, sm.gscan, sm.gtot, sm.bs, gr, Gr);
         // the gates for the final tiles, and the gated keys and queries
         const int rg = tid >> 5, c0 = 4 * (tid & 31);
 #pragma unroll
