@@ -139,3 +139,18 @@ def test_backward_long_t1m_last_window():
     report("backward long_t1m last %d tokens, heads %s" % (W, heads), **errs)
     for key, e in errs.items():
         assert e <= TOL, (key, e)
+
+
+def test_backward_on_a_side_stream():
+    """The call on a non-default stream (the library forks its serial pass
+    onto a second stream of that stream's device and joins back): the same
+    bits as on the default stream, complete once that stream is done."""
+    inp = case(LENS, 2, 350)
+    base = gpu(inp, "channel")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        other = gpu(inp, "channel")
+    side.synchronize()
+    for key, x in base.items():
+        assert torch.equal(x, other[key]), key
