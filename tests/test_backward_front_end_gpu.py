@@ -7,7 +7,8 @@ front_end activations (fp64), its gradient oracle on them, and its chain
 rule through the front-end (oracle.front_end_backward), all on the same
 stored inputs.  Cases: each part of the front-end on its own and all
 together, per-channel and per-head gates, a ragged packed batch with
-empty and one-token sequences, non-zero h0 and dhT.
+empty and one-token sequences, non-zero h0 and dhT; normalisation alone
+with no gate; an all-empty batch (dh0 = dhT).
 
 Bar: max-relative error <= 2e-2 per gradient tensor, the backward's bar.
 """
@@ -91,3 +92,37 @@ def test_backward_front_end(parts, gate):
     report("backward front-end %s %s" % (gate, parts), **errs)
     for key, e in errs.items():
         assert e <= TOL, (key, e)
+
+
+def test_backward_front_end_no_gate():
+    """Normalisation only, with no gate at all (DeltaNet): the chain rule
+    through the normalisation alone."""
+    parts = (True, False, False)
+    inp = case(parts, "channel", 510)
+    g = kda.backward(inp["q"], inp["k"], inp["v"], None, inp["beta"], inp["do"], h0=inp["h0"],
+                     dhT=inp["dhT"], cu_seqlens=inp["cu"], gate="none", l2norm_qk=True)
+    assert g["dlog_alpha"] is None
+    q, k = host(inp["q"]), host(inp["k"])
+    qn, kn, _, _ = oracle.front_end(q, k)
+    cu = inp["cu"].cpu().numpy().astype(np.int64)
+    r = oracle.backward(qn, kn, host(inp["v"]), None, host(inp["beta"]), host(inp["do"]),
+                        h0=host(inp["h0"]), dhT=host(inp["dhT"]), cu_seqlens=cu)
+    dq, dk, _, _ = oracle.front_end_backward(q, k, None, None, r["dq"], r["dk"], None, None)
+    errs = {"dq": rel_err(host(g["dq"]), dq), "dk": rel_err(host(g["dk"]), dk),
+            "dv": rel_err(host(g["dv"]), r["dv"]), "dbeta": rel_err(host(g["dbeta"]), r["dbeta"]),
+            "dh0": rel_err(host(g["dh0"]), r["dh0"])}
+    report("backward front-end, no gate", **errs)
+    for key, e in errs.items():
+        assert e <= TOL, (key, e)
+
+
+def test_backward_front_end_empty_batch():
+    """Sequences with no tokens: nothing to normalise or activate; dh0 = dhT."""
+    H, d = 2, 128
+    cu = torch.zeros(4, dtype=torch.int32, device=DEV)
+    z = lambda *s: torch.empty(s, dtype=torch.bfloat16, device=DEV)
+    dhT = gen.normal((3, H, d, d), 520, gen.DHT, DEV, torch.float32, std=0.1)
+    g = kda.backward(z(0, H, d), z(0, H, d), z(0, H, d), None, None, z(0, H, d), dhT=dhT,
+                     cu_seqlens=cu, l2norm_qk=True, gate_pre=z(0, H, d), gate_scale=C_GATE,
+                     beta_pre=z(0, H))
+    assert torch.equal(g["dh0"], dhT)
