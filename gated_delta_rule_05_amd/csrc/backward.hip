@@ -456,6 +456,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     constexpr int R = D / kCarryTile;
     const int pair = blockIdx.x / R, tile = blockIdx.x % R;
     const int n = pair / H, h = pair % H;
+    if (n >= N) return;            // the grid is exactly N * H * R work-groups
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
     // 8 waves: wave w owns value columns 16 (w % 4) .. +15 of the tile and
     // key rows 64 (w / 4) .. +63 of the state
