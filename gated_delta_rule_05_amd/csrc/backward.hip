@@ -55,7 +55,8 @@ namespace {
 constexpr int C = 64;          // chunk rows
 constexpr int D = 128;         // d_k = d_v
 constexpr int NT = 256;        // default work-group size of the LDS helpers
-constexpr int GT = 512;        // threads of the chunk-parallel kernels: 8 waves, 2 per SIMD
+constexpr int GT = 512;        // threads of the prep and the carry: 8 waves, 2 per SIMD
+constexpr int GG = 1024;       // threads of the gradient kernel: 16 waves, 4 per SIMD
 constexpr int LDD = D + 8;     // padded LDS row of a [.][D] bf16 matrix
 constexpr int LDC = C + 8;     // padded LDS row of a [.][C] bf16 matrix
 constexpr int kCarryTile = 64; // value columns per carry work-group
@@ -204,6 +205,7 @@ __device__ __forceinline__ void scan_gate_block(const f32x4 (&raw)[4], float b, 
                                                 f32x4& G) {
     static_assert(GT == (C / 4) * (D / 4), "one thread per 4 x 4 block of the chunk");
     const int tid = threadIdx.x, rg = tid >> 5, cg = tid & 31;
+    const bool own = tid < GT;    // a larger work-group's other threads only pass the barriers
     if (tid < C) bs[tid] = b;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -214,7 +216,7 @@ __device__ __forceinline__ void scan_gate_block(const f32x4 (&raw)[4], float b, 
             g[i][j] = run;
         }
     }
-    *reinterpret_cast<f32x4*>(scan + rg * D + 4 * cg) = f32x4{g[3][0], g[3][1], g[3][2], g[3][3]};
+    if (own) *reinterpret_cast<f32x4*>(scan + rg * D + 4 * cg) = f32x4{g[3][0], g[3][1], g[3][2], g[3][3]};
     __syncthreads();
     if (tid < D) {
         float run = 0.f;
@@ -227,7 +229,8 @@ __device__ __forceinline__ void scan_gate_block(const f32x4 (&raw)[4], float b, 
         tot[tid] = run;
     }
     __syncthreads();
-    const f32x4 off = *reinterpret_cast<const f32x4*>(scan + rg * D + 4 * cg);
+    const f32x4 off = own ? *reinterpret_cast<const f32x4*>(scan + rg * D + 4 * cg)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
     G = *reinterpret_cast<const f32x4*>(tot + 4 * cg);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -602,7 +605,7 @@ struct alignas(16) GradALds {
     bf16_t dol[C * LDD];       // dO
     bf16_t mvb[C * LDC];       // Minv Diag(beta)
     float bs[C];
-    float dgp[4][D];           // dgamma over four quarters of the value columns
+    float dgp[GG / D][D];      // dgamma over eight parts of the value columns
 };
 struct alignas(16) GradBLds {
     float g[C * D];            // cumulative gates
@@ -614,7 +617,9 @@ struct alignas(16) GradBLds {
     float bs[C];
     float db[C];               // dbeta
     float dbp[4][C];           // dbeta_A per 16-column block, summed in order
-    float hp[GT / 64][C];      // per-head gate: dlog_alpha per wave's channel block
+    float hp[D / 16][C];       // per-head gate: dlog_alpha per channel block
+    float ftot[4][D];          // dlog_alpha: per row block and channel, the sum of dg
+    float fdg[2][D];           // ... and the two halves of dG's sum over the rows
     float gscan[(C / 4) * D];  // the gate scan over row groups
     float gtot[D];
 };
@@ -645,7 +650,7 @@ __device__ __forceinline__ const bf16_t* recorded_state(const ChunkRef& c, const
 }
 
 template <typename T, int GATE>
-__global__ __launch_bounds__(GT)
+__global__ __launch_bounds__(GG)
 void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dsblk,
                      const bf16_t* __restrict__ deblk, const bf16_t* __restrict__ sall,
                      const float* __restrict__ h0, const T* __restrict__ q,
@@ -655,9 +660,9 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                      T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
                      float* __restrict__ dla, float* __restrict__ dbeta)
 {
-    constexpr int W = GT / 64;                 // waves
+    constexpr int W = GG / 64;                 // waves: four per SIMD
     __shared__ GradLds sm_u;
-    __shared__ float s_dgam[D], s_dbT[2][C];   // phase A -> phase B
+    __shared__ float s_dgam[D], s_dbT[4][C];   // phase A -> phase B
     ChunkRef c;
     if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
@@ -666,52 +671,46 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     const float* S0f = c.j == 0 && h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState
                                       : nullptr;
 
-    // tiles kept in registers: tile x of this wave is t = wave + 8x
-    f32x4 rKgW[4], rQgS[4], rKd[4];   // [C][D] terms, 4 x 8 tiles (row block x, column block wave)
-    f32x4 rT[2], rP[2];               // [C][C] terms, 4 x 4 tiles
-    // fp32 Minv, loaded with the first round and used later: the rows this
-    // thread stages (twice), and the entries of this wave's dT tiles (row
-    // 16 mi + 4 g4 + i, mi = wave / 4 + 2x, column s2) for dbeta_T
-    f32x4 mvr[2];
-    float mvd[2][4];
-    // phase B's inputs load with phase A's: k and q of this thread's block
-    // of rows and channels, its raw gates, and beta
-    float4 kr4[4], qr4[4];
+    // tiles kept in registers (tile x of this wave is t = wave + 16x):
+    // [C][D] terms, 4 x 8 tiles: row blocks wave / 8 + 2x, column block
+    // wave % 8; [C][C] terms, 4 x 4 tiles: row block wave / 4, column block
+    // wave % 4
+    f32x4 rKgW[2], rQgS[2], rKd[2];
+    f32x4 rT[1], rP[1];
+    // fp32 Minv, loaded with the first round and used later: the row this
+    // thread stages (twice), and the entries of this wave's dT tile (row
+    // 16 (wave / 4) + 4 g4 + i, column s2) for dbeta_T
+    f32x4 mvr;
+    float mvd[4];
+    // phase B's gates load with phase A's inputs: this thread's block of
+    // raw gates, and beta (threads past the 512 blocks of the chunk hold
+    // zeros and load nothing)
     f32x4 graw[4];
     float bsv;
-    load_rows4(k, c, H, kr4);
-    load_rows4(q, c, H, qr4);
     load_gate_block<GATE>(la, beta, c, H, graw, bsv);
     {
-        const int s2 = 16 * (wave % 4) + ln;
+        const int s2 = 16 * (wave % 4) + ln, mi = wave / 4;
+        mvr = *reinterpret_cast<const f32x4*>(mvg + (tid / (C / 4)) * C + 4 * (tid % (C / 4)));
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int u = tid + GT * x;
-            mvr[x] = *reinterpret_cast<const f32x4*>(mvg + (u / (C / 4)) * C + 4 * (u % (C / 4)));
-            const int mi = wave / 4 + 2 * x;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                mvd[x][i] = mvg[(16 * mi + 4 * g4 + i) * C + s2];
-            }
-        }
+        for (int i = 0; i < 4; ++i) mvd[i] = mvg[(16 * mi + 4 * g4 + i) * C + s2];
     }
     // =========================== phase A ===========================
     {
         GradALds& sm = sm_u.a;
         // ---- one round of loads, each matrix in its own layout: S^T, dS',
         //      Kg, V, dE, dO, beta, Minv Diag(beta)
-        if (c.j == 0) stage_f32_t<GT>(S0f, D, sm.st, LDD);
-        else copy_rows<GT>(sm.st, LDD, recorded_state(c, sall, cu, H), D, D);
-        copy_rows<GT>(sm.dsl, LDD, dsblk + c.slot * kState, D, D);
-        copy_rows<GT>(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
-        copy_rows<GT>(sm.de, LDD, deblk + c.slot * (static_cast<int64_t>(C) * D), C, D);
-        for (int u = tid; u < C * (D / 8); u += GT) {
+        if (c.j == 0) stage_f32_t<GG>(S0f, D, sm.st, LDD);
+        else copy_rows<GG>(sm.st, LDD, recorded_state(c, sall, cu, H), D, D);
+        copy_rows<GG>(sm.dsl, LDD, dsblk + c.slot * kState, D, D);
+        copy_rows<GG>(sm.kg, LDD, reinterpret_cast<const bf16_t*>(sp + kOffKg), C, D);
+        copy_rows<GG>(sm.de, LDD, deblk + c.slot * (static_cast<int64_t>(C) * D), C, D);
+        for (int u = tid; u < C * (D / 8); u += GG) {
             const int r = u / (D / 8), c8 = (u % (D / 8)) * 8;
             u32x4 x = {0u, 0u, 0u, 0u};
             if (r < c.len) x = *reinterpret_cast<const u32x4*>(dO + ((c.t0 + r) * H + c.h) * D + c8);
             *reinterpret_cast<u32x4*>(sm.dol + r * LDD + c8) = x;
         }
-        for (int u = tid; u < C * (D / 4); u += GT) {
+        for (int u = tid; u < C * (D / 4); u += GG) {
             const int r = u / (D / 4), c0 = (u % (D / 4)) * 4;
             float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
             if (r < c.len) x = elem<T>::load4(v + ((c.t0 + r) * H + c.h) * D + c0);
@@ -719,15 +718,13 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         }
         if (tid < C) sm.bs[tid] = tid < c.len ? beta[(c.t0 + tid) * H + c.h] : 0.f;
         __syncthreads();
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int u = tid + GT * x, r = u / (C / 4), s0 = (u % (C / 4)) * 4;
-            const f32x4 m = mvr[x];
-            put4t(sm.mvb + r * LDC + s0, f32x4{m[0] * sm.bs[s0], m[1] * sm.bs[s0 + 1],
-                                               m[2] * sm.bs[s0 + 2], m[3] * sm.bs[s0 + 3]});
+        {
+            const int r = tid / (C / 4), s0 = (tid % (C / 4)) * 4;
+            put4t(sm.mvb + r * LDC + s0, f32x4{mvr[0] * sm.bs[s0], mvr[1] * sm.bs[s0 + 1],
+                                               mvr[2] * sm.bs[s0 + 2], mvr[3] * sm.bs[s0 + 3]});
         }
         // ---- R = V - Kg S (B = S^T rows)
-        mm<4, 8, D, GT>(sm.kg, LDD, sm.st, LDD, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, D, GG>(sm.kg, LDD, sm.st, LDD, [&](int mi, int ni, f32x4 acc) {
             const int r0 = 16 * mi + 4 * g4, col = 16 * ni + ln;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -736,47 +733,50 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             }
         });
         // ---- dgamma = rowsum(dS' . S) from the bf16 records, summed in fp32:
-        //      thread (quarter, key c) takes value columns 32 quarter .. +31
+        //      thread (part, key c) takes value columns 16 part .. +15
         {
-            const int ch = tid & (D - 1), quarter = tid >> 7;
-            float part = 0.f;
+            const int ch = tid & (D - 1), part = tid >> 7;
+            float acc = 0.f;
 #pragma unroll
-            for (int x = 0; x < 32; x += 8) {
-                const int j0 = 32 * quarter + x;
+            for (int x = 0; x < 16; x += 8) {
+                const int j0 = 16 * part + x;
                 const u32x4 dw = *reinterpret_cast<const u32x4*>(sm.dsl + ch * LDD + j0);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    part += lo_bf(dw[e]) * bf16_to_f32(sm.st[(j0 + 2 * e) * LDD + ch]) +
-                            hi_bf(dw[e]) * bf16_to_f32(sm.st[(j0 + 2 * e + 1) * LDD + ch]);
+                    acc += lo_bf(dw[e]) * bf16_to_f32(sm.st[(j0 + 2 * e) * LDD + ch]) +
+                           hi_bf(dw[e]) * bf16_to_f32(sm.st[(j0 + 2 * e + 1) * LDD + ch]);
             }
-            sm.dgp[quarter][ch] = part;
+            sm.dgp[part][ch] = acc;
         }
         __syncthreads();
         // ---- E = (Minv Diag(beta)) R over Kg (R read by rows of K)
         bf16_t* E = sm.kg;
-        mm<4, 8, C, GT, kKc, kMc>(sm.mvb, LDC, sm.r, LDD, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, C, GG, kKc, kMc>(sm.mvb, LDC, sm.r, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) E[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
         });
         // ---- dT = dE R^T (kept), dbeta_T = diag(Minv^T dT): wave w holds
-        //      column block w % 4 of dT, row blocks w / 4 and w / 4 + 2
-        mm_regs<4, D, 2, GT>(sm.de, LDD, sm.r, LDD, rT);
+        //      the tile (row block w / 4, column block w % 4)
+        mm_regs<4, D, 1, GG>(sm.de, LDD, sm.r, LDD, rT);
         {
             const int s2 = 16 * (wave % 4) + ln;
             float part = 0.f;
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) part += mvd[x][i] * rT[x][i];
+            for (int i = 0; i < 4; ++i) part += mvd[i] * rT[0][i];
             part += __shfl_xor(part, 16);
             part += __shfl_xor(part, 32);
             if (g4 == 0) s_dbT[wave / 4][s2] = part;
         }
-        if (tid < D) s_dgam[tid] = (sm.dgp[0][tid] + sm.dgp[1][tid]) + (sm.dgp[2][tid] + sm.dgp[3][tid]);
+        if (tid < D) {
+            float acc = 0.f;
+#pragma unroll
+            for (int p = 0; p < GG / D; ++p) acc += sm.dgp[p][tid];
+            s_dgam[tid] = acc;
+        }
         __syncthreads();
         // ---- dV = T^T dE = (Minv Diag(beta))^T dE (over R; both operands by rows of K)
         bf16_t* dV = sm.r;
-        mm<4, 8, C, GT, kMc, kMc>(sm.mvb, LDC, sm.de, LDD, [&](int mi, int ni, f32x4 acc) {
+        mm<4, 8, C, GG, kMc, kMc>(sm.mvb, LDC, sm.de, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int s2 = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
@@ -786,89 +786,92 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         });
         __syncthreads();
         // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T (kept; S^T read by rows of K)
-        mm_regs<8, D, 4, GT, kKc, kMc>(dV, LDD, sm.st, LDD, rKgW);
-        mm_regs<8, D, 4, GT, kKc, kMc>(sm.dol, LDD, sm.st, LDD, rQgS);
+        mm_regs<8, D, 2, GG, kKc, kMc>(dV, LDD, sm.st, LDD, rKgW);
+        mm_regs<8, D, 2, GG, kKc, kMc>(sm.dol, LDD, sm.st, LDD, rQgS);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
+        for (int x = 0; x < 2; ++x) {
             rKgW[x] = -rKgW[x];
             rQgS[x] = scale * rQgS[x];
         }
         // ---- dKd = E dS'^T, dP = lower(scale dO E^T) (kept)
-        mm_regs<8, D, 4, GT>(E, LDD, sm.dsl, LDD, rKd);
-        mm_regs<4, D, 2, GT>(sm.dol, LDD, E, LDD, rP);
-#pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int t = wave + W * x, mi = t / 4, ni = t % 4;
+        mm_regs<8, D, 2, GG>(E, LDD, sm.dsl, LDD, rKd);
+        mm_regs<4, D, 1, GG>(sm.dol, LDD, E, LDD, rP);
+        {
+            const int mi = wave / 4, ni = wave % 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mi + 4 * g4 + i, s2 = 16 * ni + ln;
-                rP[x][i] = s2 <= r ? scale * rP[x][i] : 0.f;
+                rP[0][i] = s2 <= r ? scale * rP[0][i] : 0.f;
             }
         }
         __syncthreads();   // phase B reuses the LDS
     }
     // =========================== phase B ===========================
     GradBLds& sm = sm_u.b;
-    // Minv into LDS; the gates scanned as in the prep (the same gate bits)
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int u = tid + GT * x;
-        put4t(sm.mv + (u / (C / 4)) * LDC + 4 * (u % (C / 4)), mvr[x]);
-    }
+    // Minv into LDS; k and q of this thread's block; the gates scanned as
+    // in the prep (the same gate bits)
+    put4t(sm.mv + (tid / (C / 4)) * LDC + 4 * (tid % (C / 4)), mvr);
+    float4 kr4[4], qr4[4];
+    load_rows4(k, c, H, kr4);
+    load_rows4(q, c, H, qr4);
     {
         float gr[4][4];
         f32x4 Gr;
         scan_gate_block(graw, bsv, sm.gscan, sm.gtot, sm.bs, gr, Gr);
         // the gates for the final tiles, and the gated keys and queries
-        const int rg = tid >> 5, c0 = 4 * (tid & 31);
+        // (one thread per 4 x 4 block of the chunk)
+        if (tid < GT) {
+            const int rg = tid >> 5, c0 = 4 * (tid & 31);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * rg + i;
-            *reinterpret_cast<f32x4*>(sm.g + r * D + c0) = f32x4{gr[i][0], gr[i][1], gr[i][2], gr[i][3]};
-            const float kk[4] = {kr4[i].x, kr4[i].y, kr4[i].z, kr4[i].w};
-            const float qq[4] = {qr4[i].x, qr4[i].y, qr4[i].z, qr4[i].w};
-            f32x4 kg, kn, qg;
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rg + i;
+                *reinterpret_cast<f32x4*>(sm.g + r * D + c0) = f32x4{gr[i][0], gr[i][1], gr[i][2], gr[i][3]};
+                const float kk[4] = {kr4[i].x, kr4[i].y, kr4[i].z, kr4[i].w};
+                const float qq[4] = {qr4[i].x, qr4[i].y, qr4[i].z, qr4[i].w};
+                f32x4 kg, kn, qg;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float eg = gate_exp(gr[i][e]), en = gate_exp(-gr[i][e]);
-                kg[e] = kk[e] * eg;
-                kn[e] = kk[e] * en;
-                qg[e] = qq[e] * eg;
+                for (int e = 0; e < 4; ++e) {
+                    const float eg = gate_exp(gr[i][e]), en = gate_exp(-gr[i][e]);
+                    kg[e] = kk[e] * eg;
+                    kn[e] = kk[e] * en;
+                    qg[e] = qq[e] * eg;
+                }
+                put4t(sm.kg + r * LDT + c0, kg);
+                put4t(sm.kn + r * LDT + c0, kn);
+                put4t(sm.qg + r * LDT + c0, qg);
             }
-            put4t(sm.kg + r * LDT + c0, kg);
-            put4t(sm.kn + r * LDT + c0, kn);
-            put4t(sm.qg + r * LDT + c0, qg);
         }
     }
-    // k and q again, at this lane's positions of the final tiles: loaded
-    // here, used after the triangular-system products
-    const int ch = 16 * wave + ln;
-    float kv[4][4], qv[4][4];
+    // the final tiles of this wave: key channel block cb, row blocks
+    // wave / 8 + 2x (the tiles of rKgW, rQgS, rKd); k and q at those
+    // positions, loaded here and used after the triangular-system products
+    const int cb = wave % 8, ch = 16 * cb + ln;
+    float kv[2][4], qv[2][4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int rr = min(16 * x + 4 * g4 + i, c.len - 1);   // rows past the chunk: any valid row
+            const int r = 16 * (wave / 8 + 2 * x) + 4 * g4 + i;
+            const int rr = min(r, c.len - 1);        // rows past the chunk: any valid row
             const int64_t row = ((c.t0 + rr) * H + c.h) * D + ch;
             kv[x][i] = elem<T>::load(k + row);
             qv[x][i] = elem<T>::load(q + row);
         }
     // (dT Diag(beta))^T and dP from this wave's dT and dP tiles
+    {
+        const int mi = wave / 4, s2 = 16 * (wave % 4) + ln;
+        put4t(sm.yt + s2 * LDC + 16 * mi + 4 * g4, sm.bs[s2] * rT[0]);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int t = wave + W * x, mi = t / 4, ni = t % 4, s2 = 16 * ni + ln;
-        put4t(sm.yt + s2 * LDC + 16 * mi + 4 * g4, sm.bs[s2] * rT[x]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.dp[(16 * mi + 4 * g4 + i) * LDC + s2] = bf(rP[x][i]);
+        for (int i = 0; i < 4; ++i) sm.dp[(16 * mi + 4 * g4 + i) * LDC + s2] = bf(rP[0][i]);
     }
-    if (tid < C) sm.db[tid] = s_dbT[0][tid] + s_dbT[1][tid];
+    if (tid < C) sm.db[tid] = (s_dbT[0][tid] + s_dbT[1][tid]) + (s_dbT[2][tid] + s_dbT[3][tid]);
     __syncthreads();
-    // B = Kg Kn^T at this wave's dA tiles (for dbeta_A; the prep's inverse
+    // B = Kg Kn^T at this wave's dA tile (for dbeta_A; the prep's inverse
     // used the same bf16 operands and product order)
-    f32x4 bmt[2];
-    mm_regs<4, D, 2, GT>(sm.kg, LDT, sm.kn, LDT, bmt);
+    f32x4 bmt[1];
+    mm_regs<4, D, 1, GG>(sm.kg, LDT, sm.kn, LDT, bmt);
     // Z = Minv^T (dT Diag(beta))  (Minv read by rows of K)
-    mm<4, 4, C, GT, kMc, kKc>(sm.mv, LDC, sm.yt, LDC, [&](int mi, int ni, f32x4 acc) {
+    mm<4, 4, C, GG, kMc, kKc>(sm.mv, LDC, sm.yt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sm.z[(16 * mi + 4 * g4 + i) * LDC + 16 * ni + ln] = bf(acc[i]);
     });
@@ -876,55 +879,51 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // dA = -strict_lower(Z Minv^T); dB = Diag(beta) dA over (dT Diag(beta))^T,
     // which nothing reads any more
     {
-        f32x4 dA[2];
-        mm_regs<4, C, 2, GT>(sm.z, LDC, sm.mv, LDC, dA);
+        f32x4 dA[1];
+        mm_regs<4, C, 1, GG>(sm.z, LDC, sm.mv, LDC, dA);
+        const int mi = wave / 4, ni = wave % 4;
+        const int r0 = 16 * mi + 4 * g4, s2 = 16 * ni + ln;
+        float rowpart[4];
 #pragma unroll
-        for (int x = 0; x < 2; ++x) {
-            const int t = wave + W * x, mi = t / 4, ni = t % 4;
-            const int r0 = 16 * mi + 4 * g4, s2 = 16 * ni + ln;
-            float rowpart[4];
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            const float a = s2 < r ? -dA[0][i] : 0.f;
+            rowpart[i] = a * bmt[0][i];                  // dbeta_A
+            sm.yt[r * LDC + s2] = bf(sm.bs[r] * a);      // dB = Diag(beta) dA
+        }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = r0 + i;
-                const float a = s2 < r ? -dA[x][i] : 0.f;
-                rowpart[i] = a * bmt[x][i];                  // dbeta_A
-                sm.yt[r * LDC + s2] = bf(sm.bs[r] * a);      // dB = Diag(beta) dA
-            }
+        for (int i = 0; i < 4; ++i) {
+            float pp = rowpart[i];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float pp = rowpart[i];
-#pragma unroll
-                for (int m = 1; m < 16; m <<= 1) pp += __shfl_xor(pp, m);
-                if (ln == 0) sm.dbp[ni][r0 + i] = pp;
-            }
+            for (int m = 1; m < 16; m <<= 1) pp += __shfl_xor(pp, m);
+            if (ln == 0) sm.dbp[ni][r0 + i] = pp;
         }
     }
     __syncthreads();
     const bf16_t* dB = sm.yt;
-    if (tid >= GT - C) {
-        const int r = tid - (GT - C);
+    if (tid >= GG - C) {
+        const int r = tid - (GG - C);
         if (r < c.len)
             dbeta[(c.t0 + r) * H + c.h] = sm.db[r] + ((sm.dbp[0][r] + sm.dbp[1][r]) +
                                                       (sm.dbp[2][r] + sm.dbp[3][r]));
     }
     // per 16x16 tile of (row r, key channel c): dKg = dKg_W + dB Kn,
     // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain;
-    // wave w owns channel block w (tiles t = w + 8x: row block x), so the
-    // B fragments of Kn, Kg and Qg (read by rows of K) serve all four tiles,
-    // and every per-channel sum over the chunk's rows stays in the wave.
+    // the B fragments of Kn, Kg and Qg (read by rows of K) serve both of
+    // the wave's tiles
     u32x4 fkn[2], fkg[2], fqg[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
-        fkn[s2] = frag<kMc>(sm.kn + 16 * wave, LDT, 32 * s2, lane);
-        fkg[s2] = frag<kMc>(sm.kg + 16 * wave, LDT, 32 * s2, lane);
-        fqg[s2] = frag<kMc>(sm.qg + 16 * wave, LDT, 32 * s2, lane);
+        fkn[s2] = frag<kMc>(sm.kn + 16 * cb, LDT, 32 * s2, lane);
+        fkg[s2] = frag<kMc>(sm.kg + 16 * cb, LDT, 32 * s2, lane);
+        fqg[s2] = frag<kMc>(sm.qg + 16 * cb, LDT, 32 * s2, lane);
     }
     const float G = sm.g[(c.len - 1) * D + ch];
-    float dgr[4][4];          // dg of rows 16x + 4 g4 + i, this lane's channel
+    float dgr[2][4];          // dg of rows 16 mi + 4 g4 + i, this lane's channel
     float dGp = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int mi = x;
+    for (int x = 0; x < 2; ++x) {
+        const int mi = wave / 8 + 2 * x;
         f32x4 aKg = {0.f, 0.f, 0.f, 0.f}, aKn = aKg, aQg = aKg;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
@@ -956,20 +955,36 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         }
     }
     if constexpr (GATE != kGateNone) {
-        // dlog_alpha[r] = sum_{r' >= r} dg[r'] + dG per key channel, in
-        // registers: row r = 16x + 4 g4 + i is summed over the rows after it
-        // in its lane (i), in the lane groups after it (g4) and in the row
-        // blocks after it (x), in that fixed order
+        // dlog_alpha[r] = sum_{r' >= r} dg[r'] + dG per key channel.  The row
+        // blocks of a channel are split over waves cb and cb + 8: each
+        // publishes its blocks' totals and its part of dG; then row r =
+        // 16 mi + 4 g4 + i is summed over the rows after it in its lane (i),
+        // in the lane groups after it (g4) and in the row blocks after it,
+        // in that fixed order
+        float tot[2];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const float s = (dgr[x][0] + dgr[x][1]) + (dgr[x][2] + dgr[x][3]);
+            const float t2 = s + __shfl_xor(s, 16);
+            tot[x] = t2 + __shfl_xor(t2, 32);
+        }
         dGp += __shfl_xor(dGp, 16);
         dGp += __shfl_xor(dGp, 32);
-        const float dG = s_dgam[ch] * gate_exp(G) + dGp;
-        float after = dG;                     // rows of the row blocks after x
-        float out[4][4];
+        if (g4 == 0) {
+            sm.ftot[wave / 8][ch] = tot[0];
+            sm.ftot[wave / 8 + 2][ch] = tot[1];
+            sm.fdg[wave / 8][ch] = dGp;
+        }
+        __syncthreads();
+        const float dG = s_dgam[ch] * gate_exp(G) + (sm.fdg[0][ch] + sm.fdg[1][ch]);
+        float out[2][4];
 #pragma unroll
-        for (int x = 3; x >= 0; --x) {
-            float lane_sum = (dgr[x][0] + dgr[x][1]) + (dgr[x][2] + dgr[x][3]);
-            const float s16 = __shfl_down(lane_sum, 16), s32 = __shfl_down(lane_sum, 32),
-                        s48 = __shfl_down(lane_sum, 48);
+        for (int x = 0; x < 2; ++x) {
+            const int mi = wave / 8 + 2 * x;
+            float after = dG;                     // rows of the row blocks after mi
+            for (int m = 3; m > mi; --m) after += sm.ftot[m][ch];
+            const float s = (dgr[x][0] + dgr[x][1]) + (dgr[x][2] + dgr[x][3]);
+            const float s16 = __shfl_down(s, 16), s32 = __shfl_down(s, 32), s48 = __shfl_down(s, 48);
             const float groups_after = (g4 < 3 ? s16 : 0.f) + (g4 < 2 ? s32 : 0.f) +
                                        (g4 < 1 ? s48 : 0.f);
             float run = after + groups_after;
@@ -978,35 +993,33 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 run += dgr[x][i];
                 out[x][i] = run;
             }
-            const float block = lane_sum + __shfl_xor(lane_sum, 16);
-            after += block + __shfl_xor(block, 32);
         }
         if constexpr (GATE == kGateChannel) {
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * x + 4 * g4 + i;
+                    const int r = 16 * (wave / 8 + 2 * x) + 4 * g4 + i;
                     if (r < c.len) dla[((c.t0 + r) * H + c.h) * D + ch] = out[x][i];
                 }
         } else {
             // one gate per (token, head) reaches every key channel: the sum
             // over the channels, per wave across its 16 lanes, then over the
-            // waves in order
+            // channel blocks in order
 #pragma unroll
-            for (int x = 0; x < 4; ++x)
+            for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float v2 = out[x][i];
 #pragma unroll
                     for (int m = 1; m < 16; m <<= 1) v2 += __shfl_xor(v2, m);
-                    if (ln == 0) sm.hp[wave][16 * x + 4 * g4 + i] = v2;
+                    if (ln == 0) sm.hp[cb][16 * (wave / 8 + 2 * x) + 4 * g4 + i] = v2;
                 }
             __syncthreads();
             if (tid < C && tid < c.len) {
                 float acc = 0.f;
 #pragma unroll
-                for (int w = 0; w < W; ++w) acc += sm.hp[w][tid];
+                for (int w = 0; w < D / 16; ++w) acc += sm.hp[w][tid];
                 dla[(c.t0 + tid) * H + c.h] = acc;
             }
         }
@@ -1369,7 +1382,7 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
         if (b > 0 && (e = launch_prep(b - 1)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(stream, ev.carry[r], 0)) != hipSuccess) return e;
         if (a.total_T == 0) continue;
-        hipLaunchKernelGGL(gk, dim3(chunks), dim3(GT), 0, stream, slots[r], dsblk[r], deblk[r],
+        hipLaunchKernelGGL(gk, dim3(chunks), dim3(GG), 0, stream, slots[r], dsblk[r], deblk[r],
                            sall, a.h0, q, k, v, dO, a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo,
                            L_b, a.scale, static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
                            static_cast<bf16_t*>(a.dv), a.dlog_alpha, a.dbeta);
