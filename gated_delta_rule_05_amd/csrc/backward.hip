@@ -449,7 +449,7 @@ __device__ __forceinline__ void copy_rows(bf16_t* dst, int ld, const bf16_t* src
     }
 }
 
-__global__ __launch_bounds__(GT)
+__global__ __launch_bounds__(GG)
 void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dO,
                       const int32_t* __restrict__ cu, int N, int H, int c_lo, int L_b,
                       float* __restrict__ dstate, bf16_t* __restrict__ dsblk,
@@ -461,20 +461,20 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     const int n = pair / H, h = pair % H;
     if (n >= N) return;            // the grid is exactly N * H * R work-groups
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
-    // 8 waves: wave w owns value columns 16 (w % 4) .. +15 of the tile and
-    // key rows 64 (w / 4) .. +63 of the state
-    const int slab = wave % 4, half = wave / 4;
+    // 16 waves: wave w owns value columns 16 (w % 4) .. +15 of the tile and
+    // key rows 32 (w / 4) .. +31 of the state
+    const int slab = wave % 4, quarter = wave / 4;
     const int64_t t_begin = cu[n], t_end = cu[n + 1];
     const int nch = static_cast<int>((t_end - t_begin + C - 1) / C);
     const int hi = min(nch, c_lo + L_b) - 1;          // last chunk of this block
     const int jc = tile * kCarryTile + 16 * slab + ln; // this lane's value column
-    const int rb = 64 * half;                          // this wave's first key row
+    const int rb = 32 * quarter;                       // this wave's first key row
     float* st = dstate + (static_cast<int64_t>(n) * H + h) * kState;
     if (hi < c_lo) {
         // no chunk here; an empty sequence still gets dh0 = dhT (or zeros)
         if (c_lo == 0 && dh0) {
             float* d0 = dh0 + (static_cast<int64_t>(n) * H + h) * kState;
-            for (int e = tid; e < D * kCarryTile; e += GT) {
+            for (int e = tid; e < D * kCarryTile; e += GG) {
                 const int row = e / kCarryTile, col = tile * kCarryTile + e % kCarryTile;
                 d0[row * D + col] = st[row * D + col];
             }
@@ -482,52 +482,67 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         return;
     }
     // dS slab: S[m][i] = dS[rb + 16m + 4g + i][jc]
-    f32x4 S[4];
+    f32x4 S[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[m][i] = st[(rb + 16 * m + 4 * g4 + i) * D + jc];
 
     // The next chunk's operands load into registers while this chunk
-    // computes.  Kd, P^T, Qg and W^T are 3584 16-byte units: 7 per
-    // thread, and with 512 threads unit x * 512 + tid falls in one matrix
-    // for every thread (Kd: x < 2; P^T: x = 2; Qg: x < 5; W^T: x < 7).
-    constexpr int PER = (C * D + C * C + 2 * D * C) / 8 / GT;
-    static_assert(PER * GT * 8 == C * D + C * C + 2 * D * C, "whole rounds");
-    static_assert(GT == 512, "the unit-to-matrix map below assumes 512 threads");
-    u32x4 pre[PER], pdo;
+    // computes.  Kd, P^T, Qg and W^T are 3584 16-byte units (Kd, then P^T,
+    // Qg and W^T contiguous from kOffPt): unit x * 1024 + tid, x < 4, for
+    // the units that exist; dO's 64 x 64 tile is 512 more, one per thread
+    // of the first half.
+    constexpr int NUNIT = (C * D + C * C + 2 * D * C) / 8;
+    constexpr int PER = (NUNIT + GG - 1) / GG;
+    static_assert(NUNIT == 3584 && PER == 4 && C * kCarryTile / 8 == GG / 2,
+                  "the unit map below");
+    u32x4 pre[PER], pdo = {0u, 0u, 0u, 0u};
     float pgam = 0.f;
     auto fetch = [&](int j) {
         const int64_t slot = (static_cast<int64_t>(n) * L_b + (j - c_lo)) * H + h;
         const uint8_t* sp = slots + slot * static_cast<int64_t>(kSlot);
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int u = x * GT + tid;
-            const int byte = x < 2 ? 16 * u : kOffPt + 16 * (u - 2 * GT);
-            pre[x] = *reinterpret_cast<const u32x4*>(sp + byte);
+            const int u = x * GG + tid;
+            const int byte = u < C * D / 8 ? 16 * u : kOffPt + 16 * (u - C * D / 8);
+            if (u < NUNIT) pre[x] = *reinterpret_cast<const u32x4*>(sp + byte);
         }
         if (tid < D) pgam = reinterpret_cast<const float*>(sp + kOffGam)[tid];
-        const int64_t t0 = t_begin + static_cast<int64_t>(j) * C;
-        const int len = static_cast<int>(min<int64_t>(C, t_end - t0));
-        const int r = tid >> 3, part = tid & 7;
-        pdo = *reinterpret_cast<const u32x4*>(dO + ((t0 + min(r, len - 1)) * H + h) * D +
-                                              tile * kCarryTile + 8 * part);
-        if (r >= len) pdo = u32x4{0u, 0u, 0u, 0u};
+        if (tid < GG / 2) {
+            const int64_t t0 = t_begin + static_cast<int64_t>(j) * C;
+            const int len = static_cast<int>(min<int64_t>(C, t_end - t0));
+            const int r = tid >> 3, part = tid & 7;
+            pdo = *reinterpret_cast<const u32x4*>(dO + ((t0 + min(r, len - 1)) * H + h) * D +
+                                                  tile * kCarryTile + 8 * part);
+            if (r >= len) pdo = u32x4{0u, 0u, 0u, 0u};
+        }
     };
     auto put = [&]() {
 #pragma unroll
         for (int x = 0; x < PER; ++x) {
-            const int u = x * GT + tid;
+            const int u = x * GG + tid;
+            if (u >= NUNIT) continue;
             bf16_t* dst;
-            if (x < 2) dst = sm.kd + (u / 16) * LDD + (u % 16) * 8;
-            else if (x < 3) { const int w = u - 2 * GT; dst = sm.pt + (w / 8) * LDC + (w % 8) * 8; }
-            else if (x < 5) { const int w = u - 3 * GT; dst = sm.qg + (w / 16) * LDD + (w % 16) * 8; }
-            else { const int w = u - 5 * GT; dst = sm.wt + (w / 8) * LDC + (w % 8) * 8; }
+            if (u < C * D / 8) {
+                dst = sm.kd + (u / 16) * LDD + (u % 16) * 8;
+            } else if (u < C * D / 8 + C * C / 8) {
+                const int w = u - C * D / 8;
+                dst = sm.pt + (w / 8) * LDC + (w % 8) * 8;
+            } else if (u < 2 * C * D / 8 + C * C / 8) {
+                const int w = u - C * D / 8 - C * C / 8;
+                dst = sm.qg + (w / 16) * LDD + (w % 16) * 8;
+            } else {
+                const int w = u - 2 * C * D / 8 - C * C / 8;
+                dst = sm.wt + (w / 8) * LDC + (w % 8) * 8;
+            }
             *reinterpret_cast<u32x4*>(dst) = pre[x];
         }
         if (tid < D) sm.gam[tid] = pgam;
-        const int r = tid >> 3, part = tid & 7;
-        *reinterpret_cast<u32x4*>(sm.dol + r * LDO + 8 * part) = pdo;
+        if (tid < GG / 2) {
+            const int r = tid >> 3, part = tid & 7;
+            *reinterpret_cast<u32x4*>(sm.dol + r * LDO + 8 * part) = pdo;
+        }
     };
 
     fetch(hi);
@@ -537,20 +552,19 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         // dS' of this chunk (bf16, for the grad pass) and as a bf16 B operand
         bf16_t* dsp = dsblk + slot * kState;
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
+        for (int m = 0; m < 2; ++m) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsp[(rb + 16 * m + 4 * g4 + i) * D + jc] = bf(S[m][i]);
             put4t(&sm.dst[slab][ln * LDD + rb + 16 * m + 4 * g4], S[m]);
         }
         __syncthreads();
         if (j > c_lo) fetch(j - 1);
-        // dE = Kd dS' + scale P^T dO  (this slab's 16 columns, row tiles 2 half, 2 half + 1)
+        // dE = Kd dS' + scale P^T dO  (this slab's 16 columns, row tile `quarter`)
         bf16_t* dep = deblk + slot * (static_cast<int64_t>(C) * D);
         const bf16_t* dsw = sm.dst[slab];
         const bf16_t* dow = sm.dol + 16 * slab;   // dO by rows of K
-#pragma unroll
-        for (int mm2 = 0; mm2 < 2; ++mm2) {
-            const int m = 2 * half + mm2;
+        {
+            const int m = quarter;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = tile_mm<D>(sm.kd + 16 * m * LDD, LDD, dsw, LDD, lane, acc);
             acc = tile_mm<C, kKc, kMc>(sm.pt + 16 * m * LDC, LDC, dow, LDO, lane, acc);
@@ -562,8 +576,8 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         // dS = Diag(gamma) dS' + scale Qg^T dO - W^T dE  (this wave's key rows)
         const bf16_t* dew = sm.det[slab];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int mb = 4 * half + m;
+        for (int m = 0; m < 2; ++m) {
+            const int mb = 2 * quarter + m;
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * mb + 4 * g4 + i] * S[m][i];
@@ -577,7 +591,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     if (dst_out) {
         dst_out += c_lo == 0 ? (static_cast<int64_t>(n) * H + h) * kState : 0;
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst_out[(rb + 16 * m + 4 * g4 + i) * D + jc] = S[m][i];
     }
@@ -1375,7 +1389,7 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
         const int c_lo = static_cast<int>(b * L_b), r = static_cast<int>(b % kRing);
         if ((e = hipStreamWaitEvent(serial, ev.prep[r], 0)) != hipSuccess) return e;
         hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>(a.N * a.H * (D / kCarryTile))),
-                           dim3(GT), 0, serial, slots[r], dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
+                           dim3(GG), 0, serial, slots[r], dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
                            dstate, dsblk[r], deblk[r], a.dh0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(ev.carry[r], serial)) != hipSuccess) return e;
