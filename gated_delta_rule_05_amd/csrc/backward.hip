@@ -268,6 +268,18 @@ __device__ __forceinline__ void load_rows4(const T* x, const ChunkRef& c, int H,
     }
 }
 
+// the same block as raw bf16 pairs (half the registers of load_rows4)
+__device__ __forceinline__ void load_rows4_raw(const bf16_t* x, const ChunkRef& c, int H,
+                                               u32x2 (&out)[4]) {
+    const int tid = threadIdx.x, rg = tid >> 5, cg = tid & 31;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * rg + i;
+        out[i] = u32x2{0u, 0u};
+        if (r < c.len) out[i] = *reinterpret_cast<const u32x2*>(x + ((c.t0 + r) * H + c.h) * D + 4 * cg);
+    }
+}
+
 // ===================================================================
 // prep: a chunk's operands for the backward passes
 // ===================================================================
@@ -696,11 +708,15 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // 16 (wave / 4) + 4 g4 + i, column s2) for dbeta_T
     f32x4 mvr;
     float mvd[4];
-    // phase B's gates load with phase A's inputs: this thread's block of
-    // raw gates, and beta (threads past the 512 blocks of the chunk hold
-    // zeros and load nothing)
+    // phase B's inputs load with phase A's: this thread's block of k and q
+    // (raw bf16 pairs) and of raw gates, and beta (threads past the 512
+    // blocks of the chunk hold zeros and load nothing)
+    static_assert(sizeof(T) == 2, "bf16 inputs");
+    u32x2 kraw[4], qraw[4];
     f32x4 graw[4];
     float bsv;
+    load_rows4_raw(reinterpret_cast<const bf16_t*>(k), c, H, kraw);
+    load_rows4_raw(reinterpret_cast<const bf16_t*>(q), c, H, qraw);
     load_gate_block<GATE>(la, beta, c, H, graw, bsv);
     {
         const int s2 = 16 * (wave % 4) + ln, mi = wave / 4;
@@ -822,12 +838,8 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
     // =========================== phase B ===========================
     GradBLds& sm = sm_u.b;
-    // Minv into LDS; k and q of this thread's block; the gates scanned as
-    // in the prep (the same gate bits)
+    // Minv into LDS; the gates scanned as in the prep (the same gate bits)
     put4t(sm.mv + (tid / (C / 4)) * LDC + 4 * (tid % (C / 4)), mvr);
-    float4 kr4[4], qr4[4];
-    load_rows4(k, c, H, kr4);
-    load_rows4(q, c, H, qr4);
     {
         float gr[4][4];
         f32x4 Gr;
@@ -840,8 +852,10 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * rg + i;
                 *reinterpret_cast<f32x4*>(sm.g + r * D + c0) = f32x4{gr[i][0], gr[i][1], gr[i][2], gr[i][3]};
-                const float kk[4] = {kr4[i].x, kr4[i].y, kr4[i].z, kr4[i].w};
-                const float qq[4] = {qr4[i].x, qr4[i].y, qr4[i].z, qr4[i].w};
+                const float kk[4] = {lo_bf(kraw[i][0]), hi_bf(kraw[i][0]), lo_bf(kraw[i][1]),
+                                     hi_bf(kraw[i][1])};
+                const float qq[4] = {lo_bf(qraw[i][0]), hi_bf(qraw[i][0]), lo_bf(qraw[i][1]),
+                                     hi_bf(qraw[i][1])};
                 f32x4 kg, kn, qg;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
