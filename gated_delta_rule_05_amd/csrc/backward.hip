@@ -686,7 +686,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                      T* __restrict__ dq, T* __restrict__ dk, T* __restrict__ dv,
                      float* __restrict__ dla, float* __restrict__ dbeta)
 {
-    constexpr int W = GG / 64;                 // waves: four per SIMD
     __shared__ GradLds sm_u;
     __shared__ float s_dgam[D], s_dbT[4][C];   // phase A -> phase B
     ChunkRef c;
@@ -808,13 +807,18 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         bf16_t* dV = sm.r;
         mm<4, 8, C, GG, kMc, kMc>(sm.mvb, LDC, sm.de, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int s2 = 16 * mi + 4 * g4 + i, col = 16 * ni + ln;
-                dV[s2 * LDD + col] = bf(acc[i]);
-                if (s2 < c.len) elem<T>::store(dv + ((c.t0 + s2) * H + c.h) * D + col, acc[i]);
-            }
+            for (int i = 0; i < 4; ++i) dV[(16 * mi + 4 * g4 + i) * LDD + 16 * ni + ln] = bf(acc[i]);
         });
         __syncthreads();
+        // dV out in whole 16-byte pieces of its rows (dv takes the bf16 of
+        // the same value the products below use)
+        static_assert(sizeof(T) == 2 && C * D / 8 == GG, "one 16-byte piece of dV per thread");
+        {
+            const int r = tid / (D / 8), c8 = (tid % (D / 8)) * 8;
+            if (r < c.len)
+                *reinterpret_cast<u32x4*>(dv + ((c.t0 + r) * H + c.h) * D + c8) =
+                    *reinterpret_cast<const u32x4*>(dV + r * LDD + c8);
+        }
         // ---- dKg_W = -dV S^T, dQg_S = scale dO S^T (kept; S^T read by rows of K)
         mm_regs<8, D, 2, GG, kKc, kMc>(dV, LDD, sm.st, LDD, rKgW);
         mm_regs<8, D, 2, GG, kKc, kMc>(sm.dol, LDD, sm.st, LDD, rQgS);
@@ -947,6 +951,9 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         fqg[s2] = frag<kMc>(sm.qg + 16 * cb, LDT, 32 * s2, lane);
     }
     const float G = sm.g[(c.len - 1) * D + ch];
+    // every wave holds its fragments of the gated keys and queries: their
+    // buffers take dk and dq, which leave in whole 16-byte pieces of rows
+    __syncthreads();
     float dgr[2][4];          // dg of rows 16 mi + 4 g4 + i, this lane's channel
     float dGp = 0.f;
 #pragma unroll
@@ -965,7 +972,6 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             const int r = 16 * mi + 4 * g4 + i;
             float dgv = 0.f;
             if (r < c.len) {
-                const int64_t row = ((c.t0 + r) * H + c.h) * D + ch;
                 const float gv = sm.g[r * D + ch];
                 const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
                 const float dKg = aKg[i] + rKgW[x][i];
@@ -974,12 +980,21 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 const float dKd = rKd[x][i];
                 const float Kg = kv[x][i] * eg, Kn = kv[x][i] * en, Qg = qv[x][i] * eg;
                 const float Kd = kv[x][i] * ed;
-                elem<T>::store(dk + row, dKg * eg + dKn * en + dKd * ed);
-                elem<T>::store(dq + row, dQg * eg);
+                sm.kg[r * LDT + ch] = bf(dKg * eg + dKn * en + dKd * ed);   // dk
+                sm.kn[r * LDT + ch] = bf(dQg * eg);                         // dq
                 dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
                 dGp += dKd * Kd;
             }
             dgr[x][i] = dgv;
+        }
+    }
+    __syncthreads();
+    {
+        const int r = tid / (D / 8), c8 = (tid % (D / 8)) * 8;
+        if (r < c.len) {
+            const int64_t row = ((c.t0 + r) * H + c.h) * D + c8;
+            *reinterpret_cast<u32x4*>(dk + row) = *reinterpret_cast<const u32x4*>(sm.kg + r * LDT + c8);
+            *reinterpret_cast<u32x4*>(dq + row) = *reinterpret_cast<const u32x4*>(sm.kn + r * LDT + c8);
         }
     }
     if constexpr (GATE != kGateNone) {
@@ -1005,6 +1020,9 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         }
         __syncthreads();
         const float dG = s_dgam[ch] * gate_exp(G) + (sm.fdg[0][ch] + sm.fdg[1][ch]);
+        // per-channel gates: the results go straight into the gate buffer
+        // (its last reads were before the barrier above) and leave in whole
+        // 16-byte pieces of rows; per-head gates: kept for the channel sum
         float out[2][4];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
@@ -1019,17 +1037,19 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 #pragma unroll
             for (int i = 3; i >= 0; --i) {
                 run += dgr[x][i];
-                out[x][i] = run;
+                if constexpr (GATE == kGateChannel) sm.g[(16 * mi + 4 * g4 + i) * D + ch] = run;
+                else out[x][i] = run;
             }
         }
         if constexpr (GATE == kGateChannel) {
+            __syncthreads();
 #pragma unroll
-            for (int x = 0; x < 2; ++x)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int r = 16 * (wave / 8 + 2 * x) + 4 * g4 + i;
-                    if (r < c.len) dla[((c.t0 + r) * H + c.h) * D + ch] = out[x][i];
-                }
+            for (int x = 0; x < C * D / 4 / GG; ++x) {
+                const int u = tid + GG * x, r = u / (D / 4), c4 = (u % (D / 4)) * 4;
+                if (r < c.len)
+                    *reinterpret_cast<f32x4*>(dla + ((c.t0 + r) * H + c.h) * D + c4) =
+                        *reinterpret_cast<const f32x4*>(sm.g + r * D + c4);
+            }
         } else {
             // one gate per (token, head) reaches every key channel: the sum
             // over the channels, per wave across its 16 lanes, then over the
