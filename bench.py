@@ -204,7 +204,48 @@ def bench_backward(torch, kda, gen, inp, steps, warmup):
     out["front_end"] = {"ms": ms_f, "tokens_per_s": T / (ms_f * 1e-3), "workspace_bytes": need_f,
                         "vs_plain_pct": 100.0 * (ms_f / ms - 1.0),
                         "kernels": "front_act_kernel + the backward above + front_chain_kernel"}
-    del ws, do, gp, bp
+    del ws, gp, bp
+    grads.clear()
+    torch.cuda.empty_cache()
+
+    # training-style: the forward also writes the per-chunk state record and
+    # the backward reads it instead of recomputing the forward pass
+    rec_bytes = kda.chunk_states_bytes(T, N, H)
+    rec = torch.empty(rec_bytes, dtype=torch.uint8, device="cuda")
+    need_s = kda.backward_workspace_bytes(T, N, H, 128, 128, chunk_states=True)
+    ws = torch.empty(need_s, dtype=torch.uint8, device="cuda")
+    fwd_out = []
+
+    def run_fwd():
+        fwd_out.clear()
+        fwd_out.extend(kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                                   cu_seqlens=inp["cu_seqlens"], final_state=False,
+                                   chunk_states=rec))
+
+    def run_saved():
+        grads.clear()
+        grads.update(kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do,
+                                  cu_seqlens=inp["cu_seqlens"], workspace=ws, want_dh0=False,
+                                  chunk_states=rec))
+
+    run_fwd()
+    run_saved()
+    times = {}
+    for name, fn in (("forward", run_fwd), ("backward", run_saved)):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(3)]
+        for a0, a1 in evs:
+            a0.record(stream)
+            fn()
+            a1.record(stream)
+        torch.cuda.synchronize()
+        times[name] = sum(a0.elapsed_time(a1) for a0, a1 in evs) / len(evs)
+    out["saved_states"] = {"forward_ms": times["forward"], "backward_ms": times["backward"],
+                           "forward_plus_backward_ms": times["forward"] + times["backward"],
+                           "record_bytes": rec_bytes, "workspace_bytes": need_s,
+                           "backward_vs_plain_pct": 100.0 * (times["backward"] / ms - 1.0)}
+    del ws, rec, do
+    fwd_out.clear()
     grads.clear()
     torch.cuda.empty_cache()
     return out

@@ -57,7 +57,8 @@ class PrefillOptions(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("value_tiles", ctypes.c_int32),
                 ("block_chunks", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("snapshot_tokens", ctypes.c_int32), ("snapshot_capacity", ctypes.c_int32),
-                ("snapshots", ctypes.c_void_p), ("front", FrontEnd)]
+                ("snapshots", ctypes.c_void_p), ("front", FrontEnd),
+                ("chunk_states", ctypes.c_void_p)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -75,14 +76,14 @@ class DecodeMultiOptions(ctypes.Structure):
 class BwdOptions(ctypes.Structure):
     """Mirror of kda_bwd_options."""
     _fields_ = [("gate", ctypes.c_int32), ("block_chunks", ctypes.c_int32),
-                ("front", FrontEnd)]
+                ("front", FrontEnd), ("chunk_states", ctypes.c_void_p)]
 
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
                     "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill_workspace_bytes_ex",
                     "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step",
                     "kda_decode_step_ex", "kda_decode_multi", "kda_bwd_workspace_bytes",
-                    "kda_bwd")
+                    "kda_bwd", "kda_chunk_states_bytes")
 
 
 class KDAError(RuntimeError):
@@ -142,6 +143,8 @@ def load_library():
                             vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t,
                             ctypes.POINTER(BwdOptions), vp]
     lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_chunk_states_bytes.argtypes = [i64, i32, i32, i32, i32]
+    lib.kda_chunk_states_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -251,7 +254,7 @@ def _check_gate(log_alpha, gate, lead, dk, dev):
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
             block_chunks=0, gate="channel", snapshot_tokens=0, snapshots=None,
-            l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None):
+            l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -271,6 +274,9 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     kernel; ``gate_pre`` (bf16, log_alpha's layout; log_alpha must be None)
     gives log_alpha = -gate_scale * softplus(gate_pre); ``beta_pre`` (bf16
     [T, H]; beta must be None) gives beta = sigmoid(beta_pre).
+    ``chunk_states``: a uint8 device tensor of chunk_states_bytes(T, N, H)
+    bytes that receives every chunk's start state, for a later backward()
+    on the same inputs (which then skips recomputing this pass).
     """
     torch = _torch()
     lib = load_library()
@@ -327,6 +333,9 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
         opts.snapshot_tokens = int(snapshot_tokens)
         opts.snapshot_capacity = int(snapshots.shape[1])
         opts.snapshots = snapshots.data_ptr()
+    if chunk_states is not None:
+        _check_states(chunk_states, T, N, H, dk, dv, dev)
+        opts.chunk_states = chunk_states.data_ptr()
     need = lib.kda_fwd_prefill_workspace_bytes_ex(T, N, H, dk, dv, code, ctypes.byref(opts))
     if workspace is None:
         workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)
@@ -339,6 +348,23 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     if snapshot_tokens:
         return out, hT, snapshots
     return out, hT
+
+
+def chunk_states_bytes(total_T: int, N: int, H: int, d_k: int = 128, d_v: int = 128) -> int:
+    """Bytes of the per-chunk state record a prefill can write for the
+    backward (0 for unsupported sizes)."""
+    return int(load_library().kda_chunk_states_bytes(total_T, N, H, d_k, d_v))
+
+
+def _check_states(chunk_states, T, N, H, dk, dv, dev):
+    torch = _torch()
+    need = chunk_states_bytes(T, N, H, dk, dv)
+    if need == 0:
+        raise ValueError("chunk_states needs d_k = d_v = 128")
+    if (chunk_states.dtype != torch.uint8 or chunk_states.device != dev
+            or not chunk_states.is_contiguous() or chunk_states.numel() < need):
+        raise ValueError("chunk_states must be a contiguous uint8 tensor of at least %d bytes "
+                         "on %s" % (need, dev))
 
 
 def decode_step(q, k, v, log_alpha, beta, S, scale=None, out=None, gate="channel",
@@ -477,20 +503,21 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
 
 def backward_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
                              dtype: int = DTYPE_BF16, gate="channel", block_chunks=0,
-                             l2norm_qk=False, gate_pre=False, beta_pre=False) -> int:
-    """The front-end flags say which parts the call will use (their tensors
-    are not needed here)."""
+                             l2norm_qk=False, gate_pre=False, beta_pre=False,
+                             chunk_states=False) -> int:
+    """The front-end flags and chunk_states say which options the call will
+    use (their tensors are not needed here)."""
     dummy = ctypes.c_void_p(16)
     fe = FrontEnd(1 if l2norm_qk else 0, 1.0, dummy if gate_pre else None,
                   dummy if beta_pre else None)
-    opts = BwdOptions(_gate_code(gate), block_chunks, fe)
+    opts = BwdOptions(_gate_code(gate), block_chunks, fe, dummy if chunk_states else None)
     return int(load_library().kda_bwd_workspace_bytes(total_T, N, H, d_k, d_v, dtype,
                                                       ctypes.byref(opts)))
 
 
 def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, scale=None,
              gate="channel", want_dh0=True, block_chunks=0, workspace=None,
-             l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None):
+             l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None):
     """Gradients of <o, do> + <hT, dhT> for the prefill on these inputs.
 
     Inputs as for prefill() (bf16 q, k, v with d_k = d_v = 128); do: [T, H,
@@ -501,7 +528,10 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
 
     The fused input front-end as for prefill(): with it, dq and dk are the
     gradients with respect to the raw q and k, dlog_alpha with respect to
-    gate_pre (fp32, its layout) and dbeta with respect to beta_pre."""
+    gate_pre (fp32, its layout) and dbeta with respect to beta_pre.
+    ``chunk_states``: the record a prefill(..., chunk_states=...) call wrote
+    on these same inputs; the forward pass is then not recomputed (not with
+    the front-end)."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3:
@@ -545,6 +575,9 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
                dbeta=torch.empty((T, H), dtype=torch.float32, device=dev),
                dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
     opts = BwdOptions(gcode, block_chunks, fe if fe is not None else FrontEnd())
+    if chunk_states is not None:
+        _check_states(chunk_states, T, N, H, dk, dv, dev)
+        opts.chunk_states = chunk_states.data_ptr()
     need = int(lib.kda_bwd_workspace_bytes(T, N, H, dk, dv, code, ctypes.byref(opts)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

@@ -1199,13 +1199,16 @@ struct BwdLayout {
     size_t fwd, sall, slots, dsblk, deblk, dstate, total;
 };
 
-BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b) {
+// have_states: the chunk states come from the caller (no forward pass, no
+// record in the workspace)
+BwdLayout bwd_layout(int64_t total_T, int32_t N, int32_t H, int L_b, bool have_states) {
     BwdLayout l;
     const size_t nh = static_cast<size_t>(N) * H;
     const size_t blk = nh * L_b;
-    l.fwd = wy_workspace_bytes(N, H, D, D, wy_default_block_chunks(total_T, N, H, D));
-    l.sall = (static_cast<size_t>(N) + static_cast<size_t>(bound_chunks(total_T)) + 1) * H *
-             kState * 2;
+    l.fwd = have_states ? 0 : wy_workspace_bytes(N, H, D, D, wy_default_block_chunks(total_T, N, H, D));
+    l.sall = have_states ? 0
+                         : (static_cast<size_t>(N) + static_cast<size_t>(bound_chunks(total_T)) + 1) *
+                               H * kState * 2;
     l.slots = blk * kSlot;
     l.dsblk = blk * kState * 2;
     l.deblk = blk * C * D * 2;
@@ -1300,9 +1303,9 @@ FrontLayout front_layout(int64_t total_T, int32_t H, int gate, const FrontEnd& f
 }
 
 size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b, int gate,
-                           const FrontEnd& fe) {
+                           const FrontEnd& fe, bool have_states) {
     return (fe.active() ? front_layout(total_T, H, gate, fe).total : 0) +
-           bwd_layout(total_T, N, H, L_b).total;
+           bwd_layout(total_T, N, H, L_b, have_states).total;
 }
 
 hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream);
@@ -1345,11 +1348,13 @@ hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t
 }
 
 hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream) {
-    const BwdLayout l = bwd_layout(a.total_T, a.N, a.H, L_b);
+    const BwdLayout l = bwd_layout(a.total_T, a.N, a.H, L_b, a.states != nullptr);
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     uint8_t* p = static_cast<uint8_t*>(ws);
     uint8_t* fwd_ws = p;          p += up(l.fwd);
-    bf16_t* sall = reinterpret_cast<bf16_t*>(p);  p += up(l.sall);
+    const bf16_t* sall = a.states ? static_cast<const bf16_t*>(a.states)
+                                  : reinterpret_cast<bf16_t*>(p);
+    p += up(l.sall);
     uint8_t* slots[kRing];
     bf16_t* dsblk[kRing];
     bf16_t* deblk[kRing];
@@ -1368,17 +1373,20 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
     CallEvents ev;
     if ((e = ev.create()) != hipSuccess) return e;
 
-    // 1. forward: the state after every full chunk, no outputs
-    PrefillArgs f{};
-    f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.beta = a.beta; f.h0 = a.h0;
-    f.cu_seqlens = a.cu_seqlens; f.o = nullptr; f.hT = nullptr; f.order = nullptr;
-    f.total_T = a.total_T; f.N = a.N; f.H = a.H; f.d_k = D; f.d_v = D; f.gate = a.gate;
-    f.dtype_f32 = false; f.scale = a.scale;
-    f.snapshots = reinterpret_cast<float*>(sall);   // bf16 record (snap_cap < 0)
-    f.snap_tokens = C; f.snap_cap = -1;
-    e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D), fwd_ws,
-                          stream);
-    if (e != hipSuccess) return e;
+    // 1. forward: the state after every full chunk, no outputs (unless the
+    //    caller passes the record of its own forward pass)
+    if (!a.states) {
+        PrefillArgs f{};
+        f.q = a.q; f.k = a.k; f.v = a.v; f.log_alpha = a.log_alpha; f.beta = a.beta; f.h0 = a.h0;
+        f.cu_seqlens = a.cu_seqlens; f.o = nullptr; f.hT = nullptr; f.order = nullptr;
+        f.total_T = a.total_T; f.N = a.N; f.H = a.H; f.d_k = D; f.d_v = D; f.gate = a.gate;
+        f.dtype_f32 = false; f.scale = a.scale;
+        f.snapshots = reinterpret_cast<float*>(const_cast<bf16_t*>(sall));   // bf16 record (snap_cap < 0)
+        f.snap_tokens = C; f.snap_cap = -1;
+        e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D), fwd_ws,
+                              stream);
+        if (e != hipSuccess) return e;
+    }
 
     // 2. backward over blocks of chunks, from the last.  Caller's stream:
     //    prep(b - 1), then grad(b) once carry(b) is done; second stream:

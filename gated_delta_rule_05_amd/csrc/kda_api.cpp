@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 10;
+constexpr int kAbiVersion = 11;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -167,10 +167,15 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     const bool front = options && (options->front.l2norm_qk || options->front.gate_pre ||
                                    options->front.beta_pre);
     if (front && path == KDA_PATH_MATRIX) return KDA_STATUS_UNSUPPORTED;
+    // the per-chunk state record is written by the two-pass carry (bf16, d = 128)
+    const bool record = options && options->chunk_states;
+    if (record && (path == KDA_PATH_VECTOR || path == KDA_PATH_MATRIX || !matrix_ok ||
+                   d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16))
+        return KDA_STATUS_UNSUPPORTED;
     pl->path = path;
     if (path == KDA_PATH_AUTO) {
         pl->path = !matrix_ok ? KDA_PATH_VECTOR
-                   : front || static_cast<int64_t>(N) * H < kTwoPassMaxPairs
+                   : front || record || static_cast<int64_t>(N) * H < kTwoPassMaxPairs
                        ? KDA_PATH_MATRIX_TWO_PASS
                        : KDA_PATH_MATRIX;
     }
@@ -190,11 +195,29 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     return KDA_STATUS_OK;
 }
 
+// bytes of the per-chunk state record: one bf16 state per (chunk index,
+// head) over N + ceil(total_T / 64) + 1 indices (0 on overflow)
+int64_t chunk_states_bytes(int64_t total_T, int32_t N, int32_t H) {
+    const int64_t idx = static_cast<int64_t>(N) + (total_T + 63) / 64 + 1;
+    int64_t bytes;
+    if (!mul_ok(idx * H, int64_t{128} * 128 * 2, &bytes) || bytes > (int64_t{1} << 62)) return 0;
+    return bytes;
+}
+
 }  // namespace
 
 extern "C" {
 
 int kda_abi_version(void) { return kAbiVersion; }
+
+size_t kda_chunk_states_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v) {
+    Sizes sz;
+    if (check_sizes(total_T, N, H, d_k, d_v, KDA_DTYPE_BF16, KDA_GATE_CHANNEL, &sz) !=
+        KDA_STATUS_OK)
+        return 0;
+    if (d_k != 128 || d_v != 128) return 0;
+    return static_cast<size_t>(chunk_states_bytes(total_T, N, H));
+}
 
 const char* kda_status_string(int status) {
     switch (status) {
@@ -300,6 +323,18 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
         if (overlaps(r_s, r_o) || overlaps(r_s, r_hT) || overlaps(r_s, r_ws))
             return KDA_STATUS_INVALID_ARGUMENT;
     }
+    // the per-chunk state record (the two-pass path: resolve() checked)
+    void* rec = options ? options->chunk_states : nullptr;
+    if (rec) {
+        if (snap != 0) return KDA_STATUS_INVALID_ARGUMENT;
+        if (!aligned16(rec)) return KDA_STATUS_MISALIGNED;
+        const Range r_c = range_of(rec, chunk_states_bytes(total_T, N, H));
+        for (const Range& in : inputs)
+            if (overlaps(r_c, in)) return KDA_STATUS_INVALID_ARGUMENT;
+        if (overlaps(r_c, r_gp) || overlaps(r_c, r_bp) || overlaps(r_c, r_o) ||
+            overlaps(r_c, r_hT) || overlaps(r_c, r_ws))
+            return KDA_STATUS_INVALID_ARGUMENT;
+    }
 
     kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
     a.gate = gate;
@@ -307,9 +342,9 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     a.h0 = h0; a.cu_seqlens = cu_seqlens; a.o = o; a.hT = hT;
     a.order = static_cast<int32_t*>(workspace);
     a.scale = scale;
-    a.snapshots = snaps;
-    a.snap_tokens = snaps ? snap : 0;
-    a.snap_cap = cap;
+    a.snapshots = rec ? static_cast<float*>(rec) : snaps;
+    a.snap_tokens = rec ? 64 : snaps ? snap : 0;
+    a.snap_cap = rec ? -1 : cap;                   // < 0: the compact per-chunk record
     a.fe = fe;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -470,7 +505,9 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_
     if (check_front(options ? &options->front : nullptr, gate, nullptr, nullptr, total_T, H, d_k,
                     &fe, &la_needed, &beta_needed, &r_gp, &r_bp) != KDA_STATUS_OK)
         return 0;
-    return kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe);
+    const bool states = options && options->chunk_states;
+    if (states && fe.active()) return 0;
+    return kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe, states);
 }
 
 int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
@@ -505,7 +542,10 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     int L_b;
     const int bs = bwd_block_chunks(total_T, N, H, options, &L_b);
     if (bs != KDA_STATUS_OK) return bs;
-    const size_t need = kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe);
+    const void* states = options ? options->chunk_states : nullptr;
+    if (states && fe.active()) return KDA_STATUS_UNSUPPORTED;
+    if (states && !aligned16(states)) return KDA_STATUS_MISALIGNED;
+    const size_t need = kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe, states != nullptr);
 
     // no output may overlap an input, another output or the workspace
     const Range inputs[] = {range_of(q, sz.qk_bytes),      range_of(k, sz.qk_bytes),
@@ -513,7 +553,8 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
                             range_of(beta, sz.beta_bytes), range_of(cu_seqlens, (N + 1) * 4),
                             range_of(h0, h0 ? sz.state_bytes : 0),
                             range_of(dO, sz.v_bytes),      range_of(dhT, dhT ? sz.state_bytes : 0),
-                            r_gp,                          r_bp};
+                            r_gp,                          r_bp,
+                            range_of(states, states ? chunk_states_bytes(total_T, N, H) : 0)};
     const Range outputs[] = {range_of(dq, sz.qk_bytes),     range_of(dk, sz.qk_bytes),
                              range_of(dv, sz.v_bytes),      range_of(dlog_alpha, sz.la_bytes),
                              range_of(dbeta, sz.beta_bytes), range_of(dh0, dh0 ? sz.state_bytes : 0),
@@ -536,6 +577,7 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     a.cu_seqlens = cu_seqlens; a.dO = dO; a.dhT = dhT;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
     a.total_T = total_T; a.N = N; a.H = H; a.gate = gate; a.scale = scale; a.fe = fe;
+    a.states = states;
     if (kda::launch_backward(a, L_b, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_STATUS_HIP_ERROR;
     return KDA_STATUS_OK;

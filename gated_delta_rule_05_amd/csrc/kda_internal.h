@@ -98,12 +98,15 @@ struct BackwardArgs {
     // gate_pre / beta_pre stand in; dq, dk, dlog_alpha and dbeta are then
     // the gradients with respect to the raw inputs and pre-activations
     FrontEnd fe;
+    // the per-chunk state record of a forward pass on these inputs, or null
+    // (the forward pass is then recomputed into the workspace)
+    const void* states = nullptr;
 };
 int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H);
 // the backward's buffers, after the front-end's activated inputs when fe is
 // active
 size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b, int gate,
-                           const FrontEnd& fe);
+                           const FrontEnd& fe, bool have_states);
 hipError_t launch_backward(const BackwardArgs& a, int L_b, void* ws, hipStream_t stream);
 
 // first element of snapshot j of (sequence n, head h): [N][snap_cap][H][d_k][d_v]

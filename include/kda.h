@@ -173,6 +173,15 @@ typedef struct kda_prefill_options {
                                   May not overlap any other buffer. */
     kda_front_end front;       /* the fused input front-end (all off when
                                   zeroed); vector and two-pass paths */
+    void *chunk_states;        /* DEVICE, kda_chunk_states_bytes bytes,
+                                  16-byte aligned, or NULL: the start state
+                                  of every chunk of 64 tokens after a
+                                  sequence's first (bf16), recorded for a
+                                  later kda_bwd on the same inputs, which
+                                  then skips recomputing the forward pass.
+                                  Two-pass path, bf16, d_k = d_v = 128;
+                                  not with snapshot_tokens; no overlap with
+                                  any other buffer. */
 } kda_prefill_options;
 
 
@@ -219,10 +228,24 @@ typedef struct kda_bwd_options {
                                       (0 = automatic) */
     kda_front_end front;           /* the fused input front-end the forward
                                       used (zero = none); see kda_bwd */
+    const void *chunk_states;      /* DEVICE or NULL: the record a
+                                      kda_fwd_prefill_ex call wrote on these
+                                      same inputs (options.chunk_states);
+                                      the forward pass is then not
+                                      recomputed */
 } kda_bwd_options;
 
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
 int kda_abi_version(void);
+
+/*
+ * Bytes of the per-chunk state record (kda_prefill_options.chunk_states,
+ * kda_bwd_options.chunk_states) for these sizes: one bf16 d_k x d_v state
+ * per (chunk index, head) over N + ceil(total_T / 64) + 1 chunk indices.
+ * 0 unless d_k = d_v = 128, or for sizes kda_fwd_prefill would reject.
+ */
+size_t kda_chunk_states_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k,
+                              int32_t d_v);
 
 /* Human-readable text for a status code (static storage; never NULL). */
 const char *kda_status_string(int status);
@@ -290,6 +313,10 @@ int kda_fwd_prefill(const void *q, const void *k, const void *v,
  *     snapshot_capacity < 1, snapshots NULL, a byte count that overflows,
  *     or snapshots overlapping another buffer [INVALID_ARGUMENT];
  *     snapshots not 16-byte aligned [MISALIGNED];
+ *   chunk_states set together with snapshot_tokens, or overlapping another
+ *     buffer [INVALID_ARGUMENT]; not 16-byte aligned [MISALIGNED]; with the
+ *     vector or the fused matrix path, fp32 inputs, or d_k or d_v other
+ *     than 128 [UNSUPPORTED] (the automatic path is then the two-pass one);
  *   a matrix path requested for fp32 inputs or d_k != 128 [UNSUPPORTED];
  *   workspace_bytes below kda_fwd_prefill_workspace_bytes_ex(..., options)
  *     [WORKSPACE_TOO_SMALL].
@@ -415,6 +442,12 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * kda_bwd_workspace_bytes [WORKSPACE_TOO_SMALL].
  * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
  * adjoints, as in the forward pass.
+ * Saved states (options->chunk_states): the record of the forward pass on
+ * these inputs replaces its recomputation (the call then reads the record
+ * and needs a smaller workspace); the record must come from a forward pass
+ * on the same q, k, v, gates, beta, h0 and cu_seqlens.  Not with the
+ * front-end [UNSUPPORTED]; 16-byte aligned [MISALIGNED]; no output may
+ * overlap it [INVALID_ARGUMENT].
  * Front-end (options->front, as for kda_fwd_prefill_ex): q and k are the raw
  * inputs when l2norm_qk is set, and dq, dk the gradients with respect to
  * them; with gate_pre, log_alpha must be NULL and dlog_alpha (fp32, the

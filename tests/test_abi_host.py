@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 10
+    assert kda.abi_version() == 11
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -442,3 +442,93 @@ def test_backward_front_end_workspace():
     assert kda.backward_workspace_bytes(T, N, H, 128, 128, gate="head", gate_pre=True,
                                         beta_pre=True) == base + 2 * up(T * H * 4)
     assert kda.backward_workspace_bytes(T, N, H, 128, 128, gate="none", gate_pre=True) == 0
+
+
+# the per-chunk state record (kda_prefill_options.chunk_states /
+# kda_bwd_options.chunk_states); every case fails before any HIP call
+REC = BASE + 16 * GAP
+
+
+def test_chunk_states_bytes():
+    # one bf16 128x128 state per (chunk index, head) over N + ceil(T/64) + 1 indices
+    assert kda.chunk_states_bytes(100, 2, 4) == (2 + 2 + 1) * 4 * 128 * 128 * 2
+    assert kda.chunk_states_bytes(0, 3, 1) == (3 + 0 + 1) * 128 * 128 * 2
+    assert kda.chunk_states_bytes(100, 2, 4, 64, 64) == 0     # d = 128 only
+    assert kda.chunk_states_bytes(100, 0, 4) == 0             # invalid sizes
+
+
+def rec_prefill_call(path, rec=REC, snap=(0, 0, None), **over):
+    args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
+                cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
+                o=addr(6), hT=addr(7), ws=addr(8), wsb=1 << 34, stream=None)
+    args.update(over)
+    opts = kda.PrefillOptions(path, 0, 0, 0, snap[0], snap[1], snap[2])
+    opts.chunk_states = rec
+    lib = kda.load_library()
+    return lib.kda_fwd_prefill_ex(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                                  args["h0"], args["cu"], args["T"], args["N"], args["H"],
+                                  args["dk"], args["dv"], args["dtype"], args["scale"],
+                                  args["o"], args["hT"], args["ws"], args["wsb"],
+                                  ctypes.byref(opts), args["stream"])
+
+
+@pytest.mark.parametrize("path,kw,status", [
+    (1, {}, UNSUPPORTED),                              # written by the two-pass carry only
+    (2, {}, UNSUPPORTED),
+    (3, dict(dtype=1), UNSUPPORTED),
+    (0, dict(dk=64, dv=64), UNSUPPORTED),
+    (3, dict(wsb=256), WS_SMALL),                      # the ordinary workspace check first
+    (3, dict(snap=(64, 2, BASE + 9 * GAP)), INVALID),  # not together with snapshots
+    (3, dict(rec=REC + 8), MISALIGNED),
+    (3, dict(rec=BASE + 2 * GAP + 4096), INVALID),     # the record inside v
+    (3, dict(o=REC + 65536), INVALID),                 # o inside the record
+    (3, dict(ws=REC - 1024), INVALID),                 # the workspace runs into the record
+])
+def test_prefill_chunk_states_checks(path, kw, status):
+    assert rec_prefill_call(path, **kw) == status
+
+
+def test_prefill_chunk_states_picks_two_pass():
+    # many pairs would take the fused path; with the record the two-pass one
+    lib = kda.load_library()
+    T, N, H = 65536, 64, 64
+    plain = kda.PrefillOptions(0, 0, 0, 0)
+    rec = kda.PrefillOptions(0, 0, 0, 0)
+    rec.chunk_states = REC
+    two = kda.PrefillOptions(3, 0, 0, 0)
+    q = lambda o: lib.kda_fwd_prefill_workspace_bytes_ex(T, N, H, 128, 128, 0, ctypes.byref(o))
+    assert q(rec) == q(two) and q(rec) > q(plain)
+
+
+def test_backward_chunk_states_checks():
+    def call(rec, front=None, **over):
+        args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
+                    cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
+                    do=addr(6), dhT=None, dq=addr(7), dk_=addr(8), dv_=addr(9),
+                    dla=addr(10), dbeta=addr(11), dh0=addr(12), ws=addr(13), wsb=256,
+                    stream=None)
+        args.update(over)
+        opts = kda.BwdOptions(0, 0, kda.FrontEnd(*front) if front else kda.FrontEnd(), rec)
+        lib = kda.load_library()
+        return lib.kda_bwd(args["q"], args["k"], args["v"], args["la"], args["beta"],
+                           args["h0"], args["cu"], args["T"], args["N"], args["H"],
+                           args["dk"], args["dv"], args["dtype"], args["scale"], args["do"],
+                           args["dhT"], args["dq"], args["dk_"], args["dv_"], args["dla"],
+                           args["dbeta"], args["dh0"], args["ws"], args["wsb"],
+                           ctypes.byref(opts), args["stream"])
+    assert call(REC) == WS_SMALL                                  # every check passed
+    assert call(REC + 4) == MISALIGNED
+    assert call(REC, front=(1, 0.0, None, None)) == UNSUPPORTED   # not with the front-end
+    assert call(REC, dq=REC + 4096) == INVALID                    # an output on the record
+    assert call(REC, ws=REC + 256, wsb=1 << 34) == INVALID        # the workspace on it
+
+
+def test_backward_chunk_states_workspace():
+    # with the record the backward keeps no recomputed states of its own
+    T, N, H = 4096, 4, 16
+    full = kda.backward_workspace_bytes(T, N, H, 128, 128)
+    rec = kda.backward_workspace_bytes(T, N, H, 128, 128, chunk_states=True)
+    assert 0 < rec < full
+    assert full - rec >= T // 64 * H * 128 * 128 * 2
+    assert kda.backward_workspace_bytes(T, N, H, 128, 128, chunk_states=True,
+                                        l2norm_qk=True) == 0

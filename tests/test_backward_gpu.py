@@ -154,3 +154,43 @@ def test_backward_on_a_side_stream():
     side.synchronize()
     for key, x in base.items():
         assert torch.equal(x, other[key]), key
+
+
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+def test_backward_from_saved_chunk_states(gate):
+    """A prefill that also writes the per-chunk state record gives the same
+    o and hT as one that does not, and the backward that reads the record
+    gives the same bits as the one that recomputes the forward pass."""
+    inp = case(LENS, 2, 360, gate)
+    T, N = inp["q"].shape[0], len(LENS)
+    args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    kw = dict(h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], gate=gate)
+    rec = torch.empty(kda.chunk_states_bytes(T, N, 2), dtype=torch.uint8, device=DEV)
+    o0, hT0 = kda.prefill(*args, path="two_pass", **kw)
+    o1, hT1 = kda.prefill(*args, chunk_states=rec, **kw)
+    assert torch.equal(o0, o1) and torch.equal(hT0, hT1)
+    base = gpu(inp, gate)
+    other = gpu(inp, gate, chunk_states=rec)
+    for key, x in base.items():
+        assert (x is None) == (other[key] is None), key
+        if x is not None:
+            assert torch.equal(x, other[key]), key
+
+
+def test_backward_from_saved_chunk_states_batch4_t4096():
+    """The same on the 4 x 4096 x 16 batch, whose forward takes 32-column
+    value tiles where the backward's own recompute takes 16-column ones:
+    each state column is computed alone, so the record is the same bits."""
+    w = gen.WORKLOADS["batch4_t4096"]
+    inp = gen.workload_prefill_inputs(w, seed=370, device=DEV)
+    T, H = inp["q"].shape[:2]
+    N = inp["cu_seqlens"].shape[0] - 1
+    inp["do"] = gen.normal((T, H, 128), 370, gen.DO, DEV, torch.bfloat16)
+    inp["dhT"] = gen.normal((N, H, 128, 128), 370, gen.DHT, DEV, torch.float32, std=0.1)
+    rec = torch.empty(kda.chunk_states_bytes(T, N, H), dtype=torch.uint8, device=DEV)
+    kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], h0=inp["h0"],
+                cu_seqlens=inp["cu_seqlens"], chunk_states=rec)
+    base = gpu(inp, "channel")
+    other = gpu(inp, "channel", chunk_states=rec)
+    for key, x in base.items():
+        assert torch.equal(x, other[key]), key
