@@ -446,8 +446,8 @@ struct alignas(16) CarryLds {
     bf16_t wt[D * LDC];
     float gam[D];
     bf16_t dol[C * LDO];               // dO of the tile's columns
-    bf16_t dst[4][16 * LDD];           // each wave's dS slab, transposed
-    bf16_t det[4][16 * LDC];           // each wave's dE slab, transposed
+    bf16_t dst[kCarryTile / 16][16 * LDD];   // each 16-column slab of dS, transposed
+    bf16_t det[kCarryTile / 16][16 * LDC];   // each 16-column slab of dE, transposed
 };
 
 // copy a [rows][cols] bf16 matrix (global, contiguous) into LDS rows of ld
@@ -473,14 +473,17 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     const int n = pair / H, h = pair % H;
     if (n >= N) return;            // the grid is exactly N * H * R work-groups
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
-    // 16 waves: wave w owns value columns 16 (w % 4) .. +15 of the tile and
-    // key rows 32 (w / 4) .. +31 of the state
-    const int slab = wave % 4, quarter = wave / 4;
+    // 16 waves: wave w owns value columns 16 (w % NS) .. +15 of the tile,
+    // key rows RW (w / NS) .. +RW-1 of the state and row tiles
+    // ME (w / NS) .. +ME-1 of dE
+    constexpr int NS = kCarryTile / 16, NQ = 16 / NS, RW = D / NQ, MS = RW / 16, ME = C / 16 / NQ;
+    static_assert(NS * NQ == GG / 64 && ME >= 1, "the wave map");
+    const int slab = wave % NS, quarter = wave / NS;
     const int64_t t_begin = cu[n], t_end = cu[n + 1];
     const int nch = static_cast<int>((t_end - t_begin + C - 1) / C);
     const int hi = min(nch, c_lo + L_b) - 1;          // last chunk of this block
     const int jc = tile * kCarryTile + 16 * slab + ln; // this lane's value column
-    const int rb = 32 * quarter;                       // this wave's first key row
+    const int rb = RW * quarter;                       // this wave's first key row
     float* st = dstate + (static_cast<int64_t>(n) * H + h) * kState;
     if (hi < c_lo) {
         // no chunk here; an empty sequence still gets dh0 = dhT (or zeros)
@@ -494,21 +497,21 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         return;
     }
     // dS slab: S[m][i] = dS[rb + 16m + 4g + i][jc]
-    f32x4 S[2];
+    f32x4 S[MS];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MS; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) S[m][i] = st[(rb + 16 * m + 4 * g4 + i) * D + jc];
 
     // The next chunk's operands load into registers while this chunk
     // computes.  Kd, P^T, Qg and W^T are 3584 16-byte units (Kd, then P^T,
     // Qg and W^T contiguous from kOffPt): unit x * 1024 + tid, x < 4, for
-    // the units that exist; dO's 64 x 64 tile is 512 more, one per thread
-    // of the first half.
+    // the units that exist; dO's 64-row tile is C * kCarryTile / 8 more,
+    // one per thread of the first ones.
     constexpr int NUNIT = (C * D + C * C + 2 * D * C) / 8;
     constexpr int PER = (NUNIT + GG - 1) / GG;
-    static_assert(NUNIT == 3584 && PER == 4 && C * kCarryTile / 8 == GG / 2,
-                  "the unit map below");
+    constexpr int DOU = C * kCarryTile / 8, DOP = kCarryTile / 8;
+    static_assert(NUNIT == 3584 && PER == 4 && DOU <= GG, "the unit map below");
     u32x4 pre[PER], pdo = {0u, 0u, 0u, 0u};
     float pgam = 0.f;
     auto fetch = [&](int j) {
@@ -521,10 +524,10 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
             if (u < NUNIT) pre[x] = *reinterpret_cast<const u32x4*>(sp + byte);
         }
         if (tid < D) pgam = reinterpret_cast<const float*>(sp + kOffGam)[tid];
-        if (tid < GG / 2) {
+        if (tid < DOU) {
             const int64_t t0 = t_begin + static_cast<int64_t>(j) * C;
             const int len = static_cast<int>(min<int64_t>(C, t_end - t0));
-            const int r = tid >> 3, part = tid & 7;
+            const int r = tid / DOP, part = tid % DOP;
             pdo = *reinterpret_cast<const u32x4*>(dO + ((t0 + min(r, len - 1)) * H + h) * D +
                                                   tile * kCarryTile + 8 * part);
             if (r >= len) pdo = u32x4{0u, 0u, 0u, 0u};
@@ -551,8 +554,8 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
             *reinterpret_cast<u32x4*>(dst) = pre[x];
         }
         if (tid < D) sm.gam[tid] = pgam;
-        if (tid < GG / 2) {
-            const int r = tid >> 3, part = tid & 7;
+        if (tid < DOU) {
+            const int r = tid / DOP, part = tid % DOP;
             *reinterpret_cast<u32x4*>(sm.dol + r * LDO + 8 * part) = pdo;
         }
     };
@@ -564,19 +567,20 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         // dS' of this chunk (bf16, for the grad pass) and as a bf16 B operand
         bf16_t* dsp = dsblk + slot * kState;
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < MS; ++m) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) dsp[(rb + 16 * m + 4 * g4 + i) * D + jc] = bf(S[m][i]);
             put4t(&sm.dst[slab][ln * LDD + rb + 16 * m + 4 * g4], S[m]);
         }
         __syncthreads();
         if (j > c_lo) fetch(j - 1);
-        // dE = Kd dS' + scale P^T dO  (this slab's 16 columns, row tile `quarter`)
+        // dE = Kd dS' + scale P^T dO  (this slab's 16 columns, this wave's row tiles)
         bf16_t* dep = deblk + slot * (static_cast<int64_t>(C) * D);
         const bf16_t* dsw = sm.dst[slab];
         const bf16_t* dow = sm.dol + 16 * slab;   // dO by rows of K
-        {
-            const int m = quarter;
+#pragma unroll
+        for (int me = 0; me < ME; ++me) {
+            const int m = ME * quarter + me;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = tile_mm<D>(sm.kd + 16 * m * LDD, LDD, dsw, LDD, lane, acc);
             acc = tile_mm<C, kKc, kMc>(sm.pt + 16 * m * LDC, LDC, dow, LDO, lane, acc);
@@ -588,8 +592,8 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         // dS = Diag(gamma) dS' + scale Qg^T dO - W^T dE  (this wave's key rows)
         const bf16_t* dew = sm.det[slab];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-            const int mb = 2 * quarter + m;
+        for (int m = 0; m < MS; ++m) {
+            const int mb = MS * quarter + m;
             f32x4 acc;
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[i] = sm.gam[16 * mb + 4 * g4 + i] * S[m][i];
@@ -603,7 +607,7 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
     if (dst_out) {
         dst_out += c_lo == 0 ? (static_cast<int64_t>(n) * H + h) * kState : 0;
 #pragma unroll
-        for (int m = 0; m < 2; ++m)
+        for (int m = 0; m < MS; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i) dst_out[(rb + 16 * m + 4 * g4 + i) * D + jc] = S[m][i];
     }
@@ -1193,7 +1197,7 @@ int64_t bound_chunks(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) /
 
 // Per-block buffers come in pairs: while the gradient pass of block b reads
 // its pair, the prep and the carry of block b - 1 fill the other.
-constexpr int kRing = 2;
+constexpr int kRing = 3;
 
 struct BwdLayout {
     size_t fwd, sall, slots, dsblk, deblk, dstate, total;
@@ -1257,18 +1261,19 @@ hipError_t aux_stream(hipStream_t* out) {
 // events of one call, released when the call returns (a destroyed event
 // still completes the waits already queued on it)
 struct CallEvents {
-    hipEvent_t prep[kRing] = {}, carry[kRing] = {};
+    hipEvent_t start = nullptr, grad[kRing] = {}, carry[kRing] = {};
     hipError_t create() {
-        for (int i = 0; i < kRing; ++i) {
-            hipError_t e = hipEventCreateWithFlags(&prep[i], hipEventDisableTiming);
+        hipError_t e = hipEventCreateWithFlags(&start, hipEventDisableTiming);
+        for (int i = 0; i < kRing && e == hipSuccess; ++i) {
+            e = hipEventCreateWithFlags(&grad[i], hipEventDisableTiming);
             if (e == hipSuccess) e = hipEventCreateWithFlags(&carry[i], hipEventDisableTiming);
-            if (e != hipSuccess) return e;
         }
-        return hipSuccess;
+        return e;
     }
     ~CallEvents() {
+        if (start) (void)hipEventDestroy(start);
         for (int i = 0; i < kRing; ++i) {
-            if (prep[i]) (void)hipEventDestroy(prep[i]);
+            if (grad[i]) (void)hipEventDestroy(grad[i]);
             if (carry[i]) (void)hipEventDestroy(carry[i]);
         }
     }
@@ -1278,7 +1283,7 @@ struct CallEvents {
 
 int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
     // about 1 GiB of per-block buffers (prep operands and carry outputs:
-    // ~155 KB per (chunk, head), two blocks' worth), at most 64 chunks
+    // ~155 KB per (chunk, head), three blocks' worth), at most 64 chunks
     const size_t per_chunk = static_cast<size_t>(N) * H * kRing *
                              (kSlot + kState * 2 + static_cast<size_t>(C) * D * 2);
     int64_t L = static_cast<int64_t>((size_t{1} << 30) / per_chunk);
@@ -1388,14 +1393,15 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
         if (e != hipSuccess) return e;
     }
 
-    // 2. backward over blocks of chunks, from the last.  Caller's stream:
-    //    prep(b - 1), then grad(b) once carry(b) is done; second stream:
-    //    carry(b) once prep(b) is done.  Ring slot b % 2 holds block b's
-    //    operands and carry outputs; prep(b - 1) and carry(b - 1) reuse the
-    //    slot of block b + 1, whose readers (carry(b + 1), grad(b + 1)) come
-    //    before them in stream order.  The caller's stream ends with
-    //    grad(0), which waits for the last carry: the call's work is whole
-    //    on the caller's stream.
+    // 2. backward over blocks of chunks, from the last.  Second stream:
+    //    prep(b), then carry(b); caller's stream: grad(b) once carry(b) is
+    //    done, so grad(b) runs beside prep(b - 1) and carry(b - 1).  Ring
+    //    slot b % 3 holds block b's operands and carry outputs; prep(b)
+    //    reuses the slot of block b + 3 and first waits for its last
+    //    reader, grad(b + 3).  The second stream starts after the caller's
+    //    earlier work, and the caller's stream ends with grad(0), which
+    //    waits for the last carry: the call's work is whole on the caller's
+    //    stream.
     const int64_t n4 = static_cast<int64_t>(a.N) * a.H * kState / 4;
     hipLaunchKernelGGL(bwd_init_kernel, dim3(static_cast<unsigned>(std::min<int64_t>(4096, (n4 + 255) / 256))),
                        dim3(256), 0, stream, a.dhT, dstate, n4);
@@ -1413,29 +1419,22 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
     auto gk = a.gate == kGateChannel ? bwd_grad_kernel<bf16_t, kGateChannel>
             : a.gate == kGateHead    ? bwd_grad_kernel<bf16_t, kGateHead>
                                      : bwd_grad_kernel<bf16_t, kGateNone>;
-    // prep(b) (nothing to prepare for an empty batch) and the event the
-    // carry of block b waits for
-    auto launch_prep = [&](int64_t b) -> hipError_t {
-        const int r = static_cast<int>(b % kRing);
-        if (a.total_T > 0) {
-            hipLaunchKernelGGL(prep, dim3(chunks), dim3(GT), 0, stream, q, k, a.log_alpha,
-                               a.beta, a.cu_seqlens, a.H, static_cast<int>(b * L_b), L_b,
-                               a.scale, slots[r]);
-            const hipError_t le = hipGetLastError();
-            if (le != hipSuccess) return le;
-        }
-        return hipEventRecord(ev.prep[r], stream);
-    };
-    if ((e = launch_prep(nblk - 1)) != hipSuccess) return e;
+    if ((e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(serial, ev.start, 0)) != hipSuccess) return e;
     for (int64_t b = nblk - 1; b >= 0; --b) {
         const int c_lo = static_cast<int>(b * L_b), r = static_cast<int>(b % kRing);
-        if ((e = hipStreamWaitEvent(serial, ev.prep[r], 0)) != hipSuccess) return e;
+        if (b + kRing < nblk && (e = hipStreamWaitEvent(serial, ev.grad[r], 0)) != hipSuccess)
+            return e;
+        if (a.total_T > 0) {    // nothing to prepare for an empty batch
+            hipLaunchKernelGGL(prep, dim3(chunks), dim3(GT), 0, serial, q, k, a.log_alpha,
+                               a.beta, a.cu_seqlens, a.H, c_lo, L_b, a.scale, slots[r]);
+            if ((e = hipGetLastError()) != hipSuccess) return e;
+        }
         hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>(a.N * a.H * (D / kCarryTile))),
                            dim3(GG), 0, serial, slots[r], dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
                            dstate, dsblk[r], deblk[r], a.dh0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         if ((e = hipEventRecord(ev.carry[r], serial)) != hipSuccess) return e;
-        if (b > 0 && (e = launch_prep(b - 1)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(stream, ev.carry[r], 0)) != hipSuccess) return e;
         if (a.total_T == 0) continue;
         hipLaunchKernelGGL(gk, dim3(chunks), dim3(GG), 0, stream, slots[r], dsblk[r], deblk[r],
@@ -1443,6 +1442,7 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
                            L_b, a.scale, static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
                            static_cast<bf16_t*>(a.dv), a.dlog_alpha, a.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        if ((e = hipEventRecord(ev.grad[r], stream)) != hipSuccess) return e;
     }
     return hipSuccess;
 }

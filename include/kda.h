@@ -408,8 +408,8 @@ int kda_decode_multi(const void *q, const void *k, const void *v,
  * Bytes of device workspace kda_bwd needs for these sizes and options:
  * the start state of every chunk (one bf16 state per (chunk, head), so
  * 512 MiB per 16,384 head-chunks), the forward pass's operand block, and
- * two blocks of per-(chunk, head) backward operands (one filled while the
- * other is consumed); with the front-end, also the activated inputs it
+ * three blocks of per-(chunk, head) backward operands (one filled while
+ * the others are consumed); with the front-end, also the activated inputs it
  * produces (normalised q and k in bf16, log_alpha and beta in fp32, each
  * when its part is on; only whether options->front's pointers are set
  * matters here).  0 for arguments kda_bwd would reject.
@@ -457,8 +457,8 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * (normalised q and k are stored in bf16), and the chain rule through them
  * is applied to the gradients afterwards.  Requirements and errors as for
  * kda_fwd_prefill_ex's front-end.
- * Streams: the serial state-adjoint pass runs on a second stream of the
- * device (created by the library on first use, default priority, kept for
+ * Streams: the per-block operand pass and the serial state-adjoint pass
+ * run on a second stream of the device (created by the library on first use, default priority, kept for
  * the process), ordered against the caller's stream by events; all of the
  * call's work is complete once the caller's stream reaches the point after
  * the call.
