@@ -530,8 +530,8 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
     gradients with respect to the raw q and k, dlog_alpha with respect to
     gate_pre (fp32, its layout) and dbeta with respect to beta_pre.
     ``chunk_states``: the record a prefill(..., chunk_states=...) call wrote
-    on these same inputs; the forward pass is then not recomputed (not with
-    the front-end)."""
+    on these same inputs (with the same front-end options); the forward
+    pass is then not recomputed."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3:

@@ -506,7 +506,6 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_
                     &fe, &la_needed, &beta_needed, &r_gp, &r_bp) != KDA_STATUS_OK)
         return 0;
     const bool states = options && options->chunk_states;
-    if (states && fe.active()) return 0;
     return kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe, states);
 }
 
@@ -543,7 +542,6 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     const int bs = bwd_block_chunks(total_T, N, H, options, &L_b);
     if (bs != KDA_STATUS_OK) return bs;
     const void* states = options ? options->chunk_states : nullptr;
-    if (states && fe.active()) return KDA_STATUS_UNSUPPORTED;
     if (states && !aligned16(states)) return KDA_STATUS_MISALIGNED;
     const size_t need = kda::bwd_workspace_bytes(total_T, N, H, L_b, gate, fe, states != nullptr);
 

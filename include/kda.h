@@ -445,9 +445,9 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * Saved states (options->chunk_states): the record of the forward pass on
  * these inputs replaces its recomputation (the call then reads the record
  * and needs a smaller workspace); the record must come from a forward pass
- * on the same q, k, v, gates, beta, h0 and cu_seqlens.  Not with the
- * front-end [UNSUPPORTED]; 16-byte aligned [MISALIGNED]; no output may
- * overlap it [INVALID_ARGUMENT].
+ * on the same q, k, v, gates, beta, h0 and cu_seqlens (and, with the
+ * front-end, the same front-end options).  16-byte aligned [MISALIGNED];
+ * no output may overlap it [INVALID_ARGUMENT].
  * Front-end (options->front, as for kda_fwd_prefill_ex): q and k are the raw
  * inputs when l2norm_qk is set, and dq, dk the gradients with respect to
  * them; with gate_pre, log_alpha must be NULL and dlog_alpha (fp32, the

@@ -518,7 +518,7 @@ def test_backward_chunk_states_checks():
                            ctypes.byref(opts), args["stream"])
     assert call(REC) == WS_SMALL                                  # every check passed
     assert call(REC + 4) == MISALIGNED
-    assert call(REC, front=(1, 0.0, None, None)) == UNSUPPORTED   # not with the front-end
+    assert call(REC, front=(1, 0.0, None, None)) == WS_SMALL      # with the front-end too
     assert call(REC, dq=REC + 4096) == INVALID                    # an output on the record
     assert call(REC, ws=REC + 256, wsb=1 << 34) == INVALID        # the workspace on it
 
@@ -530,5 +530,7 @@ def test_backward_chunk_states_workspace():
     rec = kda.backward_workspace_bytes(T, N, H, 128, 128, chunk_states=True)
     assert 0 < rec < full
     assert full - rec >= T // 64 * H * 128 * 128 * 2
+    # the front-end's activated copies come on top, as without the record
+    up = lambda x: (x + 255) // 256 * 256
     assert kda.backward_workspace_bytes(T, N, H, 128, 128, chunk_states=True,
-                                        l2norm_qk=True) == 0
+                                        l2norm_qk=True) == rec + 2 * up(T * H * 256)

@@ -126,3 +126,32 @@ def test_backward_front_end_empty_batch():
                      cu_seqlens=cu, l2norm_qk=True, gate_pre=z(0, H, d), gate_scale=C_GATE,
                      beta_pre=z(0, H))
     assert torch.equal(g["dh0"], dhT)
+
+
+@pytest.mark.parametrize("parts,gate", [((True, True, True), "channel"),
+                                        ((True, True, True), "head")])
+def test_backward_front_end_from_saved_chunk_states(parts, gate):
+    """A prefill through the front-end that saves its chunk states, then the
+    backward through the same front-end from that record: the oracle's
+    gradients at the same bar, and close to the backward that recomputes
+    the forward pass (the record is bf16 either way)."""
+    inp = case(parts, gate, 510)
+    T, N, H = inp["q"].shape[0], len(LENS), 2
+    rec = torch.empty(kda.chunk_states_bytes(T, N, H), dtype=torch.uint8, device=DEV)
+    fe = dict(gate=gate, l2norm_qk=parts[0], gate_pre=inp["gp"], gate_scale=C_GATE,
+              beta_pre=inp["bp"])
+    kda.prefill(inp["q"], inp["k"], inp["v"], inp["la"], inp["beta"], h0=inp["h0"],
+                cu_seqlens=inp["cu"], chunk_states=rec, **fe)
+    args = (inp["q"], inp["k"], inp["v"], inp["la"], inp["beta"], inp["do"])
+    kw = dict(h0=inp["h0"], dhT=inp["dhT"], cu_seqlens=inp["cu"], **fe)
+    g = kda.backward(*args, chunk_states=rec, **kw)
+    base = kda.backward(*args, **kw)
+    r = reference(inp, parts)
+    errs = {key: rel_err(host(g[key]), r[key]) for key in r}
+    near = {key: rel_err(host(g[key]), host(base[key]).astype(np.float64)) for key in r}
+    report("backward front-end from saved states %s %s" % (gate, parts), **errs)
+    report("  against the recomputing backward", **near)
+    for key, e in errs.items():
+        assert e <= TOL, (key, e)
+    for key, e in near.items():
+        assert e <= 1e-2, (key, e)
