@@ -455,6 +455,7 @@ def test_chunk_states_bytes():
     assert kda.chunk_states_bytes(0, 3, 1) == (3 + 0 + 1) * 128 * 128 * 2
     assert kda.chunk_states_bytes(100, 2, 4, 64, 64) == 0     # d = 128 only
     assert kda.chunk_states_bytes(100, 0, 4) == 0             # invalid sizes
+    assert kda.chunk_states_bytes(1 << 50, 1, 1 << 14) == 0   # overflow
 
 
 def rec_prefill_call(path, rec=REC, snap=(0, 0, None), **over):
