@@ -5,10 +5,12 @@ the ``cpu_baseline`` leg of ``bench.py`` may import this package.  The GPU
 product path (``gated_delta_rule_05_amd``) never imports it, and this package
 imports nothing from there.
 
-The arithmetic lives in ``kda_oracle.c`` (a plain per-token recurrence in
-double precision, following the step list of "Kimi Delta Attention: la
-atencion lineal detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta
-Attention paso a paso").  This module only builds that file with gcc and
+The arithmetic lives in ``kda_oracle.c``: the per-token recurrence
+S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T, o_t = scale S_t^T q,
+in double precision ("Kimi Delta Attention: la atencion lineal detras de Kimi
+K2 y Qwen3", section "Cómo funciona Kimi Delta Attention paso a paso"; the
+diagonal-plus-low-rank transition of "Cos'è Kimi Delta Attention (KDA)?",
+section "Gating per canale: cosa rende KDA diverso").  This module only builds that file with gcc and
 marshals numpy arrays into it.
 
 The gradients live in ``kda_oracle_bwd.c``: the reverse-mode derivative of
@@ -21,8 +23,9 @@ Pins (the tests that tie this oracle to something other than itself) live in
 ``tests/test_oracle_bwd_pins.py``: a brute-force product of explicit transition
 matrices, the DeltaNet and Gated DeltaNet special cases, the beta = 0 closed
 form, the beta = 1 read-back, the basis-key closed form, linearity, the
-stability bound and a hand-derived worked example; the front-end's chain
-rule is pinned by finite differences in
+stability bound and a hand-derived worked example; the several-token
+decode wrapper is pinned against one decode_step per token and sequence; the
+front-end's chain rule is pinned by finite differences in
 ``tests/test_oracle_front_bwd_pins.py``.
 """
 from __future__ import annotations

@@ -7,33 +7,27 @@
  * path never calls it, and it shares no code, header or constant with the
  * GPU path.
  *
- * What it computes (the per-token definition, nothing more):
- *   "Kimi Delta Attention: la atencion lineal detras de Kimi K2 y Qwen3",
- *   section "Cómo funciona Kimi Delta Attention paso a paso" (prose, the
- *   kda_step listing and the flowchart): for every token the state is first
- *   decayed channel by channel, the decayed state predicts a value for the
- *   current key, the prediction error is scaled by beta, the error is written
- *   back along the key, and the output reads the corrected state with the
- *   query scaled by 1/sqrt(d_k).
+ * What it computes (the per-token definition, nothing more): for every
+ * token t of a sequence and every head, the state S (d_k x d_v) moves by
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = scale * S_t^T q_t,          alpha_t = exp(log_alpha_t),
+ * i.e. a per-key-channel decay of the previous state corrected by a delta
+ * rule scaled by beta_t ("Kimi Delta Attention: la atencion lineal detras
+ * de Kimi K2 y Qwen3", TL;DR and section "Cómo funciona Kimi Delta
+ * Attention paso a paso"; the transition is the diagonal-plus-low-rank
+ * matrix of "Cos'è Kimi Delta Attention (KDA)?", section "Gating per
+ * canale: cosa rende KDA diverso", which is also where the per-channel
+ * gate is set apart from Gated DeltaNet's per-head one).  The first page
+ * scales the query by 1/sqrt(d_k); here the scale is an argument.
  *
- *   The state is stored here as S[c][j], c = key channel (d_k rows),
- *   j = value channel (d_v columns).  The listing on that page keeps the
- *   transpose (d_v x d_k) and decays along its key axis; both describe the
- *   same map:
- *       S~    = Diag(alpha_t) S_{t-1}            alpha_t = exp(log_alpha_t)
- *       vhat  = S~^T k_t
- *       e     = beta_t (v_t - vhat)
- *       S_t   = S~ + k_t e^T
- *       o_t   = scale * S_t^T q_t
- *   which is S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T.
- *   The per-key-channel gate is the feature that separates KDA from Gated
- *   DeltaNet ("Cos'è Kimi Delta Attention (KDA)?", section "Gating per
- *   canale: cosa rende KDA diverso").
+ * The state is stored as S[c][j], c = key channel (rows), j = value
+ * channel (columns), so Diag(alpha_t) scales rows.  The first page keeps
+ * the transpose (d_v x d_k) and decays along its key axis: the same map.
  *
  * Numbers: every input arrives as float32 (bf16 and fp32 stored values
  * widen to float32 exactly) and is widened to double; all arithmetic and
  * all outputs are double.  The output scale is an argument; callers pass
- * 1/sqrt(d_k) to follow the listing.
+ * 1/sqrt(d_k) to follow the first page.
  *
  * Layouts (row-major, contiguous):
  *   q, k        [total_T][H][d_k]
@@ -67,36 +61,39 @@ typedef struct {
     int failed;
 } job_t;
 
-/* One token of the recurrence on state S (d_k x d_v), in the order the
- * per-token definition gives: decay, predict, error, correct, read. */
-static void kda_token(double *S, double *vhat, double *e, int64_t dk, int64_t dv,
+/* One token: S <- M S + beta k v^T with the transition
+ * M = (I - beta k k^T) Diag(alpha), then o = scale S^T q.
+ *
+ * M is a diagonal matrix plus a rank-one term, the DPLR structure the
+ * second page names for KDA's per-channel gate.  Expanding it,
+ *   M S + beta k v^T = Diag(alpha) S + k w^T,   w = beta (v - S^T Diag(alpha) k),
+ * so the token costs two sweeps over the state: the first forms the
+ * row vector u = k^T Diag(alpha) S, the second rewrites every key row c as
+ * alpha_c S[c,:] + k_c w and adds q_c times the new row into o. */
+static void kda_token(double *S, double *u, double *w, int64_t dk, int64_t dv,
                       const float *q, const float *k, const float *v,
                       const float *log_alpha, double beta, double scale,
                       double *o)
 {
-    /* 1. decay every key channel (row c) by its own alpha */
+    for (int64_t j = 0; j < dv; ++j) u[j] = 0.0;
     for (int64_t c = 0; c < dk; ++c) {
-        double a = exp((double)log_alpha[c]);
-        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= a;
+        const double ac = exp((double)log_alpha[c]);
+        const double kc = (double)k[c];
+        const double *row = S + c * dv;
+        for (int64_t j = 0; j < dv; ++j) u[j] += (ac * row[j]) * kc;
     }
-    /* 2. what the decayed state recalls for this key: vhat = S~^T k */
-    for (int64_t j = 0; j < dv; ++j) vhat[j] = 0.0;
-    for (int64_t c = 0; c < dk; ++c) {
-        double kc = (double)k[c];
-        for (int64_t j = 0; j < dv; ++j) vhat[j] += S[c * dv + j] * kc;
-    }
-    /* 3. scaled error between the true and the recalled value */
-    for (int64_t j = 0; j < dv; ++j) e[j] = beta * ((double)v[j] - vhat[j]);
-    /* 4. delta-rule correction: S = S~ + k e^T */
-    for (int64_t c = 0; c < dk; ++c) {
-        double kc = (double)k[c];
-        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] += kc * e[j];
-    }
-    /* 5. read the corrected state with the scaled query: o = scale S^T q */
+    for (int64_t j = 0; j < dv; ++j) w[j] = beta * ((double)v[j] - u[j]);
+
     for (int64_t j = 0; j < dv; ++j) o[j] = 0.0;
     for (int64_t c = 0; c < dk; ++c) {
-        double qc = (double)q[c];
-        for (int64_t j = 0; j < dv; ++j) o[j] += S[c * dv + j] * qc;
+        const double ac = exp((double)log_alpha[c]);
+        const double kc = (double)k[c], qc = (double)q[c];
+        double *row = S + c * dv;
+        for (int64_t j = 0; j < dv; ++j) {
+            const double s = ac * row[j] + kc * w[j];
+            row[j] = s;
+            o[j] += s * qc;
+        }
     }
     for (int64_t j = 0; j < dv; ++j) o[j] *= scale;
 }
@@ -105,9 +102,9 @@ static int run_pair(job_t *J, int64_t n, int64_t h)
 {
     const int64_t dk = J->dk, dv = J->dv, H = J->H;
     double *S = (double *)malloc((size_t)(dk * dv) * sizeof(double));
-    double *vhat = (double *)malloc((size_t)dv * sizeof(double));
-    double *e = (double *)malloc((size_t)dv * sizeof(double));
-    if (!S || !vhat || !e) { free(S); free(vhat); free(e); return 1; }
+    double *u = (double *)malloc((size_t)dv * sizeof(double));
+    double *w = (double *)malloc((size_t)dv * sizeof(double));
+    if (!S || !u || !w) { free(S); free(u); free(w); return 1; }
 
     const int64_t sidx = (n * H + h) * dk * dv;
     if (J->h0) memcpy(S, J->h0 + sidx, (size_t)(dk * dv) * sizeof(double));
@@ -115,13 +112,13 @@ static int run_pair(job_t *J, int64_t n, int64_t h)
 
     for (int64_t t = J->cu_seqlens[n]; t < J->cu_seqlens[n + 1]; ++t) {
         const int64_t th = t * H + h;
-        kda_token(S, vhat, e, dk, dv,
+        kda_token(S, u, w, dk, dv,
                   J->q + th * dk, J->k + th * dk, J->v + th * dv,
                   J->log_alpha + th * dk, (double)J->beta[th], J->scale,
                   J->o + th * dv);
     }
     if (J->hT) memcpy(J->hT + sidx, S, (size_t)(dk * dv) * sizeof(double));
-    free(S); free(vhat); free(e);
+    free(S); free(u); free(w);
     return 0;
 }
 
@@ -197,13 +194,13 @@ int kdaref_decode_step(const float *q, const float *k, const float *v,
                        double scale, double *o)
 {
     if (N < 0 || H <= 0 || dk <= 0 || dv <= 0 || !S) return 2;
-    double *vhat = (double *)malloc((size_t)dv * sizeof(double));
-    double *e = (double *)malloc((size_t)dv * sizeof(double));
-    if (!vhat || !e) { free(vhat); free(e); return 1; }
+    double *u = (double *)malloc((size_t)dv * sizeof(double));
+    double *w = (double *)malloc((size_t)dv * sizeof(double));
+    if (!u || !w) { free(u); free(w); return 1; }
     for (int64_t nh = 0; nh < N * H; ++nh)
-        kda_token(S + nh * dk * dv, vhat, e, dk, dv,
+        kda_token(S + nh * dk * dv, u, w, dk, dv,
                   q + nh * dk, k + nh * dk, v + nh * dv,
                   log_alpha + nh * dk, (double)beta[nh], scale, o + nh * dv);
-    free(vhat); free(e);
+    free(u); free(w);
     return 0;
 }

@@ -6,21 +6,27 @@
  * smoke check and the benchmark's CPU leg may load it, and it shares no
  * code, header or constant with the GPU path.
  *
- * What it computes: the reverse-mode derivative of the per-token definition
- * in "Kimi Delta Attention: la atencion lineal detras de Kimi K2 y Qwen3",
- * section "Cómo funciona Kimi Delta Attention paso a paso" (decay, predict,
- * error, correct, read), taken step by step in reverse order.  With the
- * state stored S[c][j] (c = key channel, j = value channel):
+ * What it computes: the reverse-mode derivative of the per-token
+ * recurrence S_t = (I - beta k k^T) Diag(alpha) S_{t-1} + beta k v^T,
+ * o_t = scale S_t^T q ("Kimi Delta Attention: la atencion lineal detras de
+ * Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta Attention paso a
+ * paso"; the diagonal-plus-low-rank transition of "Cos'è Kimi Delta
+ * Attention (KDA)?", section "Gating per canale: cosa rende KDA diverso").
+ * With the state stored S[c][j] (c = key channel, j = value channel), one
+ * token expands into
  *
- *   forward            S~ = Diag(alpha) S_prev, vhat = S~^T k,
- *                      e = beta (v - vhat), S = S~ + k e^T, o = scale S^T q
- *   backward, given L = the adjoint of S after this token (from the later
- *   tokens, or dhT after the last one) and dO = the adjoint of o:
- *     read:     L  += scale q dO^T;          dq = scale S dO
- *     correct:  dS~ = L;  dk = L e;  de = L^T k
- *     error:    dbeta = de . (v - vhat);  dv = beta de;  dvhat = -beta de
- *     predict:  dS~ += k dvhat^T;  dk += S~ dvhat
- *     decay:    dlog_alpha[c] = sum_j dS~[c][j] S~[c][j];  L = Diag(alpha) dS~
+ *   D = Diag(alpha) S_prev,  u = D^T k,  r = v - u,  w = beta r,
+ *   S = D + k w^T,           o = scale S^T q,
+ *
+ * and the adjoints run through those definitions in reverse; given
+ * L = the adjoint of S (from the later tokens, or dhT after the last one)
+ * and dO = the adjoint of o:
+ *     o = scale S^T q:   L  += scale q dO^T;        dq = scale S dO
+ *     S = D + k w^T:     dD  = L;  dk = L w;        dw = L^T k
+ *     w = beta (v - u):  dbeta = dw . r;  dv = beta dw;  du = -beta dw
+ *     u = D^T k:         dD += k du^T;    dk += D du
+ *     D = Diag(alpha) S_prev:  dlog_alpha[c] = sum_j dD[c][j] D[c][j];
+ *                        L = Diag(alpha) dD
  *   and after the first token of the sequence dh0 = L.
  *
  * The states before each token are needed in reverse order: the forward
@@ -55,22 +61,22 @@ typedef struct {
 } bjob_t;
 
 /* forward of one token on S (in place), keeping what the backward needs:
- * the decayed state St, the prediction error r = v - vhat and e = beta r */
-static void fwd_token(double *S, double *St, double *r, double *e, int64_t dk, int64_t dv,
+ * the decayed state D, the residual r = v - D^T k and w = beta r */
+static void fwd_token(double *S, double *D, double *r, double *w, int64_t dk, int64_t dv,
                       const float *k, const float *v, const float *la, double beta)
 {
     for (int64_t c = 0; c < dk; ++c) {
         const double a = exp((double)la[c]);
-        for (int64_t j = 0; j < dv; ++j) St[c * dv + j] = a * S[c * dv + j];
+        for (int64_t j = 0; j < dv; ++j) D[c * dv + j] = a * S[c * dv + j];
     }
     for (int64_t j = 0; j < dv; ++j) {
-        double vh = 0.0;
-        for (int64_t c = 0; c < dk; ++c) vh += St[c * dv + j] * (double)k[c];
-        r[j] = (double)v[j] - vh;
-        e[j] = beta * r[j];
+        double u = 0.0;
+        for (int64_t c = 0; c < dk; ++c) u += D[c * dv + j] * (double)k[c];
+        r[j] = (double)v[j] - u;
+        w[j] = beta * r[j];
     }
     for (int64_t c = 0; c < dk; ++c)
-        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] = St[c * dv + j] + (double)k[c] * e[j];
+        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] = D[c * dv + j] + (double)k[c] * w[j];
 }
 
 static int run_pair(bjob_t *J, int64_t n, int64_t h)
@@ -80,14 +86,14 @@ static int run_pair(bjob_t *J, int64_t n, int64_t h)
     const int64_t nseg = (len + kSeg - 1) / kSeg;
     double *ck = (double *)malloc((size_t)((nseg > 0 ? nseg : 1) * SE) * sizeof(double));
     double *segS = (double *)malloc((size_t)((kSeg + 1) * SE) * sizeof(double));
-    double *St = (double *)malloc((size_t)SE * sizeof(double));
+    double *D = (double *)malloc((size_t)SE * sizeof(double));
     double *L = (double *)malloc((size_t)SE * sizeof(double));
-    double *dSt = (double *)malloc((size_t)SE * sizeof(double));
+    double *dD = (double *)malloc((size_t)SE * sizeof(double));
     double *r = (double *)malloc((size_t)dv * sizeof(double));
-    double *e = (double *)malloc((size_t)dv * sizeof(double));
-    double *de = (double *)malloc((size_t)dv * sizeof(double));
+    double *w = (double *)malloc((size_t)dv * sizeof(double));
+    double *dw = (double *)malloc((size_t)dv * sizeof(double));
     int rc = 0;
-    if (!ck || !segS || !St || !L || !dSt || !r || !e || !de) { rc = 1; goto out; }
+    if (!ck || !segS || !D || !L || !dD || !r || !w || !dw) { rc = 1; goto out; }
 
     /* forward: checkpoint the state before every kSeg-th token */
     {
@@ -98,7 +104,7 @@ static int run_pair(bjob_t *J, int64_t n, int64_t h)
         for (int64_t t = t0; t < t1; ++t) {
             if ((t - t0) % kSeg == 0) memcpy(ck + ((t - t0) / kSeg) * SE, S, (size_t)SE * sizeof(double));
             const int64_t th = t * H + h;
-            fwd_token(S, St, r, e, dk, dv, J->k + th * dk, J->v + th * dv,
+            fwd_token(S, D, r, w, dk, dv, J->k + th * dk, J->v + th * dv,
                       J->log_alpha + th * dk, (double)J->beta[th]);
         }
         if (J->dhT) memcpy(L, J->dhT + sidx, (size_t)SE * sizeof(double));
@@ -114,7 +120,7 @@ static int run_pair(bjob_t *J, int64_t n, int64_t h)
         for (int64_t t = a0; t + 1 < a1; ++t) {
             const int64_t i = t - a0, th = t * H + h;
             memcpy(segS + (i + 1) * SE, segS + i * SE, (size_t)SE * sizeof(double));
-            fwd_token(segS + (i + 1) * SE, St, r, e, dk, dv, J->k + th * dk, J->v + th * dv,
+            fwd_token(segS + (i + 1) * SE, D, r, w, dk, dv, J->k + th * dk, J->v + th * dv,
                       J->log_alpha + th * dk, (double)J->beta[th]);
         }
         for (int64_t t = a1 - 1; t >= a0; --t) {
@@ -127,9 +133,9 @@ static int run_pair(bjob_t *J, int64_t n, int64_t h)
              * before token i+1, which the reverse walk has already used */
             double *S = segS + (i + 1) * SE;
             memcpy(S, segS + i * SE, (size_t)SE * sizeof(double));
-            fwd_token(S, St, r, e, dk, dv, k, v, la, beta);
+            fwd_token(S, D, r, w, dk, dv, k, v, la, beta);
 
-            /* read: o = scale S^T q */
+            /* o = scale S^T q */
             for (int64_t c = 0; c < dk; ++c) {
                 double acc = 0.0;
                 for (int64_t j = 0; j < dv; ++j) {
@@ -138,35 +144,35 @@ static int run_pair(bjob_t *J, int64_t n, int64_t h)
                 }
                 J->dq[th * dk + c] = J->scale * acc;
             }
-            /* correct: S = S~ + k e^T */
+            /* S = D + k w^T */
             for (int64_t j = 0; j < dv; ++j) {
                 double acc = 0.0;
                 for (int64_t c = 0; c < dk; ++c) acc += L[c * dv + j] * (double)k[c];
-                de[j] = acc;
+                dw[j] = acc;
             }
             double db = 0.0;
             for (int64_t j = 0; j < dv; ++j) {
-                db += de[j] * r[j];                       /* error: e = beta (v - vhat) */
-                J->dv_[th * dv + j] = beta * de[j];
+                db += dw[j] * r[j];                       /* w = beta (v - u) */
+                J->dv_[th * dv + j] = beta * dw[j];
             }
             J->dbeta[th] = db;
             for (int64_t c = 0; c < dk; ++c) {
                 double dkc = 0.0;
                 for (int64_t j = 0; j < dv; ++j) {
-                    const double dvhat = -beta * de[j];
-                    dkc += L[c * dv + j] * e[j];          /* correct: dk = L e */
-                    dkc += St[c * dv + j] * dvhat;        /* predict: dk += S~ dvhat */
-                    dSt[c * dv + j] = L[c * dv + j] + (double)k[c] * dvhat;
+                    const double du = -beta * dw[j];
+                    dkc += L[c * dv + j] * w[j];          /* from S = D + k w^T */
+                    dkc += D[c * dv + j] * du;            /* from u = D^T k */
+                    dD[c * dv + j] = L[c * dv + j] + (double)k[c] * du;
                 }
                 J->dk_[th * dk + c] = dkc;
             }
-            /* decay: S~ = Diag(alpha) S_prev */
+            /* D = Diag(alpha) S_prev */
             for (int64_t c = 0; c < dk; ++c) {
                 const double a = exp((double)la[c]);
                 double g = 0.0;
                 for (int64_t j = 0; j < dv; ++j) {
-                    g += dSt[c * dv + j] * St[c * dv + j];
-                    L[c * dv + j] = a * dSt[c * dv + j];
+                    g += dD[c * dv + j] * D[c * dv + j];
+                    L[c * dv + j] = a * dD[c * dv + j];
                 }
                 J->dla[th * dk + c] = g;
             }
@@ -174,7 +180,7 @@ static int run_pair(bjob_t *J, int64_t n, int64_t h)
     }
     if (J->dh0) memcpy(J->dh0 + (n * H + h) * SE, L, (size_t)SE * sizeof(double));
 out:
-    free(ck); free(segS); free(St); free(L); free(dSt); free(r); free(e); free(de);
+    free(ck); free(segS); free(D); free(L); free(dD); free(r); free(w); free(dw);
     return rc;
 }
 

@@ -150,13 +150,13 @@ MUTANTS = {
                                "L[c * dv + j] += 0.0 * (double)q[c] * dO[j];", 1),
     "dq from the state before the token": ("acc += S[c * dv + j] * dO[j];",
                                            "acc += segS[i * SE + c * dv + j] * dO[j];", 1),
-    "dbeta from the error, not the residual": ("db += de[j] * r[j];", "db += de[j] * e[j];", 1),
-    "predict term of dk dropped": ("dkc += St[c * dv + j] * dvhat;",
-                                   "dkc += 0.0 * St[c * dv + j] * dvhat;", 1),
-    "state adjoint not decayed": ("L[c * dv + j] = a * dSt[c * dv + j];",
-                                  "L[c * dv + j] = dSt[c * dv + j];", 1),
-    "gate gradient from the undecayed state": ("g += dSt[c * dv + j] * St[c * dv + j];",
-                                               "g += dSt[c * dv + j] * segS[i * SE + c * dv + j];", 1),
+    "dbeta from the error, not the residual": ("db += dw[j] * r[j];", "db += dw[j] * w[j];", 1),
+    "predict term of dk dropped": ("dkc += D[c * dv + j] * du;",
+                                   "dkc += 0.0 * D[c * dv + j] * du;", 1),
+    "state adjoint not decayed": ("L[c * dv + j] = a * dD[c * dv + j];",
+                                  "L[c * dv + j] = dD[c * dv + j];", 1),
+    "gate gradient from the undecayed state": ("g += dD[c * dv + j] * D[c * dv + j];",
+                                               "g += dD[c * dv + j] * segS[i * SE + c * dv + j];", 1),
     "dhT ignored": ("if (J->dhT) memcpy", "if (0) memcpy", 1),
 }
 

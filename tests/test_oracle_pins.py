@@ -332,24 +332,119 @@ def test_decode_step_equals_one_token_prefill():
     assert np.array_equal(on, oz) and np.array_equal(Sn, Sz)
 
 
+def _chained_decode(q, k, v, la, beta, S, lengths, scale):
+    """Several decode tokens per sequence, one decode_step call per token
+    and per sequence (no re-indexing of a packed batch): the plain meaning of
+    applying a sequence's first lengths[n] tokens in order."""
+    N, m, H = q.shape[:3]
+    dv = v.shape[-1]
+    o = np.full((N, m, H, dv), np.nan)
+    S_out = np.array(S, dtype=np.float64, copy=True)
+    for n in range(N):
+        L = m if lengths is None else min(max(int(lengths[n]), 0), m)
+        Sn = S_out[n:n + 1]
+        for t in range(L):
+            g = None if la is None else la[n:n + 1, t]
+            o[n, t], Sn = oracle.decode_step(q[n:n + 1, t], k[n:n + 1, t], v[n:n + 1, t], g,
+                                             beta[n:n + 1, t], Sn, scale=scale)
+        S_out[n:n + 1] = Sn
+    return o, S_out
+
+
+def _decode_multi_matches_chain(mod, gate, lengths, seed):
+    rng = np.random.default_rng(seed)
+    N, m, H, dk, dv = 6, 4, 2, 5, 3
+    q, k, v, la, beta = rand_case(rng, N * m, H, dk, dv)
+    shp = lambda x: x.reshape((N, m) + x.shape[1:])
+    q, k, v, la, beta = shp(q), shp(k), shp(v), shp(la), shp(beta)
+    if gate == "head":
+        la = f32(rng.uniform(-0.4, 0.0, (N, m, H)))
+    elif gate == "none":
+        la = None
+    S = rng.standard_normal((N, H, dk, dv))
+    o, S1 = mod.decode_multi(q, k, v, la, beta, S, lengths=lengths, scale=0.6)
+    oc, Sc = _chained_decode(q, k, v, la, beta, S, lengths, 0.6)
+    same_nan = np.array_equal(np.isnan(o), np.isnan(oc))
+    return (same_nan and np.array_equal(np.nan_to_num(o), np.nan_to_num(oc))
+            and np.array_equal(S1, Sc))
+
+
+@pytest.mark.parametrize("gate", ["channel", "head", "none"])
+@pytest.mark.parametrize("lengths", [None, [-2, 0, 1, 3, 4, 9], [4, 4, 0, 2, 1, 3]])
+def test_decode_multi_equals_chained_decode_steps(gate, lengths):
+    """decode_multi re-indexes [N, m, H, .] tokens into a packed prefill;
+    it must equal one decode_step per token and sequence: all m tokens
+    without lengths, the first clamp(lengths[n], 0, m) otherwise, NaN in the
+    rows of tokens not applied, the state untouched for a sequence that
+    applies none ("Kimi Linear acaba de superar a la atención completa en sus
+    propios términos", section "Qué observar tras el lanzamiento de Kimi
+    Linear": verifying and committing draft tokens must give the tokens'
+    own recurrence)."""
+    assert _decode_multi_matches_chain(oracle, gate, lengths, seed=31)
+
+
+# planted mistakes in the re-indexing wrapper (oracle/__init__.py)
+WRAPPER_MUTANTS = {
+    "clamp one short": ("np.clip(np.asarray(lengths, dtype=np.int64), 0, m)",
+                        "np.clip(np.asarray(lengths, dtype=np.int64), 0, m - 1)", 1),
+    "tokens taken sequence-minor": ("take = np.concatenate([n * m + np.arange(lens[n]) for n in range(N)])",
+                                    "take = np.concatenate([np.arange(lens[n]) * N + n for n in range(N)])", 1),
+    "outputs scattered to the first rows": ("o[take] = o_t", "o[:len(take)] = o_t", 1),
+    "head gate read as the first channel of a per-channel gate":
+        ("if la is not None and la.shape[-1] == 1 and np.asarray(log_alpha).ndim == 3:",
+         "if False:", 1),
+}
+
+
+def test_decode_multi_planted_mistakes_are_caught(tmp_path):
+    """Each planted mistake in decode_multi's re-indexing fails the chained
+    comparison above for at least one gate layout and length vector."""
+    import importlib.util
+    here = os.path.dirname(oracle.__file__)
+    src = open(oracle.__file__).read()
+    for name, (old, new, count) in WRAPPER_MUTANTS.items():
+        assert src.count(old) == count, "mutation anchor not found: " + name
+        d = tmp_path / re.sub(r"\W+", "_", name)
+        d.mkdir()
+        (d / "__init__.py").write_text(src.replace(old, new))
+        for f in ("libkda_oracle.so",):
+            os.symlink(os.path.join(here, f), d / f)
+        spec = importlib.util.spec_from_file_location("dm_mutant_" + d.name, str(d / "__init__.py"))
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        caught = False
+        for gate in ("channel", "head", "none"):
+            for lengths in ([-2, 0, 1, 3, 4, 9], [4, 4, 0, 2, 1, 3]):
+                try:
+                    ok = _decode_multi_matches_chain(mod, gate, lengths, seed=31)
+                except Exception:
+                    ok = False
+                caught |= not ok
+        assert caught, "planted mistake not caught: " + name
+
+
 # --------------------------------------------------------------------------
 # mutation checks: planted mistakes must be caught by the pins above
 # --------------------------------------------------------------------------
 MUTANTS = {
-    "error sign flipped": ("e[j] = beta * ((double)v[j] - vhat[j]);",
-                           "e[j] = beta * ((double)v[j] + vhat[j]);", 1),
-    "beta dropped": ("e[j] = beta * (", "e[j] = 1.0 * (", 1),
-    "decay exponent sign": ("double a = exp((double)log_alpha[c]);",
-                            "double a = exp(-(double)log_alpha[c]);", 1),
-    "predict with the query": ("double kc = (double)k[c];\n        for (int64_t j = 0; j < dv; ++j) vhat[j]",
-                               "double kc = (double)q[c];\n        for (int64_t j = 0; j < dv; ++j) vhat[j]", 1),
-    "correction term dropped": ("S[c * dv + j] += kc * e[j];",
-                                "S[c * dv + j] += 0.0 * kc * e[j];", 1),
+    "error sign flipped": ("w[j] = beta * ((double)v[j] - u[j]);",
+                           "w[j] = beta * ((double)v[j] + u[j]);", 1),
+    "beta dropped": ("w[j] = beta * (", "w[j] = 1.0 * (", 1),
+    "decay exponent sign": ("const double ac = exp((double)log_alpha[c]);",
+                            "const double ac = exp(-(double)log_alpha[c]);", 2),
+    "predict with the query": ("u[j] += (ac * row[j]) * kc;",
+                               "u[j] += (ac * row[j]) * (double)q[c];", 1),
+    "predict from the undecayed state": ("u[j] += (ac * row[j]) * kc;",
+                                         "u[j] += row[j] * kc;", 1),
+    "correction term dropped": ("const double s = ac * row[j] + kc * w[j];",
+                                "const double s = ac * row[j] + 0.0 * kc * w[j];", 1),
+    "read before the update": ("row[j] = s;\n            o[j] += s * qc;",
+                               "o[j] += row[j] * qc;\n            row[j] = s;", 1),
     "scale dropped": ("o[j] *= scale;", "o[j] *= 1.0;", 1),
     "initial state ignored": ("if (J->h0) memcpy", "if (0) memcpy", 1),
     "last token dropped": ("t < J->cu_seqlens[n + 1]; ++t", "t + 1 < J->cu_seqlens[n + 1]; ++t", 1),
-    "decay indexed by value channel": ("double a = exp((double)log_alpha[c]);\n        for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= a;",
-                                       "for (int64_t j = 0; j < dv; ++j) S[c * dv + j] *= exp((double)log_alpha[j]);", 1),
+    "decay indexed by value channel": ("const double s = ac * row[j] + kc * w[j];",
+                                       "const double s = exp((double)log_alpha[j]) * row[j] + kc * w[j];", 1),
 }
 
 
