@@ -58,7 +58,7 @@ class PrefillOptions(ctypes.Structure):
                 ("block_chunks", ctypes.c_int32), ("gate", ctypes.c_int32),
                 ("snapshot_tokens", ctypes.c_int32), ("snapshot_capacity", ctypes.c_int32),
                 ("snapshots", ctypes.c_void_p), ("front", FrontEnd),
-                ("chunk_states", ctypes.c_void_p)]
+                ("chunk_states", ctypes.c_void_p), ("max_seqlen", ctypes.c_int64)]
 
 
 class DecodeOptions(ctypes.Structure):
@@ -76,7 +76,8 @@ class DecodeMultiOptions(ctypes.Structure):
 class BwdOptions(ctypes.Structure):
     """Mirror of kda_bwd_options."""
     _fields_ = [("gate", ctypes.c_int32), ("block_chunks", ctypes.c_int32),
-                ("front", FrontEnd), ("chunk_states", ctypes.c_void_p)]
+                ("front", FrontEnd), ("chunk_states", ctypes.c_void_p),
+                ("max_seqlen", ctypes.c_int64), ("aux_stream", ctypes.c_void_p)]
 
 # Every function include/kda.h declares.
 EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
@@ -164,12 +165,13 @@ def _gate_code(gate):
 
 
 def prefill_options(path="auto", value_tiles=0, block_chunks=0, gate="channel",
-                    front=None) -> PrefillOptions:
+                    front=None, max_seqlen=0) -> PrefillOptions:
     if path not in PATHS:
         raise ValueError("path must be one of %s" % sorted(PATHS))
     opts = PrefillOptions(PATHS[path], int(value_tiles), int(block_chunks), _gate_code(gate))
     if front is not None:
         opts.front = front
+    opts.max_seqlen = int(max_seqlen or 0)
     return opts
 
 
@@ -194,11 +196,11 @@ def front_end(l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, sha
 
 def prefill_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
                             dtype: int = DTYPE_BF16, path="auto", value_tiles=0,
-                            block_chunks=0, gate="channel", front=False) -> int:
+                            block_chunks=0, gate="channel", front=False, max_seqlen=0) -> int:
     """``front``: True when the call will use the fused input front-end
     (it can change the automatic path, and with it the workspace)."""
     fe = FrontEnd(1, 0.0, None, None) if front else None
-    opts = prefill_options(path, value_tiles, block_chunks, gate, fe)
+    opts = prefill_options(path, value_tiles, block_chunks, gate, fe, max_seqlen)
     return int(load_library().kda_fwd_prefill_workspace_bytes_ex(
         total_T, N, H, d_k, d_v, dtype, ctypes.byref(opts)))
 
@@ -239,6 +241,25 @@ def _stream(device):
     return ctypes.c_void_p(_torch().cuda.current_stream(device).cuda_stream)
 
 
+_side_streams = {}
+
+
+def _side_stream(device):
+    """One extra torch stream per device (default priority) for the
+    backward's operand and serial passes; the current stream is never
+    returned."""
+    torch = _torch()
+    key = torch.device(device).index
+    if key is None:
+        key = torch.cuda.current_device()
+    s = _side_streams.get(key)
+    if s is None:
+        s = _side_streams[key] = torch.cuda.Stream(device=torch.device("cuda", key))
+    if s.cuda_stream == torch.cuda.current_stream(device).cuda_stream:
+        return None
+    return s
+
+
 def _check_gate(log_alpha, gate, lead, dk, dev):
     """log_alpha for a gate layout: [*lead, d_k] (channel), [*lead] (head),
     ignored (none; may be None)."""
@@ -254,7 +275,8 @@ def _check_gate(log_alpha, gate, lead, dk, dev):
 def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
             block_chunks=0, gate="channel", snapshot_tokens=0, snapshots=None,
-            l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None):
+            l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None,
+            max_seqlen=None):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -277,6 +299,9 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     ``chunk_states``: a uint8 device tensor of chunk_states_bytes(T, N, H)
     bytes that receives every chunk's start state, for a later backward()
     on the same inputs (which then skips recomputing this pass).
+    ``max_seqlen``: at least the longest sequence (T when cu_seqlens is
+    None); None leaves it unknown.  The two-pass path then launches blocks
+    for that many tokens only, not for total_T.
     """
     torch = _torch()
     lib = load_library()
@@ -303,6 +328,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
         raise ValueError("beta must be None with beta_pre")
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        max_seqlen = T
     if cu_seqlens.dim() != 1:
         raise ValueError("cu_seqlens must be 1-D")
     N = cu_seqlens.shape[0] - 1
@@ -322,7 +348,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     else:
         hT = final_state
         _check(hT, "final_state", (N, H, dk, dv), torch.float32, dev)
-    opts = prefill_options(path, value_tiles, block_chunks, gate, fe)
+    opts = prefill_options(path, value_tiles, block_chunks, gate, fe, max_seqlen)
     if snapshot_tokens:
         if snapshots is None:
             cap = max(1, T // int(snapshot_tokens))
@@ -504,20 +530,22 @@ def decode_multi(q, k, v, log_alpha, beta, S, scale=None, out=None, outputs=True
 def backward_workspace_bytes(total_T: int, N: int, H: int, d_k: int, d_v: int,
                              dtype: int = DTYPE_BF16, gate="channel", block_chunks=0,
                              l2norm_qk=False, gate_pre=False, beta_pre=False,
-                             chunk_states=False) -> int:
+                             chunk_states=False, max_seqlen=0) -> int:
     """The front-end flags and chunk_states say which options the call will
     use (their tensors are not needed here)."""
     dummy = ctypes.c_void_p(16)
     fe = FrontEnd(1 if l2norm_qk else 0, 1.0, dummy if gate_pre else None,
                   dummy if beta_pre else None)
-    opts = BwdOptions(_gate_code(gate), block_chunks, fe, dummy if chunk_states else None)
+    opts = BwdOptions(_gate_code(gate), block_chunks, fe, dummy if chunk_states else None,
+                      int(max_seqlen or 0))
     return int(load_library().kda_bwd_workspace_bytes(total_T, N, H, d_k, d_v, dtype,
                                                       ctypes.byref(opts)))
 
 
 def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, scale=None,
              gate="channel", want_dh0=True, block_chunks=0, workspace=None,
-             l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None):
+             l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None,
+             max_seqlen=None, aux_stream="auto"):
     """Gradients of <o, do> + <hT, dhT> for the prefill on these inputs.
 
     Inputs as for prefill() (bf16 q, k, v with d_k = d_v = 128); do: [T, H,
@@ -531,7 +559,13 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
     gate_pre (fp32, its layout) and dbeta with respect to beta_pre.
     ``chunk_states``: the record a prefill(..., chunk_states=...) call wrote
     on these same inputs (with the same front-end options); the forward
-    pass is then not recomputed."""
+    pass is then not recomputed.
+    ``max_seqlen`` as for prefill().  ``aux_stream``: a torch stream of the
+    device for the per-block operand and serial passes, which then overlap
+    the gradient pass on the current stream; "auto" takes one side stream
+    per device kept by this module (default priority); None runs the whole
+    call in order on the current stream.  The gradients are the same bits
+    either way."""
     torch = _torch()
     lib = load_library()
     if q.dim() != 3:
@@ -562,6 +596,7 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
         raise ValueError("beta must be None with beta_pre")
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+        max_seqlen = T
     _check(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
     N = cu_seqlens.shape[0] - 1
     if h0 is not None:
@@ -575,6 +610,13 @@ def backward(q, k, v, log_alpha, beta, do, h0=None, dhT=None, cu_seqlens=None, s
                dbeta=torch.empty((T, H), dtype=torch.float32, device=dev),
                dh0=torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev) if want_dh0 else None)
     opts = BwdOptions(gcode, block_chunks, fe if fe is not None else FrontEnd())
+    opts.max_seqlen = int(max_seqlen or 0)
+    if aux_stream == "auto":
+        aux_stream = _side_stream(dev)
+    if aux_stream is not None:
+        if aux_stream.device != dev:
+            raise ValueError("aux_stream must be a stream of %s" % dev)
+        opts.aux_stream = aux_stream.cuda_stream
     if chunk_states is not None:
         _check_states(chunk_states, T, N, H, dk, dv, dev)
         opts.chunk_states = chunk_states.data_ptr()

@@ -43,7 +43,6 @@
 // Every product is a bf16 MFMA (16x16x32) with fp32 accumulation on
 // operands staged in LDS; states, adjoints and gates stay fp32.
 #include <algorithm>
-#include <mutex>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -463,7 +462,7 @@ __device__ __forceinline__ void copy_rows(bf16_t* dst, int ld, const bf16_t* src
 
 __global__ __launch_bounds__(GG)
 void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict__ dO,
-                      const int32_t* __restrict__ cu, int N, int H, int c_lo, int L_b,
+                      const int32_t* __restrict__ cu, int N, int H, int c_lo, int L_b, int c_end,
                       float* __restrict__ dstate, bf16_t* __restrict__ dsblk,
                       bf16_t* __restrict__ deblk, float* __restrict__ dh0)
 {
@@ -604,12 +603,16 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
         __syncthreads();
     }
     float* dst_out = c_lo == 0 ? dh0 : st;
+    // a sequence longer than the call's chunk bound (the caller's
+    // max_seqlen) was cut short: dh0 is NaN, not a silently wrong adjoint
+    const bool cut = c_lo == 0 && nch > c_end;
     if (dst_out) {
         dst_out += c_lo == 0 ? (static_cast<int64_t>(n) * H + h) * kState : 0;
 #pragma unroll
         for (int m = 0; m < MS; ++m)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst_out[(rb + 16 * m + 4 * g4 + i) * D + jc] = S[m][i];
+            for (int i = 0; i < 4; ++i)
+                dst_out[(rb + 16 * m + 4 * g4 + i) * D + jc] = cut ? __builtin_nanf("") : S[m][i];
     }
 }
 
@@ -1240,24 +1243,6 @@ struct DeviceOfStream {
     }
 };
 
-// the serial carry runs on a second stream of the current device, created
-// once per device at the default priority and kept for the process
-hipError_t aux_stream(hipStream_t* out) {
-    static std::mutex mu;
-    static hipStream_t streams[64] = {};
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    std::lock_guard<std::mutex> lock(mu);
-    if (!streams[dev]) {
-        e = hipStreamCreateWithFlags(&streams[dev], hipStreamNonBlocking);
-        if (e != hipSuccess) { streams[dev] = nullptr; return e; }
-    }
-    *out = streams[dev];
-    return hipSuccess;
-}
-
 // events of one call, released when the call returns (a destroyed event
 // still completes the waits already queued on it)
 struct CallEvents {
@@ -1281,14 +1266,14 @@ struct CallEvents {
 
 }  // namespace
 
-int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H) {
+int bwd_default_block_chunks(int64_t seq_bound, int32_t N, int32_t H) {
     // about 1.25 GiB of per-block buffers (prep operands and carry outputs:
     // ~155 KB per (chunk, head), three blocks' worth), at most 80 chunks
     // (measured at 32 heads: 64, 72, 80 and 88 chunks per block)
     const size_t per_chunk = static_cast<size_t>(N) * H * kRing *
                              (kSlot + kState * 2 + static_cast<size_t>(C) * D * 2);
     int64_t L = static_cast<int64_t>((size_t{5} << 28) / per_chunk);
-    L = std::max<int64_t>(1, std::min<int64_t>(L, std::max<int64_t>(1, bound_chunks(total_T))));
+    L = std::max<int64_t>(1, std::min<int64_t>(L, std::max<int64_t>(1, bound_chunks(seq_bound))));
     return static_cast<int>(std::min<int64_t>(L, 80));
 }
 
@@ -1370,14 +1355,19 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
         deblk[i] = reinterpret_cast<bf16_t*>(p);       p += up(l.deblk);
     }
     float* dstate = reinterpret_cast<float*>(p);
+    // with a second stream, the events that order it against the caller's
+    // are created on the device of the streams (the previous device is
+    // restored); without one, everything runs in order on the caller's
+    // stream and no event is needed
+    const bool two = a.aux != nullptr;
+    hipStream_t serial = two ? a.aux : stream;
     DeviceOfStream on_device;
-    hipError_t e = on_device.set(stream);
-    if (e != hipSuccess) return e;
-    hipStream_t serial = nullptr;
-    e = aux_stream(&serial);
-    if (e != hipSuccess) return e;
     CallEvents ev;
-    if ((e = ev.create()) != hipSuccess) return e;
+    hipError_t e = hipSuccess;
+    if (two) {
+        if ((e = on_device.set(stream)) != hipSuccess) return e;
+        if ((e = ev.create()) != hipSuccess) return e;
+    }
 
     // 1. forward: the state after every full chunk, no outputs (unless the
     //    caller passes the record of its own forward pass)
@@ -1389,7 +1379,8 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
         f.dtype_f32 = false; f.scale = a.scale;
         f.snapshots = reinterpret_cast<float*>(const_cast<bf16_t*>(sall));   // bf16 record (snap_cap < 0)
         f.snap_tokens = C; f.snap_cap = -1;
-        e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.total_T, a.N, a.H, D), fwd_ws,
+        f.max_seqlen = a.max_seqlen;
+        e = launch_prefill_wy(f, D / 16, wy_default_block_chunks(a.seq_bound(), a.N, a.H, D), fwd_ws,
                               stream);
         if (e != hipSuccess) return e;
     }
@@ -1407,7 +1398,7 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
     hipLaunchKernelGGL(bwd_init_kernel, dim3(static_cast<unsigned>(std::min<int64_t>(4096, (n4 + 255) / 256))),
                        dim3(256), 0, stream, a.dhT, dstate, n4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int64_t bound = std::max<int64_t>(1, bound_chunks(a.total_T));
+    const int64_t bound = std::max<int64_t>(1, bound_chunks(a.seq_bound()));
     const int64_t nblk = (bound + L_b - 1) / L_b;
     const unsigned chunks = static_cast<unsigned>(static_cast<int64_t>(a.N) * L_b * a.H);
     const bf16_t* q = static_cast<const bf16_t*>(a.q);
@@ -1420,11 +1411,13 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
     auto gk = a.gate == kGateChannel ? bwd_grad_kernel<bf16_t, kGateChannel>
             : a.gate == kGateHead    ? bwd_grad_kernel<bf16_t, kGateHead>
                                      : bwd_grad_kernel<bf16_t, kGateNone>;
-    if ((e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
-    if ((e = hipStreamWaitEvent(serial, ev.start, 0)) != hipSuccess) return e;
+    if (two) {
+        if ((e = hipEventRecord(ev.start, stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(serial, ev.start, 0)) != hipSuccess) return e;
+    }
     for (int64_t b = nblk - 1; b >= 0; --b) {
         const int c_lo = static_cast<int>(b * L_b), r = static_cast<int>(b % kRing);
-        if (b + kRing < nblk && (e = hipStreamWaitEvent(serial, ev.grad[r], 0)) != hipSuccess)
+        if (two && b + kRing < nblk && (e = hipStreamWaitEvent(serial, ev.grad[r], 0)) != hipSuccess)
             return e;
         if (a.total_T > 0) {    // nothing to prepare for an empty batch
             hipLaunchKernelGGL(prep, dim3(chunks), dim3(GT), 0, serial, q, k, a.log_alpha,
@@ -1433,17 +1426,19 @@ hipError_t launch_backward_core(const BackwardArgs& a, int L_b, void* ws, hipStr
         }
         hipLaunchKernelGGL(bwd_carry_kernel, dim3(static_cast<unsigned>(a.N * a.H * (D / kCarryTile))),
                            dim3(GG), 0, serial, slots[r], dO, a.cu_seqlens, a.N, a.H, c_lo, L_b,
-                           dstate, dsblk[r], deblk[r], a.dh0);
+                           static_cast<int>(bound), dstate, dsblk[r], deblk[r], a.dh0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = hipEventRecord(ev.carry[r], serial)) != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(stream, ev.carry[r], 0)) != hipSuccess) return e;
+        if (two) {
+            if ((e = hipEventRecord(ev.carry[r], serial)) != hipSuccess) return e;
+            if ((e = hipStreamWaitEvent(stream, ev.carry[r], 0)) != hipSuccess) return e;
+        }
         if (a.total_T == 0) continue;
         hipLaunchKernelGGL(gk, dim3(chunks), dim3(GG), 0, stream, slots[r], dsblk[r], deblk[r],
                            sall, a.h0, q, k, v, dO, a.log_alpha, a.beta, a.cu_seqlens, a.H, c_lo,
                            L_b, a.scale, static_cast<bf16_t*>(a.dq), static_cast<bf16_t*>(a.dk),
                            static_cast<bf16_t*>(a.dv), a.dlog_alpha, a.dbeta);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        if ((e = hipEventRecord(ev.grad[r], stream)) != hipSuccess) return e;
+        if (two && (e = hipEventRecord(ev.grad[r], stream)) != hipSuccess) return e;
     }
     return hipSuccess;
 }

@@ -16,7 +16,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 11;
+constexpr int kAbiVersion = 12;
 // the automatic choice takes the two-pass matrix path below this many
 // (sequence, head) pairs: there the fused kernel would split each pair into
 // 4 or more value tiles that all redo the pair's state-independent work
@@ -159,7 +159,9 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     const int32_t blk = options ? options->block_chunks : 0;
     if (path < KDA_PATH_AUTO || path > KDA_PATH_MATRIX_TWO_PASS) return KDA_STATUS_INVALID_ARGUMENT;
     if (tiles < 0 || blk < 0) return KDA_STATUS_INVALID_ARGUMENT;
-    const kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
+    if (options && options->max_seqlen < 0) return KDA_STATUS_INVALID_ARGUMENT;
+    kda::PrefillArgs a = shape_args(total_T, N, H, d_k, d_v, dtype);
+    a.max_seqlen = options ? options->max_seqlen : 0;
     const bool matrix_ok = kda::mfma_supported(a) && kda::wy_supported(a);
     if ((path == KDA_PATH_MATRIX || path == KDA_PATH_MATRIX_TWO_PASS) && !matrix_ok)
         return KDA_STATUS_UNSUPPORTED;
@@ -188,7 +190,7 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
         return KDA_STATUS_INVALID_ARGUMENT;
     pl->R = tiles > 0 ? tiles : two ? kda::wy_value_tiles(a) : kda::mfma_value_tiles(a);
     if (two) {
-        pl->L_b = blk > 0 ? blk : kda::wy_default_block_chunks(total_T, N, H, d_v);
+        pl->L_b = blk > 0 ? blk : kda::wy_default_block_chunks(a.seq_bound(), N, H, d_v);
         if (!kda::wy_block_chunks_ok(N, H, pl->L_b)) return KDA_STATUS_INVALID_ARGUMENT;
         pl->ws_bytes += kda::wy_workspace_bytes(N, H, d_k, d_v, pl->L_b);
     }
@@ -204,6 +206,12 @@ int64_t chunk_states_bytes(int64_t total_T, int32_t N, int32_t H) {
     return bytes;
 }
 
+// the shapes the backward (and the chunk-state record it reads) supports:
+// the two-pass kernels' head bound (their 32-bit in-kernel offsets)
+bool bwd_shape_ok(int32_t N, int32_t H) {
+    return kda::wy_supported(shape_args(0, N, H, 128, 128, KDA_DTYPE_BF16));
+}
+
 }  // namespace
 
 extern "C" {
@@ -215,7 +223,7 @@ size_t kda_chunk_states_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_k
     if (check_sizes(total_T, N, H, d_k, d_v, KDA_DTYPE_BF16, KDA_GATE_CHANNEL, &sz) !=
         KDA_STATUS_OK)
         return 0;
-    if (d_k != 128 || d_v != 128) return 0;
+    if (d_k != 128 || d_v != 128 || !bwd_shape_ok(N, H)) return 0;
     return static_cast<size_t>(chunk_states_bytes(total_T, N, H));
 }
 
@@ -346,6 +354,7 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     a.snap_tokens = rec ? 64 : snaps ? snap : 0;
     a.snap_cap = rec ? -1 : cap;                   // < 0: the compact per-chunk record
     a.fe = fe;
+    a.max_seqlen = options ? options->max_seqlen : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
@@ -481,8 +490,10 @@ int kda_decode_step(const void* q, const void* k, const void* v, const float* lo
 static int bwd_block_chunks(int64_t total_T, int32_t N, int32_t H,
                             const kda_bwd_options* options, int* L_b) {
     const int32_t blk = options ? options->block_chunks : 0;
-    if (blk < 0) return KDA_STATUS_INVALID_ARGUMENT;
-    *L_b = blk > 0 ? blk : kda::bwd_default_block_chunks(total_T, N, H);
+    const int64_t msl = options ? options->max_seqlen : 0;
+    if (blk < 0 || msl < 0) return KDA_STATUS_INVALID_ARGUMENT;
+    const int64_t seq_bound = msl > 0 && msl < total_T ? msl : total_T;
+    *L_b = blk > 0 ? blk : kda::bwd_default_block_chunks(seq_bound, N, H);
     int64_t chunks;
     if (!mul_ok(static_cast<int64_t>(N) * H, *L_b, &chunks) || chunks >= (int64_t{1} << 31))
         return KDA_STATUS_INVALID_ARGUMENT;
@@ -495,7 +506,7 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int32_t d_
     if (check_sizes(total_T, N, H, d_k, d_v, dtype, options ? options->gate : 0, &sz) !=
         KDA_STATUS_OK)
         return 0;
-    if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16) return 0;
+    if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16 || !bwd_shape_ok(N, H)) return 0;
     int L_b;
     if (bwd_block_chunks(total_T, N, H, options, &L_b) != KDA_STATUS_OK) return 0;
     kda::FrontEnd fe;
@@ -519,8 +530,11 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     Sizes sz;
     const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, gate, &sz);
     if (st != KDA_STATUS_OK) return st;
-    if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16) return KDA_STATUS_UNSUPPORTED;
+    if (d_k != 128 || d_v != 128 || dtype != KDA_DTYPE_BF16 || !bwd_shape_ok(N, H))
+        return KDA_STATUS_UNSUPPORTED;
     if (!std::isfinite(scale) || !cu_seqlens) return KDA_STATUS_INVALID_ARGUMENT;
+    void* aux = options ? options->aux_stream : nullptr;
+    if (aux && aux == stream) return KDA_STATUS_INVALID_ARGUMENT;
     const bool any = total_T > 0;
     kda::FrontEnd fe;
     bool la_needed, beta_needed;
@@ -576,6 +590,16 @@ int kda_bwd(const void* q, const void* k, const void* v, const float* log_alpha,
     a.dq = dq; a.dk = dk; a.dv = dv; a.dlog_alpha = dlog_alpha; a.dbeta = dbeta; a.dh0 = dh0;
     a.total_T = total_T; a.N = N; a.H = H; a.gate = gate; a.scale = scale; a.fe = fe;
     a.states = states;
+    a.max_seqlen = options ? options->max_seqlen : 0;
+    a.aux = static_cast<hipStream_t>(aux);
+    if (aux) {
+        // the second stream must belong to the device of the caller's stream
+        int d0 = -1, d1 = -1;
+        if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &d0) != hipSuccess ||
+            hipStreamGetDevice(a.aux, &d1) != hipSuccess)
+            return KDA_STATUS_HIP_ERROR;
+        if (d0 != d1) return KDA_STATUS_INVALID_ARGUMENT;
+    }
     if (kda::launch_backward(a, L_b, workspace, static_cast<hipStream_t>(stream)) != hipSuccess)
         return KDA_STATUS_HIP_ERROR;
     return KDA_STATUS_OK;

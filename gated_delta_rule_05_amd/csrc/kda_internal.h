@@ -71,6 +71,12 @@ struct PrefillArgs {
     float* snapshots;
     int32_t snap_tokens, snap_cap;
     FrontEnd fe;
+    // the longest sequence, or 0 (unknown: total_T); bounds the two-pass
+    // block loop
+    int64_t max_seqlen = 0;
+    int64_t seq_bound() const {
+        return max_seqlen > 0 && max_seqlen < total_T ? max_seqlen : total_T;
+    }
 };
 
 // gradients of the prefill (bf16, d_k = d_v = 128): see backward.hip
@@ -101,8 +107,16 @@ struct BackwardArgs {
     // the per-chunk state record of a forward pass on these inputs, or null
     // (the forward pass is then recomputed into the workspace)
     const void* states = nullptr;
+    // the longest sequence, or 0 (unknown: total_T); bounds the block loop
+    int64_t max_seqlen = 0;
+    // a second stream of the device for the operand and carry passes, or
+    // null (the whole call in order on the caller's stream)
+    hipStream_t aux = nullptr;
+    int64_t seq_bound() const {
+        return max_seqlen > 0 && max_seqlen < total_T ? max_seqlen : total_T;
+    }
 };
-int bwd_default_block_chunks(int64_t total_T, int32_t N, int32_t H);
+int bwd_default_block_chunks(int64_t seq_bound, int32_t N, int32_t H);
 // the backward's buffers, after the front-end's activated inputs when fe is
 // active
 size_t bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H, int L_b, int gate,
@@ -131,7 +145,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int R, hipStream_t stream);
 bool wy_supported(const PrefillArgs& a);
 int wy_value_tiles(const PrefillArgs& a);
 bool wy_tiles_ok(int d_v, int R);
-int wy_default_block_chunks(int64_t total_T, int32_t N, int32_t H, int32_t d_v);
+int wy_default_block_chunks(int64_t seq_bound, int32_t N, int32_t H, int32_t d_v);
 bool wy_block_chunks_ok(int32_t N, int32_t H, int L_b);
 size_t wy_workspace_bytes(int32_t N, int32_t H, int32_t d_k, int32_t d_v, int L_b);
 hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hipStream_t stream);

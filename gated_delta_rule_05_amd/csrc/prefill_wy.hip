@@ -575,7 +575,8 @@ template <int TV, bool SNAP>
 __global__ __launch_bounds__(CT)
 void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __restrict__ h0,
                              float* __restrict__ hstate, const int32_t* __restrict__ cu,
-                             int64_t groups, int R, int H, int DV, int c_lo, int L_b, float scale,
+                             int64_t groups, int R, int H, int DV, int c_lo, int L_b, int c_end,
+                             float scale,
                              bf16_t* __restrict__ o, float* __restrict__ snapshots, int snap_tokens,
                              int snap_cap)
 {
@@ -828,11 +829,16 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             bx = bn;
         }
         if (count >= 2) store_o(c_lo + count - 2, count & 1);
+        // a sequence longer than the call's chunk bound (the caller's
+        // max_seqlen) was cut short: its final state is NaN, not a silently
+        // wrong state
+        const bool cut = c_lo + L_b >= c_end && nch > c_lo + count;
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                hstate[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] = S[m][i];
+                hstate[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] =
+                    cut ? __builtin_nanf("") : S[m][i];
         return;
     }
 
@@ -923,14 +929,14 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int64_t chunk_bound(int64_t total_T) { return total_T > 0 ? (total_T + C - 1) / C : 1; }
 
 template <int TV>
-hipError_t launch_carry_t(const PrefillArgs& a, int R, int c_lo, int L_b, const uint8_t* slots,
-                          float* hstate, hipStream_t stream) {
+hipError_t launch_carry_t(const PrefillArgs& a, int R, int c_lo, int L_b, int c_end,
+                          const uint8_t* slots, float* hstate, hipStream_t stream) {
     const int64_t groups = static_cast<int64_t>(a.N) * a.H;
     const int64_t blocks = prefill_grid_blocks(groups, R);
     auto carry = a.snapshots ? prefill_wy_carry_kernel<TV, true> : prefill_wy_carry_kernel<TV, false>;
     hipLaunchKernelGGL(carry, dim3(static_cast<unsigned>(blocks)), dim3(CT),
                        0, stream, slots, a.h0, hstate, a.cu_seqlens, groups, R, a.H, a.d_v, c_lo,
-                       L_b, a.scale, static_cast<bf16_t*>(a.o), a.snapshots, a.snap_tokens, a.snap_cap);
+                       L_b, c_end, a.scale, static_cast<bf16_t*>(a.o), a.snapshots, a.snap_tokens, a.snap_cap);
     return hipGetLastError();
 }
 }  // namespace
@@ -953,11 +959,11 @@ bool wy_tiles_ok(int d_v, int R) {
            d_v / R <= kMaxTwoPassTile;
 }
 
-int wy_default_block_chunks(int64_t total_T, int32_t N, int32_t H, int32_t d_v) {
+int wy_default_block_chunks(int64_t seq_bound, int32_t N, int32_t H, int32_t d_v) {
     const size_t per_chunk = static_cast<size_t>(N) * H * slot_bytes(d_v);
     int64_t L = static_cast<int64_t>(kSlotBudget / per_chunk);
     if (L >= 16) L -= L % 16;
-    L = std::max<int64_t>(1, std::min<int64_t>(L, chunk_bound(total_T)));
+    L = std::max<int64_t>(1, std::min<int64_t>(L, chunk_bound(seq_bound)));
     return static_cast<int>(L);
 }
 
@@ -977,7 +983,9 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hip
     uint8_t* slots = static_cast<uint8_t*>(ws);
     const size_t slot_total = align_up(static_cast<size_t>(a.N) * a.H * L_b * slot_bytes(a.d_v));
     float* hstate = a.hT ? a.hT : reinterpret_cast<float*>(slots + slot_total);
-    const int64_t bound = chunk_bound(a.total_T);
+    // blocks cover the longest sequence's chunks (the caller's max_seqlen),
+    // else every chunk index a sequence of total_T tokens could have
+    const int64_t bound = chunk_bound(a.seq_bound());
     const int TV = a.d_v / R;
     for (int64_t c_lo = 0; c_lo < bound; c_lo += L_b) {
         if (a.total_T > 0) {
@@ -997,8 +1005,10 @@ hipError_t launch_prefill_wy(const PrefillArgs& a, int R, int L_b, void* ws, hip
         }
         hipError_t e = hipErrorInvalidValue;
         switch (TV) {
-            case 16: e = launch_carry_t<16>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
-            case 32: e = launch_carry_t<32>(a, R, static_cast<int>(c_lo), L_b, slots, hstate, stream); break;
+            case 16: e = launch_carry_t<16>(a, R, static_cast<int>(c_lo), L_b,
+                                            static_cast<int>(bound), slots, hstate, stream); break;
+            case 32: e = launch_carry_t<32>(a, R, static_cast<int>(c_lo), L_b,
+                                            static_cast<int>(bound), slots, hstate, stream); break;
         }
         if (e != hipSuccess) return e;
     }

@@ -41,10 +41,13 @@
  * tokens cu_seqlens[n] .. cu_seqlens[n+1]-1.  The state is always fp32.
  *
  * Ownership and execution.  The caller allocates every buffer (device
- * memory), including the prefill workspace.  The library keeps no global
- * mutable state, allocates nothing and never synchronises: each call only
- * enqueues kernels on `stream` (a hipStream_t; NULL = the default stream)
- * and returns.  Faults inside those kernels surface at the caller's next
+ * memory), including the prefill workspace, and every stream.  The library
+ * keeps no global mutable state, allocates no device memory and never
+ * synchronises: each call only enqueues kernels on `stream` (a
+ * hipStream_t; NULL = the default stream) and returns.  The one call that
+ * can use a second stream, kda_bwd, takes it from the caller
+ * (kda_bwd_options.aux_stream) and orders the two with HIP events it
+ * creates and releases within the call.  Faults inside those kernels surface at the caller's next
  * synchronisation.  Calls on different streams may run concurrently if
  * their output buffers do not overlap.
  *
@@ -182,6 +185,17 @@ typedef struct kda_prefill_options {
                                   Two-pass path, bf16, d_k = d_v = 128;
                                   not with snapshot_tokens; no overlap with
                                   any other buffer. */
+    int64_t max_seqlen;        /* 0 = unknown; else at least the longest
+                                  sequence of the call (cu_seqlens lives in
+                                  device memory, so only the caller knows
+                                  it).  The two-pass path then runs its
+                                  block loop over that many tokens instead
+                                  of total_T: a batch of N equal sequences
+                                  launches 1/N of the blocks.  A sequence
+                                  longer than max_seqlen (a violated device
+                                  precondition) gets a NaN final state and
+                                  its outputs past max_seqlen are not
+                                  written.  Ignored by the other paths. */
 } kda_prefill_options;
 
 
@@ -233,6 +247,22 @@ typedef struct kda_bwd_options {
                                       same inputs (options.chunk_states);
                                       the forward pass is then not
                                       recomputed */
+    int64_t max_seqlen;            /* 0 = unknown; else at least the longest
+                                      sequence, as for the prefill: the block
+                                      loop covers that many tokens.  A
+                                      longer sequence gets NaN in dh0 (when
+                                      requested) and unwritten gradients
+                                      past max_seqlen. */
+    void *aux_stream;              /* a second hipStream_t of the same
+                                      device, or NULL.  Set: the per-block
+                                      operand pass and the serial
+                                      state-adjoint pass run on it, beside
+                                      the gradient pass on `stream` (the
+                                      call creates and destroys its own HIP
+                                      events to order the two; no device
+                                      memory).  NULL: the whole call runs
+                                      in order on `stream`.  The results are
+                                      the same bits either way. */
 } kda_bwd_options;
 
 /* Version of this ABI; bumped whenever a signature or a layout changes. */
@@ -457,11 +487,13 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * (normalised q and k are stored in bf16), and the chain rule through them
  * is applied to the gradients afterwards.  Requirements and errors as for
  * kda_fwd_prefill_ex's front-end.
- * Streams: the per-block operand pass and the serial state-adjoint pass
- * run on a second stream of the device (created by the library on first use, default priority, kept for
- * the process), ordered against the caller's stream by events; all of the
- * call's work is complete once the caller's stream reaches the point after
- * the call.
+ * Streams: with options->aux_stream set, the per-block operand pass and
+ * the serial state-adjoint pass run on that stream, ordered against
+ * `stream` by per-call events, and the first work on it waits for
+ * `stream`'s earlier work; all of the call's work is complete once `stream`
+ * reaches the point after the call.  aux_stream must belong to the device
+ * of `stream` [INVALID_ARGUMENT] and must not be `stream` itself.
+ * d_k = d_v = 128, bf16 and H <= 16384 [UNSUPPORTED].
  */
 int kda_bwd(const void *q, const void *k, const void *v,
             const float *log_alpha, const float *beta, const float *h0,

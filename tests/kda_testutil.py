@@ -25,6 +25,30 @@ def rel_err(x, ref):
     return float(np.max(np.abs(x - ref))) / denom
 
 
+def rel_err_slices(x, ref, cu, states=False):
+    """Worst max-relative error over the (sequence, head) slices of a packed
+    tensor: o / gradients [T, H, .] sliced by cu_seqlens, or (states=True)
+    [N, H, ...] per state.  Each slice is measured against its own largest
+    magnitude, so a small-magnitude head cannot hide behind a large one."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    cu = np.asarray(cu, dtype=np.int64)
+    worst = 0.0
+    for n in range(len(cu) - 1):
+        for h in range(ref.shape[1]):
+            if states:
+                a, b = x[n, h], ref[n, h]
+            else:
+                a, b = x[cu[n]:cu[n + 1], h], ref[cu[n]:cu[n + 1], h]
+            if b.size == 0 or not np.any(b):
+                # an empty slice, or an exactly-zero reference: must match exactly
+                if b.size and np.any(a != b):
+                    return float("inf")
+                continue
+            worst = max(worst, rel_err(a, b))
+    return worst
+
+
 def host(t):
     """Device tensor -> float64 numpy (bf16 and fp32 widen exactly)."""
     if t is None:

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.abi_version() == 11
+    assert kda.abi_version() == 12
     for s in range(6):
         assert kda.status_string(s)
     assert kda.status_string(99) == "unknown status"
@@ -153,12 +153,14 @@ def test_binding_rejects_cpu_tensors():
         kda.decode_step(q, q, q, q, torch.zeros(4, 2), torch.zeros(4, 2, 16, 16))
 
 
-def prefill_ex_call(path, tiles, blk=0, gate=0, snap=(0, 0, None), front=None, **over):
+def prefill_ex_call(path, tiles, blk=0, gate=0, snap=(0, 0, None), front=None, max_seqlen=0,
+                    **over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
                 o=addr(6), hT=addr(7), ws=addr(8), wsb=256, stream=None)
     args.update(over)
     opts = kda.PrefillOptions(path, tiles, blk, gate, snap[0], snap[1], snap[2])
+    opts.max_seqlen = max_seqlen
     if front is not None:
         opts.front = kda.FrontEnd(*front)
     lib = kda.load_library()
@@ -284,13 +286,15 @@ def test_decode_multi_checks(kw, status):
     assert decode_multi_call(**kw) == status
 
 
-def bwd_call(gate=0, blk=0, **over):
+def bwd_call(gate=0, blk=0, max_seqlen=0, aux=None, **over):
     args = dict(q=addr(0), k=addr(1), v=addr(2), la=addr(3), beta=addr(4), h0=None,
                 cu=addr(5), T=100, N=2, H=4, dk=128, dv=128, dtype=0, scale=0.1,
                 do=addr(6), dhT=None, dq=addr(7), dk_=addr(8), dv_=addr(9), dla=addr(10),
                 dbeta=addr(11), dh0=addr(12), ws=addr(13), wsb=256, stream=None)
     args.update(over)
     opts = kda.BwdOptions(gate, blk)
+    opts.max_seqlen = max_seqlen
+    opts.aux_stream = aux
     lib = kda.load_library()
     return lib.kda_bwd(args["q"], args["k"], args["v"], args["la"], args["beta"], args["h0"],
                        args["cu"], args["T"], args["N"], args["H"], args["dk"], args["dv"],
@@ -535,3 +539,44 @@ def test_backward_chunk_states_workspace():
     up = lambda x: (x + 255) // 256 * 256
     assert kda.backward_workspace_bytes(T, N, H, 128, 128, chunk_states=True,
                                         l2norm_qk=True) == rec + 2 * up(T * H * 256)
+
+
+# ---- max_seqlen, the backward's caller-supplied second stream, head bound
+def test_max_seqlen_bounds_the_two_pass_blocks():
+    # two one-chunk sequences: without max_seqlen a block may span the two
+    # chunk indices total_T allows; with it one chunk index suffices
+    lib = kda.load_library()
+    q = lambda o: lib.kda_fwd_prefill_workspace_bytes_ex(128, 2, 1, 128, 128, 0, ctypes.byref(o))
+    plain = kda.PrefillOptions(3, 0, 0, 0)
+    short = kda.PrefillOptions(3, 0, 0, 0)
+    short.max_seqlen = 64
+    assert 0 < q(short) < q(plain)
+    assert kda.prefill_workspace_bytes(128, 2, 1, 128, 128, path="two_pass", max_seqlen=64) == q(short)
+    bad = kda.PrefillOptions(3, 0, 0, 0)
+    bad.max_seqlen = -1
+    assert q(bad) == 0
+    assert prefill_ex_call(3, 0, max_seqlen=-1) == INVALID
+
+
+def test_backward_max_seqlen_and_aux_stream_checks():
+    lib = kda.load_library()
+    opts = kda.BwdOptions(0, 0)
+    opts.max_seqlen = -5
+    assert lib.kda_bwd_workspace_bytes(4096, 4, 16, 128, 128, 0, ctypes.byref(opts)) == 0
+    assert bwd_call(max_seqlen=-5) == INVALID
+    # the second stream may not be the caller's stream (checked before any HIP call)
+    fake = ctypes.c_void_p(BASE + 17 * GAP)
+    assert bwd_call(aux=fake, stream=fake) == INVALID
+    assert bwd_call(aux=None) == WS_SMALL
+
+
+def test_backward_head_bound():
+    # the two-pass kernels' 32-bit offsets bound the heads at 16384
+    lib = kda.load_library()
+    opts = kda.BwdOptions(0, 0)
+    assert lib.kda_bwd_workspace_bytes(128, 1, 16384, 128, 128, 0, ctypes.byref(opts)) > 0
+    assert lib.kda_bwd_workspace_bytes(128, 1, 16385, 128, 128, 0, ctypes.byref(opts)) == 0
+    assert kda.chunk_states_bytes(128, 1, 16384) > 0
+    assert kda.chunk_states_bytes(128, 1, 16385) == 0
+    assert bwd_call(H=16385) == UNSUPPORTED
+    assert bwd_call(H=70000) == UNSUPPORTED

@@ -112,10 +112,14 @@ def test_backward_batch4_t4096_sampled_heads():
 def test_backward_long_t1m_last_window():
     """The 1M-token backward in the configuration bench.py times, checked on
     the last 8192 tokens of two heads: the oracle's backward over that
-    window starts from the state the forward reaches at its first token (a
-    snapshot of the same two-pass forward the backward recomputes, so the
-    same bits) and takes the same dO and dhT; every gradient of a token in
-    the window depends on nothing else."""
+    window starts from the oracle's own forward state at the window's first
+    token (the GPU forward's snapshot there is checked against it too) and
+    takes the same dO and dhT; every gradient of a token in the window
+    depends on nothing else.  dh0 of the whole sequence is checked against
+    the oracle's backward over the first 8192 tokens with no adjoint
+    entering at their end: whatever later tokens send back is decayed by
+    the 8192 tokens' gates (about -0.04 per token and channel, so a factor
+    near e^-300) before it reaches h0."""
     w = gen.WORKLOADS["long_t1m"]
     inp = gen.workload_prefill_inputs(w, seed=340, device=DEV)
     T, H = inp["q"].shape[:2]
@@ -124,27 +128,37 @@ def test_backward_long_t1m_last_window():
     do = gen.normal((T, H, 128), 340, gen.DO, DEV, torch.bfloat16)
     dhT = gen.normal((1, H, 128, 128), 340, gen.DHT, DEV, torch.float32, std=0.1)
     args = (inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
-    g = kda.backward(*args, do, dhT=dhT, cu_seqlens=inp["cu_seqlens"], want_dh0=False)
-    win = {key: host(x[t0:, heads]) for key, x in g.items() if x is not None}
+    g = kda.backward(*args, do, dhT=dhT, cu_seqlens=inp["cu_seqlens"])
+    win = {key: host(x[t0:, heads]) for key, x in g.items() if x is not None and key != "dh0"}
+    dh0 = host(g["dh0"][:, heads])
     del g
     torch.cuda.empty_cache()
     _, _, snaps = kda.prefill(*args, cu_seqlens=inp["cu_seqlens"], final_state=False,
                               snapshot_tokens=t0)
-    S0 = host(snaps[:, 0][:, heads])
+    S0_gpu = host(snaps[:, 0][:, heads])
     del snaps
+    head = lambda x: x[:t0, heads].to(torch.float32).cpu().numpy()
+    _, S0 = oracle.prefill(head(inp["q"]), head(inp["k"]), head(inp["v"]),
+                           head(inp["log_alpha"]), inp["beta"][:t0, heads].cpu().numpy(),
+                           threads=len(heads))
     sel = lambda x: host(x[t0:, heads])
     ref = oracle.backward(sel(inp["q"]), sel(inp["k"]), sel(inp["v"]), sel(inp["log_alpha"]),
                           sel(inp["beta"]), sel(do), h0=S0, dhT=host(dhT[:, heads]))
     errs = {key: rel_err(win[key], ref[key]) for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta")}
+    errs["S0"] = rel_err(S0_gpu, S0)
+    first = lambda x: host(x[:W, heads])
+    ref0 = oracle.backward(first(inp["q"]), first(inp["k"]), first(inp["v"]),
+                           first(inp["log_alpha"]), first(inp["beta"]), first(do))
+    errs["dh0"] = rel_err(dh0, ref0["dh0"])
     report("backward long_t1m last %d tokens, heads %s" % (W, heads), **errs)
     for key, e in errs.items():
         assert e <= TOL, (key, e)
 
 
 def test_backward_on_a_side_stream():
-    """The call on a non-default stream (the library forks its serial pass
-    onto a second stream of that stream's device and joins back): the same
-    bits as on the default stream, complete once that stream is done."""
+    """The call on a non-default stream (its serial pass forked onto the
+    binding's second stream of that device and joined back): the same bits
+    as on the default stream, complete once that stream is done."""
     inp = case(LENS, 2, 350)
     base = gpu(inp, "channel")
     side = torch.cuda.Stream()
@@ -154,6 +168,37 @@ def test_backward_on_a_side_stream():
     side.synchronize()
     for key, x in base.items():
         assert torch.equal(x, other[key]), key
+
+
+def test_backward_second_stream_optional_same_bits():
+    """The per-block operand and serial passes on a caller-supplied second
+    stream, on the binding's side stream, or in order on the caller's
+    stream alone: the same bits."""
+    inp = case(LENS, 2, 355)
+    alone = gpu(inp, "channel", aux_stream=None)
+    auto = gpu(inp, "channel")
+    mine = gpu(inp, "channel", aux_stream=torch.cuda.Stream())
+    for key, x in alone.items():
+        assert torch.equal(x, auto[key]), key
+        assert torch.equal(x, mine[key]), key
+
+
+@pytest.mark.parametrize("aux", [None, "auto"])
+def test_backward_max_seqlen_same_bits(aux):
+    """max_seqlen bounds the block walk (and the forward recompute's) to the
+    longest sequence: the same bits as the walk over total_T; a sequence
+    longer than it gets NaN in dh0."""
+    inp = case(LENS, 2, 356)
+    base = gpu(inp, "channel", block_chunks=1, aux_stream=aux)
+    other = gpu(inp, "channel", block_chunks=1, aux_stream=aux, max_seqlen=max(LENS))
+    for key, x in base.items():
+        assert torch.equal(x, other[key]), key
+    cut = gpu(inp, "channel", block_chunks=1, aux_stream=aux, max_seqlen=128)
+    for n, L in enumerate(LENS):                     # 300 and 129 tokens exceed 128
+        if L > 128:
+            assert torch.isnan(cut["dh0"][n]).all(), n
+        else:
+            assert torch.equal(cut["dh0"][n], base["dh0"][n]), n
 
 
 @pytest.mark.parametrize("gate", ["channel", "head", "none"])

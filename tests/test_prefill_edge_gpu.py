@@ -75,3 +75,33 @@ def test_many_short_sequences(dtype, path):
     inp = gen.prefill_inputs(lens, 2, 128, 64, dtype, "softplus", state_std=0.05, seed=82,
                              device=DEV)
     check(inp, path, dtype, "200 short sequences")
+
+
+@pytest.mark.parametrize("N", [300, 2500, 16500])
+def test_plan_order_is_longest_first_permutation(N):
+    """The device plan (the fused and vector paths' dispatch order, kept in
+    the first N int32 of the workspace) must be bit-exactly the ranking by
+    length, longest first, ties by sequence index -- a permutation of
+    0..N-1 -- and the identity order above 16384 sequences.  Lengths with
+    many ties and zeros; N = 2500 spans three of the kernel's 1024-length
+    tiles."""
+    rng = np.random.default_rng(90 + N)
+    lens = rng.integers(0, 5, N) * 3
+    lens[::7] = 0
+    T = int(lens.sum())
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device=DEV)
+    z = torch.zeros((T, 1, 128), dtype=torch.bfloat16, device=DEV)
+    la = torch.zeros((T, 1, 128), dtype=torch.float32, device=DEV)
+    beta = torch.zeros((T, 1), dtype=torch.float32, device=DEV)
+    ws = torch.zeros(kda.prefill_workspace_bytes(T, N, 1, 128, 128, path="matrix"),
+                     dtype=torch.uint8, device=DEV)
+    kda.prefill(z, z, z, la, beta, cu_seqlens=cu, path="matrix", workspace=ws,
+                final_state=False)
+    torch.cuda.synchronize()
+    order = ws[:4 * N].view(torch.int32).cpu().numpy()
+    if N > 16384:
+        want = np.arange(N)
+    else:
+        want = np.array(sorted(range(N), key=lambda i: (-int(lens[i]), i)))
+    assert np.array_equal(np.sort(order), np.arange(N))       # a permutation
+    assert np.array_equal(order, want)

@@ -18,7 +18,7 @@ import torch
 
 import gated_delta_rule_05_amd as kda
 import kda_inputs as gen
-from kda_testutil import host, oracle_prefill, rel_err, report, tol_for, TOL_F32
+from kda_testutil import host, oracle_prefill, rel_err, rel_err_slices, report, tol_for, TOL_F32
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -33,13 +33,19 @@ def call(inp, **kw):
 
 
 def parity(inp, name, tol, scale=None, **kw):
+    """Whole-tensor and worst (sequence, head) slice errors of o and hT."""
     o, hT = call(inp, scale=scale, **kw)
     o_ref, hT_ref = oracle_prefill(inp, scale=scale)
+    cu = inp["cu_seqlens"].cpu().numpy()
     eo = rel_err(host(o), o_ref)
     es = rel_err(host(hT), hT_ref)
-    report(name, o=eo, hT=es)
+    so = rel_err_slices(host(o), o_ref, cu)
+    ss = rel_err_slices(host(hT), hT_ref, cu, states=True)
+    report(name, o=eo, hT=es, o_worst_slice=so, hT_worst_slice=ss)
     assert eo <= tol, "o max-rel error %.3e > %.1e" % (eo, tol)
     assert es <= tol, "hT max-rel error %.3e > %.1e" % (es, tol)
+    assert so <= tol, "o worst (sequence, head) error %.3e > %.1e" % (so, tol)
+    assert ss <= tol, "hT worst (sequence, head) error %.3e > %.1e" % (ss, tol)
     return eo, es
 
 
@@ -100,6 +106,36 @@ def test_two_pass_block_size_invariance_bitwise(blocks):
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
     o3, none = call(inp, path="two_pass", block_chunks=blocks, final_state=False)
     assert none is None and torch.equal(o1, o3)
+
+
+@pytest.mark.parametrize("blocks", [0, 1, 3])
+def test_two_pass_max_seqlen_bitwise(blocks):
+    """max_seqlen (the longest sequence, given by the caller) only bounds the
+    two-pass block loop: the same bits as the loop over total_T."""
+    lens = [700, 3, 0, 450, 64]
+    inp = gen.prefill_inputs(lens, 2, 128, 128, "bf16", "softplus", state_std=0.02,
+                             seed=62, device=DEV)
+    o1, h1 = call(inp, path="two_pass", block_chunks=blocks)
+    o2, h2 = call(inp, path="two_pass", block_chunks=blocks, max_seqlen=max(lens))
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    o3, h3 = call(inp, path="two_pass", block_chunks=blocks, max_seqlen=sum(lens) + 5)
+    assert torch.equal(o1, o3) and torch.equal(h1, h3)
+
+
+def test_two_pass_max_seqlen_too_small_flags_the_cut_sequence():
+    """A sequence longer than max_seqlen (a broken caller promise) gets a NaN
+    final state; the shorter sequences are untouched, and so are the cut
+    sequence's outputs up to max_seqlen."""
+    lens = [300, 64, 129, 0]
+    inp = gen.prefill_inputs(lens, 2, 128, 128, "bf16", "softplus", state_std=0.02,
+                             seed=63, device=DEV)
+    o1, h1 = call(inp, path="two_pass")
+    o2, h2 = call(inp, path="two_pass", max_seqlen=192, block_chunks=1)
+    assert torch.isnan(h2[0]).all()
+    assert torch.equal(h1[1:], h2[1:])
+    cu = inp["cu_seqlens"].cpu().numpy()
+    assert torch.equal(o1[:192], o2[:192])
+    assert torch.equal(o1[cu[1]:], o2[cu[1]:])
 
 
 def test_matrix_paths_agree():
