@@ -48,8 +48,16 @@ cpu_baseline: the fp64 oracle on a bounded sample of the same workload (a
 few heads over the first tokens), on the host's cores, scaled to tokens/s of
 the full 32-head layer.  It doubles as a parity spot check of those outputs.
 
+counters: ``python bench.py --counters`` prints no JSON; it runs, once
+each, the launches the committed rocprofv3 counter summaries (profiles/)
+are taken on -- the long-context prefill over its first 512 chunks (8
+blocks of 64), the 4 x 4096 batch, the 64-sequence varlen batch, one decode
+step of 256 x 32 states, the backward of the 512-chunk prefill, and a 512
+MiB device copy whose counter readings calibrate the rest -- under
+``rocprofv3 --pmc <counter> -- python3 bench.py --counters``.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only-backward]
+                       [--only-backward] [--counters]
 """
 import argparse
 import hashlib
@@ -80,7 +88,62 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1048576)
     ap.add_argument("--only-backward", action="store_true",
                     help="time only the prefill gradients (for profiling)")
+    ap.add_argument("--counters", action="store_true",
+                    help="run the launches the rocprofv3 counter summaries cover, once each")
+    ap.add_argument("--chunks", type=int, default=512,
+                    help="--counters: 64-token chunks of the long-context prefill")
     return ap.parse_args()
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def run_counter_workloads(torch, kda, gen, chunks):
+    """One launch of each workload the counter summaries cover, in a fixed
+    order (rocprofv3 lists dispatches in order): long-context prefill of
+    `chunks` chunks (32 heads, two-pass: 2 kernels per block of 64 chunks),
+    batch4_t4096 (two-pass), varlen_n64 (fused), one decode step, the
+    backward of the long-context prefill, then a 512 MiB device copy."""
+    dev = "cuda"
+    T, H, d = 64 * chunks, 32, 128
+    inp = gen.prefill_inputs([T], H, d, d, "bf16", "softplus", state_std=0.0, seed=2, device=dev)
+    print("counters: long prefill T=%d H=%d" % (T, H), flush=True)
+    kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"])
+    torch.cuda.synchronize()
+    for wname in ("batch4_t4096", "varlen_n64"):
+        wo = gen.WORKLOADS[wname]
+        io = gen.workload_prefill_inputs(wo, seed=11, device=dev)
+        print("counters: %s prefill" % wname, flush=True)
+        kda.prefill(io["q"], io["k"], io["v"], io["log_alpha"], io["beta"], h0=io["h0"],
+                    cu_seqlens=io["cu_seqlens"], max_seqlen=max(io["lengths"]))
+        torch.cuda.synchronize()
+        del io
+    S = gen.decode_state(256, H, d, d, std=0.02, seed=3, device=dev)
+    t = gen.decode_token_inputs(256, H, d, d, "bf16", "uniform", seed=3, step=0, device=dev)
+    print("counters: decode step", flush=True)
+    kda.decode_step(t["q"], t["k"], t["v"], t["log_alpha"], t["beta"], S)
+    torch.cuda.synchronize()
+    do = gen.normal((T, H, d), 2, gen.DO, dev, torch.bfloat16)
+    print("counters: backward T=%d" % T, flush=True)
+    kda.backward(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"], do)
+    torch.cuda.synchronize()
+    del inp, do
+    torch.cuda.empty_cache()
+    a = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    print("counters: 512 MiB copy", flush=True)
+    b.copy_(a)                       # 512 MiB read + 512 MiB written
+    torch.cuda.synchronize()
+    print("counters done", flush=True)
 
 
 def source_digest(names):
@@ -266,6 +329,9 @@ def main():
     dev = "cuda"
     kda.load_library()
     stream = torch.cuda.current_stream()
+    if args.counters:
+        run_counter_workloads(torch, kda, gen, args.chunks)
+        return
     if args.only_backward:
         wb = gen.WORKLOADS["long_t1m"]
         inb = gen.workload_prefill_inputs(wb, seed=2, device=dev)
@@ -469,12 +535,16 @@ def main():
         oo = torch.empty((To, wo.H, wo.dv), dtype=io["q"].dtype, device=dev)
         ho = torch.empty((No, wo.H, wo.dk, wo.dv), dtype=torch.float32, device=dev)
         wso = torch.empty(max(1, kda.prefill_workspace_bytes(To, No, wo.H, wo.dk, wo.dv,
-                                                             kda.DTYPE_F32 if esz == 4 else kda.DTYPE_BF16)),
+                                                             kda.DTYPE_F32 if esz == 4 else kda.DTYPE_BF16,
+                                                             max_seqlen=max(io["lengths"]))),
                           dtype=torch.uint8, device=dev)
+
+        msl = max(io["lengths"])
 
         def run_o():
             kda.prefill(io["q"], io["k"], io["v"], io["log_alpha"], io["beta"], h0=io["h0"],
-                        cu_seqlens=io["cu_seqlens"], out=oo, final_state=ho, workspace=wso)
+                        cu_seqlens=io["cu_seqlens"], out=oo, final_state=ho, workspace=wso,
+                        max_seqlen=msl)
         o_ms = timed(run_o, max(args.steps, 20))
         # q, k, v, o in the input dtype, fp32 gates and beta; states in and out
         per_ht = (2 * wo.dk + 2 * wo.dv) * esz + 4 * wo.dk + 4
@@ -558,6 +628,7 @@ def main():
         head_tokens_per_s = nt * len(heads) / cpu_s
         result["cpu_baseline"] = {
             "value": head_tokens_per_s / H, "unit": "tokens/s", "cores": threads,
+            "host_cores": os.cpu_count(), "cpu_model": cpu_model(),
             "kind": "oracle",
             "sample": "%d of %d heads x first %d tokens of the prefill workload (fp64 "
                       "token loop, one thread per head), %.1f s; tokens/s scaled to all "

@@ -299,7 +299,11 @@ struct alignas(16) PrepLds {
         float bm[C * (C + 1)];
     } u2;
     float bs[C];
+    int wild;
 };
+
+// |g| (natural log units) up to which e^{g} and e^{-g} stay inside fp32
+constexpr float kSafeGate = 80.f;
 
 template <int GATE>
 __global__ __launch_bounds__(GT, 2)
@@ -329,8 +333,20 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     load_rows4(q, c, H, qr4);
     float g[4][4];
     f32x4 G;
+    if (tid == 0) sm.wild = 0;
     chunk_gates<GATE>(la, beta, c, H, sm.u2.a.scan, sm.u2.a.tot, sm.bs, g, G);
     if (tid < D) oGam[tid] = gate_exp(sm.u2.a.tot[tid]);
+    {
+        // the factored form's range: a chunk beyond it is flagged below
+        bool wild = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            wild |= !(fabsf(G[j]) <= kSafeGate);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wild |= !(fabsf(g[i][j]) <= kSafeGate);
+        }
+        if (wild) sm.wild = 1;
+    }
     // gated keys and queries
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -433,6 +449,17 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     mm<4, 8, C, GT, kKc, kMc>(sm.u1.b.tt, LDC, sm.kg, LDD, [&](int mi, int ni, f32x4 acc) {
         put4t(oWt + (16 * ni + ln) * C + 16 * mi + 4 * g4, -acc);
     });
+    // A chunk whose decays leave the factored form's range (e^{-g} would
+    // overflow) cannot be differentiated here: its whole operand record
+    // becomes NaN, so every gradient that depends on it -- this chunk's and,
+    // through the state adjoint, every earlier chunk's of the sequence and
+    // head, and dh0 -- comes out NaN instead of silently wrong.
+    if (sm.wild) {
+        __syncthreads();
+        // 0x7fc0 is a bf16 NaN, and the pair 0x7fc07fc0 an fp32 NaN
+        const u32x4 nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+        for (int x = tid; x < kSlot / 16; x += GT) reinterpret_cast<u32x4*>(out)[x] = nan4;
+    }
 }
 
 // ===================================================================

@@ -22,6 +22,10 @@
 // The rows of S never mix in any of these maps, so each work-group owns a
 // tile of TV state columns (value channels) and the tiles run in parallel.
 //
+// Any gate: where a chunk's cumulative gate leaves the factored form's range,
+// A and P are summed entry by entry with their own factors e^{g_r - g_s}
+// from fp64 cumulative gates (see the kernel).
+//
 // One work-group of 256 threads per (sequence, head, value tile) walks the
 // sequence's chunks in order; the last chunk is masked (rows past the end
 // carry k = q = v = 0, log_alpha = 0, beta = 0, so they change nothing).
@@ -30,6 +34,11 @@
 #include "kda_sched.h"
 
 namespace kda {
+
+// |g| (natural log units) up to which the factored form e^{g} e^{-g} runs:
+// its factors then stay far inside fp32, and their relative error (about
+// |g| 2^-23 each) inside the fp32 parity bar
+constexpr float kSafeGate = 16.f;
 
 template <typename T, int DK, int TV, int C>
 __global__ __launch_bounds__(256)
@@ -49,6 +58,10 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
     __shared__ float sS[DK * TV], sV[C * TV], sX[C * TV], sE[C * TV];
     __shared__ float sBeta[C], sGl[DK], sGe[DK];
     __shared__ float sNk[C], sNq[C];   // front-end: 1 / ||k||, 1 / ||q|| per row
+    // the exact form (below): cumulative gates in fp64, so that differences
+    // g_r - g_s keep full fp32 precision however long the decay
+    __shared__ double sGd[C * KP], sGdl[DK];
+    __shared__ int sExact;
 
     int64_t pair;
     int tile;
@@ -122,17 +135,50 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
             }
             __syncthreads();
         }
-        // cumulative gate per key channel
+        // cumulative gate per key channel; a chunk where some |g| leaves the
+        // range of the factored form (or is NaN) takes the exact form
+        if (tid == 0) sExact = 0;
+        __syncthreads();
         for (int c = tid; c < DK; c += NT) {
             float g = 0.f;
+            double gd = 0.0;
+            bool wild = false;
             for (int r = 0; r < C; ++r) {
-                g += sKn[r * KP + c];
+                const float la = sKn[r * KP + c];
+                g += la;
+                gd += static_cast<double>(la);
                 sKn[r * KP + c] = g;
+                sGd[r * KP + c] = gd;
+                wild |= !(fabsf(g) <= kSafeGate);
             }
             sGl[c] = g;
+            sGdl[c] = gd;
             sGe[c] = gate_exp(g);
+            if (wild) sExact = 1;
         }
         __syncthreads();
+        const bool exact = sExact != 0;
+        if (exact) {
+            // A and P entry by entry: every factor e^{g_r - g_s} (s <= r) is
+            // at most 1 and is formed from an fp64 difference, so no decay is
+            // out of range and none loses precision
+            for (int i = tid; i < C * C; i += NT) {
+                const int r = i / C, s = i % C;
+                float a = 0.f, p = 0.f;
+                if (s <= r) {
+                    for (int c = 0; c < DK; ++c) {
+                        const float e = gate_exp(static_cast<float>(sGd[r * KP + c] - sGd[s * KP + c]));
+                        const float w = sKg[s * KP + c] * e;
+                        a += sKg[r * KP + c] * w;
+                        p += sQg[r * KP + c] * w;
+                    }
+                    a = (s < r) ? sBeta[r] * a : 0.f;
+                }
+                sA[i] = a;
+                sP[i] = p;
+            }
+            __syncthreads();
+        }
         // decay-weighted copies of k and q
         for (int i = tid; i < C * DK; i += NT) {
             const int r = i / DK, c = i % DK;
@@ -143,11 +189,12 @@ void prefill_valu_kernel(const T* __restrict__ q, const T* __restrict__ k,
             sKg[r * KP + c] = kk * eg;
             sQg[r * KP + c] = sQg[r * KP + c] * eg;
             sKn[r * KP + c] = kk * emg;
-            sKd[r * KP + c] = kk * gate_exp(sGl[c] - g);
+            sKd[r * KP + c] = kk * (exact ? gate_exp(static_cast<float>(sGdl[c] - sGd[r * KP + c]))
+                                          : gate_exp(sGl[c] - g));
         }
         __syncthreads();
         // A (strictly lower, rows scaled by beta) and P (lower, with diagonal)
-        for (int i = tid; i < C * C; i += NT) {
+        for (int i = tid; i < C * C && !exact; i += NT) {
             const int r = i / C, s = i % C;
             float a = 0.f, p = 0.f;
             if (s <= r) {

@@ -37,6 +37,7 @@
 // holds a bounded block of slots (and stays mostly cache-resident) while
 // the state is carried between blocks through hT (or a workspace copy).
 #include <algorithm>
+#include <type_traits>
 
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -88,6 +89,7 @@ struct alignas(16) PrepSmem {
     uint16_t tok[3][C * TS];   // Kg, Kn, Qg: token rows, channels in fragment order
     float beta[C];
     float glog[DK];            // G / ln 2
+    int exact;                 // nonzero: A and P by the exact pairwise factors
 };
 // 53 KB: three work-groups fit in one CU's LDS.  Reuse of the token rows:
 // - tok[0] first holds the per 4-row group gate sums and then their
@@ -126,18 +128,212 @@ __device__ __forceinline__ f32x4 row_product(const uint16_t* x, const uint16_t* 
     return acc;
 }
 
-// (I + N)^{-1} for N = strictly-lower(Diag(beta) Kg_I Kn_I^T), on MFMA.
-// With Y in the accumulator layout (lane (g, ln) holds Y[4g+i][ln]) passed
-// as the A operand of a 16x16x16 product, the product sees Y^T; keeping
-// both N and N^T lets every factor enter in the layout it is needed in.
-// The result is formed transposed, X^T = (I + N^2^T)(I + N^4^T)(I + N^8^T)
-// (I - N^T), whose accumulator layout is the A-operand layout of X: lane
-// (g, ln) gets X[ln][4g .. 4g+3].
+// ---- the exact pairwise form of the decay-weighted products ----
+// The factored operands Kg = K e^{g} and Kn = K e^{-g} stay inside fp32
+// only while every |g| of the chunk is below kSafeLog2 (log2 units; e^{80}):
+// beyond that a channel's e^{-g} overflows, although every factor the
+// products need, e^{g_r - g_s} with s <= r, lies in (0, 1].  Such a chunk
+// takes this path instead: each entry of A and P is summed over the
+// channels with its own factor,
+//   Araw[r][s] = sum_c k_r[c] k_s[c] e^{g_r[c] - g_s[c]}        (s <= r)
+//   P[r][s]    = sum_c q_r[c] k_s[c] e^{g_r[c] - g_s[c]}
+// on the vector units, into fp32 tables that the tile jobs read in place of
+// their matrix-core products.  Any per-token gate is then in range.
+constexpr float kSafeLog2 = 115.f;
+constexpr int XS = 33;          // fp32 stride of the staged 32-channel rows
+constexpr int AS = C + 1;       // fp32 stride of the 64 x 64 tables
+
+__device__ __forceinline__ float* table_a(PrepSmem& sm) { return reinterpret_cast<float*>(sm.tok[1]); }
+__device__ __forceinline__ float* table_p(PrepSmem& sm) { return reinterpret_cast<float*>(sm.tok[1]) + C * AS; }
+static_assert(2 * C * AS * sizeof(float) <= 2 * C * TS * sizeof(uint16_t), "the tables fit in tok[1..2]");
+static_assert(3 * C * XS * sizeof(float) <= 2 * C * TS * sizeof(uint16_t), "a staged round fits in tok[1..2]");
+
+// Work split over the 512 threads: the 240 blocks of 4 rows x 2 columns
+// strictly below the diagonal 4x4 blocks, two threads each (16 of every 32
+// staged channels apiece), and the 32 blocks of 4 x 2 that make up the
+// diagonal 4x4 blocks, one thread each.  Per round of 32 channels the
+// threads that own them (cg / 8 == round) reload their 4 rows x 4 channels
+// of k and q (normalised by nk, nq when the front-end asks) and their gates
+// from L2, stage k, q and the cumulative gates (log2 units: off plus the
+// sum within the thread's 4 rows) as rows of XS floats, and rewrite their
+// part of Kd^T in the slot with e^{G - g} as one exponential (the common
+// path's e^{G} e^{-g} may overflow here).  Called by every thread after a
+// barrier that ends all reads of tok[1..2]; returns after the barrier that
+// publishes the tables.  Its loops stay rolled: a small register
+// footprint keeps the common path's allocation as it is.
+template <int GATE, bool FRONT>
+__device__ __forceinline__
+void exact_ap_tables(PrepSmem& sm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                     const float* __restrict__ log_alpha, const uint16_t* __restrict__ gate_pre,
+                     float gate_scale, int64_t c0, int H, int h, int len, f32x4 off, f32x4 nk,
+                     f32x4 nq, uint8_t* __restrict__ out)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int cg = lane & 31;
+    const int rg = 2 * (tid >> 6) + (lane >> 5);
+    float* sk = reinterpret_cast<float*>(sm.tok[1]);
+    float* sq = sk + C * XS;
+    float* sg = sq + C * XS;
+    const bool diag = tid >= 480;
+    int bi, bj, cw, c0w;                 // rows 4bi .. +3, columns 2bj .. +1
+    if (!diag) {
+        const int u = tid >> 1;          // row block bi holds 2 bi column pairs
+        bi = static_cast<int>((1.f + __builtin_sqrtf(1.f + 4.f * static_cast<float>(u))) * 0.5f);
+        while (bi * (bi - 1) > u) --bi;
+        while ((bi + 1) * bi <= u) ++bi;
+        bj = u - bi * (bi - 1);
+        cw = 16;
+        c0w = 16 * (tid & 1);
+    } else {
+        const int d = tid - 480;
+        bi = d >> 1;
+        bj = 2 * bi + (d & 1);
+        cw = 32;
+        c0w = 0;
+    }
+    float a[4][2], pp[4][2];
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) a[x][y] = pp[x][y] = 0.f;
+#pragma unroll 1
+    for (int round = 0; round < 4; ++round) {          // channels 32 round .. +31
+        if (round > 0) __syncthreads();                 // the last round's reads are done
+        if ((cg >> 3) == round) {
+            const int64_t e0 = (c0 * H + h) * DK;
+            const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
+            float gsum[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rg + i;
+                f32x4 la;
+                if (FRONT && gate_pre) {
+                    if constexpr (GATE == kGateChannel) {
+                        const u32x2 w = ld64(rsrc(gate_pre + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
+                        la = f32x4{-gate_scale * softplus_f32(lo_bf(w[0])),
+                                   -gate_scale * softplus_f32(hi_bf(w[0])),
+                                   -gate_scale * softplus_f32(lo_bf(w[1])),
+                                   -gate_scale * softplus_f32(hi_bf(w[1]))};
+                    } else {
+                        const float x = -gate_scale * softplus_f32(bf16_to_f32(ld16(
+                            rsrc(gate_pre + c0 * H + h, 2u * static_cast<uint32_t>((len - 1) * H + 1)),
+                            2 * r * H)));
+                        la = f32x4{x, x, x, x};
+                    }
+                    if (r >= len) la = f32x4{0.f, 0.f, 0.f, 0.f};
+                } else if constexpr (GATE == kGateChannel) {
+                    la = __builtin_bit_cast(f32x4, ld128(rsrc(log_alpha + e0, 4u * span),
+                                                         4 * (r * H * DK + 4 * cg)));
+                } else {
+                    const float x = log_alpha
+                        ? __uint_as_float(ld32(rsrc(log_alpha + c0 * H + h,
+                                                    4u * static_cast<uint32_t>((len - 1) * H + 1)),
+                                               4 * r * H))
+                        : 0.f;
+                    la = f32x4{x, x, x, x};
+                }
+                const u32x2 kw = ld64(rsrc(k + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
+                const u32x2 qw = ld64(rsrc(q + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
+                float kd[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    gsum[j] = __builtin_fmaf(la[j], kLog2e, gsum[j]);
+                    const float gl = off[j] + gsum[j];
+                    float kx = (j & 1) ? hi_bf(kw[j >> 1]) : lo_bf(kw[j >> 1]);
+                    float qx = (j & 1) ? hi_bf(qw[j >> 1]) : lo_bf(qw[j >> 1]);
+                    if constexpr (FRONT) {
+                        kx *= nk[i];
+                        qx *= nq[i];
+                    }
+                    const int e = r * XS + 4 * (cg & 7) + j;
+                    sk[e] = kx;
+                    sq[e] = qx;
+                    sg[e] = gl;
+                    kd[j] = kx * __builtin_amdgcn_exp2f(sm.glog[4 * cg + j] - gl);
+                }
+                // Kd^T as the A operand of pass 2 (the common path's layout)
+                const int x0 = 4 * rg;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int c = 4 * cg + j;
+                    const int fl = 16 * ((x0 & 15) >> 2) + (c & 15);
+                    reinterpret_cast<uint16_t*>(out + (kFragK + 2 * (c >> 4) + (x0 >> 5)) * kFrag +
+                                                fl * 16 + 8 * ((x0 & 31) >> 4))[i] =
+                        static_cast<uint16_t>(pk(kd[j], 0.f) & 0xffffu);
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll 1
+        for (int cc = 0; cc < cw; ++cc) {
+            const int c = c0w + cc;
+            float kr[4], qr[4], gr[4], ks[2], gs[2];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                kr[x] = sk[(4 * bi + x) * XS + c];
+                qr[x] = sq[(4 * bi + x) * XS + c];
+                gr[x] = sg[(4 * bi + x) * XS + c];
+            }
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                ks[y] = sk[(2 * bj + y) * XS + c];
+                gs[y] = sg[(2 * bj + y) * XS + c];
+            }
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    if (2 * bj + y > 4 * bi + x) continue;   // above the diagonal
+                    const float w = ks[y] * __builtin_amdgcn_exp2f(gr[x] - gs[y]);
+                    a[x][y] = __builtin_fmaf(kr[x], w, a[x][y]);
+                    pp[x][y] = __builtin_fmaf(qr[x], w, pp[x][y]);
+                }
+        }
+    }
+    // the two channel halves of a block sit in adjacent lanes
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y) {
+            const float ta = a[x][y] + __shfl_xor(a[x][y], 1);
+            const float tp = pp[x][y] + __shfl_xor(pp[x][y], 1);
+            a[x][y] = diag ? a[x][y] : ta;
+            pp[x][y] = diag ? pp[x][y] : tp;
+        }
+    __syncthreads();                                    // the staged rows are dead
+    if (diag || (tid & 1) == 0) {
+        float* ta = table_a(sm);
+        float* tp = table_p(sm);
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                ta[(4 * bi + x) * AS + 2 * bj + y] = a[x][y];
+                tp[(4 * bi + x) * AS + 2 * bj + y] = pp[x][y];
+            }
+    }
+    __syncthreads();
+}
+
+// a = (Kg_I Kn_I^T)[4g+i][ln] and at = (Kg_I Kn_I^T)[ln][4g+i] from the
+// matrix cores, or from the exact table when the chunk takes that form
+template <bool EXACT>
 __device__ __forceinline__ u32x2 diag_inverse(const PrepSmem& sm, int I, int g, int ln) {
-    const uint16_t* kgI = sm.tok[0] + 16 * I * TS;
-    const uint16_t* knI = sm.tok[1] + 16 * I * TS;
-    const f32x4 a = row_product(kgI, knI, g, ln);    // (Kg_I Kn_I^T)[4g+i][ln]
-    const f32x4 at = row_product(knI, kgI, g, ln);   // (Kg_I Kn_I^T)[ln][4g+i]
+    f32x4 a, at;
+    if constexpr (EXACT) {
+        const float* ta = reinterpret_cast<const float*>(sm.tok[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            a[i] = ta[(16 * I + 4 * g + i) * AS + 16 * I + ln];
+            at[i] = ta[(16 * I + ln) * AS + 16 * I + 4 * g + i];
+        }
+    } else {
+        const uint16_t* kgI = sm.tok[0] + 16 * I * TS;
+        const uint16_t* knI = sm.tok[1] + 16 * I * TS;
+        a = row_product(kgI, knI, g, ln);
+        at = row_product(knI, kgI, g, ln);
+    }
     const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta + 16 * I + 4 * g);
     const float bl = sm.beta[16 * I + ln];
     f32x4 N, NT, eye;
@@ -208,7 +404,7 @@ __device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
 // from bf16 pre-activations (log_alpha = -fe.gate_scale softplus(x)) when
 // fe.gate_pre, beta = sigmoid(y) from bf16 fe.beta_pre
 template <int GATE, bool FRONT>
-__global__ __launch_bounds__(PT, 3)
+__global__ __launch_bounds__(PT, 5)
 void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                             const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
                             const float* __restrict__ beta, const int32_t* __restrict__ cu,
@@ -235,6 +431,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     const int ln = lane & 15;
     const int cg = lane & 31;                  // staging: channels 4cg .. 4cg+3
     const int rg = 2 * wave + (lane >> 5);     //          rows 4rg .. 4rg+3
+    if (tid == 0) sm.exact = 0;
 
     // ---------------- staging loads (rows past the end read zero) ----------
     const int64_t e0 = (c0 * H + h) * DK;
@@ -363,6 +560,9 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
 #pragma unroll
     for (int j = 0; j < 4; ++j) gamma[j] = __builtin_amdgcn_exp2f(G[j]);
     const int cpos = fpos(4 * cg);              // the 4 channels' position in a token row
+    // wild: outside the factored form's range anywhere in this thread's
+    // part of the chunk (NaN counts as outside)
+    bool wild = false;
     float kg[4][4], kd[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -373,7 +573,10 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             const float gl = off[j] + p[i][j];
             const float u = __builtin_amdgcn_exp2f(gl);
             const float w = __builtin_amdgcn_exp2f(-gl);
-            const float d = gamma[j] * w;       // e^{G - g}: both factors stay in range
+            // e^{G - g} as e^{G} e^{-g}: both factors stay in range unless the
+            // chunk is wild, where the exact form rewrites Kd^T directly
+            wild |= !(fabsf(gl) <= kSafeLog2 && fabsf(G[j]) <= kSafeLog2);
+            const float d = gamma[j] * w;
             const uint32_t kw = kr[i][j >> 1], qw = qr[i][j >> 1];
             float kx = (j & 1) ? hi_bf(kw) : lo_bf(kw);
             float qx = (j & 1) ? hi_bf(qw) : lo_bf(qw);
@@ -391,6 +594,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
         *reinterpret_cast<u32x2*>(sm.tok[2] + r * TS + cpos) =
             u32x2{pk(qg[0], qg[1]), pk(qg[2], qg[3])};
     }
+    if (wild) sm.exact = 1;
     {
         const int x = 4 * rg;                   // first of this thread's 4 tokens
 #pragma unroll
@@ -405,6 +609,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
         }
     }
     __syncthreads();   // every gate offset has been read: tok[0] takes the Kg rows
+    const bool exact = sm.exact != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         *reinterpret_cast<u32x2*>(sm.tok[0] + (4 * rg + i) * TS + cpos) =
@@ -423,44 +628,73 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             *reinterpret_cast<const u32x4*>(sm.tok[2] + (16 * I + (ul & 15)) * TS + 32 * kk + 8 * (ul >> 4));
     }
 
+    if (exact) {
+        __syncthreads();   // the copy above has read the Qg rows
+        exact_ap_tables<GATE, FRONT>(sm, q, k, log_alpha, fe.gate_pre, fe.gate_scale, c0, H, h, len,
+                                     off, f32x4{nk[0], nk[1], nk[2], nk[3]},
+                                     f32x4{nq[0], nq[1], nq[2], nq[3]}, out);
+    }
+
     // ---------------- A and P tiles, diagonal inverses ---------------------------
     // jobs 0..5: strictly-lower A blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2);
     // jobs 6..15: lower P blocks (0,0) (1,0) (1,1) (2,0) .. (3,3).  Waves 0..3
     // invert diagonal block I = wave and take job 12 + wave; waves 4..7 take
     // jobs wave-4, wave and wave+4.
+    // The exact form reads the tables instead of the matrix cores: a
+    // separate instantiation of the jobs, so the common path's code and
+    // registers stay as they are.
     u32x2 dres = {0u, 0u};
-    if (wave < 4) dres = diag_inverse(sm, wave, g, ln);
     f32x4 aval[2];
     int aidx[2] = {-1, -1};
+    auto jobs = [&](auto exact_form) {
+        constexpr bool EX = decltype(exact_form)::value;
+        const float* tab_a = table_a(sm);
+        const float* tab_p = table_p(sm);
+        if (wave < 4) dres = diag_inverse<EX>(sm, wave, g, ln);
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
-        const int j = wave < 4 ? (x == 0 ? 12 + wave : -1) : wave - 4 + 4 * x;
-        if (j < 0) continue;
-        if (j < 6) {
-            const int I = j < 1 ? 1 : j < 3 ? 2 : 3;
-            const int J = j - an_index(I, 0);
-            const f32x4 acc = row_product(sm.tok[0] + 16 * I * TS, sm.tok[1] + 16 * J * TS, g, ln);
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta + 16 * I + 4 * g);
-            const int slotx = x == 0 ? 0 : 1;      // jobs j < 6 come at x = 0 and x = 1
-            aval[slotx] = -bt * acc;
-            aidx[slotx] = j;
-        } else {
-            const int t = j - 6;
-            const int I = (t >= 1) + (t >= 3) + (t >= 6);
-            const int J = t - I * (I + 1) / 2;
-            // P^T block: acc[i] = P[16I + ln][16J + 4g + i]; diagonal blocks keep s <= r
-            const f32x4 acc = row_product(sm.tok[1] + 16 * J * TS, sm.tok[2] + 16 * I * TS, g, ln);
-            u32x2 pv = pack2(acc);
-            if (I == J) {
-                f32x4 mk;
+        for (int x = 0; x < 3; ++x) {
+            const int j = wave < 4 ? (x == 0 ? 12 + wave : -1) : wave - 4 + 4 * x;
+            if (j < 0) continue;
+            if (j < 6) {
+                const int I = j < 1 ? 1 : j < 3 ? 2 : 3;
+                const int J = j - an_index(I, 0);
+                f32x4 acc;
+                if constexpr (EX) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) mk[i] = (4 * g + i <= ln) ? acc[i] : 0.f;
-                pv = pack2(mk);
+                    for (int i = 0; i < 4; ++i) acc[i] = tab_a[(16 * I + 4 * g + i) * AS + 16 * J + ln];
+                } else {
+                    acc = row_product(sm.tok[0] + 16 * I * TS, sm.tok[1] + 16 * J * TS, g, ln);
+                }
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta + 16 * I + 4 * g);
+                const int slotx = x == 0 ? 0 : 1;      // jobs j < 6 come at x = 0 and x = 1
+                aval[slotx] = -bt * acc;
+                aidx[slotx] = j;
+            } else {
+                const int t = j - 6;
+                const int I = (t >= 1) + (t >= 3) + (t >= 6);
+                const int J = t - I * (I + 1) / 2;
+                // P^T block: acc[i] = P[16I + ln][16J + 4g + i]; diagonal blocks keep s <= r
+                f32x4 acc;
+                if constexpr (EX) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] = tab_p[(16 * I + ln) * AS + 16 * J + 4 * g + i];
+                } else {
+                    acc = row_product(sm.tok[1] + 16 * J * TS, sm.tok[2] + 16 * I * TS, g, ln);
+                }
+                u32x2 pv = pack2(acc);
+                if (I == J) {
+                    f32x4 mk;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) mk[i] = (4 * g + i <= ln) ? acc[i] : 0.f;
+                    pv = pack2(mk);
+                }
+                *reinterpret_cast<u32x2*>(out + (kFragP + p_frag(I, J >> 1)) * kFrag + lane * 16 +
+                                          8 * (J & 1)) = pv;
             }
-            *reinterpret_cast<u32x2*>(out + (kFragP + p_frag(I, J >> 1)) * kFrag + lane * 16 +
-                                      8 * (J & 1)) = pv;
         }
-    }
+    };
+    if (exact) jobs(std::true_type{});
+    else jobs(std::false_type{});
     if (wave == 0 || wave == 2)   // zero upper halves of the P operands (0,0) and (2,1)
         *reinterpret_cast<u32x2*>(out + (kFragP + p_frag(wave, wave >> 1)) * kFrag + lane * 16 + 8) =
             u32x2{0u, 0u};

@@ -109,7 +109,9 @@ enum kda_path {
     KDA_PATH_MATRIX = 2,   /* bf16 matrix cores, fp32 accumulation and
                               state, chunks of 64 tokens, one fused kernel
                               per (sequence, head, value tile); bf16 and
-                              d_k = 128 */
+                              d_k = 128; chunks whose gates leave the
+                              factored range come out NaN (see
+                              kda_fwd_prefill) */
     KDA_PATH_MATRIX_TWO_PASS = 3
                            /* the same arithmetic in two kernels: a
                               chunk-parallel pass builds each chunk's
@@ -306,9 +308,21 @@ size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H,
  * Precision: bf16 inputs use bf16 matrix-core products with fp32
  * accumulation and an fp32 state; fp32 inputs use fp32 arithmetic
  * throughout.  o is written in the input dtype (round to nearest even).
- * Within one chunk of tokens the decay factors exp(+-cumulative log_alpha)
- * are formed separately, so the summed log_alpha of one channel over a
- * chunk (64 tokens) must stay above -80 (e.g. per-token gates >= -1.25).
+ * Gate range: every path takes any log_alpha <= 0 (any alpha in (0, 1]).
+ * Within a chunk the kernels normally form the decays as
+ * exp(g) * exp(-g) of the chunk's cumulative gate g, which stays inside
+ * fp32 while |g| <= 80 (natural log).  A chunk beyond that (a channel whose
+ * gates sum below -80 over the chunk, e.g. per-token gates below -1.25 on
+ * the matrix paths' 64-token chunks) is handled as follows:
+ *   two-pass matrix and vector paths: the chunk's decay-weighted products
+ *     are summed entry by entry with their own factors exp(g_r - g_s) <= 1
+ *     (the vector path from fp64 cumulative gates, and already beyond
+ *     |g| = 16): exact, at a higher cost for that chunk (a two-pass
+ *     prefill whose every chunk takes this form runs about 2.7x longer);
+ *   fused matrix path: that chunk's outputs, every later output of the
+ *     same (sequence, head, value tile) and its final state are NaN --
+ *     never finite and wrong; request KDA_PATH_MATRIX_TWO_PASS for such
+ *     gates.
  *
  * Requirements (else the status in brackets):
  *   N >= 1, H >= 1, total_T >= 0, sizes whose byte counts fit in int64
@@ -471,7 +485,11 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * the workspace [INVALID_ARGUMENT]; workspace_bytes at least
  * kda_bwd_workspace_bytes [WORKSPACE_TOO_SMALL].
  * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
- * adjoints, as in the forward pass.
+ * adjoints, as in the forward pass.  Gate range: a chunk whose cumulative
+ * gate leaves the factored form's range (|g| > 80, see kda_fwd_prefill) is
+ * not differentiated: its gradients, those of every earlier chunk of the
+ * same (sequence, head) and that dh0 come out NaN -- never finite and
+ * wrong.
  * Saved states (options->chunk_states): the record of the forward pass on
  * these inputs replaces its recomputation (the call then reads the record
  * and needs a smaller workspace); the record must come from a forward pass

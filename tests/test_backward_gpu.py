@@ -28,6 +28,10 @@ LENS = [300, 64, 1, 129, 0, 77]
 
 
 def case(lens, H, seed, gate="channel", h0=True, dhT=True):
+    return make_case(lens, H, seed, gate, h0, dhT)
+
+
+def make_case(lens, H, seed, gate="channel", h0=True, dhT=True):
     inp = gen.prefill_inputs(lens, H, 128, 128, "bf16", "softplus", state_std=0.05 if h0 else 0.0,
                              seed=seed, device=DEV)
     T = inp["q"].shape[0]
@@ -78,6 +82,40 @@ def compare(name, g, r, heads=None):
 def test_backward_parity(gate):
     inp = case(LENS, 2, 300, gate)
     compare("backward %s" % gate, gpu(inp, gate), ref(inp))
+
+
+@pytest.mark.parametrize("case", ["decay_1", "decay_3", "mixed_0_10"])
+def test_backward_gate_domain(case):
+    """Gates up to the factored form's range (-1 per token: a chunk sums to
+    -64) match the oracle; beyond it (-3, or a mix of undecayed and -10
+    channels) the backward flags the chunks it cannot differentiate with
+    NaN: every gradient is either within the bar or NaN, never finite and
+    wrong."""
+    inp = make_case(LENS, 2, 390)
+    la = inp["log_alpha"]
+    if case == "decay_1":
+        la.fill_(-1.0)
+    elif case == "decay_3":
+        la.fill_(-3.0)
+    else:
+        la[..., 0::2] = 0.0
+        la[..., 1::2] = -10.0
+    g = gpu(inp, "channel")
+    r = ref(inp)
+    errs, finite = {}, {}
+    for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"):
+        x = host(g[key])
+        f = np.isfinite(x)
+        finite[key] = float(f.mean())
+        scale_ = max(float(np.max(np.abs(r[key]))), 1e-30)
+        errs[key] = float(np.max(np.abs(x[f] - r[key][f]), initial=0.0)) / scale_
+    report("backward gates %s (finite fraction %s)" % (case, finite), **errs)
+    for key, e in errs.items():
+        assert e <= TOL, (key, e)
+    if case == "decay_1":
+        assert all(v == 1.0 for v in finite.values()), finite
+    else:
+        assert finite["dq"] < 1.0                   # the flag fired
 
 
 def test_backward_zero_state_and_adjoint():

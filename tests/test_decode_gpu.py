@@ -101,6 +101,34 @@ def test_decode_chain_equals_prefill():
     assert e_o <= TOL_F32 and e_s <= TOL_F32
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("gate", [-3.0, -10.0, "mixed_0_10"])
+def test_decode_whole_gate_domain(dtype, gate):
+    """Strong decays (alpha = e^-3, e^-10, or a mix of 1 and e^-10 over the
+    key channels): one token at a time there is nothing to overflow, and
+    decode chained over a sequence still equals the prefill of it."""
+    N, H, dk, dv = 4, 2, 128, 64
+    S = gen.decode_state(N, H, dk, dv, std=0.5, seed=17, device=DEV)
+    S_ref = host(S)
+    eo = es = 0.0
+    for step in range(4):
+        tok = gen.decode_token_inputs(N, H, dk, dv, dtype, "uniform", seed=17, step=step,
+                                      device=DEV)
+        la = tok["log_alpha"]
+        if gate == "mixed_0_10":
+            la[..., 0::2] = 0.0
+            la[..., 1::2] = -10.0
+        else:
+            la.fill_(gate)
+        o = kda.decode_step(tok["q"], tok["k"], tok["v"], la, tok["beta"], S)
+        o_ref, S_ref = oracle.decode_step(host(tok["q"]), host(tok["k"]), host(tok["v"]),
+                                          host(la), host(tok["beta"]), S_ref)
+        eo = max(eo, rel_err(host(o), o_ref))
+        es = max(es, rel_err(host(S), S_ref))
+    report("decode %s gates %s" % (dtype, gate), o=eo, S=es)
+    assert eo <= tol_for(dtype) and es <= TOL_F32
+
+
 def test_decode_only_touches_own_state():
     N, H, d = 6, 2, 32
     S = gen.decode_state(N, H, d, d, std=1.0, seed=5, device=DEV)

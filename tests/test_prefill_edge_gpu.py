@@ -4,8 +4,15 @@ for every kernel path, against the fp64 oracle (through the C ABI).
 Gates: no decay with beta = 1 (DeltaNet with full writes); beta = 0 (the
 state only decays: outputs read the decayed initial state); per-token
 gates of -1.2 on every channel, so the summed gate over a 64-token chunk
-reaches -76.8, next to the -80 bound the library documents for its factored
-exponentials; and a mix of undecayed and strongly decayed channels.
+reaches -76.8, the edge of the factored exponentials' range; a mix of
+undecayed and -1.2 channels; and the rest of the gate domain the pages
+allow (any alpha in (0, 1], "Kimi Delta Attention: la atencion lineal
+detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta Attention
+paso a paso"): -3 and -10 per token on every channel, a mix of undecayed
+and -10 channels, and per-token gates uniform in [-12, 0].  Beyond the
+factored range the two-pass and vector paths switch to the exact pairwise
+form and must match the oracle; the fused path flags such chunks with NaN
+(its outputs are either right or NaN, never finite and wrong).
 
 Batch: 200 short sequences (lengths 0..150, empty ones included, non-zero
 initial states), through each path; on the two-pass path this also walks
@@ -56,7 +63,42 @@ def gate_case(inp, case):
     elif case == "mixed":
         la[:, :, 0::2] = 0.0
         la[:, :, 1::2] = -1.2
+    elif case == "decay_3":
+        la.fill_(-3.0)
+    elif case == "decay_10":
+        la.fill_(-10.0)
+    elif case == "mixed_0_10":
+        la[:, :, 0::2] = 0.0
+        la[:, :, 1::2] = -10.0
+    elif case == "uniform_12":
+        g = torch.Generator(device="cpu").manual_seed(83)
+        la.copy_(-12.0 * torch.rand(la.shape, generator=g))
     return inp
+
+
+WIDE = ["decay_3", "decay_10", "mixed_0_10", "uniform_12"]
+
+
+@pytest.mark.parametrize("dtype,path", PATHS)
+@pytest.mark.parametrize("case", WIDE)
+def test_whole_gate_domain(dtype, path, case):
+    inp = gen.prefill_inputs([300, 64, 1, 129], 2, 128, 128, dtype, "uniform", state_std=0.1,
+                             seed=84, device=DEV)
+    gate_case(inp, case)
+    if path != "matrix":
+        check(inp, path, dtype, "gates %s" % case)
+        return
+    o, hT = run(inp, path)
+    o_ref, h_ref = oracle_prefill(inp)
+    o_h, h_h = host(o), host(hT)
+    fin_o, fin_h = np.isfinite(o_h), np.isfinite(h_h)
+    scale_o, scale_h = np.max(np.abs(o_ref)), np.max(np.abs(h_ref))
+    eo = float(np.max(np.abs(o_h[fin_o] - o_ref[fin_o]), initial=0.0)) / scale_o
+    eh = float(np.max(np.abs(h_h[fin_h] - h_ref[fin_h]), initial=0.0)) / scale_h
+    report("gates %s fused: finite entries o %.3f hT %.3f" % (case, fin_o.mean(), fin_h.mean()),
+           o=eo, hT=eh)
+    assert eo <= tol_for(dtype) and eh <= tol_for(dtype)   # never finite and wrong
+    assert not fin_o.all()                                   # the flag fired
 
 
 @pytest.mark.parametrize("dtype,path", PATHS)
