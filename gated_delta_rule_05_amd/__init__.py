@@ -84,7 +84,7 @@ EXPORTED_SYMBOLS = ("kda_abi_version", "kda_status_string",
                     "kda_fwd_prefill_workspace_bytes", "kda_fwd_prefill_workspace_bytes_ex",
                     "kda_fwd_prefill", "kda_fwd_prefill_ex", "kda_decode_step",
                     "kda_decode_step_ex", "kda_decode_multi", "kda_bwd_workspace_bytes",
-                    "kda_bwd", "kda_chunk_states_bytes")
+                    "kda_bwd", "kda_chunk_states_bytes", "kda_fwd_prefill_noalloc")
 
 
 class KDAError(RuntimeError):
@@ -128,6 +128,9 @@ def load_library():
                                        i32, f32, vp, vp, vp, ctypes.c_size_t,
                                        ctypes.POINTER(PrefillOptions), vp]
     lib.kda_fwd_prefill_ex.restype = ctypes.c_int
+    lib.kda_fwd_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i32,
+                                            i32, f32, vp, vp, ctypes.POINTER(PrefillOptions), vp]
+    lib.kda_fwd_prefill_noalloc.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32,
                                     vp, vp]
     lib.kda_decode_step.restype = ctypes.c_int
@@ -276,7 +279,7 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
             out=None, final_state=True, workspace=None, path="auto", value_tiles=0,
             block_chunks=0, gate="channel", snapshot_tokens=0, snapshots=None,
             l2norm_qk=False, gate_pre=None, gate_scale=1.0, beta_pre=None, chunk_states=None,
-            max_seqlen=None):
+            max_seqlen=None, no_alloc=False):
     """Chunked prefill over a packed batch.
 
     q, k: [T, H, d_k]; v: [T, H, d_v] (bf16 or fp32, same dtype);
@@ -302,6 +305,9 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     ``max_seqlen``: at least the longest sequence (T when cu_seqlens is
     None); None leaves it unknown.  The two-pass path then launches blocks
     for that many tokens only, not for total_T.
+    ``no_alloc``: call kda_fwd_prefill_noalloc, whose workspace is the
+    library's static device array (``workspace`` must then be None); the
+    outputs are still allocated here unless given.
     """
     torch = _torch()
     lib = load_library()
@@ -362,6 +368,18 @@ def prefill(q, k, v, log_alpha, beta, h0=None, cu_seqlens=None, scale=None,
     if chunk_states is not None:
         _check_states(chunk_states, T, N, H, dk, dv, dev)
         opts.chunk_states = chunk_states.data_ptr()
+    if no_alloc:
+        if workspace is not None:
+            raise ValueError("no_alloc takes no workspace")
+        st = lib.kda_fwd_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha), _ptr(beta),
+                                         _ptr(h0), _ptr(cu_seqlens), T, N, H, dk, dv, code,
+                                         float(scale), _ptr(out), _ptr(hT), ctypes.byref(opts),
+                                         _stream(dev))
+        if st != 0:
+            raise KDAError(st, "kda_fwd_prefill_noalloc")
+        if snapshot_tokens:
+            return out, hT, snapshots
+        return out, hT
     need = lib.kda_fwd_prefill_workspace_bytes_ex(T, N, H, dk, dv, code, ctypes.byref(opts))
     if workspace is None:
         workspace = torch.empty((max(int(need), 1),), dtype=torch.uint8, device=dev)

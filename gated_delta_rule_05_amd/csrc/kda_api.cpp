@@ -10,6 +10,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <algorithm>
+#include <mutex>
 
 #include "../../include/kda.h"
 #include "kda_internal.h"
@@ -152,8 +154,10 @@ struct Plan {
 };
 
 // Sizes must already have passed check_sizes.
+// budget > 0: the automatic two-pass block length is capped so that the
+// workspace fits in budget bytes (the allocation-free entry point)
 int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype,
-            const kda_prefill_options* options, Plan* pl) {
+            const kda_prefill_options* options, Plan* pl, size_t budget = 0) {
     const int32_t path = options ? options->path : KDA_PATH_AUTO;
     const int32_t tiles = options ? options->value_tiles : 0;
     const int32_t blk = options ? options->block_chunks : 0;
@@ -191,6 +195,15 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     pl->R = tiles > 0 ? tiles : two ? kda::wy_value_tiles(a) : kda::mfma_value_tiles(a);
     if (two) {
         pl->L_b = blk > 0 ? blk : kda::wy_default_block_chunks(a.seq_bound(), N, H, d_v);
+        if (blk == 0 && budget > 0) {
+            // the largest block length whose workspace fits the budget
+            const size_t fixed = plan_bytes(N) + kda::wy_workspace_bytes(N, H, d_k, d_v, 0);
+            const size_t per = kda::wy_workspace_bytes(N, H, d_k, d_v, 1) -
+                               kda::wy_workspace_bytes(N, H, d_k, d_v, 0);
+            const size_t fit = budget > fixed + kWorkspaceAlign
+                                   ? (budget - fixed - kWorkspaceAlign) / per : 0;
+            pl->L_b = static_cast<int>(std::max<size_t>(1, std::min<size_t>(pl->L_b, fit)));
+        }
         if (!kda::wy_block_chunks_ok(N, H, pl->L_b)) return KDA_STATUS_INVALID_ARGUMENT;
         pl->ws_bytes += kda::wy_workspace_bytes(N, H, d_k, d_v, pl->L_b);
     }
@@ -211,6 +224,44 @@ int64_t chunk_states_bytes(int64_t total_T, int32_t N, int32_t H) {
 bool bwd_shape_ok(int32_t N, int32_t H) {
     return kda::wy_supported(shape_args(0, N, H, 128, 128, KDA_DTYPE_BF16));
 }
+
+// ---- the allocation-free prefill: its workspace is this array
+// Each GPU the library runs on holds one copy of it until the process ends.
+// In host code its name is only a stand-in for the symbol: every use of the
+// memory goes through the device address looked up below.
+constexpr size_t kNoAllocBytes = KDA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The device address of the array on the device of `stream`, looked up
+// once per device with that device current (the previous device is
+// restored) and kept.
+int scratch_of(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return KDA_STATUS_HIP_ERROR;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        int prev = -1;
+        if (hipGetDevice(&prev) != hipSuccess) return KDA_STATUS_HIP_ERROR;
+        if (prev != dev && hipSetDevice(dev) != hipSuccess) return KDA_STATUS_HIP_ERROR;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (prev != dev) (void)hipSetDevice(prev);
+        if (e != hipSuccess || !ptr) return KDA_STATUS_HIP_ERROR;
+        g_scratch[dev] = ptr;
+    }
+    *out = g_scratch[dev];
+    return KDA_STATUS_OK;
+}
+
+int prefill_call(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* h0, const int32_t* cu_seqlens, int64_t total_T,
+                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+                 void* o, float* hT, void* workspace, size_t workspace_bytes,
+                 const kda_prefill_options* options, void* stream, bool use_scratch);
 
 }  // namespace
 
@@ -262,6 +313,29 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
                        int32_t dtype, float scale, void* o, float* hT, void* workspace,
                        size_t workspace_bytes, const kda_prefill_options* options,
                        void* stream) {
+    return prefill_call(q, k, v, log_alpha, beta, h0, cu_seqlens, total_T, N, H, d_k, d_v, dtype,
+                        scale, o, hT, workspace, workspace_bytes, options, stream, false);
+}
+
+int kda_fwd_prefill_noalloc(const void* q, const void* k, const void* v, const float* log_alpha,
+                            const float* beta, const float* h0, const int32_t* cu_seqlens,
+                            int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v,
+                            int32_t dtype, float scale, void* o, float* hT,
+                            const kda_prefill_options* options, void* stream) {
+    return prefill_call(q, k, v, log_alpha, beta, h0, cu_seqlens, total_T, N, H, d_k, d_v, dtype,
+                        scale, o, hT, nullptr, 0, options, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+// kda_fwd_prefill_ex, or with use_scratch the allocation-free variant: every
+// host check first, then (only then) the device array's address
+int prefill_call(const void* q, const void* k, const void* v, const float* log_alpha,
+                 const float* beta, const float* h0, const int32_t* cu_seqlens, int64_t total_T,
+                 int32_t N, int32_t H, int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+                 void* o, float* hT, void* workspace, size_t workspace_bytes,
+                 const kda_prefill_options* options, void* stream, bool use_scratch) {
     const int32_t gate = options ? options->gate : KDA_GATE_CHANNEL;
     Sizes sz;
     const int st = check_sizes(total_T, N, H, d_k, d_v, dtype, gate, &sz);
@@ -285,10 +359,15 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
         if (p && !aligned16(p)) return KDA_STATUS_MISALIGNED;
     if (!aligned4(beta) || !aligned4(cu_seqlens)) return KDA_STATUS_MISALIGNED;
     Plan pl;
-    const int rs = resolve(total_T, N, H, d_k, d_v, dtype, options, &pl);
+    const int rs = resolve(total_T, N, H, d_k, d_v, dtype, options, &pl,
+                           use_scratch ? kNoAllocBytes : 0);
     if (rs != KDA_STATUS_OK) return rs;
     const size_t need = pl.ws_bytes;
-    if (workspace_bytes < need || (need > 0 && !workspace)) return KDA_STATUS_WORKSPACE_TOO_SMALL;
+    if (use_scratch) {
+        if (need > kNoAllocBytes) return KDA_STATUS_WORKSPACE_TOO_SMALL;   // beyond the array
+    } else if (workspace_bytes < need || (need > 0 && !workspace)) {
+        return KDA_STATUS_WORKSPACE_TOO_SMALL;
+    }
 
     // outputs may not overlap inputs (hT == h0 exactly is allowed)
     const Range r_o = range_of(o, sz.v_bytes);
@@ -357,6 +436,11 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     a.max_seqlen = options ? options->max_seqlen : 0;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (use_scratch) {
+        const int ss = scratch_of(s, &workspace);
+        if (ss != KDA_STATUS_OK) return ss;
+        a.order = static_cast<int32_t*>(workspace);
+    }
     hipError_t e = hipSuccess;
     switch (pl.path) {
         case KDA_PATH_VECTOR:
@@ -374,6 +458,9 @@ int kda_fwd_prefill_ex(const void* q, const void* k, const void* v, const float*
     }
     return e == hipSuccess ? KDA_STATUS_OK : KDA_STATUS_HIP_ERROR;
 }
+}  // namespace
+
+extern "C" {
 
 int kda_fwd_prefill(const void* q, const void* k, const void* v, const float* log_alpha,
                     const float* beta, const float* h0, const int32_t* cu_seqlens,

@@ -47,7 +47,9 @@
  * hipStream_t; NULL = the default stream) and returns.  The one call that
  * can use a second stream, kda_bwd, takes it from the caller
  * (kda_bwd_options.aux_stream) and orders the two with HIP events it
- * creates and releases within the call.  Faults inside those kernels surface at the caller's next
+ * creates and releases within the call.  The one exception to "no state":
+ * kda_fwd_prefill_noalloc, for callers that cannot allocate, works in a
+ * static device array the library keeps on each GPU (see there).  Faults inside those kernels surface at the caller's next
  * synchronisation.  Calls on different streams may run concurrently if
  * their output buffers do not overlap.
  *
@@ -378,6 +380,38 @@ int kda_fwd_prefill_ex(const void *q, const void *k, const void *v,
                        void *o, float *hT,
                        void *workspace, size_t workspace_bytes,
                        const kda_prefill_options *options, void *stream);
+
+/*
+ * The allocation-free prefill: kda_fwd_prefill_ex with no workspace
+ * argument, for callers that cannot allocate device memory -- code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Its workspace is a static device array of KDA_NOALLOC_SCRATCH_BYTES that
+ * the library holds on each GPU it runs on until the process ends (the HIP
+ * runtime places it when it loads the library's code on that GPU); its
+ * device address is looked up once per device, on the first call there.
+ * A call allocates nothing and never synchronises.
+ *
+ * Same arguments, results and requirements as kda_fwd_prefill_ex, except:
+ *   the two-pass path with options->block_chunks = 0 takes the largest
+ *     block length (up to its usual default) whose workspace fits the
+ *     array; results do not depend on the block length;
+ *   a call whose workspace does not fit the array (e.g. the two-pass path
+ *     with N * H * (55808 + 128 d_v) bytes of one block's slots above it)
+ *     [WORKSPACE_TOO_SMALL], before any HIP call;
+ *   the array's address could not be looked up [HIP_ERROR].
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (no call needs them cleared): calls that overlap on one GPU --
+ * on different streams, or from several host threads -- race on it and
+ * must be serialised by the caller.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)192 << 20)
+int kda_fwd_prefill_noalloc(const void *q, const void *k, const void *v,
+                            const float *log_alpha, const float *beta,
+                            const float *h0, const int32_t *cu_seqlens,
+                            int64_t total_T, int32_t N, int32_t H,
+                            int32_t d_k, int32_t d_v, int32_t dtype, float scale,
+                            void *o, float *hT,
+                            const kda_prefill_options *options, void *stream);
 
 /*
  * One decode step: one new token for each of N sequences.

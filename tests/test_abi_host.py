@@ -580,3 +580,21 @@ def test_backward_head_bound():
     assert kda.chunk_states_bytes(128, 1, 16385) == 0
     assert bwd_call(H=16385) == UNSUPPORTED
     assert bwd_call(H=70000) == UNSUPPORTED
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_array():
+    # the allocation-free prefill's workspace is a fixed device array: a
+    # two-pass call whose one-chunk block of slots exceeds it is refused on
+    # the host, before any HIP call (N * H * 72192 B > 192 MiB)
+    lib = kda.load_library()
+    opts = kda.PrefillOptions(3, 0, 0, 0)
+    args = [addr(0), addr(1), addr(2), addr(3), addr(4), None, addr(5), 4096, 4, 1024, 128, 128,
+            0, 0.1, addr(6), addr(7)]
+    assert lib.kda_fwd_prefill_noalloc(*args, ctypes.byref(opts), None) == WS_SMALL
+    # ordinary argument checks come first, as for kda_fwd_prefill_ex
+    bad = list(args)
+    bad[0] = None
+    assert lib.kda_fwd_prefill_noalloc(*bad, ctypes.byref(opts), None) == INVALID
+    bad = list(args)
+    bad[10] = 48
+    assert lib.kda_fwd_prefill_noalloc(*bad, ctypes.byref(opts), None) == UNSUPPORTED
