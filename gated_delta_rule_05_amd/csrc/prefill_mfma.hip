@@ -96,11 +96,17 @@ struct alignas(16) Smem {
     float gam[2][DK];                  // e^{G}
     uint16_t kn[C * KS];               // K * e^{-g} (producers only)
     float2 tot[2][4 * (DK / 2)];       // gate sums of the four 16-row blocks (log2 units)
-    int wild[2][NSTAGE];               // a stager's rows left the factored form's range
 };
 
-// |g| (log2 units) up to which e^{g} and e^{-g} stay inside fp32 (e^{80});
-// a chunk beyond it cannot be formed here and poisons its tile with NaN
+// |g| (log2 units) up to which e^{g} and e^{-g} stay inside fp32 (e^{80}).
+// Beyond it this path cannot form a chunk, and poisons it instead: each
+// channel out of range puts NaN into its row's Qg entry (one NaN channel
+// makes the row's output NaN), and e^{G} is NaN on every channel once any
+// channel's G is out of range (so the state, every later output and the
+// final state of the tile are NaN).  A row with every channel in range is
+// exact: gates <= 0 make |g| grow down the chunk, so its products only
+// involve rows in range, and such a chunk's G out of range is what any row
+// out of range implies.
 constexpr float kSafeLog2 = 115.f;
 
 // Byte-range views of one chunk of one head: row r of the chunk starts at
@@ -168,7 +174,7 @@ __device__ __forceinline__ float2 block_gate_sum(const StageRegs& rg) {
 // Qg, Kn, Kd^T (and e^{G} from stager 0).  `tot` holds the four blocks'
 // gate sums.  Rows past the end of the sequence hold zeros (they were read
 // out of range), so they add nothing to the gate and contribute zero rows.
-__device__ __forceinline__ bool stage_rows(Smem& sm, int b, const StageRegs& rg,
+__device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
                                            const float2* tot, int w, int lane) {
     float run0 = 0.f, run1 = 0.f, G0 = 0.f, G1 = 0.f;
 #pragma unroll
@@ -179,22 +185,27 @@ __device__ __forceinline__ bool stage_rows(Smem& sm, int b, const StageRegs& rg,
         G1 += t.y;
     }
     const float gl0 = __builtin_amdgcn_exp2f(G0), gl1 = __builtin_amdgcn_exp2f(G1);
-    if (w == 0) *reinterpret_cast<float2*>(sm.gam[b] + 2 * lane) = make_float2(gl0, gl1);
-    bool wild = !(fabsf(G0) <= kSafeLog2 && fabsf(G1) <= kSafeLog2);
+    const float nan = __builtin_nanf("");
+    if (w == 0) {
+        const bool wild = __ballot(!(fabsf(G0) <= kSafeLog2 && fabsf(G1) <= kSafeLog2)) != 0ull;
+        *reinterpret_cast<float2*>(sm.gam[b] + 2 * lane) =
+            wild ? make_float2(nan, nan) : make_float2(gl0, gl1);
+    }
     float kd0[4], kd1[4];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int row = 16 * w + r;
         run0 = __builtin_fmaf(__uint_as_float(rg.la[r][0]), kLog2e, run0);   // g_row / ln 2
         run1 = __builtin_fmaf(__uint_as_float(rg.la[r][1]), kLog2e, run1);
-        wild |= !(fabsf(run0) <= kSafeLog2 && fabsf(run1) <= kSafeLog2);
+        const bool wild = !(fabsf(run0) <= kSafeLog2 && fabsf(run1) <= kSafeLog2);
         const float u0 = __builtin_amdgcn_exp2f(run0), u1 = __builtin_amdgcn_exp2f(run1);
         const float w0 = __builtin_amdgcn_exp2f(-run0), w1 = __builtin_amdgcn_exp2f(-run1);
         const float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
         const float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
         const float n0 = kx * w0, n1 = ky * w1;
         *reinterpret_cast<uint32_t*>(sm.kg[b] + row * KS + 2 * lane) = pk(kx * u0, ky * u1);
-        *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) = pk(qx * u0, qy * u1);
+        *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) =
+            wild ? pk(nan, nan) : pk(qx * u0, qy * u1);
         *reinterpret_cast<uint32_t*>(sm.kn + row * KS + 2 * lane) = pk(n0, n1);
         kd0[r & 3] = n0 * gl0;
         kd1[r & 3] = n1 * gl1;
@@ -206,7 +217,6 @@ __device__ __forceinline__ bool stage_rows(Smem& sm, int b, const StageRegs& rg,
                 u32x2{pk(kd1[0], kd1[1]), pk(kd1[2], kd1[3])};
         }
     }
-    return wild;
 }
 
 // 16x16 product of two 16-row bf16 blocks: D[m][n] = sum_c X[m][c] Y[n][c]
@@ -341,8 +351,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         auto stage = [&](int m) {
             if (!stager) return;
             const int b = m & 1;
-            const bool wild = stage_rows(sm, b, rg, sm.tot[b], pw, lane);
-            if (lane == 0) sm.wild[b][pw] = __ballot(wild) != 0ull;
+            stage_rows(sm, b, rg, sm.tot[b], pw, lane);
             if (pw == 0) sm.beta[b][lane] = __uint_as_float(beta_next);
         };
         // A/P tile jobs, balanced greedily over the producers (weights: a
@@ -475,10 +484,6 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         __syncthreads();
 
         // ---------------- phase 2: O and the state update ----------------
-        // a chunk out of the factored form's range: its outputs and the
-        // state from here on are NaN (the two-pass path handles any gate)
-        const bool wild = (sm.wild[b][0] | sm.wild[b][1] | sm.wild[b][2] | sm.wild[b][3]) != 0;
-        const float nan = __builtin_nanf("");
         const __amdgpu_buffer_rsrc_t ro = rsrc(o + (chunk_start(ci) * H + h) * DV + j0,
                                                2u * static_cast<uint32_t>((len - 1) * vrow + TV));
         const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
@@ -499,7 +504,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             if (I >= 2) acc = mma32(fr[5], e23, acc);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(wild ? nan : scale * acc[i]));
+                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * acc[i]));
         }
         // S = Diag(e^{G}) S0 + Kd^T E
 #pragma unroll
@@ -508,7 +513,6 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             const u32x4 f0 = perm_row(krow, 0, g), f1 = perm_row(krow, 1, g);
             const f32x4 gm = *reinterpret_cast<const f32x4*>(sm.gam[b] + 16 * m + 4 * g);
             S[m] = mma32(f1, e23, mma32(f0, e01, gm * S[m]));
-            if (wild) S[m] = f32x4{nan, nan, nan, nan};
         }
         // a snapshot after every snap_tokens / C chunks (a countdown: one
         // decrement per chunk on the serial path)
