@@ -45,6 +45,7 @@
 #include <algorithm>
 
 #include "kda_device.h"
+#include "kda_exact.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
 
@@ -337,7 +338,8 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     chunk_gates<GATE>(la, beta, c, H, sm.u2.a.scan, sm.u2.a.tot, sm.bs, g, G);
     if (tid < D) oGam[tid] = gate_exp(sm.u2.a.tot[tid]);
     {
-        // the factored form's range: a chunk beyond it is flagged below
+        // the factored form's range: a chunk beyond it takes the exact form
+        // for B and P below (Kg, Qg, Kd and gamma are in range either way)
         bool wild = false;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -371,21 +373,79 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
         put4t(oQg + r * D + c0, scale * vqg);
     }
     __syncthreads();
-    // B = Kg Kn^T (fp32) and scale P^T, P = lower(Qg Kn^T)
-    mm<4, 4, D, GT>(sm.kg, LDD, sm.u1.a.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+    if (!sm.wild) {
+        // B = Kg Kn^T (fp32) and scale P^T, P = lower(Qg Kn^T)
+        mm<4, 4, D, GT>(sm.kg, LDD, sm.u1.a.kn, LDD, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
-            sm.u2.bm[r * (C + 1) + s] = acc[i];
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i, s = 16 * ni + ln;
+                sm.u2.bm[r * (C + 1) + s] = acc[i];
+            }
+        });
+        mm<4, 4, D, GT>(sm.u1.a.qg, LDD, sm.u1.a.kn, LDD, [&](int mi, int ni, f32x4 acc) {
+            const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
+            f32x4 x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = s <= r0 + i ? scale * acc[i] : 0.f;
+            put4t(oPt + s * C + r0, x);
+        });
+    } else {
+        // The chunk's gates leave the factored form's range (K e^-g
+        // overflows): B and P entry by entry, each with its own factor
+        // e^{g_r - g_s} <= 1 (kda_exact.h), from the raw k, q and gates
+        // staged 32 channels at a time in the dead K e^-g / Q e^g rows.
+        static_assert(GT == kExactThreads, "one exact unit per thread");
+        static_assert(3 * C * kExactXS * sizeof(float) <= sizeof(sm.u1.a) &&
+                          C * (C + 1) * sizeof(float) <= sizeof(sm.u1.a),
+                      "the staged rows and P fit the dead rows");
+        float* sk = reinterpret_cast<float*>(&sm.u1.a);
+        float* sq = sk + C * kExactXS;
+        float* sg = sq + C * kExactXS;
+        const ExactUnit u = exact_unit(tid);
+        float a[4][2], pp[4][2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) a[x][y] = pp[x][y] = 0.f;
+#pragma unroll 1
+        for (int round = 0; round < 4; ++round) {
+            if (round > 0) __syncthreads();
+            if ((cg >> 3) == round) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float kk[4] = {kr4[i].x, kr4[i].y, kr4[i].z, kr4[i].w};
+                    const float qq[4] = {qr4[i].x, qr4[i].y, qr4[i].z, qr4[i].w};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int e = (4 * rg + i) * kExactXS + 4 * (cg & 7) + j;
+                        sk[e] = kk[j];
+                        sq[e] = qq[j];
+                        sg[e] = g[i][j];
+                    }
+                }
+            }
+            __syncthreads();
+            exact_accumulate(u, sk, sq, sg, kLog2e, a, pp);
         }
-    });
-    mm<4, 4, D, GT>(sm.u1.a.qg, LDD, sm.u1.a.kn, LDD, [&](int mi, int ni, f32x4 acc) {
-        const int r0 = 16 * mi + 4 * g4, s = 16 * ni + ln;
-        f32x4 x;
+        exact_reduce(u, a, pp);
+        __syncthreads();                       // the staged rows are dead
+        float* ptab = sk;                      // P, [C][C + 1]
+        if (exact_writer(u, tid)) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) x[i] = s <= r0 + i ? scale * acc[i] : 0.f;
-        put4t(oPt + s * C + r0, x);
-    });
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int r = 4 * u.bi + x, s = 2 * u.bj + y;
+                    if (s < r) sm.u2.bm[r * (C + 1) + s] = a[x][y];
+                    if (s <= r) ptab[r * (C + 1) + s] = pp[x][y];
+                }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += GT) {
+            const int s = idx / C, r = idx % C;
+            oPt[s * C + r] = bf(s <= r ? scale * ptab[r * (C + 1) + s] : 0.f);
+        }
+    }
     __syncthreads();
     // Minv = (I + A)^-1, A = strict_lower(Diag(beta) B), blockwise in 16x16
     // blocks.  The diagonal blocks (unit lower triangular) by forward
@@ -449,17 +509,6 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     mm<4, 8, C, GT, kKc, kMc>(sm.u1.b.tt, LDC, sm.kg, LDD, [&](int mi, int ni, f32x4 acc) {
         put4t(oWt + (16 * ni + ln) * C + 16 * mi + 4 * g4, -acc);
     });
-    // A chunk whose decays leave the factored form's range (e^{-g} would
-    // overflow) cannot be differentiated here: its whole operand record
-    // becomes NaN, so every gradient that depends on it -- this chunk's and,
-    // through the state adjoint, every earlier chunk's of the sequence and
-    // head, and dh0 -- comes out NaN instead of silently wrong.
-    if (sm.wild) {
-        __syncthreads();
-        // 0x7fc0 is a bf16 NaN, and the pair 0x7fc07fc0 an fp32 NaN
-        const u32x4 nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
-        for (int x = tid; x < kSlot / 16; x += GT) reinterpret_cast<u32x4*>(out)[x] = nan4;
-    }
 }
 
 // ===================================================================
@@ -722,9 +771,11 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 {
     __shared__ GradLds sm_u;
     __shared__ float s_dgam[D], s_dbT[4][C];   // phase A -> phase B
+    __shared__ int s_wild;                     // the chunk takes the exact form
     ChunkRef c;
     if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
+    if (tid == 0) s_wild = 0;
     const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
     const float* mvg = reinterpret_cast<const float*>(sp + kOffMinv);
     const float* S0f = c.j == 0 && h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState
@@ -882,6 +933,16 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         float gr[4][4];
         f32x4 Gr;
         scan_gate_block(graw, bsv, sm.gscan, sm.gtot, sm.bs, gr, Gr);
+        if (tid < GT) {
+            bool wild = false;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                wild |= !(fabsf(Gr[j]) <= kSafeGate);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) wild |= !(fabsf(gr[i][j]) <= kSafeGate);
+            }
+            if (wild) s_wild = 1;
+        }
         // the gates for the final tiles, and the gated keys and queries
         // (one thread per 4 x 4 block of the chunk)
         if (tid < GT) {
@@ -932,10 +993,44 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     }
     if (tid < C) sm.db[tid] = (s_dbT[0][tid] + s_dbT[1][tid]) + (s_dbT[2][tid] + s_dbT[3][tid]);
     __syncthreads();
+    // A chunk whose gates leave the factored form's range takes the exact
+    // form (kda_exact.h): its B and the products with dB and dP are summed
+    // pair by pair with factors e^{g_r - g_s} <= 1, from the raw k and q,
+    // which replace the gated copies in LDS
+    const bool exact = s_wild != 0;
+    if (exact) {
+        if (tid < GT) {
+            const int rg = tid >> 5, c0 = 4 * (tid & 31);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rg + i;
+                put4t(sm.kn + r * LDT + c0, f32x4{lo_bf(kraw[i][0]), hi_bf(kraw[i][0]),
+                                                  lo_bf(kraw[i][1]), hi_bf(kraw[i][1])});
+                put4t(sm.qg + r * LDT + c0, f32x4{lo_bf(qraw[i][0]), hi_bf(qraw[i][0]),
+                                                  lo_bf(qraw[i][1]), hi_bf(qraw[i][1])});
+            }
+        }
+        __syncthreads();
+    }
     // B = Kg Kn^T at this wave's dA tile (for dbeta_A; the prep's inverse
-    // used the same bf16 operands and product order)
+    // used the same bf16 operands and product order, or the same exact form)
     f32x4 bmt[1];
-    mm_regs<4, D, 1, GG>(sm.kg, LDT, sm.kn, LDT, bmt);
+    if (!exact) {
+        mm_regs<4, D, 1, GG>(sm.kg, LDT, sm.kn, LDT, bmt);
+    } else {
+        const int mi = wave / 4, s = 16 * (wave % 4) + ln;
+        bmt[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+        for (int c2 = 0; c2 < D; ++c2) {
+            const float ks = bf16_to_f32(sm.kn[s * LDT + c2]), gs = sm.g[s * D + c2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i;
+                const float e = __builtin_amdgcn_exp2f((sm.g[r * D + c2] - gs) * kLog2e);
+                bmt[0][i] += s < r ? bf16_to_f32(sm.kn[r * LDT + c2]) * ks * e : 0.f;
+            }
+        }
+    }
     // Z = Minv^T (dT Diag(beta))  (Minv read by rows of K)
     mm<4, 4, C, GG, kMc, kKc>(sm.mv, LDC, sm.yt, LDC, [&](int mi, int ni, f32x4 acc) {
 #pragma unroll
@@ -977,49 +1072,121 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain;
     // the B fragments of Kn, Kg and Qg (read by rows of K) serve both of
     // the wave's tiles
-    u32x4 fkn[2], fkg[2], fqg[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-        fkn[s2] = frag<kMc>(sm.kn + 16 * cb, LDT, 32 * s2, lane);
-        fkg[s2] = frag<kMc>(sm.kg + 16 * cb, LDT, 32 * s2, lane);
-        fqg[s2] = frag<kMc>(sm.qg + 16 * cb, LDT, 32 * s2, lane);
-    }
     const float G = sm.g[(c.len - 1) * D + ch];
-    // every wave holds its fragments of the gated keys and queries: their
-    // buffers take dk and dq, which leave in whole 16-byte pieces of rows
-    __syncthreads();
     float dgr[2][4];          // dg of rows 16 mi + 4 g4 + i, this lane's channel
     float dGp = 0.f;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        const int mi = wave / 8 + 2 * x;
-        f32x4 aKg = {0.f, 0.f, 0.f, 0.f}, aKn = aKg, aQg = aKg;
+    if (!exact) {
+        u32x4 fkn[2], fkg[2], fqg[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-            aKg = mma32(frag<kKc>(dB + 16 * mi * LDC, LDC, 32 * s2, lane), fkn[s2], aKg);
-            aKn = mma32(frag<kMc>(dB + 16 * mi, LDC, 32 * s2, lane), fkg[s2], aKn);
-            aKn = mma32(frag<kMc>(sm.dp + 16 * mi, LDC, 32 * s2, lane), fqg[s2], aKn);
-            aQg = mma32(frag<kKc>(sm.dp + 16 * mi * LDC, LDC, 32 * s2, lane), fkn[s2], aQg);
+            fkn[s2] = frag<kMc>(sm.kn + 16 * cb, LDT, 32 * s2, lane);
+            fkg[s2] = frag<kMc>(sm.kg + 16 * cb, LDT, 32 * s2, lane);
+            fqg[s2] = frag<kMc>(sm.qg + 16 * cb, LDT, 32 * s2, lane);
         }
+        // every wave holds its fragments of the gated keys and queries:
+        // their buffers take dk and dq, which leave in whole 16-byte pieces
+        // of rows
+        __syncthreads();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mi + 4 * g4 + i;
-            float dgv = 0.f;
-            if (r < c.len) {
-                const float gv = sm.g[r * D + ch];
-                const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
-                const float dKg = aKg[i] + rKgW[x][i];
-                const float dQg = aQg[i] + rQgS[x][i];
-                const float dKn = aKn[i];
-                const float dKd = rKd[x][i];
-                const float Kg = kv[x][i] * eg, Kn = kv[x][i] * en, Qg = qv[x][i] * eg;
-                const float Kd = kv[x][i] * ed;
-                sm.kg[r * LDT + ch] = bf(dKg * eg + dKn * en + dKd * ed);   // dk
-                sm.kn[r * LDT + ch] = bf(dQg * eg);                         // dq
-                dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
-                dGp += dKd * Kd;
+        for (int x = 0; x < 2; ++x) {
+            const int mi = wave / 8 + 2 * x;
+            f32x4 aKg = {0.f, 0.f, 0.f, 0.f}, aKn = aKg, aQg = aKg;
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                aKg = mma32(frag<kKc>(dB + 16 * mi * LDC, LDC, 32 * s2, lane), fkn[s2], aKg);
+                aKn = mma32(frag<kMc>(dB + 16 * mi, LDC, 32 * s2, lane), fkg[s2], aKn);
+                aKn = mma32(frag<kMc>(sm.dp + 16 * mi, LDC, 32 * s2, lane), fqg[s2], aKn);
+                aQg = mma32(frag<kKc>(sm.dp + 16 * mi * LDC, LDC, 32 * s2, lane), fkn[s2], aQg);
             }
-            dgr[x][i] = dgv;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i;
+                float dgv = 0.f;
+                if (r < c.len) {
+                    const float gv = sm.g[r * D + ch];
+                    const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
+                    const float dKg = aKg[i] + rKgW[x][i];
+                    const float dQg = aQg[i] + rQgS[x][i];
+                    const float dKn = aKn[i];
+                    const float dKd = rKd[x][i];
+                    const float Kg = kv[x][i] * eg, Kn = kv[x][i] * en, Qg = qv[x][i] * eg;
+                    const float Kd = kv[x][i] * ed;
+                    sm.kg[r * LDT + ch] = bf(dKg * eg + dKn * en + dKd * ed);   // dk
+                    sm.kn[r * LDT + ch] = bf(dQg * eg);                         // dq
+                    dgv = dKg * Kg - dKn * Kn + dQg * Qg - dKd * Kd;
+                    dGp += dKd * Kd;
+                }
+                dgr[x][i] = dgv;
+            }
+        }
+    } else {
+        // per row r and this lane's channel c, with E(r, s) = e^{g_r[c] - g_s[c]}:
+        //   FK = sum_{s<r} dB[r][s] k_s E(r, s)     (= (dB Kn)[r] e^{g_r})
+        //   FQ = sum_{s<=r} dP[r][s] k_s E(r, s)    (= (dP Kn)[r] e^{g_r})
+        //   GS = sum_{r'>r} dB[r'][r] k_r' E(r', r) + sum_{r'>=r} dP[r'][r] q_r' E(r', r)
+        //                                           (= (dB^T Kg + dP^T Qg)[r] e^{-g_r})
+        // then the chain of the common path with those in place of its
+        // products: dk = FK + GS + ..., dq = FQ + ..., dg = FK k + FQ q - GS k + ...
+        // dk and dq of each row wait in registers (bf16 pairs) until every
+        // wave has read the raw keys and queries
+        uint32_t dkq[2][4];
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int mi = wave / 8 + 2 * x;
+            float gr4[4], fk[4], fq[4], gsum[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                gr4[i] = sm.g[(16 * mi + 4 * g4 + i) * D + ch];
+                fk[i] = fq[i] = gsum[i] = 0.f;
+            }
+#pragma unroll 2
+            for (int s2 = 0; s2 < C; ++s2) {
+                const float ks = bf16_to_f32(sm.kn[s2 * LDT + ch]), qs = bf16_to_f32(sm.qg[s2 * LDT + ch]);
+                const float gs = sm.g[s2 * D + ch];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * mi + 4 * g4 + i;
+                    // s2 as the column of row r, or as the row over row r
+                    const float d = (gr4[i] - gs) * kLog2e;
+                    const float e = __builtin_amdgcn_exp2f(s2 <= r ? d : -d);
+                    if (s2 < r) fk[i] += bf16_to_f32(dB[r * LDC + s2]) * ks * e;
+                    if (s2 <= r) fq[i] += bf16_to_f32(sm.dp[r * LDC + s2]) * ks * e;
+                    if (s2 > r) gsum[i] += bf16_to_f32(dB[s2 * LDC + r]) * ks * e;
+                    if (s2 >= r) gsum[i] += bf16_to_f32(sm.dp[s2 * LDC + r]) * qs * e;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i;
+                float dgv = 0.f;
+                dkq[x][i] = 0u;
+                if (r < c.len) {
+                    const float eg = gate_exp(gr4[i]), ed = gate_exp(G - gr4[i]);
+                    const float dKd = rKd[x][i];
+                    const float kx = kv[x][i], qx = qv[x][i];
+                    const float dkv = fk[i] + gsum[i] + rKgW[x][i] * eg + dKd * ed;
+                    const float dqv = fq[i] + rQgS[x][i] * eg;
+                    dkq[x][i] = uint32_t(bf(dkv)) | (uint32_t(bf(dqv)) << 16);
+                    dgv = (fk[i] - gsum[i]) * kx + fq[i] * qx + rKgW[x][i] * kx * eg +
+                          rQgS[x][i] * qx * eg - dKd * kx * ed;
+                    dGp += dKd * kx * ed;
+                }
+                dgr[x][i] = dgv;
+            }
+        }
+        // every wave has read the raw keys and queries: their buffers take dk and dq
+        __syncthreads();
+#pragma unroll
+        for (int x = 0; x < 2; ++x) {
+            const int mi = wave / 8 + 2 * x;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 16 * mi + 4 * g4 + i;
+                if (r < c.len) {
+                    sm.kg[r * LDT + ch] = uint16_t(dkq[x][i] & 0xffffu);   // dk
+                    sm.kn[r * LDT + ch] = uint16_t(dkq[x][i] >> 16);       // dq
+                }
+            }
         }
     }
     __syncthreads();

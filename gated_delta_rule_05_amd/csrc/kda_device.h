@@ -82,7 +82,8 @@ __device__ __forceinline__ float sigmoid_f32(float x) {
 
 // exp(x) through the hardware base-2 exponential.  Relative error is a few
 // ulp plus |x| * 2^-24 from scaling x by log2(e); |x| stays below ~90 on
-// every path that calls it.
+// every factored path that calls it; in a chunk beyond that range only its
+// values for x <= 0 are used (they underflow to 0 as e^x does).
 __device__ __forceinline__ float gate_exp(float x) {
     return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }

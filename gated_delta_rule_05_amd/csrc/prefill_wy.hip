@@ -40,6 +40,7 @@
 #include <type_traits>
 
 #include "kda_device.h"
+#include "kda_exact.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_sched.h"
@@ -140,7 +141,7 @@ __device__ __forceinline__ f32x4 row_product(const uint16_t* x, const uint16_t* 
 // on the vector units, into fp32 tables that the tile jobs read in place of
 // their matrix-core products.  Any per-token gate is then in range.
 constexpr float kSafeLog2 = 115.f;
-constexpr int XS = 33;          // fp32 stride of the staged 32-channel rows
+constexpr int XS = kExactXS;    // fp32 stride of the staged 32-channel rows
 constexpr int AS = C + 1;       // fp32 stride of the 64 x 64 tables
 
 __device__ __forceinline__ float* table_a(PrepSmem& sm) { return reinterpret_cast<float*>(sm.tok[1]); }
@@ -148,11 +149,8 @@ __device__ __forceinline__ float* table_p(PrepSmem& sm) { return reinterpret_cas
 static_assert(2 * C * AS * sizeof(float) <= 2 * C * TS * sizeof(uint16_t), "the tables fit in tok[1..2]");
 static_assert(3 * C * XS * sizeof(float) <= 2 * C * TS * sizeof(uint16_t), "a staged round fits in tok[1..2]");
 
-// Work split over the 512 threads: the 240 blocks of 4 rows x 2 columns
-// strictly below the diagonal 4x4 blocks, two threads each (16 of every 32
-// staged channels apiece), and the 32 blocks of 4 x 2 that make up the
-// diagonal 4x4 blocks, one thread each.  Per round of 32 channels the
-// threads that own them (cg / 8 == round) reload their 4 rows x 4 channels
+// The work split is kda_exact.h's.  Per round of 32 channels the threads
+// that own them (cg / 8 == round) reload their 4 rows x 4 channels
 // of k and q (normalised by nk, nq when the front-end asks) and their gates
 // from L2, stage k, q and the cumulative gates (log2 units: off plus the
 // sum within the thread's 4 rows) as rows of XS floats, and rewrite their
@@ -175,23 +173,7 @@ void exact_ap_tables(PrepSmem& sm, const bf16_t* __restrict__ q, const bf16_t* _
     float* sk = reinterpret_cast<float*>(sm.tok[1]);
     float* sq = sk + C * XS;
     float* sg = sq + C * XS;
-    const bool diag = tid >= 480;
-    int bi, bj, cw, c0w;                 // rows 4bi .. +3, columns 2bj .. +1
-    if (!diag) {
-        const int u = tid >> 1;          // row block bi holds 2 bi column pairs
-        bi = static_cast<int>((1.f + __builtin_sqrtf(1.f + 4.f * static_cast<float>(u))) * 0.5f);
-        while (bi * (bi - 1) > u) --bi;
-        while ((bi + 1) * bi <= u) ++bi;
-        bj = u - bi * (bi - 1);
-        cw = 16;
-        c0w = 16 * (tid & 1);
-    } else {
-        const int d = tid - 480;
-        bi = d >> 1;
-        bj = 2 * bi + (d & 1);
-        cw = 32;
-        c0w = 0;
-    }
+    const ExactUnit u = exact_unit(tid);
     float a[4][2], pp[4][2];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
@@ -265,52 +247,19 @@ void exact_ap_tables(PrepSmem& sm, const bf16_t* __restrict__ q, const bf16_t* _
             }
         }
         __syncthreads();
-#pragma unroll 1
-        for (int cc = 0; cc < cw; ++cc) {
-            const int c = c0w + cc;
-            float kr[4], qr[4], gr[4], ks[2], gs[2];
-#pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                kr[x] = sk[(4 * bi + x) * XS + c];
-                qr[x] = sq[(4 * bi + x) * XS + c];
-                gr[x] = sg[(4 * bi + x) * XS + c];
-            }
-#pragma unroll
-            for (int y = 0; y < 2; ++y) {
-                ks[y] = sk[(2 * bj + y) * XS + c];
-                gs[y] = sg[(2 * bj + y) * XS + c];
-            }
-#pragma unroll
-            for (int x = 0; x < 4; ++x)
-#pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    if (2 * bj + y > 4 * bi + x) continue;   // above the diagonal
-                    const float w = ks[y] * __builtin_amdgcn_exp2f(gr[x] - gs[y]);
-                    a[x][y] = __builtin_fmaf(kr[x], w, a[x][y]);
-                    pp[x][y] = __builtin_fmaf(qr[x], w, pp[x][y]);
-                }
-        }
+        exact_accumulate(u, sk, sq, sg, 1.f, a, pp);
     }
-    // the two channel halves of a block sit in adjacent lanes
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {
-            const float ta = a[x][y] + __shfl_xor(a[x][y], 1);
-            const float tp = pp[x][y] + __shfl_xor(pp[x][y], 1);
-            a[x][y] = diag ? a[x][y] : ta;
-            pp[x][y] = diag ? pp[x][y] : tp;
-        }
+    exact_reduce(u, a, pp);
     __syncthreads();                                    // the staged rows are dead
-    if (diag || (tid & 1) == 0) {
+    if (exact_writer(u, tid)) {
         float* ta = table_a(sm);
         float* tp = table_p(sm);
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
-                ta[(4 * bi + x) * AS + 2 * bj + y] = a[x][y];
-                tp[(4 * bi + x) * AS + 2 * bj + y] = pp[x][y];
+                ta[(4 * u.bi + x) * AS + 2 * u.bj + y] = a[x][y];
+                tp[(4 * u.bi + x) * AS + 2 * u.bj + y] = pp[x][y];
             }
     }
     __syncthreads();
@@ -404,7 +353,7 @@ __device__ __forceinline__ void t_column(PrepSmem& sm, int g, int ln) {
 // from bf16 pre-activations (log_alpha = -fe.gate_scale softplus(x)) when
 // fe.gate_pre, beta = sigmoid(y) from bf16 fe.beta_pre
 template <int GATE, bool FRONT>
-__global__ __launch_bounds__(PT, 5)
+__global__ __launch_bounds__(PT, 4)
 void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                             const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
                             const float* __restrict__ beta, const int32_t* __restrict__ cu,

@@ -519,11 +519,11 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * the workspace [INVALID_ARGUMENT]; workspace_bytes at least
  * kda_bwd_workspace_bytes [WORKSPACE_TOO_SMALL].
  * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
- * adjoints, as in the forward pass.  Gate range: a chunk whose cumulative
- * gate leaves the factored form's range (|g| > 80, see kda_fwd_prefill) is
- * not differentiated: its gradients, those of every earlier chunk of the
- * same (sequence, head) and that dh0 come out NaN -- never finite and
- * wrong.
+ * adjoints, as in the forward pass.  Gate range: the whole domain
+ * (log_alpha <= 0, any finite value).  A chunk whose cumulative gate leaves
+ * the factored form's range (|g| > 80, see kda_fwd_prefill) takes the exact
+ * pairwise form for its decay-weighted products, in the operand pass and in
+ * the gradient pass, at some cost in time for that chunk only.
  * Saved states (options->chunk_states): the record of the forward pass on
  * these inputs replaces its recomputation (the call then reads the record
  * and needs a smaller workspace); the record must come from a forward pass

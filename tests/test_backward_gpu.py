@@ -65,10 +65,12 @@ def ref(inp, heads=None):
                            cu_seqlens=cu)
 
 
-def compare(name, g, r, heads=None):
+def compare(name, g, r, heads=None, skip=()):
     sel = (lambda x: x) if heads is None else (lambda x: x[:, heads])
     errs = {}
     for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"):
+        if key in skip:
+            continue
         if r[key] is None:
             assert g[key] is None
             continue
@@ -84,38 +86,45 @@ def test_backward_parity(gate):
     compare("backward %s" % gate, gpu(inp, gate), ref(inp))
 
 
-@pytest.mark.parametrize("case", ["decay_1", "decay_3", "mixed_0_10"])
+@pytest.mark.parametrize("case", ["decay_1", "decay_3", "decay_10", "mixed_0_10", "uniform_12"])
 def test_backward_gate_domain(case):
-    """Gates up to the factored form's range (-1 per token: a chunk sums to
-    -64) match the oracle; beyond it (-3, or a mix of undecayed and -10
-    channels) the backward flags the chunks it cannot differentiate with
-    NaN: every gradient is either within the bar or NaN, never finite and
-    wrong."""
+    """The whole gate domain the pages allow (any alpha in (0, 1]): -1 per
+    token keeps a 64-token chunk inside the factored form's range (its gates
+    sum to -64); -3 and -10 per token, a mix of undecayed and -10 channels,
+    and gates uniform in [-12, 0] leave it, and those chunks take the exact
+    pairwise form.  Every gradient must match the oracle and be finite."""
     inp = make_case(LENS, 2, 390)
     la = inp["log_alpha"]
     if case == "decay_1":
         la.fill_(-1.0)
     elif case == "decay_3":
         la.fill_(-3.0)
-    else:
+    elif case == "decay_10":
+        la.fill_(-10.0)
+    elif case == "mixed_0_10":
         la[..., 0::2] = 0.0
         la[..., 1::2] = -10.0
-    g = gpu(inp, "channel")
-    r = ref(inp)
-    errs, finite = {}, {}
-    for key in ("dq", "dk", "dv", "dlog_alpha", "dbeta", "dh0"):
-        x = host(g[key])
-        f = np.isfinite(x)
-        finite[key] = float(f.mean())
-        scale_ = max(float(np.max(np.abs(r[key]))), 1e-30)
-        errs[key] = float(np.max(np.abs(x[f] - r[key][f]), initial=0.0)) / scale_
-    report("backward gates %s (finite fraction %s)" % (case, finite), **errs)
-    for key, e in errs.items():
-        assert e <= TOL, (key, e)
-    if case == "decay_1":
-        assert all(v == 1.0 for v in finite.values()), finite
     else:
-        assert finite["dq"] < 1.0                   # the flag fired
+        g = torch.Generator(device="cpu").manual_seed(391)
+        la.copy_(-12.0 * torch.rand(la.shape, generator=g))
+    g = gpu(inp, "channel")
+    for key, x in g.items():
+        assert x is None or torch.isfinite(x).all(), key
+    r = ref(inp)
+    compare("backward gates %s" % case, g, r, skip=("dlog_alpha",))
+    # dlog_alpha is a difference of products of the gradients of q and k
+    # with q and k (the terms the gate's factors e^{+-g} multiply); under
+    # strong decay the difference is many times smaller than its terms, and
+    # the bf16 rounding of those terms bounds its error: measure it against
+    # the larger of its own magnitude and theirs
+    terms = max(float(np.max(np.abs(r["dq"] * host(inp["q"])))),
+                float(np.max(np.abs(r["dk"] * host(inp["k"])))))
+    dla, dla_ref = host(g["dlog_alpha"]), r["dlog_alpha"]
+    err = float(np.max(np.abs(dla - dla_ref)))
+    scale_ = max(float(np.max(np.abs(dla_ref))), terms)
+    report("backward gates %s dlog_alpha (max |ref| %.3e, max |q dq|, |k dk| %.3e)"
+           % (case, float(np.max(np.abs(dla_ref))), terms), dlog_alpha=err / scale_)
+    assert err / scale_ <= TOL
 
 
 def test_backward_zero_state_and_adjoint():
