@@ -56,8 +56,18 @@ step of 256 x 32 states, the backward of the 512-chunk prefill, and a 512
 MiB device copy whose counter readings calibrate the rest -- under
 ``rocprofv3 --pmc <counter> -- python3 bench.py --counters``.
 
+digest: ``python bench.py --digest DIR`` reads the rocprofv3 output of
+those runs (DIR/ks: --kernel-trace; DIR/pmc_<counter>: one --pmc counter
+each, FETCH_SIZE, WRITE_SIZE, MfmaUtil), splits the dispatches into the
+workloads above (each is a run of this library's kernels between the torch
+kernels that generate the next inputs), scales FETCH_SIZE and WRITE_SIZE by
+the copy's readings, and writes profiles/traffic.json (with a digest of the
+kernel sources: the bench reports the figures only while it matches) and a
+markdown summary; with DIR/bench_ks (a --kernel-trace --stats run of the
+bench itself) also the bench's kernel statistics.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                       [--only-backward] [--counters]
+                       [--only-backward] [--counters] [--digest DIR]
 """
 import argparse
 import hashlib
@@ -88,6 +98,8 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=1048576)
     ap.add_argument("--only-backward", action="store_true",
                     help="time only the prefill gradients (for profiling)")
+    ap.add_argument("--digest", default=None,
+                    help="summarise the rocprofv3 output of the --counters runs in this folder")
     ap.add_argument("--counters", action="store_true",
                     help="run the launches the rocprofv3 counter summaries cover, once each")
     ap.add_argument("--chunks", type=int, default=512,
@@ -146,28 +158,241 @@ def run_counter_workloads(torch, kda, gen, chunks):
     print("counters done", flush=True)
 
 
-def source_digest(names):
+KDA_KERNELS = ("prefill_wy_prep_kernel", "prefill_wy_carry_kernel", "prefill_mfma_kernel",
+               "prefill_valu_kernel", "plan_order_kernel", "decode_step_kernel",
+               "decode_multi_kernel", "bwd_init_kernel", "bwd_prep_kernel", "bwd_carry_kernel",
+               "bwd_grad_kernel", "front_act_kernel", "front_chain_kernel")
+# the --counters workloads in launch order, and the factor from what each
+# measures to the figure reported (the long-context runs cover 512 of the
+# 16,384 chunks of the 1M-token call)
+COUNTER_WORKLOADS = (("long_t1m_prefill", 16384 / 512.0), ("batch4_t4096", 1.0),
+                     ("varlen_n64", 1.0), ("decode_n256_step", 1.0),
+                     ("long_t1m_backward", 16384 / 512.0))
+COPY_BYTES = 512 << 20
+
+
+def kernel_short(name):
+    """'prefill_wy_prep_kernel<0, false>' from a full kernel name, or None
+    for a kernel that is not this library's."""
+    for k in KDA_KERNELS:
+        i = name.find(k)
+        if i >= 0:
+            j = name.find("(", i)
+            return name[i:j if j > 0 else len(name)]
+    return None
+
+
+def source_digest():
+    """Digest of every kernel and host source of the library."""
     h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "gated_delta_rule_05_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+    src = os.path.join(ROOT, "gated_delta_rule_05_amd", "csrc")
+    for n in sorted(os.listdir(src)):
+        if n.endswith((".hip", ".h", ".cpp")):
+            h.update(n.encode())
+            with open(os.path.join(src, n), "rb") as f:
+                h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def load_counters(kernel_file, digest, key="bytes_per_launch"):
-    """A figure from the committed rocprofv3 counter summary
-    (profiles/traffic.json), if it was taken on the current kernel source;
-    else None.  bytes_per_launch: HBM traffic (bytes read + written beyond
-    L2, FETCH_SIZE and WRITE_SIZE scaled by a device copy's readings);
-    mfma: MfmaUtil (busy %) and MfmaFlopsBF16 per kernel."""
+def load_counters():
+    """The per-workload figures of the committed rocprofv3 counter summary
+    (profiles/traffic.json) if it was taken on the current sources, else
+    None."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
-        rec = json.load(f).get(kernel_file)
-    if not rec or rec.get("source_digest") != digest:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
         return None
-    return rec.get(key)
+    return rec.get("workloads")
+
+
+def _dispatches(path, value_col=None):
+    """[(dispatch id, full kernel name, value or (start, end))] in dispatch
+    order from a rocprofv3 csv."""
+    import csv
+    out = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            did = int(r["Dispatch_Id"])
+            v = (float(r[value_col]) if value_col else
+                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+            out.append((did, r["Kernel_Name"], v))
+    out.sort(key=lambda x: x[0])
+    return out
+
+
+def _split_workloads(disp):
+    """Runs of this library's dispatches, in order; returns a list of lists
+    of (short name, value)."""
+    runs, cur = [], []
+    for _, name, v in disp:
+        s = kernel_short(name)
+        if s is None:
+            if cur:
+                runs.append(cur)
+                cur = []
+        else:
+            cur.append((s, v))
+    if cur:
+        runs.append(cur)
+    return runs
+
+
+def digest_counters(folder):
+    import glob
+
+    def one(pattern):
+        hits = sorted(glob.glob(os.path.join(folder, pattern), recursive=True))
+        if not hits:
+            sys.exit("no %s under %s" % (pattern, folder))
+        return hits[0]
+
+    trace = _dispatches(one("ks/**/*kernel_trace.csv"))
+    pmc = {c: _dispatches(one("pmc_%s/**/*counter_collection.csv" % c), "Counter_Value")
+           for c in ("FETCH_SIZE", "WRITE_SIZE", "MfmaUtil")}
+    copies = [v for _, n, v in pmc["FETCH_SIZE"] if "copyBuffer" in n]
+    wcopies = [v for _, n, v in pmc["WRITE_SIZE"] if "copyBuffer" in n]
+    fetch_factor = COPY_BYTES / 1024.0 / copies[-1]
+    write_factor = COPY_BYTES / 1024.0 / wcopies[-1]
+    runs = {key: _split_workloads(d) for key, d in
+            (("time", trace), ("fetch", pmc["FETCH_SIZE"]), ("write", pmc["WRITE_SIZE"]),
+             ("mfma", pmc["MfmaUtil"]))}
+    for key, r in runs.items():
+        if len(r) != len(COUNTER_WORKLOADS):
+            sys.exit("%s: %d runs of library kernels, expected %d" %
+                     (key, len(r), len(COUNTER_WORKLOADS)))
+    workloads = {}
+    for i, (wname, scale) in enumerate(COUNTER_WORKLOADS):
+        kern = {}
+        for key in ("time", "fetch", "write", "mfma"):
+            for s, v in runs[key][i]:
+                k = kern.setdefault(s, {"dispatches": 0, "us": 0.0, "read_bytes": 0.0,
+                                        "written_bytes": 0.0, "mfma_sum": 0.0, "n_mfma": 0})
+                if key == "time":
+                    k["dispatches"] += 1
+                    k["us"] += (v[1] - v[0]) * 1e-3
+                elif key == "fetch":
+                    k["read_bytes"] += v * 1024.0 * fetch_factor
+                elif key == "write":
+                    k["written_bytes"] += v * 1024.0 * write_factor
+                else:
+                    k["mfma_sum"] += v
+                    k["n_mfma"] += 1
+        total = 0.0
+        for s, k in kern.items():
+            k["avg_us"] = k["us"] / max(k["dispatches"], 1)
+            k["mfma_busy_pct"] = k.pop("mfma_sum") / max(k.pop("n_mfma"), 1)
+            total += k["read_bytes"] + k["written_bytes"]
+        workloads[wname] = {"measured_bytes": total, "scale_to_reported": scale,
+                            "bytes_per_call": total * scale,
+                            "us_per_call": sum(k["us"] for k in kern.values()) * scale,
+                            "kernels": kern}
+    rec = {"source_digest": source_digest(),
+           "what": "rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB between L2 and the fabric, scaled by "
+                   "a 512 MiB device copy's readings), MfmaUtil and kernel-trace durations of "
+                   "`python3 bench.py --counters`, per workload: long_t1m figures cover 512 of "
+                   "the call's 16,384 chunks and are scaled to the whole call",
+           "calibration": {"kernel": "__amd_rocclr_copyBuffer (512 MiB device copy)",
+                           "fetch_kib": copies[-1], "write_kib": wcopies[-1],
+                           "fetch_factor": fetch_factor, "write_factor": write_factor},
+           "workloads": workloads,
+           "commands": COUNTER_COMMANDS}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = ["# rocprofv3 HBM traffic, MFMA use and kernel times, per workload of `bench.py --counters`", "",
+             "Commands (one MI355X; `R` = the repository root; each counter in a run of its own):",
+             "", "```"] + COUNTER_COMMANDS + ["```", "",
+             "Calibration: a 512 MiB device copy reads FETCH_SIZE %.0f KiB (factor %.3f) and "
+             "WRITE_SIZE %.0f KiB (factor %.3f); the byte figures below are scaled by those "
+             "factors. Source digest `%s`." % (copies[-1], fetch_factor, wcopies[-1],
+                                              write_factor, rec["source_digest"]), ""]
+    for wname, scale in COUNTER_WORKLOADS:
+        w = workloads[wname]
+        lines += ["## %s" % wname, "",
+                  "| kernel | dispatches | avg µs | read MB | written MB | MfmaUtil % |",
+                  "|---|---:|---:|---:|---:|---:|"]
+        for s, k in w["kernels"].items():
+            lines.append("| `%s` | %d | %.2f | %.1f | %.1f | %.2f |" % (
+                s, k["dispatches"], k["avg_us"], k["read_bytes"] / 1e6, k["written_bytes"] / 1e6,
+                k["mfma_busy_pct"]))
+        lines += ["", "Measured: %.3f GB in %.1f µs of kernel time%s." % (
+            w["measured_bytes"] / 1e9, w["us_per_call"] / scale,
+            "" if scale == 1.0 else "; scaled ×%g to the whole call: %.2f GB, %.2f ms" % (
+                scale, w["bytes_per_call"] / 1e9, w["us_per_call"] / 1e3)), ""]
+    with open(os.path.join(ROOT, "profiles", COUNTERS_MD), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/traffic.json and profiles/%s" % COUNTERS_MD)
+    stats = sorted(glob.glob(os.path.join(folder, "bench_ks/**/*kernel_stats.csv"), recursive=True))
+    if stats:
+        digest_bench_stats(stats[0], rec["source_digest"])
+
+
+def digest_bench_stats(path, digest):
+    """Summary of the kernel statistics of a rocprofv3 run of the bench
+    itself: every kernel's calls and average, and the per-call figures the
+    bench's roofline uses."""
+    import csv
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            s = kernel_short(r["Name"]) or r["Name"]
+            if s.startswith("void ") or "at::native" in s:
+                s = "torch: " + s.split("<")[0].split("(")[0].replace("void ", "")[:60]
+            rows.append((s, int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["TotalDurationNs"]) / 1e6, float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[3])
+    avg = {s: a for s, _, a, _, _ in rows}
+    prep, carry = avg.get("prefill_wy_prep_kernel<0, false>"), avg.get("prefill_wy_carry_kernel<16, false>")
+    dec = avg.get("decode_step_kernel<unsigned short, 128, 128, 0, false, false>")
+    lines = ["# rocprofv3 kernel statistics of bench.py (all legs; long_t1m prefill, decode_n256, ...)",
+             "", "Command (one MI355X; `R` = the repository root):", "", "```",
+             BENCH_STATS_COMMAND, "python3 $R/bench.py --digest $R/gpurun_out", "```", "",
+             "Source digest `%s`. The run makes 1 warm-up and 5 timed calls of every bench leg "
+             "(KDA, Gated DeltaNet and DeltaNet prefills, the front-end prefill, the prefill "
+             "with snapshots, decode on dense and pooled states, several-token decode, the "
+             "backward), plus the other prefill workloads; torch kernels generate inputs." % digest,
+             "", "| kernel | calls | average (µs) | total (ms) | share |", "|---|---:|---:|---:|---:|"]
+    for s, n, a, t, pct in rows[:24]:
+        lines.append("| `%s` | %d | %.1f | %.2f | %.1f%% |" % (s, n, a, t, pct))
+    lines.append("")
+    if prep and carry:
+        call_ms = 256 * (prep + carry) / 1e3
+        nbytes = PREFILL_BYTES_PER_HT * 1048576 * 32 + 32 * 128 * 128 * 4
+        lines += ["Derived (long_t1m prefill call = 256 blocks of 64 chunks x 32 heads, one "
+                  "prep and one carry launch each):",
+                  "- prep %.1f µs + carry %.1f µs per block (carry: %.2f µs per chunk step)" % (
+                      prep, carry, carry / 64),
+                  "- call = %.2f ms from these averages: %.1f GB/s algorithmic, %.3f of 8 TB/s" % (
+                      call_ms, nbytes / (call_ms * 1e-3) / 1e9, nbytes / (call_ms * 1e-3) / 8e12)]
+    if dec:
+        lines.append("- decode step %.1f µs: %.2f TB/s of algorithmic state traffic (%.3f of 8 TB/s)"
+                     % (dec, 256 * 32 * DECODE_BYTES_PER_HS / (dec * 1e-6) / 1e12,
+                        256 * 32 * DECODE_BYTES_PER_HS / (dec * 1e-6) / 8e12))
+    with open(os.path.join(ROOT, "profiles", BENCH_STATS_MD), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote profiles/%s" % BENCH_STATS_MD)
+
+
+COUNTERS_MD = "hbm_traffic_mfma_kernel_times_by_workload.md"
+BENCH_STATS_MD = "kernel_stats_bench_long_t1m_decode_n256_all_legs.md"
+BENCH_STATS_COMMAND = ("cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d "
+                       "$R/gpurun_out/bench_ks -o bench --output-format csv -- python3 $R/bench.py "
+                       "--steps 5 --warmup 1 --no-cpu-baseline")
+
+
+COUNTER_COMMANDS = [
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats -d $R/gpurun_out/ks "
+    "-o ks --output-format csv -- python3 $R/bench.py --counters",
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $R/gpurun_out/pmc_FETCH_SIZE "
+    "-o pmc --output-format csv -- python3 $R/bench.py --counters",
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $R/gpurun_out/pmc_WRITE_SIZE "
+    "-o pmc --output-format csv -- python3 $R/bench.py --counters",
+    "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc MfmaUtil -d $R/gpurun_out/pmc_MfmaUtil "
+    "-o pmc --output-format csv -- python3 $R/bench.py --counters",
+    "python3 $R/bench.py --digest $R/gpurun_out",
+]
 
 
 def copy_rate_gbps(torch, nbytes=2 << 30, reps=5):
@@ -316,6 +541,9 @@ def bench_backward(torch, kda, gen, inp, steps, warmup):
 
 def main():
     args = parse()
+    if args.digest:
+        digest_counters(args.digest)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU; this build has no multi-GPU path "
               "(heads and sequences shard across GPUs without communication).",
@@ -560,10 +788,23 @@ def main():
     backward = bench_backward(torch, kda, gen, inp, args.steps, args.warmup)
     backward["vs_forward"] = backward["ms"] / pre_avg
 
-    digest = source_digest(["prefill_wy.hip", "kda_mfma.h", "kda_device.h", "kda_sched.h"])
-    traffic = load_counters("prefill_wy.hip", digest)
-    mfma = load_counters("prefill_wy.hip", digest, "mfma")
-    dec_traffic = load_counters("decode.hip", source_digest(["decode.hip", "kda_device.h"]))
+    counters = load_counters() or {}
+
+    def counted(wname, field="bytes_per_call"):
+        w = counters.get(wname)
+        return None if w is None else w[field]
+    traffic = counted("long_t1m_prefill")
+    mfma = None
+    if "long_t1m_prefill" in counters:
+        mfma = {k: v["mfma_busy_pct"] for k, v in counters["long_t1m_prefill"]["kernels"].items()}
+    dec_traffic = counted("decode_n256_step")
+    for wname in ("batch4_t4096", "varlen_n64"):
+        others[wname]["traffic"] = counted(wname)
+        if wname in counters:
+            others[wname]["kernels_avg_us"] = {k: v["avg_us"] for k, v in
+                                               counters[wname]["kernels"].items()}
+    others["tiny_f32"]["traffic"] = None
+    backward["traffic"] = counted("long_t1m_backward")
     copy_gbps = copy_rate_gbps(torch)
 
     result = {
