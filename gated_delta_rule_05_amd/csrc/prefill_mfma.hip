@@ -65,7 +65,7 @@ constexpr int KS = DK + 4;   // bf16 row stride of Kg / Qg / Kn (8-byte aligned 
 constexpr int RS = C + 8;    // bf16 row stride of Kd^T and P
 constexpr int DS = 20;       // bf16 row stride of 16x16 blocks (-A off-diagonal, inverses)
 constexpr int NSTAGE = 4;    // stager waves, 16 rows of each chunk apiece
-constexpr int kMaxTileColumns = 64;  // one 16-column slab per consumer wave
+constexpr int kMaxTileColumns = 128; // four consumer waves of up to two 16-column slabs
 constexpr int kMaxHeads = 16384;     // keeps every chunk-relative byte offset in 31 bits
 
 // A-operand fragment of a bf16 row with the permuted K order of K-step kk
@@ -236,6 +236,39 @@ __device__ __forceinline__ f32x4 row_product(const uint16_t* x, const uint16_t* 
     return acc;
 }
 
+// The K-step fragments of one 16-row block of a [C][KS] operand, kept in
+// registers so several products can share them.
+struct BlockFrag {
+    u32x4 f[4];
+};
+__device__ __forceinline__ BlockFrag block_frag(const uint16_t* rows, int blk, int g, int ln) {
+    const uint16_t* r = rows + (16 * blk + ln) * KS;
+    BlockFrag x;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) x.f[kk] = perm_row(r, kk, g);
+    return x;
+}
+__device__ __forceinline__ f32x4 block_product(const BlockFrag& x, const BlockFrag& y) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = mma32(x.f[kk], y.f[kk], acc);
+    return acc;
+}
+// tile (I, J) of P (lower, diagonal included) and of -A (strictly lower)
+__device__ __forceinline__ void put_p(Smem& sm, int b, int I, int J, const f32x4& acc, int g, int ln) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * g + i;
+        sm.p[b][(16 * I + r) * RS + 16 * J + ln] = bf((I > J || r >= ln) ? acc[i] : 0.f);
+    }
+}
+__device__ __forceinline__ void put_a(Smem& sm, int b, int I, int J, const f32x4& acc, int g, int ln) {
+    uint16_t* blk = sm.an[b] + offdiag_index(I, J) * 16 * DS;
+    const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta[b] + 16 * I + 4 * g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) blk[(4 * g + i) * DS + ln] = bf(-bt[i] * acc[i]);
+}
+
 // One strictly-lower tile of A (which = 0) or any lower tile of P (which =
 // 1) for LDS slot b.
 __device__ __forceinline__ void tile_job(Smem& sm, int b, int which, int t, int g, int ln) {
@@ -263,11 +296,18 @@ __device__ __forceinline__ void tile_job(Smem& sm, int b, int which, int t, int 
 // N and N^T lets every factor enter in the layout it is needed in.  The
 // result is formed transposed, X^T = (I + N^2^T)(I + N^4^T)(I + N^8^T)(I -
 // N^T), whose accumulator layout is exactly the A-operand layout of X.
+__device__ __forceinline__ void diag_inverse(Smem& sm, int b, int I, const f32x4& a, const f32x4& at,
+                                             int g, int ln);
 __device__ __forceinline__ void diag_job(Smem& sm, int b, int I, int g, int ln) {
     const uint16_t* kgI = sm.kg[b] + 16 * I * KS;
     const uint16_t* knI = sm.kn + 16 * I * KS;
     const f32x4 a = row_product(kgI, knI, g, ln);    // (Kg_I Kn_I^T)[4g+i][ln]
     const f32x4 at = row_product(knI, kgI, g, ln);   // (Kg_I Kn_I^T)[ln][4g+i]
+    diag_inverse(sm, b, I, a, at, g, ln);
+}
+// the inverse from a = (Kg_I Kn_I^T)[4g+i][ln] and at = (Kg_I Kn_I^T)[ln][4g+i]
+__device__ __forceinline__ void diag_inverse(Smem& sm, int b, int I, const f32x4& a, const f32x4& at,
+                                             int g, int ln) {
     const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta[b] + 16 * I + 4 * g);
     const float bl = sm.beta[b][16 * I + ln];
     f32x4 N, NT, eye;
@@ -306,9 +346,10 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                          float* __restrict__ snapshots, int snap_tokens, int snap_cap)
 {
     constexpr int NSLAB = TV / 16;                   // 16-column state slabs in the tile
-    constexpr int NC = NSLAB < 4 ? NSLAB : 4;        // consumer waves, one slab each
+    constexpr int NC = NSLAB < 4 ? NSLAB : 4;        // consumer waves
+    constexpr int SPW = NSLAB / NC;                  // slabs per consumer wave (1 or 2)
     constexpr int NP = NW - NC;                      // producer waves
-    static_assert(TV <= kMaxTileColumns && NSLAB == NC, "one slab per consumer wave");
+    static_assert(TV <= kMaxTileColumns && NSLAB == NC * SPW && SPW <= 2, "the slab map");
     static_assert(NP >= NSTAGE, "four stager waves");
     __shared__ Smem sm;
 
@@ -366,7 +407,69 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             load[best] += (j < 4) ? 3 : 1;
             if (best == pw) mine |= 1u << j;
         }
+        // With four producers, a fixed plan of six block products per wave
+        // in which each wave reuses the blocks it has loaded (4 to 6 of the
+        // 16-row blocks of Kg, Qg, Kn instead of 12) and issues the
+        // independent products ahead of the inversion chain:
+        //   wave 0: diagonal 0; P(0,0); P(3,0), P(3,1), P(3,2)
+        //   wave 1: diagonal 1; A(1,0); P(1,0), P(1,1); P(3,3)
+        //   wave 2: diagonal 2; A(2,0); P(2,0), P(2,1), P(2,2)
+        //   wave 3: diagonal 3; A(3,0), A(3,1), A(3,2); A(2,1)
+        auto tiles4 = [&](int m) {
+            const int b = m & 1;
+            const uint16_t* KG = sm.kg[b];
+            const uint16_t* QG = sm.qg[b];
+            const uint16_t* KN = sm.kn;
+            if (pw == 0) {
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg3 = block_frag(QG, 3, g, ln);
+                const BlockFrag kg0 = block_frag(KG, 0, g, ln);
+                const f32x4 a = block_product(kg0, kn0), at = block_product(kn0, kg0);
+                put_p(sm, b, 3, 0, block_product(qg3, kn0), g, ln);
+                const BlockFrag kn1 = block_frag(KN, 1, g, ln);
+                put_p(sm, b, 3, 1, block_product(qg3, kn1), g, ln);
+                const BlockFrag kn2 = block_frag(KN, 2, g, ln);
+                put_p(sm, b, 3, 2, block_product(qg3, kn2), g, ln);
+                const BlockFrag qg0 = block_frag(QG, 0, g, ln);
+                put_p(sm, b, 0, 0, block_product(qg0, kn0), g, ln);
+                diag_inverse(sm, b, 0, a, at, g, ln);
+            } else if (pw == 1) {
+                const BlockFrag kn1 = block_frag(KN, 1, g, ln), kg1 = block_frag(KG, 1, g, ln);
+                const f32x4 a = block_product(kg1, kn1), at = block_product(kn1, kg1);
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg1 = block_frag(QG, 1, g, ln);
+                put_a(sm, b, 1, 0, block_product(kg1, kn0), g, ln);
+                put_p(sm, b, 1, 0, block_product(qg1, kn0), g, ln);
+                put_p(sm, b, 1, 1, block_product(qg1, kn1), g, ln);
+                const BlockFrag qg3 = block_frag(QG, 3, g, ln), kn3 = block_frag(KN, 3, g, ln);
+                put_p(sm, b, 3, 3, block_product(qg3, kn3), g, ln);
+                diag_inverse(sm, b, 1, a, at, g, ln);
+            } else if (pw == 2) {
+                const BlockFrag kn2 = block_frag(KN, 2, g, ln), kg2 = block_frag(KG, 2, g, ln);
+                const f32x4 a = block_product(kg2, kn2), at = block_product(kn2, kg2);
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg2 = block_frag(QG, 2, g, ln);
+                put_a(sm, b, 2, 0, block_product(kg2, kn0), g, ln);
+                put_p(sm, b, 2, 0, block_product(qg2, kn0), g, ln);
+                put_p(sm, b, 2, 2, block_product(qg2, kn2), g, ln);
+                const BlockFrag kn1 = block_frag(KN, 1, g, ln);
+                put_p(sm, b, 2, 1, block_product(qg2, kn1), g, ln);
+                diag_inverse(sm, b, 2, a, at, g, ln);
+            } else {
+                const BlockFrag kn3 = block_frag(KN, 3, g, ln), kg3 = block_frag(KG, 3, g, ln);
+                const f32x4 a = block_product(kg3, kn3), at = block_product(kn3, kg3);
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln), kn1 = block_frag(KN, 1, g, ln);
+                put_a(sm, b, 3, 0, block_product(kg3, kn0), g, ln);
+                put_a(sm, b, 3, 1, block_product(kg3, kn1), g, ln);
+                const BlockFrag kn2 = block_frag(KN, 2, g, ln);
+                put_a(sm, b, 3, 2, block_product(kg3, kn2), g, ln);
+                const BlockFrag kg2 = block_frag(KG, 2, g, ln);
+                put_a(sm, b, 2, 1, block_product(kg2, kn1), g, ln);
+                diag_inverse(sm, b, 3, a, at, g, ln);
+            }
+        };
         auto tiles = [&](int m) {
+            if (NP == 4) {
+                tiles4(m);
+                return;
+            }
             const int b = m & 1;
             // jobs 0..3: diagonal blocks; 4..9: strictly-lower A tiles 1,3,4,6,7,8;
             // 10..19: P tiles 0..9
@@ -408,29 +511,35 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     }
 
     // ======================= consumer waves =======================
-    // fp32 state slab in the accumulator layout:
-    // S[m][i] = state[c = 16m + 4g + i][j = wave * 16 + ln]
-    const int jc = wave * 16 + ln;
-    f32x4 S[8];
+    // SPW fp32 state slabs in the accumulator layout:
+    // S[s][m][i] = state[c = 16m + 4g + i][j = (wave SPW + s) 16 + ln]
+    f32x4 S[SPW][8];
+    int jc[SPW];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int s = 0; s < SPW; ++s) {
+        jc[s] = (wave * SPW + s) * 16 + ln;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            S[m][i] = h0 ? h0[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] : 0.f;
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                S[s][m][i] = h0 ? h0[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc[s]] : 0.f;
+    }
     const int vrow = H * DV;                         // elements between token rows
     auto v_view = [&](int m) {
         const int len = chunk_len(m);
         return rsrc(v + (chunk_start(m) * H + h) * DV + j0,
                     2u * static_cast<uint32_t>((len - 1) * vrow + TV));
     };
-    uint16_t vnext[16];                              // V of the next chunk, rows 16I + 4g + i
+    uint16_t vnext[SPW][16];                         // V of the next chunk, rows 16I + 4g + i
     auto load_v = [&](int m) {
         const __amdgpu_buffer_rsrc_t rv = v_view(m);
 #pragma unroll
-        for (int I = 0; I < 4; ++I)
+        for (int s = 0; s < SPW; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                vnext[4 * I + i] = ld16(rv, 2 * ((16 * I + 4 * g + i) * vrow + jc));
+            for (int I = 0; I < 4; ++I)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    vnext[s][4 * I + i] = ld16(rv, 2 * ((16 * I + 4 * g + i) * vrow + jc[s]));
     };
 
     if (nch > 0) {
@@ -445,23 +554,28 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         const int len = chunk_len(ci);
 
         // ---------------- phase 1: Y = Kg S0, X, E ----------------
-        u32x4 sb[4];
+        u32x4 sb[SPW][4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
-        f32x4 X[4];
+        for (int s = 0; s < SPW; ++s)
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) sb[s][kk] = pack4(S[s][2 * kk], S[s][2 * kk + 1]);
+        f32x4 X[SPW][4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const uint16_t* row = sm.kg[b] + (16 * I + ln) * KS;
             u32x4 fr[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) fr[kk] = perm_row(row, kk, g);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mma32(fr[kk], sb[kk], acc);
             const f32x4 bt = *reinterpret_cast<const f32x4*>(sm.beta[b] + 16 * I + 4 * g);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                X[I][i] = bt[i] * (__uint_as_float(static_cast<uint32_t>(vnext[4 * I + i]) << 16) - acc[i]);
+            for (int s = 0; s < SPW; ++s) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mma32(fr[kk], sb[s][kk], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    X[s][I][i] = bt[i] * (__uint_as_float(static_cast<uint32_t>(vnext[s][4 * I + i]) << 16) - acc[i]);
+            }
         }
         if (ci + 1 < nch) load_v(ci + 1);
         // (I + A) E = X by block forward substitution
@@ -472,21 +586,28 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 #pragma unroll
         for (int I = 0; I < 4; ++I)
             di_f[I] = *reinterpret_cast<const u32x2*>(sm.dinv[b] + (I * 16 + ln) * DS + 4 * g);
-        u32x2 eb[4];
+        u32x2 eb[SPW][4];
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-            f32x4 z = X[I];
+        for (int I = 0; I < 4; ++I)
 #pragma unroll
-            for (int J = 0; J < I; ++J) z = mma16(an_f[offdiag_index(I, J)], eb[J], z);
-            eb[I] = pack2(mma16(di_f[I], pack2(z), zero));
-        }
+            for (int s = 0; s < SPW; ++s) {
+                f32x4 z = X[s][I];
+#pragma unroll
+                for (int J = 0; J < I; ++J) z = mma16(an_f[offdiag_index(I, J)], eb[s][J], z);
+                eb[s][I] = pack2(mma16(di_f[I], pack2(z), zero));
+            }
         __syncthreads();
 
         // ---------------- phase 2: O and the state update ----------------
         const __amdgpu_buffer_rsrc_t ro = rsrc(o + (chunk_start(ci) * H + h) * DV + j0,
                                                2u * static_cast<uint32_t>((len - 1) * vrow + TV));
-        const u32x4 e01 = cat(eb[0], eb[1]), e23 = cat(eb[2], eb[3]);
+        u32x4 e01[SPW], e23[SPW];
+#pragma unroll
+        for (int s = 0; s < SPW; ++s) {
+            e01[s] = cat(eb[s][0], eb[s][1]);
+            e23[s] = cat(eb[s][2], eb[s][3]);
+        }
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             // O = scale (Qg S0 + P E); rows past the end are dropped by the range check
@@ -497,14 +618,17 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             for (int kk = 0; kk < 4; ++kk) fr[kk] = perm_row(qrow, kk, g);
             fr[4] = perm_row(prow, 0, g);
             if (I >= 2) fr[5] = perm_row(prow, 1, g);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mma32(fr[kk], sb[kk], acc);
-            acc = mma32(fr[4], e01, acc);
-            if (I >= 2) acc = mma32(fr[5], e23, acc);
+            for (int s = 0; s < SPW; ++s) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc), bf(scale * acc[i]));
+                for (int kk = 0; kk < 4; ++kk) acc = mma32(fr[kk], sb[s][kk], acc);
+                acc = mma32(fr[4], e01[s], acc);
+                if (I >= 2) acc = mma32(fr[5], e23[s], acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc[s]), bf(scale * acc[i]));
+            }
         }
         // S = Diag(e^{G}) S0 + Kd^T E
 #pragma unroll
@@ -512,28 +636,34 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             const uint16_t* krow = sm.kdt[b] + (16 * m + ln) * RS;
             const u32x4 f0 = perm_row(krow, 0, g), f1 = perm_row(krow, 1, g);
             const f32x4 gm = *reinterpret_cast<const f32x4*>(sm.gam[b] + 16 * m + 4 * g);
-            S[m] = mma32(f1, e23, mma32(f0, e01, gm * S[m]));
+#pragma unroll
+            for (int s = 0; s < SPW; ++s) S[s][m] = mma32(f1, e23[s], mma32(f0, e01[s], gm * S[s][m]));
         }
         // a snapshot after every snap_tokens / C chunks (a countdown: one
         // decrement per chunk on the serial path)
         const int js = snapshots && --snap_left == 0
                            ? (snap_left = snap_tokens / C, (ci + 1) / (snap_tokens / C) - 1) : -1;
         if (js >= 0 && js < snap_cap && len == C) {      // only a full chunk ends on a boundary
-            float* dst = snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0 + jc;
+            float* dst = snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0;
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
+            for (int s = 0; s < SPW; ++s)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dst[static_cast<int64_t>(16 * m + 4 * g + i) * DV] = S[m][i];
+                for (int m = 0; m < 8; ++m)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        dst[static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc[s]] = S[s][m][i];
         }
         __syncthreads();
     }
 
     if (hT) {
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int s = 0; s < SPW; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                hT[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc] = S[m][i];
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    hT[sbase + static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc[s]] = S[s][m][i];
     }
 }
 
@@ -581,6 +711,7 @@ hipError_t launch_prefill_mfma(const PrefillArgs& a, int R, hipStream_t stream) 
         case 16: return launch_mfma_t<16>(a, R, stream);
         case 32: return launch_mfma_t<32>(a, R, stream);
         case 64: return launch_mfma_t<64>(a, R, stream);
+        case 128: return launch_mfma_t<128>(a, R, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -152,8 +152,7 @@ typedef struct kda_prefill_options {
     int32_t value_tiles;   /* work-groups per (sequence, head), each owning
                               d_v / value_tiles state columns; 0 = automatic.
                               A power of two with 16 <= d_v / value_tiles
-                              <= 64 (fused matrix path) or <= 32 (two-pass
-                              path).  Ignored by the vector
+                              (<= 32 on the two-pass path).  Ignored by the vector
                               path, which always uses 32-column tiles
                               (16 when d_v = 16). */
     int32_t block_chunks;  /* two-pass path: chunks of every sequence per

@@ -181,7 +181,7 @@ def prefill_ex_call(path, tiles, blk=0, gate=0, snap=(0, 0, None), front=None, m
     (3, 0, 5, dict(wsb=two_pass_bytes(2, 4, 128, 128, 5) - 1), WS_SMALL),
     (2, 3, 0, {}, INVALID), (2, 16, 0, {}, INVALID), (2, -2, 0, {}, INVALID),
     (2, 4, 0, dict(dv=32), INVALID),              # 8 columns per tile
-    (2, 1, 0, {}, INVALID),                       # 128 columns per tile
+    (2, 1, 0, dict(wsb=0), WS_SMALL),             # 128 columns per tile pass the tile check
     (2, 0, 0, dict(dtype=1), UNSUPPORTED),        # matrix path needs bf16
     (2, 0, 0, dict(dk=64), UNSUPPORTED),          # matrix path needs d_k = 128
     (1, -1, 0, {}, INVALID),

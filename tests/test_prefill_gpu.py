@@ -81,10 +81,10 @@ def test_matrix_paths_ragged(path, dv):
     parity(inp, "%s dv=%d ragged" % (path, dv), tol_for("bf16"), path=path)
 
 
-@pytest.mark.parametrize("path,tiles", [("matrix", 2), ("matrix", 4), ("matrix", 8),
+@pytest.mark.parametrize("path,tiles", [("matrix", 1), ("matrix", 2), ("matrix", 4), ("matrix", 8),
                                         ("two_pass", 4), ("two_pass", 8)])
 def test_matrix_path_every_tile_width(path, tiles):
-    """Each value-tile width of both matrix paths (64 (fused only), 32, 16 columns)."""
+    """Each value-tile width of both matrix paths (128 and 64 (fused only), 32, 16 columns)."""
     inp = gen.prefill_inputs([200, 64, 1, 129], 3, 128, 128, "bf16", "softplus",
                              state_std=0.02, seed=40 + tiles, device=DEV)
     o, hT = call(inp, path=path, value_tiles=tiles)

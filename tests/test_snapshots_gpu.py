@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 SNAP, CAP = 64, 4
 LENS = [300, 64, 1, 129, 0, 256, 200]
-PATHS = [("f32", "vector", 64, 0), ("bf16", "matrix", 128, 4), ("bf16", "two_pass", 128, 8)]
+PATHS = [("f32", "vector", 64, 0), ("bf16", "matrix", 128, 4), ("bf16", "matrix", 128, 1),
+         ("bf16", "two_pass", 128, 8)]
 
 
 @pytest.mark.parametrize("dtype,path,d,tiles", PATHS)
