@@ -106,7 +106,9 @@ struct alignas(16) Smem {
 // final state of the tile are NaN).  A row with every channel in range is
 // exact: gates <= 0 make |g| grow down the chunk, so its products only
 // involve rows in range, and such a chunk's G out of range is what any row
-// out of range implies.
+// out of range implies.  The outputs leave through one identity product per
+// 16-row block, which spreads a NaN row over its block: the blocks before
+// the first row out of range stay exact.
 constexpr float kSafeLog2 = 115.f;
 
 // Byte-range views of one chunk of one head: row r of the chunk starts at
@@ -357,6 +359,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     int tile;
     if (!prefill_map_block(blockIdx.x, groups, R, pair, tile)) return;
     const int tid = threadIdx.x;
+    // the wave index is uniform across the wave: the roles below branch on it
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int g = lane >> 4;
@@ -374,9 +377,49 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 
     for (int i = tid; i < C * RS; i += NT) reinterpret_cast<uint32_t*>(&sm.p[0][0])[i] = 0u;
 
+    // P for LDS slot m & 1, with four consumers (the producers then take A
+    // and the diagonal blocks):
+    //   wave 0: P(0,0), P(3,0), P(3,3)    wave 1: P(1,0), P(1,1), P(3,1)
+    //   wave 2: P(2,0), P(2,1)            wave 3: P(2,2), P(3,2)
+    auto p_tiles4 = [](int m, int c, int g, int ln) __attribute__((noinline)) {
+        const int b = m & 1;
+        const uint16_t* QG = sm.qg[b];
+        const uint16_t* KN = sm.kn;
+        if (c == 0) {
+            const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg3 = block_frag(QG, 3, g, ln);
+            const BlockFrag qg0 = block_frag(QG, 0, g, ln);
+            put_p(sm, b, 3, 0, block_product(qg3, kn0), g, ln);
+            put_p(sm, b, 0, 0, block_product(qg0, kn0), g, ln);
+            const BlockFrag kn3 = block_frag(KN, 3, g, ln);
+            put_p(sm, b, 3, 3, block_product(qg3, kn3), g, ln);
+        } else if (c == 1) {
+            const BlockFrag kn0 = block_frag(KN, 0, g, ln), kn1 = block_frag(KN, 1, g, ln);
+            const BlockFrag qg1 = block_frag(QG, 1, g, ln);
+            put_p(sm, b, 1, 0, block_product(qg1, kn0), g, ln);
+            put_p(sm, b, 1, 1, block_product(qg1, kn1), g, ln);
+            const BlockFrag qg3 = block_frag(QG, 3, g, ln);
+            put_p(sm, b, 3, 1, block_product(qg3, kn1), g, ln);
+        } else if (c == 2) {
+            const BlockFrag kn0 = block_frag(KN, 0, g, ln), kn1 = block_frag(KN, 1, g, ln);
+            const BlockFrag qg2 = block_frag(QG, 2, g, ln);
+            put_p(sm, b, 2, 0, block_product(qg2, kn0), g, ln);
+            put_p(sm, b, 2, 1, block_product(qg2, kn1), g, ln);
+        } else {
+            const BlockFrag kn2 = block_frag(KN, 2, g, ln), qg2 = block_frag(QG, 2, g, ln);
+            const BlockFrag qg3 = block_frag(QG, 3, g, ln);
+            put_p(sm, b, 2, 2, block_product(qg2, kn2), g, ln);
+            put_p(sm, b, 3, 2, block_product(qg3, kn2), g, ln);
+        }
+    };
+
     if (wave >= NC) {
         // ======================= producer waves =======================
         const int pw = wave - NC;
+        // the producers' own copies of the lane coordinates: their LDS
+        // addresses are then not shared with (and kept live for) the
+        // consumer path
+        int pg = g, pln = ln;
+        asm volatile("" : "+v"(pg), "+v"(pln));
         const bool stager = pw < NSTAGE;
         StageRegs rg;
         uint32_t beta_next = 0u;
@@ -407,67 +450,51 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             load[best] += (j < 4) ? 3 : 1;
             if (best == pw) mine |= 1u << j;
         }
-        // With four producers, a fixed plan of six block products per wave
-        // in which each wave reuses the blocks it has loaded (4 to 6 of the
-        // 16-row blocks of Kg, Qg, Kn instead of 12) and issues the
-        // independent products ahead of the inversion chain:
-        //   wave 0: diagonal 0; P(0,0); P(3,0), P(3,1), P(3,2)
-        //   wave 1: diagonal 1; A(1,0); P(1,0), P(1,1); P(3,3)
-        //   wave 2: diagonal 2; A(2,0); P(2,0), P(2,1), P(2,2)
-        //   wave 3: diagonal 3; A(3,0), A(3,1), A(3,2); A(2,1)
-        auto tiles4 = [&](int m) {
+        // With four producers (and four consumers), the producers take A and
+        // the diagonal blocks, each wave reusing the 16-row blocks it has
+        // loaded and issuing its independent products ahead of the inversion
+        // chain; the consumers take P (p_tiles4):
+        //   wave 0: diagonal 0; A(3,0)
+        //   wave 1: diagonal 1; A(1,0), A(3,1)
+        //   wave 2: diagonal 2; A(2,0), A(2,1)
+        //   wave 3: diagonal 3; A(3,2)
+        auto tiles4 = [](int m, int pw, int g, int ln) __attribute__((noinline)) {
             const int b = m & 1;
             const uint16_t* KG = sm.kg[b];
-            const uint16_t* QG = sm.qg[b];
             const uint16_t* KN = sm.kn;
             if (pw == 0) {
-                const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg3 = block_frag(QG, 3, g, ln);
-                const BlockFrag kg0 = block_frag(KG, 0, g, ln);
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln), kg0 = block_frag(KG, 0, g, ln);
+                const BlockFrag kg3 = block_frag(KG, 3, g, ln);
                 const f32x4 a = block_product(kg0, kn0), at = block_product(kn0, kg0);
-                put_p(sm, b, 3, 0, block_product(qg3, kn0), g, ln);
-                const BlockFrag kn1 = block_frag(KN, 1, g, ln);
-                put_p(sm, b, 3, 1, block_product(qg3, kn1), g, ln);
-                const BlockFrag kn2 = block_frag(KN, 2, g, ln);
-                put_p(sm, b, 3, 2, block_product(qg3, kn2), g, ln);
-                const BlockFrag qg0 = block_frag(QG, 0, g, ln);
-                put_p(sm, b, 0, 0, block_product(qg0, kn0), g, ln);
+                put_a(sm, b, 3, 0, block_product(kg3, kn0), g, ln);
                 diag_inverse(sm, b, 0, a, at, g, ln);
             } else if (pw == 1) {
                 const BlockFrag kn1 = block_frag(KN, 1, g, ln), kg1 = block_frag(KG, 1, g, ln);
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln);
                 const f32x4 a = block_product(kg1, kn1), at = block_product(kn1, kg1);
-                const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg1 = block_frag(QG, 1, g, ln);
                 put_a(sm, b, 1, 0, block_product(kg1, kn0), g, ln);
-                put_p(sm, b, 1, 0, block_product(qg1, kn0), g, ln);
-                put_p(sm, b, 1, 1, block_product(qg1, kn1), g, ln);
-                const BlockFrag qg3 = block_frag(QG, 3, g, ln), kn3 = block_frag(KN, 3, g, ln);
-                put_p(sm, b, 3, 3, block_product(qg3, kn3), g, ln);
+                const BlockFrag kg3 = block_frag(KG, 3, g, ln);
+                put_a(sm, b, 3, 1, block_product(kg3, kn1), g, ln);
                 diag_inverse(sm, b, 1, a, at, g, ln);
             } else if (pw == 2) {
                 const BlockFrag kn2 = block_frag(KN, 2, g, ln), kg2 = block_frag(KG, 2, g, ln);
+                const BlockFrag kn0 = block_frag(KN, 0, g, ln);
                 const f32x4 a = block_product(kg2, kn2), at = block_product(kn2, kg2);
-                const BlockFrag kn0 = block_frag(KN, 0, g, ln), qg2 = block_frag(QG, 2, g, ln);
                 put_a(sm, b, 2, 0, block_product(kg2, kn0), g, ln);
-                put_p(sm, b, 2, 0, block_product(qg2, kn0), g, ln);
-                put_p(sm, b, 2, 2, block_product(qg2, kn2), g, ln);
                 const BlockFrag kn1 = block_frag(KN, 1, g, ln);
-                put_p(sm, b, 2, 1, block_product(qg2, kn1), g, ln);
+                put_a(sm, b, 2, 1, block_product(kg2, kn1), g, ln);
                 diag_inverse(sm, b, 2, a, at, g, ln);
             } else {
                 const BlockFrag kn3 = block_frag(KN, 3, g, ln), kg3 = block_frag(KG, 3, g, ln);
-                const f32x4 a = block_product(kg3, kn3), at = block_product(kn3, kg3);
-                const BlockFrag kn0 = block_frag(KN, 0, g, ln), kn1 = block_frag(KN, 1, g, ln);
-                put_a(sm, b, 3, 0, block_product(kg3, kn0), g, ln);
-                put_a(sm, b, 3, 1, block_product(kg3, kn1), g, ln);
                 const BlockFrag kn2 = block_frag(KN, 2, g, ln);
+                const f32x4 a = block_product(kg3, kn3), at = block_product(kn3, kg3);
                 put_a(sm, b, 3, 2, block_product(kg3, kn2), g, ln);
-                const BlockFrag kg2 = block_frag(KG, 2, g, ln);
-                put_a(sm, b, 2, 1, block_product(kg2, kn1), g, ln);
                 diag_inverse(sm, b, 3, a, at, g, ln);
             }
         };
         auto tiles = [&](int m) {
             if (NP == 4) {
-                tiles4(m);
+                tiles4(m, pw, pg, pln);
                 return;
             }
             const int b = m & 1;
@@ -530,22 +557,35 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         return rsrc(v + (chunk_start(m) * H + h) * DV + j0,
                     2u * static_cast<uint32_t>((len - 1) * vrow + TV));
     };
-    uint16_t vnext[SPW][16];                         // V of the next chunk, rows 16I + 4g + i
+    // V and O move in 8-byte row pieces: lane (g, ln) of a 16 x 16 block
+    // holds row ln, columns 4g .. 4g+3 -- the A-operand layout of that block.
+    // One 16x16x16 product with the identity turns it into the accumulator
+    // layout (rows 4g + i, column ln) and back; bf16 values times 1 and 0
+    // summed in fp32 are exact.
+    const int slab_col = wave * SPW * 16 + 4 * g;   // first column of the lane's piece, slab 0
+    u32x2 ident;
+    {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = (4 * g + i == ln) ? 1.f : 0.f;
+        ident = u32x2{pk(e[0], e[1]), pk(e[2], e[3])};
+    }
+    u32x2 vnext[SPW][4];                             // V of the next chunk, block I, slab s
     auto load_v = [&](int m) {
         const __amdgpu_buffer_rsrc_t rv = v_view(m);
 #pragma unroll
-        for (int s = 0; s < SPW; ++s)
+        for (int I = 0; I < 4; ++I) {
+            const int off = 2 * ((16 * I + ln) * vrow + slab_col);
 #pragma unroll
-            for (int I = 0; I < 4; ++I)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vnext[s][4 * I + i] = ld16(rv, 2 * ((16 * I + 4 * g + i) * vrow + jc[s]));
+            for (int s = 0; s < SPW; ++s) vnext[s][I] = ld64(rv, off + 32 * s);
+        }
     };
 
     if (nch > 0) {
         load_v(0);
         __syncthreads();
         __syncthreads();
+        if (NP == 4) p_tiles4(0, wave, g, ln);
         __syncthreads();
     }
     int snap_left = snapshots ? snap_tokens / C : 0;
@@ -554,12 +594,23 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         const int len = chunk_len(ci);
 
         // ---------------- phase 1: Y = Kg S0, X, E ----------------
+        // row block by row block: Y_I = Kg_I S0, X_I = Diag(beta_I)(V_I - Y_I),
+        // then (I + A) E = X by block forward substitution,
+        //   E_I = (I + A_II)^{-1} (X_I - sum_{J<I} A_IJ E_J)
         u32x4 sb[SPW][4];
 #pragma unroll
         for (int s = 0; s < SPW; ++s)
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) sb[s][kk] = pack4(S[s][2 * kk], S[s][2 * kk + 1]);
-        f32x4 X[SPW][4];
+        u32x2 an_f[6], di_f[4];
+#pragma unroll
+        for (int x = 0; x < 6; ++x)
+            an_f[x] = *reinterpret_cast<const u32x2*>(sm.an[b] + (x * 16 + ln) * DS + 4 * g);
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+            di_f[I] = *reinterpret_cast<const u32x2*>(sm.dinv[b] + (I * 16 + ln) * DS + 4 * g);
+        u32x2 eb[SPW][4];
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             const uint16_t* row = sm.kg[b] + (16 * I + ln) * KS;
@@ -572,34 +623,18 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) acc = mma32(fr[kk], sb[s][kk], acc);
+                const f32x4 vv = mma16(vnext[s][I], ident, zero);   // V rows 4g + i, column ln
+                f32x4 z;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    X[s][I][i] = bt[i] * (__uint_as_float(static_cast<uint32_t>(vnext[s][4 * I + i]) << 16) - acc[i]);
-            }
-        }
-        if (ci + 1 < nch) load_v(ci + 1);
-        // (I + A) E = X by block forward substitution
-        u32x2 an_f[6], di_f[4];
-#pragma unroll
-        for (int x = 0; x < 6; ++x)
-            an_f[x] = *reinterpret_cast<const u32x2*>(sm.an[b] + (x * 16 + ln) * DS + 4 * g);
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-            di_f[I] = *reinterpret_cast<const u32x2*>(sm.dinv[b] + (I * 16 + ln) * DS + 4 * g);
-        u32x2 eb[SPW][4];
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-            for (int s = 0; s < SPW; ++s) {
-                f32x4 z = X[s][I];
+                for (int i = 0; i < 4; ++i) z[i] = bt[i] * (vv[i] - acc[i]);
 #pragma unroll
                 for (int J = 0; J < I; ++J) z = mma16(an_f[offdiag_index(I, J)], eb[s][J], z);
                 eb[s][I] = pack2(mma16(di_f[I], pack2(z), zero));
             }
-        __syncthreads();
+        }
+        if (ci + 1 < nch) load_v(ci + 1);
 
-        // ---------------- phase 2: O and the state update ----------------
+        // O: the start state's bf16 copy dies here, before the barrier
         const __amdgpu_buffer_rsrc_t ro = rsrc(o + (chunk_start(ci) * H + h) * DV + j0,
                                                2u * static_cast<uint32_t>((len - 1) * vrow + TV));
         u32x4 e01[SPW], e23[SPW];
@@ -625,11 +660,14 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                 for (int kk = 0; kk < 4; ++kk) acc = mma32(fr[kk], sb[s][kk], acc);
                 acc = mma32(fr[4], e01[s], acc);
                 if (I >= 2) acc = mma32(fr[5], e23[s], acc);
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    st16(ro, 2 * ((16 * I + 4 * g + i) * vrow + jc[s]), bf(scale * acc[i]));
+                // bf16 (round to nearest even), then to row pieces and out
+                const f32x4 t = mma16(pack2(scale * acc), ident, zero);
+                st64(ro, 2 * ((16 * I + ln) * vrow + slab_col) + 32 * s, pack2(t));
             }
         }
+        __syncthreads();
+
+        // ---------------- phase 2: the state update ----------------
         // S = Diag(e^{G}) S0 + Kd^T E
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -645,14 +683,19 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                            ? (snap_left = snap_tokens / C, (ci + 1) / (snap_tokens / C) - 1) : -1;
         if (js >= 0 && js < snap_cap && len == C) {      // only a full chunk ends on a boundary
             float* dst = snapshot_at(snapshots, snap_cap, H, static_cast<int64_t>(DK) * DV, n, js, h) + j0;
+            // the lane's part of the offsets, formed here: hoisted out of
+            // the chunk loop, 64 per-element addresses would stay live
+            int lp = 4 * g * DV + jc[0];
+            asm volatile("" : "+v"(lp));
 #pragma unroll
             for (int s = 0; s < SPW; ++s)
 #pragma unroll
                 for (int m = 0; m < 8; ++m)
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        dst[static_cast<int64_t>(16 * m + 4 * g + i) * DV + jc[s]] = S[s][m][i];
+                        dst[static_cast<int64_t>(16 * m + i) * DV + lp + 16 * s] = S[s][m][i];
         }
+        if (NP == 4 && ci + 1 < nch) p_tiles4(ci + 1, wave, g, ln);
         __syncthreads();
     }
 

@@ -320,10 +320,10 @@ size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H,
  *     (the vector path from fp64 cumulative gates, and already beyond
  *     |g| = 16): exact, at a higher cost for that chunk (a two-pass
  *     prefill whose every chunk takes this form runs about 2.7x longer);
- *   fused matrix path: that chunk's outputs, every later output of the
- *     same (sequence, head, value tile) and its final state are NaN --
- *     never finite and wrong; request KDA_PATH_MATRIX_TWO_PASS for such
- *     gates.
+ *   fused matrix path: that chunk's outputs from the 16-token block of
+ *     its first such token on, every later output of the same (sequence,
+ *     head, value tile) and its final state are NaN -- never finite and
+ *     wrong; request KDA_PATH_MATRIX_TWO_PASS for such gates.
  *
  * Requirements (else the status in brackets):
  *   N >= 1, H >= 1, total_T >= 0, sizes whose byte counts fit in int64
