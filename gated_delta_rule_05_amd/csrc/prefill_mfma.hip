@@ -50,6 +50,7 @@
 // unchanged.  For the 16x16x16 products of the substitution the
 // accumulator layout already is the B-operand layout.
 #include "kda_device.h"
+#include "kda_exact.h"
 #include "kda_internal.h"
 #include "kda_mfma.h"
 #include "kda_sched.h"
@@ -96,19 +97,17 @@ struct alignas(16) Smem {
     float gam[2][DK];                  // e^{G}
     uint16_t kn[C * KS];               // K * e^{-g} (producers only)
     float2 tot[2][4 * (DK / 2)];       // gate sums of the four 16-row blocks (log2 units)
+    int xflag[2];                      // the chunk takes the exact pairwise form
 };
 
 // |g| (log2 units) up to which e^{g} and e^{-g} stay inside fp32 (e^{80}).
-// Beyond it this path cannot form a chunk, and poisons it instead: each
-// channel out of range puts NaN into its row's Qg entry (one NaN channel
-// makes the row's output NaN), and e^{G} is NaN on every channel once any
-// channel's G is out of range (so the state, every later output and the
-// final state of the tile are NaN).  A row with every channel in range is
-// exact: gates <= 0 make |g| grow down the chunk, so its products only
-// involve rows in range, and such a chunk's G out of range is what any row
-// out of range implies.  The outputs leave through one identity product per
-// 16-row block, which spreads a NaN row over its block: the blocks before
-// the first row out of range stay exact.
+// A chunk whose total gate G leaves that range on some channel (for gates
+// <= 0, |g| <= |G| on every row) takes the exact pairwise form instead: its
+// staging forms only factors <= 1 (Kg, Qg, Kd = K e^{G - g}, e^{G}; no Kn),
+// and all eight waves then sum A and P entry by entry (exact_chunk).  A row
+// whose own |g| leaves the range while G does not (only possible with
+// positive gates, outside the domain) gets NaN in its Qg entry: never
+// finite and wrong.
 constexpr float kSafeLog2 = 115.f;
 
 // Byte-range views of one chunk of one head: row r of the chunk starts at
@@ -173,9 +172,11 @@ __device__ __forceinline__ float2 block_gate_sum(const StageRegs& rg) {
 }
 
 // Stage rows 16w .. 16w+15 into LDS slot b: cumulative gate, e^{+-g}, Kg,
-// Qg, Kn, Kd^T (and e^{G} from stager 0).  `tot` holds the four blocks'
-// gate sums.  Rows past the end of the sequence hold zeros (they were read
-// out of range), so they add nothing to the gate and contribute zero rows.
+// Qg, Kn, Kd^T (and e^{G} and the chunk's exact-form flag from stager 0).
+// `tot` holds the four blocks' gate sums.  Rows past the end of the
+// sequence hold zeros (they were read out of range), so they add nothing to
+// the gate and contribute zero rows.  Every stager sees every channel's G,
+// so all of them take the same branch.
 __device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
                                            const float2* tot, int w, int lane) {
     float run0 = 0.f, run1 = 0.f, G0 = 0.f, G1 = 0.f;
@@ -186,37 +187,63 @@ __device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
         G0 += t.x;
         G1 += t.y;
     }
+    const bool exact = __ballot(!(fabsf(G0) <= kSafeLog2 && fabsf(G1) <= kSafeLog2)) != 0ull;
     const float gl0 = __builtin_amdgcn_exp2f(G0), gl1 = __builtin_amdgcn_exp2f(G1);
-    const float nan = __builtin_nanf("");
     if (w == 0) {
-        const bool wild = __ballot(!(fabsf(G0) <= kSafeLog2 && fabsf(G1) <= kSafeLog2)) != 0ull;
-        *reinterpret_cast<float2*>(sm.gam[b] + 2 * lane) =
-            wild ? make_float2(nan, nan) : make_float2(gl0, gl1);
+        *reinterpret_cast<float2*>(sm.gam[b] + 2 * lane) = make_float2(gl0, gl1);
+        if (lane == 0) sm.xflag[b] = exact ? 1 : 0;
     }
     float kd0[4], kd1[4];
+    if (!exact) {
+        const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int row = 16 * w + r;
-        run0 = __builtin_fmaf(__uint_as_float(rg.la[r][0]), kLog2e, run0);   // g_row / ln 2
-        run1 = __builtin_fmaf(__uint_as_float(rg.la[r][1]), kLog2e, run1);
-        const bool wild = !(fabsf(run0) <= kSafeLog2 && fabsf(run1) <= kSafeLog2);
-        const float u0 = __builtin_amdgcn_exp2f(run0), u1 = __builtin_amdgcn_exp2f(run1);
-        const float w0 = __builtin_amdgcn_exp2f(-run0), w1 = __builtin_amdgcn_exp2f(-run1);
-        const float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
-        const float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
-        const float n0 = kx * w0, n1 = ky * w1;
-        *reinterpret_cast<uint32_t*>(sm.kg[b] + row * KS + 2 * lane) = pk(kx * u0, ky * u1);
-        *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) =
-            wild ? pk(nan, nan) : pk(qx * u0, qy * u1);
-        *reinterpret_cast<uint32_t*>(sm.kn + row * KS + 2 * lane) = pk(n0, n1);
-        kd0[r & 3] = n0 * gl0;
-        kd1[r & 3] = n1 * gl1;
-        if ((r & 3) == 3) {
-            const int c0 = row - 3;
-            *reinterpret_cast<u32x2*>(sm.kdt[b] + (2 * lane) * RS + c0) =
-                u32x2{pk(kd0[0], kd0[1]), pk(kd0[2], kd0[3])};
-            *reinterpret_cast<u32x2*>(sm.kdt[b] + (2 * lane + 1) * RS + c0) =
-                u32x2{pk(kd1[0], kd1[1]), pk(kd1[2], kd1[3])};
+        for (int r = 0; r < 16; ++r) {
+            const int row = 16 * w + r;
+            run0 = __builtin_fmaf(__uint_as_float(rg.la[r][0]), kLog2e, run0);   // g_row / ln 2
+            run1 = __builtin_fmaf(__uint_as_float(rg.la[r][1]), kLog2e, run1);
+            const bool wild = !(fabsf(run0) <= kSafeLog2 && fabsf(run1) <= kSafeLog2);
+            const float u0 = __builtin_amdgcn_exp2f(run0), u1 = __builtin_amdgcn_exp2f(run1);
+            const float w0 = __builtin_amdgcn_exp2f(-run0), w1 = __builtin_amdgcn_exp2f(-run1);
+            const float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
+            const float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
+            const float n0 = kx * w0, n1 = ky * w1;
+            *reinterpret_cast<uint32_t*>(sm.kg[b] + row * KS + 2 * lane) = pk(kx * u0, ky * u1);
+            *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) =
+                wild ? pk(nan, nan) : pk(qx * u0, qy * u1);
+            *reinterpret_cast<uint32_t*>(sm.kn + row * KS + 2 * lane) = pk(n0, n1);
+            kd0[r & 3] = n0 * gl0;
+            kd1[r & 3] = n1 * gl1;
+            if ((r & 3) == 3) {
+                const int c0 = row - 3;
+                *reinterpret_cast<u32x2*>(sm.kdt[b] + (2 * lane) * RS + c0) =
+                    u32x2{pk(kd0[0], kd0[1]), pk(kd0[2], kd0[3])};
+                *reinterpret_cast<u32x2*>(sm.kdt[b] + (2 * lane + 1) * RS + c0) =
+                    u32x2{pk(kd1[0], kd1[1]), pk(kd1[2], kd1[3])};
+            }
+        }
+    } else {
+        // factors <= 1 only: e^{g}, e^{G - g}; A and P come from exact_chunk
+        // (fully unrolled: the staged registers are indexed by row)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = 16 * w + r;
+            run0 = __builtin_fmaf(__uint_as_float(rg.la[r][0]), kLog2e, run0);
+            run1 = __builtin_fmaf(__uint_as_float(rg.la[r][1]), kLog2e, run1);
+            const float u0 = __builtin_amdgcn_exp2f(run0), u1 = __builtin_amdgcn_exp2f(run1);
+            const float d0 = __builtin_amdgcn_exp2f(G0 - run0), d1 = __builtin_amdgcn_exp2f(G1 - run1);
+            const float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
+            const float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
+            *reinterpret_cast<uint32_t*>(sm.kg[b] + row * KS + 2 * lane) = pk(kx * u0, ky * u1);
+            *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) = pk(qx * u0, qy * u1);
+            kd0[r & 3] = kx * d0;
+            kd1[r & 3] = ky * d1;
+            if ((r & 3) == 3) {
+                const int c0 = row - 3;
+                *reinterpret_cast<u32x2*>(sm.kdt[b] + (2 * lane) * RS + c0) =
+                    u32x2{pk(kd0[0], kd0[1]), pk(kd0[2], kd0[3])};
+                *reinterpret_cast<u32x2*>(sm.kdt[b] + (2 * lane + 1) * RS + c0) =
+                    u32x2{pk(kd1[0], kd1[1]), pk(kd1[2], kd1[3])};
+            }
         }
     }
 }
@@ -381,7 +408,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     // and the diagonal blocks):
     //   wave 0: P(0,0), P(3,0), P(3,3)    wave 1: P(1,0), P(1,1), P(3,1)
     //   wave 2: P(2,0), P(2,1)            wave 3: P(2,2), P(3,2)
-    auto p_tiles4 = [](int m, int c, int g, int ln) __attribute__((noinline)) {
+    auto p_tiles4 = [](int m, int c, int g, int ln) __attribute__((always_inline)) {
         const int b = m & 1;
         const uint16_t* QG = sm.qg[b];
         const uint16_t* KN = sm.kn;
@@ -410,6 +437,89 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             put_p(sm, b, 2, 2, block_product(qg2, kn2), g, ln);
             put_p(sm, b, 3, 2, block_product(qg3, kn2), g, ln);
         }
+    };
+
+    // A, P and the diagonal-block inverses of the chunk in LDS slot b, in the
+    // exact pairwise form (kda_exact.h), by all eight waves.  The chunk's k,
+    // q and gates are read again (the stagers loaded them two chunks ago, so
+    // they are likely still in L2) and staged 32 channels at a time in LDS
+    // that is dead at this point: the other slot's Kg and Qg rows (the
+    // consumers read them in the first phase only) and Kn (not formed for
+    // such a chunk).  Contains barriers: every wave calls it, or none.
+    auto exact_chunk = [](int b, ChunkView cv, int H, int tid, int wave, int g, int ln)
+                           __attribute__((always_inline)) {
+        float* sk = reinterpret_cast<float*>(sm.kg[b ^ 1]);
+        float* sq = reinterpret_cast<float*>(sm.qg[b ^ 1]);
+        float* sg = reinterpret_cast<float*>(sm.kn);
+        float* dt = sg + C * kExactXS;      // strictly lower entries of B's diagonal blocks
+        float* gs = dt + 4 * 16 * 16;       // [16][32] gate sums of four-row groups
+        const ExactUnit u = exact_unit(tid);
+        float a[4][2], pp[4][2];
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 2; ++y) a[x][y] = pp[x][y] = 0.f;
+        const int c = tid & 31, r16 = tid >> 5;
+#pragma unroll 1
+        for (int j = 0; j < 4; ++j) {
+            // channels 32j .. 32j + 31; this thread: channel c of rows 4 r16 .. +3
+            float kk[4], qq[4], gg[4], run = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 4 * r16 + i;
+                const int off = row * H * DK + 32 * j + c;
+                kk[i] = __uint_as_float(static_cast<uint32_t>(ld16(cv.k, 2 * off)) << 16);
+                qq[i] = __uint_as_float(static_cast<uint32_t>(ld16(cv.q, 2 * off)) << 16);
+                const uint32_t lb = GATE == kGateChannel ? ld32(cv.la, 4 * off) : ld32(cv.la, 4 * row * H);
+                run += __uint_as_float(lb);
+                gg[i] = run;
+            }
+            gs[r16 * 32 + c] = run;
+            __syncthreads();
+            float base = 0.f;
+            for (int x = 0; x < r16; ++x) base += gs[x * 32 + c];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = (4 * r16 + i) * kExactXS + c;
+                sk[e] = kk[i];
+                sq[e] = qq[i];
+                sg[e] = base + gg[i];
+            }
+            __syncthreads();
+            exact_accumulate(u, sk, sq, sg, kLog2e, a, pp);
+            __syncthreads();
+        }
+        exact_reduce(u, a, pp);
+        if (exact_writer(u, tid)) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int r = 4 * u.bi + x, s2 = 2 * u.bj + y;
+                    if (s2 <= r) sm.p[b][r * RS + s2] = bf(pp[x][y]);
+                    if (s2 < r) {
+                        const int I = r >> 4, J = s2 >> 4;
+                        if (I > J)
+                            sm.an[b][offdiag_index(I, J) * 16 * DS + (r & 15) * DS + (s2 & 15)] =
+                                bf(-sm.beta[b][r] * a[x][y]);
+                        else
+                            dt[I * 256 + (r & 15) * 16 + (s2 & 15)] = a[x][y];
+                    }
+                }
+        }
+        __syncthreads();
+        if (wave < 4) {
+            f32x4 av, at;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                av[i] = dt[wave * 256 + (4 * g + i) * 16 + ln];
+                at[i] = dt[wave * 256 + ln * 16 + 4 * g + i];
+            }
+            diag_inverse(sm, b, wave, av, at, g, ln);
+        }
+    };
+    auto view_of = [&](int m) {
+        return chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h, GATE);
     };
 
     if (wave >= NC) {
@@ -458,7 +568,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         //   wave 1: diagonal 1; A(1,0), A(3,1)
         //   wave 2: diagonal 2; A(2,0), A(2,1)
         //   wave 3: diagonal 3; A(3,2)
-        auto tiles4 = [](int m, int pw, int g, int ln) __attribute__((noinline)) {
+        auto tiles4 = [](int m, int pw, int g, int ln) __attribute__((always_inline)) {
             const int b = m & 1;
             const uint16_t* KG = sm.kg[b];
             const uint16_t* KN = sm.kn;
@@ -520,8 +630,10 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             stage(0);
             if (nch > 1) prefetch(1);
             __syncthreads();
-            tiles(0);
+            const bool x0 = sm.xflag[0] != 0;
+            if (!x0) tiles(0);
             if (nch > 1) totals(1);
+            if (x0) exact_chunk(0, view_of(0), H, tid, wave, g, ln);
             __syncthreads();
         }
         for (int ci = 0; ci < nch; ++ci) {
@@ -530,8 +642,10 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                 if (ci + 2 < nch) prefetch(ci + 2);
             }
             __syncthreads();
-            if (ci + 1 < nch) tiles(ci + 1);
+            const bool xn = ci + 1 < nch && sm.xflag[(ci + 1) & 1] != 0;
+            if (ci + 1 < nch && !xn) tiles(ci + 1);
             if (ci + 2 < nch) totals(ci + 2);
+            if (xn) exact_chunk((ci + 1) & 1, view_of(ci + 1), H, tid, wave, g, ln);
             __syncthreads();
         }
         return;
@@ -585,7 +699,10 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         load_v(0);
         __syncthreads();
         __syncthreads();
-        if (NP == 4) p_tiles4(0, wave, g, ln);
+        if (sm.xflag[0] != 0)
+            exact_chunk(0, view_of(0), H, tid, wave, g, ln);
+        else if (NP == 4)
+            p_tiles4(0, wave, g, ln);
         __syncthreads();
     }
     int snap_left = snapshots ? snap_tokens / C : 0;
@@ -695,7 +812,12 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                     for (int i = 0; i < 4; ++i)
                         dst[static_cast<int64_t>(16 * m + i) * DV + lp + 16 * s] = S[s][m][i];
         }
-        if (NP == 4 && ci + 1 < nch) p_tiles4(ci + 1, wave, g, ln);
+        if (ci + 1 < nch) {
+            if (sm.xflag[(ci + 1) & 1] != 0)
+                exact_chunk((ci + 1) & 1, view_of(ci + 1), H, tid, wave, g, ln);
+            else if (NP == 4)
+                p_tiles4(ci + 1, wave, g, ln);
+        }
         __syncthreads();
     }
 

@@ -111,9 +111,7 @@ enum kda_path {
     KDA_PATH_MATRIX = 2,   /* bf16 matrix cores, fp32 accumulation and
                               state, chunks of 64 tokens, one fused kernel
                               per (sequence, head, value tile); bf16 and
-                              d_k = 128; chunks whose gates leave the
-                              factored range come out NaN (see
-                              kda_fwd_prefill) */
+                              d_k = 128 */
     KDA_PATH_MATRIX_TWO_PASS = 3
                            /* the same arithmetic in two kernels: a
                               chunk-parallel pass builds each chunk's
@@ -314,16 +312,14 @@ size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H,
  * exp(g) * exp(-g) of the chunk's cumulative gate g, which stays inside
  * fp32 while |g| <= 80 (natural log).  A chunk beyond that (a channel whose
  * gates sum below -80 over the chunk, e.g. per-token gates below -1.25 on
- * the matrix paths' 64-token chunks) is handled as follows:
- *   two-pass matrix and vector paths: the chunk's decay-weighted products
- *     are summed entry by entry with their own factors exp(g_r - g_s) <= 1
- *     (the vector path from fp64 cumulative gates, and already beyond
- *     |g| = 16): exact, at a higher cost for that chunk (a two-pass
- *     prefill whose every chunk takes this form runs about 2.7x longer);
- *   fused matrix path: that chunk's outputs from the 16-token block of
- *     its first such token on, every later output of the same (sequence,
- *     head, value tile) and its final state are NaN -- never finite and
- *     wrong; request KDA_PATH_MATRIX_TWO_PASS for such gates.
+ * the matrix paths' 64-token chunks) takes the exact pairwise form on every
+ * path: its decay-weighted products are summed entry by entry with their
+ * own factors exp(g_r - g_s) <= 1 (the vector path from fp64 cumulative
+ * gates, and already beyond |g| = 16), at a higher cost for that chunk
+ * only (a two-pass prefill whose every chunk takes this form runs about
+ * 2.7x longer).  Positive log_alpha (outside the domain) is not checked;
+ * where it pushes a row beyond the range on the fused path, that row's
+ * output is NaN.
  *
  * Requirements (else the status in brackets):
  *   N >= 1, H >= 1, total_T >= 0, sizes whose byte counts fit in int64

@@ -10,9 +10,10 @@ allow (any alpha in (0, 1], "Kimi Delta Attention: la atencion lineal
 detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta Attention
 paso a paso"): -3 and -10 per token on every channel, a mix of undecayed
 and -10 channels, and per-token gates uniform in [-12, 0].  Beyond the
-factored range the two-pass and vector paths switch to the exact pairwise
-form and must match the oracle; the fused path flags such chunks with NaN
-(its outputs are either right or NaN, never finite and wrong).
+factored range every path switches to the exact pairwise form for the
+chunks concerned and must match the oracle; a further case alternates such
+chunks with ordinary ones inside each sequence (the first chunk included),
+so the switch between the two forms is exercised chunk by chunk.
 
 Batch: 200 short sequences (lengths 0..150, empty ones included, non-zero
 initial states), through each path; on the two-pass path this also walks
@@ -73,10 +74,18 @@ def gate_case(inp, case):
     elif case == "uniform_12":
         g = torch.Generator(device="cpu").manual_seed(83)
         la.copy_(-12.0 * torch.rand(la.shape, generator=g))
+    elif case == "alternating":
+        # -3 per token in the even 64-token chunks of each sequence (beyond
+        # the factored range), -0.1 in the odd ones
+        cu = inp["cu_seqlens"].cpu().tolist()
+        for n in range(len(cu) - 1):
+            for c0 in range(cu[n], cu[n + 1], 64):
+                wild = ((c0 - cu[n]) // 64) % 2 == 0
+                la[c0:min(c0 + 64, cu[n + 1])] = -3.0 if wild else -0.1
     return inp
 
 
-WIDE = ["decay_3", "decay_10", "mixed_0_10", "uniform_12"]
+WIDE = ["decay_3", "decay_10", "mixed_0_10", "uniform_12", "alternating"]
 
 
 @pytest.mark.parametrize("dtype,path", PATHS)
@@ -84,21 +93,25 @@ WIDE = ["decay_3", "decay_10", "mixed_0_10", "uniform_12"]
 def test_whole_gate_domain(dtype, path, case):
     inp = gen.prefill_inputs([300, 64, 1, 129], 2, 128, 128, dtype, "uniform", state_std=0.1,
                              seed=84, device=DEV)
-    gate_case(inp, case)
-    if path != "matrix":
-        check(inp, path, dtype, "gates %s" % case)
-        return
-    o, hT = run(inp, path)
+    check(gate_case(inp, case), path, dtype, "gates %s" % case)
+
+
+@pytest.mark.parametrize("tiles", [1, 2, 4])
+def test_fused_exact_form_every_tile_width(tiles):
+    """The fused path's exact pairwise form at each value-tile width (its
+    producer/consumer split differs with the width), on a batch with enough
+    pairs for the automatic tiling to matter."""
+    inp = gen.prefill_inputs([300, 64, 1, 129, 200], 8, 128, 128, "bf16", "uniform",
+                             state_std=0.1, seed=85, device=DEV)
+    gate_case(inp, "alternating")
+    o, hT = kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
+                        h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], path="matrix",
+                        value_tiles=tiles)
     o_ref, h_ref = oracle_prefill(inp)
-    o_h, h_h = host(o), host(hT)
-    fin_o, fin_h = np.isfinite(o_h), np.isfinite(h_h)
-    scale_o, scale_h = np.max(np.abs(o_ref)), np.max(np.abs(h_ref))
-    eo = float(np.max(np.abs(o_h[fin_o] - o_ref[fin_o]), initial=0.0)) / scale_o
-    eh = float(np.max(np.abs(h_h[fin_h] - h_ref[fin_h]), initial=0.0)) / scale_h
-    report("gates %s fused: finite entries o %.3f hT %.3f" % (case, fin_o.mean(), fin_h.mean()),
-           o=eo, hT=eh)
-    assert eo <= tol_for(dtype) and eh <= tol_for(dtype)   # never finite and wrong
-    assert not fin_o.all()                                   # the flag fired
+    eo, eh = rel_err(host(o), o_ref), rel_err(host(hT), h_ref)
+    report("fused exact form, %d value tiles" % tiles, o=eo, hT=eh)
+    assert eo <= tol_for("bf16") and eh <= tol_for("bf16")
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
 
 
 @pytest.mark.parametrize("dtype,path", PATHS)
