@@ -144,3 +144,31 @@ def test_decode_state_pool(dtype, d, gate):
     owned = set(int(slots[n]) for n in live)
     free = torch.tensor([m for m in range(M) if m not in owned], device=DEV)
     assert torch.equal(pool[free], pool0[free])
+
+
+@pytest.mark.parametrize("dtype,path,d", PATHS)
+@pytest.mark.parametrize("pattern", ["all", "alternating"])
+def test_gated_deltanet_beyond_factored_range(dtype, path, d, pattern):
+    """Gated DeltaNet with gates of -3 per token (every 64-token chunk, or
+    every other chunk of each sequence, beyond the factored form's range):
+    the exact pairwise form on every path, with the scalar gate loaded per
+    (token, head); parity with the oracle and bitwise equality with the KDA
+    call on the expanded gate."""
+    inp = inputs(dtype, d, 92)
+    g = inp["head_gate"]
+    if pattern == "all":
+        g.fill_(-3.0)
+    else:
+        cu = inp["cu_seqlens"].cpu().tolist()
+        for n in range(len(cu) - 1):
+            for c0 in range(cu[n], cu[n + 1], 64):
+                g[c0:min(c0 + 64, cu[n + 1])] = -3.0 if ((c0 - cu[n]) // 64) % 2 == 0 else -0.05
+    o, hT = run(inp, path, g, "head")
+    o_ref, h_ref = oracle_run(inp, host(g))
+    eo, eh = rel_err(host(o), o_ref), rel_err(host(hT), h_ref)
+    report("gated deltanet beyond the factored range (%s) %s %s" % (pattern, dtype, path),
+           o=eo, hT=eh)
+    assert eo <= tol_for(dtype) and eh <= tol_for(dtype)
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+    o2, hT2 = run(inp, path, g[:, :, None].expand(-1, -1, d).contiguous(), "channel")
+    assert torch.equal(o, o2) and torch.equal(hT, hT2)
