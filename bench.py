@@ -777,10 +777,18 @@ def main():
         # q, k, v, o in the input dtype, fp32 gates and beta; states in and out
         per_ht = (2 * wo.dk + 2 * wo.dv) * esz + 4 * wo.dk + 4
         nb = per_ht * To * wo.H + ho.numel() * 4 * (2 if io["h0"] is not None else 1)
+        # the chunked form's matrix work, 10 C d + 6 d^2 flops per head-token
+        # (C = 64 on the matrix paths, 32 on the fp32 vector path)
+        cc = 32 if esz == 4 else 64
+        flops = (10 * cc * wo.dk + 6 * wo.dk * wo.dv) * To * wo.H
         others[wname] = {"tokens": To, "sequences": No, "heads": wo.H, "dtype": wo.dtype,
                          "ms": o_ms, "tokens_per_s": To / (o_ms * 1e-3),
+                         "head_tokens_per_s": To * wo.H / (o_ms * 1e-3),
                          "algorithmic_bytes": nb, "achieved_GBps": nb / (o_ms * 1e-3) / 1e9,
-                         "frac_of_hbm_peak": nb / (o_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+                         "frac_of_hbm_peak": nb / (o_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                         "useful_TFLOPs": flops / (o_ms * 1e-3) / 1e12,
+                         "mfma_useful_frac": (flops / (o_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
+                                              if esz == 2 else None)}
         del io, oo, ho, wso
     torch.cuda.empty_cache()
 
@@ -803,6 +811,8 @@ def main():
         if wname in counters:
             others[wname]["kernels_avg_us"] = {k: v["avg_us"] for k, v in
                                                counters[wname]["kernels"].items()}
+            others[wname]["mfma_busy_pct"] = {k: v["mfma_busy_pct"] for k, v in
+                                              counters[wname]["kernels"].items()}
     others["tiny_f32"]["traffic"] = None
     backward["traffic"] = counted("long_t1m_backward")
     copy_gbps = copy_rate_gbps(torch)
@@ -825,12 +835,14 @@ def main():
                    "global_batch": 1, "seq_len": T, "heads": H, "d_k": 128, "d_v": 128,
                    "parallelism": "none (1 GPU)"},
         "prefill_ms": pre_avg,
+        "head_tokens_per_s": tokens_per_s * H,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "kernel": PREFILL_KERNELS, "unit_of_launch": "one kda_fwd_prefill call",
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "d2d_copy_GBps": copy_gbps,
                      "frac_of_d2d_copy": achieved / copy_gbps,
+                     "useful_TFLOPs_c64": flops_c64 / (pre_avg * 1e-3) / 1e12,
                      "mfma_useful_frac_c64": flops_c64 / (pre_avg * 1e-3) / 1e12
                      / MFMA_BF16_PEAK_TFLOPS,
                      "mfma_busy_pct": mfma},
