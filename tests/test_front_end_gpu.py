@@ -93,6 +93,29 @@ def test_prefill_front_end(parts, dtype, path, d, gate):
     assert eo <= tol_for(dtype) and eh <= tol_for(dtype)
 
 
+@pytest.mark.parametrize("dtype,path,d,gate", [("bf16", "two_pass", 128, "channel"),
+                                               ("bf16", "two_pass", 128, "head"),
+                                               ("f32", "vector", 64, "channel")])
+def test_prefill_front_end_strong_gates(dtype, path, d, gate):
+    """A gate scale of 4 (log_alpha = -4 softplus(x), about -3 per token):
+    every chunk leaves the factored range, so the front-end's gates feed the
+    exact pairwise form, which recomputes them from the pre-activations."""
+    c = 4.0
+    inp = raw_inputs(LENS, 2, d, dtype, 420, gate)
+    o, hT = kda.prefill(inp["q"], inp["k"], inp["v"], None, None, h0=inp["h0"],
+                        cu_seqlens=inp["cu_seqlens"], path=path, gate=gate, l2norm_qk=True,
+                        gate_pre=inp["gate_pre"], gate_scale=c, beta_pre=inp["beta_pre"])
+    q, k, la, beta = oracle.front_end(host(inp["q"]), host(inp["k"]), host(inp["gate_pre"]),
+                                      host(inp["beta_pre"]), gate_scale=c, l2norm=True)
+    cu = inp["cu_seqlens"].cpu().numpy().astype(np.int64)
+    o_ref, h_ref = oracle.prefill(q, k, host(inp["v"]), la, beta, h0=host(inp["h0"]),
+                                  cu_seqlens=cu)
+    eo, eh = rel_err(host(o), o_ref), rel_err(host(hT), h_ref)
+    report("front-end, gate scale %g, %s %s %s" % (c, dtype, path, gate), o=eo, hT=eh)
+    assert eo <= tol_for(dtype) and eh <= tol_for(dtype)
+    assert torch.isfinite(o).all() and torch.isfinite(hT).all()
+
+
 def test_prefill_normalisation_matches_outside():
     """Normalising in the kernel agrees with normalising outside (both within
     the bar of the oracle; not bitwise: outside, the unit rows are rounded

@@ -2,8 +2,10 @@
 its outputs equal kda_fwd_prefill_ex's on the same inputs, bit for bit,
 for each kernel path, over two calls in a row on one GPU -- the second with
 a smaller input, so it must not depend on what the first left in the
-library's device array.  The same kernels run on both entry points; only
-the workspace differs (a caller buffer vs the static array)."""
+library's device array.  The second call's first half of tokens has gates
+of -3 per token, so its chunks there take the exact pairwise form.  The
+same kernels run on both entry points; only the workspace differs (a
+caller buffer vs the static array)."""
 import pytest
 import torch
 
@@ -42,7 +44,10 @@ def test_noalloc_prefill_equals_workspace_prefill(first, second, H, dtype, path)
     for i, lens in enumerate((first, second)):
         print("[no_alloc] path=%s dtype=%s H=%d call %d: %d sequences, %d tokens"
               % (path, dtype, H, i, len(lens), sum(lens)), flush=True)
-        (o1, h1), (o2, h2) = _both(_inputs(lens, H, dtype, 700 + 10 * i + H), path)
+        inp = _inputs(lens, H, dtype, 700 + 10 * i + H)
+        if i == 1:
+            inp["log_alpha"][: sum(lens) // 2] = -3.0
+        (o1, h1), (o2, h2) = _both(inp, path)
         assert torch.equal(o1, o2), "o differs on call %d" % i
         assert torch.equal(h1, h2), "hT differs on call %d" % i
         assert torch.isfinite(o2).all() and torch.isfinite(h2).all()
