@@ -90,7 +90,9 @@ struct alignas(16) PrepSmem {
     uint16_t tok[3][C * TS];   // Kg, Kn, Qg: token rows, channels in fragment order
     float beta[C];
     float glog[DK];            // G / ln 2
-    int exact;                 // nonzero: A and P by the exact pairwise factors
+    float rho[3][DK];          // cumulative gate before row block 1, 2, 3 (log2 units)
+    int exact;                 // nonzero: A and P outside the factored form
+    int pairwise;              // nonzero: ... and a 16-row block spans beyond it too
 };
 // 53 KB: three work-groups fit in one CU's LDS.  Reuse of the token rows:
 // - tok[0] first holds the per 4-row group gate sums and then their
@@ -138,28 +140,44 @@ __device__ __forceinline__ f32x4 row_product(const uint16_t* x, const uint16_t* 
 // channels with its own factor,
 //   Araw[r][s] = sum_c k_r[c] k_s[c] e^{g_r[c] - g_s[c]}        (s <= r)
 //   P[r][s]    = sum_c q_r[c] k_s[c] e^{g_r[c] - g_s[c]}
-// on the vector units, into fp32 tables that the tile jobs read in place of
-// their matrix-core products.  Any per-token gate is then in range.
+// into fp32 tables that the tile jobs read in place of their matrix-core
+// products.  Two forms, by how far the gates go:
+// - blocked (every 16-row block's own gate span in range): the factors split
+//   at a reference gate rho_I, the cumulative gate just before row block I,
+//   e^{g_r - g_s} = e^{g_r - rho_I} e^{rho_I - g_s} for r in block I and
+//   s in block J <= I.  For J < I both factors are <= 1; for J = I the
+//   second is at most e^{the block's span}, in range by the condition.  So
+//   the tiles of row block I are again matrix-core products, of
+//   X_I = K_I e^{g - rho_I} (and Q_I e^{g - rho_I}) with
+//   Y_J^(I) = K_J e^{rho_I - g}, staged as bf16 32 channels at a time;
+// - pairwise (otherwise): each entry summed over the channels with its own
+//   factor on the vector units (kda_exact.h).
+// Any per-token gate is then in range.
 constexpr float kSafeLog2 = 115.f;
 constexpr int XS = kExactXS;    // fp32 stride of the staged 32-channel rows
 constexpr int AS = C + 1;       // fp32 stride of the 64 x 64 tables
+
+constexpr int BRS = 40;         // bf16 stride of the blocked form's staged rows (32 channels)
+static_assert((2 * C + 160) * BRS * sizeof(uint16_t) <= 2 * C * TS * sizeof(uint16_t),
+              "the blocked form's staged rows fit in tok[1..2]");
 
 __device__ __forceinline__ float* table_a(PrepSmem& sm) { return reinterpret_cast<float*>(sm.tok[1]); }
 __device__ __forceinline__ float* table_p(PrepSmem& sm) { return reinterpret_cast<float*>(sm.tok[1]) + C * AS; }
 static_assert(2 * C * AS * sizeof(float) <= 2 * C * TS * sizeof(uint16_t), "the tables fit in tok[1..2]");
 static_assert(3 * C * XS * sizeof(float) <= 2 * C * TS * sizeof(uint16_t), "a staged round fits in tok[1..2]");
 
-// The work split is kda_exact.h's.  Per round of 32 channels the threads
-// that own them (cg / 8 == round) reload their 4 rows x 4 channels
-// of k and q (normalised by nk, nq when the front-end asks) and their gates
-// from L2, stage k, q and the cumulative gates (log2 units: off plus the
-// sum within the thread's 4 rows) as rows of XS floats, and rewrite their
-// part of Kd^T in the slot with e^{G - g} as one exponential (the common
-// path's e^{G} e^{-g} may overflow here).  Called by every thread after a
-// barrier that ends all reads of tok[1..2]; returns after the barrier that
-// publishes the tables.  Its loops stay rolled: a small register
-// footprint keeps the common path's allocation as it is.
-template <int GATE, bool FRONT>
+// Every thread reloads its 4 rows x 4 channels of k and q (normalised by
+// nk, nq when the front-end asks) and their gates from L2 once, and rewrites
+// its part of Kd^T in the slot with e^{G - g} as one exponential (the common
+// path's e^{G} e^{-g} may overflow here).  Then, in 4 rounds of 32 channels,
+// BLOCKED: the threads stage X, Q X and the Y^(I) as bf16 rows of BRS, and
+// wave w accumulates the A and P tiles w, w + 8, w + 16 (of 20) with one
+// matrix-core step per round.  Otherwise they stage k, q and the cumulative
+// gates as rows of XS floats for kda_exact.h's pairwise sums.  Called by every thread after a barrier that ends all reads of
+// tok[1..2]; returns after the barrier that publishes the tables.  Its
+// loops stay rolled: a small register footprint keeps the common path's
+// allocation as it is.
+template <int GATE, bool FRONT, bool BLOCKED>
 __device__ __forceinline__
 void exact_ap_tables(PrepSmem& sm, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                      const float* __restrict__ log_alpha, const uint16_t* __restrict__ gate_pre,
@@ -173,87 +191,163 @@ void exact_ap_tables(PrepSmem& sm, const bf16_t* __restrict__ q, const bf16_t* _
     float* sk = reinterpret_cast<float*>(sm.tok[1]);
     float* sq = sk + C * XS;
     float* sg = sq + C * XS;
+    // blocked form: bf16 rows of 32 channels (X, Q X, then Y^(I) for I = 0..3,
+    // 16 (I + 1) rows each)
+    uint16_t* bx = sm.tok[1];
+    uint16_t* bqx = bx + C * BRS;
+    uint16_t* by = bqx + C * BRS;
+    const int wave = tid >> 6, g = lane >> 4, ln = lane & 15;
+    f32x4 acc[3];
+#pragma unroll
+    for (int x = 0; x < 3; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
     const ExactUnit u = exact_unit(tid);
     float a[4][2], pp[4][2];
 #pragma unroll
     for (int x = 0; x < 4; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y) a[x][y] = pp[x][y] = 0.f;
-#pragma unroll 1
-    for (int round = 0; round < 4; ++round) {          // channels 32 round .. +31
-        if (round > 0) __syncthreads();                 // the last round's reads are done
-        if ((cg >> 3) == round) {
-            const int64_t e0 = (c0 * H + h) * DK;
-            const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
-            float gsum[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * rg + i;
-                f32x4 la;
-                if (FRONT && gate_pre) {
-                    if constexpr (GATE == kGateChannel) {
-                        const u32x2 w = ld64(rsrc(gate_pre + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
-                        la = f32x4{-gate_scale * softplus_f32(lo_bf(w[0])),
-                                   -gate_scale * softplus_f32(hi_bf(w[0])),
-                                   -gate_scale * softplus_f32(lo_bf(w[1])),
-                                   -gate_scale * softplus_f32(hi_bf(w[1]))};
-                    } else {
-                        const float x = -gate_scale * softplus_f32(bf16_to_f32(ld16(
-                            rsrc(gate_pre + c0 * H + h, 2u * static_cast<uint32_t>((len - 1) * H + 1)),
-                            2 * r * H)));
-                        la = f32x4{x, x, x, x};
-                    }
-                    if (r >= len) la = f32x4{0.f, 0.f, 0.f, 0.f};
-                } else if constexpr (GATE == kGateChannel) {
-                    la = __builtin_bit_cast(f32x4, ld128(rsrc(log_alpha + e0, 4u * span),
-                                                         4 * (r * H * DK + 4 * cg)));
+    // this thread's 4 rows x 4 channels, loaded once: k and q as bf16 (each
+    // row's 4 channels in one 64-bit word, channel j in bits 16j..) and the
+    // cumulative gates in log2 units (off plus the sum within the 4 rows)
+    uint64_t kw[4], qw[4];
+    f32x4 gl[4];
+    {
+        const int64_t e0 = (c0 * H + h) * DK;
+        const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
+        f32x4 la[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            if (FRONT && gate_pre) {
+                if constexpr (GATE == kGateChannel) {
+                    const u32x2 w = ld64(rsrc(gate_pre + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
+                    la[i] = f32x4{-gate_scale * softplus_f32(lo_bf(w[0])),
+                                  -gate_scale * softplus_f32(hi_bf(w[0])),
+                                  -gate_scale * softplus_f32(lo_bf(w[1])),
+                                  -gate_scale * softplus_f32(hi_bf(w[1]))};
                 } else {
-                    const float x = log_alpha
-                        ? __uint_as_float(ld32(rsrc(log_alpha + c0 * H + h,
-                                                    4u * static_cast<uint32_t>((len - 1) * H + 1)),
-                                               4 * r * H))
-                        : 0.f;
-                    la = f32x4{x, x, x, x};
+                    const float x = -gate_scale * softplus_f32(bf16_to_f32(ld16(
+                        rsrc(gate_pre + c0 * H + h, 2u * static_cast<uint32_t>((len - 1) * H + 1)),
+                        2 * r * H)));
+                    la[i] = f32x4{x, x, x, x};
                 }
-                const u32x2 kw = ld64(rsrc(k + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
-                const u32x2 qw = ld64(rsrc(q + e0, 2u * span), 2 * (r * H * DK + 4 * cg));
-                float kd[4];
+                if (r >= len) la[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            } else if constexpr (GATE == kGateChannel) {
+                la[i] = __builtin_bit_cast(f32x4, ld128(rsrc(log_alpha + e0, 4u * span),
+                                                        4 * (r * H * DK + 4 * cg)));
+            } else {
+                const float x = log_alpha
+                    ? __uint_as_float(ld32(rsrc(log_alpha + c0 * H + h,
+                                                4u * static_cast<uint32_t>((len - 1) * H + 1)),
+                                           4 * r * H))
+                    : 0.f;
+                la[i] = f32x4{x, x, x, x};
+            }
+            kw[i] = __builtin_bit_cast(uint64_t, ld64(rsrc(k + e0, 2u * span), 2 * (r * H * DK + 4 * cg)));
+            qw[i] = __builtin_bit_cast(uint64_t, ld64(rsrc(q + e0, 2u * span), 2 * (r * H * DK + 4 * cg)));
+        }
+        f32x4 gsum = {0.f, 0.f, 0.f, 0.f};
+        float kd[4][4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    gsum[j] = __builtin_fmaf(la[j], kLog2e, gsum[j]);
-                    const float gl = off[j] + gsum[j];
-                    float kx = (j & 1) ? hi_bf(kw[j >> 1]) : lo_bf(kw[j >> 1]);
-                    float qx = (j & 1) ? hi_bf(qw[j >> 1]) : lo_bf(qw[j >> 1]);
-                    if constexpr (FRONT) {
-                        kx *= nk[i];
-                        qx *= nq[i];
-                    }
-                    const int e = r * XS + 4 * (cg & 7) + j;
-                    sk[e] = kx;
-                    sq[e] = qx;
-                    sg[e] = gl;
-                    kd[j] = kx * __builtin_amdgcn_exp2f(sm.glog[4 * cg + j] - gl);
-                }
-                // Kd^T as the A operand of pass 2 (the common path's layout)
-                const int x0 = 4 * rg;
+        for (int i = 0; i < 4; ++i) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int c = 4 * cg + j;
-                    const int fl = 16 * ((x0 & 15) >> 2) + (c & 15);
-                    reinterpret_cast<uint16_t*>(out + (kFragK + 2 * (c >> 4) + (x0 >> 5)) * kFrag +
-                                                fl * 16 + 8 * ((x0 & 31) >> 4))[i] =
-                        static_cast<uint16_t>(pk(kd[j], 0.f) & 0xffffu);
-                }
+            for (int j = 0; j < 4; ++j) {
+                gsum[j] = __builtin_fmaf(la[i][j], kLog2e, gsum[j]);
+                gl[i][j] = off[j] + gsum[j];
+                float kx = lo_bf(static_cast<uint32_t>(kw[i] >> (16 * j)));
+                if constexpr (FRONT) kx *= nk[i];
+                kd[i][j] = kx * __builtin_amdgcn_exp2f(sm.glog[4 * cg + j] - gl[i][j]);
             }
         }
-        __syncthreads();
-        exact_accumulate(u, sk, sq, sg, 1.f, a, pp);
+        // Kd^T as the A operand of pass 2 (the common path's layout)
+        const int x = 4 * rg;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 4 * cg + j;
+            const int fl = 16 * ((x & 15) >> 2) + (c & 15);
+            *reinterpret_cast<u32x2*>(out + (kFragK + 2 * (c >> 4) + (x >> 5)) * kFrag + fl * 16 +
+                                      8 * ((x & 31) >> 4)) =
+                u32x2{pk(kd[0][j], kd[1][j]), pk(kd[2][j], kd[3][j])};
+        }
     }
-    exact_reduce(u, a, pp);
+    // round j takes channel 4 cg + j of every thread (column cg of the staged
+    // rows): any split of the channels into 4 sets of 32 sums to the same
+    // tables, and this one keeps every thread busy in every round.  After a
+    // round each thread's words and gates move down by one channel.
+#pragma unroll 1
+    for (int round = 0; round < 4; ++round) {
+        if (round > 0) __syncthreads();                 // the last round's reads are done
+        const int ch = 4 * cg + round;
+        float rho[3];
+        if constexpr (BLOCKED) {
+#pragma unroll
+            for (int I = 0; I < 3; ++I) rho[I] = sm.rho[I][ch];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * rg + i;
+            float kx = lo_bf(static_cast<uint32_t>(kw[i]));
+            float qx = lo_bf(static_cast<uint32_t>(qw[i]));
+            if constexpr (FRONT) {
+                kx *= nk[i];
+                qx *= nq[i];
+            }
+            const float gr = gl[i][0];
+            if constexpr (BLOCKED) {
+                const int Ir = rg >> 2;                 // the row block of all 4 rows
+                const float f = __builtin_amdgcn_exp2f(gr - (Ir == 0 ? 0.f : rho[Ir - 1]));
+                bx[r * BRS + cg] = bf(kx * f);
+                bqx[r * BRS + cg] = bf(qx * f);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    if (I < Ir) continue;
+                    const float rI = I == 0 ? 0.f : rho[I - 1];
+                    by[(8 * I * (I + 1) + r) * BRS + cg] = bf(kx * __builtin_amdgcn_exp2f(rI - gr));
+                }
+            } else {
+                sk[r * XS + cg] = kx;
+                sq[r * XS + cg] = qx;
+                sg[r * XS + cg] = gr;
+            }
+            kw[i] >>= 16;
+            qw[i] >>= 16;
+            gl[i] = f32x4{gl[i][1], gl[i][2], gl[i][3], 0.f};
+        }
+        __syncthreads();
+        if constexpr (BLOCKED) {
+            // tiles t = wave, wave + 8, wave + 16 of the 20: A (I, J) for t < 10,
+            // P (I, J) for t >= 10, lower tiles numbered row by row
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                const int t = wave + 8 * x;
+                if (t >= 20) continue;
+                const int tt = t < 10 ? t : t - 10;
+                const int I = (tt >= 1) + (tt >= 3) + (tt >= 6), J = tt - I * (I + 1) / 2;
+                const uint16_t* xs = (t < 10 ? bx : bqx) + (16 * I + ln) * BRS + 8 * g;
+                const uint16_t* ys = by + (8 * I * (I + 1) + 16 * J + ln) * BRS + 8 * g;
+                acc[x] = mma32(*reinterpret_cast<const u32x4*>(xs), *reinterpret_cast<const u32x4*>(ys),
+                               acc[x]);
+            }
+        } else {
+            exact_accumulate(u, sk, sq, sg, 1.f, a, pp);
+        }
+    }
+    if constexpr (!BLOCKED) exact_reduce(u, a, pp);
     __syncthreads();                                    // the staged rows are dead
-    if (exact_writer(u, tid)) {
-        float* ta = table_a(sm);
-        float* tp = table_p(sm);
+    float* ta = table_a(sm);
+    float* tp = table_p(sm);
+    if constexpr (BLOCKED) {
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const int t = wave + 8 * x;
+            if (t >= 20) continue;
+            const int tt = t < 10 ? t : t - 10;
+            const int I = (tt >= 1) + (tt >= 3) + (tt >= 6), J = tt - I * (I + 1) / 2;
+            float* tab = t < 10 ? ta : tp;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tab[(16 * I + 4 * g + i) * AS + 16 * J + ln] = acc[x][i];
+        }
+    } else if (exact_writer(u, tid)) {
 #pragma unroll
         for (int x = 0; x < 4; ++x)
 #pragma unroll
@@ -380,7 +474,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     const int ln = lane & 15;
     const int cg = lane & 31;                  // staging: channels 4cg .. 4cg+3
     const int rg = 2 * wave + (lane >> 5);     //          rows 4rg .. 4rg+3
-    if (tid == 0) sm.exact = 0;
+    if (tid == 0) sm.exact = sm.pairwise = 0;
 
     // ---------------- staging loads (rows past the end read zero) ----------
     const int64_t e0 = (c0 * H + h) * DK;
@@ -490,13 +584,21 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     *reinterpret_cast<f32x4*>(scan + rg * DK + 4 * cg) = f32x4{p[3][0], p[3][1], p[3][2], p[3][3]};
     __syncthreads();
     if (tid < DK) {
-        float run = 0.f;
+        float run = 0.f, start = 0.f;
+        bool far = false;                       // a 16-row block spans beyond the range
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
+            if (x > 0 && (x & 3) == 0) {
+                sm.rho[(x >> 2) - 1][tid] = run;
+                far |= !(fabsf(run - start) <= kSafeLog2);
+                start = run;
+            }
             const float t = scan[x * DK + tid];
             scan[x * DK + tid] = run;
             run += t;
         }
+        far |= !(fabsf(run - start) <= kSafeLog2);
+        if (far) sm.pairwise = 1;
         sm.glog[tid] = run;
         reinterpret_cast<float*>(out + kOffGam)[tid] = __builtin_amdgcn_exp2f(run);
     }
@@ -579,9 +681,13 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
 
     if (exact) {
         __syncthreads();   // the copy above has read the Qg rows
-        exact_ap_tables<GATE, FRONT>(sm, q, k, log_alpha, fe.gate_pre, fe.gate_scale, c0, H, h, len,
-                                     off, f32x4{nk[0], nk[1], nk[2], nk[3]},
-                                     f32x4{nq[0], nq[1], nq[2], nq[3]}, out);
+        const f32x4 nk4{nk[0], nk[1], nk[2], nk[3]}, nq4{nq[0], nq[1], nq[2], nq[3]};
+        if (sm.pairwise)
+            exact_ap_tables<GATE, FRONT, false>(sm, q, k, log_alpha, fe.gate_pre, fe.gate_scale, c0, H, h,
+                                                len, off, nk4, nq4, out);
+        else
+            exact_ap_tables<GATE, FRONT, true>(sm, q, k, log_alpha, fe.gate_pre, fe.gate_scale, c0, H, h,
+                                               len, off, nk4, nq4, out);
     }
 
     // ---------------- A and P tiles, diagonal inverses ---------------------------

@@ -82,10 +82,31 @@ def gate_case(inp, case):
             for c0 in range(cu[n], cu[n + 1], 64):
                 wild = ((c0 - cu[n]) // 64) % 2 == 0
                 la[c0:min(c0 + 64, cu[n + 1])] = -3.0 if wild else -0.1
+    elif case == "tiers":
+        # each 64-token chunk takes one of the forms by (chunk index + sequence)
+        # mod 4: 0 factored (-0.1 per token); 1 every 16-row block in range
+        # but the chunk not (-3); 2 one block beyond the range (-10 on its
+        # rows 16..31, -0.1 elsewhere); 3 channels alternating 0 and -4.5, so
+        # 16-row blocks span 72 nats and the within-block factors are large
+        cu = inp["cu_seqlens"].cpu().tolist()
+        for n in range(len(cu) - 1):
+            for c0 in range(cu[n], cu[n + 1], 64):
+                c1 = min(c0 + 64, cu[n + 1])
+                kind = ((c0 - cu[n]) // 64 + n) % 4
+                if kind == 0:
+                    la[c0:c1] = -0.1
+                elif kind == 1:
+                    la[c0:c1] = -3.0
+                elif kind == 2:
+                    la[c0:c1] = -0.1
+                    la[c0 + 16:min(c0 + 32, c1)] = -10.0
+                else:
+                    la[c0:c1, :, 0::2] = 0.0
+                    la[c0:c1, :, 1::2] = -4.5
     return inp
 
 
-WIDE = ["decay_3", "decay_10", "mixed_0_10", "uniform_12", "alternating"]
+WIDE = ["decay_3", "decay_10", "mixed_0_10", "uniform_12", "alternating", "tiers"]
 
 
 @pytest.mark.parametrize("dtype,path", PATHS)
