@@ -97,18 +97,34 @@ struct alignas(16) Smem {
     float gam[2][DK];                  // e^{G}
     uint16_t kn[C * KS];               // K * e^{-g} (producers only)
     float2 tot[2][4 * (DK / 2)];       // gate sums of the four 16-row blocks (log2 units)
-    int xflag[2];                      // the chunk takes the exact pairwise form
+    int xflag[2];                      // the chunk's form beyond the factored range: 0 none,
+                                       // 1 blocked, 2 pairwise
 };
 
 // |g| (log2 units) up to which e^{g} and e^{-g} stay inside fp32 (e^{80}).
 // A chunk whose total gate G leaves that range on some channel (for gates
-// <= 0, |g| <= |G| on every row) takes the exact pairwise form instead: its
-// staging forms only factors <= 1 (Kg, Qg, Kd = K e^{G - g}, e^{G}; no Kn),
-// and all eight waves then sum A and P entry by entry (exact_chunk).  A row
-// whose own |g| leaves the range while G does not (only possible with
+// <= 0, |g| <= |G| on every row) takes another form instead: its staging
+// forms only factors <= 1 (Kg, Qg, Kd = K e^{G - g}, e^{G}; no Kn), and all
+// eight waves then form A and P (exact_chunk):
+// - blocked, when each 16-row block's own gate sum is in range: the decay
+//   between rows r and s (s <= r) splits at the cumulative gate rho_I before
+//   r's row block I, e^{g_r - g_s} = e^{g_r - rho_I} e^{rho_I - g_s}, so the
+//   tiles of row block I are matrix-core products of X_I = K_I e^{g - rho_I}
+//   (and Q_I e^{g - rho_I}) with Y^(I) = K e^{rho_I - g} over the rows of
+//   blocks 0..I: every factor is <= 1 except the second one inside block I,
+//   which its gate sum bounds;
+// - pairwise, otherwise: each entry summed over the channels with its own
+//   factor (kda_exact.h).
+// A row whose own |g| leaves the range while G does not (only possible with
 // positive gates, outside the domain) gets NaN in its Qg entry: never
 // finite and wrong.
 constexpr float kSafeLog2 = 115.f;
+constexpr int BRS = 40;      // bf16 stride of the blocked form's staged rows (32 channels)
+static_assert(2 * C * BRS <= C * KS && (C + 32 * 3) * BRS <= C * KS,
+              "X and Q X fit in one slot's Kg rows, the Y^(I) in its Qg rows");
+static_assert((16 * DK + 4 * 256) * sizeof(float) <= C * KS * sizeof(uint16_t),
+              "the group sums and B's diagonal blocks fit in Kn");
+static_assert(NT == 16 * 32, "one 4 x 4 block of the chunk per thread");
 
 // Byte-range views of one chunk of one head: row r of the chunk starts at
 // r * row_bytes; the range ends with the last valid row's head segment.
@@ -191,7 +207,14 @@ __device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
     const float gl0 = __builtin_amdgcn_exp2f(G0), gl1 = __builtin_amdgcn_exp2f(G1);
     if (w == 0) {
         *reinterpret_cast<float2*>(sm.gam[b] + 2 * lane) = make_float2(gl0, gl1);
-        if (lane == 0) sm.xflag[b] = exact ? 1 : 0;
+        bool span = false;                      // a 16-row block's own sum beyond the range
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const float2 t = tot[x * (DK / 2) + lane];
+            span |= !(fabsf(t.x) <= kSafeLog2 && fabsf(t.y) <= kSafeLog2);
+        }
+        const bool pairwise = __ballot(span) != 0ull;
+        if (lane == 0) sm.xflag[b] = exact ? (pairwise ? 2 : 1) : 0;
     }
     float kd0[4], kd1[4];
     if (!exact) {
@@ -439,15 +462,141 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         }
     };
 
-    // A, P and the diagonal-block inverses of the chunk in LDS slot b, in the
-    // exact pairwise form (kda_exact.h), by all eight waves.  The chunk's k,
-    // q and gates are read again (the stagers loaded them two chunks ago, so
-    // they are likely still in L2) and staged 32 channels at a time in LDS
-    // that is dead at this point: the other slot's Kg and Qg rows (the
-    // consumers read them in the first phase only) and Kn (not formed for
-    // such a chunk).  Contains barriers: every wave calls it, or none.
+    // A, P and the diagonal-block inverses of the chunk in LDS slot b beyond
+    // the factored range, by all eight waves.  The chunk's k, q and gates are
+    // read again (the stagers loaded them two chunks ago, so they are likely
+    // still in L2) and staged 32 channels at a time in LDS that is dead at
+    // this point: the other slot's Kg and Qg rows (the consumers read them in
+    // the first phase only) and Kn (not formed for such a chunk).  Contains
+    // barriers: every wave calls it, or none.
     auto exact_chunk = [](int b, ChunkView cv, int H, int tid, int wave, int g, int ln)
                            __attribute__((always_inline)) {
+        if (sm.xflag[b] == 1) {
+            // blocked form.  In each half, thread (rg, cg) loads rows
+            // 4 rg .. +3, channels 4 cg + 2 half + {0, 1} (k, q as bf16
+            // pairs), sums the gates within its row block (the 4-row group
+            // sums go through LDS), and in round j stages channel
+            // 4 cg + 2 half + j at column cg: X and Q X in the other slot's Kg
+            // rows, Y^(I), I = 0..3 (16 (I + 1) rows each) in its Qg rows.
+            // Wave w accumulates the 20 lower tiles w, w + 8, w + 16 (A, then
+            // P) with one matrix-core step per round.
+            uint16_t* bx = sm.kg[b ^ 1];
+            uint16_t* bqx = bx + C * BRS;
+            uint16_t* by = sm.qg[b ^ 1];
+            float* gs = reinterpret_cast<float*>(sm.kn);     // [16][DK] 4-row group sums
+            float* dt = gs + 16 * DK;                        // B's diagonal blocks, fp32
+            // lane coordinates as opaque values: addresses formed from them
+            // stay inside this rare branch instead of being hoisted out of
+            // the chunk loop, where they would hold registers throughout
+            int cg = tid & 31, rg = tid >> 5;
+            asm volatile("" : "+v"(cg), "+v"(rg), "+v"(g), "+v"(ln), "+v"(wave));
+            const int Ir = rg >> 2;
+            f32x4 acc[3];
+#pragma unroll
+            for (int x = 0; x < 3; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+            for (int half = 0; half < 2; ++half) {
+                uint32_t kw[4], qw[4];
+                float gw[4][2];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int off = (4 * rg + i) * H * DK + 4 * cg + 2 * half;   // elements
+                    kw[i] = ld32(cv.k, 2 * off);
+                    qw[i] = ld32(cv.q, 2 * off);
+                    if constexpr (GATE == kGateChannel) {
+                        const u32x2 l = ld64(cv.la, 4 * off);
+                        gw[i][0] = __uint_as_float(l[0]);
+                        gw[i][1] = __uint_as_float(l[1]);
+                    } else {
+                        gw[i][0] = gw[i][1] = __uint_as_float(ld32(cv.la, 4 * (4 * rg + i) * H));
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        gw[i][j] = __builtin_fmaf(gw[i][j], kLog2e, i > 0 ? gw[i - 1][j] : 0.f);
+                *reinterpret_cast<float2*>(gs + rg * DK + 4 * cg + 2 * half) = make_float2(gw[3][0], gw[3][1]);
+                __syncthreads();      // also: the last round's reads of the staged rows are done
+                {
+                    float b0 = 0.f, b1 = 0.f;           // the groups before this one in the block
+                    for (int x = 4 * Ir; x < rg; ++x) {
+                        const float2 t = *reinterpret_cast<const float2*>(gs + x * DK + 4 * cg + 2 * half);
+                        b0 += t.x;
+                        b1 += t.y;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        gw[i][0] += b0;
+                        gw[i][1] += b1;
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    // the gate sums of blocks 0..2 on this round's channel
+                    const float2* tb = sm.tot[b] + 2 * cg + half;
+                    float tt[3];
+#pragma unroll
+                    for (int x = 0; x < 3; ++x) tt[x] = j ? tb[x * (DK / 2)].y : tb[x * (DK / 2)].x;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = 4 * rg + i;
+                        const float kx = j ? hi_bf(kw[i]) : lo_bf(kw[i]);
+                        const float qx = j ? hi_bf(qw[i]) : lo_bf(qw[i]);
+                        const float gr = gw[i][j];               // g_r - rho_Ir
+                        const float f = __builtin_amdgcn_exp2f(gr);
+                        bx[r * BRS + cg] = bf(kx * f);
+                        bqx[r * BRS + cg] = bf(qx * f);
+                        float e = -gr;                           // rho_I - g_r for I = Ir, Ir + 1, ..
+#pragma unroll
+                        for (int I = 0; I < 4; ++I) {
+                            if (I < Ir) continue;
+                            by[(8 * I * (I + 1) + r) * BRS + cg] = bf(kx * __builtin_amdgcn_exp2f(e));
+                            if (I < 3) e += tt[I];
+                        }
+                    }
+                    __syncthreads();
+#pragma unroll
+                    for (int x = 0; x < 3; ++x) {
+                        const int t = wave + 8 * x;
+                        if (t >= 20) continue;
+                        const int tl = t < 10 ? t : t - 10;
+                        const int I = tile_row(tl), J = tile_col(tl);
+                        const uint16_t* xs = (t < 10 ? bx : bqx) + (16 * I + ln) * BRS + 8 * g;
+                        const uint16_t* ys = by + (8 * I * (I + 1) + 16 * J + ln) * BRS + 8 * g;
+                        acc[x] = mma32(*reinterpret_cast<const u32x4*>(xs),
+                                       *reinterpret_cast<const u32x4*>(ys), acc[x]);
+                    }
+                    if (j == 0) __syncthreads();            // the staged rows are read
+                }
+            }
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                const int t = wave + 8 * x;
+                if (t >= 20) continue;
+                const int tl = t < 10 ? t : t - 10;
+                const int I = tile_row(tl), J = tile_col(tl);
+                if (t >= 10) {
+                    put_p(sm, b, I, J, acc[x], g, ln);
+                } else if (I > J) {
+                    put_a(sm, b, I, J, acc[x], g, ln);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dt[I * 256 + (4 * g + i) * 16 + ln] = acc[x][i];
+                }
+            }
+            __syncthreads();
+            if (wave < 4) {
+                f32x4 av, at;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    av[i] = dt[wave * 256 + (4 * g + i) * 16 + ln];
+                    at[i] = dt[wave * 256 + ln * 16 + 4 * g + i];
+                }
+                diag_inverse(sm, b, wave, av, at, g, ln);
+            }
+            return;
+        }
         float* sk = reinterpret_cast<float*>(sm.kg[b ^ 1]);
         float* sq = reinterpret_cast<float*>(sm.qg[b ^ 1]);
         float* sg = reinterpret_cast<float*>(sm.kn);
