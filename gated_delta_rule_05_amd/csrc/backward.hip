@@ -168,6 +168,11 @@ __device__ __forceinline__ void mm(const bf16_t* a, int lda, const bf16_t* b, in
     }
 }
 
+// component j (a constant after unrolling) of a float4
+__device__ __forceinline__ float f4_at(const float4& v, int j) {
+    return j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+}
+
 // store 4 values of one column, rows r0..r0+3, into a transposed bf16
 // matrix (row = column index): one 8-byte LDS or global store
 __device__ __forceinline__ void put4t(bf16_t* p, f32x4 x) {
@@ -300,11 +305,13 @@ struct alignas(16) PrepLds {
         float bm[C * (C + 1)];
     } u2;
     float bs[C];
-    int wild;
+    int wild;                  // beyond the factored range ...
+    int pairwise;              // ... and a 16-row block's own gate sum beyond it too
 };
 
 // |g| (natural log units) up to which e^{g} and e^{-g} stay inside fp32
 constexpr float kSafeGate = 80.f;
+constexpr int BRS = 40;        // bf16 stride of the blocked form's staged rows (32 channels)
 
 template <int GATE>
 __global__ __launch_bounds__(GT, 2)
@@ -334,9 +341,17 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     load_rows4(q, c, H, qr4);
     float g[4][4];
     f32x4 G;
-    if (tid == 0) sm.wild = 0;
+    if (tid == 0) sm.wild = sm.pairwise = 0;
     chunk_gates<GATE>(la, beta, c, H, sm.u2.a.scan, sm.u2.a.tot, sm.bs, g, G);
-    if (tid < D) oGam[tid] = gate_exp(sm.u2.a.tot[tid]);
+    if (tid < D) {
+        oGam[tid] = gate_exp(sm.u2.a.tot[tid]);
+        // the gate sums of the four 16-row blocks on channel tid
+        const float r1 = sm.u2.a.scan[4 * D + tid], r2 = sm.u2.a.scan[8 * D + tid];
+        const float r3 = sm.u2.a.scan[12 * D + tid], gt = sm.u2.a.tot[tid];
+        const bool far = !(fabsf(r1) <= kSafeGate && fabsf(r2 - r1) <= kSafeGate &&
+                           fabsf(r3 - r2) <= kSafeGate && fabsf(gt - r3) <= kSafeGate);
+        if (far) sm.pairwise = 1;
+    }
     {
         // the factored form's range: a chunk beyond it takes the exact form
         // for B and P below (Kg, Qg, Kd and gamma are in range either way)
@@ -389,11 +404,84 @@ void bwd_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
             for (int i = 0; i < 4; ++i) x[i] = s <= r0 + i ? scale * acc[i] : 0.f;
             put4t(oPt + s * C + r0, x);
         });
-    } else {
+    } else if (!sm.pairwise) {
         // The chunk's gates leave the factored form's range (K e^-g
-        // overflows): B and P entry by entry, each with its own factor
-        // e^{g_r - g_s} <= 1 (kda_exact.h), from the raw k, q and gates
-        // staged 32 channels at a time in the dead K e^-g / Q e^g rows.
+        // overflows) but each 16-row block's own sum stays in it: the decay
+        // between rows r and s (s <= r) splits at the cumulative gate rho_I
+        // before r's row block I, e^{g_r - g_s} = e^{g_r - rho_I} e^{rho_I - g_s},
+        // so B and P are again matrix-core products, of X_I = K_I e^{g - rho_I}
+        // (and Q_I e^{g - rho_I}) with Y^(I) = K e^{rho_I - g} over the rows of
+        // blocks 0..I; every factor is <= 1 except the second one inside
+        // block I, which the block's sum bounds.  Per round of 32 channels
+        // thread (rg, cg) stages channel 4 cg + round of its 4 rows as bf16
+        // in the dead K e^-g / Q e^g rows; wave w accumulates the 20 lower
+        // tiles w, w + 8, w + 16 (B, then P).
+        static_assert((2 * C + 160) * BRS * sizeof(uint16_t) <= sizeof(sm.u1.a),
+                      "the staged rows fit the dead rows");
+        uint16_t* bx = reinterpret_cast<uint16_t*>(&sm.u1.a);
+        uint16_t* bqx = bx + C * BRS;
+        uint16_t* by = bqx + C * BRS;
+        const int wave = tid >> 6, Ir = rg >> 2;
+        // rho_1..3 on the thread's channels (read before B overwrites the scan)
+        f32x4 rho[3];
+#pragma unroll
+        for (int I = 0; I < 3; ++I) rho[I] = *reinterpret_cast<const f32x4*>(sm.u2.a.scan + 4 * (I + 1) * D + 4 * cg);
+        f32x4 acc[3];
+#pragma unroll
+        for (int x = 0; x < 3; ++x) acc[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int round = 0; round < 4; ++round) {
+            if (round > 0) __syncthreads();            // the last round's reads are done
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * rg + i;
+                const float kx = f4_at(kr4[i], round), qx = f4_at(qr4[i], round);
+                const float gv = g[i][round];
+                const float f = gate_exp(gv - (Ir == 0 ? 0.f : rho[Ir - 1][round]));
+                bx[r * BRS + cg] = bf(kx * f);
+                bqx[r * BRS + cg] = bf(qx * f);
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    if (I < Ir) continue;
+                    const float rI = I == 0 ? 0.f : rho[I - 1][round];
+                    by[(8 * I * (I + 1) + r) * BRS + cg] = bf(kx * gate_exp(rI - gv));
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < 3; ++x) {
+                const int t = wave + 8 * x;
+                if (t >= 20) continue;
+                const int tl = t < 10 ? t : t - 10;
+                const int I = (tl >= 1) + (tl >= 3) + (tl >= 6), J = tl - I * (I + 1) / 2;
+                const uint16_t* xs = (t < 10 ? bx : bqx) + (16 * I + ln) * BRS + 8 * g4;
+                const uint16_t* ys = by + (8 * I * (I + 1) + 16 * J + ln) * BRS + 8 * g4;
+                acc[x] = mma32(*reinterpret_cast<const u32x4*>(xs), *reinterpret_cast<const u32x4*>(ys),
+                               acc[x]);
+            }
+        }
+        __syncthreads();                       // the staged rows are dead
+        float* ptab = reinterpret_cast<float*>(&sm.u1.a);   // P, [C][C + 1]
+#pragma unroll
+        for (int x = 0; x < 3; ++x) {
+            const int t = wave + 8 * x;
+            if (t >= 20) continue;
+            const int tl = t < 10 ? t : t - 10;
+            const int I = (tl >= 1) + (tl >= 3) + (tl >= 6), J = tl - I * (I + 1) / 2;
+            float* tab = t < 10 ? sm.u2.bm : ptab;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) tab[(16 * I + 4 * g4 + i) * (C + 1) + 16 * J + ln] = acc[x][i];
+        }
+        __syncthreads();
+        for (int idx = tid; idx < C * C; idx += GT) {
+            const int s = idx / C, r = idx % C;
+            oPt[s * C + r] = bf(s <= r ? scale * ptab[r * (C + 1) + s] : 0.f);
+        }
+    } else {
+        // ... and a 16-row block's own sum leaves it too: B and P entry by
+        // entry, each with its own factor e^{g_r - g_s} <= 1 (kda_exact.h),
+        // from the raw k, q and gates staged 32 channels at a time in the
+        // dead K e^-g / Q e^g rows.
         static_assert(GT == kExactThreads, "one exact unit per thread");
         static_assert(3 * C * kExactXS * sizeof(float) <= sizeof(sm.u1.a) &&
                           C * (C + 1) * sizeof(float) <= sizeof(sm.u1.a),
@@ -704,6 +792,8 @@ void bwd_carry_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restric
 // contracts over its rows with transpose reads (kMc).
 // ===================================================================
 constexpr int LDT = D + 16;    // rows read only by transpose reads: a row step of 8 banks
+constexpr int LDG = D + 4;     // fp32 row stride of the gates: rows 4 banks apart, so 16
+                               // lanes reading one channel of 16 rows hit 16 banks
 
 struct alignas(16) GradALds {
     bf16_t st[D * LDD];        // S^T [value j][key c] (the recorded layout)
@@ -717,7 +807,7 @@ struct alignas(16) GradALds {
     float dgp[GG / D][D];      // dgamma over eight parts of the value columns
 };
 struct alignas(16) GradBLds {
-    float g[C * D];            // cumulative gates
+    float g[C * LDG];          // cumulative gates
     bf16_t kg[C * LDT], kn[C * LDT], qg[C * LDT];   // gated keys and queries, row-major
     bf16_t mv[C * LDC];        // Minv
     bf16_t dp[C * LDC];        // dP
@@ -771,11 +861,12 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 {
     __shared__ GradLds sm_u;
     __shared__ float s_dgam[D], s_dbT[4][C];   // phase A -> phase B
-    __shared__ int s_wild;                     // the chunk takes the exact form
+    __shared__ int s_wild;                     // the chunk is beyond the factored range ...
+    __shared__ int s_pair;                     // ... and a 16-row block's own gate sum too
     ChunkRef c;
     if (!chunk_of(blockIdx.x, H, c_lo, L_b, cu, c)) return;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g4 = lane >> 4, ln = lane & 15;
-    if (tid == 0) s_wild = 0;
+    if (tid == 0) s_wild = s_pair = 0;
     const uint8_t* sp = slots + c.slot * static_cast<int64_t>(kSlot);
     const float* mvg = reinterpret_cast<const float*>(sp + kOffMinv);
     const float* S0f = c.j == 0 && h0 ? h0 + (static_cast<int64_t>(c.n) * H + c.h) * kState
@@ -943,6 +1034,14 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             }
             if (wild) s_wild = 1;
         }
+        if (tid < D) {
+            // the gate sums of the four 16-row blocks on channel tid
+            const float r1 = sm.gscan[4 * D + tid], r2 = sm.gscan[8 * D + tid];
+            const float r3 = sm.gscan[12 * D + tid], gt = sm.gtot[tid];
+            const bool far = !(fabsf(r1) <= kSafeGate && fabsf(r2 - r1) <= kSafeGate &&
+                               fabsf(r3 - r2) <= kSafeGate && fabsf(gt - r3) <= kSafeGate);
+            if (far) s_pair = 1;
+        }
         // the gates for the final tiles, and the gated keys and queries
         // (one thread per 4 x 4 block of the chunk)
         if (tid < GT) {
@@ -950,7 +1049,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * rg + i;
-                *reinterpret_cast<f32x4*>(sm.g + r * D + c0) = f32x4{gr[i][0], gr[i][1], gr[i][2], gr[i][3]};
+                *reinterpret_cast<f32x4*>(sm.g + r * LDG + c0) = f32x4{gr[i][0], gr[i][1], gr[i][2], gr[i][3]};
                 const float kk[4] = {lo_bf(kraw[i][0]), hi_bf(kraw[i][0]), lo_bf(kraw[i][1]),
                                      hi_bf(kraw[i][1])};
                 const float qq[4] = {lo_bf(qraw[i][0]), hi_bf(qraw[i][0]), lo_bf(qraw[i][1]),
@@ -1013,20 +1112,60 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
         __syncthreads();
     }
     // B = Kg Kn^T at this wave's dA tile (for dbeta_A; the prep's inverse
-    // used the same bf16 operands and product order, or the same exact form)
+    // used the same bf16 operands and product order, or the same form beyond
+    // the factored range)
     f32x4 bmt[1];
     if (!exact) {
         mm_regs<4, D, 1, GG>(sm.kg, LDT, sm.kn, LDT, bmt);
+    } else if (!s_pair) {
+        // the prep's blocked form: per round j, X = K e^{g - rho_I} and the
+        // Y^(I) = K e^{rho_I - g} of channels 4 c + j at column c, bf16, from
+        // the same gate bits (rho_I: the scan's prefix before row block I),
+        // in the dead gated-key rows; thread (r, cp) stages row r, columns
+        // 2 cp and 2 cp + 1
+        static_assert((C + 160) * BRS <= C * LDT && GG == C * 16, "the staged rows; one row per 16 threads");
+        uint16_t* bx = sm.kg;
+        uint16_t* by = sm.kg + C * BRS;
+        // lane coordinates as opaque values: no address of this rare branch
+        // is hoisted to where it would hold registers on the common path
+        int r = tid >> 4, cp = tid & 15, w = wave, l16 = ln, gq = g4;
+        asm volatile("" : "+v"(r), "+v"(cp), "+v"(w), "+v"(l16), "+v"(gq));
+        const int Ir = r >> 4, mi = w / 4, ni = w % 4;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int round = 0; round < 4; ++round) {
+            if (round > 0) __syncthreads();            // the last round's reads are done
+#pragma unroll 1
+            for (int e = 0; e < 2; ++e) {
+                const int col = 2 * cp + e, ch = 4 * col + round;
+                const float kx = bf16_to_f32(sm.kn[r * LDT + ch]);
+                const float gv = sm.g[r * LDG + ch];
+                const float ref = Ir == 0 ? 0.f : sm.gscan[4 * Ir * D + ch];
+                bx[r * BRS + col] = bf(kx * gate_exp(gv - ref));
+#pragma unroll
+                for (int I = 0; I < 4; ++I) {
+                    if (I < Ir) continue;
+                    const float rI = I == 0 ? 0.f : sm.gscan[4 * I * D + ch];
+                    by[(8 * I * (I + 1) + r) * BRS + col] = bf(kx * gate_exp(rI - gv));
+                }
+            }
+            __syncthreads();
+            if (ni <= mi)
+                acc = mma32(*reinterpret_cast<const u32x4*>(bx + (16 * mi + l16) * BRS + 8 * gq),
+                            *reinterpret_cast<const u32x4*>(by + (8 * mi * (mi + 1) + 16 * ni + l16) * BRS + 8 * gq),
+                            acc);
+        }
+        bmt[0] = acc;
     } else {
         const int mi = wave / 4, s = 16 * (wave % 4) + ln;
         bmt[0] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 2
         for (int c2 = 0; c2 < D; ++c2) {
-            const float ks = bf16_to_f32(sm.kn[s * LDT + c2]), gs = sm.g[s * D + c2];
+            const float ks = bf16_to_f32(sm.kn[s * LDT + c2]), gs = sm.g[s * LDG + c2];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * mi + 4 * g4 + i;
-                const float e = __builtin_amdgcn_exp2f((sm.g[r * D + c2] - gs) * kLog2e);
+                const float e = __builtin_amdgcn_exp2f((sm.g[r * LDG + c2] - gs) * kLog2e);
                 bmt[0][i] += s < r ? bf16_to_f32(sm.kn[r * LDT + c2]) * ks * e : 0.f;
             }
         }
@@ -1072,7 +1211,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
     // dKn = dP^T Qg + dB^T Kg, dQg = dQg_S + dP Kn, then the gate chain;
     // the B fragments of Kn, Kg and Qg (read by rows of K) serve both of
     // the wave's tiles
-    const float G = sm.g[(c.len - 1) * D + ch];
+    const float G = sm.g[(c.len - 1) * LDG + ch];
     float dgr[2][4];          // dg of rows 16 mi + 4 g4 + i, this lane's channel
     float dGp = 0.f;
     if (!exact) {
@@ -1103,7 +1242,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 const int r = 16 * mi + 4 * g4 + i;
                 float dgv = 0.f;
                 if (r < c.len) {
-                    const float gv = sm.g[r * D + ch];
+                    const float gv = sm.g[r * LDG + ch];
                     const float eg = gate_exp(gv), en = gate_exp(-gv), ed = gate_exp(G - gv);
                     const float dKg = aKg[i] + rKgW[x][i];
                     const float dQg = aQg[i] + rQgS[x][i];
@@ -1136,13 +1275,13 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
             float gr4[4], fk[4], fq[4], gsum[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                gr4[i] = sm.g[(16 * mi + 4 * g4 + i) * D + ch];
+                gr4[i] = sm.g[(16 * mi + 4 * g4 + i) * LDG + ch];
                 fk[i] = fq[i] = gsum[i] = 0.f;
             }
 #pragma unroll 2
             for (int s2 = 0; s2 < C; ++s2) {
                 const float ks = bf16_to_f32(sm.kn[s2 * LDT + ch]), qs = bf16_to_f32(sm.qg[s2 * LDT + ch]);
-                const float gs = sm.g[s2 * D + ch];
+                const float gs = sm.g[s2 * LDG + ch];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int r = 16 * mi + 4 * g4 + i;
@@ -1238,7 +1377,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
 #pragma unroll
             for (int i = 3; i >= 0; --i) {
                 run += dgr[x][i];
-                if constexpr (GATE == kGateChannel) sm.g[(16 * mi + 4 * g4 + i) * D + ch] = run;
+                if constexpr (GATE == kGateChannel) sm.g[(16 * mi + 4 * g4 + i) * LDG + ch] = run;
                 else out[x][i] = run;
             }
         }
@@ -1249,7 +1388,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 const int u = tid + GG * x, r = u / (D / 4), c4 = (u % (D / 4)) * 4;
                 if (r < c.len)
                     *reinterpret_cast<f32x4*>(dla + ((c.t0 + r) * H + c.h) * D + c4) =
-                        *reinterpret_cast<const f32x4*>(sm.g + r * D + c4);
+                        *reinterpret_cast<const f32x4*>(sm.g + r * LDG + c4);
             }
         } else {
             // one gate per (token, head) reaches every key channel: the sum

@@ -86,16 +86,37 @@ def test_backward_parity(gate):
     compare("backward %s" % gate, gpu(inp, gate), ref(inp))
 
 
-@pytest.mark.parametrize("case", ["decay_1", "decay_3", "decay_10", "mixed_0_10", "uniform_12"])
+@pytest.mark.parametrize("case", ["decay_1", "decay_3", "decay_10", "mixed_0_10", "uniform_12", "tiers"])
 def test_backward_gate_domain(case):
     """The whole gate domain the pages allow (any alpha in (0, 1]): -1 per
     token keeps a 64-token chunk inside the factored form's range (its gates
-    sum to -64); -3 and -10 per token, a mix of undecayed and -10 channels,
-    and gates uniform in [-12, 0] leave it, and those chunks take the exact
-    pairwise form.  Every gradient must match the oracle and be finite."""
+    sum to -64); -3 per token leaves it with every 16-row block inside (the
+    blocked form); -10 per token, a mix of undecayed and -10 channels, and
+    gates uniform in [-12, 0] leave it by 16-row blocks too (the pairwise
+    form); "tiers" mixes the three forms chunk by chunk.  Every gradient must
+    match the oracle and be finite."""
     inp = make_case(LENS, 2, 390)
     la = inp["log_alpha"]
-    if case == "decay_1":
+    if case == "tiers":
+        # by (chunk index + sequence) mod 4: -0.1 (factored), -3 (blocked),
+        # -10 on rows 16..31 only (pairwise), channels alternating 0 and
+        # -4.5 (blocked, with 16-row blocks spanning 72 nats)
+        cu = inp["cu_seqlens"].cpu().tolist()
+        for n in range(len(cu) - 1):
+            for c0 in range(cu[n], cu[n + 1], 64):
+                c1 = min(c0 + 64, cu[n + 1])
+                kind = ((c0 - cu[n]) // 64 + n) % 4
+                if kind == 0:
+                    la[c0:c1] = -0.1
+                elif kind == 1:
+                    la[c0:c1] = -3.0
+                elif kind == 2:
+                    la[c0:c1] = -0.1
+                    la[c0 + 16:min(c0 + 32, c1)] = -10.0
+                else:
+                    la[c0:c1, :, 0::2] = 0.0
+                    la[c0:c1, :, 1::2] = -4.5
+    elif case == "decay_1":
         la.fill_(-1.0)
     elif case == "decay_3":
         la.fill_(-3.0)
