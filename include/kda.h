@@ -312,14 +312,18 @@ size_t kda_fwd_prefill_workspace_bytes_ex(int64_t total_T, int32_t N, int32_t H,
  * exp(g) * exp(-g) of the chunk's cumulative gate g, which stays inside
  * fp32 while |g| <= 80 (natural log).  A chunk beyond that (a channel whose
  * gates sum below -80 over the chunk, e.g. per-token gates below -1.25 on
- * the matrix paths' 64-token chunks) takes the exact pairwise form on every
- * path: its decay-weighted products are summed entry by entry with their
- * own factors exp(g_r - g_s) <= 1 (the vector path from fp64 cumulative
- * gates, and already beyond |g| = 16), at a higher cost for that chunk
- * only (a two-pass prefill whose every chunk takes this form runs about
- * 2.7x longer).  Positive log_alpha (outside the domain) is not checked;
- * where it pushes a row beyond the range on the fused path, that row's
- * output is NaN.
+ * the matrix paths' 64-token chunks) takes another form for its
+ * decay-weighted products, at a higher cost for that chunk only:
+ *  - on the matrix paths, when each 16-row block of the chunk keeps its own
+ *    gate sum within 80: the blocked form, matrix-core products again, with
+ *    the decays factored through the cumulative gate before each row block
+ *    (a two-pass prefill whose every chunk takes it runs about 1.3x longer,
+ *    a fused one about 1.9x);
+ *  - otherwise (and on the vector path, already beyond |g| = 16, from fp64
+ *    cumulative gates): the exact pairwise form, each entry summed with its
+ *    own factors exp(g_r - g_s) <= 1 (about 2.2x to 7x longer).
+ * Positive log_alpha (outside the domain) is not checked; where it pushes a
+ * row beyond the range on the fused path, that row's output is NaN.
  *
  * Requirements (else the status in brackets):
  *   N >= 1, H >= 1, total_T >= 0, sizes whose byte counts fit in int64
@@ -516,9 +520,12 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * Precision: bf16 matrix products with fp32 accumulation, fp32 states and
  * adjoints, as in the forward pass.  Gate range: the whole domain
  * (log_alpha <= 0, any finite value).  A chunk whose cumulative gate leaves
- * the factored form's range (|g| > 80, see kda_fwd_prefill) takes the exact
- * pairwise form for its decay-weighted products, in the operand pass and in
- * the gradient pass, at some cost in time for that chunk only.
+ * the factored form's range (|g| > 80, see kda_fwd_prefill) takes the
+ * blocked or the exact pairwise form for its decay-weighted products, as in
+ * kda_fwd_prefill, in the operand pass and in the gradient pass (whose
+ * dk, dq and dlog_alpha terms of such a chunk are always summed pairwise),
+ * at some cost in time for that chunk only (every chunk at -3 per token:
+ * about 2.8x).
  * Saved states (options->chunk_states): the record of the forward pass on
  * these inputs replaces its recomputation (the call then reads the record
  * and needs a smaller workspace); the record must come from a forward pass
