@@ -1278,6 +1278,65 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                 gr4[i] = sm.g[(16 * mi + 4 * g4 + i) * LDG + ch];
                 fk[i] = fq[i] = gsum[i] = 0.f;
             }
+            if (!s_pair) {
+                // blocked form: with rho_I the gate before row block I (this
+                // lane's channel) and the rows r of block mi,
+                //   FK, FQ = e^{g_r - rho_mi} (dB, dP)[r, :] Y,  Y[s] = k_s e^{rho_mi - g_s}
+                //     over the rows s of blocks 0..mi (zero beyond);
+                //   GS = sum_{I >= mi} e^{rho_I - g_r} (dB_{I,mi}^T X_I + dP_{I,mi}^T QX_I),
+                //     X_I[r'] = k_r' e^{g_r' - rho_I}, QX_I with q, r' in block I.
+                // Every factor is <= 1 except those inside one row block, which
+                // the block's gate sum bounds.  Each lane forms its B fragment
+                // (8 rows of its channel) in registers; the GS products take
+                // dB's rows in lane groups 0, 1 and dP's in 2, 3 (transpose
+                // reads), so one 16x16x32 step covers both terms of a block.
+                // lane coordinates as opaque values: no address of this rare
+                // branch is hoisted to where it would hold registers
+                int l16 = ln, gq = g4, cx = ch, la_ = lane, bm = mi;
+                asm volatile("" : "+v"(l16), "+v"(gq), "+v"(cx), "+v"(la_), "+v"(bm));
+                auto rho_of = [&](int I) { return I == 0 ? 0.f : sm.gscan[4 * I * D + cx]; };
+                const float rm = rho_of(bm);
+                f32x4 aK = {0.f, 0.f, 0.f, 0.f}, aQ = aK;
+#pragma unroll
+                for (int kc = 0; kc < 2; ++kc) {
+                    if (32 * kc >= 16 * (bm + 1)) continue;
+                    float yv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int s3 = 32 * kc + 8 * gq + j;
+                        yv[j] = s3 < 16 * (bm + 1)
+                                    ? bf16_to_f32(sm.kn[s3 * LDT + cx]) * gate_exp(rm - sm.g[s3 * LDG + cx])
+                                    : 0.f;
+                    }
+                    const u32x4 yb = {pk(yv[0], yv[1]), pk(yv[2], yv[3]), pk(yv[4], yv[5]), pk(yv[6], yv[7])};
+                    aK = mma32(frag<kKc>(dB + 16 * bm * LDC, LDC, 32 * kc, la_), yb, aK);
+                    aQ = mma32(frag<kKc>(sm.dp + 16 * bm * LDC, LDC, 32 * kc, la_), yb, aQ);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float f = gate_exp(gr4[i] - rm);
+                    fk[i] = aK[i] * f;
+                    fq[i] = aQ[i] * f;
+                }
+                const bf16_t* asrc = gq < 2 ? dB : sm.dp;        // dB^T or dP^T rows
+                const bf16_t* bsrc = gq < 2 ? sm.kn : sm.qg;     // k or q
+#pragma unroll 1
+                for (int I = bm; I < 4; ++I) {
+                    const float rI = rho_of(I);
+                    const int r0 = 16 * I + 8 * (gq & 1);
+                    const bf16_t* pa = asrc + (r0 + (l16 >> 2)) * LDC + 16 * bm + 4 * (l16 & 3);
+                    const u32x4 af = cat(ld_tr4(pa), ld_tr4(pa + 4 * LDC));
+                    float xv[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        xv[j] = bf16_to_f32(bsrc[(r0 + j) * LDT + cx]) *
+                                gate_exp(sm.g[(r0 + j) * LDG + cx] - rI);
+                    const u32x4 xb = {pk(xv[0], xv[1]), pk(xv[2], xv[3]), pk(xv[4], xv[5]), pk(xv[6], xv[7])};
+                    const f32x4 a = mma32(af, xb, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) gsum[i] += a[i] * gate_exp(rI - gr4[i]);
+                }
+            } else {
 #pragma unroll 2
             for (int s2 = 0; s2 < C; ++s2) {
                 const float ks = bf16_to_f32(sm.kn[s2 * LDT + ch]), qs = bf16_to_f32(sm.qg[s2 * LDT + ch]);
@@ -1293,6 +1352,7 @@ void bwd_grad_kernel(const uint8_t* __restrict__ slots, const bf16_t* __restrict
                     if (s2 > r) gsum[i] += bf16_to_f32(dB[s2 * LDC + r]) * ks * e;
                     if (s2 >= r) gsum[i] += bf16_to_f32(sm.dp[s2 * LDC + r]) * qs * e;
                 }
+            }
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {

@@ -522,10 +522,9 @@ size_t kda_bwd_workspace_bytes(int64_t total_T, int32_t N, int32_t H,
  * (log_alpha <= 0, any finite value).  A chunk whose cumulative gate leaves
  * the factored form's range (|g| > 80, see kda_fwd_prefill) takes the
  * blocked or the exact pairwise form for its decay-weighted products, as in
- * kda_fwd_prefill, in the operand pass and in the gradient pass (whose
- * dk, dq and dlog_alpha terms of such a chunk are always summed pairwise),
- * at some cost in time for that chunk only (every chunk at -3 per token:
- * about 2.8x).
+ * kda_fwd_prefill, in the operand pass and in the gradient pass, at some
+ * cost in time for that chunk only (every chunk at -3 per token, blocked:
+ * about 1.3x).
  * Saved states (options->chunk_states): the record of the forward pass on
  * these inputs replaces its recomputation (the call then reads the record
  * and needs a smaller workspace); the record must come from a forward pass
