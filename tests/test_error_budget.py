@@ -22,7 +22,9 @@ and must equal the fp64 token-loop oracle to ~1e-12 (so the chunked form
 itself is pinned against the recurrence).  Each site alone, then all of
 them, give the error budget against the bar of the bf16 parity tests
 (max-relative 2e-2), at the workloads' gates and at stronger ones (-1 per
-token, inside the factored range).  The chunk, block and rounding layout
+token, inside the factored range), and for the blocked form the matrix
+paths take beyond that range (per-token gates of -3, channels alternating
+0 and -4.5).  The chunk, block and rounding layout
 follow the kernels' (C = 64, 16-row blocks); the order of fp32
 accumulations inside a product is not modelled (fp64 instead), so the
 model bounds the rounding of stored values, which dominates.
@@ -64,9 +66,31 @@ def diag_inverse(N, on):
     return rb(Z3, on)
 
 
-def chunk_model(q, k, v, la, beta, S, scale, s):
+def blocked_products(q, k, g, on):
+    """B = [k_r . (k_s e^{g_r - g_s})] and Pq = [q_r . (k_s e^{g_r - g_s})] for
+    s in the row blocks up to r's, by the blocked form: the decay between r
+    (block I) and s splits at rho_I, the cumulative gate before block I, into
+    X_I = K_I e^{g - rho_I} (Q_I for Pq) and Y^(I) = K e^{rho_I - g} over the
+    rows of blocks 0..I, each rounded to bf16 when `on` (the kernels'
+    operands).  Entries with s in a later block stay zero."""
+    L = q.shape[0]
+    B = torch.zeros((L, L), dtype=torch.float64)
+    Pq = torch.zeros((L, L), dtype=torch.float64)
+    for I in range((L + BLK - 1) // BLK):
+        r0, r1 = BLK * I, min(BLK * (I + 1), L)
+        rho = g[r0 - 1] if I > 0 else torch.zeros_like(g[0])
+        X = rb(k[r0:r1] * torch.exp(g[r0:r1] - rho), on)
+        QX = rb(q[r0:r1] * torch.exp(g[r0:r1] - rho), on)
+        Y = rb(k[:r1] * torch.exp(rho - g[:r1]), on)
+        B[r0:r1, :r1] = X @ Y.T
+        Pq[r0:r1, :r1] = QX @ Y.T
+    return B, Pq
+
+
+def chunk_model(q, k, v, la, beta, S, scale, s, form="factored"):
     """One chunk (rows of one head) through the chunked form; s: the set of
-    sites that round.  Returns (o, S_next)."""
+    sites that round; form: how B and P are formed ("factored": Kg Kn^T and
+    Qg Kn^T; "blocked": blocked_products).  Returns (o, S_next)."""
     L = q.shape[0]
     g = torch.cumsum(la, 0)                                  # [L, dk] natural units
     G = g[-1]
@@ -74,7 +98,10 @@ def chunk_model(q, k, v, la, beta, S, scale, s):
     Kn = rb(k * torch.exp(-g), "operands" in s)
     Qg = rb(q * torch.exp(g), "operands" in s)
     Kd = rb(k * torch.exp(G - g), "operands" in s)
-    B = Kg @ Kn.T
+    if form == "blocked":
+        B, Pq = blocked_products(q, k, g, "operands" in s)
+    else:
+        B, Pq = Kg @ Kn.T, Qg @ Kn.T
     A = torch.tril(beta[:, None] * B, -1)                    # (I + A) E = Diag(beta)(V - Kg S0)
     # T = (I + A)^{-1}: diagonal blocks by the doubling product, the rest
     # by block forward substitution with the kernels' roundings
@@ -100,7 +127,7 @@ def chunk_model(q, k, v, la, beta, S, scale, s):
     Tb = rb(T * beta[None, :], "T" in s)                     # T Diag(beta)
     W = rb(Tb @ Kg, "W, U" in s)
     U = rb(Tb @ v, "W, U" in s)
-    P = rb(torch.tril(Qg @ Kn.T), "P" in s)
+    P = rb(torch.tril(Pq), "P" in s)
     S0 = rb(S, "S0 copy" in s)
     E = U - W @ S0
     Eb = rb(E, "E copy" in s)
@@ -109,7 +136,7 @@ def chunk_model(q, k, v, la, beta, S, scale, s):
     return rb(o, "output" in s), S_next
 
 
-def model_prefill(inp, scale, sites):
+def model_prefill(inp, scale, sites, form="factored"):
     """All sequences and heads of a packed batch through the chunk model."""
     f = lambda t: t.to(torch.float64)
     q, k, v, la, beta = (f(inp[x]) for x in ("q", "k", "v", "log_alpha", "beta"))
@@ -125,7 +152,7 @@ def model_prefill(inp, scale, sites):
             for c0 in range(cu[n], cu[n + 1], C):
                 c1 = min(c0 + C, cu[n + 1])
                 o[c0:c1, h], S = chunk_model(q[c0:c1, h], k[c0:c1, h], v[c0:c1, h],
-                                             la[c0:c1, h], beta[c0:c1, h], S, scale, sites)
+                                             la[c0:c1, h], beta[c0:c1, h], S, scale, sites, form)
             hT[n, h] = S
     return o.numpy(), hT.numpy()
 
@@ -167,3 +194,38 @@ def test_error_budget(case):
     # exceeds the total by much (roundings do not cancel systematically)
     assert rel(o_all, o_ref) <= 1e-2 and rel(h_all, h_ref) <= 1e-2
     assert max(e for e, _ in budget.values()) <= 1.5 * rel(o_all, o_ref) + 1e-4
+
+
+def strong_inputs(case):
+    inp = gen.prefill_inputs([300, 129], 2, 128, 128, "bf16", "uniform", state_std=0.02,
+                             seed=98, device="cpu")
+    la = inp["log_alpha"]
+    if case == "decay_3":
+        la.fill_(-3.0)
+    else:                        # channels alternating 0 and -4.5: 16-row blocks sum to -72
+        la[..., 0::2] = 0.0
+        la[..., 1::2] = -4.5
+    return inp
+
+
+@pytest.mark.parametrize("case", ["decay_3", "channels_0_4.5"])
+def test_blocked_form_error_budget(case):
+    """The blocked form the matrix paths take for chunks beyond the factored
+    range (every 16-row block's gate sum still inside it).  In exact
+    arithmetic it is the recurrence (pins the per-block factorisation); with
+    every bf16 rounding site on it stays well inside the bf16 bar, where the
+    factored form's bf16 operands overflow (e^{-g} past bf16's range)."""
+    inp = strong_inputs(case)
+    scale = 1.0 / math.sqrt(128)
+    h = lambda t: t.to(torch.float32).numpy()
+    o_ref, h_ref = oracle.prefill(h(inp["q"]), h(inp["k"]), h(inp["v"]), h(inp["log_alpha"]),
+                                  h(inp["beta"]), h0=h(inp["h0"]),
+                                  cu_seqlens=inp["cu_seqlens"].numpy().astype(np.int64),
+                                  scale=scale)
+    o0, h0_ = model_prefill(inp, scale, set(), "blocked")
+    assert rel(o0, o_ref) < 1e-10 and rel(h0_, h_ref) < 1e-10, (rel(o0, o_ref), rel(h0_, h_ref))
+    o1, h1 = model_prefill(inp, scale, set(SITES), "blocked")
+    report("budget %s: blocked form, every site" % case, o=rel(o1, o_ref), hT=rel(h1, h_ref))
+    assert rel(o1, o_ref) <= 1e-2 and rel(h1, h_ref) <= 1e-2
+    of, _ = model_prefill(inp, scale, {"operands"}, "factored")
+    assert not np.isfinite(of).all()
