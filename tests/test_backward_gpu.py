@@ -148,6 +148,29 @@ def test_backward_gate_domain(case):
     assert err / scale_ <= TOL
 
 
+@pytest.mark.parametrize("strength", [-3.0, -12.0])
+def test_backward_head_gate_beyond_factored_range(strength):
+    """Gated DeltaNet's one gate per (token, head) beyond the factored range:
+    -3 per token keeps every 16-row block inside it (the blocked form), -12
+    does not (the pairwise form).  The per-head gate's own kernels; every
+    gradient matches the oracle and is finite (dlog_alpha against the
+    magnitude of the terms it is a difference of, as for channel gates)."""
+    inp = make_case(LENS, 2, 395, gate="head")
+    inp["log_alpha"].fill_(strength)
+    g = gpu(inp, "head")
+    for key, x in g.items():
+        assert x is None or torch.isfinite(x).all(), key
+    r = ref(inp)
+    compare("backward head gate %g" % strength, g, r, skip=("dlog_alpha",))
+    # the head's gate sums its channels' terms: their per-row sums set the scale
+    terms = max(float(np.max(np.sum(np.abs(r["dq"] * host(inp["q"])), axis=-1))),
+                float(np.max(np.sum(np.abs(r["dk"] * host(inp["k"])), axis=-1))))
+    dla, dla_ref = host(g["dlog_alpha"]), r["dlog_alpha"]
+    err = float(np.max(np.abs(dla - dla_ref))) / max(float(np.max(np.abs(dla_ref))), terms)
+    report("backward head gate %g dlog_alpha" % strength, dlog_alpha=err)
+    assert err <= TOL
+
+
 def test_backward_zero_state_and_adjoint():
     inp = case([200, 64, 5], 2, 310, h0=False, dhT=False)
     compare("backward h0=0 dhT=0", gpu(inp, "channel"), ref(inp))
