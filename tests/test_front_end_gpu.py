@@ -98,8 +98,9 @@ def test_prefill_front_end(parts, dtype, path, d, gate):
                                                ("f32", "vector", 64, "channel")])
 def test_prefill_front_end_strong_gates(dtype, path, d, gate):
     """A gate scale of 4 (log_alpha = -4 softplus(x), about -3 per token):
-    every chunk leaves the factored range, so the front-end's gates feed the
-    exact pairwise form, which recomputes them from the pre-activations."""
+    every chunk leaves the factored range (its 16-row blocks stay inside
+    it), so the front-end's gates feed the blocked form (the vector path:
+    the pairwise form), which recomputes them from the pre-activations."""
     c = 4.0
     inp = raw_inputs(LENS, 2, d, dtype, 420, gate)
     o, hT = kda.prefill(inp["q"], inp["k"], inp["v"], None, None, h0=inp["h0"],

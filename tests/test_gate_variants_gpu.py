@@ -151,9 +151,9 @@ def test_decode_state_pool(dtype, d, gate):
 def test_gated_deltanet_beyond_factored_range(dtype, path, d, pattern):
     """Gated DeltaNet with gates of -3 per token (every 64-token chunk, or
     every other chunk of each sequence, beyond the factored form's range):
-    the exact pairwise form on every path, with the scalar gate loaded per
-    (token, head); parity with the oracle and bitwise equality with the KDA
-    call on the expanded gate."""
+    the blocked form on the matrix paths (the pairwise form on the vector
+    path), with the scalar gate loaded per (token, head); parity with the
+    oracle and bitwise equality with the KDA call on the expanded gate."""
     inp = inputs(dtype, d, 92)
     g = inp["head_gate"]
     if pattern == "all":

@@ -10,10 +10,12 @@ allow (any alpha in (0, 1], "Kimi Delta Attention: la atencion lineal
 detras de Kimi K2 y Qwen3", section "Cómo funciona Kimi Delta Attention
 paso a paso"): -3 and -10 per token on every channel, a mix of undecayed
 and -10 channels, and per-token gates uniform in [-12, 0].  Beyond the
-factored range every path switches to the exact pairwise form for the
-chunks concerned and must match the oracle; a further case alternates such
-chunks with ordinary ones inside each sequence (the first chunk included),
-so the switch between the two forms is exercised chunk by chunk.
+factored range every path switches, for the chunks concerned, to the
+blocked form (each 16-row block's own gate sum still in range: -3 per
+token) or the exact pairwise form (the vector path always) and must match
+the oracle; further cases alternate such chunks with ordinary ones inside
+each sequence (the first chunk included), and cycle through the factored,
+blocked and pairwise forms chunk by chunk.
 
 Batch: 200 short sequences (lengths 0..150, empty ones included, non-zero
 initial states), through each path; on the two-pass path this also walks
@@ -117,20 +119,23 @@ def test_whole_gate_domain(dtype, path, case):
     check(gate_case(inp, case), path, dtype, "gates %s" % case)
 
 
+@pytest.mark.parametrize("case", ["alternating", "tiers"])
 @pytest.mark.parametrize("tiles", [1, 2, 4])
-def test_fused_exact_form_every_tile_width(tiles):
-    """The fused path's exact pairwise form at each value-tile width (its
+def test_fused_exact_form_every_tile_width(tiles, case):
+    """The fused path's strong-gate forms at each value-tile width (its
     producer/consumer split differs with the width), on a batch with enough
-    pairs for the automatic tiling to matter."""
+    pairs for the automatic tiling to matter: blocked chunks alternating with
+    ordinary ones, and chunks cycling through the factored, blocked and
+    pairwise forms."""
     inp = gen.prefill_inputs([300, 64, 1, 129, 200], 8, 128, 128, "bf16", "uniform",
                              state_std=0.1, seed=85, device=DEV)
-    gate_case(inp, "alternating")
+    gate_case(inp, case)
     o, hT = kda.prefill(inp["q"], inp["k"], inp["v"], inp["log_alpha"], inp["beta"],
                         h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], path="matrix",
                         value_tiles=tiles)
     o_ref, h_ref = oracle_prefill(inp)
     eo, eh = rel_err(host(o), o_ref), rel_err(host(hT), h_ref)
-    report("fused exact form, %d value tiles" % tiles, o=eo, hT=eh)
+    report("fused %s gates, %d value tiles" % (case, tiles), o=eo, hT=eh)
     assert eo <= tol_for("bf16") and eh <= tol_for("bf16")
     assert torch.isfinite(o).all() and torch.isfinite(hT).all()
 

@@ -3,7 +3,8 @@ its outputs equal kda_fwd_prefill_ex's on the same inputs, bit for bit,
 for each kernel path, over two calls in a row on one GPU -- the second with
 a smaller input, so it must not depend on what the first left in the
 library's device array.  The second call's first half of tokens has gates
-of -3 per token, so its chunks there take the exact pairwise form.  The
+of -3 per token, so its chunks there take the blocked form (the vector
+path: the pairwise form).  The
 same kernels run on both entry points; only the workspace differs (a
 caller buffer vs the static array)."""
 import pytest
