@@ -169,10 +169,6 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     const bool matrix_ok = kda::mfma_supported(a) && kda::wy_supported(a);
     if ((path == KDA_PATH_MATRIX || path == KDA_PATH_MATRIX_TWO_PASS) && !matrix_ok)
         return KDA_STATUS_UNSUPPORTED;
-    // the fused input front-end runs on the vector and two-pass paths
-    const bool front = options && (options->front.l2norm_qk || options->front.gate_pre ||
-                                   options->front.beta_pre);
-    if (front && path == KDA_PATH_MATRIX) return KDA_STATUS_UNSUPPORTED;
     // the per-chunk state record is written by the two-pass carry (bf16, d = 128)
     const bool record = options && options->chunk_states;
     if (record && (path == KDA_PATH_VECTOR || path == KDA_PATH_MATRIX || !matrix_ok ||
@@ -181,7 +177,7 @@ int resolve(int64_t total_T, int32_t N, int32_t H, int32_t d_k, int32_t d_v, int
     pl->path = path;
     if (path == KDA_PATH_AUTO) {
         pl->path = !matrix_ok ? KDA_PATH_VECTOR
-                   : front || record || static_cast<int64_t>(N) * H < kTwoPassMaxPairs
+                   : record || static_cast<int64_t>(N) * H < kTwoPassMaxPairs
                        ? KDA_PATH_MATRIX_TWO_PASS
                        : KDA_PATH_MATRIX;
     }

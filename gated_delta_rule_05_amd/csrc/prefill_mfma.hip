@@ -99,6 +99,7 @@ struct alignas(16) Smem {
     float2 tot[2][4 * (DK / 2)];       // gate sums of the four 16-row blocks (log2 units)
     int xflag[2];                      // the chunk's form beyond the factored range: 0 none,
                                        // 1 blocked, 2 pairwise
+    float nrm[2][2][C];                // front-end: 1 / ||k||, 1 / ||q|| of each row
 };
 
 // |g| (log2 units) up to which e^{g} and e^{-g} stay inside fp32 (e^{80}).
@@ -132,24 +133,46 @@ struct ChunkView {
     __amdgpu_buffer_rsrc_t k, q, la, beta;
 };
 
+// With the front-end, la ranges over the bf16 gate pre-activations and
+// beta over the bf16 beta pre-activations when they are given.
 __device__ __forceinline__ ChunkView chunk_view(const bf16_t* k, const bf16_t* q,
                                                 const float* log_alpha, const float* beta,
-                                                int64_t c0, int len, int H, int h, int gate) {
+                                                int64_t c0, int len, int H, int h, int gate,
+                                                const FrontEnd& fe) {
     const int64_t e0 = (c0 * H + h) * DK;               // first element of row 0
     const uint32_t span = static_cast<uint32_t>((len - 1) * H * DK + DK);
+    const uint32_t hspan = static_cast<uint32_t>((len - 1) * H + 1);
     ChunkView cv;
     cv.k = rsrc(k + e0, 2u * span);
     cv.q = rsrc(q + e0, 2u * span);
     // gates: per key channel, or one per (token, head); none at all (a null
     // log_alpha) gives an empty range, where every load reads zero
-    if (gate == kGateChannel)
+    if (fe.gate_pre)
+        cv.la = gate == kGateChannel ? rsrc(fe.gate_pre + e0, 2u * span)
+                                     : rsrc(fe.gate_pre + c0 * H + h, 2u * hspan);
+    else if (gate == kGateChannel)
         cv.la = rsrc(log_alpha + e0, 4u * span);
     else if (log_alpha)
-        cv.la = rsrc(log_alpha + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
+        cv.la = rsrc(log_alpha + c0 * H + h, 4u * hspan);
     else
         cv.la = rsrc(log_alpha, 0u);
-    cv.beta = rsrc(beta + c0 * H + h, 4u * static_cast<uint32_t>((len - 1) * H + 1));
+    cv.beta = fe.beta_pre ? rsrc(fe.beta_pre + c0 * H + h, 2u * hspan)
+                          : rsrc(beta + c0 * H + h, 4u * hspan);
     return cv;
+}
+
+// The gate of row `row` of a chunk of `len` rows, channel pair (x, y), from
+// what a stager or the strong-gate step loaded: fp32 gates as they are, or
+// with the front-end's gate pre-activations (bf16, both channels in `raw`,
+// or the row's one value) log_alpha = -scale softplus(x), zero past the
+// sequence end (the loads read zero there, and softplus(0) is not).
+template <int GATE>
+__device__ __forceinline__ float2 front_gates(uint32_t raw, int row, int len, float scale) {
+    if (row >= len) return make_float2(0.f, 0.f);
+    if constexpr (GATE == kGateChannel)
+        return make_float2(-scale * softplus_f32(lo_bf(raw)), -scale * softplus_f32(hi_bf(raw)));
+    const float x = -scale * softplus_f32(lo_bf(raw));
+    return make_float2(x, x);
 }
 
 // Stager registers: rows 16w .. 16w+15 of one chunk, key channels 2l, 2l+1
@@ -159,19 +182,78 @@ struct StageRegs {
     u32x2 la[16];
 };
 
-template <int GATE>
+// gate_pre: the front-end's bf16 gate pre-activations (raw bits in la[r][0],
+// activated in place by front_rows before anything reads them).  In the
+// front-end's instantiation a per-head gate's row offsets are formed at the
+// load (opaque): hoisted, both layouts' 16 offsets would hold registers for
+// the whole kernel.
+template <int GATE, bool FRONT>
 __device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, int H, int w,
-                                          int lane) {
+                                          int lane, bool gate_pre) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
         const int off = (16 * w + r) * H * DK + 2 * lane;   // elements
         rg.k2[r] = ld32(cv.k, 2 * off);
         rg.q2[r] = ld32(cv.q, 2 * off);
         if constexpr (GATE == kGateChannel) {
-            rg.la[r] = ld64(cv.la, 4 * off);
+            rg.la[r] = FRONT && gate_pre ? u32x2{ld32(cv.la, 2 * off), 0u} : ld64(cv.la, 4 * off);
         } else {                                           // the row's scalar gate, both channels
-            const uint32_t x = ld32(cv.la, 4 * (16 * w + r) * H);
-            rg.la[r] = u32x2{x, x};
+            int ro = 16 * w + r;
+            if constexpr (FRONT) asm volatile("" : "+v"(ro));
+            if (FRONT && gate_pre) {
+                rg.la[r] = u32x2{static_cast<uint32_t>(ld16(cv.la, 2 * ro * H)), 0u};
+            } else {
+                const uint32_t x = ld32(cv.la, 4 * ro * H);
+                rg.la[r] = u32x2{x, x};
+            }
+        }
+    }
+}
+
+// x plus x of the lane DPP control CTRL selects, in the rows ROWS enables
+// (the others add zero)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float x) {
+    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+// Sum of x over the 64 lanes of the wave, in every lane: butterflies within
+// each row of 16 lanes (quad permutations, then the half-row and row
+// mirrors), the rows gathered into lane 63 by the row broadcasts of lanes
+// 15 and 31, and that lane read out.  Data-parallel-primitive moves, not the
+// LDS crossbar of a generic shuffle.
+__device__ __forceinline__ float wave_sum64(float x) {
+    x = dpp_add<0xb1, 0xf>(x);      // quad_perm [1, 0, 3, 2]
+    x = dpp_add<0x4e, 0xf>(x);      // quad_perm [2, 3, 0, 1]
+    x = dpp_add<0x141, 0xf>(x);     // row_half_mirror
+    x = dpp_add<0x140, 0xf>(x);     // row_mirror
+    x = dpp_add<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
+    x = dpp_add<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// The front-end on a stager's loaded rows (before their gate sums): the
+// gates from their pre-activations, in place, and the L2 norms of each
+// row's k and q (reduced over the wave: a row is its 64 lanes' channel
+// pairs) into nrm[0..1][row] as 1 / max(norm, eps).
+template <int GATE>
+__device__ __forceinline__ void front_rows(StageRegs& rg, float (*nrm)[C], const FrontEnd& fe,
+                                           int w, int lane, int len) {
+    if (fe.gate_pre) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float2 a = front_gates<GATE>(rg.la[r][0], 16 * w + r, len, fe.gate_scale);
+            rg.la[r] = u32x2{__float_as_uint(a.x), __float_as_uint(a.y)};
+        }
+    }
+    if (fe.l2norm) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float sk = wave_sum64(lo_bf(rg.k2[r]) * lo_bf(rg.k2[r]) + hi_bf(rg.k2[r]) * hi_bf(rg.k2[r]));
+            const float sq = wave_sum64(lo_bf(rg.q2[r]) * lo_bf(rg.q2[r]) + hi_bf(rg.q2[r]) * hi_bf(rg.q2[r]));
+            if (lane == 0) {
+                nrm[0][16 * w + r] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sk), kFrontEps));
+                nrm[1][16 * w + r] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sq), kFrontEps));
+            }
         }
     }
 }
@@ -193,8 +275,10 @@ __device__ __forceinline__ float2 block_gate_sum(const StageRegs& rg) {
 // sequence hold zeros (they were read out of range), so they add nothing to
 // the gate and contribute zero rows.  Every stager sees every channel's G,
 // so all of them take the same branch.
+// FRONT with l2norm: k and q of each row scaled by its 1 / norm (nrm[b]).
+template <bool FRONT>
 __device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
-                                           const float2* tot, int w, int lane) {
+                                           const float2* tot, int w, int lane, bool l2norm) {
     float run0 = 0.f, run1 = 0.f, G0 = 0.f, G1 = 0.f;
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -227,8 +311,15 @@ __device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
             const bool wild = !(fabsf(run0) <= kSafeLog2 && fabsf(run1) <= kSafeLog2);
             const float u0 = __builtin_amdgcn_exp2f(run0), u1 = __builtin_amdgcn_exp2f(run1);
             const float w0 = __builtin_amdgcn_exp2f(-run0), w1 = __builtin_amdgcn_exp2f(-run1);
-            const float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
-            const float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
+            float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
+            float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
+            if (FRONT && l2norm) {
+                const float nk = sm.nrm[b][0][row], nq = sm.nrm[b][1][row];
+                kx *= nk;
+                ky *= nk;
+                qx *= nq;
+                qy *= nq;
+            }
             const float n0 = kx * w0, n1 = ky * w1;
             *reinterpret_cast<uint32_t*>(sm.kg[b] + row * KS + 2 * lane) = pk(kx * u0, ky * u1);
             *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) =
@@ -254,8 +345,15 @@ __device__ __forceinline__ void stage_rows(Smem& sm, int b, const StageRegs& rg,
             run1 = __builtin_fmaf(__uint_as_float(rg.la[r][1]), kLog2e, run1);
             const float u0 = __builtin_amdgcn_exp2f(run0), u1 = __builtin_amdgcn_exp2f(run1);
             const float d0 = __builtin_amdgcn_exp2f(G0 - run0), d1 = __builtin_amdgcn_exp2f(G1 - run1);
-            const float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
-            const float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
+            float kx = lo_bf(rg.k2[r]), ky = hi_bf(rg.k2[r]);
+            float qx = lo_bf(rg.q2[r]), qy = hi_bf(rg.q2[r]);
+            if (FRONT && l2norm) {
+                const float nk = sm.nrm[b][0][row], nq = sm.nrm[b][1][row];
+                kx *= nk;
+                ky *= nk;
+                qx *= nq;
+                qy *= nq;
+            }
             *reinterpret_cast<uint32_t*>(sm.kg[b] + row * KS + 2 * lane) = pk(kx * u0, ky * u1);
             *reinterpret_cast<uint32_t*>(sm.qg[b] + row * KS + 2 * lane) = pk(qx * u0, qy * u1);
             kd0[r & 3] = kx * d0;
@@ -387,7 +485,12 @@ __device__ __forceinline__ void diag_inverse(Smem& sm, int b, int I, const f32x4
 
 }  // namespace
 
-template <int TV, int GATE>
+// FRONT: the fused input front-end (its own instantiation): q and k
+// L2-normalised per row when fe.l2norm, gates from bf16 pre-activations
+// (log_alpha = -fe.gate_scale softplus(x)) when fe.gate_pre, beta =
+// sigmoid(y) from bf16 fe.beta_pre.  The stagers apply it to the rows they
+// load, and the strong-gate step to the rows it reloads.
+template <int TV, int GATE, bool FRONT>
 __global__ __launch_bounds__(NT)
 void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
                          const bf16_t* __restrict__ v, const float* __restrict__ log_alpha,
@@ -395,8 +498,10 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                          const int32_t* __restrict__ cu, const int32_t* __restrict__ order,
                          int64_t groups, int R, int H, int DV, float scale,
                          bf16_t* __restrict__ o, float* __restrict__ hT,
-                         float* __restrict__ snapshots, int snap_tokens, int snap_cap)
+                         float* __restrict__ snapshots, int snap_tokens, int snap_cap,
+                         FrontEnd fe)
 {
+    if constexpr (!FRONT) fe = FrontEnd{};
     constexpr int NSLAB = TV / 16;                   // 16-column state slabs in the tile
     constexpr int NC = NSLAB < 4 ? NSLAB : 4;        // consumer waves
     constexpr int SPW = NSLAB / NC;                  // slabs per consumer wave (1 or 2)
@@ -469,8 +574,8 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     // this point: the other slot's Kg and Qg rows (the consumers read them in
     // the first phase only) and Kn (not formed for such a chunk).  Contains
     // barriers: every wave calls it, or none.
-    auto exact_chunk = [](int b, ChunkView cv, int H, int tid, int wave, int g, int ln)
-                           __attribute__((always_inline)) {
+    auto exact_chunk = [](int b, ChunkView cv, int H, int tid, int wave, int g, int ln,
+                          FrontEnd fe, int len) __attribute__((always_inline)) {
         if (sm.xflag[b] == 1) {
             // blocked form.  In each half, thread (rg, cg) loads rows
             // 4 rg .. +3, channels 4 cg + 2 half + {0, 1} (k, q as bf16
@@ -503,7 +608,14 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                     const int off = (4 * rg + i) * H * DK + 4 * cg + 2 * half;   // elements
                     kw[i] = ld32(cv.k, 2 * off);
                     qw[i] = ld32(cv.q, 2 * off);
-                    if constexpr (GATE == kGateChannel) {
+                    if (FRONT && fe.gate_pre) {
+                        const uint32_t raw = GATE == kGateChannel
+                                                 ? ld32(cv.la, 2 * off)
+                                                 : static_cast<uint32_t>(ld16(cv.la, 2 * (4 * rg + i) * H));
+                        const float2 a = front_gates<GATE>(raw, 4 * rg + i, len, fe.gate_scale);
+                        gw[i][0] = a.x;
+                        gw[i][1] = a.y;
+                    } else if constexpr (GATE == kGateChannel) {
                         const u32x2 l = ld64(cv.la, 4 * off);
                         gw[i][0] = __uint_as_float(l[0]);
                         gw[i][1] = __uint_as_float(l[1]);
@@ -541,8 +653,12 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = 4 * rg + i;
-                        const float kx = j ? hi_bf(kw[i]) : lo_bf(kw[i]);
-                        const float qx = j ? hi_bf(qw[i]) : lo_bf(qw[i]);
+                        float kx = j ? hi_bf(kw[i]) : lo_bf(kw[i]);
+                        float qx = j ? hi_bf(qw[i]) : lo_bf(qw[i]);
+                        if (FRONT && fe.l2norm) {
+                            kx *= sm.nrm[b][0][r];
+                            qx *= sm.nrm[b][1][r];
+                        }
                         const float gr = gw[i][j];               // g_r - rho_Ir
                         const float f = __builtin_amdgcn_exp2f(gr);
                         bx[r * BRS + cg] = bf(kx * f);
@@ -619,8 +735,18 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
                 const int off = row * H * DK + 32 * j + c;
                 kk[i] = __uint_as_float(static_cast<uint32_t>(ld16(cv.k, 2 * off)) << 16);
                 qq[i] = __uint_as_float(static_cast<uint32_t>(ld16(cv.q, 2 * off)) << 16);
-                const uint32_t lb = GATE == kGateChannel ? ld32(cv.la, 4 * off) : ld32(cv.la, 4 * row * H);
-                run += __uint_as_float(lb);
+                if (FRONT && fe.l2norm) {
+                    kk[i] *= sm.nrm[b][0][row];
+                    qq[i] *= sm.nrm[b][1][row];
+                }
+                if (FRONT && fe.gate_pre) {
+                    // one channel (or the row's one gate): the low half
+                    const uint32_t raw = ld16(cv.la, 2 * (GATE == kGateChannel ? off : row * H));
+                    run += front_gates<kGateHead>(raw, row, len, fe.gate_scale).x;
+                } else {
+                    const uint32_t lb = GATE == kGateChannel ? ld32(cv.la, 4 * off) : ld32(cv.la, 4 * row * H);
+                    run += __uint_as_float(lb);
+                }
                 gg[i] = run;
             }
             gs[r16 * 32 + c] = run;
@@ -668,7 +794,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         }
     };
     auto view_of = [&](int m) {
-        return chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h, GATE);
+        return chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h, GATE, fe);
     };
 
     if (wave >= NC) {
@@ -684,18 +810,30 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         uint32_t beta_next = 0u;
         auto prefetch = [&](int m) {
             if (!stager) return;
-            const ChunkView cv = chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h, GATE);
-            load_rows<GATE>(rg, cv, H, pw, lane);
-            if (pw == 0) beta_next = ld32(cv.beta, 4 * lane * H);
+            const ChunkView cv = chunk_view(k, q, log_alpha, beta, chunk_start(m), chunk_len(m), H, h, GATE, fe);
+            load_rows<GATE, FRONT>(rg, cv, H, pw, lane, FRONT && fe.gate_pre);
+            if (pw == 0) {
+                // the row offset formed here (an opaque lane index): hoisted,
+                // it would hold a register for the whole kernel
+                int lb = lane;
+                asm volatile("" : "+v"(lb));
+                beta_next = FRONT && fe.beta_pre ? static_cast<uint32_t>(ld16(cv.beta, 2 * lb * H))
+                                                 : ld32(cv.beta, 4 * lb * H);
+            }
         };
         auto totals = [&](int m) {
-            if (stager) sm.tot[m & 1][pw * (DK / 2) + lane] = block_gate_sum(rg);
+            if (!stager) return;
+            if constexpr (FRONT) front_rows<GATE>(rg, sm.nrm[m & 1], fe, pw, lane, chunk_len(m));
+            sm.tot[m & 1][pw * (DK / 2) + lane] = block_gate_sum(rg);
         };
         auto stage = [&](int m) {
             if (!stager) return;
             const int b = m & 1;
-            stage_rows(sm, b, rg, sm.tot[b], pw, lane);
-            if (pw == 0) sm.beta[b][lane] = __uint_as_float(beta_next);
+            stage_rows<FRONT>(sm, b, rg, sm.tot[b], pw, lane, fe.l2norm);
+            if (pw == 0)
+                sm.beta[b][lane] = FRONT && fe.beta_pre
+                                       ? (lane < chunk_len(m) ? sigmoid_f32(lo_bf(beta_next)) : 0.f)
+                                       : __uint_as_float(beta_next);
         };
         // A/P tile jobs, balanced greedily over the producers (weights: a
         // diagonal job with its inversion 3, a plain tile 1, the stagers'
@@ -782,7 +920,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             const bool x0 = sm.xflag[0] != 0;
             if (!x0) tiles(0);
             if (nch > 1) totals(1);
-            if (x0) exact_chunk(0, view_of(0), H, tid, wave, g, ln);
+            if (x0) exact_chunk(0, view_of(0), H, tid, wave, g, ln, fe, chunk_len(0));
             __syncthreads();
         }
         for (int ci = 0; ci < nch; ++ci) {
@@ -794,7 +932,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
             const bool xn = ci + 1 < nch && sm.xflag[(ci + 1) & 1] != 0;
             if (ci + 1 < nch && !xn) tiles(ci + 1);
             if (ci + 2 < nch) totals(ci + 2);
-            if (xn) exact_chunk((ci + 1) & 1, view_of(ci + 1), H, tid, wave, g, ln);
+            if (xn) exact_chunk((ci + 1) & 1, view_of(ci + 1), H, tid, wave, g, ln, fe, chunk_len(ci + 1));
             __syncthreads();
         }
         return;
@@ -849,7 +987,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         __syncthreads();
         __syncthreads();
         if (sm.xflag[0] != 0)
-            exact_chunk(0, view_of(0), H, tid, wave, g, ln);
+            exact_chunk(0, view_of(0), H, tid, wave, g, ln, fe, chunk_len(0));
         else if (NP == 4)
             p_tiles4(0, wave, g, ln);
         __syncthreads();
@@ -963,7 +1101,7 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
         }
         if (ci + 1 < nch) {
             if (sm.xflag[(ci + 1) & 1] != 0)
-                exact_chunk((ci + 1) & 1, view_of(ci + 1), H, tid, wave, g, ln);
+                exact_chunk((ci + 1) & 1, view_of(ci + 1), H, tid, wave, g, ln, fe, chunk_len(ci + 1));
             else if (NP == 4)
                 p_tiles4(ci + 1, wave, g, ln);
         }
@@ -981,24 +1119,27 @@ void prefill_mfma_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict_
     }
 }
 
-template <int TV, int GATE>
+template <int TV, int GATE, bool FRONT>
 static hipError_t launch_mfma_g(const PrefillArgs& a, int R, hipStream_t stream) {
     const int64_t groups = static_cast<int64_t>(a.N) * a.H;
     const int64_t blocks = prefill_grid_blocks(groups, R);
-    hipLaunchKernelGGL((prefill_mfma_kernel<TV, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
+    hipLaunchKernelGGL((prefill_mfma_kernel<TV, GATE, FRONT>), dim3(static_cast<unsigned>(blocks)), dim3(NT),
                        0, stream, static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                        static_cast<const bf16_t*>(a.v), a.log_alpha, a.beta, a.h0, a.cu_seqlens,
                        a.order, groups, R, a.H, a.d_v, a.scale, static_cast<bf16_t*>(a.o), a.hT,
-                       a.snapshots, a.snap_tokens, a.snap_cap);
+                       a.snapshots, a.snap_tokens, a.snap_cap, a.fe);
     return hipGetLastError();
 }
 
 // a per-head gate and no gate share one instantiation (no gate reads an
-// empty range: zeros)
+// empty range: zeros); the front-end has instantiations of its own
 template <int TV>
 static hipError_t launch_mfma_t(const PrefillArgs& a, int R, hipStream_t stream) {
-    return a.gate == kGateChannel ? launch_mfma_g<TV, kGateChannel>(a, R, stream)
-                                  : launch_mfma_g<TV, kGateHead>(a, R, stream);
+    if (a.fe.active())
+        return a.gate == kGateChannel ? launch_mfma_g<TV, kGateChannel, true>(a, R, stream)
+                                      : launch_mfma_g<TV, kGateHead, true>(a, R, stream);
+    return a.gate == kGateChannel ? launch_mfma_g<TV, kGateChannel, false>(a, R, stream)
+                                  : launch_mfma_g<TV, kGateHead, false>(a, R, stream);
 }
 
 bool mfma_supported(const PrefillArgs& a) {

@@ -176,7 +176,7 @@ typedef struct kda_prefill_options {
                                   sequence; other entries are not written.
                                   May not overlap any other buffer. */
     kda_front_end front;       /* the fused input front-end (all off when
-                                  zeroed); vector and two-pass paths */
+                                  zeroed); every path */
     void *chunk_states;        /* DEVICE, kda_chunk_states_bytes bytes,
                                   16-byte aligned, or NULL: the start state
                                   of every chunk of 64 tokens after a

@@ -346,7 +346,8 @@ GP, BP = BASE + 14 * GAP, BASE + 15 * GAP
     (0, (0, float("nan"), GP, None), dict(la=None), INVALID),
     (0, (0, 0.05, GP + 8, None), dict(la=None), MISALIGNED),         # per-channel: 16 bytes
     (0, (0, 0.05, None, BP + 1), dict(beta=None), MISALIGNED),
-    (2, (1, 0.0, None, None), {}, UNSUPPORTED),                      # not on the fused path
+    (2, (1, 0.0, None, None), dict(wsb=0), WS_SMALL),               # the fused path takes it too
+    (2, (0, 0.05, GP, BP), dict(la=None, beta=None, wsb=0), WS_SMALL),
     (3, (0, 0.05, GP, BP), dict(la=None, beta=None, o=addr(14, 64), wsb=1 << 34), INVALID),
 ])
 def test_prefill_front_end_checks(path, front, over, status):

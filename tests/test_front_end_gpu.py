@@ -4,8 +4,8 @@ Raw q and k (not normalised), bf16 gate pre-activations x and bf16 beta
 pre-activations y go in; the kernels normalise q and k per (token, head),
 form log_alpha = -c softplus(x) and beta = sigmoid(y) while staging, and
 run the recurrence.  Reference: the oracle's front_end activations (fp64)
-fed to the oracle's prefill / decode.  Cases: the two-pass matrix path
-(bf16, d = 128) and the vector path (fp32), ragged batches, per-channel
+fed to the oracle's prefill / decode.  Cases: both matrix paths (bf16,
+d = 128) and the vector path (fp32), ragged batches, per-channel
 and per-head gates, each part of the front-end on its own; decode at three
 head sizes.  Also: a call with only normalisation equals, within the bar,
 the plain call on inputs normalised outside.
@@ -71,6 +71,8 @@ PARTS = [(True, True, True), (True, False, False), (False, True, False), (False,
 @pytest.mark.parametrize("parts", PARTS)
 @pytest.mark.parametrize("dtype,path,d,gate", [("bf16", "two_pass", 128, "channel"),
                                                ("bf16", "two_pass", 128, "head"),
+                                               ("bf16", "matrix", 128, "channel"),
+                                               ("bf16", "matrix", 128, "head"),
                                                ("f32", "vector", 64, "channel")])
 def test_prefill_front_end(parts, dtype, path, d, gate):
     inp = raw_inputs(LENS, 2, d, dtype, 400, gate)
@@ -95,13 +97,16 @@ def test_prefill_front_end(parts, dtype, path, d, gate):
 
 @pytest.mark.parametrize("dtype,path,d,gate", [("bf16", "two_pass", 128, "channel"),
                                                ("bf16", "two_pass", 128, "head"),
+                                               ("bf16", "matrix", 128, "channel"),
+                                               ("bf16", "matrix", 128, "head"),
                                                ("f32", "vector", 64, "channel")])
-def test_prefill_front_end_strong_gates(dtype, path, d, gate):
-    """A gate scale of 4 (log_alpha = -4 softplus(x), about -3 per token):
-    every chunk leaves the factored range (its 16-row blocks stay inside
-    it), so the front-end's gates feed the blocked form (the vector path:
-    the pairwise form), which recomputes them from the pre-activations."""
-    c = 4.0
+@pytest.mark.parametrize("c", [4.0, 12.0])
+def test_prefill_front_end_strong_gates(dtype, path, d, gate, c):
+    """Gate scales of 4 and 12 (log_alpha = -c softplus(x), about -3 and -9
+    per token): every chunk leaves the factored range, its 16-row blocks
+    inside it at 4 (the blocked form) and beyond it at 12 (the pairwise
+    form; the vector path is pairwise at both), so the front-end's gates
+    feed those forms, which recompute them from the pre-activations."""
     inp = raw_inputs(LENS, 2, d, dtype, 420, gate)
     o, hT = kda.prefill(inp["q"], inp["k"], inp["v"], None, None, h0=inp["h0"],
                         cu_seqlens=inp["cu_seqlens"], path=path, gate=gate, l2norm_qk=True,
