@@ -184,23 +184,23 @@ struct StageRegs {
 
 // gate_pre: the front-end's bf16 gate pre-activations (raw bits in la[r][0],
 // activated in place by front_rows before anything reads them).  In the
-// front-end's instantiation a per-head gate's row offsets are formed at the
-// load (opaque): hoisted, both layouts' 16 offsets would hold registers for
+// front-end's instantiation the row offsets are formed at the load
+// (opaque): hoisted, both gate layouts' 16 offsets would hold registers for
 // the whole kernel.
-template <int GATE, bool FRONT>
-__device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, int H, int w,
-                                          int lane, bool gate_pre) {
+template <int GATE, bool PRE>
+__device__ __forceinline__ void load_rows_as(StageRegs& rg, const ChunkView& cv, int H, int w,
+                                             int lane, bool opaque) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-        const int off = (16 * w + r) * H * DK + 2 * lane;   // elements
+        int ro = 16 * w + r;
+        if (opaque) asm volatile("" : "+v"(ro));
+        const int off = ro * H * DK + 2 * lane;             // elements
         rg.k2[r] = ld32(cv.k, 2 * off);
         rg.q2[r] = ld32(cv.q, 2 * off);
         if constexpr (GATE == kGateChannel) {
-            rg.la[r] = FRONT && gate_pre ? u32x2{ld32(cv.la, 2 * off), 0u} : ld64(cv.la, 4 * off);
+            rg.la[r] = PRE ? u32x2{ld32(cv.la, 2 * off), 0u} : ld64(cv.la, 4 * off);
         } else {                                           // the row's scalar gate, both channels
-            int ro = 16 * w + r;
-            if constexpr (FRONT) asm volatile("" : "+v"(ro));
-            if (FRONT && gate_pre) {
+            if constexpr (PRE) {
                 rg.la[r] = u32x2{static_cast<uint32_t>(ld16(cv.la, 2 * ro * H)), 0u};
             } else {
                 const uint32_t x = ld32(cv.la, 4 * ro * H);
@@ -209,6 +209,12 @@ __device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, in
         }
     }
 }
+template <int GATE, bool FRONT>
+__device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, int H, int w,
+                                          int lane, bool gate_pre) {
+    if (FRONT && gate_pre) load_rows_as<GATE, true>(rg, cv, H, w, lane, FRONT);
+    else load_rows_as<GATE, false>(rg, cv, H, w, lane, FRONT);
+}
 
 // x plus x of the lane DPP control CTRL selects, in the rows ROWS enables
 // (the others add zero)
@@ -216,19 +222,19 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_add(float x) {
     return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
 }
-// Sum of x over the 64 lanes of the wave, in every lane: butterflies within
-// each row of 16 lanes (quad permutations, then the half-row and row
+// Sum of x over the 64 lanes of the wave, valid in lane 63: butterflies
+// within each row of 16 lanes (quad permutations, then the half-row and row
 // mirrors), the rows gathered into lane 63 by the row broadcasts of lanes
-// 15 and 31, and that lane read out.  Data-parallel-primitive moves, not the
-// LDS crossbar of a generic shuffle.
-__device__ __forceinline__ float wave_sum64(float x) {
+// 15 and 31.  Data-parallel-primitive moves, not the LDS crossbar of a
+// generic shuffle.
+__device__ __forceinline__ float wave_sum64_to_last(float x) {
     x = dpp_add<0xb1, 0xf>(x);      // quad_perm [1, 0, 3, 2]
     x = dpp_add<0x4e, 0xf>(x);      // quad_perm [2, 3, 0, 1]
     x = dpp_add<0x141, 0xf>(x);     // row_half_mirror
     x = dpp_add<0x140, 0xf>(x);     // row_mirror
     x = dpp_add<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
     x = dpp_add<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    return x;
 }
 
 // The front-end on a stager's loaded rows (before their gate sums): the
@@ -238,6 +244,13 @@ __device__ __forceinline__ float wave_sum64(float x) {
 template <int GATE>
 __device__ __forceinline__ void front_rows(StageRegs& rg, float (*nrm)[C], const FrontEnd& fe,
                                            int w, int lane, int len) {
+    // the loaded registers pass through an empty asm here, after the barrier
+    // that precedes this step: the arithmetic below, which reads nothing
+    // else from memory, would otherwise be scheduled right after the loads,
+    // ahead of that barrier, and wait for them there (in the critical phase)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+        asm volatile("" : "+v"(rg.la[r][0]), "+v"(rg.la[r][1]), "+v"(rg.k2[r]), "+v"(rg.q2[r]));
     if (fe.gate_pre) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -248,9 +261,9 @@ __device__ __forceinline__ void front_rows(StageRegs& rg, float (*nrm)[C], const
     if (fe.l2norm) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float sk = wave_sum64(lo_bf(rg.k2[r]) * lo_bf(rg.k2[r]) + hi_bf(rg.k2[r]) * hi_bf(rg.k2[r]));
-            const float sq = wave_sum64(lo_bf(rg.q2[r]) * lo_bf(rg.q2[r]) + hi_bf(rg.q2[r]) * hi_bf(rg.q2[r]));
-            if (lane == 0) {
+            const float sk = wave_sum64_to_last(lo_bf(rg.k2[r]) * lo_bf(rg.k2[r]) + hi_bf(rg.k2[r]) * hi_bf(rg.k2[r]));
+            const float sq = wave_sum64_to_last(lo_bf(rg.q2[r]) * lo_bf(rg.q2[r]) + hi_bf(rg.q2[r]) * hi_bf(rg.q2[r]));
+            if (lane == 63) {
                 nrm[0][16 * w + r] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sk), kFrontEps));
                 nrm[1][16 * w + r] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sq), kFrontEps));
             }
