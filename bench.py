@@ -29,7 +29,8 @@ reading a state once, beside the time of 4 single decode steps.
 
 other_prefill_workloads: the tiny fp32 batch, the 4 x 4096-token batch and
 the 64-sequence varlen batch, each timed alone against its algorithmic
-bytes (the library picks the path).
+bytes (the library picks the path); the varlen batch also from raw inputs
+(front_end: the fused input front-end on the fused path).
 
 front_end: the same prefill from raw inputs (the fused input front-end:
 q, k normalised in the kernel, bf16 gate and beta pre-activations, 1282
@@ -774,6 +775,32 @@ def main():
                         cu_seqlens=io["cu_seqlens"], out=oo, final_state=ho, workspace=wso,
                         max_seqlen=msl)
         o_ms = timed(run_o, max(args.steps, 20))
+        fe_o = None
+        if wname == "varlen_n64":
+            # the same batch from raw inputs (the fused input front-end on the
+            # path the library picks for it): q, k normalised in the kernel,
+            # bf16 gate and beta pre-activations with this workload's gate law
+            gpo = gen.normal((To, wo.H, wo.dk), 11, gen.LOG_ALPHA, dev, torch.bfloat16)
+            bpo = gen.normal((To, wo.H), 11, gen.BETA, dev, torch.bfloat16)
+            wsf = torch.empty(max(1, kda.prefill_workspace_bytes(To, No, wo.H, wo.dk, wo.dv,
+                                                                 kda.DTYPE_BF16, front=True,
+                                                                 max_seqlen=msl)),
+                              dtype=torch.uint8, device=dev)
+
+            def run_of():
+                kda.prefill(io["q"], io["k"], io["v"], None, None, h0=io["h0"],
+                            cu_seqlens=io["cu_seqlens"], out=oo, final_state=ho, workspace=wsf,
+                            max_seqlen=msl, l2norm_qk=True, gate_pre=gpo, gate_scale=0.05,
+                            beta_pre=bpo)
+            f_ms = timed(run_of, max(args.steps, 20))
+            fb = FRONT_BYTES_PER_HT * To * wo.H + ho.numel() * 4 * 2
+            fe_o = {"ms": f_ms, "tokens_per_s": To / (f_ms * 1e-3),
+                    "algorithmic_bytes_per_head_token": FRONT_BYTES_PER_HT,
+                    "achieved_GBps": fb / (f_ms * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": fb / (f_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "vs_plain_pct": 100.0 * (f_ms / o_ms - 1.0),
+                    "kernel": "prefill_mfma_kernel<128, 0, true>"}
+            del gpo, bpo, wsf
         # q, k, v, o in the input dtype, fp32 gates and beta; states in and out
         per_ht = (2 * wo.dk + 2 * wo.dv) * esz + 4 * wo.dk + 4
         nb = per_ht * To * wo.H + ho.numel() * 4 * (2 if io["h0"] is not None else 1)
@@ -789,6 +816,8 @@ def main():
                          "useful_TFLOPs": flops / (o_ms * 1e-3) / 1e12,
                          "mfma_useful_frac": (flops / (o_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS
                                               if esz == 2 else None)}
+        if fe_o is not None:
+            others[wname]["front_end"] = fe_o
         del io, oo, ho, wso
     torch.cuda.empty_cache()
 
