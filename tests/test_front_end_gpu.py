@@ -155,3 +155,37 @@ def test_decode_front_end(dtype, d, gate):
     eo, es = rel_err(host(o), o_ref), rel_err(host(S1), S_ref)
     report("front-end decode %s d=%d %s" % (dtype, d, gate), o=eo, S=es)
     assert eo <= tol_for(dtype) and es <= tol_for(dtype)
+
+
+@pytest.mark.parametrize("path,tiles", [("matrix", 1), ("two_pass", 8)])
+def test_prefill_front_end_with_snapshots(path, tiles):
+    """The front-end together with state snapshots (every 64 tokens, up to
+    4 per sequence): o and hT equal the front-end call without snapshots,
+    and each snapshot equals, bit for bit, the final state of a front-end
+    prefill of that prefix alone (the same path and value tiles)."""
+    lens = [300, 64, 1, 129, 0, 256]
+    H, snap, cap = 2, 64, 4
+    inp = raw_inputs(lens, H, 128, "bf16", 430)
+    kw = dict(path=path, value_tiles=tiles, l2norm_qk=True, gate_scale=C_GATE)
+    N = len(lens)
+    snaps = torch.full((N, cap, H, 128, 128), 5.0, dtype=torch.float32, device=DEV)
+    o, hT, snaps = kda.prefill(inp["q"], inp["k"], inp["v"], None, None, h0=inp["h0"],
+                               cu_seqlens=inp["cu_seqlens"], gate_pre=inp["gate_pre"],
+                               beta_pre=inp["beta_pre"], snapshot_tokens=snap, snapshots=snaps,
+                               **kw)
+    o0, hT0 = kda.prefill(inp["q"], inp["k"], inp["v"], None, None, h0=inp["h0"],
+                          cu_seqlens=inp["cu_seqlens"], gate_pre=inp["gate_pre"],
+                          beta_pre=inp["beta_pre"], **kw)
+    assert torch.equal(o, o0) and torch.equal(hT, hT0)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    pairs = [(n, j) for n in range(N) for j in range(cap) if (j + 1) * snap <= lens[n]]
+    idx = np.concatenate([np.arange(cu[n], cu[n] + (j + 1) * snap) for n, j in pairs])
+    sel = torch.tensor(idx, device=DEV)
+    plens = [(j + 1) * snap for _, j in pairs]
+    pcu = torch.tensor(np.concatenate([[0], np.cumsum(plens)]), dtype=torch.int32, device=DEV)
+    ph0 = inp["h0"][torch.tensor([n for n, _ in pairs], device=DEV)].contiguous()
+    sub = {x: inp[x][sel].contiguous() for x in ("q", "k", "v", "gate_pre", "beta_pre")}
+    _, phT = kda.prefill(sub["q"], sub["k"], sub["v"], None, None, h0=ph0, cu_seqlens=pcu,
+                         gate_pre=sub["gate_pre"], beta_pre=sub["beta_pre"], **kw)
+    got = torch.stack([snaps[n, j] for n, j in pairs])
+    assert torch.equal(got, phT)
