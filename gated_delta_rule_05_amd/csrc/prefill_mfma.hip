@@ -216,25 +216,47 @@ __device__ __forceinline__ void load_rows(StageRegs& rg, const ChunkView& cv, in
     else load_rows_as<GATE, false>(rg, cv, H, w, lane, FRONT);
 }
 
-// x plus x of the lane DPP control CTRL selects, in the rows ROWS enables
-// (the others add zero)
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_add(float x) {
-    return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+// The lane that DPP control CTRL selects (every row enabled).
+template <int CTRL>
+__device__ __forceinline__ float dpp_from(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
 }
-// Sum of x over the 64 lanes of the wave, valid in lane 63: butterflies
-// within each row of 16 lanes (quad permutations, then the half-row and row
-// mirrors), the rows gathered into lane 63 by the row broadcasts of lanes
-// 15 and 31.  Data-parallel-primitive moves, not the LDS crossbar of a
-// generic shuffle.
-__device__ __forceinline__ float wave_sum64_to_last(float x) {
-    x = dpp_add<0xb1, 0xf>(x);      // quad_perm [1, 0, 3, 2]
-    x = dpp_add<0x4e, 0xf>(x);      // quad_perm [2, 3, 0, 1]
-    x = dpp_add<0x141, 0xf>(x);     // row_half_mirror
-    x = dpp_add<0x140, 0xf>(x);     // row_mirror
-    x = dpp_add<0x142, 0xa>(x);     // row_bcast:15 into rows 1 and 3
-    x = dpp_add<0x143, 0xc>(x);     // row_bcast:31 into rows 2 and 3
-    return x;
+// x + y after v_permlane32_swap / v_permlane16_swap exchange the halves of
+// the pair across lane bit 5 / bit 4: in lanes with that bit clear both
+// terms are x (own and partner's), in the others both are y.
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+// Sums over the 64 lanes of the wave of 16 values per lane (v[r]: row r),
+// as a reduce-scatter: each step pairs lanes across one bit of the lane
+// index, and each lane keeps half of its values (its partner the other
+// half) and adds its partner's copy of that half -- lane bit 5 and bit 4
+// through the permlane swaps, bit 3 and bit 2 through the row and half-row
+// mirrors (each pairs across that bit), the last two bits summed by quad
+// permutations.  Lane L ends with the total of row L / 4.  Every step is a
+// VALU lane move; none goes through LDS.
+__device__ __forceinline__ float wave_sum16_scatter(const float (&v)[16], int lane) {
+    const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0;
+    float w[8], x[4], y[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = swap32_sum(v[j], v[j + 8]);      // row j + 8 b5
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = swap16_sum(w[j], w[j + 4]);      // row 8 b5 + 4 b4 + j
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float keep = b3 ? x[j + 2] : x[j], send = b3 ? x[j] : x[j + 2];
+        y[j] = keep + dpp_from<0x140>(send);          // row_mirror: lane 15 - p of the row
+    }
+    const float keep = b2 ? y[1] : y[0], send = b2 ? y[0] : y[1];
+    float z = keep + dpp_from<0x141>(send);           // row_half_mirror: lane 7 - p of the 8
+    z += dpp_from<0xb1>(z);                           // quad_perm [1, 0, 3, 2]
+    z += dpp_from<0x4e>(z);                           // quad_perm [2, 3, 0, 1]
+    return z;
 }
 
 // The front-end on a stager's loaded rows (before their gate sums): the
@@ -259,14 +281,16 @@ __device__ __forceinline__ void front_rows(StageRegs& rg, float (*nrm)[C], const
         }
     }
     if (fe.l2norm) {
+        float vk[16], vq[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float sk = wave_sum64_to_last(lo_bf(rg.k2[r]) * lo_bf(rg.k2[r]) + hi_bf(rg.k2[r]) * hi_bf(rg.k2[r]));
-            const float sq = wave_sum64_to_last(lo_bf(rg.q2[r]) * lo_bf(rg.q2[r]) + hi_bf(rg.q2[r]) * hi_bf(rg.q2[r]));
-            if (lane == 63) {
-                nrm[0][16 * w + r] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sk), kFrontEps));
-                nrm[1][16 * w + r] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sq), kFrontEps));
-            }
+            vk[r] = lo_bf(rg.k2[r]) * lo_bf(rg.k2[r]) + hi_bf(rg.k2[r]) * hi_bf(rg.k2[r]);
+            vq[r] = lo_bf(rg.q2[r]) * lo_bf(rg.q2[r]) + hi_bf(rg.q2[r]) * hi_bf(rg.q2[r]);
+        }
+        const float sk = wave_sum16_scatter(vk, lane), sq = wave_sum16_scatter(vq, lane);
+        if ((lane & 3) == 0) {                        // lane L holds row L / 4
+            nrm[0][16 * w + (lane >> 2)] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sk), kFrontEps));
+            nrm[1][16 * w + (lane >> 2)] = __builtin_amdgcn_rcpf(fmaxf(__builtin_sqrtf(sq), kFrontEps));
         }
     }
 }
