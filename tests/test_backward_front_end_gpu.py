@@ -8,7 +8,9 @@ rule through the front-end (oracle.front_end_backward), all on the same
 stored inputs.  Cases: each part of the front-end on its own and all
 together, per-channel and per-head gates, a ragged packed batch with
 empty and one-token sequences, non-zero h0 and dhT; normalisation alone
-with no gate; an all-empty batch (dh0 = dhT).
+with no gate; an all-empty batch (dh0 = dhT); per-row power-of-two scales
+of q and k, which scale dq and dk by the inverse factor, bit for bit, and
+leave the other gradients unchanged.
 
 Bar: max-relative error <= 2e-2 per gradient tensor, the backward's bar.
 """
@@ -155,3 +157,29 @@ def test_backward_front_end_from_saved_chunk_states(parts, gate):
         assert e <= TOL, (key, e)
     for key, e in near.items():
         assert e <= 1e-2, (key, e)
+
+
+def test_backward_front_end_row_scale_invariance():
+    """Normalisation is invariant to a positive factor per (token, head) row,
+    so with q and k rows scaled by powers of two (2^-8 .. 2^8) the gradient
+    with respect to a raw row scales by the inverse factor and every other
+    gradient is unchanged.  A power of two passes exactly through each step
+    (the norm, its reciprocal, the projection, the bf16 rounding), so both
+    hold bit for bit: dq = 2^-e dq_unscaled and dk likewise, the same bits
+    for dv, dlog_alpha, dbeta and dh0."""
+    parts, gate = (True, True, True), "channel"
+    inp = case(parts, gate, 530)
+    T, H = inp["q"].shape[:2]
+    rng = np.random.default_rng(531)
+    eq = torch.from_numpy(rng.integers(-8, 9, size=(T, H))).to(DEV).double()
+    ek = torch.from_numpy(rng.integers(-8, 9, size=(T, H))).to(DEV).double()
+    scaled = lambda x, e, s: (x.double() * torch.pow(2.0, s * e)[..., None]).to(x.dtype)
+    kw = dict(h0=inp["h0"], dhT=inp["dhT"], cu_seqlens=inp["cu"], gate=gate, l2norm_qk=True,
+              gate_pre=inp["gp"], gate_scale=C_GATE, beta_pre=inp["bp"])
+    g1 = kda.backward(inp["q"], inp["k"], inp["v"], None, None, inp["do"], **kw)
+    g2 = kda.backward(scaled(inp["q"], eq, 1), scaled(inp["k"], ek, 1), inp["v"], None, None,
+                      inp["do"], **kw)
+    assert torch.equal(g2["dq"], scaled(g1["dq"], eq, -1))
+    assert torch.equal(g2["dk"], scaled(g1["dk"], ek, -1))
+    for key in ("dv", "dlog_alpha", "dbeta", "dh0"):
+        assert torch.equal(g2[key], g1[key]), key

@@ -8,7 +8,9 @@ fed to the oracle's prefill / decode.  Cases: both matrix paths (bf16,
 d = 128) and the vector path (fp32), ragged batches, per-channel
 and per-head gates, each part of the front-end on its own; decode at three
 head sizes.  Also: a call with only normalisation equals, within the bar,
-the plain call on inputs normalised outside.
+the plain call on inputs normalised outside; and per-row power-of-two
+scales of q and k (with some all-zero rows) leave every bit of the
+outputs unchanged, on every prefill path and in decode.
 
 Bars: max-relative error <= 1e-5 (fp32) or 2e-2 (bf16).
 """
@@ -189,3 +191,80 @@ def test_prefill_front_end_with_snapshots(path, tiles):
                          gate_pre=sub["gate_pre"], beta_pre=sub["beta_pre"], **kw)
     got = torch.stack([snaps[n, j] for n, j in pairs])
     assert torch.equal(got, phT)
+
+
+def scaled_rows(x, e):
+    """x with row (token, head) multiplied by 2^e[token, head]: exact in bf16
+    and fp32 (only the exponent changes)."""
+    return (x.double() * torch.pow(2.0, e.double())[..., None]).to(x.dtype)
+
+
+@pytest.mark.parametrize("dtype,path,d,gate", [("bf16", "two_pass", 128, "channel"),
+                                               ("bf16", "matrix", 128, "channel"),
+                                               ("bf16", "matrix", 128, "head"),
+                                               ("f32", "vector", 64, "channel")])
+def test_prefill_normalisation_row_scale_invariance(dtype, path, d, gate):
+    """The in-kernel normalisation of q and k is a per-(token, head) row
+    operation, so scaling each row of q and of k by its own power of two
+    (2^-8 .. 2^8) changes no normalised value: a power-of-two factor passes
+    exactly through every step (the squares and their sum, the square root
+    at an even power, the reciprocal, the products), so the call on the
+    scaled inputs must give the same bits as the call on the originals.  A
+    row that picked up another row's norm (inside one reduction, the rows
+    differ by up to 2^16) would be far off.  Some rows are all zero (q, k or
+    both), which the normalisation keeps at zero (their norm is below the
+    1e-6 floor); the unscaled call is also checked against the oracle."""
+    inp = raw_inputs(LENS, 2, d, dtype, 440, gate)
+    T, H = inp["q"].shape[:2]
+    rng = np.random.default_rng(441)
+    zq = torch.from_numpy(rng.random((T, H)) < 0.05).to(DEV)
+    zk = torch.from_numpy(rng.random((T, H)) < 0.05).to(DEV)
+    inp["q"][zq] = 0
+    inp["k"][zk] = 0
+    eq = torch.from_numpy(rng.integers(-8, 9, size=(T, H))).to(DEV)
+    ek = torch.from_numpy(rng.integers(-8, 9, size=(T, H))).to(DEV)
+    kw = dict(h0=inp["h0"], cu_seqlens=inp["cu_seqlens"], path=path, gate=gate, l2norm_qk=True,
+              gate_pre=inp["gate_pre"], gate_scale=C_GATE, beta_pre=inp["beta_pre"])
+    o1, h1 = kda.prefill(inp["q"], inp["k"], inp["v"], None, None, **kw)
+    o2, h2 = kda.prefill(scaled_rows(inp["q"], eq), scaled_rows(inp["k"], ek), inp["v"], None,
+                         None, **kw)
+    o_ref, h_ref = reference(inp, (True, True, True))
+    eo, eh = rel_err(host(o1), o_ref), rel_err(host(h1), h_ref)
+    so, sh = rel_err(host(o2), host(o1)), rel_err(host(h2), host(h1))
+    report("front-end row scales %s %s %s" % (dtype, path, gate), o=eo, hT=eh, o_scaled=so,
+           hT_scaled=sh)
+    assert eo <= tol_for(dtype) and eh <= tol_for(dtype)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_decode_normalisation_row_scale_invariance(dtype, d):
+    """Decode's normalisation is applied after its reductions (they are
+    linear in q and k, so a power-of-two row factor passes through them
+    exactly): row scales of 2^-8 .. 2^8 on q and k give the same bits, and
+    all-zero rows stay zero."""
+    N, H = 37, 3
+    inp = raw_inputs([1] * N, H, d, dtype, 450)
+    S = gen.decode_state(N, H, d, d, std=0.05, seed=451, device=DEV)
+    q, k, v = (inp[x].reshape(N, H, d).clone() for x in ("q", "k", "v"))
+    q[0, 1] = 0
+    k[2, 0] = 0
+    q[5, 2] = 0
+    k[5, 2] = 0
+    rng = np.random.default_rng(452)
+    eq = torch.from_numpy(rng.integers(-8, 9, size=(N, H))).to(DEV)
+    ek = torch.from_numpy(rng.integers(-8, 9, size=(N, H))).to(DEV)
+    gp = inp["gate_pre"].reshape(N, H, d)
+    bp = inp["beta_pre"].reshape(N, H)
+    kw = dict(gate_pre=gp, gate_scale=C_GATE, beta_pre=bp, l2norm_qk=True)
+    S1, S2 = S.clone(), S.clone()
+    o1 = kda.decode_step(q, k, v, None, None, S1, **kw)
+    o2 = kda.decode_step(scaled_rows(q, eq), scaled_rows(k, ek), v, None, None, S2, **kw)
+    qf, kf, la, beta = oracle.front_end(host(q), host(k), host(gp), host(bp), gate_scale=C_GATE)
+    o_ref, S_ref = oracle.decode_step(qf, kf, host(v), la, beta, host(S))
+    eo, es = rel_err(host(o1), o_ref), rel_err(host(S1), S_ref)
+    so, ss = rel_err(host(o2), host(o1)), rel_err(host(S2), host(S1))
+    report("front-end decode row scales %s d=%d" % (dtype, d), o=eo, S=es, o_scaled=so,
+           S_scaled=ss)
+    assert eo <= tol_for(dtype) and es <= tol_for(dtype)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
