@@ -974,10 +974,15 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
         // NSET iterations run without an early exit, so every path into the
         // loop header has the same loads in flight and the compiler's waits
         // cover only the set being stored.
+        // The stores wait ~256 clocks after the barrier: the state waves
+        // read this chunk's fragments from LDS first, and 35 KB of stores
+        // queued ahead of those reads lengthen the serial step (1.4 % of a
+        // 16-column carry call measured; 0 and 512 clocks are slower).
         int x = 0;
         for (; x + NSET <= count; x += NSET) {
 #pragma unroll
             for (int k = 0; k < NSET; ++k) {
+                __builtin_amdgcn_s_sleep(4);
                 put(r[(k + 2) % NSET], (k + 2) % 3);
                 fetch(r[(k + 2) % NSET], m0 + x + k + 2 + NSET);
                 __syncthreads();
