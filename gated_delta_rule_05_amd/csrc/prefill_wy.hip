@@ -1049,6 +1049,15 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             for (int I = 0; I < 4; ++I) uw[I] = U[I * 64 + lane];
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
+            // Kd^T of this chunk: read ahead of the E products (serviced
+            // while they run, before the loaders' stores reach LDS) in the
+            // plain carry; after them where the snapshot code needs the
+            // registers (0.7 % of a call measured)
+            u32x4 kf[16];
+            if constexpr (!SNAP) {
+#pragma unroll
+                for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
+            }
             u32x4 sb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
@@ -1066,9 +1075,10 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
                 for (int I = 0; I < 4; ++I) y[I] = mma32(wf[4 * I + kk], sb[kk], y[I]);
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) S[mm] = gm[mm] * S[mm];
-            u32x4 kf[16];
+            if constexpr (SNAP) {
 #pragma unroll
-            for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
+                for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
+            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int f = 0; f < 16; ++f) wf[f] = buf[bn][f * 64 + lane];   // -W of chunk x+1
