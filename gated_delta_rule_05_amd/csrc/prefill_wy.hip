@@ -1049,15 +1049,12 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             for (int I = 0; I < 4; ++I) uw[I] = U[I * 64 + lane];
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) gm[mm] = *reinterpret_cast<const f32x4*>(gam + 16 * mm + 4 * g);
-            // Kd^T of this chunk: read ahead of the E products (serviced
-            // while they run, before the loaders' stores reach LDS) in the
-            // plain carry; after them where the snapshot code needs the
-            // registers (0.7 % of a call measured)
+            // Kd^T of this chunk: read ahead of the E products, so it is
+            // serviced while they run, before the loaders' stores reach LDS
+            // (0.7 % of a call measured)
             u32x4 kf[16];
-            if constexpr (!SNAP) {
 #pragma unroll
-                for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
-            }
+            for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
             u32x4 sb[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) sb[kk] = pack4(S[2 * kk], S[2 * kk + 1]);
@@ -1075,10 +1072,6 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
                 for (int I = 0; I < 4; ++I) y[I] = mma32(wf[4 * I + kk], sb[kk], y[I]);
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm) S[mm] = gm[mm] * S[mm];
-            if constexpr (SNAP) {
-#pragma unroll
-                for (int f = 0; f < 16; ++f) kf[f] = F[(kFragK - kFragW + f) * 64 + lane];
-            }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int f = 0; f < 16; ++f) wf[f] = buf[bn][f * 64 + lane];   // -W of chunk x+1
@@ -1111,8 +1104,13 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             // least ceil(len / C) indices on)
             if (js >= 0 && (snap_cap < 0 || js < snap_cap) && (c_lo + x + 1) * C <= seq_len) {
                 const int64_t SE = static_cast<int64_t>(DK) * DV;
-                const int lo = 4 * g * DV + jc;
                 if (snap_cap >= 0) {
+                    // the lane's first element offset, opaque: formed here,
+                    // not ahead of the branch on every chunk (32 offsets,
+                    // ~70 instructions on the serial path of the record
+                    // mode, which never takes this branch)
+                    int lo = 4 * g * DV + jc;
+                    asm volatile("" : "+v"(lo));
                     float* sp = snapshot_at(snapshots, snap_cap, H, SE, n, js, h);
                     const __amdgpu_buffer_rsrc_t rs = rsrc(sp + j0, 4u * DK * DV);
 #pragma unroll
