@@ -98,14 +98,15 @@ struct alignas(16) PrepSmem {
 // - tok[0] first holds the per 4-row group gate sums and then their
 //   exclusive prefix (float [16][DK]), until the Kg rows are written;
 // - once A and P are formed, Kn and Qg (tok[1..2]) are dead and hold V
-//   (channel rows, tokens in fragment order), the -A strictly-lower
+//   (token rows in fragment order, channels in order), the -A strictly-lower
 //   blocks, the inverses (I + A_II)^{-1} and T Diag(beta) (upper blocks
 //   zero); Kg stays for W = T Kg.
-constexpr int kVtOff = 0;                          // d_k rows x CS
+constexpr int kVtOff = 0;                          // V: C token rows x TS (room for d_k rows x CS)
 constexpr int kAnOff = kVtOff + DK * CS;           // 6 blocks
 constexpr int kDinvOff = kAnOff + 6 * 16 * BS;     // 4 blocks
 constexpr int kTbOff = kDinvOff + 4 * 16 * BS;     // 64 rows x CS
 static_assert(kTbOff + C * CS <= 2 * C * TS, "V and T fit in two token arrays");
+static_assert(C * TS <= DK * CS, "token-major V fits before the -A blocks");
 static_assert(kAnOff % 8 == 0 && kDinvOff % 8 == 0 && kTbOff % 8 == 0, "16-byte aligned");
 static_assert(16 * DK * sizeof(float) <= C * TS * sizeof(uint16_t), "gate sums fit in one token array");
 static_assert(sizeof(PrepSmem) * 3 <= 160 * 1024, "three work-groups per CU");
@@ -767,16 +768,15 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
             for (int i = 0; i < 4; ++i) an[(aidx[x] * 16 + 4 * g + i) * BS + ln] = bf(aval[x][i]);
         }
         if (4 * cg < DV) {
+            // V token-major, token t in row fpos(t): a thread's 4 tokens are 4
+            // consecutive rows, each written as one 8-byte piece of 4
+            // channels, so the 32 lanes of a row group fill whole rows (the
+            // channel-major copy written before put 32 lanes on two bank
+            // offsets, a 16-way conflict)
             uint16_t* vt = spare_rows(sm) + kVtOff;
             const int pos = fpos(4 * rg);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int sh = 16 * (j & 1);
-                const uint32_t v0 = (vr[0][j >> 1] >> sh) & 0xffffu, v1 = (vr[1][j >> 1] >> sh) & 0xffffu;
-                const uint32_t v2 = (vr[2][j >> 1] >> sh) & 0xffffu, v3 = (vr[3][j >> 1] >> sh) & 0xffffu;
-                *reinterpret_cast<u32x2*>(vt + (4 * cg + j) * CS + pos) =
-                    u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
-            }
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x2*>(vt + (pos + i) * TS + 4 * cg) = vr[i];
         }
     }
     __syncthreads();
@@ -830,10 +830,12 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
     }
     const uint16_t* vt = spare_rows(sm) + kVtOff;
     for (int sl = wave; sl < DV / 16; sl += PT / 64) {
+        // B operand of K-step kk: rows 32 kk + 8g .. +7 hold the tokens of
+        // fragment order (T's order along K), read down channel 16 sl + ln
+        // with the LDS transpose read
         u32x4 vf[2];
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            vf[kk] = *reinterpret_cast<const u32x4*>(vt + (16 * sl + ln) * CS + 32 * kk + 8 * g);
+        for (int kk = 0; kk < 2; ++kk) vf[kk] = frag_tr(vt + 32 * kk * TS + 16 * sl, TS, lane);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
