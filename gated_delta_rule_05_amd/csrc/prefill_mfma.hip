@@ -63,7 +63,11 @@ constexpr int DK = 128;      // key channels
 constexpr int NW = 8;        // waves per work-group
 constexpr int NT = NW * 64;  // threads per work-group
 constexpr int KS = DK + 4;   // bf16 row stride of Kg / Qg / Kn (8-byte aligned rows)
-constexpr int RS = C + 8;    // bf16 row stride of Kd^T and P
+// bf16 row stride of Kd^T and P: 8-byte aligned rows (the operand reads take
+// 8-byte pieces), 34 dwords apart, so the stagers' Kd^T stores (one channel
+// row per lane, the same token columns) reach 16 bank pairs where a stride of
+// C + 8 reached 4, and P's 2-byte stores (rows 4 apart) no bank twice
+constexpr int RS = C + 4;
 constexpr int DS = 20;       // bf16 row stride of 16x16 blocks (-A off-diagonal, inverses)
 constexpr int NSTAGE = 4;    // stager waves, 16 rows of each chunk apiece
 constexpr int kMaxTileColumns = 128; // four consumer waves of up to two 16-column slabs
