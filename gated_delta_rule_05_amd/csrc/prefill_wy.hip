@@ -502,7 +502,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (GATE == kGateChannel) {
-                const u32x2 w = ld64(rgp, 2 * ((4 * rg + i) * H * DK + 4 * cg));
+                const u32x2 w = ld64_stream(rgp, 2 * ((4 * rg + i) * H * DK + 4 * cg));
                 la[i] = f32x4{-fe.gate_scale * softplus_f32(lo_bf(w[0])),
                               -fe.gate_scale * softplus_f32(hi_bf(w[0])),
                               -fe.gate_scale * softplus_f32(lo_bf(w[1])),
@@ -519,7 +519,7 @@ void prefill_wy_prep_kernel(const bf16_t* __restrict__ q, const bf16_t* __restri
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if constexpr (GATE == kGateChannel) {
-                la[i] = __builtin_bit_cast(f32x4, ld128(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
+                la[i] = __builtin_bit_cast(f32x4, ld128_stream(rla, 4 * ((4 * rg + i) * H * DK + 4 * cg)));
             } else {                                  // the row's scalar gate on every channel
                 const float x = __uint_as_float(ld32(rla, 4 * (4 * rg + i) * H));
                 la[i] = f32x4{x, x, x, x};
@@ -1016,7 +1016,7 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             const __amdgpu_buffer_rsrc_t ro = out_rsrc(m);
 #pragma unroll
             for (int I = 0; I < 4; ++I)
-                st64(ro, 2 * ((16 * I + ln) * vrow + 16 * wave + 4 * g), xob[b][wave][I][lane]);
+                st64_stream(ro, 2 * ((16 * I + ln) * vrow + 16 * wave + 4 * g), xob[b][wave][I][lane]);
         };
         // ======================= state waves =======================
         // fp32 state slab in the accumulator layout:
