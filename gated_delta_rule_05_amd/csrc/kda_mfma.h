@@ -45,18 +45,18 @@ __device__ __forceinline__ u32x2 ld64(__amdgpu_buffer_rsrc_t r, int off) {
 __device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
-// Single-use streams (the gates a prefill reads once, the outputs it writes
-// once) carry the non-temporal cache-policy bit, so they displace less of
-// the workspace data that a later pass reads back from the caches.
+// Single-use input streams (the gates a prefill reads once) carry the
+// non-temporal cache-policy bit, so they displace less of the workspace data
+// that a later pass reads back from the caches.  (Output tiles narrower than
+// a cache line keep the default policy: with the bit, partial lines leave
+// the cache before the neighbouring tiles fill them, and more bytes are
+// written.)
 constexpr int kCachePolicyNT = 2;
 __device__ __forceinline__ u32x2 ld64_stream(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, kCachePolicyNT));
 }
 __device__ __forceinline__ u32x4 ld128_stream(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT));
-}
-__device__ __forceinline__ void st64_stream(__amdgpu_buffer_rsrc_t r, int off, u32x2 x) {
-    __builtin_amdgcn_raw_buffer_store_b64(x, r, off, 0, kCachePolicyNT);
 }
 __device__ __forceinline__ uint16_t ld16(__amdgpu_buffer_rsrc_t r, int off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);

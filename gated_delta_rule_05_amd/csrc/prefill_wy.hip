@@ -1016,7 +1016,7 @@ void prefill_wy_carry_kernel(const uint8_t* __restrict__ ws, const float* __rest
             const __amdgpu_buffer_rsrc_t ro = out_rsrc(m);
 #pragma unroll
             for (int I = 0; I < 4; ++I)
-                st64_stream(ro, 2 * ((16 * I + ln) * vrow + 16 * wave + 4 * g), xob[b][wave][I][lane]);
+                st64(ro, 2 * ((16 * I + ln) * vrow + 16 * wave + 4 * g), xob[b][wave][I][lane]);
         };
         // ======================= state waves =======================
         // fp32 state slab in the accumulator layout:
