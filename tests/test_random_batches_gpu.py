@@ -14,6 +14,8 @@ ragged batches are those of the varlen path.  Every prefill path and the
 backward are compared with the fp64 oracle, including the worst single
 (sequence, head) slice of o.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -27,6 +29,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 PATHS = [("f32", "vector"), ("bf16", "matrix"), ("bf16", "two_pass")]
+# KDA_RANDOM_SEEDS=n adds n more seeded prefill cases (and n // 5 backward
+# cases) for a longer sweep; the default run keeps the fixed seeds only
+EXTRA = int(os.environ.get("KDA_RANDOM_SEEDS", "0"))
+PREFILL_SEEDS = [501, 502, 503, 504, 505, 506] + [10_000 + i for i in range(EXTRA)]
+BACKWARD_SEEDS = [511, 512, 513, 514] + [20_000 + i for i in range(EXTRA // 5)]
 
 
 def random_case(seed, dtype):
@@ -61,7 +68,7 @@ def random_case(seed, dtype):
     return inp, lens, kinds
 
 
-@pytest.mark.parametrize("seed", [501, 502, 503, 504, 505, 506])
+@pytest.mark.parametrize("seed", PREFILL_SEEDS)
 @pytest.mark.parametrize("dtype,path", PATHS)
 def test_random_batch_prefill(dtype, path, seed):
     inp, lens, kinds = random_case(seed, dtype)
@@ -78,7 +85,7 @@ def test_random_batch_prefill(dtype, path, seed):
     assert eo <= tol and eh <= tol and ew <= tol
 
 
-@pytest.mark.parametrize("seed", [511, 512, 513, 514])
+@pytest.mark.parametrize("seed", BACKWARD_SEEDS)
 def test_random_batch_backward(seed):
     inp, lens, kinds = random_case(seed, "bf16")
     T, H = inp["q"].shape[:2]
