@@ -546,7 +546,7 @@ def main():
         digest_counters(args.digest)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU; this build has no multi-GPU path "
+        print("bench.py measures one GPU; the library has no multi-GPU path "
               "(heads and sequences shard across GPUs without communication).",
               file=sys.stderr)
         sys.exit(2)
